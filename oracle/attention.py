@@ -1,0 +1,59 @@
+"""Single-query (decode) softmax attention over dequantized K/V, in float64
+(test infrastructure only).
+
+What the pages fix
+------------------
+* Attention runs over the K/V values that dequantization gives back,
+  x_hat = (Q(x) - zero_point) * scale, computed on the fly inside the
+  attention (tbr8.org §5, point 2; yunthe.com "quantization principle").
+* K/V of a layer are [heads, seq_len, head_dim] per sequence (yunthe.com,
+  "quantization principle").
+
+Readings
+--------
+* The attention itself is the standard scaled dot-product attention of one
+  query token against every stored token of its sequence (the stored tokens
+  include the current one): score_t = sm_scale * <q, K_hat_t>,
+  p = softmax(score), out = sum_t p_t * V_hat_t.  The pages do not print it;
+  ``sm_scale`` is an argument and the workloads use 1 / sqrt(head_dim).
+* Grouped-query attention: query head h reads KV head h // (Hq / Hkv).
+* An empty context (ctx = 0) gives a zero output.
+"""
+
+import numpy as np
+
+
+def decode_attention(q, khat, vhat, sm_scale: float):
+    """q: [Hq, D] (any float dtype); khat, vhat: float64 [Hkv, ctx, D].
+    Returns float64 [Hq, D]."""
+    q = np.asarray(q, np.float64)
+    hq, d = q.shape
+    hkv, ctx, _ = khat.shape
+    if hq % hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    group = hq // hkv
+    out = np.zeros((hq, d), np.float64)
+    if ctx == 0:
+        return out
+    for h in range(hq):
+        g = h // group
+        scores = float(sm_scale) * (khat[g] @ q[h])          # [ctx]
+        m = np.max(scores)
+        p = np.exp(scores - m)
+        out[h] = (p @ vhat[g]) / np.sum(p)
+    return out
+
+
+def paged_decode(pool, tables, ctx_lens, q, sm_scale: float):
+    """Decode attention for a batch read through block tables.
+
+    pool: ``paged.PoolArrays``; tables: list of per-sequence block-id lists;
+    ctx_lens: tokens per sequence; q: [S, Hq, D].  Returns float64 [S, Hq, D].
+    """
+    from .paged import gather_dequant
+    q = np.asarray(q)
+    out = np.zeros(q.shape, np.float64)
+    for s, (table, ctx) in enumerate(zip(tables, ctx_lens)):
+        khat, vhat = gather_dequant(pool, table, int(ctx))
+        out[s] = decode_attention(q[s], khat, vhat, sm_scale)
+    return out

@@ -1,0 +1,136 @@
+"""Pins for the oracle's block-pool model (oracle/allocator.py): a hand-traced
+golden sequence, the page's demo, the workloads' block counts, and invariants
+under random operation sequences."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as hst
+
+from oracle import allocator as A
+from oracle import kv_size
+
+from alloc_harness import GOLDEN, apply_op, random_ops, run_golden_trace
+
+
+class ModelAdapter:
+    def __init__(self, n, bs, max_seqs, free_order):
+        self.m = A.BlockPoolModel(n, bs, max_seqs, free_order)
+
+    def alloc(self, s, n):
+        return self.m.alloc(s, n)
+
+    def fork(self, p, c):
+        return self.m.fork(p, c)
+
+    def append(self, s, n):
+        return self.m.append(s, n)
+
+    def release(self, s):
+        return self.m.release(s)
+
+    def table(self, s):
+        return self.m.table(s)
+
+    def stats(self):
+        return self.m.stats()
+
+    def free_list(self):
+        return list(self.m.free)
+
+
+def test_golden_trace():
+    run_golden_trace(ModelAdapter, A.AllocError)
+
+
+def test_page_demo_counts():
+    g = json.load(open(os.path.join(GOLDEN, "page_figures.json")))["demo_allocation"]
+    m = A.BlockPoolModel(g["num_blocks"], g["block_size"], 4)
+    t = m.alloc(0, g["request_tokens"])
+    assert len(t) == g["blocks_taken"]
+    assert m.stats()["free"] == g["free_after"]
+
+
+def test_workload_block_counts():
+    g = json.load(open(os.path.join(GOLDEN, "page_figures.json")))["workload_block_counts"]
+    tiny = g["tiny"]
+    perm = np.random.default_rng(0).permutation(tiny["pool"])
+    m = A.BlockPoolModel(tiny["pool"], tiny["block_size"], 8, perm)
+    for s, c in enumerate(tiny["ctx"]):
+        assert len(m.alloc(s, c)) == tiny["blocks"][s]
+    st = m.stats()
+    assert st["used"] == tiny["used"] and st["free"] == tiny["free"]
+    # LIFO over the permutation: sequence 0 takes the permutation's last id
+    assert m.table(0)[0] == [int(perm[-1])]
+    assert m.table(1)[0] == [int(perm[-2]), int(perm[-3])]
+
+    g7 = g["llama7b_layer"]
+    assert g7["seqs"] * kv_size.num_blocks_for(g7["ctx"], g7["block_size"]) == g7["blocks_total"]
+    gp = g["prefill_store"]
+    assert gp["seqs"] * kv_size.num_blocks_for(gp["tokens"], gp["block_size"]) == gp["blocks_total"]
+
+    sp = g["shared_prefix"]
+    m = A.BlockPoolModel(sp["physical"], sp["block_size"], sp["seqs"] + 1)
+    m.alloc(-1, sp["prefix"])
+    for s in range(sp["seqs"]):
+        assert m.fork(-1, s) == []            # block-aligned prefix: no slot copy
+    m.release(-1)
+    for s in range(sp["seqs"]):
+        assert m.append(s, sp["ctx"] - sp["prefix"]) == []   # no COW at an aligned boundary
+    m.check_invariants()
+    st = m.stats()
+    assert st["used"] == sp["physical"] and st["free"] == 0
+    assert st["shared"] == sp["prefix_blocks"]
+    t0 = m.table(0)[0]
+    assert len(t0) == sp["logical_per_seq"]
+    assert all(m.refcount[b] == sp["prefix_refcount"] for b in t0[:sp["prefix_blocks"]])
+    with pytest.raises(A.NoBlocks):
+        m.append(0, 1)
+
+
+def test_unaligned_prefix_copy_path():
+    """A prefix ending mid-block: the fork copies the tail slot and the first
+    append of each child copies only the shared partial block."""
+    bs = 32
+    m = A.BlockPoolModel(64, bs, 4)
+    m.alloc(100, 4080 % 1024)          # 1008 tokens = 31.5 blocks
+    last = m.table(100)[0][-1]
+    assert m.fork(100, 0) == [(A.COPY_SLOT, 0, 1)]
+    cp = m.append(0, 1)
+    assert len(cp) == 1 and cp[0][0] == A.COPY_BLOCK and cp[0][1] == last
+    assert m.table(0)[0][:-1] == m.table(100)[0][:-1]
+    assert m.table(0)[0][-1] != last
+    assert m.append(100, 1) == []      # the parent now owns `last` alone
+    m.check_invariants()
+
+
+def test_failed_ops_leave_state_unchanged():
+    m = A.BlockPoolModel(4, 4, 2)
+    m.alloc(0, 9)
+    snap = (list(m.free), list(m.refcount), {k: (list(v.table), v.num_tokens) for k, v in m.seqs.items()})
+    with pytest.raises(A.NoBlocks):
+        m.alloc(1, 8)
+    with pytest.raises(A.NoBlocks):
+        m.append(0, 8)
+    with pytest.raises(A.UnknownSeq):
+        m.append(5, 1)
+    with pytest.raises(A.BadState):
+        m.alloc(0, 1)
+    m.alloc(1, 0)
+    with pytest.raises(A.NoSlots):
+        m.alloc(2, 0)
+    m.release(1)
+    assert snap == (list(m.free), list(m.refcount), {k: (list(v.table), v.num_tokens) for k, v in m.seqs.items()})
+
+
+@settings(max_examples=60, deadline=None)
+@given(seed=hst.integers(0, 2 ** 31 - 1), n_blocks=hst.integers(1, 24),
+       bs=hst.sampled_from([1, 2, 4, 16]))
+def test_random_ops_keep_invariants(seed, n_blocks, bs):
+    rng = np.random.default_rng(seed)
+    m = A.BlockPoolModel(n_blocks, bs, 6, rng.permutation(n_blocks))
+    for op in random_ops(rng, 80):
+        apply_op(m, op, A.AllocError)
+        m.check_invariants()

@@ -1,0 +1,150 @@
+"""Pins for oracle/paged.py and oracle/attention.py: paging indirection
+against the contiguous layout, pool-permutation invariance, closed-form
+special cases, a pure-Python brute force and torch's float64 SDPA."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import allocator as A
+from oracle import attention, paged, quant
+
+
+def _fill(rng, ctx_lens, hkv, d, bs, n_blocks, v_int4, perm):
+    pool = paged.PoolArrays(n_blocks, hkv, bs, d, v_int4)
+    m = A.BlockPoolModel(n_blocks, bs, len(ctx_lens), perm)
+    tables, hist = [], []
+    for s, c in enumerate(ctx_lens):
+        t = m.alloc(s, c)
+        k = rng.standard_normal((c, hkv, d)).astype(np.float16)
+        v = rng.standard_normal((c, hkv, d)).astype(np.float16)
+        paged.store_range(pool, t, k, v, 0, c)
+        tables.append(t)
+        hist.append((k, v))
+    return pool, tables, hist
+
+
+@pytest.mark.parametrize("v_int4", [False, True])
+def test_gather_equals_contiguous(v_int4):
+    rng = np.random.default_rng(0)
+    ctx = [1, 17, 50, 100]
+    pool, tables, hist = _fill(rng, ctx, 2, 64, 16, 64, v_int4, rng.permutation(64))
+    for s, c in enumerate(ctx):
+        kh, vh = paged.gather_dequant(pool, tables[s], c)
+        k, v = hist[s]
+        assert np.array_equal(kh, paged.quantize_contiguous(k.transpose(1, 0, 2), 16))
+        assert np.array_equal(vh, paged.quantize_contiguous(v.transpose(1, 0, 2), 16, v_int4))
+
+
+def test_rows_beyond_context_are_zero_and_ignored():
+    rng = np.random.default_rng(1)
+    pool, tables, hist = _fill(rng, [5], 1, 64, 16, 4, True, None)
+    b = tables[0][0]
+    assert not pool.k_codes[b, :, 5:].any() and not pool.v_codes[b, :, 5:].any()
+
+
+def test_permutation_invariance():
+    rng = np.random.default_rng(2)
+    ctx = [3, 40, 33]
+    q = rng.standard_normal((3, 4, 64)).astype(np.float16)
+    outs = []
+    for perm_seed in (10, 11):
+        r2 = np.random.default_rng(5)
+        pool, tables, _ = _fill(r2, ctx, 2, 64, 16, 16, False,
+                                np.random.default_rng(perm_seed).permutation(16))
+        outs.append(attention.paged_decode(pool, tables, ctx, q, 0.125))
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_append_equals_prefill():
+    """Re-quantizing a partial block from its exact rows after each one-token
+    append ends with the same bytes as quantizing the full block once."""
+    rng = np.random.default_rng(3)
+    bs, h, d = 16, 2, 64
+    k = rng.standard_normal((40, h, d)).astype(np.float16)
+    v = rng.standard_normal((40, h, d)).astype(np.float16)
+    pre = paged.PoolArrays(8, h, bs, d, True)
+    app = paged.PoolArrays(8, h, bs, d, True)
+    table = [4, 1, 6]
+    paged.store_range(pre, table, k, v, 0, 40)
+    paged.store_range(app, table, k, v, 0, 3)
+    for p in range(3, 40):
+        paged.store_range(app, table, k, v, p, p + 1)
+    for arr in ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp"):
+        assert np.array_equal(getattr(pre, arr), getattr(app, arr)), arr
+
+
+def test_ctx1_identical_keys_dominant_key():
+    rng = np.random.default_rng(4)
+    d = 64
+    v = rng.standard_normal((1, 9, d))
+    q = rng.standard_normal((1, d))
+    k = rng.standard_normal((1, 9, d))
+    # ctx = 1: the output is the single value row
+    assert np.array_equal(attention.decode_attention(q, k[:, :1], v[:, :1], 0.3)[0], v[0, 0])
+    # identical keys: uniform weights -> mean of the values
+    ksame = np.repeat(k[:, :1], 9, axis=1)
+    out = attention.decode_attention(q, ksame, v, 0.3)[0]
+    assert np.allclose(out, v[0].mean(0), rtol=0, atol=1e-12)
+    # one dominant key: weight ~1 on its row
+    kdom = np.zeros((1, 9, d))
+    kdom[0, 4] = 1000.0 * q[0] / np.linalg.norm(q[0])
+    out = attention.decode_attention(q, kdom, v, 1.0)[0]
+    assert np.allclose(out, v[0, 4], rtol=0, atol=1e-12)
+    # empty context -> zeros
+    assert not attention.decode_attention(q, k[:, :0], v[:, :0], 1.0).any()
+
+
+def test_brute_force_pure_python_tiny():
+    rng = np.random.default_rng(6)
+    hq, hkv, ctx, d = 4, 2, 7, 8
+    q = rng.standard_normal((hq, d))
+    k = rng.standard_normal((hkv, ctx, d))
+    v = rng.standard_normal((hkv, ctx, d))
+    out = attention.decode_attention(q, k, v, 0.7)
+    for h in range(hq):
+        g = h // 2
+        sc = [0.7 * sum(q[h][i] * k[g][t][i] for i in range(d)) for t in range(ctx)]
+        w = [math.exp(x - max(sc)) for x in sc]
+        z = sum(w)
+        for i in range(d):
+            ref = sum(w[t] * v[g][t][i] for t in range(ctx)) / z
+            assert abs(out[h][i] - ref) < 1e-12
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (8, 2), (64, 8)])
+def test_against_torch_sdpa_float64(hq, hkv):
+    rng = np.random.default_rng(hq)
+    ctx, d = 70, 128
+    q = rng.standard_normal((hq, d))
+    k = rng.standard_normal((hkv, ctx, d))
+    v = rng.standard_normal((hkv, ctx, d))
+    out = attention.decode_attention(q, k, v, 1 / math.sqrt(d))
+    rep = hq // hkv
+    kt = torch.from_numpy(np.repeat(k, rep, axis=0))[None]
+    vt = torch.from_numpy(np.repeat(v, rep, axis=0))[None]
+    qt = torch.from_numpy(q)[None, :, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[0, :, 0].numpy()
+    assert np.allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_tiny_config_end_to_end_quantized():
+    """The tiny decode shape: 4 sequences {1,17,50,100}, 2 heads, D=64,
+    bs=16 over a permuted 64-block pool; the paged result equals attention
+    over the contiguous quantize->dequantize of each sequence."""
+    rng = np.random.default_rng(8)
+    ctx = [1, 17, 50, 100]
+    pool, tables, hist = _fill(rng, ctx, 2, 64, 16, 64, False, rng.permutation(64))
+    q = rng.standard_normal((4, 2, 64)).astype(np.float16)
+    out = attention.paged_decode(pool, tables, ctx, q, 1 / 8)
+    for s, c in enumerate(ctx):
+        k, v = hist[s]
+        kh = paged.quantize_contiguous(k.transpose(1, 0, 2), 16)
+        vh = paged.quantize_contiguous(v.transpose(1, 0, 2), 16)
+        assert np.array_equal(out[s], attention.decode_attention(q[s], kh, vh, 1 / 8))
+    # ctx = 1 sequence: output equals its dequantized single V row
+    k0, v0 = hist[0]
+    c, sc = quant.quantize_int8_sym(v0[:, 0, :])
+    assert np.array_equal(out[0, 0], quant.dequantize_int8_sym(c, sc)[0])
