@@ -1,0 +1,207 @@
+"""Benchmark: one decode step of a block-quantized paged KV cache on one
+MI355X -- store each sequence's current token (re-quantizing its block) and
+run the fused dequantizing split-K attention plus its log-sum-exp reduce.
+
+Prints ONE JSON line.  ``value`` is the step's algorithmic HBM bytes per
+second (GB/s = 1e9 B/s) with all inputs resident in HBM; the line also gives
+tokens/s per layer, the fraction of the 8 TB/s HBM peak, the roofline of the
+decode kernels measured with HIP events on their stream, and the CPU oracle
+timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "quantized-KV decode attention GB/s (% of HBM peak) + tokens/s per layer"
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("paged_attn.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "paged_block_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode call from the committed rocprofv3 counter runs,
+    or None when they are missing or were taken on a different kernel."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_decode")
+
+
+def cpu_baseline(setup, seconds):
+    """The oracle's decode step (store the current token, attend over the
+    whole context) on a bounded sample of sequences, single-threaded."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention, paged
+    from paged_block_quantized_amd import runner
+
+    w = setup.w
+    bs = w.block_size
+    prepared = []
+    budget_seqs = min(w.num_seqs, 4)
+    for s in range(budget_seqs):
+        ctx = int(setup.ctx[s])
+        hk, hv = runner.sequence_history(setup, s)
+        nb = (ctx + bs - 1) // bs
+        pool = paged.PoolArrays(nb, w.num_kv_heads, bs, w.head_dim, w.v_codec == "i4")
+        paged.store_range(pool, list(range(nb)), hk, hv, 0, ctx - 1)
+        prepared.append((s, ctx, nb, pool, hk, hv, setup.q[s].cpu().numpy()))
+    with threadpool_limits(limits=1):
+        done, t0 = [], time.perf_counter()
+        while True:
+            for s, ctx, nb, pool, hk, hv, q in prepared:
+                paged.store_range(pool, list(range(nb)), hk, hv, ctx - 1, ctx)
+                khat, vhat = paged.gather_dequant(pool, list(range(nb)), ctx)
+                attention.decode_attention(q, khat, vhat, setup.sm_scale)
+                done.append(s)
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    ctx_done = np.array([int(setup.ctx[s]) for s in done])
+    sub = dataclasses.replace(w, num_seqs=len(done), prefix=0)
+    nbytes = runner.decode_bytes(sub, ctx_done) + runner.store_step_bytes(sub, ctx_done)
+    return {
+        "value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "tokens_per_s_per_layer": round(len(done) / dt, 2),
+        "sample": (f"{len(done)} sequence-steps over the first {budget_seqs} sequences of the "
+                   f"same workload (oracle store of the current token + float64 attention), "
+                   f"{dt:.1f} s, one thread; shared prefixes counted per sequence"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b")
+    ap.add_argument("--partition", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this path has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sys.path.insert(0, ROOT)
+    from paged_block_quantized_amd import runner, workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    print(f"setup {w.name}", file=sys.stderr, flush=True)
+    setup = runner.setup_decode(w, partition=args.partition)
+    S = w.num_seqs
+    dbytes = runner.decode_bytes(w, setup.ctx)
+    sbytes = runner.store_step_bytes(w, setup.ctx)
+
+    for _ in range(args.warmup):
+        setup.step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(K)] for _ in range(3)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[0][i].record(stream)
+        setup.store_current()
+        ev[1][i].record(stream)
+        setup.attend()
+        ev[2][i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    store_ms = float(np.mean([ev[0][i].elapsed_time(ev[1][i]) for i in range(K)]))
+    dec = np.array([ev[1][i].elapsed_time(ev[2][i]) for i in range(K)])
+    dec_ms = float(np.mean(dec))
+
+    # decode with a 1 GiB cache-clearing write before each call (outside the events)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    fl = []
+    for _ in range(10):
+        flush.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        setup.attend()
+        b.record(stream)
+        torch.cuda.synchronize()
+        fl.append(a.elapsed_time(b))
+    del flush
+
+    step_bytes = dbytes + sbytes
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = dbytes / (dec_ms * 1e-3) / 1e9
+    traffic = measured_traffic(w.name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "layers": 1, "num_seqs": S,
+            "context": int(setup.ctx.max()) if w.ctx_kind == "fixed" else [int(setup.ctx.min()), int(setup.ctx.max())],
+            "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+            "block_size": w.block_size, "k_codec": "int8_sym",
+            "v_codec": "int4_asym" if w.v_codec == "i4" else "int8_sym",
+            "partition": setup.partition, "shared_prefix": w.prefix,
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s_per_layer": round(S / (ms_step * 1e-3), 1),
+        "step_bytes": step_bytes,
+        "kernels_ms": {"quantize_store_1tok": round(store_ms, 5),
+                       "paged_attn_decode": round(dec_ms, 5),
+                       "paged_attn_decode_p10": round(float(np.percentile(dec, 10)), 5),
+                       "paged_attn_decode_p90": round(float(np.percentile(dec, 90)), 5),
+                       "paged_attn_decode_after_1GiB_flush": round(float(np.median(fl)), 5)},
+        "roofline": {
+            "kernel": "paged_attn_decode (split-K partition kernel + log-sum-exp reduce, one call)",
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": dbytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("cpu baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(setup, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,265 @@
+/*
+ * pbq.h -- C ABI of libpbq: PagedAttention decode over a block-quantized KV
+ * cache on one MI355X (gfx950).
+ *
+ * Sources (web pages, cited by site and section):
+ *   [tbr8]      tbr8.org, "How PagedAttention combined with block-wise
+ *               quantization solves long-text OOM caused by memory
+ *               fragmentation on mobile": §2 block virtualisation, §3
+ *               block-wise quantization, §4 the PagedKVCacheManager code
+ *               (pool tensors, allocate_for_request, store_kv), §5 advice
+ *               (INT8 K / INT4 V, fused QuantizedPagedAttention, pre-allocated
+ *               pool with reference counts).
+ *   [deepinsea] deepinsea.top, "PagedAttention memory management in depth":
+ *               "paging mechanism design" (BlockManager allocate/free),
+ *               "Copy-on-Write".
+ *   [yunthe]    yunthe.com, "KV-cache quantization and PagedAttention":
+ *               "quantization principle" (Q(x) and dequantization formulas),
+ *               "PagedAttention mechanism" (block_size, num_blocks sizing,
+ *               block_table, prefix sharing, fork writes to new blocks).
+ *
+ * Conventions for every entry point
+ *   - Every call returns kv_status; nothing is thrown or aborted across the
+ *     boundary.  On failure kv_last_error() returns a message for the calling
+ *     thread.  A failed host call leaves all state unchanged.
+ *   - Pointers named *_dev are device pointers (hipMalloc / torch CUDA
+ *     memory); all other pointers are host pointers.  The caller owns all
+ *     memory, device and host, and the stream.  The library never allocates
+ *     device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is enqueued asynchronously on it; the call returns after
+ *     enqueueing.  Launch failures return KV_ERR_HIP.
+ *   - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
+ *   - A kv_pool handle is not thread-safe: calls on one pool must not
+ *     overlap.  Distinct pools are independent.
+ */
+#ifndef PBQ_H
+#define PBQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kv_status {
+    KV_OK = 0,
+    KV_ERR_INVALID = 1,     /* bad argument (shape, alignment, size, range) */
+    KV_ERR_NO_BLOCKS = 2,   /* not enough free blocks; nothing was taken */
+    KV_ERR_UNKNOWN_SEQ = 3, /* sequence id not present */
+    KV_ERR_STATE = 4,       /* sequence id already present */
+    KV_ERR_NO_SLOTS = 5,    /* every tail slot is in use (max_seqs live) */
+    KV_ERR_HIP = 6          /* a HIP launch or runtime call failed */
+} kv_status;
+
+/* Codecs, one per (block, head) tile of block_size x head_dim values.
+ *   KV_CODEC_I8_SYM : int8 codes in [-127, 127], fp16 scale = fp16(absmax/127)
+ *                     over the rows the block holds; code = round-half-even
+ *                     of the fp32 quotient x / scale, clamped.  This is
+ *                     [yunthe] Q(x) with bits = 8 and zero point 128, stored
+ *                     as Q - 128; [tbr8] §4 store_kv's absmax/127 scale.
+ *   KV_CODEC_I4_ASYM: codes in [0, 15], two per byte along head_dim (even
+ *                     dimension in the low nibble); lo = min(0, min x),
+ *                     hi = max(0, max x), scale = fp16((hi - lo) / 15),
+ *                     zero point = clamp(round(-lo / scale), 0, 15) as u8;
+ *                     code = clamp(round(x / scale + zero point), 0, 15)
+ *                     ([yunthe] Q(x) with bits = 4).
+ *   A block whose statistics give scale 0 stores scale 0, zero point 0 and
+ *   all-zero codes.  Rows a block does not hold yet are zero bytes.
+ *   Dequantization is ([yunthe]) x_hat = (code - zero point) * scale. */
+typedef enum kv_codec { KV_CODEC_I8_SYM = 0, KV_CODEC_I4_ASYM = 1 } kv_codec;
+
+/* Shape of one layer's block pool ([tbr8] §4 PagedKVCacheManager.__init__). */
+typedef struct kv_pool_desc {
+    int32_t num_blocks;   /* N physical blocks, >= 1 */
+    int32_t block_size;   /* tokens per block: 16 or 32 ([tbr8] §2) */
+    int32_t num_kv_heads; /* Hkv >= 1 */
+    int32_t head_dim;     /* D: 64 or 128 */
+    int32_t k_codec;      /* must be KV_CODEC_I8_SYM ([tbr8] §5: K in INT8) */
+    int32_t v_codec;      /* KV_CODEC_I8_SYM or KV_CODEC_I4_ASYM */
+    int32_t max_seqs;     /* tail slots = most sequences alive at once, >= 1 */
+} kv_pool_desc;
+
+/* Byte sizes of the device arrays of one pool (all row-major):
+ *   k_codes  int8  [N, Hkv, bs, D]
+ *   v_codes  int8  [N, Hkv, bs, D]      (I8_SYM)
+ *            uint8 [N, Hkv, bs, D / 2]  (I4_ASYM, two codes per byte)
+ *   k_scale  fp16  [N, Hkv]
+ *   v_scale  fp16  [N, Hkv]
+ *   v_zp     uint8 [N, Hkv]  (0 bytes unless I4_ASYM)
+ *   tail_k   fp16  [max_seqs, Hkv, bs, D]  exact rows of each sequence's
+ *   tail_v   fp16  [max_seqs, Hkv, bs, D]  partially filled last block
+ * Every array must be 16-byte aligned. */
+typedef struct kv_pool_sizes {
+    size_t k_codes, v_codes, k_scale, v_scale, v_zp, tail_k, tail_v;
+} kv_pool_sizes;
+
+/* Device pointers to the arrays above (v_zp may be NULL for I8_SYM V). */
+typedef struct kv_pool_mem {
+    void* k_codes;
+    void* v_codes;
+    void* k_scale;
+    void* v_scale;
+    void* v_zp;
+    void* tail_k;
+    void* tail_v;
+} kv_pool_mem;
+
+/* A copy the caller must perform on the device before writing new tokens
+ * (copy-on-write, [deepinsea] "Copy-on-Write"; [yunthe] fork).
+ *   kind KV_COPY_BLOCK: codes, scales and zero point of block src -> dst.
+ *   kind KV_COPY_SLOT : fp16 tail slot src -> dst (K and V). */
+enum { KV_COPY_BLOCK = 0, KV_COPY_SLOT = 1 };
+typedef struct kv_copy {
+    int32_t kind;
+    int32_t src;
+    int32_t dst;
+} kv_copy;
+
+typedef struct kv_pool_stats_t {
+    int32_t total;  /* N */
+    int32_t free;   /* blocks on the free stack */
+    int32_t used;   /* blocks with refcount > 0 */
+    int32_t shared; /* blocks with refcount > 1 */
+    int32_t seqs;   /* live sequences */
+} kv_pool_stats_t;
+
+typedef struct kv_pool kv_pool; /* opaque host state */
+
+/* ---- sizing ------------------------------------------------------------
+ * Fills *out with the byte size of every device array for desc (the
+ * per-block form of [yunthe] "PagedAttention mechanism": num_blocks =
+ * memory / bytes per block).  KV_ERR_INVALID if desc is not supported. */
+kv_status kv_pool_bytes(const kv_pool_desc* desc, kv_pool_sizes* out);
+
+/* ---- host allocator ([deepinsea] "paging mechanism design"; [tbr8] §4, §5)
+ * The free list is a stack popped from its end.  It starts as free_order
+ * (a permutation of 0..N-1, length N) or 0..N-1 when free_order is NULL.
+ * KV_ERR_INVALID for a bad desc or a free_order that is not a permutation. */
+kv_status kv_pool_create(const kv_pool_desc* desc, const int32_t* free_order,
+                         kv_pool** out);
+void kv_pool_destroy(kv_pool* pool); /* NULL is ignored */
+
+/* Reserve ceil(num_tokens / bs) blocks (refcount 1) and the lowest free tail
+ * slot for a new sequence.  All-or-nothing: KV_ERR_NO_BLOCKS /
+ * KV_ERR_NO_SLOTS leave the pool unchanged; KV_ERR_STATE if seq exists;
+ * KV_ERR_INVALID if num_tokens < 0. */
+kv_status kv_seq_alloc(kv_pool* pool, int64_t seq, int32_t num_tokens);
+
+/* child shares every block of parent (refcount + 1 each) and takes the lowest
+ * free tail slot.  If parent's last block is partial, one KV_COPY_SLOT
+ * (parent slot -> child slot) is written to copies[0] (cap >= 1 required
+ * then).  *n_copies receives the count (0 or 1). */
+kv_status kv_seq_fork(kv_pool* pool, int64_t parent, int64_t child,
+                      kv_copy* copies, int32_t cap, int32_t* n_copies);
+
+/* Reserve n_tokens more positions.  If the last block is partial and shared,
+ * it is first replaced by a fresh block and one KV_COPY_BLOCK (old -> new) is
+ * reported; every position on a block boundary takes a fresh block.
+ * All-or-nothing (KV_ERR_NO_BLOCKS).  cap >= 1 is always enough. */
+kv_status kv_seq_append(kv_pool* pool, int64_t seq, int32_t n_tokens,
+                        kv_copy* copies, int32_t cap, int32_t* n_copies);
+
+/* Decrement every block of seq in table order; blocks reaching 0 are pushed
+ * on the free stack at once.  Releases the tail slot. */
+kv_status kv_seq_free(kv_pool* pool, int64_t seq);
+
+/* Host copy of seq's block table (cap entries available in out; out may be
+ * NULL with cap 0 to query), its token count and tail slot.  Any of the
+ * output pointers may be NULL. */
+kv_status kv_seq_table(const kv_pool* pool, int64_t seq, int32_t* out,
+                       int32_t cap, int32_t* n_blocks, int32_t* n_tokens,
+                       int32_t* slot);
+
+/* Batch form for building the decode arguments: for seqs[i], row i of
+ * tables[n, max_blocks] (unused entries set to 0), ctx_lens[i] and
+ * slots[i] (either of the last two may be NULL).  KV_ERR_INVALID if a table
+ * needs more than max_blocks entries. */
+kv_status kv_batch_tables(const kv_pool* pool, const int64_t* seqs, int32_t n,
+                          int32_t* tables, int32_t max_blocks,
+                          int32_t* ctx_lens, int32_t* slots);
+
+kv_status kv_pool_stats(const kv_pool* pool, kv_pool_stats_t* out);
+
+/* The free stack, bottom first (cap entries available; *n gets its size). */
+kv_status kv_pool_free_list(const kv_pool* pool, int32_t* out, int32_t cap,
+                            int32_t* n);
+
+/* ---- device calls -------------------------------------------------------- */
+
+/* Perform n copies (copies_dev: device array of kv_copy) on stream.  Block
+ * copies move codes, scales and zero points; slot copies move tail rows.
+ * Destinations must be distinct and not also sources in the same call. */
+kv_status kv_copy_blocks(const kv_pool_desc* desc, const kv_pool_mem* mem,
+                         const kv_copy* copies_dev, int32_t n, void* stream);
+
+/* Quantize and store new K/V tokens ([tbr8] §4 store_kv, per (block, head)
+ * as the scale tensor's shape gives; [yunthe] Q(x)).
+ *   k_dev, v_dev   fp16 [T, Hkv, D], token-major; the new tokens of
+ *                  sequence i are rows cu_seqlens[i] .. cu_seqlens[i+1]-1.
+ *   cu_seqlens_dev int32 [num_seqs + 1], non-decreasing, cu[0] = 0.
+ *   start_pos_dev  int32 [num_seqs]: position of sequence i's first new token
+ *                  (its token count before this store).
+ *   block_tables_dev int32 [num_seqs, max_blocks_per_seq]: row i covers every
+ *                  block up to position start + new - 1.
+ *   tail_slots_dev int32 [num_seqs]: each sequence's tail slot.
+ *   max_new_tokens >= every sequence's new-token count (sizes the grid).
+ * Every (block, head) touched is re-quantized from the exact fp16 rows it
+ * holds: rows before start_pos come from the tail slot, the rest from k/v.
+ * When a sequence's last touched block stays partial, its new rows are also
+ * written to the tail slot.  Device-resident indices are not checked: block
+ * ids must be < N, slots < max_seqs, and no block may be written twice in one
+ * call (shared blocks must have been copied first). */
+kv_status kv_quantize_store(const kv_pool_desc* desc, const kv_pool_mem* mem,
+                            const uint16_t* k_dev, const uint16_t* v_dev,
+                            int32_t num_seqs, const int32_t* cu_seqlens_dev,
+                            const int32_t* start_pos_dev,
+                            const int32_t* block_tables_dev,
+                            int32_t max_blocks_per_seq,
+                            const int32_t* tail_slots_dev,
+                            int32_t max_new_tokens, void* stream);
+
+/* Workspace bytes paged_attn_decode needs for these sizes (fp32 partial
+ * outputs and per-partition max / sum).  partition_size as below. */
+size_t paged_attn_workspace_bytes(const kv_pool_desc* desc, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_context_len,
+                                  int32_t partition_size);
+
+/* Fused dequantizing decode attention ([tbr8] §5 point 2: dequantize inside
+ * the attention, no intermediate buffers; [yunthe] x_hat):
+ *   out[s, h, :] = sum_t softmax_t(sm_scale * <q[s,h], K_hat[s, g, t]>) *
+ *                  V_hat[s, g, t, :],  g = h / (num_q_heads / Hkv),
+ *   over t < context_lens[s], token t read from block
+ *   block_tables[s][t / bs], row t % bs.
+ *   q_dev, out_dev fp16 [num_seqs, num_q_heads, D]; out written in full.
+ *   context_lens_dev int32 [num_seqs]; 0 gives a zero output row.
+ *   max_context_len >= every context length (sizes the grid).
+ *   partition_size: tokens per split-K partition, a multiple of block_size,
+ *   or 0 to let the library choose.  Partitions are combined by a second
+ *   log-sum-exp kernel.  workspace_dev (16-byte aligned, workspace_bytes >=
+ *   paged_attn_workspace_bytes(...)) may be NULL when that is 0.
+ *   num_q_heads must be a multiple of Hkv. */
+kv_status paged_attn_decode(const kv_pool_desc* desc, const kv_pool_mem* mem,
+                            const uint16_t* q_dev, uint16_t* out_dev,
+                            int32_t num_seqs, int32_t num_q_heads,
+                            const int32_t* block_tables_dev,
+                            int32_t max_blocks_per_seq,
+                            const int32_t* context_lens_dev,
+                            int32_t max_context_len, float sm_scale,
+                            int32_t partition_size, void* workspace_dev,
+                            size_t workspace_bytes, void* stream);
+
+/* Partition size (tokens) paged_attn_decode uses when given 0. */
+int32_t paged_attn_default_partition(const kv_pool_desc* desc,
+                                     int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t max_context_len);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* kv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PBQ_H */

@@ -1,0 +1,239 @@
+// C-ABI layer: argument validation, sizing, and dispatch of the device calls
+// declared in include/pbq.h.  No exception crosses the boundary; every
+// failure sets a thread-local message.
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include <cmath>
+#include <string>
+
+#include "pbq_internal.h"
+
+namespace pbq {
+
+namespace {
+thread_local std::string g_last_error;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+kv_status check_device_desc(const kv_pool_desc* d) {
+    if (!d) return fail(KV_ERR_INVALID, "desc is NULL");
+    if (d->num_blocks < 1) return fail(KV_ERR_INVALID, "num_blocks must be >= 1");
+    if (d->block_size != 16 && d->block_size != 32)
+        return fail(KV_ERR_INVALID, "block_size must be 16 or 32");
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(KV_ERR_INVALID, "head_dim must be 64 or 128");
+    if (d->num_kv_heads < 1 || d->num_kv_heads > 65535)
+        return fail(KV_ERR_INVALID, "num_kv_heads must be in [1, 65535]");
+    if (d->max_seqs < 1) return fail(KV_ERR_INVALID, "max_seqs must be >= 1");
+    if (d->k_codec != KV_CODEC_I8_SYM) return fail(KV_ERR_INVALID, "k_codec must be KV_CODEC_I8_SYM");
+    if (d->v_codec != KV_CODEC_I8_SYM && d->v_codec != KV_CODEC_I4_ASYM)
+        return fail(KV_ERR_INVALID, "v_codec must be KV_CODEC_I8_SYM or KV_CODEC_I4_ASYM");
+    return KV_OK;
+}
+
+kv_status check_mem(const kv_pool_desc* d, const kv_pool_mem* m, bool need_tail) {
+    if (!m) return fail(KV_ERR_INVALID, "mem is NULL");
+    const void* req[] = {m->k_codes, m->v_codes, m->k_scale, m->v_scale};
+    for (const void* p : req)
+        if (!p || !aligned16(p)) return fail(KV_ERR_INVALID, "pool arrays must be non-NULL and 16-byte aligned");
+    if (d->v_codec == KV_CODEC_I4_ASYM && (!m->v_zp || !aligned16(m->v_zp)))
+        return fail(KV_ERR_INVALID, "v_zp must be non-NULL and 16-byte aligned for INT4 V");
+    if (need_tail && (!m->tail_k || !m->tail_v || !aligned16(m->tail_k) || !aligned16(m->tail_v)))
+        return fail(KV_ERR_INVALID, "tail slots must be non-NULL and 16-byte aligned");
+    return KV_OK;
+}
+
+kv_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return KV_OK;
+    return fail(KV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+}  // namespace
+
+kv_status fail(kv_status st, const std::string& msg) {
+    g_last_error = msg;
+    return st;
+}
+
+}  // namespace pbq
+
+using pbq::fail;
+
+extern "C" {
+
+const char* kv_last_error(void) { return pbq::g_last_error.c_str(); }
+
+kv_status kv_pool_bytes(const kv_pool_desc* d, kv_pool_sizes* out) {
+    if (!out) return fail(KV_ERR_INVALID, "out is NULL");
+    kv_status st = pbq::check_device_desc(d);
+    if (st != KV_OK) return st;
+    const size_t tile = (size_t)d->block_size * d->head_dim;
+    const size_t bh = (size_t)d->num_blocks * d->num_kv_heads;
+    out->k_codes = bh * tile;
+    out->v_codes = d->v_codec == KV_CODEC_I4_ASYM ? bh * tile / 2 : bh * tile;
+    out->k_scale = bh * 2;
+    out->v_scale = bh * 2;
+    out->v_zp = d->v_codec == KV_CODEC_I4_ASYM ? bh : 0;
+    out->tail_k = (size_t)d->max_seqs * d->num_kv_heads * tile * 2;
+    out->tail_v = out->tail_k;
+    return KV_OK;
+}
+
+kv_status kv_copy_blocks(const kv_pool_desc* d, const kv_pool_mem* m,
+                         const kv_copy* copies_dev, int32_t n, void* stream) {
+    kv_status st = pbq::check_device_desc(d);
+    if (st != KV_OK) return st;
+    if ((st = pbq::check_mem(d, m, true)) != KV_OK) return st;
+    if (n < 0) return fail(KV_ERR_INVALID, "n < 0");
+    if (n == 0) return KV_OK;
+    if (!copies_dev) return fail(KV_ERR_INVALID, "copies_dev is NULL");
+    pbq::CopyArgs a{};
+    a.block_size = d->block_size;
+    a.num_kv_heads = d->num_kv_heads;
+    a.head_dim = d->head_dim;
+    a.v_codec = d->v_codec;
+    a.k_codes = (int8_t*)m->k_codes;
+    a.v_codes = (uint8_t*)m->v_codes;
+    a.k_scale = (uint16_t*)m->k_scale;
+    a.v_scale = (uint16_t*)m->v_scale;
+    a.v_zp = (uint8_t*)m->v_zp;
+    a.tail_k = (uint16_t*)m->tail_k;
+    a.tail_v = (uint16_t*)m->tail_v;
+    a.copies = copies_dev;
+    a.n = n;
+    return pbq::hip_status(pbq::launch_copy_blocks(a, (hipStream_t)stream), "kv_copy_blocks launch");
+}
+
+kv_status kv_quantize_store(const kv_pool_desc* d, const kv_pool_mem* m,
+                            const uint16_t* k, const uint16_t* v,
+                            int32_t num_seqs, const int32_t* cu_seqlens,
+                            const int32_t* start_pos, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* tail_slots,
+                            int32_t max_new_tokens, void* stream) {
+    kv_status st = pbq::check_device_desc(d);
+    if (st != KV_OK) return st;
+    if ((st = pbq::check_mem(d, m, true)) != KV_OK) return st;
+    if (num_seqs < 0 || max_new_tokens < 0 || max_blocks_per_seq < 0)
+        return fail(KV_ERR_INVALID, "negative size argument");
+    if (num_seqs == 0 || max_new_tokens == 0) return KV_OK;
+    if (!k || !v || !pbq::aligned16(k) || !pbq::aligned16(v))
+        return fail(KV_ERR_INVALID, "k and v must be non-NULL and 16-byte aligned");
+    if (!cu_seqlens || !start_pos || !block_tables || !tail_slots)
+        return fail(KV_ERR_INVALID, "index arrays must be non-NULL");
+    if (max_blocks_per_seq < 1) return fail(KV_ERR_INVALID, "max_blocks_per_seq must be >= 1");
+    pbq::QuantStoreArgs a{};
+    a.block_size = d->block_size;
+    a.num_kv_heads = d->num_kv_heads;
+    a.head_dim = d->head_dim;
+    a.v_codec = d->v_codec;
+    a.k_codes = (int8_t*)m->k_codes;
+    a.v_codes = (uint8_t*)m->v_codes;
+    a.k_scale = (uint16_t*)m->k_scale;
+    a.v_scale = (uint16_t*)m->v_scale;
+    a.v_zp = (uint8_t*)m->v_zp;
+    a.tail_k = (uint16_t*)m->tail_k;
+    a.tail_v = (uint16_t*)m->tail_v;
+    a.k = k;
+    a.v = v;
+    a.num_seqs = num_seqs;
+    a.cu_seqlens = cu_seqlens;
+    a.start_pos = start_pos;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.tail_slots = tail_slots;
+    // a run of n tokens starting anywhere inside a block spans at most
+    // ceil((bs - 1 + n) / bs) blocks
+    a.tiles_per_seq = pbq::ceil_div((int64_t)d->block_size - 1 + max_new_tokens, d->block_size);
+    if ((int64_t)a.tiles_per_seq * num_seqs * d->num_kv_heads > (int64_t)INT32_MAX * 4)
+        return fail(KV_ERR_INVALID, "store too large for one launch");
+    return pbq::hip_status(pbq::launch_quantize_store(a, (hipStream_t)stream), "kv_quantize_store launch");
+}
+
+int32_t paged_attn_default_partition(const kv_pool_desc* d, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t max_context_len) {
+    if (!d || d->block_size < 1) return 0;
+    (void)num_seqs;
+    (void)num_q_heads;
+    (void)max_context_len;
+    return 512;  // a multiple of 16 and 32
+}
+
+size_t paged_attn_workspace_bytes(const kv_pool_desc* d, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_context_len,
+                                  int32_t partition_size) {
+    if (!d || num_seqs <= 0 || num_q_heads <= 0 || max_context_len < 0 || d->head_dim <= 0)
+        return 0;
+    int32_t part = partition_size > 0 ? partition_size
+                                      : paged_attn_default_partition(d, num_seqs, num_q_heads, max_context_len);
+    if (part <= 0) return 0;
+    int32_t max_parts = max_context_len > 0 ? pbq::ceil_div(max_context_len, part) : 1;
+    if (max_parts <= 1) return 0;
+    size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
+    return rows * (size_t)d->head_dim * 4 + rows * 8;
+}
+
+kv_status paged_attn_decode(const kv_pool_desc* d, const kv_pool_mem* m,
+                            const uint16_t* q, uint16_t* out, int32_t num_seqs,
+                            int32_t num_q_heads, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t max_context_len, float sm_scale,
+                            int32_t partition_size, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    kv_status st = pbq::check_device_desc(d);
+    if (st != KV_OK) return st;
+    if ((st = pbq::check_mem(d, m, false)) != KV_OK) return st;
+    if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0)
+        return fail(KV_ERR_INVALID, "negative size argument");
+    if (num_q_heads < 1 || num_q_heads % d->num_kv_heads != 0)
+        return fail(KV_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
+    if (num_q_heads / d->num_kv_heads > 16 && (num_q_heads / d->num_kv_heads) % 16 != 0)
+        return fail(KV_ERR_INVALID, "query-group sizes above 16 must be multiples of 16");
+    if (num_seqs == 0) return KV_OK;
+    if (!q || !out || !pbq::aligned16(q) || !pbq::aligned16(out))
+        return fail(KV_ERR_INVALID, "q and out must be non-NULL and 16-byte aligned");
+    if (!block_tables || !context_lens) return fail(KV_ERR_INVALID, "index arrays must be non-NULL");
+    if ((int64_t)max_blocks_per_seq * d->block_size < max_context_len)
+        return fail(KV_ERR_INVALID, "max_blocks_per_seq * block_size < max_context_len");
+    if (!std::isfinite(sm_scale))
+        return fail(KV_ERR_INVALID, "sm_scale must be finite");
+    int32_t part = partition_size;
+    if (part == 0) part = paged_attn_default_partition(d, num_seqs, num_q_heads, max_context_len);
+    if (part <= 0 || part % d->block_size != 0)
+        return fail(KV_ERR_INVALID, "partition_size must be a positive multiple of block_size (or 0)");
+    const int32_t max_parts = max_context_len > 0 ? pbq::ceil_div(max_context_len, part) : 1;
+    if (max_parts > 65535) return fail(KV_ERR_INVALID, "too many partitions; use a larger partition_size");
+    const size_t need = paged_attn_workspace_bytes(d, num_seqs, num_q_heads, max_context_len, part);
+    if (workspace_bytes < need) return fail(KV_ERR_INVALID, "workspace too small");
+    if (need > 0 && (!workspace || !pbq::aligned16(workspace)))
+        return fail(KV_ERR_INVALID, "workspace must be non-NULL and 16-byte aligned");
+    pbq::AttnArgs a{};
+    a.block_size = d->block_size;
+    a.num_kv_heads = d->num_kv_heads;
+    a.head_dim = d->head_dim;
+    a.v_codec = d->v_codec;
+    a.k_codes = (const int8_t*)m->k_codes;
+    a.v_codes = (const uint8_t*)m->v_codes;
+    a.k_scale = (const uint16_t*)m->k_scale;
+    a.v_scale = (const uint16_t*)m->v_scale;
+    a.v_zp = (const uint8_t*)m->v_zp;
+    a.q = q;
+    a.out = out;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.sm_scale = sm_scale;
+    a.partition_blocks = part / d->block_size;
+    a.max_partitions = max_parts;
+    const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
+    a.ws_out = need ? (float*)workspace : nullptr;
+    a.ws_ml = need ? (float*)((char*)workspace + rows * (size_t)d->head_dim * 4) : nullptr;
+    return pbq::hip_status(pbq::launch_paged_attn(a, (hipStream_t)stream), "paged_attn_decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Internal interface between the C-ABI layer (capi.cpp) and the HIP launchers
+// (*.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/pbq.h"
+
+namespace pbq {
+
+// Records a message for kv_last_error() on this thread and returns st.
+kv_status fail(kv_status st, const std::string& msg);
+
+struct QuantStoreArgs {
+    int32_t block_size, num_kv_heads, head_dim, v_codec;
+    int8_t* k_codes;
+    uint8_t* v_codes;
+    uint16_t* k_scale;
+    uint16_t* v_scale;
+    uint8_t* v_zp;
+    uint16_t* tail_k;
+    uint16_t* tail_v;
+    const uint16_t* k;
+    const uint16_t* v;
+    int32_t num_seqs;
+    const int32_t* cu_seqlens;
+    const int32_t* start_pos;
+    const int32_t* block_tables;
+    int32_t max_blocks_per_seq;
+    const int32_t* tail_slots;
+    int32_t tiles_per_seq;  // upper bound on blocks touched per sequence
+};
+
+struct AttnArgs {
+    int32_t block_size, num_kv_heads, head_dim, v_codec;
+    const int8_t* k_codes;
+    const uint8_t* v_codes;
+    const uint16_t* k_scale;
+    const uint16_t* v_scale;
+    const uint8_t* v_zp;
+    const uint16_t* q;
+    uint16_t* out;
+    int32_t num_seqs, num_q_heads;
+    const int32_t* block_tables;
+    int32_t max_blocks_per_seq;
+    const int32_t* context_lens;
+    float sm_scale;
+    int32_t partition_blocks;  // blocks per split-K partition
+    int32_t max_partitions;    // ceil(max_context_len / partition tokens), >= 1
+    float* ws_out;             // [S, Hq, max_partitions, D]
+    float* ws_ml;              // [S, Hq, max_partitions, 2]  (max, sum) base 2
+};
+
+struct CopyArgs {
+    int32_t block_size, num_kv_heads, head_dim, v_codec;
+    int8_t* k_codes;
+    uint8_t* v_codes;
+    uint16_t* k_scale;
+    uint16_t* v_scale;
+    uint8_t* v_zp;
+    uint16_t* tail_k;
+    uint16_t* tail_v;
+    const kv_copy* copies;
+    int32_t n;
+};
+
+hipError_t launch_quantize_store(const QuantStoreArgs& a, hipStream_t stream);
+hipError_t launch_paged_attn(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
+
+}  // namespace pbq

@@ -1,0 +1,264 @@
+// Host block-pool allocator: free stack, block tables, reference counts,
+// copy-on-write and tail slots.
+//
+// Policy (web pages cited by site and section):
+//  * deepinsea.top "PagedAttention memory management in depth", "paging
+//    mechanism design": a request takes ceil(n / block_size) blocks popped
+//    from the end of the free list after checking that enough are free (the
+//    call fails as a whole otherwise); freeing appends each block back in
+//    table order.
+//  * tbr8.org "PagedAttention + block-wise quantization against mobile OOM",
+//    §5 point 3: blocks are pre-allocated once and carry logical reference
+//    counts, so that releasing a conversation only frees unshared blocks.
+//  * deepinsea.top "Copy-on-Write" and yunthe.com "PagedAttention mechanism":
+//    forked sequences share prefix blocks; only a block about to be modified
+//    is copied, and tokens after a fork go to new blocks.
+//  * Tail slots (the pages are silent on how a partial block grows): each live
+//    sequence owns an fp16 slot with the exact rows of its partially filled
+//    last block, so the block can be re-quantized from exact values; a
+//    sequence takes the lowest free slot.
+// The pool is single-threaded per handle; no call touches device memory.
+
+#include <stdint.h>
+
+#include <algorithm>
+#include <new>
+#include <set>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "pbq_internal.h"
+
+struct SeqState {
+    std::vector<int32_t> table;
+    int32_t num_tokens = 0;
+    int32_t slot = 0;
+};
+
+struct kv_pool {
+    kv_pool_desc desc{};
+    std::vector<int32_t> free_stack;  // popped from the back
+    std::vector<int32_t> refcount;
+    std::unordered_map<int64_t, SeqState> seqs;
+    std::set<int32_t> free_slots;
+};
+
+namespace {
+
+int64_t blocks_for(int64_t n, int64_t bs) { return (n + bs - 1) / bs; }
+
+kv_status check_host_desc(const kv_pool_desc* d) {
+    if (!d) return pbq::fail(KV_ERR_INVALID, "desc is NULL");
+    if (d->num_blocks < 1) return pbq::fail(KV_ERR_INVALID, "num_blocks must be >= 1");
+    if (d->block_size < 1) return pbq::fail(KV_ERR_INVALID, "block_size must be >= 1");
+    if (d->max_seqs < 1) return pbq::fail(KV_ERR_INVALID, "max_seqs must be >= 1");
+    if (d->num_kv_heads < 1 || d->head_dim < 1)
+        return pbq::fail(KV_ERR_INVALID, "num_kv_heads and head_dim must be >= 1");
+    return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kv_status kv_pool_create(const kv_pool_desc* desc, const int32_t* free_order,
+                         kv_pool** out) {
+    if (!out) return pbq::fail(KV_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    kv_status st = check_host_desc(desc);
+    if (st != KV_OK) return st;
+    const int32_t n = desc->num_blocks;
+    std::vector<int32_t> order(n);
+    if (free_order) {
+        std::vector<uint8_t> seen(n, 0);
+        for (int32_t i = 0; i < n; ++i) {
+            int32_t b = free_order[i];
+            if (b < 0 || b >= n || seen[b])
+                return pbq::fail(KV_ERR_INVALID, "free_order is not a permutation of 0..N-1");
+            seen[b] = 1;
+            order[i] = b;
+        }
+    } else {
+        for (int32_t i = 0; i < n; ++i) order[i] = i;
+    }
+    kv_pool* p = new (std::nothrow) kv_pool();
+    if (!p) return pbq::fail(KV_ERR_INVALID, "out of host memory");
+    p->desc = *desc;
+    p->free_stack = std::move(order);
+    p->refcount.assign(n, 0);
+    for (int32_t s = 0; s < desc->max_seqs; ++s) p->free_slots.insert(s);
+    *out = p;
+    return KV_OK;
+}
+
+void kv_pool_destroy(kv_pool* pool) { delete pool; }
+
+kv_status kv_seq_alloc(kv_pool* pool, int64_t seq, int32_t num_tokens) {
+    if (!pool) return pbq::fail(KV_ERR_INVALID, "pool is NULL");
+    if (num_tokens < 0) return pbq::fail(KV_ERR_INVALID, "num_tokens < 0");
+    if (pool->seqs.count(seq)) return pbq::fail(KV_ERR_STATE, "sequence already present");
+    if (pool->free_slots.empty()) return pbq::fail(KV_ERR_NO_SLOTS, "no free tail slot");
+    const int64_t need = blocks_for(num_tokens, pool->desc.block_size);
+    if (need > (int64_t)pool->free_stack.size())
+        return pbq::fail(KV_ERR_NO_BLOCKS, "not enough free blocks");
+    SeqState st;
+    st.table.reserve(need);
+    for (int64_t i = 0; i < need; ++i) {
+        int32_t b = pool->free_stack.back();
+        pool->free_stack.pop_back();
+        pool->refcount[b] = 1;
+        st.table.push_back(b);
+    }
+    st.num_tokens = num_tokens;
+    st.slot = *pool->free_slots.begin();
+    pool->free_slots.erase(pool->free_slots.begin());
+    pool->seqs.emplace(seq, std::move(st));
+    return KV_OK;
+}
+
+kv_status kv_seq_fork(kv_pool* pool, int64_t parent, int64_t child,
+                      kv_copy* copies, int32_t cap, int32_t* n_copies) {
+    if (!pool) return pbq::fail(KV_ERR_INVALID, "pool is NULL");
+    auto it = pool->seqs.find(parent);
+    if (it == pool->seqs.end()) return pbq::fail(KV_ERR_UNKNOWN_SEQ, "unknown parent");
+    if (pool->seqs.count(child)) return pbq::fail(KV_ERR_STATE, "child already present");
+    if (pool->free_slots.empty()) return pbq::fail(KV_ERR_NO_SLOTS, "no free tail slot");
+    const SeqState& p = it->second;
+    const bool partial = p.num_tokens % pool->desc.block_size != 0;
+    if (partial && (cap < 1 || !copies))
+        return pbq::fail(KV_ERR_INVALID, "fork needs room for one copy (cap >= 1)");
+    SeqState c;
+    c.table = p.table;
+    c.num_tokens = p.num_tokens;
+    c.slot = *pool->free_slots.begin();
+    pool->free_slots.erase(pool->free_slots.begin());
+    for (int32_t b : c.table) pool->refcount[b] += 1;
+    int32_t n = 0;
+    if (partial) copies[n++] = kv_copy{KV_COPY_SLOT, p.slot, c.slot};
+    if (n_copies) *n_copies = n;
+    pool->seqs.emplace(child, std::move(c));
+    return KV_OK;
+}
+
+kv_status kv_seq_append(kv_pool* pool, int64_t seq, int32_t n_tokens,
+                        kv_copy* copies, int32_t cap, int32_t* n_copies) {
+    if (!pool) return pbq::fail(KV_ERR_INVALID, "pool is NULL");
+    if (n_tokens < 0) return pbq::fail(KV_ERR_INVALID, "n_tokens < 0");
+    auto it = pool->seqs.find(seq);
+    if (it == pool->seqs.end()) return pbq::fail(KV_ERR_UNKNOWN_SEQ, "unknown sequence");
+    SeqState& st = it->second;
+    const int64_t bs = pool->desc.block_size;
+    const int64_t ntok = st.num_tokens;
+    if (ntok + (int64_t)n_tokens > INT32_MAX)
+        return pbq::fail(KV_ERR_INVALID, "token count overflows int32");
+    const bool cow = n_tokens > 0 && ntok % bs != 0 && pool->refcount[st.table.back()] > 1;
+    // positions p in [ntok, ntok + n) with p % bs == 0
+    const int64_t boundaries = blocks_for(ntok + n_tokens, bs) - blocks_for(ntok, bs);
+    if ((cow ? 1 : 0) + boundaries > (int64_t)pool->free_stack.size())
+        return pbq::fail(KV_ERR_NO_BLOCKS, "not enough free blocks");
+    if (cow && (cap < 1 || !copies))
+        return pbq::fail(KV_ERR_INVALID, "append needs room for one copy (cap >= 1)");
+    int32_t n = 0;
+    if (cow) {
+        int32_t src = st.table.back();
+        int32_t dst = pool->free_stack.back();
+        pool->free_stack.pop_back();
+        pool->refcount[src] -= 1;
+        pool->refcount[dst] = 1;
+        st.table.back() = dst;
+        copies[n++] = kv_copy{KV_COPY_BLOCK, src, dst};
+    }
+    for (int64_t i = 0; i < boundaries; ++i) {
+        int32_t b = pool->free_stack.back();
+        pool->free_stack.pop_back();
+        pool->refcount[b] = 1;
+        st.table.push_back(b);
+    }
+    st.num_tokens = (int32_t)(ntok + n_tokens);
+    if (n_copies) *n_copies = n;
+    return KV_OK;
+}
+
+kv_status kv_seq_free(kv_pool* pool, int64_t seq) {
+    if (!pool) return pbq::fail(KV_ERR_INVALID, "pool is NULL");
+    auto it = pool->seqs.find(seq);
+    if (it == pool->seqs.end()) return pbq::fail(KV_ERR_UNKNOWN_SEQ, "unknown sequence");
+    for (int32_t b : it->second.table) {
+        pool->refcount[b] -= 1;
+        if (pool->refcount[b] == 0) pool->free_stack.push_back(b);
+    }
+    pool->free_slots.insert(it->second.slot);
+    pool->seqs.erase(it);
+    return KV_OK;
+}
+
+kv_status kv_seq_table(const kv_pool* pool, int64_t seq, int32_t* out,
+                       int32_t cap, int32_t* n_blocks, int32_t* n_tokens,
+                       int32_t* slot) {
+    if (!pool) return pbq::fail(KV_ERR_INVALID, "pool is NULL");
+    auto it = pool->seqs.find(seq);
+    if (it == pool->seqs.end()) return pbq::fail(KV_ERR_UNKNOWN_SEQ, "unknown sequence");
+    const SeqState& st = it->second;
+    const int32_t nb = (int32_t)st.table.size();
+    if (out) {
+        if (cap < nb) return pbq::fail(KV_ERR_INVALID, "cap smaller than the table");
+        std::copy(st.table.begin(), st.table.end(), out);
+    }
+    if (n_blocks) *n_blocks = nb;
+    if (n_tokens) *n_tokens = st.num_tokens;
+    if (slot) *slot = st.slot;
+    return KV_OK;
+}
+
+kv_status kv_batch_tables(const kv_pool* pool, const int64_t* seqs, int32_t n,
+                          int32_t* tables, int32_t max_blocks,
+                          int32_t* ctx_lens, int32_t* slots) {
+    if (!pool) return pbq::fail(KV_ERR_INVALID, "pool is NULL");
+    if (n < 0 || max_blocks < 0 || (n > 0 && (!seqs || !tables)))
+        return pbq::fail(KV_ERR_INVALID, "bad batch arguments");
+    for (int32_t i = 0; i < n; ++i) {  // validate first: no partial output
+        auto it = pool->seqs.find(seqs[i]);
+        if (it == pool->seqs.end()) return pbq::fail(KV_ERR_UNKNOWN_SEQ, "unknown sequence");
+        if ((int64_t)it->second.table.size() > max_blocks)
+            return pbq::fail(KV_ERR_INVALID, "a table needs more than max_blocks entries");
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        const SeqState& st = pool->seqs.find(seqs[i])->second;
+        int32_t* row = tables + (int64_t)i * max_blocks;
+        std::fill(row, row + max_blocks, 0);
+        std::copy(st.table.begin(), st.table.end(), row);
+        if (ctx_lens) ctx_lens[i] = st.num_tokens;
+        if (slots) slots[i] = st.slot;
+    }
+    return KV_OK;
+}
+
+kv_status kv_pool_stats(const kv_pool* pool, kv_pool_stats_t* out) {
+    if (!pool || !out) return pbq::fail(KV_ERR_INVALID, "NULL argument");
+    int32_t used = 0, shared = 0;
+    for (int32_t r : pool->refcount) {
+        used += r > 0;
+        shared += r > 1;
+    }
+    out->total = pool->desc.num_blocks;
+    out->free = (int32_t)pool->free_stack.size();
+    out->used = used;
+    out->shared = shared;
+    out->seqs = (int32_t)pool->seqs.size();
+    return KV_OK;
+}
+
+kv_status kv_pool_free_list(const kv_pool* pool, int32_t* out, int32_t cap,
+                            int32_t* n) {
+    if (!pool) return pbq::fail(KV_ERR_INVALID, "pool is NULL");
+    const int32_t sz = (int32_t)pool->free_stack.size();
+    if (out) {
+        if (cap < sz) return pbq::fail(KV_ERR_INVALID, "cap smaller than the free list");
+        std::copy(pool->free_stack.begin(), pool->free_stack.end(), out);
+    }
+    if (n) *n = sz;
+    return KV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,243 @@
+// Quantize-and-store kernel: fp16 K/V tokens -> per-(block, head) quantized
+// tiles in scattered pool blocks.
+//
+// What it computes (web pages cited by site and section):
+//  * tbr8.org "PagedAttention + block-wise quantization against mobile OOM",
+//    §3: every block is quantized on its own; §4 store_kv: K codes are int8
+//    with an fp16 scale of absmax / 127, one per (block, head) as the scale
+//    tensor [num_blocks, num_heads, 1, 1] has it.
+//  * yunthe.com "KV-cache quantization and PagedAttention", "quantization
+//    principle": Q(x) = clamp(round(x / scale + zero_point), 0, 2^bits - 1),
+//    used here for the INT4 V codec (bits = 4) and, with zero point 128 and a
+//    signed store, for INT8.
+//  Readings: rounding is to nearest with ties to even on the exact quotient;
+//  the statistics cover only the rows a block holds; the INT4 range is
+//  widened to contain 0 and its zero point is an integer; rows not yet held
+//  are zero bytes; a partially filled block is re-quantized from the exact
+//  fp16 rows kept in its sequence's tail slot.
+//
+// Mapping: one wavefront per (sequence, touched block, KV head); a workgroup
+// of four waves takes four consecutive heads of one block, so each token row
+// is read as 4 x D x 2 contiguous bytes.  Lane l holds rows
+// it * (64 / (D/8)) + l / (D/8) and dims (l % (D/8)) * 8 .. + 8, read and
+// written with 16-byte (fp16 in) and 8- or 4-byte (codes out) accesses that
+// are contiguous across the wave.
+//
+// Exact codes without a per-element division: n = rint(x * (1/s)) is within
+// one of the answer; the remainder x - n*s is exact in one FMA (x and s are
+// fp16 values, |n| <= 255), and comparing |rem| with s/2 (also exact) decides
+// the nearest integer and the tie, so the result equals round-half-even of
+// the exact quotient, which is what a correctly rounded fp32 division
+// followed by rint gives for fp16 operands.
+
+#include "device_common.h"
+#include "pbq_internal.h"
+
+namespace pbq {
+namespace {
+
+// Round-half-even of x / s + zp for s > 0, x and s fp16 values held in fp32.
+__device__ __forceinline__ int rne_quot(float x, float s, float rcp, float half_s, int zp) {
+    const float n = __builtin_rintf(x * rcp);
+    const float rem = __builtin_fmaf(-n, s, x);  // exact
+    const float arem = __builtin_fabsf(rem);
+    const int dir = rem > 0.f ? 1 : -1;
+    int q = (int)n + zp;
+    q += arem > half_s ? dir : 0;                     // n was one off
+    q += (arem == half_s && (q & 1)) ? dir : 0;       // exact tie -> even
+    return q;
+}
+
+template <int BS, int D, bool V4>
+__global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
+    constexpr int LPR = D / 8;     // lanes per token row
+    constexpr int RPI = 64 / LPR;  // rows per wave access
+    constexpr int NIT = BS / RPI;  // accesses per lane per tensor
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int H = a.num_kv_heads;
+    const int g = (int)(wave % H);
+    const int64_t rest = wave / H;
+    const int jj = (int)(rest % a.tiles_per_seq);
+    const int64_t s = rest / a.tiles_per_seq;
+    if (s >= a.num_seqs) return;
+
+    const int c0 = a.cu_seqlens[s];
+    const int n_new = a.cu_seqlens[s + 1] - c0;
+    const int sp = a.start_pos[s];
+    const int end = sp + n_new;
+    const int j = sp / BS + jj;
+    if (n_new <= 0 || j * BS >= end) return;
+    const int row0 = j * BS;
+    const int valid = min(BS, end - row0);
+    const int phys = a.block_tables[s * a.max_blocks_per_seq + j];
+    const int slot = a.tail_slots[s];
+    const int r_in = lane / LPR;
+    const int col = (lane % LPR) * 8;
+
+    const int64_t tail_base = ((int64_t)slot * H + g) * BS * D;
+    f16x8 kx[NIT], vx[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int r = it * RPI + r_in;
+        const int p = row0 + r;
+        kx[it] = (f16x8)(_Float16)0;
+        vx[it] = (f16x8)(_Float16)0;
+        if (r < valid) {
+            const uint16_t *ks, *vs;
+            if (p < sp) {
+                ks = a.tail_k + tail_base + r * D + col;
+                vs = a.tail_v + tail_base + r * D + col;
+            } else {
+                const int64_t row = (int64_t)(c0 + p - sp) * H + g;
+                ks = a.k + row * D + col;
+                vs = a.v + row * D + col;
+            }
+            kx[it] = *(const f16x8*)ks;
+            vx[it] = *(const f16x8*)vs;
+        }
+    }
+
+    const int64_t tile = (int64_t)phys * H + g;
+
+    // ---- K: INT8 symmetric -------------------------------------------------
+    {
+        uint32_t amax = 0;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const uint32_t b = absmax_bits_f16x8(kx[it]);
+            amax = amax > b ? amax : b;
+        }
+        amax = wave_max_u32(amax);
+        const float absmax = bits_to_f16f((uint16_t)amax);
+        const uint16_t s16 = f32_to_f16_bits(absmax / 127.0f);
+        const float sc = bits_to_f16f(s16);
+        const float rcp = sc > 0.f ? 1.0f / sc : 0.f;
+        const float half_s = 0.5f * sc;
+        int8_t* dst = a.k_codes + tile * (BS * D);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            uint32_t w[2] = {0u, 0u};
+            if (sc > 0.f) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    int q = rne_quot((float)kx[it][e], sc, rcp, half_s, 0);
+                    q = q > 127 ? 127 : (q < -127 ? -127 : q);
+                    w[e >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (e & 3));
+                }
+            }
+            const int r = it * RPI + r_in;
+            *(u32x2*)(dst + r * D + col) = u32x2{w[0], w[1]};
+        }
+        if (lane == 0) a.k_scale[tile] = s16;
+    }
+
+    // ---- V: INT8 symmetric or INT4 asymmetric -------------------------------
+    if constexpr (!V4) {
+        uint32_t amax = 0;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const uint32_t b = absmax_bits_f16x8(vx[it]);
+            amax = amax > b ? amax : b;
+        }
+        amax = wave_max_u32(amax);
+        const float absmax = bits_to_f16f((uint16_t)amax);
+        const uint16_t s16 = f32_to_f16_bits(absmax / 127.0f);
+        const float sc = bits_to_f16f(s16);
+        const float rcp = sc > 0.f ? 1.0f / sc : 0.f;
+        const float half_s = 0.5f * sc;
+        uint8_t* dst = a.v_codes + tile * (BS * D);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            uint32_t w[2] = {0u, 0u};
+            if (sc > 0.f) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    int q = rne_quot((float)vx[it][e], sc, rcp, half_s, 0);
+                    q = q > 127 ? 127 : (q < -127 ? -127 : q);
+                    w[e >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (e & 3));
+                }
+            }
+            const int r = it * RPI + r_in;
+            *(u32x2*)(dst + r * D + col) = u32x2{w[0], w[1]};
+        }
+        if (lane == 0) a.v_scale[tile] = s16;
+    } else {
+        float lo = 0.f, hi = 0.f;  // range widened to contain 0
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = (float)vx[it][e];
+                lo = fminf(lo, x);
+                hi = fmaxf(hi, x);
+            }
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        const uint16_t s16 = f32_to_f16_bits((hi - lo) / 15.0f);
+        const float sc = bits_to_f16f(s16);
+        int zp = 0;
+        if (sc > 0.f) {
+            const float z = __builtin_rintf(-lo / sc);
+            zp = z > 15.f ? 15 : (z < 0.f ? 0 : (int)z);
+        }
+        const float rcp = sc > 0.f ? 1.0f / sc : 0.f;
+        const float half_s = 0.5f * sc;
+        uint8_t* dst = a.v_codes + tile * (BS * D / 2);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int r = it * RPI + r_in;
+            uint32_t w = 0u;
+            if (sc > 0.f && r < valid) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    int q = rne_quot((float)vx[it][e], sc, rcp, half_s, zp);
+                    q = q > 15 ? 15 : (q < 0 ? 0 : q);
+                    w |= (uint32_t)q << (4 * e);
+                }
+            }
+            *(uint32_t*)(dst + r * (D / 2) + col / 2) = w;
+        }
+        if (lane == 0) {
+            a.v_scale[tile] = s16;
+            a.v_zp[tile] = (uint8_t)zp;
+        }
+    }
+
+    // ---- tail slot: exact rows of a block that stays partial ----------------
+    if (end % BS != 0 && j == (end - 1) / BS) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int r = it * RPI + r_in;
+            if (r < valid && row0 + r >= sp) {
+                *(f16x8*)(a.tail_k + tail_base + r * D + col) = kx[it];
+                *(f16x8*)(a.tail_v + tail_base + r * D + col) = vx[it];
+            }
+        }
+    }
+}
+
+template <int BS, int D, bool V4>
+hipError_t launch_qs(const QuantStoreArgs& a, hipStream_t stream) {
+    const int64_t waves = (int64_t)a.num_seqs * a.tiles_per_seq * a.num_kv_heads;
+    const int64_t blocks = (waves + 3) / 4;
+    hipLaunchKernelGGL((quantize_store_kernel<BS, D, V4>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_store(const QuantStoreArgs& a, hipStream_t stream) {
+    const bool v4 = a.v_codec == KV_CODEC_I4_ASYM;
+#define PBQ_QS(BS, D)                                                          \
+    if (a.block_size == BS && a.head_dim == D)                                 \
+        return v4 ? launch_qs<BS, D, true>(a, stream) : launch_qs<BS, D, false>(a, stream);
+    PBQ_QS(16, 64)
+    PBQ_QS(16, 128)
+    PBQ_QS(32, 64)
+    PBQ_QS(32, 128)
+#undef PBQ_QS
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pbq

@@ -1,0 +1,123 @@
+"""KVPool: one layer's block pool -- the host allocator handle plus the device
+arrays it indexes, allocated as torch CUDA tensors.  Marshalling only: every
+operation is a call into libpbq (include/pbq.h)."""
+
+import torch
+
+from . import _lib as L
+
+
+class KVPool:
+    """Host allocator (``kv_pool_create``) + device arrays sized by
+    ``kv_pool_bytes``.
+
+    v_codec: "i8" (INT8 symmetric V) or "i4" (INT4 asymmetric V).
+    free_order: initial free stack (a permutation of 0..N-1) or None.
+    """
+
+    def __init__(self, num_blocks, block_size, num_kv_heads, head_dim, v_codec="i8",
+                 max_seqs=1, free_order=None, device="cuda"):
+        codec = {"i8": L.KV_CODEC_I8_SYM, "i4": L.KV_CODEC_I4_ASYM}[v_codec]
+        self.desc = L.make_desc(num_blocks, block_size, num_kv_heads, head_dim, codec, max_seqs)
+        self.num_blocks, self.block_size = num_blocks, block_size
+        self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
+        self.v_int4 = v_codec == "i4"
+        self.max_seqs = max_seqs
+        self.handle = L.kv_pool_create(self.desc, free_order)
+        self.sizes = L.kv_pool_bytes(self.desc)
+        self.device = device
+        self.arrays = {}
+        if device is not None:
+            N, H, bs, D = num_blocks, num_kv_heads, block_size, head_dim
+            dev = torch.device(device)
+            self.arrays = {
+                "k_codes": torch.zeros((N, H, bs, D), dtype=torch.int8, device=dev),
+                "v_codes": torch.zeros((N, H, bs, D // 2 if self.v_int4 else D),
+                                       dtype=torch.uint8 if self.v_int4 else torch.int8, device=dev),
+                "k_scale": torch.zeros((N, H), dtype=torch.float16, device=dev),
+                "v_scale": torch.zeros((N, H), dtype=torch.float16, device=dev),
+                "v_zp": torch.zeros((N, H) if self.v_int4 else (1,), dtype=torch.uint8, device=dev),
+                "tail_k": torch.zeros((max_seqs, H, bs, D), dtype=torch.float16, device=dev),
+                "tail_v": torch.zeros((max_seqs, H, bs, D), dtype=torch.float16, device=dev),
+            }
+            for name, t in self.arrays.items():
+                if name == "v_zp" and not self.v_int4:
+                    continue
+                assert t.numel() * t.element_size() == self.sizes[name], name
+            self.mem = L.kv_pool_mem(*[
+                None if (n == "v_zp" and not self.v_int4) else self.arrays[n].data_ptr()
+                for n in ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "tail_k", "tail_v")])
+
+    def __getattr__(self, name):
+        arrays = self.__dict__.get("arrays", {})
+        if name in arrays:
+            return arrays[name]
+        raise AttributeError(name)
+
+    def close(self):
+        if getattr(self, "handle", None) is not None:
+            L.kv_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ---- host allocator ----------------------------------------------------
+    def alloc(self, seq, num_tokens):
+        L.kv_seq_alloc(self.handle, seq, num_tokens)
+        return self.table(seq)[0]
+
+    def fork(self, parent, child):
+        return L.kv_seq_fork(self.handle, parent, child)
+
+    def append(self, seq, n_tokens):
+        return L.kv_seq_append(self.handle, seq, n_tokens)
+
+    def release(self, seq):
+        L.kv_seq_free(self.handle, seq)
+
+    def table(self, seq):
+        return L.kv_seq_table(self.handle, seq)
+
+    def batch_tables(self, seqs, max_blocks):
+        return L.kv_batch_tables(self.handle, seqs, max_blocks)
+
+    def stats(self):
+        return L.kv_pool_stats(self.handle)
+
+    def free_list(self):
+        return L.kv_pool_free_list(self.handle)
+
+    # ---- device calls ------------------------------------------------------
+    def copy_blocks(self, copies, stream=None):
+        """Perform (kind, src, dst) copies returned by fork/append."""
+        if not copies:
+            return
+        t = torch.tensor([list(c) for c in copies], dtype=torch.int32).to(self.device)
+        L.kv_copy_blocks(self.desc, self.mem, t, len(copies), stream)
+        return t  # keep alive until the stream has consumed it
+
+    def quantize_store(self, k, v, cu_seqlens, start_pos, block_tables, tail_slots,
+                       max_new_tokens, stream=None):
+        L.kv_quantize_store(self.desc, self.mem, k, v, cu_seqlens.numel() - 1, cu_seqlens,
+                            start_pos, block_tables, block_tables.shape[1], tail_slots,
+                            max_new_tokens, stream)
+
+    def workspace_bytes(self, num_seqs, num_q_heads, max_context_len, partition_size=0):
+        return L.paged_attn_workspace_bytes(self.desc, num_seqs, num_q_heads, max_context_len,
+                                            partition_size)
+
+    def decode(self, q, out, block_tables, context_lens, max_context_len, sm_scale,
+               partition_size=0, workspace=None, stream=None):
+        S, Hq, _ = q.shape
+        need = self.workspace_bytes(S, Hq, max_context_len, partition_size)
+        if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        L.paged_attn_decode(self.desc, self.mem, q, out, S, Hq, block_tables,
+                            block_tables.shape[1], context_lens, max_context_len, sm_scale,
+                            partition_size, workspace, nbytes, stream)
+        return workspace

@@ -1,0 +1,177 @@
+"""Sets up a decode workload through libpbq and runs decode steps.
+
+Orchestration of library calls only (allocate, fork, store, build tables,
+decode); every step of the computation happens in the HIP kernels.
+
+A decode step for one layer stores the current token of every sequence
+(re-quantizing its block from the tail slot) and then runs the fused
+dequantizing attention over the whole context, current token included.
+"""
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import workloads as W
+from .pool import KVPool
+
+
+def blocks_needed(w: W.Workload, ctx: np.ndarray) -> int:
+    bs = w.block_size
+    per_seq = (ctx + bs - 1) // bs
+    if w.prefix:
+        assert w.prefix % bs == 0, "shared prefix must end on a block boundary"
+        return int(w.prefix // bs + np.sum(per_seq - w.prefix // bs))
+    return int(np.sum(per_seq))
+
+
+@dataclass
+class DecodeSetup:
+    w: W.Workload
+    pool: KVPool
+    ctx: np.ndarray
+    tables: torch.Tensor        # int32 [S, max_blocks] on the device
+    ctx_dev: torch.Tensor       # int32 [S]
+    slots: torch.Tensor         # int32 [S]
+    start_pos: torch.Tensor     # int32 [S] = ctx - 1
+    cu_step: torch.Tensor       # int32 [S+1] = 0..S
+    k_new: torch.Tensor         # fp16 [S, Hkv, D]: the current token
+    v_new: torch.Tensor
+    q: torch.Tensor             # fp16 [S, Hq, D]
+    out: torch.Tensor           # fp16 [S, Hq, D]
+    workspace: torch.Tensor
+    max_ctx: int
+    sm_scale: float
+    partition: int
+
+    def store_current(self, stream=None):
+        self.pool.quantize_store(self.k_new, self.v_new, self.cu_step, self.start_pos,
+                                 self.tables, self.slots, 1, stream)
+
+    def attend(self, stream=None):
+        self.pool.decode(self.q, self.out, self.tables, self.ctx_dev, self.max_ctx,
+                         self.sm_scale, self.partition, self.workspace, stream)
+
+    def step(self, stream=None):
+        self.store_current(stream)
+        self.attend(stream)
+
+
+def _store(pool, k, v, seq_ids, starts, device):
+    """Store rows k/v [T, Hkv, D] (device fp16) for several sequences:
+    sequence seq_ids[i] receives the i-th run of rows at position starts[i]."""
+    lens = [int(x.shape[0]) for x in k]
+    kk = torch.cat(k).contiguous()
+    vv = torch.cat(v).contiguous()
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=device)
+    st = torch.tensor(starts, dtype=torch.int32, device=device)
+    max_blocks = max(len(pool.table(s)[0]) for s in seq_ids)
+    tables, _, slots = pool.batch_tables(seq_ids, max_blocks)
+    pool.quantize_store(kk, vv, cu, st, tables.to(device), slots.to(device), max(lens))
+
+
+def setup_decode(w: W.Workload, device="cuda", chunk_seqs=8, partition=None) -> DecodeSetup:
+    """Build the pool for workload ``w`` holding ctx-1 tokens per sequence,
+    reserve the current token's position, and allocate the step's tensors."""
+    ctx = W.context_lengths(w)
+    S, bs = w.num_seqs, w.block_size
+    N = w.pool_blocks or blocks_needed(w, ctx)
+    pool = KVPool(N, bs, w.num_kv_heads, w.head_dim, w.v_codec, max_seqs=S + 1,
+                  free_order=W.free_order(w, N), device=device)
+    if w.prefix:
+        parent = S
+        pool.alloc(parent, w.prefix)
+        kp, vp = W.kv_tokens(w, "prefix", w.prefix, device)
+        _store(pool, [kp], [vp], [parent], [0], device)
+        for s in range(S):
+            copies = pool.fork(parent, s)
+            assert copies == [], "aligned prefix: no tail copy"
+        pool.release(parent)
+    for c0 in range(0, S, chunk_seqs):
+        ids = list(range(c0, min(S, c0 + chunk_seqs)))
+        ks, vs, starts = [], [], []
+        for s in ids:
+            n_hist = int(ctx[s]) - 1 - w.prefix
+            if w.prefix:
+                copies = pool.append(s, n_hist)
+                assert copies == []
+            else:
+                pool.alloc(s, n_hist)
+            k, v = W.kv_tokens(w, s, int(ctx[s]) - w.prefix, device)
+            ks.append(k[:n_hist])
+            vs.append(v[:n_hist])
+            starts.append(w.prefix)
+        if any(x.shape[0] for x in ks):
+            _store(pool, ks, vs, ids, starts, device)
+    # reserve the current token; copies (COW) would precede its store
+    k_new, v_new = [], []
+    for s in range(S):
+        copies = pool.append(s, 1)
+        if copies:
+            pool.copy_blocks(copies)
+        k, v = W.kv_tokens(w, s, int(ctx[s]) - w.prefix, device)
+        k_new.append(k[-1:])
+        v_new.append(v[-1:])
+    max_blocks = int(np.max((ctx + bs - 1) // bs))
+    tables, ctx_h, slots = pool.batch_tables(list(range(S)), max_blocks)
+    assert np.array_equal(ctx_h.numpy(), ctx)
+    part = w.partition if partition is None else partition
+    max_ctx = int(ctx.max())
+    q = W.queries(w, device)
+    out = torch.empty_like(q)
+    ws_bytes = pool.workspace_bytes(S, w.num_q_heads, max_ctx, part)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=device)
+    torch.cuda.synchronize()
+    return DecodeSetup(
+        w=w, pool=pool, ctx=ctx, tables=tables.to(device), ctx_dev=ctx_h.to(device),
+        slots=slots.to(device),
+        start_pos=torch.tensor(ctx - 1, dtype=torch.int32, device=device),
+        cu_step=torch.arange(S + 1, dtype=torch.int32, device=device),
+        k_new=torch.cat(k_new).contiguous(), v_new=torch.cat(v_new).contiguous(),
+        q=q, out=out, workspace=workspace, max_ctx=max_ctx,
+        sm_scale=1.0 / float(np.sqrt(w.head_dim)), partition=part)
+
+
+def sequence_history(setup: DecodeSetup, s: int, device="cuda"):
+    """fp16 K/V of every token of sequence s (host numpy [ctx, Hkv, D]),
+    regenerated from the seeded streams."""
+    w = setup.w
+    k, v = W.kv_tokens(w, s, int(setup.ctx[s]) - w.prefix, device)
+    if w.prefix:
+        kp, vp = W.kv_tokens(w, "prefix", w.prefix, device)
+        k, v = torch.cat([kp, k]), torch.cat([vp, v])
+    return k.cpu().numpy(), v.cpu().numpy()
+
+
+def decode_bytes(w: W.Workload, ctx: np.ndarray) -> int:
+    """Algorithmic HBM bytes of one decode attention pass: the codes of every
+    valid token, the metadata of every block read, Q, O, the block tables and
+    the context lengths; a shared prefix counted once."""
+    S, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    vbits = 4 if w.v_codec == "i4" else 8
+    meta = 2 + 2 + (1 if w.v_codec == "i4" else 0)
+    tokens = int(np.sum(ctx))
+    blocks = int(np.sum((ctx + bs - 1) // bs))
+    if w.prefix:
+        tokens -= (S - 1) * w.prefix
+        blocks -= (S - 1) * (w.prefix // bs)
+    codes = tokens * Hkv * D * (8 + vbits) // 8
+    meta_b = blocks * Hkv * meta
+    qo = 2 * S * Hq * D * 2
+    tables = int(np.sum((ctx + bs - 1) // bs)) * 4 + S * 4
+    return codes + meta_b + qo + tables
+
+
+def store_step_bytes(w: W.Workload, ctx: np.ndarray) -> int:
+    """Algorithmic bytes of storing the current token: the block's exact rows
+    read (tail slot + new row, fp16 K and V), its codes and metadata written,
+    and the per-sequence index arrays."""
+    Hkv, D, bs = w.num_kv_heads, w.head_dim, w.block_size
+    vbits = 4 if w.v_codec == "i4" else 8
+    meta = 2 + 2 + (1 if w.v_codec == "i4" else 0)
+    rows = (ctx - 1) % bs + 1                    # rows the block holds after the store
+    read = int(np.sum(rows)) * Hkv * D * 2 * 2
+    write = len(ctx) * Hkv * (bs * D * (8 + vbits) // 8 + meta)
+    tail_write = int(np.sum(rows < bs)) * Hkv * D * 2 * 2
+    return read + write + tail_write + len(ctx) * 4 * 4

@@ -1,0 +1,109 @@
+"""Helpers for the GPU parity tests: run a small case through the HIP path
+(libpbq via the binding) and through the oracle on the same inputs."""
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import allocator as A
+from oracle import attention, paged
+
+ATOL, RTOL = 2e-3, 1e-2   # |gpu - ref| <= ATOL + RTOL * |ref|, fp32 accumulate
+
+
+def announce(*what):
+    print("CASE", *what, flush=True)
+    sys.stdout.flush()
+
+
+def assert_close(gpu, ref, what=""):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
+    err = np.abs(gpu - ref)
+    bound = ATOL + RTOL * np.abs(ref)
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; "
+                           f"max abs err {err.max():.3e}")
+    return float(err.max())
+
+
+def pool_numpy(pool):
+    out = {n: pool.arrays[n].cpu().numpy() for n in ("k_codes", "v_codes", "k_scale", "v_scale")}
+    out["v_zp"] = pool.arrays["v_zp"].cpu().numpy() if pool.v_int4 else None
+    return out
+
+
+def assert_pool_equal(gpu_pool, opool, blocks=None):
+    """Bit-exact comparison of codes, fp16 scale bits and zero points."""
+    g = pool_numpy(gpu_pool)
+    sel = slice(None) if blocks is None else np.asarray(blocks)
+    assert np.array_equal(g["k_codes"][sel], opool.k_codes[sel]), "K codes differ"
+    assert np.array_equal(g["v_codes"][sel].view(np.uint8), opool.v_codes[sel].view(np.uint8)), "V codes differ"
+    assert np.array_equal(g["k_scale"][sel].view(np.uint16), opool.k_scale[sel].view(np.uint16)), "K scales differ"
+    assert np.array_equal(g["v_scale"][sel].view(np.uint16), opool.v_scale[sel].view(np.uint16)), "V scales differ"
+    if gpu_pool.v_int4:
+        assert np.array_equal(g["v_zp"][sel], opool.v_zp[sel]), "V zero points differ"
+
+
+class SmallCase:
+    """A batch of sequences with explicit fp16 histories, stored by one
+    prefill call and decoded, on the GPU and in the oracle."""
+
+    def __init__(self, hist_k, hist_v, q, hq, hkv, d, bs, v_codec, n_blocks, free_order,
+                 device="cuda"):
+        from paged_block_quantized_amd import KVPool
+        self.S = len(hist_k)
+        self.ctx = [int(k.shape[0]) for k in hist_k]
+        self.hist_k, self.hist_v, self.q = hist_k, hist_v, q
+        self.hq, self.hkv, self.d, self.bs = hq, hkv, d, bs
+        self.v_int4 = v_codec == "i4"
+        self.device = device
+        self.pool = KVPool(n_blocks, bs, hkv, d, v_codec, max_seqs=self.S,
+                           free_order=free_order, device=device)
+        self.model = A.BlockPoolModel(n_blocks, bs, self.S, free_order)
+        self.opool = paged.PoolArrays(n_blocks, hkv, bs, d, self.v_int4)
+        for s, c in enumerate(self.ctx):
+            t_gpu = self.pool.alloc(s, c)
+            t_ref = self.model.alloc(s, c)
+            assert t_gpu == t_ref
+        self.max_blocks = max(1, max((c + bs - 1) // bs for c in self.ctx))
+        tables, ctx_h, slots = self.pool.batch_tables(list(range(self.S)), self.max_blocks)
+        self.tables = tables.to(device)
+        self.ctx_dev = ctx_h.to(device)
+        self.slots = slots.to(device)
+
+    def store_all(self):
+        lens = self.ctx
+        k = torch.from_numpy(np.concatenate(self.hist_k)).to(self.device)
+        v = torch.from_numpy(np.concatenate(self.hist_v)).to(self.device)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=self.device)
+        st = torch.zeros(self.S, dtype=torch.int32, device=self.device)
+        self.pool.quantize_store(k, v, cu, st, self.tables, self.slots, max(max(lens), 1))
+        for s, c in enumerate(lens):
+            paged.store_range(self.opool, self.model.table(s)[0], self.hist_k[s], self.hist_v[s], 0, c)
+
+    def decode(self, partition=0, sm_scale=None):
+        sm = 1.0 / np.sqrt(self.d) if sm_scale is None else sm_scale
+        qd = torch.from_numpy(self.q).to(self.device)
+        out = torch.empty_like(qd)
+        self.pool.decode(qd, out, self.tables, self.ctx_dev, max(max(self.ctx), 0), sm, partition)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def reference(self, sm_scale=None):
+        sm = 1.0 / np.sqrt(self.d) if sm_scale is None else sm_scale
+        tables = [self.model.table(s)[0] for s in range(self.S)]
+        return attention.paged_decode(self.opool, tables, self.ctx, self.q, sm)
+
+
+def normal_case(ctx, hq, hkv, d, bs, v_codec, seed, extra_blocks=3, perm=True):
+    rng = np.random.default_rng(seed)
+    hk = [rng.standard_normal((c, hkv, d)).astype(np.float16) for c in ctx]
+    hv = [rng.standard_normal((c, hkv, d)).astype(np.float16) for c in ctx]
+    q = rng.standard_normal((len(ctx), hq, d)).astype(np.float16)
+    n_blocks = sum((c + bs - 1) // bs for c in ctx) + extra_blocks
+    order = rng.permutation(n_blocks) if perm else None
+    return SmallCase(hk, hv, q, hq, hkv, d, bs, v_codec, n_blocks, order)

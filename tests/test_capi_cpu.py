@@ -1,0 +1,171 @@
+"""CPU tests of libpbq's C ABI: the library loads and exports every entry
+point include/pbq.h declares; its host allocator matches the oracle's model
+bit for bit; sizing and argument validation behave as documented.  No device
+computation is launched here."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as hst
+
+from oracle import allocator as A
+from oracle import kv_size
+
+from alloc_harness import apply_op, random_ops, run_golden_trace
+
+pbq = pytest.importorskip("paged_block_quantized_amd")
+from paged_block_quantized_amd import _lib as L  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "pbq.h")).read()
+    return re.findall(r"^(?:kv_status|void|size_t|int32_t|const char\*)\s+(\w+)\(", text, re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libpbq.so is not built (run python -m paged_block_quantized_amd.build)")
+    return L.lib()
+
+
+def test_exports_every_header_symbol(lib):
+    names = _header_functions()
+    assert len(names) >= 17
+    assert sorted(names) == sorted(L.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+class CAdapter:
+    """The C allocator behind the same interface as the oracle model."""
+
+    def __init__(self, n, bs, max_seqs, free_order):
+        desc = L.make_desc(n, bs, 1, 1, max_seqs=max_seqs)
+        self.h = L.kv_pool_create(desc, free_order)
+
+    def alloc(self, s, n):
+        L.kv_seq_alloc(self.h, s, n)
+        return L.kv_seq_table(self.h, s)[0]
+
+    def fork(self, p, c):
+        return L.kv_seq_fork(self.h, p, c)
+
+    def append(self, s, n):
+        return L.kv_seq_append(self.h, s, n)
+
+    def release(self, s):
+        return L.kv_seq_free(self.h, s)
+
+    def table(self, s):
+        return L.kv_seq_table(self.h, s)
+
+    def stats(self):
+        return L.kv_pool_stats(self.h)
+
+    def free_list(self):
+        return L.kv_pool_free_list(self.h)
+
+    def __del__(self):
+        L.kv_pool_destroy(self.h)
+
+
+def test_golden_trace_c(lib):
+    run_golden_trace(CAdapter, L.PBQError)
+
+
+@settings(max_examples=80, deadline=None)
+@given(seed=hst.integers(0, 2 ** 31 - 1), n_blocks=hst.integers(1, 24),
+       bs=hst.sampled_from([1, 2, 4, 16, 32]))
+def test_c_allocator_matches_model(lib, seed, n_blocks, bs):
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(n_blocks)
+    model = A.BlockPoolModel(n_blocks, bs, 6, perm)
+    c = CAdapter(n_blocks, bs, 6, perm)
+    for op in random_ops(rng, 120):
+        a = apply_op(model, op, A.AllocError)
+        b = apply_op(c, op, L.PBQError)
+        assert a == b, op
+        assert model.free == c.free_list()
+        assert model.stats() == c.stats()
+    for sid, st in model.seqs.items():
+        assert (st.table, st.num_tokens, st.slot) == tuple(c.table(sid))
+
+
+def test_batch_tables(lib):
+    c = CAdapter(16, 4, 4, None)
+    c.alloc(7, 9)
+    c.alloc(3, 1)
+    t, ctx, slots = L.kv_batch_tables(c.h, [3, 7], 5)
+    assert t.tolist() == [c.table(3)[0] + [0] * 4, c.table(7)[0] + [0] * 2]
+    assert ctx.tolist() == [1, 9] and slots.tolist() == [1, 0]
+    with pytest.raises(L.PBQError):
+        L.kv_batch_tables(c.h, [7], 2)
+    with pytest.raises(L.PBQError) as e:
+        L.kv_batch_tables(c.h, [8], 5)
+    assert e.value.kind == "unknown_seq"
+
+
+def test_pool_bytes_match_closed_form(lib):
+    for bs, D, H, v4, N in [(16, 128, 32, False, 8192), (32, 128, 8, True, 1000), (16, 64, 2, False, 64)]:
+        desc = L.make_desc(N, bs, H, D, L.KV_CODEC_I4_ASYM if v4 else L.KV_CODEC_I8_SYM, 3)
+        sz = L.kv_pool_bytes(desc)
+        per_block = sum(sz[n] for n in ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp")) // N
+        assert per_block == kv_size.pool_block_bytes(H, D, bs, 8, 4 if v4 else 8, v4)
+        assert sz["tail_k"] == sz["tail_v"] == 3 * H * bs * D * 2
+
+
+def test_create_rejects_bad_arguments(lib):
+    with pytest.raises(L.PBQError) as e:
+        L.kv_pool_create(L.make_desc(4, 16, 1, 64), [0, 1, 1, 2])
+    assert e.value.kind == "invalid"
+    with pytest.raises(L.PBQError):
+        L.kv_pool_create(L.make_desc(0, 16, 1, 64))
+    with pytest.raises(L.PBQError):
+        L.kv_pool_bytes(L.make_desc(4, 8, 1, 64))      # block_size 8 has no kernel
+    with pytest.raises(L.PBQError):
+        L.kv_pool_bytes(L.make_desc(4, 16, 1, 96))     # head_dim 96 has no kernel
+    with pytest.raises(L.PBQError):
+        L.kv_pool_bytes(L.make_desc(4, 16, 1, 64, v_codec=7))
+
+
+def test_device_calls_validate_before_launch(lib):
+    """Invalid arguments are rejected on the host; nothing reaches HIP."""
+    desc = L.make_desc(8, 16, 2, 64)
+    buf = ctypes.create_string_buffer(1 << 16)
+    base = (ctypes.addressof(buf) + 15) & ~15
+    mem = L.kv_pool_mem(base, base, base, base, None, base, base)
+    with pytest.raises(L.PBQError, match="multiple of num_kv_heads"):
+        L.paged_attn_decode(desc, mem, base, base, 1, 3, base, 4, base, 64, 0.1, 0, None, 0, 0)
+    with pytest.raises(L.PBQError, match="partition_size"):
+        L.paged_attn_decode(desc, mem, base, base, 1, 2, base, 4, base, 64, 0.1, 24, None, 0, 0)
+    with pytest.raises(L.PBQError, match="max_blocks_per_seq"):
+        L.paged_attn_decode(desc, mem, base, base, 1, 2, base, 2, base, 64, 0.1, 0, None, 0, 0)
+    with pytest.raises(L.PBQError, match="workspace"):
+        L.paged_attn_decode(desc, mem, base, base, 1, 2, base, 64, base, 1024, 0.1, 16, None, 0, 0)
+    with pytest.raises(L.PBQError, match="aligned"):
+        L.paged_attn_decode(desc, mem, base + 2, base, 1, 2, base, 4, base, 64, 0.1, 0, None, 0, 0)
+    with pytest.raises(L.PBQError, match="finite"):
+        L.paged_attn_decode(desc, mem, base, base, 1, 2, base, 4, base, 64, float("nan"), 0, None, 0, 0)
+    bad = L.kv_pool_mem(base + 1, base, base, base, None, base, base)
+    with pytest.raises(L.PBQError, match="aligned"):
+        L.kv_quantize_store(desc, bad, base, base, 1, base, base, base, 4, base, 1, 0)
+    desc4 = L.make_desc(8, 16, 2, 64, L.KV_CODEC_I4_ASYM)
+    with pytest.raises(L.PBQError, match="v_zp"):
+        L.kv_copy_blocks(desc4, mem, base, 1, 0)
+    # zero-sized work is a no-op that succeeds without touching the device
+    L.kv_quantize_store(desc, mem, base, base, 0, base, base, base, 4, base, 0, 0)
+    L.kv_copy_blocks(desc, mem, None, 0, 0)
+
+
+def test_workspace_bytes(lib):
+    desc = L.make_desc(8192, 16, 32, 128)
+    # 32 seqs x 32 heads x 8 partitions x (128 floats + max + sum)
+    assert L.paged_attn_workspace_bytes(desc, 32, 32, 4096, 512) == 32 * 32 * 8 * (128 * 4 + 8)
+    assert L.paged_attn_workspace_bytes(desc, 32, 32, 512, 512) == 0
+    assert L.paged_attn_default_partition(desc, 32, 32, 4096) % 32 == 0

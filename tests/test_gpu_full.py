@@ -1,0 +1,148 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times: sampled sequences are checked against the oracle (codes and
+scales bit-exact through the block tables, attention within tolerance), and
+the rest through properties that hold at any size."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, paged
+
+from gpu_util import announce, assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _gathered_pool(setup, s):
+    """This sequence's blocks as stored on the GPU, in logical order."""
+    pool = setup.pool
+    nb = (int(setup.ctx[s]) + pool.block_size - 1) // pool.block_size
+    table = setup.tables[s, :nb].long()
+    g = paged.PoolArrays(nb, pool.num_kv_heads, pool.block_size, pool.head_dim, pool.v_int4)
+    g.k_codes = pool.k_codes[table].cpu().numpy()
+    g.v_codes = pool.v_codes[table].cpu().numpy()
+    g.k_scale = pool.k_scale[table].cpu().numpy()
+    g.v_scale = pool.v_scale[table].cpu().numpy()
+    if pool.v_int4:
+        g.v_zp = pool.v_zp[table].cpu().numpy()
+    return g
+
+
+def _check_sequence(setup, s, out):
+    from paged_block_quantized_amd import runner
+    w = setup.w
+    ctx = int(setup.ctx[s])
+    hk, hv = runner.sequence_history(setup, s)
+    nb = (ctx + w.block_size - 1) // w.block_size
+    ref_pool = paged.PoolArrays(nb, w.num_kv_heads, w.block_size, w.head_dim, w.v_codec == "i4")
+    paged.store_range(ref_pool, list(range(nb)), hk, hv, 0, ctx)
+    g = _gathered_pool(setup, s)
+    assert np.array_equal(g.k_codes, ref_pool.k_codes), f"seq {s}: K codes"
+    assert np.array_equal(g.v_codes.view(np.uint8), ref_pool.v_codes.view(np.uint8)), f"seq {s}: V codes"
+    assert np.array_equal(g.k_scale.view(np.uint16), ref_pool.k_scale.view(np.uint16)), f"seq {s}: K scales"
+    assert np.array_equal(g.v_scale.view(np.uint16), ref_pool.v_scale.view(np.uint16)), f"seq {s}: V scales"
+    if ref_pool.v_int4:
+        assert np.array_equal(g.v_zp, ref_pool.v_zp), f"seq {s}: zero points"
+    khat, vhat = paged.gather_dequant(ref_pool, list(range(nb)), ctx)
+    q = setup.q[s].cpu().numpy()
+    ref = attention.decode_attention(q, khat, vhat, setup.sm_scale)
+    return assert_close(out[s], ref, f"{w.name} seq {s}")
+
+
+def _run(name, samples):
+    from paged_block_quantized_amd import runner, workloads as W
+    w = W.WORKLOADS[name]
+    announce("full", name, "setup")
+    setup = runner.setup_decode(w)
+    announce("full", name, "step")
+    setup.step()
+    torch.cuda.synchronize()
+    out = setup.out.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    for s in samples:
+        announce("full", name, "oracle seq", s)
+        _check_sequence(setup, s, out)
+    # the step is idempotent: a second step gives bitwise the same output
+    setup.step()
+    torch.cuda.synchronize()
+    assert np.array_equal(setup.out.cpu().numpy().view(np.uint16), out.view(np.uint16))
+    return setup
+
+
+def test_llama7b_full():
+    _run("llama7b", samples=[0, 13, 31])
+
+
+def test_shared_prefix_full():
+    setup = _run("shared_prefix", samples=[0, 31])
+    st = setup.pool.stats()
+    assert st["used"] == 28800 and st["shared"] == 128 and st["free"] == 0
+
+
+def test_prefill_store_full():
+    """64 prompts x 2048 tokens stored in one call into a 16384-block pool in
+    random order; sampled sequences bit-exact; then 64 partially filled
+    blocks grow by one token per step through their fill point."""
+    from paged_block_quantized_amd import KVPool, workloads as W
+    w = W.WORKLOADS["prefill_store"]
+    announce("full prefill_store")
+    S, T, H, D, bs = w.num_seqs, w.ctx[0], w.num_kv_heads, w.head_dim, w.block_size
+    pool = KVPool(w.pool_blocks, bs, H, D, "i8", max_seqs=S,
+                  free_order=W.free_order(w, w.pool_blocks))
+    for s in range(S):
+        pool.alloc(s, T)
+    tables, _, slots = pool.batch_tables(list(range(S)), T // bs)
+    tables, slots = tables.cuda(), slots.cuda()
+    ks, vs = zip(*[W.kv_tokens(w, s, T, "cuda") for s in range(S)])
+    k, v = torch.cat(ks), torch.cat(vs)
+    cu = torch.arange(0, (S + 1) * T, T, dtype=torch.int32, device="cuda")
+    st = torch.zeros(S, dtype=torch.int32, device="cuda")
+    pool.quantize_store(k, v, cu, st, tables, slots, T)
+    torch.cuda.synchronize()
+    for s in (0, 37, 63):
+        announce("full prefill_store oracle seq", s)
+        hk, hv = ks[s].cpu().numpy(), vs[s].cpu().numpy()
+        nb = T // bs
+        ref = paged.PoolArrays(nb, H, bs, D, False)
+        paged.store_range(ref, list(range(nb)), hk, hv, 0, T)
+        t = tables[s].long()
+        assert np.array_equal(pool.k_codes[t].cpu().numpy(), ref.k_codes)
+        assert np.array_equal(pool.v_codes[t].cpu().numpy(), ref.v_codes)
+        assert np.array_equal(pool.k_scale[t].cpu().numpy().view(np.uint16), ref.k_scale.view(np.uint16))
+        assert np.array_equal(pool.v_scale[t].cpu().numpy().view(np.uint16), ref.v_scale.view(np.uint16))
+    # decode appends: 64 fresh sequences with partial last blocks (1..15 rows)
+    announce("full prefill_store appends")
+    rng = np.random.default_rng([w.seed, 7])
+    fill = rng.integers(1, bs, S)
+    for s in range(S):
+        pool.release(s)
+    for s in range(S):
+        pool.alloc(s, int(fill[s]))
+    hist = [W.kv_tokens(w, 100 + s, int(fill[s]) + 16, "cuda") for s in range(S)]
+    tables, _, slots = pool.batch_tables(list(range(S)), 2)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(fill)]), dtype=torch.int32, device="cuda")
+    pool.quantize_store(torch.cat([h[0][:f] for h, f in zip(hist, fill)]),
+                        torch.cat([h[1][:f] for h, f in zip(hist, fill)]),
+                        cu, torch.zeros(S, dtype=torch.int32, device="cuda"),
+                        tables.cuda(), slots.cuda(), int(fill.max()))
+    for step in range(16):
+        for s in range(S):
+            assert pool.append(s, 1) == []
+        tables, _, slots = pool.batch_tables(list(range(S)), 2)
+        kn = torch.cat([h[0][f + step:f + step + 1] for h, f in zip(hist, fill)])
+        vn = torch.cat([h[1][f + step:f + step + 1] for h, f in zip(hist, fill)])
+        pool.quantize_store(kn, vn, torch.arange(S + 1, dtype=torch.int32, device="cuda"),
+                            torch.tensor(fill + step, dtype=torch.int32, device="cuda"),
+                            tables.cuda(), slots.cuda(), 1)
+    torch.cuda.synchronize()
+    tables, ctx_h, _ = pool.batch_tables(list(range(S)), 2)
+    for s in range(S):
+        n = int(ctx_h[s])
+        hk, hv = hist[s][0].cpu().numpy(), hist[s][1].cpu().numpy()
+        ref = paged.PoolArrays(2, H, bs, D, False)
+        paged.store_range(ref, [0, 1], hk, hv, 0, n)
+        t = tables[s].long()
+        assert np.array_equal(pool.k_codes[t].cpu().numpy(), ref.k_codes), s
+        assert np.array_equal(pool.v_codes[t].cpu().numpy(), ref.v_codes), s
+        assert np.array_equal(pool.v_scale[t].cpu().numpy().view(np.uint16), ref.v_scale.view(np.uint16)), s

@@ -1,0 +1,232 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle on
+small and ragged cases: quantized codes, fp16 scale bits, zero points and
+block tables bit-exact; attention outputs within |d| <= 2e-3 + 1e-2 |ref|."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import allocator as A
+from oracle import attention, paged
+
+from gpu_util import SmallCase, announce, assert_close, assert_pool_equal, normal_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _tiny_inputs():
+    from paged_block_quantized_amd import workloads as W
+    w = W.WORKLOADS["tiny"]
+    ctx = W.context_lengths(w)
+    hk, hv = [], []
+    for s, c in enumerate(ctx):
+        k, v = W.kv_tokens(w, s, int(c), "cpu")
+        hk.append(k.numpy())
+        hv.append(v.numpy())
+    q = W.queries(w, "cpu").numpy()
+    return w, hk, hv, q
+
+
+@pytest.mark.parametrize("partition", [0, 16, 32, 48])
+def test_tiny_workload(partition):
+    announce("tiny", partition)
+    w, hk, hv, q = _tiny_inputs()
+    from paged_block_quantized_amd import workloads as W
+    case = SmallCase(hk, hv, q, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                     w.v_codec, w.pool_blocks, W.free_order(w, w.pool_blocks))
+    case.store_all()
+    assert_pool_equal(case.pool, case.opool)
+    out = case.decode(partition)
+    assert_close(out, case.reference(), "tiny")
+    # ctx = 1: the output is that token's dequantized V row (fp16-rounded)
+    vrow = paged.gather_dequant(case.opool, case.model.table(0)[0], 1)[1][:, 0, :]
+    assert np.array_equal(out[0], vrow.astype(np.float16))
+
+
+SHAPES = [(bs, d, vc) for bs in (16, 32) for d in (64, 128) for vc in ("i8", "i4")]
+
+
+@pytest.mark.parametrize("bs,d,vc", SHAPES)
+def test_shapes_ragged(bs, d, vc):
+    announce("ragged", bs, d, vc)
+    ctx = [1, bs - 1, bs, bs + 1, 3 * bs + 5, 700, 257]
+    case = normal_case(ctx, 3, 3, d, bs, vc, seed=bs * 1000 + d + (vc == "i4"))
+    case.store_all()
+    assert_pool_equal(case.pool, case.opool)
+    ref = case.reference()
+    for part in (0, bs, 4 * bs, 128 if bs == 16 else 256):
+        assert_close(case.decode(part), ref, f"ragged bs{bs} d{d} {vc} part{part}")
+
+
+def test_zero_context_and_zero_blocks():
+    announce("zero")
+    rng = np.random.default_rng(5)
+    d, bs = 128, 16
+    hk = [np.zeros((0, 1, d), np.float16), np.zeros((20, 1, d), np.float16),
+          rng.standard_normal((33, 1, d)).astype(np.float16)]
+    hv = [np.zeros((0, 1, d), np.float16), np.zeros((20, 1, d), np.float16),
+          rng.standard_normal((33, 1, d)).astype(np.float16)]
+    hv[2][16:32] = 0           # an all-zero V block between non-zero ones
+    hk[2][:16] = np.float16(0.5)  # a constant K block
+    q = rng.standard_normal((3, 1, d)).astype(np.float16)
+    for vc in ("i8", "i4"):
+        case = SmallCase(hk, hv, q, 1, 1, d, bs, vc, 8, rng.permutation(8))
+        case.store_all()
+        assert_pool_equal(case.pool, case.opool)
+        out = case.decode(16)
+        assert not out[0].any(), "ctx 0 must give a zero row"
+        assert not out[1].any(), "all-zero K/V must give a zero row"
+        assert_close(out, case.reference(), f"zero {vc}")
+
+
+def test_rounding_ties():
+    """Values that sit exactly on half-way points of the code grid."""
+    announce("ties")
+    d, bs = 64, 16
+    base = np.arange(-64, 64, dtype=np.float64)[:d]
+    rows = []
+    for r in range(bs):
+        x = (base + 0.5) * (1.0 if r % 2 else 0.25)
+        x[0] = 127.0 if r % 3 else -127.0        # absmax -> scale 1 or a round value
+        rows.append(x)
+    k = np.array(rows, np.float16)[:, None, :]
+    v = np.array(rows, np.float16)[::-1][:, None, :].copy()
+    v4 = np.array([[-5.0, 10.0, 2.5, -0.5, 3.5] * 12 + [0.5, 1.5, -4.5, 7.5]] * bs, np.float16)[:, None, :]
+    q = np.ones((2, 1, d), np.float16)
+    for vc, vv in (("i8", v), ("i4", v4)):
+        case = SmallCase([k, k[:7]], [vv, vv[:7]], q, 1, 1, d, bs, vc, 4, None)
+        case.store_all()
+        assert_pool_equal(case.pool, case.opool)
+
+
+def test_permutation_invariance_bitwise():
+    announce("perm-invariance")
+    rng = np.random.default_rng(9)
+    ctx = [300, 45, 1000]
+    hk = [rng.standard_normal((c, 2, 128)).astype(np.float16) for c in ctx]
+    hv = [rng.standard_normal((c, 2, 128)).astype(np.float16) for c in ctx]
+    q = rng.standard_normal((3, 2, 128)).astype(np.float16)
+    outs = []
+    for seed in (1, 2):
+        n = sum((c + 15) // 16 for c in ctx) + 5
+        case = SmallCase(hk, hv, q, 2, 2, 128, 16, "i8", n, np.random.default_rng(seed).permutation(n))
+        case.store_all()
+        outs.append(case.decode(128))
+    assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16))
+
+
+def test_partition_size_invariance():
+    announce("partition-invariance")
+    case = normal_case([2000, 513, 1], 2, 2, 128, 32, "i4", seed=11)
+    case.store_all()
+    outs = [case.decode(p) for p in (32, 256, 512, 1024, 2048)]
+    for o in outs[1:]:
+        assert_close(o, outs[-1], "partition sizes")
+    assert_close(outs[-1], case.reference(), "single partition")
+
+
+def _store_chunk(pool, k, v, s, start, tables, slots):
+    cu = torch.tensor([0, k.shape[0]], dtype=torch.int32, device="cuda")
+    st = torch.tensor([start], dtype=torch.int32, device="cuda")
+    pool.quantize_store(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), cu, st,
+                        tables[s:s + 1], slots[s:s + 1], k.shape[0])
+
+
+@pytest.mark.parametrize("vc", ["i8", "i4"])
+def test_append_requantize_from_tail(vc):
+    """One-token appends re-quantize the partial block from the exact rows in
+    the tail slot; the result equals the oracle's quantization of the rows."""
+    announce("append", vc)
+    from paged_block_quantized_amd import KVPool
+    rng = np.random.default_rng(21)
+    bs, d, h = 16, 128, 2
+    total = 40
+    hk = rng.standard_normal((total, h, d)).astype(np.float16)
+    hv = rng.standard_normal((total, h, d)).astype(np.float16)
+    pool = KVPool(8, bs, h, d, vc, max_seqs=2, free_order=rng.permutation(8))
+    model = A.BlockPoolModel(8, bs, 2, pool.free_list())
+    opool = paged.PoolArrays(8, h, bs, d, vc == "i4")
+    pool.alloc(0, 3)
+    model.alloc(0, 3)
+    tables, _, slots = pool.batch_tables([0], 3)
+    tables, slots = tables.cuda(), slots.cuda()
+    _store_chunk(pool, hk[:3], hv[:3], 0, 0, tables, slots)
+    for p in range(3, total):
+        assert pool.append(0, 1) == model.append(0, 1) == []
+        tables, _, slots = pool.batch_tables([0], 3)
+        tables, slots = tables.cuda(), slots.cuda()
+        _store_chunk(pool, hk[p:p + 1], hv[p:p + 1], 0, p, tables, slots)
+        paged.store_range(opool, model.table(0)[0], hk, hv, 0, p + 1)
+        if p % 7 == 0 or p == total - 1:
+            torch.cuda.synchronize()
+            assert_pool_equal(pool, opool)
+    # tail slot holds the exact rows of the partial last block
+    slot = pool.table(0)[2]
+    n_tail = total % bs
+    tk = pool.tail_k[slot].cpu().numpy()            # [H, bs, D]
+    assert np.array_equal(tk[:, :n_tail].transpose(1, 0, 2).view(np.uint16),
+                          hk[total - n_tail:].view(np.uint16))
+    # append-built blocks equal a prefill of the same rows
+    pre = paged.PoolArrays(8, h, bs, d, vc == "i4")
+    paged.store_range(pre, model.table(0)[0], hk, hv, 0, total)
+    assert_pool_equal(pool, pre)
+
+
+@pytest.mark.parametrize("vc", ["i8", "i4"])
+def test_fork_copy_on_write(vc):
+    """An unaligned shared prefix: fork copies the tail slot; each child's
+    first append copies only the shared partial block; shared prefix blocks
+    are unchanged; outputs equal the oracle's."""
+    announce("fork-cow", vc)
+    from paged_block_quantized_amd import KVPool
+    rng = np.random.default_rng(31)
+    bs, d, h = 32, 128, 2
+    pre, n_children, extra = 72, 2, 50        # 72 = 2.25 blocks
+    hp_k = rng.standard_normal((pre, h, d)).astype(np.float16)
+    hp_v = rng.standard_normal((pre, h, d)).astype(np.float16)
+    N = 16
+    order = rng.permutation(N)
+    pool = KVPool(N, bs, h, d, vc, max_seqs=4, free_order=order)
+    model = A.BlockPoolModel(N, bs, 4, order)
+    opool = paged.PoolArrays(N, h, bs, d, vc == "i4")
+    parent = 9
+    pool.alloc(parent, pre)
+    model.alloc(parent, pre)
+    t, _, sl = pool.batch_tables([parent], 8)
+    _store_chunk(pool, hp_k, hp_v, 0, 0, t.cuda(), sl.cuda())
+    paged.store_range(opool, model.table(parent)[0], hp_k, hp_v, 0, pre)
+    hist = {}
+    for c in range(n_children):
+        cp = pool.fork(parent, c)
+        assert cp == model.fork(parent, c) == [(A.COPY_SLOT, 0, c + 1)]
+        keep = pool.copy_blocks(cp)
+        ck = rng.standard_normal((extra, h, d)).astype(np.float16)
+        cv = rng.standard_normal((extra, h, d)).astype(np.float16)
+        cp = pool.append(c, extra)
+        assert cp == model.append(c, extra)
+        if c == 0:
+            assert len(cp) == 1 and cp[0][0] == A.COPY_BLOCK
+        keep2 = pool.copy_blocks(cp)   # the oracle re-quantizes dst in full below
+        t, _, sl = pool.batch_tables([c], 8)
+        _store_chunk(pool, ck, cv, 0, pre, t.cuda(), sl.cuda())
+        torch.cuda.synchronize()
+        del keep, keep2
+        hk, hv = np.concatenate([hp_k, ck]), np.concatenate([hp_v, cv])
+        paged.store_range(opool, model.table(c)[0], hk, hv, pre, pre + extra)
+        hist[c] = (hk, hv)
+    assert_pool_equal(pool, opool)
+    # decode the parent and both children together
+    seqs = [parent] + list(range(n_children))
+    tables, ctx_h, _ = pool.batch_tables(seqs, 8)
+    q = rng.standard_normal((3, h, d)).astype(np.float16)
+    qd = torch.from_numpy(q).cuda()
+    out = torch.empty_like(qd)
+    pool.decode(qd, out, tables.cuda(), ctx_h.cuda(), int(ctx_h.max()), 1 / np.sqrt(d), 64)
+    ref = attention.paged_decode(opool, [model.table(s)[0] for s in seqs], ctx_h.numpy(), q, 1 / np.sqrt(d))
+    assert_close(out.cpu().numpy(), ref, "fork")
+    # the shared blocks were not modified by the children's stores
+    shared = [b for b in model.table(parent)[0] if model.refcount[b] > 1]
+    assert len(shared) == 2
+    ref_parent = paged.PoolArrays(N, h, bs, d, vc == "i4")
+    paged.store_range(ref_parent, model.table(parent)[0], hp_k, hp_v, 0, pre)
+    assert_pool_equal(pool, ref_parent, blocks=model.table(parent)[0])
