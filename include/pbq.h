@@ -54,13 +54,15 @@ typedef enum kv_status {
 } kv_status;
 
 /* Codecs, one per (block, head) tile of block_size x head_dim values.
+ * INT4 packing is along the tile's contiguous axis: tokens for V (see the
+ * layout under kv_pool_sizes).
  *   KV_CODEC_I8_SYM : int8 codes in [-127, 127], fp16 scale = fp16(absmax/127)
  *                     over the rows the block holds; code = round-half-even
  *                     of the fp32 quotient x / scale, clamped.  This is
  *                     [yunthe] Q(x) with bits = 8 and zero point 128, stored
  *                     as Q - 128; [tbr8] §4 store_kv's absmax/127 scale.
- *   KV_CODEC_I4_ASYM: codes in [0, 15], two per byte along head_dim (even
- *                     dimension in the low nibble); lo = min(0, min x),
+ *   KV_CODEC_I4_ASYM: codes in [0, 15], two per byte (the lower index in the
+ *                     low nibble); lo = min(0, min x),
  *                     hi = max(0, max x), scale = fp16((hi - lo) / 15),
  *                     zero point = clamp(round(-lo / scale), 0, 15) as u8;
  *                     code = clamp(round(x / scale + zero point), 0, 15)
@@ -82,9 +84,12 @@ typedef struct kv_pool_desc {
 } kv_pool_desc;
 
 /* Byte sizes of the device arrays of one pool (all row-major):
- *   k_codes  int8  [N, Hkv, bs, D]
- *   v_codes  int8  [N, Hkv, bs, D]      (I8_SYM)
- *            uint8 [N, Hkv, bs, D / 2]  (I4_ASYM, two codes per byte)
+ *   k_codes  int8  [N, Hkv, bs, D]      token-major K tiles ([tbr8] §4)
+ *   v_codes  int8  [N, Hkv, D, bs]      (I8_SYM) dim-major V tiles
+ *            uint8 [N, Hkv, D, bs / 2]  (I4_ASYM, two consecutive tokens per
+ *                                        byte, the earlier in the low nibble)
+ *            The pages show only the K pool; V is stored dim-major so that a
+ *            sum over a block's tokens reads one contiguous row per dim.
  *   k_scale  fp16  [N, Hkv]
  *   v_scale  fp16  [N, Hkv]
  *   v_zp     uint8 [N, Hkv]  (0 bytes unless I4_ASYM)
@@ -235,8 +240,10 @@ size_t paged_attn_workspace_bytes(const kv_pool_desc* desc, int32_t num_seqs,
  *   q_dev, out_dev fp16 [num_seqs, num_q_heads, D]; out written in full.
  *   context_lens_dev int32 [num_seqs]; 0 gives a zero output row.
  *   max_context_len >= every context length (sizes the grid).
- *   partition_size: tokens per split-K partition, a multiple of block_size,
- *   or 0 to let the library choose.  Partitions are combined by a second
+ *   partition_size: tokens per split-K partition, a multiple of block_size
+ *   (and of 32 when num_q_heads > Hkv), or 0 to let the library choose.
+ *   One query head per KV head runs on the vector ALUs; grouped query heads
+ *   (up to 16 per KV head, or a multiple of 16) run on MFMA.  Partitions are combined by a second
  *   log-sum-exp kernel.  workspace_dev (16-byte aligned, workspace_bytes >=
  *   paged_attn_workspace_bytes(...)) may be NULL when that is 0.
  *   num_q_heads must be a multiple of Hkv. */

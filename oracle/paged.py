@@ -20,8 +20,12 @@ Readings
 * A block is always (re)quantized from the exact fp16 rows it holds, never
   from earlier codes: storing tokens into a partially filled block quantizes
   that block again over all of its rows.  Unfilled rows are zero bytes.
-* V INT4 codes are packed two per byte (see ``quant``), so the V pool is
-  [num_blocks, heads, block_size, head_dim / 2] bytes, with a u8 zero point
+* The pages show only the K pool; the V pool's layout is open.  V tiles are
+  stored dim-major, [head_dim, block_size] per (block, head), so that a sum
+  over a block's tokens reads one contiguous row per dimension: the V pool is
+  [num_blocks, heads, head_dim, block_size] int8, or for INT4
+  [num_blocks, heads, head_dim, block_size / 2] bytes holding two consecutive
+  tokens per byte (the earlier token in the low nibble), with a u8 zero point
   per (block, head).
 """
 
@@ -40,12 +44,11 @@ class PoolArrays:
         self.block_size = block_size
         self.head_dim = head_dim
         self.v_int4 = v_int4
-        shape = (num_blocks, num_kv_heads, block_size, head_dim)
-        self.k_codes = np.zeros(shape, np.int8)
+        self.k_codes = np.zeros((num_blocks, num_kv_heads, block_size, head_dim), np.int8)
         if v_int4:
-            self.v_codes = np.zeros(shape[:-1] + (head_dim // 2,), np.uint8)
+            self.v_codes = np.zeros((num_blocks, num_kv_heads, head_dim, block_size // 2), np.uint8)
         else:
-            self.v_codes = np.zeros(shape, np.int8)
+            self.v_codes = np.zeros((num_blocks, num_kv_heads, head_dim, block_size), np.int8)
         self.k_scale = np.zeros((num_blocks, num_kv_heads), np.float16)
         self.v_scale = np.zeros((num_blocks, num_kv_heads), np.float16)
         self.v_zp = np.zeros((num_blocks, num_kv_heads), np.uint8)
@@ -63,14 +66,18 @@ def store_block(pool: PoolArrays, phys: int, k_rows, v_rows):
         pool.k_codes[phys, h] = 0
         pool.k_codes[phys, h, :n] = kc
         pool.k_scale[phys, h] = ks
-        pool.v_codes[phys, h] = 0
+        # V tile, dim-major: codes[d, t]; tokens >= n stay zero
         if pool.v_int4:
             vc, vs, vz = quant.quantize_int4_asym(v_rows[:, h, :])
-            pool.v_codes[phys, h, :n] = quant.pack_int4(vc)
+            tile = np.zeros((pool.head_dim, pool.block_size), np.uint8)
+            tile[:, :n] = vc.T
+            pool.v_codes[phys, h] = quant.pack_int4(tile)
             pool.v_zp[phys, h] = vz
         else:
             vc, vs = quant.quantize_int8_sym(v_rows[:, h, :])
-            pool.v_codes[phys, h, :n] = vc
+            tile = np.zeros((pool.head_dim, pool.block_size), np.int8)
+            tile[:, :n] = vc.T
+            pool.v_codes[phys, h] = tile
             pool.v_zp[phys, h] = 0
         pool.v_scale[phys, h] = vs
 
@@ -98,11 +105,12 @@ def gather_dequant(pool: PoolArrays, table, ctx: int):
     ks = pool.k_scale[phys, :].astype(np.float64)                # [ctx, H]
     khat = kc * ks[:, :, None]
     if pool.v_int4:
-        vc = quant.unpack_int4(pool.v_codes[phys, :, row, :]).astype(np.float64)
+        tiles = quant.unpack_int4(pool.v_codes[phys])                # [ctx, H, D, bs]
+        vc = tiles[np.arange(ctx), :, :, row].astype(np.float64)      # [ctx, H, D]
         vz = pool.v_zp[phys, :].astype(np.float64)
         vhat = (vc - vz[:, :, None]) * pool.v_scale[phys, :].astype(np.float64)[:, :, None]
     else:
-        vc = pool.v_codes[phys, :, row, :].astype(np.float64)
+        vc = pool.v_codes[phys][np.arange(ctx), :, :, row].astype(np.float64)
         vhat = vc * pool.v_scale[phys, :].astype(np.float64)[:, :, None]
     return khat.transpose(1, 0, 2), vhat.transpose(1, 0, 2)
 

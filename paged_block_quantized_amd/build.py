@@ -37,25 +37,27 @@ def _run(cmd, verbose):
     return r
 
 
-def build(verbose: bool = False, extra_hip_flags=()):
-    """Compile every source and link libpbq.so (always rebuilds)."""
+def build(verbose: bool = False, extra_hip_flags=(), out=LIB, build_dir=BUILD):
+    """Compile every source and link libpbq.so (always rebuilds).  ``out`` and
+    ``build_dir`` let variants with other compile-time settings be built
+    beside the default library."""
     hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
     cxx = shutil.which("g++") or "g++"
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
     jobs = []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(build_dir, src + ".o")
         jobs.append([hipcc, *HIP_FLAGS, *extra_hip_flags, "-c", os.path.join(CSRC, src), "-o", obj])
     for src in CPP_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(build_dir, src + ".o")
         jobs.append([cxx, *CPP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     objs = [j[-1] for j in jobs]
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -204,6 +204,8 @@ kv_status paged_attn_decode(const kv_pool_desc* d, const kv_pool_mem* m,
     if (part == 0) part = paged_attn_default_partition(d, num_seqs, num_q_heads, max_context_len);
     if (part <= 0 || part % d->block_size != 0)
         return fail(KV_ERR_INVALID, "partition_size must be a positive multiple of block_size (or 0)");
+    if (num_q_heads != d->num_kv_heads && part % 32 != 0)
+        return fail(KV_ERR_INVALID, "grouped-query partition_size must be a multiple of 32 tokens");
     const int32_t max_parts = max_context_len > 0 ? pbq::ceil_div(max_context_len, part) : 1;
     if (max_parts > 65535) return fail(KV_ERR_INVALID, "too many partitions; use a larger partition_size");
     const size_t need = paged_attn_workspace_bytes(d, num_seqs, num_q_heads, max_context_len, part);

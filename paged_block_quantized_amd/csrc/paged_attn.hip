@@ -48,17 +48,6 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <bool V4, int NR>
-struct VRegs;
-template <int NR>
-struct VRegs<false, NR> {
-    u32x4 r[NR];
-};
-template <int NR>
-struct VRegs<true, NR> {
-    u32x2 r[NR];
-};
-
 // Code bytes -> fp16 pairs without a conversion instruction: v_perm_b32
 // places a code byte u under the byte 0x64, giving the fp16 value 1024 + u
 // exactly.  INT8 codes are first offset to u = c + 128 (xor 0x80), so the pair
@@ -75,13 +64,32 @@ __device__ __forceinline__ f16x2 as_h2(uint32_t x) { return __builtin_bit_cast(f
 __device__ __forceinline__ f16x2 perm_lo(uint32_t w) { return as_h2(__builtin_amdgcn_perm(kF16Hi, w, kSelLo)); }
 __device__ __forceinline__ f16x2 perm_hi(uint32_t w) { return as_h2(__builtin_amdgcn_perm(kF16Hi, w, kSelHi)); }
 
+#ifndef PBQ_MHA_WAVES_PER_EU
+#define PBQ_MHA_WAVES_PER_EU 1
+#endif
+
+// MHA partition kernel.  K tiles are token-major [bs, D]: lane l owns dims
+// (l % (D/16)) * 16 .. +16 of rows r * (64 / (D/16)) + l / (D/16).  V tiles are
+// dim-major [D, bs]: lane l owns dims l + 64 k (k < D/64), each a contiguous
+// row of the block's tokens.  The softmax weights of a block (times its V
+// scale) are broadcast to scalar registers with readlane and every lane
+// accumulates its own dims, so no lane combination is needed for V.
 template <int BS, int D, bool V4, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_partition_mha(AttnArgs a) {
-    constexpr int LPR = D / 16;    // lanes per token row (16 dims each)
-    constexpr int RPI = 64 / LPR;  // token rows per wave access
-    constexpr int NR = BS / RPI;   // rows per lane per block
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_MHA_WAVES_PER_EU)))
+void attn_partition_mha(AttnArgs a) {
+    constexpr int LPR = D / 16;    // K: lanes per token row (16 dims each)
+    constexpr int RPI = 64 / LPR;  // K: token rows per wave access
+    constexpr int NR = BS / RPI;   // K: rows per lane per block
     constexpr int KT = BS * D;     // K tile bytes
-    constexpr int VT = V4 ? KT / 2 : KT;
+    constexpr int DPL = D / 64;    // V: dims per lane
+    constexpr int VROW = V4 ? BS / 2 : BS;  // V: bytes per dim row
+    constexpr int VT = D * VROW;   // V tile bytes
+    constexpr int VW = VROW / 4;   // V: dwords per dim row
+
+    struct Regs {
+        u32x4 k[NR];
+        uint32_t v[DPL][VW];
+    };
 
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
@@ -116,149 +124,167 @@ __global__ __launch_bounds__(64 * NW) void attn_partition_mha(AttnArgs a) {
 
     const float c2 = a.sm_scale * kLog2e;
     float m = -INFINITY, l = 0.f, zacc = 0.f;
-    float acc[16];
+    float acc[DPL][2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int k = 0; k < DPL; ++k) acc[k][0] = acc[k][1] = 0.f;
 
     const int32_t* tab = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
     const int row_lane = lane / LPR;
 
     for (int base = b0 + w; base < b1; base += 64 * NW) {
-        // stage this wave's next (up to) 64 blocks: ids, scales, zero points
+        // stage this wave's next (up to) 64 blocks: ids, then (after the first
+        // block's codes are in flight) scales and zero points
         const int bi = base + lane * NW;
-        int id = 0;
-        float sk = 0.f, sv = 0.f, vb = 0.f;
-        if (bi < b1) {
-            id = tab[bi];
-            const int64_t t = (int64_t)id * H + h;
-            sk = bits_to_f16f(a.k_scale[t]) * c2;
-            sv = bits_to_f16f(a.v_scale[t]);
-            if constexpr (V4) vb = kI4Bias + (float)a.v_zp[t];
-            else vb = kI8Bias;
-        }
+        const int id = bi < b1 ? tab[bi] : 0;
         const int cnt = min(64, (b1 - base + NW - 1) / NW);
+        float sk = 0.f, sv = 0.f, vb = kI8Bias;
 
-        auto load = [&](int i, u32x4 (&kr)[NR], VRegs<V4, NR>& vr) {
+        auto load = [&](int i, Regs& r) {
             const int phys = readlane(id, i);
             const int64_t t = (int64_t)phys * H + h;
             const int8_t* kp = a.k_codes + t * KT + lane * 16;
-            const uint8_t* vp = a.v_codes + t * VT + lane * (V4 ? 8 : 16);
 #pragma unroll
-            for (int r = 0; r < NR; ++r) kr[r] = *(const u32x4*)(kp + r * 1024);
+            for (int j = 0; j < NR; ++j) r.k[j] = *(const u32x4*)(kp + j * 1024);
+            const uint8_t* vp = a.v_codes + t * VT;
 #pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                if constexpr (V4) vr.r[r] = *(const u32x2*)(vp + r * 512);
-                else vr.r[r] = *(const u32x4*)(vp + r * 1024);
+            for (int k = 0; k < DPL; ++k) {
+                const uint8_t* row = vp + (lane + 64 * k) * VROW;
+                if constexpr (VROW == 8) {
+                    const u32x2 x = *(const u32x2*)row;
+                    r.v[k][0] = x[0];
+                    r.v[k][1] = x[1];
+                } else {
+#pragma unroll
+                    for (int c = 0; c < VROW / 16; ++c) {
+                        const u32x4 x = *(const u32x4*)(row + 16 * c);
+                        r.v[k][4 * c + 0] = x[0];
+                        r.v[k][4 * c + 1] = x[1];
+                        r.v[k][4 * c + 2] = x[2];
+                        r.v[k][4 * c + 3] = x[3];
+                    }
+                }
             }
         };
 
-        auto compute = [&](const u32x4 (&kr)[NR], const VRegs<V4, NR>& vr, int i) {
+        auto compute = [&](const Regs& r, int i) {
             const int blk = base + i * NW;
             const float skc = readlane(sk, i);
             float sc[NR];
 #pragma unroll
-            for (int r = 0; r < NR; ++r) {
+            for (int j = 0; j < NR; ++j) {
                 float d = 0.f;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const uint32_t u = kr[r][k] ^ 0x80808080u;
+                    const uint32_t u = r.k[j][k] ^ 0x80808080u;
                     d = __builtin_amdgcn_fdot2(perm_lo(u), q2[2 * k], d, false);
                     d = __builtin_amdgcn_fdot2(perm_hi(u), q2[2 * k + 1], d, false);
                 }
-                sc[r] = d - qbias;
+                sc[j] = d - qbias;
             }
 #pragma unroll
-            for (int r = 0; r < NR; ++r) sc[r] = group_sum<LPR>(sc[r]);
+            for (int j = 0; j < NR; ++j) sc[j] = group_sum<LPR>(sc[j]);
             float bmax = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                const int t = blk * BS + r * RPI + row_lane;
-                sc[r] = t < ctx ? sc[r] * skc : -INFINITY;
-                bmax = fmaxf(bmax, sc[r]);
+            for (int j = 0; j < NR; ++j) {
+                const int t = blk * BS + j * RPI + row_lane;
+                sc[j] = t < ctx ? sc[j] * skc : -INFINITY;
+                bmax = fmaxf(bmax, sc[j]);
             }
             bmax = strided_max<LPR>(bmax);
             if (bmax > m) {
                 const float alpha = __builtin_amdgcn_exp2f(m - bmax);
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[e] *= alpha;
+                for (int k = 0; k < DPL; ++k) {
+                    acc[k][0] *= alpha;
+                    acc[k][1] *= alpha;
+                }
                 l *= alpha;
                 zacc *= alpha;
                 m = bmax;
             }
             const float svv = readlane(sv, i);
             const float vbias = readlane(vb, i);
+            float pv[NR];
 #pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                const float pr = __builtin_amdgcn_exp2f(sc[r] - m);
+            for (int j = 0; j < NR; ++j) {
+                const float pr = __builtin_amdgcn_exp2f(sc[j] - m);
                 l += pr;
-                const float pv = pr * svv;
-                zacc = __builtin_fmaf(pv, vbias, zacc);
+                pv[j] = pr * svv;
+                zacc = __builtin_fmaf(pv[j], vbias, zacc);
+            }
+            // weights of all tokens of the block, uniform across the wave
+            float sp[BS];
+#pragma unroll
+            for (int t = 0; t < BS; ++t) sp[t] = readlane(pv[t / RPI], (t % RPI) * LPR);
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) {
                 if constexpr (V4) {
 #pragma unroll
-                    for (int k = 0; k < 2; ++k) {
-                        const uint32_t wv = vr.r[r][k];
-                        const uint32_t lo = wv & 0x0F0F0F0Fu;         // dims 8k + 0,2,4,6
-                        const uint32_t hi = (wv >> 4) & 0x0F0F0F0Fu;  // dims 8k + 1,3,5,7
-                        const f16x2 a0 = perm_lo(lo), a1 = perm_hi(lo);
-                        const f16x2 b0 = perm_lo(hi), b1 = perm_hi(hi);
-                        acc[8 * k + 0] = __builtin_fmaf(pv, (float)a0[0], acc[8 * k + 0]);
-                        acc[8 * k + 2] = __builtin_fmaf(pv, (float)a0[1], acc[8 * k + 2]);
-                        acc[8 * k + 4] = __builtin_fmaf(pv, (float)a1[0], acc[8 * k + 4]);
-                        acc[8 * k + 6] = __builtin_fmaf(pv, (float)a1[1], acc[8 * k + 6]);
-                        acc[8 * k + 1] = __builtin_fmaf(pv, (float)b0[0], acc[8 * k + 1]);
-                        acc[8 * k + 3] = __builtin_fmaf(pv, (float)b0[1], acc[8 * k + 3]);
-                        acc[8 * k + 5] = __builtin_fmaf(pv, (float)b1[0], acc[8 * k + 5]);
-                        acc[8 * k + 7] = __builtin_fmaf(pv, (float)b1[1], acc[8 * k + 7]);
+                    for (int c = 0; c < VW; ++c) {   // tokens 8c .. 8c+7
+                        const uint32_t wv = r.v[k][c];
+                        const uint32_t lo = wv & 0x0F0F0F0Fu;         // tokens 0,2,4,6
+                        const uint32_t hi = (wv >> 4) & 0x0F0F0F0Fu;  // tokens 1,3,5,7
+                        const f16x2 e0 = perm_lo(lo), e1 = perm_hi(lo);
+                        const f16x2 o0 = perm_lo(hi), o1 = perm_hi(hi);
+                        const int t = 8 * c;
+                        acc[k][0] = __builtin_fmaf(sp[t + 0], (float)e0[0], acc[k][0]);
+                        acc[k][1] = __builtin_fmaf(sp[t + 1], (float)o0[0], acc[k][1]);
+                        acc[k][0] = __builtin_fmaf(sp[t + 2], (float)e0[1], acc[k][0]);
+                        acc[k][1] = __builtin_fmaf(sp[t + 3], (float)o0[1], acc[k][1]);
+                        acc[k][0] = __builtin_fmaf(sp[t + 4], (float)e1[0], acc[k][0]);
+                        acc[k][1] = __builtin_fmaf(sp[t + 5], (float)o1[0], acc[k][1]);
+                        acc[k][0] = __builtin_fmaf(sp[t + 6], (float)e1[1], acc[k][0]);
+                        acc[k][1] = __builtin_fmaf(sp[t + 7], (float)o1[1], acc[k][1]);
                     }
                 } else {
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint32_t u = vr.r[r][k] ^ 0x80808080u;
+                    for (int c = 0; c < VW; ++c) {   // tokens 4c .. 4c+3
+                        const uint32_t u = r.v[k][c] ^ 0x80808080u;
                         const f16x2 a0 = perm_lo(u), a1 = perm_hi(u);
-                        acc[4 * k + 0] = __builtin_fmaf(pv, (float)a0[0], acc[4 * k + 0]);
-                        acc[4 * k + 1] = __builtin_fmaf(pv, (float)a0[1], acc[4 * k + 1]);
-                        acc[4 * k + 2] = __builtin_fmaf(pv, (float)a1[0], acc[4 * k + 2]);
-                        acc[4 * k + 3] = __builtin_fmaf(pv, (float)a1[1], acc[4 * k + 3]);
+                        const int t = 4 * c;
+                        acc[k][0] = __builtin_fmaf(sp[t + 0], (float)a0[0], acc[k][0]);
+                        acc[k][1] = __builtin_fmaf(sp[t + 1], (float)a0[1], acc[k][1]);
+                        acc[k][0] = __builtin_fmaf(sp[t + 2], (float)a1[0], acc[k][0]);
+                        acc[k][1] = __builtin_fmaf(sp[t + 3], (float)a1[1], acc[k][1]);
                     }
                 }
             }
         };
 
         // ping-pong: the next block's codes are in flight while one is computed
-        u32x4 kA[NR], kB[NR];
-        VRegs<V4, NR> vA, vB;
-        load(0, kA, vA);
+        Regs rA, rB;
+        load(0, rA);
+        if (bi < b1) {
+            const int64_t t = (int64_t)id * H + h;
+            sk = bits_to_f16f(a.k_scale[t]) * c2;
+            sv = bits_to_f16f(a.v_scale[t]);
+            if constexpr (V4) vb = kI4Bias + (float)a.v_zp[t];
+        }
         int i = 0;
         for (; i + 1 < cnt; i += 2) {
-            load(i + 1, kB, vB);
-            compute(kA, vA, i);
-            if (i + 2 < cnt) load(i + 2, kA, vA);
-            compute(kB, vB, i + 1);
+            load(i + 1, rB);
+            compute(rA, i);
+            if (i + 2 < cnt) load(i + 2, rA);
+            compute(rB, i + 1);
         }
-        if (i < cnt) compute(kA, vA, i);
+        if (i < cnt) compute(rA, i);
     }
 
-    // combine the lanes that own the same dims (different token rows)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = strided_sum<LPR>(acc[e]);
-    l = strided_sum<LPR>(l);
-    zacc = strided_sum<LPR>(zacc);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] -= zacc;
+    // every token row is held by LPR lanes: full-wave sums count it LPR times
+    const float inv_lpr = 1.0f / (float)LPR;
+    l = group_sum<64>(l) * inv_lpr;
+    zacc = group_sum<64>(zacc) * inv_lpr;
 
     __shared__ float s_acc[NW][D];
     __shared__ float s_ml[NW][2];
-    if (lane < LPR) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s_acc[w][dl + e] = acc[e];
-    }
+    for (int k = 0; k < DPL; ++k) s_acc[w][lane + 64 * k] = acc[k][0] + acc[k][1] - zacc;
     if (lane == 0) {
         s_ml[w][0] = m;
         s_ml[w][1] = l;
     }
     __syncthreads();
-    const int tid = threadIdx.x;
-    if (tid < D) {
+    for (int tid = threadIdx.x; tid < D; tid += 64 * NW) {
         float M = -INFINITY;
 #pragma unroll
         for (int k = 0; k < NW; ++k) M = fmaxf(M, s_ml[k][0]);
@@ -284,11 +310,281 @@ __global__ __launch_bounds__(64 * NW) void attn_partition_mha(AttnArgs a) {
     }
 }
 
+// ---- grouped-query attention on MFMA ---------------------------------------
+//
+// Several query heads share one KV head, so the contraction is dense enough
+// for matrix cores: per 32-token step and per group of up to 16 query heads,
+// S^T[32 tok x 16 heads] = K_hat[32 x D] * Q^T[D x 16] takes 2 x D/32
+// v_mfma_f32_16x16x32_f16, and O^T[D x 16] += V_hat^T[D x 32] * P^T[32 x 16]
+// takes D/16 more.  Codes become fp16 exactly (v_perm under 0x64, offset
+// removed with v_pk_add_f16 for V); products are exact in fp32.
+//
+// MFMA 16x16x32 f16 lane layout (A: m = l%16, k = 8(l/16)+i; B: n = l%16,
+// k = 8(l/16)+i; C: n = l%16, m = 4(l/16)+i).  Token order inside a step is
+// arranged so that no value moves between lanes:
+//   * the PV contraction slot j of lane group g is token 8g + kappa(j), where
+//     kappa is the order in which v_perm emits a V row's codes (identity for
+//     INT8, even-then-odd tokens for INT4 nibbles);
+//   * the QK product's M slot 4g+i of tile mt is token 8g + kappa(4mt + i),
+//     so lane (head n, group g) ends up holding the scores of exactly the
+//     tokens its PV B operand needs.
+// A lane group g therefore touches the tokens 8g..8g+7 of the step, i.e. one
+// block (bs 32) or block g/2 (bs 16): its V scale, zero point and K scale are
+// per-lane values.
+template <bool V4>
+__device__ __forceinline__ int kappa(int j) {
+    if constexpr (V4) return (j & 4) ? 2 * (j & 3) + 1 : 2 * (j & 3);
+    else return j;
+}
+
+typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t pk_sub_f16(uint32_t x, uint32_t off2) {
+    // exact: both operands are small integers in fp16
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, x) - __builtin_bit_cast(f16x2, off2));
+}
+
+template <int BS, int D, bool V4, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_partition_gqa(AttnArgs a) {
+    static_assert(BS == 16 || BS == 32, "block size");
+    constexpr int KS = D / 32;                 // QK k-steps
+    constexpr int DT = D / 16;                 // PV dim tiles
+    constexpr int KCH = D / 4;                 // K bytes per lane per row
+    constexpr int BPS = 32 / BS;               // blocks per 32-token step
+    constexpr int VB = V4 ? 4 : 8;             // V bytes per lane per dim tile
+    constexpr int VROW = V4 ? BS / 2 : BS;     // V bytes per dim row
+    constexpr int KT = BS * D;
+    constexpr int VT = D * VROW;
+
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int n16 = lane & 15;       // head (C/B layouts) or M row (A layout)
+    const int grp = lane >> 4;       // lane group
+    const int p = blockIdx.x;
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int n_ht = (G + 15) / 16;
+    const int kvh = blockIdx.y / n_ht;
+    const int ht = blockIdx.y % n_ht;
+    const int s = blockIdx.z;
+    const int H = a.num_kv_heads;
+    const int ctx = a.context_lens[s];
+    const int nblk = (ctx + BS - 1) / BS;
+    const int PB = a.partition_blocks;
+    const int nparts = max(1, (nblk + PB - 1) / PB);
+    if (p >= nparts) return;
+    const int tok0 = p * PB * BS;
+    const int tok1 = min(tok0 + PB * BS, ctx);
+    const int nsteps = (tok1 - tok0 + 31) / 32;
+    const int head_base = kvh * G + ht * 16;
+    const int nheads = min(16, G - ht * 16);
+
+    // Q as the B operand of the QK product: lane (head n16, group grp) holds
+    // q[n16][(D/4) grp + 8 j + i] for k-step j
+    f16x8v qop[KS];
+    float qbias;
+    {
+        float qs = 0.f;
+        const bool live = n16 < nheads;
+        const uint16_t* qp = a.q + ((int64_t)s * a.num_q_heads + head_base + n16) * D + KCH * grp;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            f16x8v x = (f16x8v)(_Float16)0;
+            if (live) x = *(const f16x8v*)(qp + 8 * j);
+            qop[j] = x;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qs += (float)x[i];
+        }
+        qs += shfl_xor_f(qs, 16);
+        qs += shfl_xor_f(qs, 32);
+        qbias = kI8Bias * qs;
+    }
+
+    const float c2 = a.sm_scale * kLog2e;
+    float m = -INFINITY, l = 0.f;
+    f32x4 acc[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) acc[t] = (f32x4)0.f;
+
+    const int32_t* tab = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    const int blk0 = tok0 / BS;
+    // the block (within a step) whose K row this lane loads for tile mt, and
+    // the row inside it: token 8(n16/4) + kappa(4mt + n16%4)
+    int krow[2], kblk[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        const int tk = 8 * (n16 >> 2) + kappa<V4>(4 * mt + (n16 & 3));
+        kblk[mt] = tk / BS;
+        krow[mt] = tk % BS;
+    }
+    const int my_blk = (8 * grp) / BS;       // block of tokens 8grp..8grp+7
+    const int vcol = ((8 * grp) % BS) / (V4 ? 2 : 1);
+
+    struct Raw {
+        u32x4 k[2][KCH / 16];
+        uint32_t v[DT][VB / 4];
+    };
+
+    for (int st = w; st < nsteps; st += NW) {
+        const int sb = blk0 + st * BPS;        // first block of this step
+        // block ids of the step (lane-select between two for bs 16)
+        int ids[BPS];
+#pragma unroll
+        for (int b = 0; b < BPS; ++b) ids[b] = sb + b < nblk ? tab[sb + b] : -1;
+        Raw r;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int id = BPS == 1 ? ids[0] : (kblk[mt] ? ids[BPS - 1] : ids[0]);
+            const bool ok = id >= 0;
+            const int8_t* kp = a.k_codes + ((int64_t)(ok ? id : 0) * H + kvh) * KT + krow[mt] * D + KCH * grp;
+#pragma unroll
+            for (int c = 0; c < KCH / 16; ++c) r.k[mt][c] = ok ? *(const u32x4*)(kp + 16 * c) : (u32x4)0u;
+        }
+        const int vid = BPS == 1 ? ids[0] : (my_blk ? ids[BPS - 1] : ids[0]);
+        const bool vok = vid >= 0;
+        {
+            const uint8_t* vp = a.v_codes + ((int64_t)(vok ? vid : 0) * H + kvh) * VT + vcol;
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                const uint8_t* row = vp + (16 * t + n16) * VROW;
+                if constexpr (V4) {
+                    r.v[t][0] = vok ? *(const uint32_t*)row : 0u;
+                } else {
+                    const u32x2 x = vok ? *(const u32x2*)row : (u32x2)0u;
+                    r.v[t][0] = x[0];
+                    r.v[t][1] = x[1];
+                }
+            }
+        }
+        float sk = 0.f, sv = 0.f, zpv = 0.f;
+        if (vok) {
+            const int64_t t = (int64_t)vid * H + kvh;
+            sk = bits_to_f16f(a.k_scale[t]) * c2;
+            sv = bits_to_f16f(a.v_scale[t]);
+            if constexpr (V4) zpv = (float)a.v_zp[t];
+        }
+
+        // ---- S^T = K_hat Q^T --------------------------------------------------
+        f32x4 sc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            sc[mt] = (f32x4)0.f;
+#pragma unroll
+            for (int j = 0; j < KS; ++j) {
+                const uint32_t u0 = r.k[mt][j / 2][2 * (j & 1)] ^ 0x80808080u;
+                const uint32_t u1 = r.k[mt][j / 2][2 * (j & 1) + 1] ^ 0x80808080u;
+                const uint32_t a4[4] = {__builtin_amdgcn_perm(kF16Hi, u0, kSelLo), __builtin_amdgcn_perm(kF16Hi, u0, kSelHi),
+                                        __builtin_amdgcn_perm(kF16Hi, u1, kSelLo), __builtin_amdgcn_perm(kF16Hi, u1, kSelHi)};
+                const f16x8v aop = __builtin_bit_cast(f16x8v, a4);
+                sc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, qop[j], sc[mt], 0, 0, 0);
+            }
+        }
+        // lane (head n16, group grp): sc[mt][i] is token 8 grp + kappa(4 mt + i)
+        float x[8];
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = tok0 + 32 * st + 8 * grp + kappa<V4>(4 * mt + i);
+                const float v = (sc[mt][i] - qbias) * sk;
+                x[4 * mt + i] = t < tok1 ? v : -INFINITY;
+                bmax = fmaxf(bmax, x[4 * mt + i]);
+            }
+        bmax = fmaxf(bmax, shfl_xor_f(bmax, 16));
+        bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
+        if (bmax > m) {   // per head; lanes of one head agree
+            const float alpha = __builtin_amdgcn_exp2f(m - bmax);
+#pragma unroll
+            for (int t = 0; t < DT; ++t) acc[t] *= alpha;
+            l *= alpha;
+            m = bmax;
+        }
+        uint32_t pw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(x[2 * e] - m);
+            const float p1 = __builtin_amdgcn_exp2f(x[2 * e + 1] - m);
+            l += p0 + p1;
+            const f16x2 h2 = f16x2{(_Float16)(p0 * sv), (_Float16)(p1 * sv)};
+            pw[e] = __builtin_bit_cast(uint32_t, h2);
+        }
+        const f16x8v pop = __builtin_bit_cast(f16x8v, pw);
+
+        // ---- O^T += V_hat^T P^T ------------------------------------------------
+        const _Float16 vo = (_Float16)((V4 ? kI4Bias : kI8Bias) + zpv);
+        const uint32_t off2 = __builtin_bit_cast(uint32_t, f16x2{vo, vo});
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            uint32_t a4[4];
+            if constexpr (V4) {
+                const uint32_t wv = r.v[t][0];
+                const uint32_t lo = wv & 0x0F0F0F0Fu, hi = (wv >> 4) & 0x0F0F0F0Fu;
+                a4[0] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, lo, kSelLo), off2);
+                a4[1] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, lo, kSelHi), off2);
+                a4[2] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, hi, kSelLo), off2);
+                a4[3] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, hi, kSelHi), off2);
+            } else {
+                const uint32_t u0 = r.v[t][0] ^ 0x80808080u, u1 = r.v[t][1] ^ 0x80808080u;
+                a4[0] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u0, kSelLo), off2);
+                a4[1] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u0, kSelHi), off2);
+                a4[2] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u1, kSelLo), off2);
+                a4[3] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u1, kSelHi), off2);
+            }
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8v, a4), pop, acc[t], 0, 0, 0);
+        }
+    }
+    // lanes of one head split its tokens by group: sum their partial sums
+    l += shfl_xor_f(l, 16);
+    l += shfl_xor_f(l, 32);
+
+    __shared__ float s_acc[NW][16][D];
+    __shared__ float s_ml[NW][16][2];
+    // acc[t][i] is (dim 16t + 4 grp + i, head n16)
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_acc[w][n16][16 * t + 4 * grp + i] = acc[t][i];
+    if (grp == 0) {
+        s_ml[w][n16][0] = m;
+        s_ml[w][n16][1] = l;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < nheads * D; idx += 64 * NW) {
+        const int hh = idx / D, d = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) M = fmaxf(M, s_ml[k][hh][0]);
+        float L = 0.f, o = 0.f;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) {
+            const float f = s_ml[k][hh][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_ml[k][hh][0] - M);
+            L = __builtin_fmaf(s_ml[k][hh][1], f, L);
+            o = __builtin_fmaf(s_acc[k][hh][d], f, o);
+        }
+        const float res = L > 0.f ? o / L : 0.f;
+        const int64_t row = (int64_t)s * a.num_q_heads + head_base + hh;
+        if (nparts == 1) {
+            a.out[row * D + d] = f32_to_f16_bits(res);
+        } else {
+            const int64_t prow = row * a.max_partitions + p;
+            a.ws_out[prow * D + d] = res;
+            if (d == 0) {
+                a.ws_ml[prow * 2] = M;
+                a.ws_ml[prow * 2 + 1] = L;
+            }
+        }
+    }
+}
+
 // One wavefront per (query head, sequence): merges the partitions of
-// sequences that have more than one.
+// sequences that have more than one.  Lane p holds partition p's (max, sum)
+// and weight; the partial outputs are read eight partitions at a time so that
+// their loads are in flight together.
 template <int BS, int D>
 __global__ __launch_bounds__(64) void attn_reduce(AttnArgs a) {
     constexpr int PER = D / 64;
+    constexpr int BATCH = 8;
     const int lane = threadIdx.x;
     const int h = blockIdx.x;
     const int s = blockIdx.y;
@@ -298,31 +594,69 @@ __global__ __launch_bounds__(64) void attn_reduce(AttnArgs a) {
     if (nparts == 1) return;
     const int64_t row = (int64_t)s * a.num_q_heads + h;
     const int64_t prow0 = row * a.max_partitions;
+    const float* ml = a.ws_ml + prow0 * 2;
+    const float* op = a.ws_out + prow0 * D + lane;
+
     float M = -INFINITY;
-    for (int pp = lane; pp < nparts; pp += 64) M = fmaxf(M, a.ws_ml[(prow0 + pp) * 2]);
+    for (int pp = lane; pp < nparts; pp += 64) M = fmaxf(M, ml[2 * pp]);
     M = wave_max(M);
+
     float L = 0.f;
     float o[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) o[k] = 0.f;
-    for (int pp = 0; pp < nparts; ++pp) {
-        const float mp = a.ws_ml[(prow0 + pp) * 2];
-        const float lp = a.ws_ml[(prow0 + pp) * 2 + 1];
-        const float wgt = mp == -INFINITY ? 0.f : lp * __builtin_amdgcn_exp2f(mp - M);
+    for (int base = 0; base < nparts; base += 64) {
+        const int pp = base + lane;
+        float wgt = 0.f;
+        if (pp < nparts) {
+            const float mp = ml[2 * pp];
+            wgt = mp == -INFINITY ? 0.f : ml[2 * pp + 1] * __builtin_amdgcn_exp2f(mp - M);
+        }
         L += wgt;
-        const float* op = a.ws_out + (prow0 + pp) * D;
+        const int cnt = min(64, nparts - base);
+        for (int i = 0; i < cnt; i += BATCH) {
+            float v[BATCH][PER];
 #pragma unroll
-        for (int k = 0; k < PER; ++k) o[k] = __builtin_fmaf(wgt, op[lane + 64 * k], o[k]);
+            for (int b = 0; b < BATCH; ++b)
+#pragma unroll
+                for (int k = 0; k < PER; ++k)
+                    v[b][k] = i + b < cnt ? op[(int64_t)(base + i + b) * D + 64 * k] : 0.f;
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) {
+                const float wb = readlane(wgt, min(i + b, 63));
+#pragma unroll
+                for (int k = 0; k < PER; ++k) o[k] = __builtin_fmaf(wb, v[b][k], o[k]);
+            }
+        }
     }
+    L = group_sum<64>(L);
 #pragma unroll
     for (int k = 0; k < PER; ++k) a.out[row * D + lane + 64 * k] = f32_to_f16_bits(L > 0.f ? o[k] / L : 0.f);
 }
 
+#ifndef PBQ_MHA_WAVES
+#define PBQ_MHA_WAVES 4
+#endif
+
 template <int BS, int D, bool V4>
 hipError_t launch_mha(const AttnArgs& a, hipStream_t stream) {
-    constexpr int NW = 4;
+    constexpr int NW = PBQ_MHA_WAVES;
     dim3 grid((unsigned)a.max_partitions, (unsigned)a.num_q_heads, (unsigned)a.num_seqs);
     hipLaunchKernelGGL((attn_partition_mha<BS, D, V4, NW>), grid, dim3(64 * NW), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.max_partitions <= 1) return e;
+    hipLaunchKernelGGL((attn_reduce<BS, D>), dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(64), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+template <int BS, int D, bool V4>
+hipError_t launch_gqa(const AttnArgs& a, hipStream_t stream) {
+    constexpr int NW = 4;
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int n_ht = (G + 15) / 16;
+    dim3 grid((unsigned)a.max_partitions, (unsigned)(a.num_kv_heads * n_ht), (unsigned)a.num_seqs);
+    hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, NW>), grid, dim3(64 * NW), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_partitions <= 1) return e;
     hipLaunchKernelGGL((attn_reduce<BS, D>), dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(64), 0,
@@ -333,11 +667,13 @@ hipError_t launch_mha(const AttnArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_paged_attn(const AttnArgs& a, hipStream_t stream) {
-    if (a.num_q_heads != a.num_kv_heads) return hipErrorNotSupported;
     const bool v4 = a.v_codec == KV_CODEC_I4_ASYM;
-#define PBQ_ATTN(BS, D)                                                        \
-    if (a.block_size == BS && a.head_dim == D)                                 \
-        return v4 ? launch_mha<BS, D, true>(a, stream) : launch_mha<BS, D, false>(a, stream);
+    const bool gqa = a.num_q_heads != a.num_kv_heads;
+#define PBQ_ATTN(BS, D)                                                                        \
+    if (a.block_size == BS && a.head_dim == D) {                                               \
+        if (gqa) return v4 ? launch_gqa<BS, D, true>(a, stream) : launch_gqa<BS, D, false>(a, stream); \
+        return v4 ? launch_mha<BS, D, true>(a, stream) : launch_mha<BS, D, false>(a, stream);  \
+    }
     PBQ_ATTN(16, 64)
     PBQ_ATTN(16, 128)
     PBQ_ATTN(32, 64)

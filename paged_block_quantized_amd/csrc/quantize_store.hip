@@ -18,10 +18,12 @@
 //
 // Mapping: one wavefront per (sequence, touched block, KV head); a workgroup
 // of four waves takes four consecutive heads of one block, so each token row
-// is read as 4 x D x 2 contiguous bytes.  Lane l holds rows
-// it * (64 / (D/8)) + l / (D/8) and dims (l % (D/8)) * 8 .. + 8, read and
-// written with 16-byte (fp16 in) and 8- or 4-byte (codes out) accesses that
-// are contiguous across the wave.
+// is read as 4 x D x 2 contiguous bytes.  K tiles are token-major
+// ([block_size, D] codes): lane l holds rows it * (64 / (D/8)) + l / (D/8) and
+// dims (l % (D/8)) * 8 .. + 8.  V tiles are dim-major ([D, block_size] codes,
+// INT4 packing two consecutive tokens per byte): lane l holds the D/64
+// adjacent dims starting at l * D/64 of every row, so each fp16 row read and
+// the lane's code rows are contiguous.
 //
 // Exact codes without a per-element division: n = rint(x * (1/s)) is within
 // one of the answer; the remainder x - n*s is exact in one FMA (x and s are
@@ -76,25 +78,16 @@ __global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
     const int col = (lane % LPR) * 8;
 
     const int64_t tail_base = ((int64_t)slot * H + g) * BS * D;
-    f16x8 kx[NIT], vx[NIT];
+    f16x8 kx[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
         const int r = it * RPI + r_in;
         const int p = row0 + r;
         kx[it] = (f16x8)(_Float16)0;
-        vx[it] = (f16x8)(_Float16)0;
         if (r < valid) {
-            const uint16_t *ks, *vs;
-            if (p < sp) {
-                ks = a.tail_k + tail_base + r * D + col;
-                vs = a.tail_v + tail_base + r * D + col;
-            } else {
-                const int64_t row = (int64_t)(c0 + p - sp) * H + g;
-                ks = a.k + row * D + col;
-                vs = a.v + row * D + col;
-            }
+            const uint16_t* ks = p < sp ? a.tail_k + tail_base + r * D + col
+                                        : a.k + ((int64_t)(c0 + p - sp) * H + g) * D + col;
             kx[it] = *(const f16x8*)ks;
-            vx[it] = *(const f16x8*)vs;
         }
     }
 
@@ -132,14 +125,35 @@ __global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
         if (lane == 0) a.k_scale[tile] = s16;
     }
 
-    // ---- V: INT8 symmetric or INT4 asymmetric -------------------------------
+    // ---- V (dim-major tile): INT8 symmetric or INT4 asymmetric ----------------
+    constexpr int DPL = D / 64;  // dims per lane
+    _Float16 vx[DPL][BS];
+#pragma unroll
+    for (int r = 0; r < BS; ++r) {
+        const int p = row0 + r;
+        const uint16_t* src = nullptr;
+        if (r < valid) {
+            src = p < sp ? a.tail_v + tail_base + r * D
+                         : a.v + ((int64_t)(c0 + p - sp) * H + g) * D;
+        }
+        if constexpr (DPL == 2) {
+            const uint32_t w = src ? *(const uint32_t*)(src + 2 * lane) : 0u;
+            vx[0][r] = __builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+            vx[1][r] = __builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+        } else {
+            vx[0][r] = __builtin_bit_cast(_Float16, src ? src[lane] : (uint16_t)0);
+        }
+    }
     if constexpr (!V4) {
         uint32_t amax = 0;
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const uint32_t b = absmax_bits_f16x8(vx[it]);
-            amax = amax > b ? amax : b;
-        }
+        for (int k = 0; k < DPL; ++k)
+#pragma unroll
+            for (int r = 0; r < BS; ++r) {
+                const _Float16 x = vx[k][r];
+                const uint32_t b = __builtin_bit_cast(uint16_t, x) & 0x7FFFu;
+                amax = amax > b ? amax : b;
+            }
         amax = wave_max_u32(amax);
         const float absmax = bits_to_f16f((uint16_t)amax);
         const uint16_t s16 = f32_to_f16_bits(absmax / 127.0f);
@@ -148,27 +162,31 @@ __global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
         const float half_s = 0.5f * sc;
         uint8_t* dst = a.v_codes + tile * (BS * D);
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            uint32_t w[2] = {0u, 0u};
+        for (int k = 0; k < DPL; ++k) {
+            uint32_t w[BS / 4];
+#pragma unroll
+            for (int i = 0; i < BS / 4; ++i) w[i] = 0u;
             if (sc > 0.f) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    int q = rne_quot((float)vx[it][e], sc, rcp, half_s, 0);
+                for (int r = 0; r < BS; ++r) {
+                    int q = rne_quot((float)vx[k][r], sc, rcp, half_s, 0);
                     q = q > 127 ? 127 : (q < -127 ? -127 : q);
-                    w[e >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (e & 3));
+                    w[r >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (r & 3));
                 }
             }
-            const int r = it * RPI + r_in;
-            *(u32x2*)(dst + r * D + col) = u32x2{w[0], w[1]};
+            uint32_t* drow = (uint32_t*)(dst + (DPL * lane + k) * BS);
+#pragma unroll
+            for (int i = 0; i < BS / 16; ++i)
+                *(u32x4*)(drow + 4 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
         }
         if (lane == 0) a.v_scale[tile] = s16;
     } else {
         float lo = 0.f, hi = 0.f;  // range widened to contain 0
 #pragma unroll
-        for (int it = 0; it < NIT; ++it)
+        for (int k = 0; k < DPL; ++k)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = (float)vx[it][e];
+            for (int r = 0; r < BS; ++r) {
+                const float x = (float)vx[k][r];
                 lo = fminf(lo, x);
                 hi = fmaxf(hi, x);
             }
@@ -185,18 +203,28 @@ __global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
         const float half_s = 0.5f * sc;
         uint8_t* dst = a.v_codes + tile * (BS * D / 2);
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int r = it * RPI + r_in;
-            uint32_t w = 0u;
-            if (sc > 0.f && r < valid) {
+        for (int k = 0; k < DPL; ++k) {
+            uint32_t w[BS / 8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    int q = rne_quot((float)vx[it][e], sc, rcp, half_s, zp);
-                    q = q > 15 ? 15 : (q < 0 ? 0 : q);
-                    w |= (uint32_t)q << (4 * e);
+            for (int i = 0; i < BS / 8; ++i) w[i] = 0u;
+            if (sc > 0.f) {
+#pragma unroll
+                for (int r = 0; r < BS; ++r) {
+                    if (r < valid) {
+                        int q = rne_quot((float)vx[k][r], sc, rcp, half_s, zp);
+                        q = q > 15 ? 15 : (q < 0 ? 0 : q);
+                        w[r >> 3] |= (uint32_t)q << (4 * (r & 7));
+                    }
                 }
             }
-            *(uint32_t*)(dst + r * (D / 2) + col / 2) = w;
+            uint32_t* drow = (uint32_t*)(dst + (DPL * lane + k) * (BS / 2));
+            if constexpr (BS == 16) {
+                *(u32x2*)drow = u32x2{w[0], w[1]};
+            } else {
+#pragma unroll
+                for (int i = 0; i < BS / 32; ++i)
+                    *(u32x4*)(drow + 4 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+            }
         }
         if (lane == 0) {
             a.v_scale[tile] = s16;
@@ -209,9 +237,20 @@ __global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int r = it * RPI + r_in;
+            if (r < valid && row0 + r >= sp) *(f16x8*)(a.tail_k + tail_base + r * D + col) = kx[it];
+        }
+#pragma unroll
+        for (int r = 0; r < BS; ++r) {
             if (r < valid && row0 + r >= sp) {
-                *(f16x8*)(a.tail_k + tail_base + r * D + col) = kx[it];
-                *(f16x8*)(a.tail_v + tail_base + r * D + col) = vx[it];
+                uint16_t* t = a.tail_v + tail_base + r * D + DPL * lane;
+                if constexpr (DPL == 2) {
+                    const _Float16 x0 = vx[0][r], x1 = vx[1][r];
+                    *(uint32_t*)t = (uint32_t)__builtin_bit_cast(uint16_t, x0) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
+                } else {
+                    const _Float16 x0 = vx[0][r];
+                    *t = __builtin_bit_cast(uint16_t, x0);
+                }
             }
         }
     }

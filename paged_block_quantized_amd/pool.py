@@ -32,7 +32,8 @@ class KVPool:
             dev = torch.device(device)
             self.arrays = {
                 "k_codes": torch.zeros((N, H, bs, D), dtype=torch.int8, device=dev),
-                "v_codes": torch.zeros((N, H, bs, D // 2 if self.v_int4 else D),
+                # V tiles are dim-major: [D, bs] codes per (block, head)
+                "v_codes": torch.zeros((N, H, D, bs // 2 if self.v_int4 else bs),
                                        dtype=torch.uint8 if self.v_int4 else torch.int8, device=dev),
                 "k_scale": torch.zeros((N, H), dtype=torch.float16, device=dev),
                 "v_scale": torch.zeros((N, H), dtype=torch.float16, device=dev),

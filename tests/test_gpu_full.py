@@ -146,3 +146,8 @@ def test_prefill_store_full():
         assert np.array_equal(pool.k_codes[t].cpu().numpy(), ref.k_codes), s
         assert np.array_equal(pool.v_codes[t].cpu().numpy(), ref.v_codes), s
         assert np.array_equal(pool.v_scale[t].cpu().numpy().view(np.uint16), ref.v_scale.view(np.uint16)), s
+
+
+def test_gqa70b_full():
+    setup = _run("gqa70b", samples=[0, 64, 127])
+    assert setup.w.num_q_heads // setup.w.num_kv_heads == 8

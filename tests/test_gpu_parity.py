@@ -230,3 +230,37 @@ def test_fork_copy_on_write(vc):
     ref_parent = paged.PoolArrays(N, h, bs, d, vc == "i4")
     paged.store_range(ref_parent, model.table(parent)[0], hp_k, hp_v, 0, pre)
     assert_pool_equal(pool, ref_parent, blocks=model.table(parent)[0])
+
+
+GQA_SHAPES = [
+    # (block_size, head_dim, v codec, query heads per KV head, KV heads)
+    (32, 128, "i4", 8, 2),
+    (16, 128, "i8", 4, 2),
+    (32, 64, "i8", 16, 1),
+    (16, 64, "i4", 2, 3),
+    (32, 128, "i8", 32, 1),
+    (16, 128, "i4", 7, 2),
+]
+
+
+@pytest.mark.parametrize("bs,d,vc,g,hkv", GQA_SHAPES)
+def test_gqa_ragged(bs, d, vc, g, hkv):
+    """Grouped-query heads (the MFMA path), ragged contexts, several
+    partition sizes including ones that split inside a 32-token step."""
+    announce("gqa", bs, d, vc, g, hkv)
+    ctx = [1, 31, 32, 33, bs + 7, 300, 1027]
+    case = normal_case(ctx, g * hkv, hkv, d, bs, vc, seed=7 * bs + d + g)
+    case.store_all()
+    assert_pool_equal(case.pool, case.opool)
+    ref = case.reference()
+    for part in (0, 32, 96, 256):
+        assert_close(case.decode(part), ref, f"gqa bs{bs} d{d} {vc} g{g} part{part}")
+
+
+def test_gqa_rejects_partition_not_multiple_of_32():
+    announce("gqa-partition-check")
+    from paged_block_quantized_amd import PBQError
+    case = normal_case([40], 4, 2, 64, 16, "i8", seed=3)
+    case.store_all()
+    with pytest.raises(PBQError, match="multiple of 32"):
+        case.decode(16)

@@ -42,7 +42,9 @@ def test_rows_beyond_context_are_zero_and_ignored():
     rng = np.random.default_rng(1)
     pool, tables, hist = _fill(rng, [5], 1, 64, 16, 4, True, None)
     b = tables[0][0]
-    assert not pool.k_codes[b, :, 5:].any() and not pool.v_codes[b, :, 5:].any()
+    assert not pool.k_codes[b, :, 5:].any()
+    vt = quant.unpack_int4(pool.v_codes[b])          # [H, D, bs], dim-major V tile
+    assert not vt[:, :, 5:].any() and vt[:, :, :5].any()
 
 
 def test_permutation_invariance():
@@ -148,3 +150,26 @@ def test_tiny_config_end_to_end_quantized():
     k0, v0 = hist[0]
     c, sc = quant.quantize_int8_sym(v0[:, 0, :])
     assert np.array_equal(out[0, 0], quant.dequantize_int8_sym(c, sc)[0])
+
+
+def test_v_tile_layout_dim_major():
+    """V tiles are stored [head_dim, block_size] per (block, head); INT4 packs
+    two consecutive tokens per byte with the earlier token in the low nibble.
+    Values are chosen so that the scale is exactly 1 and the codes are known."""
+    bs, d = 16, 64
+    k = np.zeros((bs, 1, d), np.float16)
+    v = np.zeros((bs, 1, d), np.float16)
+    v[0, 0, 0] = 127.0                          # absmax 127 -> INT8 scale 1
+    v[:, 0, 3] = np.arange(1, bs + 1)           # dim 3 holds token index + 1
+    pool = paged.PoolArrays(2, 1, bs, d, False)
+    paged.store_block(pool, 1, k, v)
+    assert float(pool.v_scale[1, 0]) == 1.0
+    assert pool.v_codes[1, 0, 3].tolist() == list(range(1, bs + 1))
+    assert pool.v_codes[1, 0, 0, 0] == 127 and not pool.v_codes[1, 0, 0, 1:].any()
+    v4 = np.zeros((bs, 1, d), np.float16)
+    v4[:, 0, 5] = np.arange(bs) % 16            # lo 0, hi 15 -> scale 1, zp 0
+    pool4 = paged.PoolArrays(2, 1, bs, d, True)
+    paged.store_block(pool4, 0, k, v4)
+    assert float(pool4.v_scale[0, 0]) == 1.0 and int(pool4.v_zp[0, 0]) == 0
+    assert pool4.v_codes[0, 0, 5].tolist() == [(2 * j) | ((2 * j + 1) << 4) for j in range(bs // 2)]
+    assert not pool4.v_codes[0, 0, 4].any()
