@@ -96,6 +96,8 @@ def main():
     ap.add_argument("--workload", default="llama7b")
     ap.add_argument("--partition", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--rotate", type=int, default=4,
+                    help="copies of the pool the timed steps cycle through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -121,29 +123,44 @@ def main():
     dbytes = runner.decode_bytes(w, setup.ctx)
     sbytes = runner.store_step_bytes(w, setup.ctx)
 
-    for _ in range(args.warmup):
-        setup.step()
+    # The timed steps cycle through R copies of the pool at different
+    # addresses, as the layers of a model would, so no step finds its codes in
+    # a cache left by the step before (the 256 MB last-level cache is far
+    # smaller than R copies).
+    R = max(1, args.rotate)
+    if R > 1:
+        setup.add_replicas(R - 1)
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        setup.step(r=i % R)
     torch.cuda.synchronize()
+
+    def timed(steps, rot):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(steps)] for _ in range(3)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            r = i % rot
+            ev[0][i].record(stream)
+            setup.store_current(r=r)
+            ev[1][i].record(stream)
+            setup.attend(r=r)
+            ev[2][i].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        st = np.array([ev[0][i].elapsed_time(ev[1][i]) for i in range(steps)])
+        de = np.array([ev[1][i].elapsed_time(ev[2][i]) for i in range(steps)])
+        return (t1 - t0) * 1e3 / steps, st, de
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(K)] for _ in range(3)]
-    stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[0][i].record(stream)
-        setup.store_current()
-        ev[1][i].record(stream)
-        setup.attend()
-        ev[2][i].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / K
-    store_ms = float(np.mean([ev[0][i].elapsed_time(ev[1][i]) for i in range(K)]))
-    dec = np.array([ev[1][i].elapsed_time(ev[2][i]) for i in range(K)])
+    ms_step, st_ms, dec = timed(K, R)
+    store_ms = float(np.mean(st_ms))
     dec_ms = float(np.mean(dec))
+    print(f"timed {K} steps over {R} pool copies: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+    # context: the same pool every step (its codes partly in the last-level cache)
+    _, _, dec_same = timed(min(K, 20), 1)
 
-    # decode with a 1 GiB cache-clearing write before each call (outside the events)
+    # context: decode after a 1 GiB cache-clearing write (outside the events)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     fl = []
     for _ in range(10):
@@ -180,6 +197,7 @@ def main():
             "block_size": w.block_size, "k_codec": "int8_sym",
             "v_codec": "int4_asym" if w.v_codec == "i4" else "int8_sym",
             "partition": setup.partition, "shared_prefix": w.prefix,
+            "pool_copies_rotated": R,
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s_per_layer": round(S / (ms_step * 1e-3), 1),
@@ -188,6 +206,7 @@ def main():
                        "paged_attn_decode": round(dec_ms, 5),
                        "paged_attn_decode_p10": round(float(np.percentile(dec, 10)), 5),
                        "paged_attn_decode_p90": round(float(np.percentile(dec, 90)), 5),
+                       "paged_attn_decode_same_pool_back_to_back": round(float(np.mean(dec_same)), 5),
                        "paged_attn_decode_after_1GiB_flush": round(float(np.median(fl)), 5)},
         "roofline": {
             "kernel": "paged_attn_decode (split-K partition kernel + log-sum-exp reduce, one call)",

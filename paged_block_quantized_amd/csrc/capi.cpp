@@ -5,6 +5,7 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <cmath>
 #include <string>
 
@@ -51,6 +52,28 @@ kv_status hip_status(hipError_t e, const char* what) {
 }
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+// Compute units of the current device, cached per device; 256 (MI355X) when
+// no device can be queried.
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        n = 256;
+    }
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 }  // namespace
 
@@ -155,11 +178,22 @@ kv_status kv_quantize_store(const kv_pool_desc* d, const kv_pool_mem* m,
 
 int32_t paged_attn_default_partition(const kv_pool_desc* d, int32_t num_seqs,
                                      int32_t num_q_heads, int32_t max_context_len) {
-    if (!d || d->block_size < 1) return 0;
-    (void)num_seqs;
-    (void)num_q_heads;
-    (void)max_context_len;
-    return 512;  // a multiple of 16 and 32
+    if (!d || d->block_size < 1 || d->num_kv_heads < 1 || num_seqs < 1 || num_q_heads < 1) return 0;
+    // Work groups: one per (sequence, head) for one query head per KV head,
+    // one per (sequence, KV head, tile of 16 query heads) otherwise.
+    const int64_t group = num_q_heads / d->num_kv_heads;
+    const int64_t units = (int64_t)num_seqs *
+                          (group == 1 ? num_q_heads : (int64_t)d->num_kv_heads * pbq::ceil_div(group, 16));
+    const int64_t target = 4 * (int64_t)pbq::device_cu_count();
+    const int32_t ctx = max_context_len > 0 ? max_context_len : 1;
+    // A single pass (no reduce kernel, no workspace) when the units alone give
+    // enough work groups and each stays within 4096 tokens; otherwise
+    // 2048-token partitions, halved (down to 256) while the grid is too small
+    // to fill the GPU.  Partitions are multiples of 32 tokens.
+    if (units >= target && ctx <= 4096) return (int32_t)pbq::ceil_div(ctx, 32) * 32;
+    int32_t part = 2048;
+    while (part > 256 && units * pbq::ceil_div(ctx, part) < target) part /= 2;
+    return part;
 }
 
 size_t paged_attn_workspace_bytes(const kv_pool_desc* d, int32_t num_seqs,

@@ -68,6 +68,50 @@ __device__ __forceinline__ f16x2 perm_hi(uint32_t w) { return as_h2(__builtin_am
 #define PBQ_MHA_WAVES_PER_EU 1
 #endif
 
+// Software pipeline over cnt >= 1 steps: the codes of the next DEPTH-1 steps
+// are in flight while one step is computed.  Every load outside the short
+// tail is unconditional (the prologue loads step cnt-1 again when
+// cnt < DEPTH, a cache hit), because a load under a branch makes the
+// compiler's wait at the join cover every outstanding load, the prefetched
+// ones included.  first() runs once, after the first step's loads are issued.
+template <int DEPTH, class Regs, class Load, class Compute, class First>
+__device__ __forceinline__ void pipelined(int cnt, Load&& load, Compute&& compute, First&& first) {
+    Regs r[DEPTH];
+    load(0, r[0]);
+    first();
+#pragma unroll
+    for (int k = 1; k < DEPTH; ++k) load(min(k, cnt - 1), r[k]);
+    int i = 0;
+    for (; i + 2 * DEPTH <= cnt; i += DEPTH) {
+#pragma unroll
+        for (int k = 0; k < DEPTH; ++k) {
+            compute(r[k], i + k);
+            load(i + k + DEPTH, r[k]);
+        }
+    }
+    // fewer than 2 DEPTH steps remain; r[k] holds step i + k
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) {
+        if (i + k < cnt) {
+            compute(r[k], i + k);
+            if (i + k + DEPTH < cnt) load(i + k + DEPTH, r[k]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k)
+        if (i + DEPTH + k < cnt) compute(r[k], i + DEPTH + k);
+}
+
+#ifndef PBQ_HEAD_FASTEST
+#define PBQ_HEAD_FASTEST 0
+#endif
+#ifndef PBQ_MHA_DEPTH
+#define PBQ_MHA_DEPTH 2
+#endif
+#ifndef PBQ_GQA_DEPTH
+#define PBQ_GQA_DEPTH 2
+#endif
+
 // MHA partition kernel.  K tiles are token-major [bs, D]: lane l owns dims
 // (l % (D/16)) * 16 .. +16 of rows r * (64 / (D/16)) + l / (D/16).  V tiles are
 // dim-major [D, bs]: lane l owns dims l + 64 k (k < D/64), each a contiguous
@@ -93,8 +137,13 @@ void attn_partition_mha(AttnArgs a) {
 
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
+#if PBQ_HEAD_FASTEST
+    const int h = blockIdx.x;
+    const int p = blockIdx.y;
+#else
     const int p = blockIdx.x;
     const int h = blockIdx.y;
+#endif
     const int s = blockIdx.z;
     const int H = a.num_kv_heads;
     const int ctx = a.context_lens[s];
@@ -137,7 +186,10 @@ void attn_partition_mha(AttnArgs a) {
         const int bi = base + lane * NW;
         const int id = bi < b1 ? tab[bi] : 0;
         const int cnt = min(64, (b1 - base + NW - 1) / NW);
-        float sk = 0.f, sv = 0.f, vb = kI8Bias;
+        // raw fp16 scale bits and zero point, converted where they are used
+        // (any arithmetic here would make the first step's wait cover the
+        // prefetched codes too)
+        int sk = 0, sv = 0, zp = 0;
 
         auto load = [&](int i, Regs& r) {
             const int phys = readlane(id, i);
@@ -168,7 +220,7 @@ void attn_partition_mha(AttnArgs a) {
 
         auto compute = [&](const Regs& r, int i) {
             const int blk = base + i * NW;
-            const float skc = readlane(sk, i);
+            const float skc = bits_to_f16f((uint16_t)readlane(sk, i)) * c2;
             float sc[NR];
 #pragma unroll
             for (int j = 0; j < NR; ++j) {
@@ -202,8 +254,8 @@ void attn_partition_mha(AttnArgs a) {
                 zacc *= alpha;
                 m = bmax;
             }
-            const float svv = readlane(sv, i);
-            const float vbias = readlane(vb, i);
+            const float svv = bits_to_f16f((uint16_t)readlane(sv, i));
+            const float vbias = V4 ? kI4Bias + (float)readlane(zp, i) : kI8Bias;
             float pv[NR];
 #pragma unroll
             for (int j = 0; j < NR; ++j) {
@@ -251,23 +303,17 @@ void attn_partition_mha(AttnArgs a) {
             }
         };
 
-        // ping-pong: the next block's codes are in flight while one is computed
-        Regs rA, rB;
-        load(0, rA);
-        if (bi < b1) {
+        // scales of the staged blocks (zeroed past the end, so that stale pool
+        // contents cannot reach the sums); issued after the first codes
+        // only the wave's own blocks (i < cnt) are ever read back, so lanes
+        // past the end may hold any finite or non-finite value
+        auto scales = [&]() {
             const int64_t t = (int64_t)id * H + h;
-            sk = bits_to_f16f(a.k_scale[t]) * c2;
-            sv = bits_to_f16f(a.v_scale[t]);
-            if constexpr (V4) vb = kI4Bias + (float)a.v_zp[t];
-        }
-        int i = 0;
-        for (; i + 1 < cnt; i += 2) {
-            load(i + 1, rB);
-            compute(rA, i);
-            if (i + 2 < cnt) load(i + 2, rA);
-            compute(rB, i + 1);
-        }
-        if (i < cnt) compute(rA, i);
+            sk = a.k_scale[t];
+            sv = a.v_scale[t];
+            if constexpr (V4) zp = a.v_zp[t];
+        };
+        pipelined<PBQ_MHA_DEPTH, Regs>(cnt, load, compute, scales);
     }
 
     // every token row is held by LPR lanes: full-wave sums count it LPR times
@@ -331,6 +377,10 @@ void attn_partition_mha(AttnArgs a) {
 // A lane group g therefore touches the tokens 8g..8g+7 of the step, i.e. one
 // block (bs 32) or block g/2 (bs 16): its V scale, zero point and K scale are
 // per-lane values.
+#ifndef PBQ_GQA_WAVES_PER_EU
+#define PBQ_GQA_WAVES_PER_EU 3
+#endif
+
 template <bool V4>
 __device__ __forceinline__ int kappa(int j) {
     if constexpr (V4) return (j & 4) ? 2 * (j & 3) + 1 : 2 * (j & 3);
@@ -346,12 +396,13 @@ __device__ __forceinline__ uint32_t pk_sub_f16(uint32_t x, uint32_t off2) {
 }
 
 template <int BS, int D, bool V4, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_partition_gqa(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA_WAVES_PER_EU))) void attn_partition_gqa(AttnArgs a) {
     static_assert(BS == 16 || BS == 32, "block size");
     constexpr int KS = D / 32;                 // QK k-steps
     constexpr int DT = D / 16;                 // PV dim tiles
     constexpr int KCH = D / 4;                 // K bytes per lane per row
     constexpr int BPS = 32 / BS;               // blocks per 32-token step
+    constexpr int SPB = 64 / BPS;              // steps whose block ids one wave stages at once
     constexpr int VB = V4 ? 4 : 8;             // V bytes per lane per dim tile
     constexpr int VROW = V4 ? BS / 2 : BS;     // V bytes per dim row
     constexpr int KT = BS * D;
@@ -361,11 +412,17 @@ __global__ __launch_bounds__(64 * NW) void attn_partition_gqa(AttnArgs a) {
     const int w = threadIdx.x >> 6;
     const int n16 = lane & 15;       // head (C/B layouts) or M row (A layout)
     const int grp = lane >> 4;       // lane group
-    const int p = blockIdx.x;
     const int G = a.num_q_heads / a.num_kv_heads;
     const int n_ht = (G + 15) / 16;
+#if PBQ_HEAD_FASTEST
+    const int p = blockIdx.y;
+    const int kvh = blockIdx.x / n_ht;
+    const int ht = blockIdx.x % n_ht;
+#else
+    const int p = blockIdx.x;
     const int kvh = blockIdx.y / n_ht;
     const int ht = blockIdx.y % n_ht;
+#endif
     const int s = blockIdx.z;
     const int H = a.num_kv_heads;
     const int ctx = a.context_lens[s];
@@ -378,6 +435,8 @@ __global__ __launch_bounds__(64 * NW) void attn_partition_gqa(AttnArgs a) {
     const int nsteps = (tok1 - tok0 + 31) / 32;
     const int head_base = kvh * G + ht * 16;
     const int nheads = min(16, G - ht * 16);
+    const int blk0 = tok0 / BS;
+    const int blk_end = (tok1 + BS - 1) / BS;
 
     // Q as the B operand of the QK product: lane (head n16, group grp) holds
     // q[n16][(D/4) grp + 8 j + i] for k-step j
@@ -407,7 +466,6 @@ __global__ __launch_bounds__(64 * NW) void attn_partition_gqa(AttnArgs a) {
     for (int t = 0; t < DT; ++t) acc[t] = (f32x4)0.f;
 
     const int32_t* tab = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-    const int blk0 = tok0 / BS;
     // the block (within a step) whose K row this lane loads for tile mt, and
     // the row inside it: token 8(n16/4) + kappa(4mt + n16%4)
     int krow[2], kblk[2];
@@ -425,129 +483,166 @@ __global__ __launch_bounds__(64 * NW) void attn_partition_gqa(AttnArgs a) {
         uint32_t v[DT][VB / 4];
     };
 
-    for (int st = w; st < nsteps; st += NW) {
-        const int sb = blk0 + st * BPS;        // first block of this step
-        // block ids of the step (lane-select between two for bs 16)
-        int ids[BPS];
+    // A wave takes the steps w, w + NW, ... of the partition.  Lane L stages
+    // the block id, scales and zero point of sub-block L % BPS of the wave's
+    // (L / BPS)-th step of the batch; the loop reads them with readlane.  The
+    // next step's codes are loaded before the current step is computed.
+    for (int base = w; base < nsteps; base += NW * SPB) {
+        const int st_l = base + (lane / BPS) * NW;
+        const int blk_l = blk0 + st_l * BPS + lane % BPS;
+        const bool ok_l = st_l < nsteps && blk_l < blk_end;
+        const int id_l = ok_l ? tab[blk_l] : 0;
+        const int cnt = min(SPB, (nsteps - base + NW - 1) / NW);
+        int sk_l, sv_l, zp_l = 0;   // raw scale bits and zero point (converted at use)
+
+        // Loads are unconditional: a block past the partition's end has id 0
+        // (any valid block); its tokens are masked, so its codes only meet
+        // zero softmax weights.  (Branches here would also make the compiler
+        // wait for every outstanding load, the prefetch included.)
+        auto load = [&](int i, Raw& r) {
+            int ids[BPS];
 #pragma unroll
-        for (int b = 0; b < BPS; ++b) ids[b] = sb + b < nblk ? tab[sb + b] : -1;
-        Raw r;
+            for (int b = 0; b < BPS; ++b) ids[b] = readlane(id_l, i * BPS + b);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int id = BPS == 1 ? ids[0] : (kblk[mt] ? ids[BPS - 1] : ids[0]);
-            const bool ok = id >= 0;
-            const int8_t* kp = a.k_codes + ((int64_t)(ok ? id : 0) * H + kvh) * KT + krow[mt] * D + KCH * grp;
+            for (int mt = 0; mt < 2; ++mt) {
+                const int id = BPS == 1 ? ids[0] : (kblk[mt] ? ids[BPS - 1] : ids[0]);
+                const int8_t* kp = a.k_codes + ((int64_t)id * H + kvh) * KT + krow[mt] * D + KCH * grp;
 #pragma unroll
-            for (int c = 0; c < KCH / 16; ++c) r.k[mt][c] = ok ? *(const u32x4*)(kp + 16 * c) : (u32x4)0u;
-        }
-        const int vid = BPS == 1 ? ids[0] : (my_blk ? ids[BPS - 1] : ids[0]);
-        const bool vok = vid >= 0;
-        {
-            const uint8_t* vp = a.v_codes + ((int64_t)(vok ? vid : 0) * H + kvh) * VT + vcol;
+                for (int c = 0; c < KCH / 16; ++c) r.k[mt][c] = *(const u32x4*)(kp + 16 * c);
+            }
+            const int vid = BPS == 1 ? ids[0] : (my_blk ? ids[BPS - 1] : ids[0]);
+            const uint8_t* vp = a.v_codes + ((int64_t)vid * H + kvh) * VT + vcol;
 #pragma unroll
             for (int t = 0; t < DT; ++t) {
                 const uint8_t* row = vp + (16 * t + n16) * VROW;
                 if constexpr (V4) {
-                    r.v[t][0] = vok ? *(const uint32_t*)row : 0u;
+                    r.v[t][0] = *(const uint32_t*)row;
                 } else {
-                    const u32x2 x = vok ? *(const u32x2*)row : (u32x2)0u;
+                    const u32x2 x = *(const u32x2*)row;
                     r.v[t][0] = x[0];
                     r.v[t][1] = x[1];
                 }
             }
-        }
-        float sk = 0.f, sv = 0.f, zpv = 0.f;
-        if (vok) {
-            const int64_t t = (int64_t)vid * H + kvh;
-            sk = bits_to_f16f(a.k_scale[t]) * c2;
-            sv = bits_to_f16f(a.v_scale[t]);
-            if constexpr (V4) zpv = (float)a.v_zp[t];
-        }
+        };
 
-        // ---- S^T = K_hat Q^T --------------------------------------------------
-        f32x4 sc[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            sc[mt] = (f32x4)0.f;
-#pragma unroll
-            for (int j = 0; j < KS; ++j) {
-                const uint32_t u0 = r.k[mt][j / 2][2 * (j & 1)] ^ 0x80808080u;
-                const uint32_t u1 = r.k[mt][j / 2][2 * (j & 1) + 1] ^ 0x80808080u;
-                const uint32_t a4[4] = {__builtin_amdgcn_perm(kF16Hi, u0, kSelLo), __builtin_amdgcn_perm(kF16Hi, u0, kSelHi),
-                                        __builtin_amdgcn_perm(kF16Hi, u1, kSelLo), __builtin_amdgcn_perm(kF16Hi, u1, kSelHi)};
-                const f16x8v aop = __builtin_bit_cast(f16x8v, a4);
-                sc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, qop[j], sc[mt], 0, 0, 0);
-            }
-        }
-        // lane (head n16, group grp): sc[mt][i] is token 8 grp + kappa(4 mt + i)
-        float x[8];
-        float bmax = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = tok0 + 32 * st + 8 * grp + kappa<V4>(4 * mt + i);
-                const float v = (sc[mt][i] - qbias) * sk;
-                x[4 * mt + i] = t < tok1 ? v : -INFINITY;
-                bmax = fmaxf(bmax, x[4 * mt + i]);
-            }
-        bmax = fmaxf(bmax, shfl_xor_f(bmax, 16));
-        bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
-        if (bmax > m) {   // per head; lanes of one head agree
-            const float alpha = __builtin_amdgcn_exp2f(m - bmax);
-#pragma unroll
-            for (int t = 0; t < DT; ++t) acc[t] *= alpha;
-            l *= alpha;
-            m = bmax;
-        }
-        uint32_t pw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(x[2 * e] - m);
-            const float p1 = __builtin_amdgcn_exp2f(x[2 * e + 1] - m);
-            l += p0 + p1;
-            const f16x2 h2 = f16x2{(_Float16)(p0 * sv), (_Float16)(p1 * sv)};
-            pw[e] = __builtin_bit_cast(uint32_t, h2);
-        }
-        const f16x8v pop = __builtin_bit_cast(f16x8v, pw);
-
-        // ---- O^T += V_hat^T P^T ------------------------------------------------
-        const _Float16 vo = (_Float16)((V4 ? kI4Bias : kI8Bias) + zpv);
-        const uint32_t off2 = __builtin_bit_cast(uint32_t, f16x2{vo, vo});
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-            uint32_t a4[4];
-            if constexpr (V4) {
-                const uint32_t wv = r.v[t][0];
-                const uint32_t lo = wv & 0x0F0F0F0Fu, hi = (wv >> 4) & 0x0F0F0F0Fu;
-                a4[0] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, lo, kSelLo), off2);
-                a4[1] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, lo, kSelHi), off2);
-                a4[2] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, hi, kSelLo), off2);
-                a4[3] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, hi, kSelHi), off2);
+        auto compute = [&](const Raw& r, int i) {
+            const int st = base + i * NW;
+            // per-lane scales of the block holding this lane group's tokens.
+            // The second block of a 16-token pair may lie past the end (its
+            // staged id is 0): its tokens are masked, and its scales are
+            // replaced by 0 so that stale pool contents cannot reach the sums.
+            float sk, sv, zpv;
+            if constexpr (BPS == 1) {
+                sk = bits_to_f16f((uint16_t)readlane(sk_l, i)) * c2;
+                sv = bits_to_f16f((uint16_t)readlane(sv_l, i));
+                zpv = (float)readlane(zp_l, i);
             } else {
-                const uint32_t u0 = r.v[t][0] ^ 0x80808080u, u1 = r.v[t][1] ^ 0x80808080u;
-                a4[0] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u0, kSelLo), off2);
-                a4[1] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u0, kSelHi), off2);
-                a4[2] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u1, kSelLo), off2);
-                a4[3] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u1, kSelHi), off2);
+                const bool live1 = blk0 + st * BPS + 1 < blk_end;
+                const int k0 = readlane(sk_l, 2 * i), k1 = live1 ? readlane(sk_l, 2 * i + 1) : 0;
+                const int v0 = readlane(sv_l, 2 * i), v1 = live1 ? readlane(sv_l, 2 * i + 1) : 0;
+                const int z0 = readlane(zp_l, 2 * i), z1 = live1 ? readlane(zp_l, 2 * i + 1) : 0;
+                sk = bits_to_f16f((uint16_t)(my_blk ? k1 : k0)) * c2;
+                sv = bits_to_f16f((uint16_t)(my_blk ? v1 : v0));
+                zpv = (float)(my_blk ? z1 : z0);
             }
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8v, a4), pop, acc[t], 0, 0, 0);
-        }
+
+            // ---- S^T = K_hat Q^T ----------------------------------------------
+            f32x4 sc[2];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                sc[mt] = (f32x4)0.f;
+#pragma unroll
+                for (int j = 0; j < KS; ++j) {
+                    const uint32_t u0 = r.k[mt][j / 2][2 * (j & 1)] ^ 0x80808080u;
+                    const uint32_t u1 = r.k[mt][j / 2][2 * (j & 1) + 1] ^ 0x80808080u;
+                    const uint32_t a4[4] = {__builtin_amdgcn_perm(kF16Hi, u0, kSelLo), __builtin_amdgcn_perm(kF16Hi, u0, kSelHi),
+                                            __builtin_amdgcn_perm(kF16Hi, u1, kSelLo), __builtin_amdgcn_perm(kF16Hi, u1, kSelHi)};
+                    const f16x8v aop = __builtin_bit_cast(f16x8v, a4);
+                    sc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, qop[j], sc[mt], 0, 0, 0);
+                }
+            }
+            // lane (head n16, group grp): sc[mt][i] is token 8 grp + kappa(4 mt + i)
+            float x[8];
+            float bmax = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = tok0 + 32 * st + 8 * grp + kappa<V4>(4 * mt + e);
+                    const float v = (sc[mt][e] - qbias) * sk;
+                    x[4 * mt + e] = t < tok1 ? v : -INFINITY;
+                    bmax = fmaxf(bmax, x[4 * mt + e]);
+                }
+            // every step holds at least one valid token, so bmax is finite
+            bmax = fmaxf(bmax, shfl_xor_f(bmax, 16));
+            bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
+            if (bmax > m) {   // per head; lanes of one head agree
+                const float alpha = __builtin_amdgcn_exp2f(m - bmax);
+#pragma unroll
+                for (int t = 0; t < DT; ++t) acc[t] *= alpha;
+                l *= alpha;
+                m = bmax;
+            }
+            uint32_t pw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = __builtin_amdgcn_exp2f(x[2 * e] - m);
+                const float p1 = __builtin_amdgcn_exp2f(x[2 * e + 1] - m);
+                l += p0 + p1;
+                const f16x2 h2 = f16x2{(_Float16)(p0 * sv), (_Float16)(p1 * sv)};
+                pw[e] = __builtin_bit_cast(uint32_t, h2);
+            }
+            const f16x8v pop = __builtin_bit_cast(f16x8v, pw);
+
+            // ---- O^T += V_hat^T P^T --------------------------------------------
+            const _Float16 vo = (_Float16)((V4 ? kI4Bias : kI8Bias) + zpv);
+            const uint32_t off2 = __builtin_bit_cast(uint32_t, f16x2{vo, vo});
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                uint32_t a4[4];
+                if constexpr (V4) {
+                    const uint32_t wv = r.v[t][0];
+                    const uint32_t lo = wv & 0x0F0F0F0Fu, hi = (wv >> 4) & 0x0F0F0F0Fu;
+                    a4[0] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, lo, kSelLo), off2);
+                    a4[1] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, lo, kSelHi), off2);
+                    a4[2] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, hi, kSelLo), off2);
+                    a4[3] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, hi, kSelHi), off2);
+                } else {
+                    const uint32_t u0 = r.v[t][0] ^ 0x80808080u, u1 = r.v[t][1] ^ 0x80808080u;
+                    a4[0] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u0, kSelLo), off2);
+                    a4[1] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u0, kSelHi), off2);
+                    a4[2] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u1, kSelLo), off2);
+                    a4[3] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u1, kSelHi), off2);
+                }
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8v, a4), pop, acc[t], 0, 0, 0);
+            }
+        };
+
+        auto scales = [&]() {
+            const int64_t t = (int64_t)id_l * H + kvh;
+            sk_l = a.k_scale[t];
+            sv_l = a.v_scale[t];
+            if constexpr (V4) zp_l = a.v_zp[t];
+        };
+        pipelined<PBQ_GQA_DEPTH, Raw>(cnt, load, compute, scales);
     }
     // lanes of one head split its tokens by group: sum their partial sums
     l += shfl_xor_f(l, 16);
     l += shfl_xor_f(l, 32);
 
-    __shared__ float s_acc[NW][16][D];
+    // Merge the waves' partial results in LDS.  Rows are padded by 4 floats
+    // so that the 16-byte writes of one instruction spread over the banks.
+    constexpr int DP = D + 4;
+    __shared__ float s_acc[NW][16][DP];
     __shared__ float s_ml[NW][16][2];
-    // acc[t][i] is (dim 16t + 4 grp + i, head n16)
+    if (n16 < nheads) {
+        // acc[t] holds dims 16t + 4 grp .. +3 of head n16
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s_acc[w][n16][16 * t + 4 * grp + i] = acc[t][i];
-    if (grp == 0) {
-        s_ml[w][n16][0] = m;
-        s_ml[w][n16][1] = l;
+        for (int t = 0; t < DT; ++t) *(f32x4*)&s_acc[w][n16][16 * t + 4 * grp] = acc[t];
+        if (grp == 0) {
+            s_ml[w][n16][0] = m;
+            s_ml[w][n16][1] = l;
+        }
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < nheads * D; idx += 64 * NW) {
@@ -634,15 +729,19 @@ __global__ __launch_bounds__(64) void attn_reduce(AttnArgs a) {
     for (int k = 0; k < PER; ++k) a.out[row * D + lane + 64 * k] = f32_to_f16_bits(L > 0.f ? o[k] / L : 0.f);
 }
 
-#ifndef PBQ_MHA_WAVES
-#define PBQ_MHA_WAVES 4
-#endif
-
+// Waves per work group of the MHA kernel: 8 when a partition holds at least
+// 64 blocks, else 4, so that each wave still streams several blocks.
 template <int BS, int D, bool V4>
 hipError_t launch_mha(const AttnArgs& a, hipStream_t stream) {
-    constexpr int NW = PBQ_MHA_WAVES;
+#if PBQ_HEAD_FASTEST
+    dim3 grid((unsigned)a.num_q_heads, (unsigned)a.max_partitions, (unsigned)a.num_seqs);
+#else
     dim3 grid((unsigned)a.max_partitions, (unsigned)a.num_q_heads, (unsigned)a.num_seqs);
-    hipLaunchKernelGGL((attn_partition_mha<BS, D, V4, NW>), grid, dim3(64 * NW), 0, stream, a);
+#endif
+    if (a.partition_blocks >= 64)
+        hipLaunchKernelGGL((attn_partition_mha<BS, D, V4, 8>), grid, dim3(64 * 8), 0, stream, a);
+    else
+        hipLaunchKernelGGL((attn_partition_mha<BS, D, V4, 4>), grid, dim3(64 * 4), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_partitions <= 1) return e;
     hipLaunchKernelGGL((attn_reduce<BS, D>), dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(64), 0,
@@ -650,12 +749,20 @@ hipError_t launch_mha(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+#ifndef PBQ_GQA_WAVES
+#define PBQ_GQA_WAVES 4
+#endif
+
 template <int BS, int D, bool V4>
 hipError_t launch_gqa(const AttnArgs& a, hipStream_t stream) {
-    constexpr int NW = 4;
+    constexpr int NW = PBQ_GQA_WAVES;
     const int G = a.num_q_heads / a.num_kv_heads;
     const int n_ht = (G + 15) / 16;
+#if PBQ_HEAD_FASTEST
+    dim3 grid((unsigned)(a.num_kv_heads * n_ht), (unsigned)a.max_partitions, (unsigned)a.num_seqs);
+#else
     dim3 grid((unsigned)a.max_partitions, (unsigned)(a.num_kv_heads * n_ht), (unsigned)a.num_seqs);
+#endif
     hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, NW>), grid, dim3(64 * NW), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_partitions <= 1) return e;

@@ -7,7 +7,7 @@
 
 #include <string>
 
-#include "../../include/pbq.h"
+#include "pbq.h"
 
 namespace pbq {
 

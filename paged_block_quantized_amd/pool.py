@@ -101,24 +101,38 @@ class KVPool:
         L.kv_copy_blocks(self.desc, self.mem, t, len(copies), stream)
         return t  # keep alive until the stream has consumed it
 
+    def replica(self):
+        """A copy of the pool's code, scale and zero-point arrays in fresh
+        device memory (tail slots shared), as a kv_pool_mem: the same cache
+        contents at other addresses, e.g. to stand for another layer's pool."""
+        keep = {n: (t if n.startswith("tail") or (n == "v_zp" and not self.v_int4) else t.clone())
+                for n, t in self.arrays.items()}
+        mem = L.kv_pool_mem(*[
+            None if (n == "v_zp" and not self.v_int4) else keep[n].data_ptr()
+            for n in ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "tail_k", "tail_v")])
+        return mem, keep
+
     def quantize_store(self, k, v, cu_seqlens, start_pos, block_tables, tail_slots,
-                       max_new_tokens, stream=None):
-        L.kv_quantize_store(self.desc, self.mem, k, v, cu_seqlens.numel() - 1, cu_seqlens,
-                            start_pos, block_tables, block_tables.shape[1], tail_slots,
-                            max_new_tokens, stream)
+                       max_new_tokens, stream=None, mem=None):
+        L.kv_quantize_store(self.desc, self.mem if mem is None else mem, k, v,
+                            cu_seqlens.numel() - 1, cu_seqlens, start_pos, block_tables,
+                            block_tables.shape[1], tail_slots, max_new_tokens, stream)
 
     def workspace_bytes(self, num_seqs, num_q_heads, max_context_len, partition_size=0):
         return L.paged_attn_workspace_bytes(self.desc, num_seqs, num_q_heads, max_context_len,
                                             partition_size)
 
+    def default_partition(self, num_seqs, num_q_heads, max_context_len):
+        return L.paged_attn_default_partition(self.desc, num_seqs, num_q_heads, max_context_len)
+
     def decode(self, q, out, block_tables, context_lens, max_context_len, sm_scale,
-               partition_size=0, workspace=None, stream=None):
+               partition_size=0, workspace=None, stream=None, mem=None):
         S, Hq, _ = q.shape
         need = self.workspace_bytes(S, Hq, max_context_len, partition_size)
         if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-        L.paged_attn_decode(self.desc, self.mem, q, out, S, Hq, block_tables,
-                            block_tables.shape[1], context_lens, max_context_len, sm_scale,
-                            partition_size, workspace, nbytes, stream)
+        L.paged_attn_decode(self.desc, self.mem if mem is None else mem, q, out, S, Hq,
+                            block_tables, block_tables.shape[1], context_lens, max_context_len,
+                            sm_scale, partition_size, workspace, nbytes, stream)
         return workspace

@@ -44,18 +44,28 @@ class DecodeSetup:
     max_ctx: int
     sm_scale: float
     partition: int
+    replicas: list = None       # [(kv_pool_mem, arrays)] copies of the pool
 
-    def store_current(self, stream=None):
+    def add_replicas(self, n):
+        """n more copies of the pool arrays at other addresses (each the same
+        cache contents), so that consecutive steps can read memory that no
+        earlier step has left in a cache, as the layers of a model would."""
+        self.replicas = (self.replicas or []) + [self.pool.replica() for _ in range(n)]
+
+    def _mem(self, r):
+        return None if not r else self.replicas[r - 1][0]
+
+    def store_current(self, stream=None, r=0):
         self.pool.quantize_store(self.k_new, self.v_new, self.cu_step, self.start_pos,
-                                 self.tables, self.slots, 1, stream)
+                                 self.tables, self.slots, 1, stream, mem=self._mem(r))
 
-    def attend(self, stream=None):
+    def attend(self, stream=None, r=0):
         self.pool.decode(self.q, self.out, self.tables, self.ctx_dev, self.max_ctx,
-                         self.sm_scale, self.partition, self.workspace, stream)
+                         self.sm_scale, self.partition, self.workspace, stream, mem=self._mem(r))
 
-    def step(self, stream=None):
-        self.store_current(stream)
-        self.attend(stream)
+    def step(self, stream=None, r=0):
+        self.store_current(stream, r)
+        self.attend(stream, r)
 
 
 def _store(pool, k, v, seq_ids, starts, device):
@@ -118,6 +128,8 @@ def setup_decode(w: W.Workload, device="cuda", chunk_seqs=8, partition=None) -> 
     assert np.array_equal(ctx_h.numpy(), ctx)
     part = w.partition if partition is None else partition
     max_ctx = int(ctx.max())
+    if not part:
+        part = pool.default_partition(S, w.num_q_heads, max_ctx)
     q = W.queries(w, device)
     out = torch.empty_like(q)
     ws_bytes = pool.workspace_bytes(S, w.num_q_heads, max_ctx, part)

@@ -60,9 +60,9 @@ WORKLOADS = {
     "tiny": Workload("tiny", 4, 2, 2, 64, 16, "i8", "list", (1, 17, 50, 100),
                      pool_blocks=64, seed=1),
     "llama7b": Workload("llama7b", 32, 32, 32, 128, 16, "i8", "fixed", (4096,),
-                        channel_sigma=0.5, partition=512, seed=2),
+                        channel_sigma=0.5, seed=2),
     "gqa70b": Workload("gqa70b", 128, 64, 8, 128, 32, "i4", "uniform", (500, 2000),
-                       outlier_frac=0.01, outlier_mult=8.0, partition=512, seed=3),
+                       outlier_frac=0.01, outlier_mult=8.0, seed=3),
     "prefill_store": Workload("prefill_store", 64, 32, 32, 128, 16, "i8", "fixed", (2048,),
                               pool_blocks=16384, seed=4),
     "shared_prefix": Workload("shared_prefix", 32, 32, 32, 128, 32, "i4", "fixed", (32768,),

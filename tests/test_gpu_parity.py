@@ -49,12 +49,13 @@ SHAPES = [(bs, d, vc) for bs in (16, 32) for d in (64, 128) for vc in ("i8", "i4
 @pytest.mark.parametrize("bs,d,vc", SHAPES)
 def test_shapes_ragged(bs, d, vc):
     announce("ragged", bs, d, vc)
-    ctx = [1, bs - 1, bs, bs + 1, 3 * bs + 5, 700, 257]
+    ctx = [1, bs - 1, bs, bs + 1, 3 * bs + 5, 700, 257, 2100]
     case = normal_case(ctx, 3, 3, d, bs, vc, seed=bs * 1000 + d + (vc == "i4"))
     case.store_all()
     assert_pool_equal(case.pool, case.opool)
     ref = case.reference()
-    for part in (0, bs, 4 * bs, 128 if bs == 16 else 256):
+    # 64 * bs: partitions of 64 blocks take the 8-wave kernel, with a reduce
+    for part in (0, bs, 4 * bs, 128 if bs == 16 else 256, 64 * bs):
         assert_close(case.decode(part), ref, f"ragged bs{bs} d{d} {vc} part{part}")
 
 
