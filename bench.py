@@ -13,7 +13,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 import argparse
 import dataclasses
-import hashlib
 import json
 import os
 import sys
@@ -24,14 +23,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "quantized-KV decode attention GB/s (% of HBM peak) + tokens/s per layer"
 
 
-def kernel_source_hash():
-    h = hashlib.sha256()
-    for f in ("paged_attn.hip", "device_common.h"):
-        with open(os.path.join(ROOT, "paged_block_quantized_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(workload):
     """HBM bytes per decode call from the committed rocprofv3 counter runs,
     or None when they are missing or were taken on a different kernel."""
@@ -40,9 +31,15 @@ def measured_traffic(workload):
         return None
     with open(path) as fh:
         rec = json.load(fh)
+    from paged_block_quantized_amd.traffic import kernel_source_hash
     if rec.get("kernel_hash") != kernel_source_hash():
         return None
     return rec.get("bytes_per_decode")
+
+
+def _r5(x):
+    x = float(x)
+    return round(x, 5) if x == x else None
 
 
 def cpu_baseline(setup, seconds):
@@ -99,6 +96,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=4,
                     help="copies of the pool the timed steps cycle through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-timed", action="store_true",
+                    help="skip the same-pool and cache-flush context measurements "
+                         "(for profiling the timed loop alone)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -157,21 +157,23 @@ def main():
     store_ms = float(np.mean(st_ms))
     dec_ms = float(np.mean(dec))
     print(f"timed {K} steps over {R} pool copies: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
-    # context: the same pool every step (its codes partly in the last-level cache)
-    _, _, dec_same = timed(min(K, 20), 1)
-
-    # context: decode after a 1 GiB cache-clearing write (outside the events)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    fl = []
-    for _ in range(10):
-        flush.zero_()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        setup.attend()
-        b.record(stream)
-        torch.cuda.synchronize()
-        fl.append(a.elapsed_time(b))
-    del flush
+    dec_same, fl = np.array([np.nan]), [np.nan]
+    if not args.only_timed:
+        # context: the same pool every step (its codes partly in the last-level cache)
+        _, _, dec_same = timed(min(K, 20), 1)
+        # context: decode after a 1 GiB cache-clearing write (outside the events);
+        # the write leaves dirty lines whose write-back slows the next reads
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        fl = []
+        for _ in range(10):
+            flush.zero_()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            setup.attend()
+            b.record(stream)
+            torch.cuda.synchronize()
+            fl.append(a.elapsed_time(b))
+        del flush
 
     step_bytes = dbytes + sbytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -206,8 +208,8 @@ def main():
                        "paged_attn_decode": round(dec_ms, 5),
                        "paged_attn_decode_p10": round(float(np.percentile(dec, 10)), 5),
                        "paged_attn_decode_p90": round(float(np.percentile(dec, 90)), 5),
-                       "paged_attn_decode_same_pool_back_to_back": round(float(np.mean(dec_same)), 5),
-                       "paged_attn_decode_after_1GiB_flush": round(float(np.median(fl)), 5)},
+                       "paged_attn_decode_same_pool_back_to_back": _r5(np.mean(dec_same)),
+                       "paged_attn_decode_after_1GiB_flush": _r5(np.median(fl))},
         "roofline": {
             "kernel": "paged_attn_decode (split-K partition kernel + log-sum-exp reduce, one call)",
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -210,6 +210,8 @@ kv_status kv_copy_blocks(const kv_pool_desc* desc, const kv_pool_mem* mem,
  *                  block up to position start + new - 1.
  *   tail_slots_dev int32 [num_seqs]: each sequence's tail slot.
  *   max_new_tokens >= every sequence's new-token count (sizes the grid).
+ *   num_seqs and ceil((block_size - 1 + max_new_tokens) / block_size) must
+ *   stay below 65536 (launch grid limits); KV_ERR_INVALID otherwise.
  * Every (block, head) touched is re-quantized from the exact fp16 rows it
  * holds: rows before start_pos come from the tail slot, the rest from k/v.
  * When a sequence's last touched block stays partial, its new rows are also
@@ -243,10 +245,11 @@ size_t paged_attn_workspace_bytes(const kv_pool_desc* desc, int32_t num_seqs,
  *   partition_size: tokens per split-K partition, a multiple of block_size
  *   (and of 32 when num_q_heads > Hkv), or 0 to let the library choose.
  *   One query head per KV head runs on the vector ALUs; grouped query heads
- *   (up to 16 per KV head, or a multiple of 16) run on MFMA.  Partitions are combined by a second
- *   log-sum-exp kernel.  workspace_dev (16-byte aligned, workspace_bytes >=
- *   paged_attn_workspace_bytes(...)) may be NULL when that is 0.
- *   num_q_heads must be a multiple of Hkv. */
+ *   (up to 16 per KV head, or a multiple of 16) run on MFMA.  Partitions
+ *   are combined by a second log-sum-exp kernel.  workspace_dev (16-byte
+ *   aligned, workspace_bytes >= paged_attn_workspace_bytes(...)) may be NULL
+ *   when that is 0.  num_q_heads must be a multiple of Hkv; num_seqs and
+ *   num_q_heads must stay below 65536 (launch grid limits). */
 kv_status paged_attn_decode(const kv_pool_desc* desc, const kv_pool_mem* mem,
                             const uint16_t* q_dev, uint16_t* out_dev,
                             int32_t num_seqs, int32_t num_q_heads,
@@ -257,7 +260,12 @@ kv_status paged_attn_decode(const kv_pool_desc* desc, const kv_pool_mem* mem,
                             int32_t partition_size, void* workspace_dev,
                             size_t workspace_bytes, void* stream);
 
-/* Partition size (tokens) paged_attn_decode uses when given 0. */
+/* Partition size (tokens) paged_attn_decode uses when given 0: a single
+ * pass when num_seqs x (heads, or KV heads x 16-head tiles) gives at least
+ * four work groups per compute unit of the current device and every context
+ * fits in 4096 tokens; otherwise 2048 tokens, halved (down to 256) while the
+ * grid would have fewer work groups than that.  Always a multiple of 32;
+ * 0 for invalid arguments. */
 int32_t paged_attn_default_partition(const kv_pool_desc* desc,
                                      int32_t num_seqs, int32_t num_q_heads,
                                      int32_t max_context_len);

@@ -171,8 +171,10 @@ kv_status kv_quantize_store(const kv_pool_desc* d, const kv_pool_mem* m,
     // a run of n tokens starting anywhere inside a block spans at most
     // ceil((bs - 1 + n) / bs) blocks
     a.tiles_per_seq = pbq::ceil_div((int64_t)d->block_size - 1 + max_new_tokens, d->block_size);
-    if ((int64_t)a.tiles_per_seq * num_seqs * d->num_kv_heads > (int64_t)INT32_MAX * 4)
-        return fail(KV_ERR_INVALID, "store too large for one launch");
+    // launch grid: (KV heads / 4, blocks per sequence, sequences)
+    if (a.tiles_per_seq > 65535 || num_seqs > 65535)
+        return fail(KV_ERR_INVALID, "store too large for one launch (max_new_tokens / block_size and "
+                                    "num_seqs must stay below 65536)");
     return pbq::hip_status(pbq::launch_quantize_store(a, (hipStream_t)stream), "kv_quantize_store launch");
 }
 
@@ -227,6 +229,8 @@ kv_status paged_attn_decode(const kv_pool_desc* d, const kv_pool_mem* m,
     if (num_q_heads / d->num_kv_heads > 16 && (num_q_heads / d->num_kv_heads) % 16 != 0)
         return fail(KV_ERR_INVALID, "query-group sizes above 16 must be multiples of 16");
     if (num_seqs == 0) return KV_OK;
+    if (num_seqs > 65535 || num_q_heads > 65535)
+        return fail(KV_ERR_INVALID, "num_seqs and num_q_heads must stay below 65536");
     if (!q || !out || !pbq::aligned16(q) || !pbq::aligned16(out))
         return fail(KV_ERR_INVALID, "q and out must be non-NULL and 16-byte aligned");
     if (!block_tables || !context_lens) return fail(KV_ERR_INVALID, "index arrays must be non-NULL");

@@ -91,6 +91,49 @@ __device__ __forceinline__ float strided_max(float x) {
     return x;
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+// Wave-wide reductions with a wave-uniform (scalar) result: DPP within each
+// row of 16 lanes, then the four row results read with readlane.
+__device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t x) {
+    x = max(x, dpp_u<kDppQuadXor1>(x));
+    x = max(x, dpp_u<kDppQuadXor2>(x));
+    x = max(x, dpp_u<kDppHalfMirror>(x));
+    x = max(x, dpp_u<kDppRowRor8>(x));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+    return max(max(a, b), max(c, d));
+}
+
+__device__ __forceinline__ float wave_max_uniform(float x) {
+    x = fmaxf(x, dpp<kDppQuadXor1>(x));
+    x = fmaxf(x, dpp<kDppQuadXor2>(x));
+    x = fmaxf(x, dpp<kDppHalfMirror>(x));
+    x = fmaxf(x, dpp<kDppRowRor8>(x));
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+__device__ __forceinline__ float wave_min_uniform(float x) {
+    x = fminf(x, dpp<kDppQuadXor1>(x));
+    x = fminf(x, dpp<kDppQuadXor2>(x));
+    x = fminf(x, dpp<kDppHalfMirror>(x));
+    x = fminf(x, dpp<kDppRowRor8>(x));
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+    return fminf(fminf(a, b), fminf(c, d));
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));

@@ -102,9 +102,33 @@ __device__ __forceinline__ void pipelined(int cnt, Load&& load, Compute&& comput
         if (i + DEPTH + k < cnt) compute(r[k], i + DEPTH + k);
 }
 
-#ifndef PBQ_HEAD_FASTEST
-#define PBQ_HEAD_FASTEST 0
+// Work-group order of the partition kernels: 0 = partition fastest, then
+// head, then sequence; 1 = head, partition, sequence; 2 = head, sequence,
+// partition (every sequence's first partition is dispatched before any
+// second one, so the short, partial last partitions come at the end).
+#ifndef PBQ_GRID_ORDER
+#define PBQ_GRID_ORDER 0
 #endif
+
+__device__ __forceinline__ void grid_coords(int& p, int& h, int& s) {
+#if PBQ_GRID_ORDER == 0
+    p = blockIdx.x; h = blockIdx.y; s = blockIdx.z;
+#elif PBQ_GRID_ORDER == 1
+    h = blockIdx.x; p = blockIdx.y; s = blockIdx.z;
+#else
+    h = blockIdx.x; s = blockIdx.y; p = blockIdx.z;
+#endif
+}
+
+inline dim3 grid_dims(int parts, int heads, int seqs) {
+#if PBQ_GRID_ORDER == 0
+    return dim3((unsigned)parts, (unsigned)heads, (unsigned)seqs);
+#elif PBQ_GRID_ORDER == 1
+    return dim3((unsigned)heads, (unsigned)parts, (unsigned)seqs);
+#else
+    return dim3((unsigned)heads, (unsigned)seqs, (unsigned)parts);
+#endif
+}
 #ifndef PBQ_MHA_DEPTH
 #define PBQ_MHA_DEPTH 2
 #endif
@@ -137,14 +161,8 @@ void attn_partition_mha(AttnArgs a) {
 
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-#if PBQ_HEAD_FASTEST
-    const int h = blockIdx.x;
-    const int p = blockIdx.y;
-#else
-    const int p = blockIdx.x;
-    const int h = blockIdx.y;
-#endif
-    const int s = blockIdx.z;
+    int p, h, s;
+    grid_coords(p, h, s);
     const int H = a.num_kv_heads;
     const int ctx = a.context_lens[s];
     const int nblk = (ctx + BS - 1) / BS;
@@ -414,16 +432,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
     const int grp = lane >> 4;       // lane group
     const int G = a.num_q_heads / a.num_kv_heads;
     const int n_ht = (G + 15) / 16;
-#if PBQ_HEAD_FASTEST
-    const int p = blockIdx.y;
-    const int kvh = blockIdx.x / n_ht;
-    const int ht = blockIdx.x % n_ht;
-#else
-    const int p = blockIdx.x;
-    const int kvh = blockIdx.y / n_ht;
-    const int ht = blockIdx.y % n_ht;
-#endif
-    const int s = blockIdx.z;
+    int p, tile, s;
+    grid_coords(p, tile, s);
+    const int kvh = tile / n_ht;
+    const int ht = tile % n_ht;
     const int H = a.num_kv_heads;
     const int ctx = a.context_lens[s];
     const int nblk = (ctx + BS - 1) / BS;
@@ -438,18 +450,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
     const int blk0 = tok0 / BS;
     const int blk_end = (tok1 + BS - 1) / BS;
 
-    // Q as the B operand of the QK product: lane (head n16, group grp) holds
-    // q[n16][(D/4) grp + 8 j + i] for k-step j
+    // Q as the B operand of the QK product.  The contraction index of k-step
+    // j, lane group grp, element i is head dim 64 (j/2) + 16 grp + 8 (j%2) + i,
+    // so that a lane's K codes for two k-steps are 16 contiguous bytes and
+    // the four lane groups of one row read 64 contiguous bytes.
     f16x8v qop[KS];
     float qbias;
     {
         float qs = 0.f;
         const bool live = n16 < nheads;
-        const uint16_t* qp = a.q + ((int64_t)s * a.num_q_heads + head_base + n16) * D + KCH * grp;
+        const uint16_t* qp = a.q + ((int64_t)s * a.num_q_heads + head_base + n16) * D + 16 * grp;
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
             f16x8v x = (f16x8v)(_Float16)0;
-            if (live) x = *(const f16x8v*)(qp + 8 * j);
+            if (live) x = *(const f16x8v*)(qp + 64 * (j / 2) + 8 * (j % 2));
             qop[j] = x;
 #pragma unroll
             for (int i = 0; i < 8; ++i) qs += (float)x[i];
@@ -506,9 +520,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 const int id = BPS == 1 ? ids[0] : (kblk[mt] ? ids[BPS - 1] : ids[0]);
-                const int8_t* kp = a.k_codes + ((int64_t)id * H + kvh) * KT + krow[mt] * D + KCH * grp;
+                const int8_t* kp = a.k_codes + ((int64_t)id * H + kvh) * KT + krow[mt] * D + 16 * grp;
 #pragma unroll
-                for (int c = 0; c < KCH / 16; ++c) r.k[mt][c] = *(const u32x4*)(kp + 16 * c);
+                for (int c = 0; c < KCH / 16; ++c) r.k[mt][c] = *(const u32x4*)(kp + 64 * c);
             }
             const int vid = BPS == 1 ? ids[0] : (my_blk ? ids[BPS - 1] : ids[0]);
             const uint8_t* vp = a.v_codes + ((int64_t)vid * H + kvh) * VT + vcol;
@@ -733,11 +747,7 @@ __global__ __launch_bounds__(64) void attn_reduce(AttnArgs a) {
 // 64 blocks, else 4, so that each wave still streams several blocks.
 template <int BS, int D, bool V4>
 hipError_t launch_mha(const AttnArgs& a, hipStream_t stream) {
-#if PBQ_HEAD_FASTEST
-    dim3 grid((unsigned)a.num_q_heads, (unsigned)a.max_partitions, (unsigned)a.num_seqs);
-#else
-    dim3 grid((unsigned)a.max_partitions, (unsigned)a.num_q_heads, (unsigned)a.num_seqs);
-#endif
+    const dim3 grid = grid_dims(a.max_partitions, a.num_q_heads, a.num_seqs);
     if (a.partition_blocks >= 64)
         hipLaunchKernelGGL((attn_partition_mha<BS, D, V4, 8>), grid, dim3(64 * 8), 0, stream, a);
     else
@@ -749,21 +759,17 @@ hipError_t launch_mha(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-#ifndef PBQ_GQA_WAVES
-#define PBQ_GQA_WAVES 4
-#endif
-
+// Waves per work group of the grouped-query kernel: 2 for a single pass (the
+// sequences' work groups then all fit on the GPU at once), else 4.
 template <int BS, int D, bool V4>
 hipError_t launch_gqa(const AttnArgs& a, hipStream_t stream) {
-    constexpr int NW = PBQ_GQA_WAVES;
     const int G = a.num_q_heads / a.num_kv_heads;
     const int n_ht = (G + 15) / 16;
-#if PBQ_HEAD_FASTEST
-    dim3 grid((unsigned)(a.num_kv_heads * n_ht), (unsigned)a.max_partitions, (unsigned)a.num_seqs);
-#else
-    dim3 grid((unsigned)a.max_partitions, (unsigned)(a.num_kv_heads * n_ht), (unsigned)a.num_seqs);
-#endif
-    hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, NW>), grid, dim3(64 * NW), 0, stream, a);
+    const dim3 grid = grid_dims(a.max_partitions, a.num_kv_heads * n_ht, a.num_seqs);
+    if (a.max_partitions == 1)
+        hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, 2>), grid, dim3(64 * 2), 0, stream, a);
+    else
+        hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, 4>), grid, dim3(64 * 4), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_partitions <= 1) return e;
     hipLaunchKernelGGL((attn_reduce<BS, D>), dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(64), 0,

@@ -18,8 +18,11 @@
 //
 // Mapping: one wavefront per (sequence, touched block, KV head); a workgroup
 // of four waves takes four consecutive heads of one block, so each token row
-// is read as 4 x D x 2 contiguous bytes.  K tiles are token-major
-// ([block_size, D] codes): lane l holds rows it * (64 / (D/8)) + l / (D/8) and
+// is read as 4 x D x 2 contiguous bytes.  All of a wave's fp16 rows are
+// loaded before any arithmetic, and reductions use DPP within rows of 16
+// lanes plus readlane, so a store is a short chain: the sequence's scalars,
+// the rows (with the block id beside them), the reductions, the codes.
+// K tiles are token-major ([block_size, D] codes): lane l holds rows it * (64 / (D/8)) + l / (D/8) and
 // dims (l % (D/8)) * 8 .. + 8.  V tiles are dim-major ([D, block_size] codes,
 // INT4 packing two consecutive tokens per byte): lane l holds the D/64
 // adjacent dims starting at l * D/64 of every row, so each fp16 row read and
@@ -55,40 +58,63 @@ __global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
     constexpr int LPR = D / 8;     // lanes per token row
     constexpr int RPI = 64 / LPR;  // rows per wave access
     constexpr int NIT = BS / RPI;  // accesses per lane per tensor
+    constexpr int DPL = D / 64;    // V: dims per lane
     const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int H = a.num_kv_heads;
-    const int g = (int)(wave % H);
-    const int64_t rest = wave / H;
-    const int jj = (int)(rest % a.tiles_per_seq);
-    const int64_t s = rest / a.tiles_per_seq;
-    if (s >= a.num_seqs) return;
+    const int g = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int jj = blockIdx.y;
+    const int s = blockIdx.z;   // < num_seqs by the grid
 
+    // per-sequence scalars, all loaded before the first branch
+    const int H = a.num_kv_heads;
     const int c0 = a.cu_seqlens[s];
-    const int n_new = a.cu_seqlens[s + 1] - c0;
+    const int c1 = a.cu_seqlens[s + 1];
     const int sp = a.start_pos[s];
+    const int slot = a.tail_slots[s];
+    // keep the four loads ahead of the branch (the compiler would otherwise
+    // sink each load below it and wait for them one after another)
+    __asm__ volatile("" : : "s"(c0), "s"(c1), "s"(sp), "s"(slot));
+    const int n_new = c1 - c0;
     const int end = sp + n_new;
     const int j = sp / BS + jj;
-    if (n_new <= 0 || j * BS >= end) return;
+    if (g >= H || n_new <= 0 || j * BS >= end) return;
     const int row0 = j * BS;
-    const int valid = min(BS, end - row0);
-    const int phys = a.block_tables[s * a.max_blocks_per_seq + j];
-    const int slot = a.tail_slots[s];
+    const int valid = min(BS, end - row0);   // >= 1
+    const int phys = a.block_tables[(int64_t)s * a.max_blocks_per_seq + j];
     const int r_in = lane / LPR;
     const int col = (lane % LPR) * 8;
 
+    // Row r of the block comes from the tail slot (positions before sp) or
+    // from the new tokens.  Every row is loaded unconditionally -- rows past
+    // `valid` read row 0 again and are then replaced by zeros -- and the
+    // source is chosen arithmetically, so that all loads are in flight
+    // together, beside the block id's.
     const int64_t tail_base = ((int64_t)slot * H + g) * BS * D;
+    auto row_src = [&](const uint16_t* tail, const uint16_t* fresh, int r) -> const uint16_t* {
+        const int rr = r < valid ? r : 0;
+        const int p = row0 + rr;
+        const uintptr_t t = (uintptr_t)(tail + tail_base + rr * D);
+        const uintptr_t f = (uintptr_t)(fresh + ((int64_t)(c0 + p - sp) * H + g) * D);
+        const uintptr_t from_tail = (uintptr_t)0 - (uintptr_t)(p < sp);
+        return (const uint16_t*)(f ^ ((t ^ f) & from_tail));
+    };
     f16x8 kx[NIT];
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-        const int r = it * RPI + r_in;
-        const int p = row0 + r;
-        kx[it] = (f16x8)(_Float16)0;
-        if (r < valid) {
-            const uint16_t* ks = p < sp ? a.tail_k + tail_base + r * D + col
-                                        : a.k + ((int64_t)(c0 + p - sp) * H + g) * D + col;
-            kx[it] = *(const f16x8*)ks;
-        }
+    for (int it = 0; it < NIT; ++it) kx[it] = *(const f16x8*)(row_src(a.tail_k, a.k, it * RPI + r_in) + col);
+    uint32_t vw[BS];   // V row r: dims DPL*lane .. +DPL-1 (fp16 bits)
+#pragma unroll
+    for (int r = 0; r < BS; ++r) {
+        const uint16_t* src = row_src(a.tail_v, a.v, r) + DPL * lane;
+        vw[r] = DPL == 2 ? *(const uint32_t*)src : (uint32_t)*src;
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+        if (it * RPI + r_in >= valid) kx[it] = (f16x8)(_Float16)0;
+    _Float16 vx[DPL][BS];
+#pragma unroll
+    for (int r = 0; r < BS; ++r) {
+        const uint32_t w = r < valid ? vw[r] : 0u;
+        vx[0][r] = __builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+        if constexpr (DPL == 2) vx[1][r] = __builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
     }
 
     const int64_t tile = (int64_t)phys * H + g;
@@ -101,7 +127,7 @@ __global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
             const uint32_t b = absmax_bits_f16x8(kx[it]);
             amax = amax > b ? amax : b;
         }
-        amax = wave_max_u32(amax);
+        amax = wave_max_u32_uniform(amax);
         const float absmax = bits_to_f16f((uint16_t)amax);
         const uint16_t s16 = f32_to_f16_bits(absmax / 127.0f);
         const float sc = bits_to_f16f(s16);
@@ -126,24 +152,6 @@ __global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
     }
 
     // ---- V (dim-major tile): INT8 symmetric or INT4 asymmetric ----------------
-    constexpr int DPL = D / 64;  // dims per lane
-    _Float16 vx[DPL][BS];
-#pragma unroll
-    for (int r = 0; r < BS; ++r) {
-        const int p = row0 + r;
-        const uint16_t* src = nullptr;
-        if (r < valid) {
-            src = p < sp ? a.tail_v + tail_base + r * D
-                         : a.v + ((int64_t)(c0 + p - sp) * H + g) * D;
-        }
-        if constexpr (DPL == 2) {
-            const uint32_t w = src ? *(const uint32_t*)(src + 2 * lane) : 0u;
-            vx[0][r] = __builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
-            vx[1][r] = __builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-        } else {
-            vx[0][r] = __builtin_bit_cast(_Float16, src ? src[lane] : (uint16_t)0);
-        }
-    }
     if constexpr (!V4) {
         uint32_t amax = 0;
 #pragma unroll
@@ -154,7 +162,7 @@ __global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
                 const uint32_t b = __builtin_bit_cast(uint16_t, x) & 0x7FFFu;
                 amax = amax > b ? amax : b;
             }
-        amax = wave_max_u32(amax);
+        amax = wave_max_u32_uniform(amax);
         const float absmax = bits_to_f16f((uint16_t)amax);
         const uint16_t s16 = f32_to_f16_bits(absmax / 127.0f);
         const float sc = bits_to_f16f(s16);
@@ -190,8 +198,8 @@ __global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
                 lo = fminf(lo, x);
                 hi = fmaxf(hi, x);
             }
-        lo = wave_min(lo);
-        hi = wave_max(hi);
+        lo = wave_min_uniform(lo);
+        hi = wave_max_uniform(hi);
         const uint16_t s16 = f32_to_f16_bits((hi - lo) / 15.0f);
         const float sc = bits_to_f16f(s16);
         int zp = 0;
@@ -256,11 +264,12 @@ __global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
     }
 }
 
+// Grid: x = groups of four KV heads, y = blocks a sequence's new tokens can
+// touch, z = sequences.
 template <int BS, int D, bool V4>
 hipError_t launch_qs(const QuantStoreArgs& a, hipStream_t stream) {
-    const int64_t waves = (int64_t)a.num_seqs * a.tiles_per_seq * a.num_kv_heads;
-    const int64_t blocks = (waves + 3) / 4;
-    hipLaunchKernelGGL((quantize_store_kernel<BS, D, V4>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    dim3 grid((unsigned)((a.num_kv_heads + 3) / 4), (unsigned)a.tiles_per_seq, (unsigned)a.num_seqs);
+    hipLaunchKernelGGL((quantize_store_kernel<BS, D, V4>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

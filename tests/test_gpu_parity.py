@@ -254,7 +254,8 @@ def test_gqa_ragged(bs, d, vc, g, hkv):
     case.store_all()
     assert_pool_equal(case.pool, case.opool)
     ref = case.reference()
-    for part in (0, 32, 96, 256):
+    # 2048: one partition per sequence (the 2-wave single-pass launch)
+    for part in (0, 32, 96, 256, 2048):
         assert_close(case.decode(part), ref, f"gqa bs{bs} d{d} {vc} g{g} part{part}")
 
 
