@@ -175,6 +175,24 @@ def main():
             fl.append(a.elapsed_time(b))
         del flush
 
+    # context: a plain streaming read of the same size (torch's sum over int32
+    # words), cycling through four buffers, as a practical read ceiling
+    ceiling = None
+    if not args.only_timed:
+        words = max(1, min(dbytes, 1 << 30) // 4)
+        bufs = [torch.ones(words, dtype=torch.int32, device="cuda") for _ in range(4)]
+        for b in bufs:
+            b.sum()
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ea.record(stream)
+        for i in range(20):
+            bufs[i % 4].sum()
+        eb.record(stream)
+        torch.cuda.synchronize()
+        ceiling = round(words * 4 * 20 / (ea.elapsed_time(eb) * 1e-3) / 1e9, 1)
+        del bufs
+
     step_bytes = dbytes + sbytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = dbytes / (dec_ms * 1e-3) / 1e9
@@ -202,6 +220,7 @@ def main():
             "pool_copies_rotated": R,
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "plain_read_gbs": ceiling,
         "tokens_per_s_per_layer": round(S / (ms_step * 1e-3), 1),
         "step_bytes": step_bytes,
         "kernels_ms": {"quantize_store_1tok": round(store_ms, 5),

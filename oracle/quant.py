@@ -34,8 +34,8 @@ Readings where the pages are silent, garbled or contradictory
   zero_point = clamp(rint(fp32(-lo) / scale), 0, 15).  The code is
   clamp(rint(fp32(fp32(x / scale) + zero_point)), 0, 15): division and
   addition each rounded in fp32, no fused multiply-add.
-* INT4 packing: two codes per byte along head_dim, even dimension in the low
-  nibble.
+* INT4 packing: two codes per byte along the last axis, the even index in the
+  low nibble (V tiles are dim-major, so the last axis is the block's tokens).
 * Only the rows a block actually holds take part in the statistics; rows not
   yet written are stored as zero bytes.
 Inputs must be finite fp16.
@@ -104,7 +104,7 @@ def dequantize_int4_asym(codes: np.ndarray, scale, zero_point) -> np.ndarray:
 
 
 def pack_int4(codes: np.ndarray) -> np.ndarray:
-    """[..., D] codes in 0..15 -> [..., D/2] bytes, even dim in the low nibble."""
+    """[..., n] codes in 0..15 -> [..., n/2] bytes, even index in the low nibble."""
     c = np.asarray(codes, np.uint8)
     if c.shape[-1] % 2:
         raise ValueError("head_dim must be even")
