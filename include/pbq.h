@@ -260,6 +260,33 @@ kv_status paged_attn_decode(const kv_pool_desc* desc, const kv_pool_mem* mem,
                             int32_t partition_size, void* workspace_dev,
                             size_t workspace_bytes, void* stream);
 
+/* One decode step with the current token's store fused in: for every
+ * sequence s with context_lens[s] > 0, first the work of kv_quantize_store
+ * for one new token at position context_lens[s] - 1 (its fp16 rows
+ * k_new_dev / v_new_dev [num_seqs, Hkv, D], row s; the block's earlier rows
+ * from tail slot tail_slots_dev[s]; the same codes, scales, zero point and
+ * tail-slot rows, bit for bit), then the attention of paged_attn_decode over
+ * context_lens[s] tokens, the new one included.  The caller has reserved the
+ * position (kv_seq_append) and performed its copy-on-write copies; the
+ * block may not be shared with another sequence of the call.  One query head
+ * per KV head and a single partition per sequence: the last block's store
+ * runs inside the attention kernel (two of the work group's waves quantize
+ * its K and V tiles, which the attention then reads from LDS), a single
+ * launch; otherwise the store kernel, then the decode.  Arguments and errors otherwise as paged_attn_decode; the pool's
+ * tail slots must be set in mem.  [tbr8] §4 store_kv and §5 point 2;
+ * [yunthe] Q(x) and x_hat. */
+kv_status paged_attn_decode_append(const kv_pool_desc* desc, const kv_pool_mem* mem,
+                                   const uint16_t* k_new_dev, const uint16_t* v_new_dev,
+                                   const int32_t* tail_slots_dev,
+                                   const uint16_t* q_dev, uint16_t* out_dev,
+                                   int32_t num_seqs, int32_t num_q_heads,
+                                   const int32_t* block_tables_dev,
+                                   int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens_dev,
+                                   int32_t max_context_len, float sm_scale,
+                                   int32_t partition_size, void* workspace_dev,
+                                   size_t workspace_bytes, void* stream);
+
 /* Partition size (tokens) paged_attn_decode uses when given 0: a single
  * pass when num_seqs x (heads, or KV heads x 16-head tiles) gives at least
  * four work groups per compute unit of the current device and every context

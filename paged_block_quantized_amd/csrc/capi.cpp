@@ -86,6 +86,119 @@ kv_status fail(kv_status st, const std::string& msg) {
 
 using pbq::fail;
 
+namespace {
+
+// New-token arguments of the fused store + decode (NULL for plain decode).
+struct AppendArgs {
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    const int32_t* tail_slots;
+};
+
+kv_status decode_impl(const kv_pool_desc* d, const kv_pool_mem* m, const AppendArgs* app,
+                            const uint16_t* q, uint16_t* out, int32_t num_seqs,
+                            int32_t num_q_heads, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t max_context_len, float sm_scale,
+                            int32_t partition_size, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    kv_status st = pbq::check_device_desc(d);
+    if (st != KV_OK) return st;
+    if ((st = pbq::check_mem(d, m, app != nullptr)) != KV_OK) return st;
+    if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0)
+        return fail(KV_ERR_INVALID, "negative size argument");
+    if (num_q_heads < 1 || num_q_heads % d->num_kv_heads != 0)
+        return fail(KV_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
+    if (num_q_heads / d->num_kv_heads > 16 && (num_q_heads / d->num_kv_heads) % 16 != 0)
+        return fail(KV_ERR_INVALID, "query-group sizes above 16 must be multiples of 16");
+    if (num_seqs == 0) return KV_OK;
+    if (num_seqs > 65535 || num_q_heads > 65535)
+        return fail(KV_ERR_INVALID, "num_seqs and num_q_heads must stay below 65536");
+    if (!q || !out || !pbq::aligned16(q) || !pbq::aligned16(out))
+        return fail(KV_ERR_INVALID, "q and out must be non-NULL and 16-byte aligned");
+    if (!block_tables || !context_lens) return fail(KV_ERR_INVALID, "index arrays must be non-NULL");
+    if (app && (!app->k_new || !app->v_new || !pbq::aligned16(app->k_new) || !pbq::aligned16(app->v_new)))
+        return fail(KV_ERR_INVALID, "k_new and v_new must be non-NULL and 16-byte aligned");
+    if (app && !app->tail_slots) return fail(KV_ERR_INVALID, "tail_slots must be non-NULL");
+    if (app && max_blocks_per_seq < 1) return fail(KV_ERR_INVALID, "max_blocks_per_seq must be >= 1");
+    if ((int64_t)max_blocks_per_seq * d->block_size < max_context_len)
+        return fail(KV_ERR_INVALID, "max_blocks_per_seq * block_size < max_context_len");
+    if (!std::isfinite(sm_scale))
+        return fail(KV_ERR_INVALID, "sm_scale must be finite");
+    int32_t part = partition_size;
+    if (part == 0) part = paged_attn_default_partition(d, num_seqs, num_q_heads, max_context_len);
+    if (part <= 0 || part % d->block_size != 0)
+        return fail(KV_ERR_INVALID, "partition_size must be a positive multiple of block_size (or 0)");
+    if (num_q_heads != d->num_kv_heads && part % 32 != 0)
+        return fail(KV_ERR_INVALID, "grouped-query partition_size must be a multiple of 32 tokens");
+    const int32_t max_parts = max_context_len > 0 ? pbq::ceil_div(max_context_len, part) : 1;
+    if (max_parts > 65535) return fail(KV_ERR_INVALID, "too many partitions; use a larger partition_size");
+    const size_t need = paged_attn_workspace_bytes(d, num_seqs, num_q_heads, max_context_len, part);
+    if (workspace_bytes < need) return fail(KV_ERR_INVALID, "workspace too small");
+    if (need > 0 && (!workspace || !pbq::aligned16(workspace)))
+        return fail(KV_ERR_INVALID, "workspace must be non-NULL and 16-byte aligned");
+    pbq::AttnArgs a{};
+    a.block_size = d->block_size;
+    a.num_kv_heads = d->num_kv_heads;
+    a.head_dim = d->head_dim;
+    a.v_codec = d->v_codec;
+    a.k_codes = (const int8_t*)m->k_codes;
+    a.v_codes = (const uint8_t*)m->v_codes;
+    a.k_scale = (const uint16_t*)m->k_scale;
+    a.v_scale = (const uint16_t*)m->v_scale;
+    a.v_zp = (const uint8_t*)m->v_zp;
+    a.q = q;
+    a.out = out;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.sm_scale = sm_scale;
+    a.partition_blocks = part / d->block_size;
+    a.max_partitions = max_parts;
+    const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
+    a.ws_out = need ? (float*)workspace : nullptr;
+    a.ws_ml = need ? (float*)((char*)workspace + rows * (size_t)d->head_dim * 4) : nullptr;
+    if (app && (num_q_heads != d->num_kv_heads || max_parts > 1)) {
+        // the store kernel in one-token append mode, then the decode: for
+        // grouped query heads, and for split partitions (where all but one
+        // work group per sequence and head would carry the fused store's
+        // registers for nothing)
+        pbq::QuantStoreArgs sa{};
+        sa.block_size = d->block_size;
+        sa.num_kv_heads = d->num_kv_heads;
+        sa.head_dim = d->head_dim;
+        sa.v_codec = d->v_codec;
+        sa.k_codes = (int8_t*)m->k_codes;
+        sa.v_codes = (uint8_t*)m->v_codes;
+        sa.k_scale = (uint16_t*)m->k_scale;
+        sa.v_scale = (uint16_t*)m->v_scale;
+        sa.v_zp = (uint8_t*)m->v_zp;
+        sa.tail_k = (uint16_t*)m->tail_k;
+        sa.tail_v = (uint16_t*)m->tail_v;
+        sa.k = app->k_new;
+        sa.v = app->v_new;
+        sa.num_seqs = num_seqs;
+        sa.block_tables = block_tables;
+        sa.max_blocks_per_seq = max_blocks_per_seq;
+        sa.tail_slots = app->tail_slots;
+        sa.tiles_per_seq = 1;
+        sa.append_ctx = context_lens;
+        st = pbq::hip_status(pbq::launch_quantize_store(sa, (hipStream_t)stream), "paged_attn_decode_append store launch");
+        if (st != KV_OK) return st;
+    } else if (app) {
+        a.k_new = app->k_new;
+        a.v_new = app->v_new;
+        a.tail_slots = app->tail_slots;
+        a.tail_k = (uint16_t*)m->tail_k;
+        a.tail_v = (uint16_t*)m->tail_v;
+    }
+    return pbq::hip_status(pbq::launch_paged_attn(a, (hipStream_t)stream), "paged_attn_decode launch");
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* kv_last_error(void) { return pbq::g_last_error.c_str(); }
@@ -219,61 +332,23 @@ kv_status paged_attn_decode(const kv_pool_desc* d, const kv_pool_mem* m,
                             int32_t max_context_len, float sm_scale,
                             int32_t partition_size, void* workspace,
                             size_t workspace_bytes, void* stream) {
-    kv_status st = pbq::check_device_desc(d);
-    if (st != KV_OK) return st;
-    if ((st = pbq::check_mem(d, m, false)) != KV_OK) return st;
-    if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0)
-        return fail(KV_ERR_INVALID, "negative size argument");
-    if (num_q_heads < 1 || num_q_heads % d->num_kv_heads != 0)
-        return fail(KV_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
-    if (num_q_heads / d->num_kv_heads > 16 && (num_q_heads / d->num_kv_heads) % 16 != 0)
-        return fail(KV_ERR_INVALID, "query-group sizes above 16 must be multiples of 16");
-    if (num_seqs == 0) return KV_OK;
-    if (num_seqs > 65535 || num_q_heads > 65535)
-        return fail(KV_ERR_INVALID, "num_seqs and num_q_heads must stay below 65536");
-    if (!q || !out || !pbq::aligned16(q) || !pbq::aligned16(out))
-        return fail(KV_ERR_INVALID, "q and out must be non-NULL and 16-byte aligned");
-    if (!block_tables || !context_lens) return fail(KV_ERR_INVALID, "index arrays must be non-NULL");
-    if ((int64_t)max_blocks_per_seq * d->block_size < max_context_len)
-        return fail(KV_ERR_INVALID, "max_blocks_per_seq * block_size < max_context_len");
-    if (!std::isfinite(sm_scale))
-        return fail(KV_ERR_INVALID, "sm_scale must be finite");
-    int32_t part = partition_size;
-    if (part == 0) part = paged_attn_default_partition(d, num_seqs, num_q_heads, max_context_len);
-    if (part <= 0 || part % d->block_size != 0)
-        return fail(KV_ERR_INVALID, "partition_size must be a positive multiple of block_size (or 0)");
-    if (num_q_heads != d->num_kv_heads && part % 32 != 0)
-        return fail(KV_ERR_INVALID, "grouped-query partition_size must be a multiple of 32 tokens");
-    const int32_t max_parts = max_context_len > 0 ? pbq::ceil_div(max_context_len, part) : 1;
-    if (max_parts > 65535) return fail(KV_ERR_INVALID, "too many partitions; use a larger partition_size");
-    const size_t need = paged_attn_workspace_bytes(d, num_seqs, num_q_heads, max_context_len, part);
-    if (workspace_bytes < need) return fail(KV_ERR_INVALID, "workspace too small");
-    if (need > 0 && (!workspace || !pbq::aligned16(workspace)))
-        return fail(KV_ERR_INVALID, "workspace must be non-NULL and 16-byte aligned");
-    pbq::AttnArgs a{};
-    a.block_size = d->block_size;
-    a.num_kv_heads = d->num_kv_heads;
-    a.head_dim = d->head_dim;
-    a.v_codec = d->v_codec;
-    a.k_codes = (const int8_t*)m->k_codes;
-    a.v_codes = (const uint8_t*)m->v_codes;
-    a.k_scale = (const uint16_t*)m->k_scale;
-    a.v_scale = (const uint16_t*)m->v_scale;
-    a.v_zp = (const uint8_t*)m->v_zp;
-    a.q = q;
-    a.out = out;
-    a.num_seqs = num_seqs;
-    a.num_q_heads = num_q_heads;
-    a.block_tables = block_tables;
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.context_lens = context_lens;
-    a.sm_scale = sm_scale;
-    a.partition_blocks = part / d->block_size;
-    a.max_partitions = max_parts;
-    const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
-    a.ws_out = need ? (float*)workspace : nullptr;
-    a.ws_ml = need ? (float*)((char*)workspace + rows * (size_t)d->head_dim * 4) : nullptr;
-    return pbq::hip_status(pbq::launch_paged_attn(a, (hipStream_t)stream), "paged_attn_decode launch");
+    return decode_impl(d, m, nullptr, q, out, num_seqs, num_q_heads, block_tables, max_blocks_per_seq,
+                       context_lens, max_context_len, sm_scale, partition_size, workspace, workspace_bytes,
+                       stream);
+}
+
+kv_status paged_attn_decode_append(const kv_pool_desc* d, const kv_pool_mem* m,
+                                   const uint16_t* k_new, const uint16_t* v_new,
+                                   const int32_t* tail_slots, const uint16_t* q, uint16_t* out,
+                                   int32_t num_seqs, int32_t num_q_heads,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t max_context_len,
+                                   float sm_scale, int32_t partition_size, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    const AppendArgs app{k_new, v_new, tail_slots};
+    return decode_impl(d, m, &app, q, out, num_seqs, num_q_heads, block_tables, max_blocks_per_seq,
+                       context_lens, max_context_len, sm_scale, partition_size, workspace, workspace_bytes,
+                       stream);
 }
 
 }  // extern "C"

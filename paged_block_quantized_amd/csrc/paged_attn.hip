@@ -22,8 +22,8 @@
 // raises the maximum.
 //
 // MHA partition kernel (one query head per KV head): one workgroup per
-// (partition, head, sequence); its NW wavefronts take the partition's blocks
-// round-robin.  Within a wave, lane l owns head dims (l % (D/16)) * 16 .. +16
+// (partition, head, sequence); each of its NW wavefronts takes a contiguous
+// run of the partition's blocks.  Within a wave, lane l owns head dims (l % (D/16)) * 16 .. +16
 // and token rows r * (64 / (D/16)) + l / (D/16) of every block, so one K tile
 // (block_size x D int8 codes, contiguous) is read with 16-byte loads that are
 // contiguous across the wave (1 KiB per instruction), and the INT8 V tile
@@ -42,6 +42,7 @@
 
 #include "device_common.h"
 #include "pbq_internal.h"
+#include "store_tile.h"
 
 namespace pbq {
 namespace {
@@ -129,6 +130,11 @@ inline dim3 grid_dims(int parts, int heads, int seqs) {
     return dim3((unsigned)heads, (unsigned)seqs, (unsigned)parts);
 #endif
 }
+// Tokens' worth of blocks that waves 0 and 1 of a fused partition hand to
+// the other waves for the store they do first.
+#ifndef PBQ_STORE_HANDICAP_TOKENS
+#define PBQ_STORE_HANDICAP_TOKENS 48
+#endif
 #ifndef PBQ_MHA_DEPTH
 #define PBQ_MHA_DEPTH 2
 #endif
@@ -142,8 +148,8 @@ inline dim3 grid_dims(int parts, int heads, int seqs) {
 // row of the block's tokens.  The softmax weights of a block (times its V
 // scale) are broadcast to scalar registers with readlane and every lane
 // accumulates its own dims, so no lane combination is needed for V.
-template <int BS, int D, bool V4, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_MHA_WAVES_PER_EU)))
+template <int BS, int D, bool V4, int NW, bool FUSED>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(FUSED ? (BS == 16 ? 5 : (V4 ? 4 : 3)) : PBQ_MHA_WAVES_PER_EU)))
 void attn_partition_mha(AttnArgs a) {
     constexpr int LPR = D / 16;    // K: lanes per token row (16 dims each)
     constexpr int RPI = 64 / LPR;  // K: token rows per wave access
@@ -171,6 +177,36 @@ void attn_partition_mha(AttnArgs a) {
     if (p >= nparts) return;
     const int b0 = p * PB;
     const int b1 = min(b0 + PB, nblk);
+    const int32_t* tab = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+
+    // Fused store of the current token (position ctx - 1): in the sequence's
+    // last partition, waves 0 and 1 first re-quantize the last block's K and
+    // V tiles from the tail-slot rows and the new row (store_tile, the code
+    // of the store kernel), leaving LDS copies of the codes and scales, and
+    // take correspondingly fewer of the other blocks; after a barrier, wave
+    // NW - 1 adds the last block's contribution from the LDS copy.
+    __shared__ __align__(16) uint8_t s_tile[FUSED ? KT + VT : 16];
+    __shared__ uint32_t s_tscale[3];
+    const bool fused = FUSED && p == nparts - 1 && nblk > 0;   // uniform in the group
+    if (fused && w < 2) {
+        const TileStoreArgs t{const_cast<int8_t*>(a.k_codes), const_cast<uint8_t*>(a.v_codes),
+                              const_cast<uint16_t*>(a.k_scale), const_cast<uint16_t*>(a.v_scale),
+                              const_cast<uint8_t*>(a.v_zp), a.tail_k, a.tail_v, a.k_new, a.v_new, H};
+        const int last = nblk - 1;
+        const int slot = a.tail_slots[s], phys = tab[last];
+        if (w == 0) {
+            const TileScales ts = store_tile<BS, D, V4, true, true, false>(
+                t, h, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT);
+            if (lane == 0) s_tscale[0] = ts.k_scale;
+        } else {
+            const TileScales ts = store_tile<BS, D, V4, true, false, true>(
+                t, h, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT);
+            if (lane == 0) {
+                s_tscale[1] = ts.v_scale;
+                s_tscale[2] = ts.v_zp;
+            }
+        }
+    }
 
     const int dl = (lane % LPR) * 16;
     f16x2 q2[8];
@@ -195,136 +231,151 @@ void attn_partition_mha(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < DPL; ++k) acc[k][0] = acc[k][1] = 0.f;
 
-    const int32_t* tab = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
     const int row_lane = lane / LPR;
 
-    for (int base = b0 + w; base < b1; base += 64 * NW) {
+    // One block's contribution: scores, online softmax update, weighted V.
+    auto compute_blk = [&](const Regs& r, int blk, float skc, float svv, float vbias) {
+        float sc[NR];
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            float d = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t u = r.k[j][k] ^ 0x80808080u;
+                d = __builtin_amdgcn_fdot2(perm_lo(u), q2[2 * k], d, false);
+                d = __builtin_amdgcn_fdot2(perm_hi(u), q2[2 * k + 1], d, false);
+            }
+            sc[j] = d - qbias;
+        }
+#pragma unroll
+        for (int j = 0; j < NR; ++j) sc[j] = group_sum<LPR>(sc[j]);
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            const int t = blk * BS + j * RPI + row_lane;
+            sc[j] = t < ctx ? sc[j] * skc : -INFINITY;
+            bmax = fmaxf(bmax, sc[j]);
+        }
+        bmax = strided_max<LPR>(bmax);
+        if (bmax > m) {
+            const float alpha = __builtin_amdgcn_exp2f(m - bmax);
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) {
+                acc[k][0] *= alpha;
+                acc[k][1] *= alpha;
+            }
+            l *= alpha;
+            zacc *= alpha;
+            m = bmax;
+        }
+        float pv[NR];
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            const float pr = __builtin_amdgcn_exp2f(sc[j] - m);
+            l += pr;
+            pv[j] = pr * svv;
+            zacc = __builtin_fmaf(pv[j], vbias, zacc);
+        }
+        // weights of all tokens of the block, uniform across the wave
+        float sp[BS];
+#pragma unroll
+        for (int t = 0; t < BS; ++t) sp[t] = readlane(pv[t / RPI], (t % RPI) * LPR);
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) {
+            if constexpr (V4) {
+#pragma unroll
+                for (int c = 0; c < VW; ++c) {   // tokens 8c .. 8c+7
+                    const uint32_t wv = r.v[k][c];
+                    const uint32_t lo = wv & 0x0F0F0F0Fu;         // tokens 0,2,4,6
+                    const uint32_t hi = (wv >> 4) & 0x0F0F0F0Fu;  // tokens 1,3,5,7
+                    const f16x2 e0 = perm_lo(lo), e1 = perm_hi(lo);
+                    const f16x2 o0 = perm_lo(hi), o1 = perm_hi(hi);
+                    const int t = 8 * c;
+                    acc[k][0] = __builtin_fmaf(sp[t + 0], (float)e0[0], acc[k][0]);
+                    acc[k][1] = __builtin_fmaf(sp[t + 1], (float)o0[0], acc[k][1]);
+                    acc[k][0] = __builtin_fmaf(sp[t + 2], (float)e0[1], acc[k][0]);
+                    acc[k][1] = __builtin_fmaf(sp[t + 3], (float)o0[1], acc[k][1]);
+                    acc[k][0] = __builtin_fmaf(sp[t + 4], (float)e1[0], acc[k][0]);
+                    acc[k][1] = __builtin_fmaf(sp[t + 5], (float)o1[0], acc[k][1]);
+                    acc[k][0] = __builtin_fmaf(sp[t + 6], (float)e1[1], acc[k][0]);
+                    acc[k][1] = __builtin_fmaf(sp[t + 7], (float)o1[1], acc[k][1]);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < VW; ++c) {   // tokens 4c .. 4c+3
+                    const uint32_t u = r.v[k][c] ^ 0x80808080u;
+                    const f16x2 a0 = perm_lo(u), a1 = perm_hi(u);
+                    const int t = 4 * c;
+                    acc[k][0] = __builtin_fmaf(sp[t + 0], (float)a0[0], acc[k][0]);
+                    acc[k][1] = __builtin_fmaf(sp[t + 1], (float)a0[1], acc[k][1]);
+                    acc[k][0] = __builtin_fmaf(sp[t + 2], (float)a1[0], acc[k][0]);
+                    acc[k][1] = __builtin_fmaf(sp[t + 3], (float)a1[1], acc[k][1]);
+                }
+            }
+        }
+    };
+
+    // Codes of one (block, head) tile: K from kp (the tile's first byte), V
+    // from vp; either may point into the pool or into the LDS copy of a tile.
+    auto load_tile = [&](const int8_t* kp, const uint8_t* vp, Regs& r) {
+        kp += lane * 16;
+#pragma unroll
+        for (int j = 0; j < NR; ++j) r.k[j] = *(const u32x4*)(kp + j * 1024);
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) {
+            const uint8_t* row = vp + (lane + 64 * k) * VROW;
+            if constexpr (VROW == 8) {
+                const u32x2 x = *(const u32x2*)row;
+                r.v[k][0] = x[0];
+                r.v[k][1] = x[1];
+            } else {
+#pragma unroll
+                for (int c = 0; c < VROW / 16; ++c) {
+                    const u32x4 x = *(const u32x4*)(row + 16 * c);
+                    r.v[k][4 * c + 0] = x[0];
+                    r.v[k][4 * c + 1] = x[1];
+                    r.v[k][4 * c + 2] = x[2];
+                    r.v[k][4 * c + 3] = x[3];
+                }
+            }
+        }
+    };
+
+    // Each wave takes a contiguous run of the partition's blocks.  In a fused
+    // partition the last block is left out, and waves 0 and 1 (which store
+    // it) take `hc` fewer blocks each, spread over the other waves.
+    const int b_end = fused ? nblk - 1 : b1;
+    const int n = b_end - b0;
+    const int hc = fused ? min(PBQ_STORE_HANDICAP_TOKENS / BS, n / NW) : 0;
+    const int q = (n + 2 * hc) / NW, rem = (n + 2 * hc) % NW;
+    const int w_start = b0 + w * q + min(w, rem) - min(w, 2) * hc;
+    const int w_stop = w_start + q + (w < rem ? 1 : 0) - (w < 2 ? hc : 0);
+
+    for (int base = w_start; base < w_stop; base += 64) {
         // stage this wave's next (up to) 64 blocks: ids, then (after the first
         // block's codes are in flight) scales and zero points
-        const int bi = base + lane * NW;
-        const int id = bi < b1 ? tab[bi] : 0;
-        const int cnt = min(64, (b1 - base + NW - 1) / NW);
+        const int bi = base + lane;
+        const int id = bi < w_stop ? tab[bi] : 0;
+        const int cnt = min(64, w_stop - base);
         // raw fp16 scale bits and zero point, converted where they are used
         // (any arithmetic here would make the first step's wait cover the
         // prefetched codes too)
         int sk = 0, sv = 0, zp = 0;
 
         auto load = [&](int i, Regs& r) {
-            const int phys = readlane(id, i);
-            const int64_t t = (int64_t)phys * H + h;
-            const int8_t* kp = a.k_codes + t * KT + lane * 16;
-#pragma unroll
-            for (int j = 0; j < NR; ++j) r.k[j] = *(const u32x4*)(kp + j * 1024);
-            const uint8_t* vp = a.v_codes + t * VT;
-#pragma unroll
-            for (int k = 0; k < DPL; ++k) {
-                const uint8_t* row = vp + (lane + 64 * k) * VROW;
-                if constexpr (VROW == 8) {
-                    const u32x2 x = *(const u32x2*)row;
-                    r.v[k][0] = x[0];
-                    r.v[k][1] = x[1];
-                } else {
-#pragma unroll
-                    for (int c = 0; c < VROW / 16; ++c) {
-                        const u32x4 x = *(const u32x4*)(row + 16 * c);
-                        r.v[k][4 * c + 0] = x[0];
-                        r.v[k][4 * c + 1] = x[1];
-                        r.v[k][4 * c + 2] = x[2];
-                        r.v[k][4 * c + 3] = x[3];
-                    }
-                }
-            }
+            const int64_t t = (int64_t)readlane(id, i) * H + h;
+            load_tile(a.k_codes + t * KT, a.v_codes + t * VT, r);
         };
 
         auto compute = [&](const Regs& r, int i) {
-            const int blk = base + i * NW;
-            const float skc = bits_to_f16f((uint16_t)readlane(sk, i)) * c2;
-            float sc[NR];
-#pragma unroll
-            for (int j = 0; j < NR; ++j) {
-                float d = 0.f;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint32_t u = r.k[j][k] ^ 0x80808080u;
-                    d = __builtin_amdgcn_fdot2(perm_lo(u), q2[2 * k], d, false);
-                    d = __builtin_amdgcn_fdot2(perm_hi(u), q2[2 * k + 1], d, false);
-                }
-                sc[j] = d - qbias;
-            }
-#pragma unroll
-            for (int j = 0; j < NR; ++j) sc[j] = group_sum<LPR>(sc[j]);
-            float bmax = -INFINITY;
-#pragma unroll
-            for (int j = 0; j < NR; ++j) {
-                const int t = blk * BS + j * RPI + row_lane;
-                sc[j] = t < ctx ? sc[j] * skc : -INFINITY;
-                bmax = fmaxf(bmax, sc[j]);
-            }
-            bmax = strided_max<LPR>(bmax);
-            if (bmax > m) {
-                const float alpha = __builtin_amdgcn_exp2f(m - bmax);
-#pragma unroll
-                for (int k = 0; k < DPL; ++k) {
-                    acc[k][0] *= alpha;
-                    acc[k][1] *= alpha;
-                }
-                l *= alpha;
-                zacc *= alpha;
-                m = bmax;
-            }
-            const float svv = bits_to_f16f((uint16_t)readlane(sv, i));
-            const float vbias = V4 ? kI4Bias + (float)readlane(zp, i) : kI8Bias;
-            float pv[NR];
-#pragma unroll
-            for (int j = 0; j < NR; ++j) {
-                const float pr = __builtin_amdgcn_exp2f(sc[j] - m);
-                l += pr;
-                pv[j] = pr * svv;
-                zacc = __builtin_fmaf(pv[j], vbias, zacc);
-            }
-            // weights of all tokens of the block, uniform across the wave
-            float sp[BS];
-#pragma unroll
-            for (int t = 0; t < BS; ++t) sp[t] = readlane(pv[t / RPI], (t % RPI) * LPR);
-#pragma unroll
-            for (int k = 0; k < DPL; ++k) {
-                if constexpr (V4) {
-#pragma unroll
-                    for (int c = 0; c < VW; ++c) {   // tokens 8c .. 8c+7
-                        const uint32_t wv = r.v[k][c];
-                        const uint32_t lo = wv & 0x0F0F0F0Fu;         // tokens 0,2,4,6
-                        const uint32_t hi = (wv >> 4) & 0x0F0F0F0Fu;  // tokens 1,3,5,7
-                        const f16x2 e0 = perm_lo(lo), e1 = perm_hi(lo);
-                        const f16x2 o0 = perm_lo(hi), o1 = perm_hi(hi);
-                        const int t = 8 * c;
-                        acc[k][0] = __builtin_fmaf(sp[t + 0], (float)e0[0], acc[k][0]);
-                        acc[k][1] = __builtin_fmaf(sp[t + 1], (float)o0[0], acc[k][1]);
-                        acc[k][0] = __builtin_fmaf(sp[t + 2], (float)e0[1], acc[k][0]);
-                        acc[k][1] = __builtin_fmaf(sp[t + 3], (float)o0[1], acc[k][1]);
-                        acc[k][0] = __builtin_fmaf(sp[t + 4], (float)e1[0], acc[k][0]);
-                        acc[k][1] = __builtin_fmaf(sp[t + 5], (float)o1[0], acc[k][1]);
-                        acc[k][0] = __builtin_fmaf(sp[t + 6], (float)e1[1], acc[k][0]);
-                        acc[k][1] = __builtin_fmaf(sp[t + 7], (float)o1[1], acc[k][1]);
-                    }
-                } else {
-#pragma unroll
-                    for (int c = 0; c < VW; ++c) {   // tokens 4c .. 4c+3
-                        const uint32_t u = r.v[k][c] ^ 0x80808080u;
-                        const f16x2 a0 = perm_lo(u), a1 = perm_hi(u);
-                        const int t = 4 * c;
-                        acc[k][0] = __builtin_fmaf(sp[t + 0], (float)a0[0], acc[k][0]);
-                        acc[k][1] = __builtin_fmaf(sp[t + 1], (float)a0[1], acc[k][1]);
-                        acc[k][0] = __builtin_fmaf(sp[t + 2], (float)a1[0], acc[k][0]);
-                        acc[k][1] = __builtin_fmaf(sp[t + 3], (float)a1[1], acc[k][1]);
-                    }
-                }
-            }
+            compute_blk(r, base + i, bits_to_f16f((uint16_t)readlane(sk, i)) * c2,
+                        bits_to_f16f((uint16_t)readlane(sv, i)),
+                        V4 ? kI4Bias + (float)readlane(zp, i) : kI8Bias);
         };
 
-        // scales of the staged blocks (zeroed past the end, so that stale pool
-        // contents cannot reach the sums); issued after the first codes
-        // only the wave's own blocks (i < cnt) are ever read back, so lanes
-        // past the end may hold any finite or non-finite value
+        // scale bits of the staged blocks, issued after the first codes; only
+        // the wave's own blocks (i < cnt) are ever read back, so lanes past
+        // the end may hold any value
         auto scales = [&]() {
             const int64_t t = (int64_t)id * H + h;
             sk = a.k_scale[t];
@@ -332,6 +383,15 @@ void attn_partition_mha(AttnArgs a) {
             if constexpr (V4) zp = a.v_zp[t];
         };
         pipelined<PBQ_MHA_DEPTH, Regs>(cnt, load, compute, scales);
+    }
+    if (FUSED && fused) {
+        __syncthreads();   // waves 0 and 1 have left the tiles in LDS
+        if (w == NW - 1) {
+            Regs r;
+            load_tile((const int8_t*)s_tile, s_tile + KT, r);
+            compute_blk(r, b_end, bits_to_f16f((uint16_t)s_tscale[0]) * c2, bits_to_f16f((uint16_t)s_tscale[1]),
+                        V4 ? kI4Bias + (float)s_tscale[2] : kI8Bias);
+        }
     }
 
     // every token row is held by LPR lanes: full-wave sums count it LPR times
@@ -748,10 +808,14 @@ __global__ __launch_bounds__(64) void attn_reduce(AttnArgs a) {
 template <int BS, int D, bool V4>
 hipError_t launch_mha(const AttnArgs& a, hipStream_t stream) {
     const dim3 grid = grid_dims(a.max_partitions, a.num_q_heads, a.num_seqs);
-    if (a.partition_blocks >= 64)
-        hipLaunchKernelGGL((attn_partition_mha<BS, D, V4, 8>), grid, dim3(64 * 8), 0, stream, a);
-    else
-        hipLaunchKernelGGL((attn_partition_mha<BS, D, V4, 4>), grid, dim3(64 * 4), 0, stream, a);
+    const bool fused = a.k_new != nullptr;
+    if (a.partition_blocks >= 64) {
+        if (fused) hipLaunchKernelGGL((attn_partition_mha<BS, D, V4, 8, true>), grid, dim3(64 * 8), 0, stream, a);
+        else hipLaunchKernelGGL((attn_partition_mha<BS, D, V4, 8, false>), grid, dim3(64 * 8), 0, stream, a);
+    } else {
+        if (fused) hipLaunchKernelGGL((attn_partition_mha<BS, D, V4, 4, true>), grid, dim3(64 * 4), 0, stream, a);
+        else hipLaunchKernelGGL((attn_partition_mha<BS, D, V4, 4, false>), grid, dim3(64 * 4), 0, stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_partitions <= 1) return e;
     hipLaunchKernelGGL((attn_reduce<BS, D>), dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(64), 0,

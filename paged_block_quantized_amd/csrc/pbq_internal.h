@@ -32,6 +32,9 @@ struct QuantStoreArgs {
     int32_t max_blocks_per_seq;
     const int32_t* tail_slots;
     int32_t tiles_per_seq;  // upper bound on blocks touched per sequence
+    // one-token append mode (cu_seqlens / start_pos unused): sequence s
+    // stores row s of k / v at position append_ctx[s] - 1 (none if 0)
+    const int32_t* append_ctx;
 };
 
 struct AttnArgs {
@@ -52,6 +55,13 @@ struct AttnArgs {
     int32_t max_partitions;    // ceil(max_context_len / partition tokens), >= 1
     float* ws_out;             // [S, Hq, max_partitions, D]
     float* ws_ml;              // [S, Hq, max_partitions, 2]  (max, sum) base 2
+    // fused store of the current token (all NULL for plain decode): the new
+    // token's fp16 K/V rows [S, Hkv, D], tail slots, and the writable pool
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    const int32_t* tail_slots;
+    uint16_t* tail_k;
+    uint16_t* tail_v;
 };
 
 struct CopyArgs {

@@ -1,0 +1,289 @@
+// Quantization of one (block, KV head) tile from its exact fp16 rows: shared
+// by the store kernel and the fused store + decode kernels, so both write
+// the same bytes.
+//
+// The codec (web pages cited by site and section): tbr8.org "PagedAttention +
+// block-wise quantization against mobile OOM", §3 and §4 store_kv -- INT8
+// codes with an fp16 absmax/127 scale per (block, head); yunthe.com
+// "KV-cache quantization and PagedAttention", "quantization principle" --
+// Q(x) = clamp(round(x / scale + zero_point), 0, 2^bits - 1), used for INT4 V
+// (bits = 4) and, with zero point 128 and a signed store, for INT8.
+// Readings: round half to even on the exact quotient; statistics over the
+// rows the block holds; the INT4 range widened to contain 0 with an integer
+// zero point; rows not yet held are zero bytes.
+//
+// Lane mapping (one full wave per tile): K tiles are token-major ([bs, D]
+// codes): lane l holds rows it * (64 / (D/8)) + l / (D/8) and dims
+// (l % (D/8)) * 8 .. + 8.  V tiles are dim-major ([D, bs] codes, INT4 packing
+// two consecutive tokens per byte): lane l holds the D/64 adjacent dims
+// starting at l * D/64 of every row, so each fp16 row read and the lane's
+// code rows are contiguous.
+//
+// Exact codes without a per-element division: n = rint(x * (1/s)) is within
+// one of the answer; the remainder x - n*s is exact in one FMA (x and s are
+// fp16 values, |n| <= 255), and comparing |rem| with s/2 (also exact) decides
+// the nearest integer and the tie, so the result equals round-half-even of
+// the exact quotient, which is what a correctly rounded fp32 division
+// followed by rint gives for fp16 operands.
+#pragma once
+
+#include "device_common.h"
+
+namespace pbq {
+
+// Pool arrays a tile store writes and the fp16 rows it reads.
+struct TileStoreArgs {
+    int8_t* k_codes;
+    uint8_t* v_codes;
+    uint16_t* k_scale;
+    uint16_t* v_scale;
+    uint8_t* v_zp;
+    uint16_t* tail_k;      // [max_seqs, H, bs, D] fp16
+    uint16_t* tail_v;
+    const uint16_t* k;     // new rows, token-major [T, H, D] fp16
+    const uint16_t* v;
+    int32_t num_kv_heads;
+};
+
+// Raw bits of the scales (and zero point) a tile store wrote.
+struct TileScales {
+    uint32_t k_scale, v_scale, v_zp;
+};
+
+// Round-half-even of x / s + zp for s > 0, x and s fp16 values held in fp32.
+__device__ __forceinline__ int rne_quot(float x, float s, float rcp, float half_s, int zp) {
+    const float n = __builtin_rintf(x * rcp);
+    const float rem = __builtin_fmaf(-n, s, x);  // exact
+    const float arem = __builtin_fabsf(rem);
+    const int dir = rem > 0.f ? 1 : -1;
+    int q = (int)n + zp;
+    q += arem > half_s ? dir : 0;                     // n was one off
+    q += (arem == half_s && (q & 1)) ? dir : 0;       // exact tie -> even
+    return q;
+}
+
+// Quantize block j (physical id phys) of head g of a sequence whose rows
+// before position sp sit in tail slot `slot` and whose rows sp .. end-1 are
+// the new rows c0 .. c0 + end - sp - 1 of a.k / a.v.  Requires j * BS < end.
+// Writes codes, scales, zero point, and -- when the sequence's last block
+// stays partial -- its new rows to the tail slot.  With LDS set, the codes are
+// also written to lds_k / lds_v in the tile layout.  Called by a whole wave.
+// DO_K / DO_V select the tensors: the store kernel does both in one wave
+// (all rows in flight at once); the fused decode gives them to two waves,
+// which halves the registers either needs.
+template <int BS, int D, bool V4, bool LDS, bool DO_K = true, bool DO_V = true>
+__device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, int slot, int c0, int sp,
+                                                 int end, int j, int phys, int8_t* lds_k, uint8_t* lds_v) {
+    constexpr int LPR = D / 8;     // lanes per token row
+    constexpr int RPI = 64 / LPR;  // rows per wave access
+    constexpr int NIT = BS / RPI;  // accesses per lane per tensor
+    constexpr int DPL = D / 64;    // V: dims per lane
+    const int lane = threadIdx.x & 63;
+    const int H = a.num_kv_heads;
+    TileScales out{};
+    const int row0 = j * BS;
+    const int valid = min(BS, end - row0);   // >= 1
+    const int r_in = lane / LPR;
+    const int col = (lane % LPR) * 8;
+
+    // Row r of the block comes from the tail slot (positions before sp) or
+    // from the new tokens.  Every row is loaded unconditionally -- rows past
+    // `valid` read row 0 again and are then replaced by zeros -- and the
+    // source is chosen arithmetically, so that all loads are in flight
+    // together, beside the block id's.
+    const int64_t tail_base = ((int64_t)slot * H + g) * BS * D;
+    auto row_src = [&](const uint16_t* tail, const uint16_t* fresh, int r) -> const uint16_t* {
+        const int rr = r < valid ? r : 0;
+        const int p = row0 + rr;
+        const uintptr_t t = (uintptr_t)(tail + tail_base + rr * D);
+        const uintptr_t f = (uintptr_t)(fresh + ((int64_t)(c0 + p - sp) * H + g) * D);
+        const uintptr_t from_tail = (uintptr_t)0 - (uintptr_t)(p < sp);
+        return (const uint16_t*)(f ^ ((t ^ f) & from_tail));
+    };
+    f16x8 kx[DO_K ? NIT : 1];
+    if constexpr (DO_K) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) kx[it] = *(const f16x8*)(row_src(a.tail_k, a.k, it * RPI + r_in) + col);
+    }
+    uint32_t vw[DO_V ? BS : 1];   // V row r: dims DPL*lane .. +DPL-1 (fp16 bits)
+    if constexpr (DO_V) {
+#pragma unroll
+        for (int r = 0; r < BS; ++r) {
+            const uint16_t* src = row_src(a.tail_v, a.v, r) + DPL * lane;
+            vw[r] = DPL == 2 ? *(const uint32_t*)src : (uint32_t)*src;
+        }
+    }
+    if constexpr (DO_K) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+            if (it * RPI + r_in >= valid) kx[it] = (f16x8)(_Float16)0;
+    }
+    // rows past `valid` become zeros; the fp16 values stay packed (dims
+    // DPL*lane and DPL*lane + 1 in the low and high halves)
+    if constexpr (DO_V) {
+#pragma unroll
+        for (int r = 0; r < BS; ++r) vw[r] = r < valid ? vw[r] : 0u;
+    }
+    auto vx = [&](int k, int r) -> float {
+        return bits_to_f16f((uint16_t)(k ? vw[r] >> 16 : vw[r] & 0xFFFFu));
+    };
+
+    const int64_t tile = (int64_t)phys * H + g;
+
+    // ---- K: INT8 symmetric -------------------------------------------------
+    if constexpr (DO_K) {
+        uint32_t amax = 0;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const uint32_t b = absmax_bits_f16x8(kx[it]);
+            amax = amax > b ? amax : b;
+        }
+        amax = wave_max_u32_uniform(amax);
+        const float absmax = bits_to_f16f((uint16_t)amax);
+        const uint16_t s16 = f32_to_f16_bits(absmax / 127.0f);
+        const float sc = bits_to_f16f(s16);
+        const float rcp = sc > 0.f ? 1.0f / sc : 0.f;
+        const float half_s = 0.5f * sc;
+        int8_t* dst = a.k_codes + tile * (BS * D);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            uint32_t w[2] = {0u, 0u};
+            if (sc > 0.f) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    int q = rne_quot((float)kx[it][e], sc, rcp, half_s, 0);
+                    q = q > 127 ? 127 : (q < -127 ? -127 : q);
+                    w[e >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (e & 3));
+                }
+            }
+            const int r = it * RPI + r_in;
+            *(u32x2*)(dst + r * D + col) = u32x2{w[0], w[1]};
+            if constexpr (LDS) *(u32x2*)(lds_k + r * D + col) = u32x2{w[0], w[1]};
+        }
+        if (lane == 0) a.k_scale[tile] = s16;
+        out.k_scale = s16;
+    }
+
+    // ---- V (dim-major tile): INT8 symmetric or INT4 asymmetric ----------------
+    if constexpr (DO_V && !V4) {
+        uint32_t amax = 0;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k)
+#pragma unroll
+            for (int r = 0; r < BS; ++r) {
+                const uint32_t b = (k ? vw[r] >> 16 : vw[r]) & 0x7FFFu;
+                amax = amax > b ? amax : b;
+            }
+        amax = wave_max_u32_uniform(amax);
+        const float absmax = bits_to_f16f((uint16_t)amax);
+        const uint16_t s16 = f32_to_f16_bits(absmax / 127.0f);
+        const float sc = bits_to_f16f(s16);
+        const float rcp = sc > 0.f ? 1.0f / sc : 0.f;
+        const float half_s = 0.5f * sc;
+        uint8_t* dst = a.v_codes + tile * (BS * D);
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) {
+            uint32_t w[BS / 4];
+#pragma unroll
+            for (int i = 0; i < BS / 4; ++i) w[i] = 0u;
+            if (sc > 0.f) {
+#pragma unroll
+                for (int r = 0; r < BS; ++r) {
+                    int q = rne_quot(vx(k, r), sc, rcp, half_s, 0);
+                    q = q > 127 ? 127 : (q < -127 ? -127 : q);
+                    w[r >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (r & 3));
+                }
+            }
+            uint32_t* drow = (uint32_t*)(dst + (DPL * lane + k) * BS);
+#pragma unroll
+            for (int i = 0; i < BS / 16; ++i)
+                *(u32x4*)(drow + 4 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+            if constexpr (LDS) {
+                uint32_t* lrow = (uint32_t*)(lds_v + (DPL * lane + k) * BS);
+#pragma unroll
+                for (int i = 0; i < BS / 16; ++i)
+                    *(u32x4*)(lrow + 4 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+            }
+        }
+        if (lane == 0) a.v_scale[tile] = s16;
+        out.v_scale = s16;
+    } else if constexpr (DO_V) {
+        float lo = 0.f, hi = 0.f;  // range widened to contain 0
+#pragma unroll
+        for (int k = 0; k < DPL; ++k)
+#pragma unroll
+            for (int r = 0; r < BS; ++r) {
+                const float x = vx(k, r);
+                lo = fminf(lo, x);
+                hi = fmaxf(hi, x);
+            }
+        lo = wave_min_uniform(lo);
+        hi = wave_max_uniform(hi);
+        const uint16_t s16 = f32_to_f16_bits((hi - lo) / 15.0f);
+        const float sc = bits_to_f16f(s16);
+        int zp = 0;
+        if (sc > 0.f) {
+            const float z = __builtin_rintf(-lo / sc);
+            zp = z > 15.f ? 15 : (z < 0.f ? 0 : (int)z);
+        }
+        const float rcp = sc > 0.f ? 1.0f / sc : 0.f;
+        const float half_s = 0.5f * sc;
+        uint8_t* dst = a.v_codes + tile * (BS * D / 2);
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) {
+            uint32_t w[BS / 8];
+#pragma unroll
+            for (int i = 0; i < BS / 8; ++i) w[i] = 0u;
+            if (sc > 0.f) {
+#pragma unroll
+                for (int r = 0; r < BS; ++r) {
+                    if (r < valid) {
+                        int q = rne_quot(vx(k, r), sc, rcp, half_s, zp);
+                        q = q > 15 ? 15 : (q < 0 ? 0 : q);
+                        w[r >> 3] |= (uint32_t)q << (4 * (r & 7));
+                    }
+                }
+            }
+            uint32_t* drow = (uint32_t*)(dst + (DPL * lane + k) * (BS / 2));
+            uint32_t* lrow = LDS ? (uint32_t*)(lds_v + (DPL * lane + k) * (BS / 2)) : nullptr;
+            if constexpr (BS == 16) {
+                *(u32x2*)drow = u32x2{w[0], w[1]};
+                if constexpr (LDS) *(u32x2*)lrow = u32x2{w[0], w[1]};
+            } else {
+#pragma unroll
+                for (int i = 0; i < BS / 32; ++i) {
+                    *(u32x4*)(drow + 4 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+                    if constexpr (LDS) *(u32x4*)(lrow + 4 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+                }
+            }
+        }
+        if (lane == 0) {
+            a.v_scale[tile] = s16;
+            a.v_zp[tile] = (uint8_t)zp;
+        }
+        out.v_scale = s16;
+        out.v_zp = (uint32_t)zp;
+    }
+
+    // ---- tail slot: exact rows of a block that stays partial ----------------
+    if (end % BS != 0 && j == (end - 1) / BS) {
+        if constexpr (DO_K) {
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int r = it * RPI + r_in;
+                if (r < valid && row0 + r >= sp) *(f16x8*)(a.tail_k + tail_base + r * D + col) = kx[it];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < (DO_V ? BS : 0); ++r) {
+            if (r < valid && row0 + r >= sp) {
+                uint16_t* t = a.tail_v + tail_base + r * D + DPL * lane;
+                if constexpr (DPL == 2) *(uint32_t*)t = vw[r];
+                else *t = (uint16_t)vw[r];
+            }
+        }
+    }
+    return out;
+}
+
+}  // namespace pbq

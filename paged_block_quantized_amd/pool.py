@@ -136,3 +136,19 @@ class KVPool:
                             block_tables, block_tables.shape[1], context_lens, max_context_len,
                             sm_scale, partition_size, workspace, nbytes, stream)
         return workspace
+
+    def decode_append(self, k_new, v_new, tail_slots, q, out, block_tables, context_lens,
+                      max_context_len, sm_scale, partition_size=0, workspace=None, stream=None,
+                      mem=None):
+        """Store each sequence's current token (k_new / v_new [S, Hkv, D] fp16,
+        at position context_lens - 1) and decode, in one library call."""
+        S, Hq, _ = q.shape
+        need = self.workspace_bytes(S, Hq, max_context_len, partition_size)
+        if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        L.paged_attn_decode_append(self.desc, self.mem if mem is None else mem, k_new, v_new,
+                                   tail_slots, q, out, S, Hq, block_tables, block_tables.shape[1],
+                                   context_lens, max_context_len, sm_scale, partition_size,
+                                   workspace, nbytes, stream)
+        return workspace

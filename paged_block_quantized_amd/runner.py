@@ -4,8 +4,10 @@ Orchestration of library calls only (allocate, fork, store, build tables,
 decode); every step of the computation happens in the HIP kernels.
 
 A decode step for one layer stores the current token of every sequence
-(re-quantizing its block from the tail slot) and then runs the fused
-dequantizing attention over the whole context, current token included.
+(re-quantizing its block from the tail slot) and runs the fused dequantizing
+attention over the whole context, current token included: one call of
+paged_attn_decode_append, or (step_separate) kv_quantize_store followed by
+paged_attn_decode.
 """
 
 from dataclasses import dataclass
@@ -63,9 +65,16 @@ class DecodeSetup:
         self.pool.decode(self.q, self.out, self.tables, self.ctx_dev, self.max_ctx,
                          self.sm_scale, self.partition, self.workspace, stream, mem=self._mem(r))
 
-    def step(self, stream=None, r=0):
+    def step_separate(self, stream=None, r=0):
+        """The step as two calls: kv_quantize_store, then paged_attn_decode."""
         self.store_current(stream, r)
         self.attend(stream, r)
+
+    def step(self, stream=None, r=0):
+        """The step as one call: paged_attn_decode_append (store fused in)."""
+        self.pool.decode_append(self.k_new, self.v_new, self.slots, self.q, self.out, self.tables,
+                                self.ctx_dev, self.max_ctx, self.sm_scale, self.partition,
+                                self.workspace, stream, mem=self._mem(r))
 
 
 def _store(pool, k, v, seq_ids, starts, device):

@@ -1,10 +1,11 @@
-"""HBM traffic of one paged_attn_decode call, from rocprofv3 counters.
+"""HBM traffic of one decode step (paged_attn_decode_append: the current
+token's store and the attention), from rocprofv3 counters.
 
 Two steps, each a command of its own:
 
 ``python -m paged_block_quantized_amd.traffic run --workload W``
     the program to profile: sets up workload W, makes ``--calls`` decode
-    calls cycling through ``--rotate`` copies of the pool (as bench.py times
+    steps cycling through ``--rotate`` copies of the pool (as bench.py times
     them), then ``--copies`` passes of a plain elementwise kernel that reads
     1 GiB and writes 1 GiB (bitwise not of a uint8 tensor; a torch copy_
     would go to the DMA engine, which the counters do not see).  Run it
@@ -14,7 +15,8 @@ Two steps, each a command of its own:
 ``python -m paged_block_quantized_amd.traffic summarize --workload W
   --fetch DIR --write DIR --out profiles/traffic_W.json``
     reads the two counter_collection CSV files, takes the median counter per
-    dispatch of the decode kernels (partition + reduce) and of the
+    dispatch of the step's kernels (partition, reduce, and the store kernel
+    where the step launches it; the last --calls dispatches) and of the
     calibration kernel, scales each counter by (known bytes / calibration
     counter), and writes bytes per decode call with the hash of the kernel
     source.
@@ -34,7 +36,7 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 COPY_BYTES = 1 << 30
-DECODE_KERNELS = ("attn_partition_", "attn_reduce")
+DECODE_KERNELS = ("attn_partition_", "attn_reduce", "quantize_store")
 
 
 def kernel_source_hash():
@@ -56,7 +58,7 @@ def run(args):
     if args.rotate > 1:
         setup.add_replicas(args.rotate - 1)
     for i in range(args.calls):
-        setup.attend(r=i % max(1, args.rotate))
+        setup.step(r=i % max(1, args.rotate))
     torch.cuda.synchronize()
     src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -79,16 +81,16 @@ def _counter_rows(d):
 
 
 def _per_kernel(rows, counter):
-    """{kernel name: [counter value per dispatch]} (values summed over the
-    dimensions rocprofv3 reports for one dispatch)."""
+    """{kernel name: [counter value per dispatch]} in dispatch order (values
+    summed over the dimensions rocprofv3 reports for one dispatch)."""
     per = {}
     for r in rows:
         if r.get("Counter_Name") != counter:
             continue
-        key = (r["Kernel_Name"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        key = (r["Kernel_Name"], int(r.get("Dispatch_Id") or r.get("Correlation_Id")))
         per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
     out = {}
-    for (name, _), v in per.items():
+    for (name, _), v in sorted(per.items(), key=lambda kv: kv[0][1]):
         out.setdefault(name, []).append(v)
     return out
 
@@ -110,7 +112,10 @@ def summarize(args):
         ck = _copy_kernel(per)
         copy_val = statistics.median(per[ck])
         scale = known / copy_val
-        dec = {n: statistics.median(v) for n, v in per.items() if any(k in n for k in DECODE_KERNELS)}
+        # the step calls are each kernel's last `calls` dispatches (earlier
+        # store dispatches build the pool)
+        dec = {n: statistics.median(v[-args.calls:]) for n, v in per.items()
+               if any(k in n for k in DECODE_KERNELS)}
         if not dec:
             raise SystemExit("decode kernels not found")
         dec_bytes = sum(v * scale for v in dec.values())
@@ -144,6 +149,7 @@ def main():
     s.add_argument("--write", required=True)
     s.add_argument("--out", required=True)
     s.add_argument("--algorithmic", type=int, default=0)
+    s.add_argument("--calls", type=int, default=8)
     args = ap.parse_args()
     (run if args.cmd == "run" else summarize)(args)
 

@@ -158,8 +158,27 @@ def test_device_calls_validate_before_launch(lib):
     desc4 = L.make_desc(8, 16, 2, 64, L.KV_CODEC_I4_ASYM)
     with pytest.raises(L.PBQError, match="v_zp"):
         L.kv_copy_blocks(desc4, mem, base, 1, 0)
+    # the fused store + decode checks its new-token arguments as well
+    with pytest.raises(L.PBQError, match="k_new"):
+        L.paged_attn_decode_append(desc, mem, None, base, base, base, base, 1, 2, base, 4, base,
+                                   64, 0.1, 0, None, 0, 0)
+    with pytest.raises(L.PBQError, match="k_new"):
+        L.paged_attn_decode_append(desc, mem, base + 4, base, base, base, base, 1, 2, base, 4,
+                                   base, 64, 0.1, 0, None, 0, 0)
+    with pytest.raises(L.PBQError, match="tail_slots"):
+        L.paged_attn_decode_append(desc, mem, base, base, None, base, base, 1, 2, base, 4, base,
+                                   64, 0.1, 0, None, 0, 0)
+    no_tail = L.kv_pool_mem(base, base, base, base, None, None, None)
+    with pytest.raises(L.PBQError, match="tail slots"):
+        L.paged_attn_decode_append(desc, no_tail, base, base, base, base, base, 1, 2, base, 4,
+                                   base, 64, 0.1, 0, None, 0, 0)
+    with pytest.raises(L.PBQError, match="multiple of num_kv_heads"):
+        L.paged_attn_decode_append(desc, mem, base, base, base, base, base, 1, 3, base, 4, base,
+                                   64, 0.1, 0, None, 0, 0)
     # zero-sized work is a no-op that succeeds without touching the device
     L.kv_quantize_store(desc, mem, base, base, 0, base, base, base, 4, base, 0, 0)
+    L.paged_attn_decode_append(desc, mem, base, base, base, base, base, 0, 2, base, 4, base, 64,
+                               0.1, 0, None, 0, 0)
     L.kv_copy_blocks(desc, mem, None, 0, 0)
 
 
@@ -169,3 +188,26 @@ def test_workspace_bytes(lib):
     assert L.paged_attn_workspace_bytes(desc, 32, 32, 4096, 512) == 32 * 32 * 8 * (128 * 4 + 8)
     assert L.paged_attn_workspace_bytes(desc, 32, 32, 512, 512) == 0
     assert L.paged_attn_default_partition(desc, 32, 32, 4096) % 32 == 0
+
+
+def test_default_partition_policy(lib):
+    """One pass when the sequence x head units fill the GPU (four work
+    groups per compute unit; 256 when no device can be queried) and contexts
+    fit in 4096 tokens; otherwise 2048-token partitions, halved to 256 while
+    the grid is small."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
+    mha = L.make_desc(8192, 16, 32, 128)
+    gqa = L.make_desc(8192, 32, 8, 128)
+    target = 4 * cus
+    if 32 * 32 >= target:
+        assert L.paged_attn_default_partition(mha, 32, 32, 4096) == 4096
+    assert L.paged_attn_default_partition(mha, 32, 32, 4000) % 32 == 0
+    # long contexts: 2048-token partitions when the grid is large enough
+    assert L.paged_attn_default_partition(mha, 32, 32, 32768) == 2048
+    # one sequence, one head: the smallest partition
+    assert L.paged_attn_default_partition(mha, 1, 32, 4096) == 256
+    # grouped query heads count KV heads x 16-head tiles
+    p = L.paged_attn_default_partition(gqa, 128, 64, 1968)
+    assert p == (1984 if 128 * 8 >= target else p) and p % 32 == 0
+    assert lib.paged_attn_default_partition(None, 1, 1, 1) == 0

@@ -266,3 +266,85 @@ def test_gqa_rejects_partition_not_multiple_of_32():
     case.store_all()
     with pytest.raises(PBQError, match="multiple of 32"):
         case.decode(16)
+
+
+APPEND_SHAPES = [(bs, d, vc, 1) for bs in (16, 32) for d in (64, 128) for vc in ("i8", "i4")] + [
+    (32, 128, "i4", 8), (16, 128, "i8", 4)]
+
+
+@pytest.mark.parametrize("bs,d,vc,g", APPEND_SHAPES)
+def test_decode_append_equals_store_then_decode(bs, d, vc, g):
+    """paged_attn_decode_append (the current token's store fused into the
+    decode) leaves the pool bit-identical to kv_quantize_store followed by
+    paged_attn_decode -- codes, scales, zero points and tail slots -- and both
+    outputs agree with the oracle.  Context lengths put the new token at the
+    start, the middle and the end of a block."""
+    announce("decode-append", bs, d, vc, g)
+    from paged_block_quantized_amd import KVPool
+    hkv = 2
+    hq = g * hkv
+    ctx = [1, 2, bs - 1, bs, bs + 1, 2 * bs, 3 * bs + 5, 700, 1100]
+    S = len(ctx)
+    rng = np.random.default_rng(1000 * bs + d + 7 * g + (vc == "i4"))
+    hk = [rng.standard_normal((c, hkv, d)).astype(np.float16) for c in ctx]
+    hv = [rng.standard_normal((c, hkv, d)).astype(np.float16) for c in ctx]
+    q = rng.standard_normal((S, hq, d)).astype(np.float16)
+    n_blocks = sum((c + bs - 1) // bs for c in ctx) + 2
+    order = rng.permutation(n_blocks)
+    max_blocks = max((c + bs - 1) // bs for c in ctx)
+    sm = 1.0 / np.sqrt(d)
+    dev = torch.device("cuda")
+
+    def build():
+        pool = KVPool(n_blocks, bs, hkv, d, vc, max_seqs=S, free_order=order)
+        for s, c in enumerate(ctx):
+            pool.alloc(s, c - 1)
+        tables, _, slots = pool.batch_tables(list(range(S)), max_blocks)
+        lens = [c - 1 for c in ctx]
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+        k = torch.from_numpy(np.concatenate([h[:c - 1] for h, c in zip(hk, ctx)])).to(dev)
+        v = torch.from_numpy(np.concatenate([h[:c - 1] for h, c in zip(hv, ctx)])).to(dev)
+        pool.quantize_store(k, v, cu, torch.zeros(S, dtype=torch.int32, device=dev),
+                            tables.to(dev), slots.to(dev), max(lens))
+        for s in range(S):
+            assert pool.append(s, 1) == []
+        tables, ctx_h, slots = pool.batch_tables(list(range(S)), max_blocks)
+        assert list(ctx_h.numpy()) == ctx
+        for s in range(S):
+            assert pool.table(s)[0] == model.table(s)[0], f"seq {s} table"
+        return pool, tables.to(dev), ctx_h.to(dev), slots.to(dev)
+
+    k_new = torch.from_numpy(np.stack([h[c - 1] for h, c in zip(hk, ctx)])).to(dev)
+    v_new = torch.from_numpy(np.stack([h[c - 1] for h, c in zip(hv, ctx)])).to(dev)
+    qd = torch.from_numpy(q).to(dev)
+    # the oracle: every row stored, tables from the allocator model
+    model = A.BlockPoolModel(n_blocks, bs, S, order)
+    opool = paged.PoolArrays(n_blocks, hkv, bs, d, vc == "i4")
+    for s, c in enumerate(ctx):          # the same call order as build()
+        model.alloc(s, c - 1)
+    for s, c in enumerate(ctx):
+        model.append(s, 1)
+        paged.store_range(opool, model.table(s)[0], hk[s], hv[s], 0, c)
+    ref = attention.paged_decode(opool, [model.table(s)[0] for s in range(S)], ctx, q, sm)
+
+    # 2048 covers every context: one partition (the fused kernel for MHA)
+    for part in (0, 32 if g > 1 else bs, 1024, 2048):
+        pa, ta, ca, sa = build()
+        pa.quantize_store(k_new, v_new, torch.arange(S + 1, dtype=torch.int32, device=dev),
+                          ca - 1, ta, sa, 1)
+        out_a = torch.empty_like(qd)
+        pa.decode(qd, out_a, ta, ca, max(ctx), sm, part)
+        pb, tb, cb, sb = build()
+        out_b = torch.empty_like(qd)
+        pb.decode_append(k_new, v_new, sb, qd, out_b, tb, cb, max(ctx), sm, part)
+        torch.cuda.synchronize()
+        for name in ("k_codes", "v_codes", "k_scale", "v_scale", "tail_k", "tail_v") + (("v_zp",) if vc == "i4" else ()):
+            x, y = pa.arrays[name].cpu().numpy(), pb.arrays[name].cpu().numpy()
+            assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f"{name} differs (part {part})"
+        g_k = pb.k_codes.cpu().numpy()
+        bad = [(s, j, b) for s in range(S) for j, b in enumerate(model.table(s)[0])
+               if not np.array_equal(g_k[b], opool.k_codes[b])]
+        assert not bad, f"K codes differ at (seq, block, phys) {bad[:6]}"
+        assert_pool_equal(pb, opool)
+        assert_close(out_a.cpu().numpy(), ref, f"store+decode part {part}")
+        assert_close(out_b.cpu().numpy(), ref, f"decode_append part {part}")
