@@ -268,11 +268,11 @@ kv_status paged_attn_decode(const kv_pool_desc* desc, const kv_pool_mem* mem,
  * tail-slot rows, bit for bit), then the attention of paged_attn_decode over
  * context_lens[s] tokens, the new one included.  The caller has reserved the
  * position (kv_seq_append) and performed its copy-on-write copies; the
- * block may not be shared with another sequence of the call.  One query head
- * per KV head and a single partition per sequence: the last block's store
- * runs inside the attention kernel (two of the work group's waves quantize
- * its K and V tiles, which the attention then reads from LDS), a single
- * launch; otherwise the store kernel, then the decode.  Arguments and errors otherwise as paged_attn_decode; the pool's
+ * block may not be shared with another sequence of the call.  With a single
+ * partition per sequence, the last block's store runs inside the attention
+ * kernel (two of the work group's waves quantize its K and V tiles, which
+ * the attention then reads from LDS): one launch.  With split partitions,
+ * the store kernel runs first, then the decode.  Arguments and errors otherwise as paged_attn_decode; the pool's
  * tail slots must be set in mem.  [tbr8] §4 store_kv and §5 point 2;
  * [yunthe] Q(x) and x_hat. */
 kv_status paged_attn_decode_append(const kv_pool_desc* desc, const kv_pool_mem* mem,

@@ -473,7 +473,7 @@ __device__ __forceinline__ uint32_t pk_sub_f16(uint32_t x, uint32_t off2) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, x) - __builtin_bit_cast(f16x2, off2));
 }
 
-template <int BS, int D, bool V4, int NW>
+template <int BS, int D, bool V4, int NW, bool FUSED>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA_WAVES_PER_EU))) void attn_partition_gqa(AttnArgs a) {
     static_assert(BS == 16 || BS == 32, "block size");
     constexpr int KS = D / 32;                 // QK k-steps
@@ -557,16 +557,149 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
         uint32_t v[DT][VB / 4];
     };
 
-    // A wave takes the steps w, w + NW, ... of the partition.  Lane L stages
-    // the block id, scales and zero point of sub-block L % BPS of the wave's
+    // Codes of one 32-token step: the lane's K rows and V row come from the
+    // tile of block 0 or block 1 of the step (bs 16), whose K and V tile
+    // bases are given (pool or LDS copy).
+    auto load_step = [&](const int8_t* k0, const int8_t* k1, const uint8_t* v0, const uint8_t* v1, Raw& r) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int8_t* kp = (BPS == 1 || !kblk[mt] ? k0 : k1) + krow[mt] * D + 16 * grp;
+#pragma unroll
+            for (int c = 0; c < KCH / 16; ++c) r.k[mt][c] = *(const u32x4*)(kp + 64 * c);
+        }
+        const uint8_t* vp = (BPS == 1 || !my_blk ? v0 : v1) + vcol;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            const uint8_t* row = vp + (16 * t + n16) * VROW;
+            if constexpr (V4) {
+                r.v[t][0] = *(const uint32_t*)row;
+            } else {
+                const u32x2 x = *(const u32x2*)row;
+                r.v[t][0] = x[0];
+                r.v[t][1] = x[1];
+            }
+        }
+    };
+
+    // One step: scores on MFMA, online softmax, PV on MFMA.  sk, sv, zpv are
+    // this lane's block's scales (sk times sm_scale log2 e) and zero point.
+    auto compute_step = [&](const Raw& r, int st, float sk, float sv, float zpv) {
+        // ---- S^T = K_hat Q^T ----------------------------------------------
+        f32x4 sc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            sc[mt] = (f32x4)0.f;
+#pragma unroll
+            for (int j = 0; j < KS; ++j) {
+                const uint32_t u0 = r.k[mt][j / 2][2 * (j & 1)] ^ 0x80808080u;
+                const uint32_t u1 = r.k[mt][j / 2][2 * (j & 1) + 1] ^ 0x80808080u;
+                const uint32_t a4[4] = {__builtin_amdgcn_perm(kF16Hi, u0, kSelLo), __builtin_amdgcn_perm(kF16Hi, u0, kSelHi),
+                                        __builtin_amdgcn_perm(kF16Hi, u1, kSelLo), __builtin_amdgcn_perm(kF16Hi, u1, kSelHi)};
+                const f16x8v aop = __builtin_bit_cast(f16x8v, a4);
+                sc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, qop[j], sc[mt], 0, 0, 0);
+            }
+        }
+        // lane (head n16, group grp): sc[mt][i] is token 8 grp + kappa(4 mt + i)
+        float x[8];
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = tok0 + 32 * st + 8 * grp + kappa<V4>(4 * mt + e);
+                const float v = (sc[mt][e] - qbias) * sk;
+                x[4 * mt + e] = t < tok1 ? v : -INFINITY;
+                bmax = fmaxf(bmax, x[4 * mt + e]);
+            }
+        // every step holds at least one valid token, so bmax is finite
+        bmax = fmaxf(bmax, shfl_xor_f(bmax, 16));
+        bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
+        if (bmax > m) {   // per head; lanes of one head agree
+            const float alpha = __builtin_amdgcn_exp2f(m - bmax);
+#pragma unroll
+            for (int t = 0; t < DT; ++t) acc[t] *= alpha;
+            l *= alpha;
+            m = bmax;
+        }
+        uint32_t pw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(x[2 * e] - m);
+            const float p1 = __builtin_amdgcn_exp2f(x[2 * e + 1] - m);
+            l += p0 + p1;
+            const f16x2 h2 = f16x2{(_Float16)(p0 * sv), (_Float16)(p1 * sv)};
+            pw[e] = __builtin_bit_cast(uint32_t, h2);
+        }
+        const f16x8v pop = __builtin_bit_cast(f16x8v, pw);
+
+        // ---- O^T += V_hat^T P^T --------------------------------------------
+        const _Float16 vo = (_Float16)((V4 ? kI4Bias : kI8Bias) + zpv);
+        const uint32_t off2 = __builtin_bit_cast(uint32_t, f16x2{vo, vo});
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            uint32_t a4[4];
+            if constexpr (V4) {
+                const uint32_t wv = r.v[t][0];
+                const uint32_t lo = wv & 0x0F0F0F0Fu, hi = (wv >> 4) & 0x0F0F0F0Fu;
+                a4[0] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, lo, kSelLo), off2);
+                a4[1] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, lo, kSelHi), off2);
+                a4[2] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, hi, kSelLo), off2);
+                a4[3] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, hi, kSelHi), off2);
+            } else {
+                const uint32_t u0 = r.v[t][0] ^ 0x80808080u, u1 = r.v[t][1] ^ 0x80808080u;
+                a4[0] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u0, kSelLo), off2);
+                a4[1] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u0, kSelHi), off2);
+                a4[2] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u1, kSelLo), off2);
+                a4[3] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u1, kSelHi), off2);
+            }
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8v, a4), pop, acc[t], 0, 0, 0);
+        }
+    };
+
+    // Fused store of the current token (position ctx - 1), single-partition
+    // launches: waves 0 and 1 re-quantize the last block's K and V tiles
+    // (store_tile; only the first 16-head tile of a KV head writes the pool),
+    // leave LDS copies, and take fewer of the other steps; after a barrier,
+    // wave NW - 1 computes the last step with the last block read from LDS.
+    __shared__ __align__(16) uint8_t s_tile[FUSED ? KT + VT : 16];
+    __shared__ uint32_t s_tscale[3];
+    const bool fused = FUSED && nblk > 0;   // one partition: this group holds the last block
+    if (fused && w < 2) {
+        const TileStoreArgs t{const_cast<int8_t*>(a.k_codes), const_cast<uint8_t*>(a.v_codes),
+                              const_cast<uint16_t*>(a.k_scale), const_cast<uint16_t*>(a.v_scale),
+                              const_cast<uint8_t*>(a.v_zp), a.tail_k, a.tail_v, a.k_new, a.v_new, H};
+        const int last = nblk - 1;
+        const int slot = a.tail_slots[s], phys = tab[last];
+        if (w == 0) {
+            const TileScales ts = store_tile<BS, D, V4, true, true, false>(
+                t, kvh, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, ht == 0);
+            if (lane == 0) s_tscale[0] = ts.k_scale;
+        } else {
+            const TileScales ts = store_tile<BS, D, V4, true, false, true>(
+                t, kvh, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, ht == 0);
+            if (lane == 0) {
+                s_tscale[1] = ts.v_scale;
+                s_tscale[2] = ts.v_zp;
+            }
+        }
+    }
+
+    // Each wave takes a contiguous run of the steps (the last one excluded in
+    // a fused group, where waves 0 and 1 take `hc` fewer).  Lane L stages the
+    // block id and raw scale bits of sub-block L % BPS of the run's
     // (L / BPS)-th step of the batch; the loop reads them with readlane.  The
-    // next step's codes are loaded before the current step is computed.
-    for (int base = w; base < nsteps; base += NW * SPB) {
-        const int st_l = base + (lane / BPS) * NW;
+    // next steps' codes are loaded while one is computed.
+    const int n_loop = fused ? nsteps - 1 : nsteps;
+    const int hc = fused ? min(PBQ_STORE_HANDICAP_TOKENS / 32, n_loop / NW) : 0;
+    const int q = (n_loop + 2 * hc) / NW, rem = (n_loop + 2 * hc) % NW;
+    const int w_start = w * q + min(w, rem) - min(w, 2) * hc;
+    const int w_stop = w_start + q + (w < rem ? 1 : 0) - (w < 2 ? hc : 0);
+    for (int base = w_start; base < w_stop; base += SPB) {
+        const int st_l = base + lane / BPS;
         const int blk_l = blk0 + st_l * BPS + lane % BPS;
-        const bool ok_l = st_l < nsteps && blk_l < blk_end;
+        const bool ok_l = st_l < w_stop && blk_l < blk_end;
         const int id_l = ok_l ? tab[blk_l] : 0;
-        const int cnt = min(SPB, (nsteps - base + NW - 1) / NW);
+        const int cnt = min(SPB, w_stop - base);
         int sk_l, sv_l, zp_l = 0;   // raw scale bits and zero point (converted at use)
 
         // Loads are unconditional: a block past the partition's end has id 0
@@ -574,121 +707,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
         // zero softmax weights.  (Branches here would also make the compiler
         // wait for every outstanding load, the prefetch included.)
         auto load = [&](int i, Raw& r) {
-            int ids[BPS];
-#pragma unroll
-            for (int b = 0; b < BPS; ++b) ids[b] = readlane(id_l, i * BPS + b);
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const int id = BPS == 1 ? ids[0] : (kblk[mt] ? ids[BPS - 1] : ids[0]);
-                const int8_t* kp = a.k_codes + ((int64_t)id * H + kvh) * KT + krow[mt] * D + 16 * grp;
-#pragma unroll
-                for (int c = 0; c < KCH / 16; ++c) r.k[mt][c] = *(const u32x4*)(kp + 64 * c);
-            }
-            const int vid = BPS == 1 ? ids[0] : (my_blk ? ids[BPS - 1] : ids[0]);
-            const uint8_t* vp = a.v_codes + ((int64_t)vid * H + kvh) * VT + vcol;
-#pragma unroll
-            for (int t = 0; t < DT; ++t) {
-                const uint8_t* row = vp + (16 * t + n16) * VROW;
-                if constexpr (V4) {
-                    r.v[t][0] = *(const uint32_t*)row;
-                } else {
-                    const u32x2 x = *(const u32x2*)row;
-                    r.v[t][0] = x[0];
-                    r.v[t][1] = x[1];
-                }
-            }
+            const int id0 = readlane(id_l, i * BPS), id1 = readlane(id_l, i * BPS + BPS - 1);
+            load_step(a.k_codes + ((int64_t)id0 * H + kvh) * KT, a.k_codes + ((int64_t)id1 * H + kvh) * KT,
+                      a.v_codes + ((int64_t)id0 * H + kvh) * VT, a.v_codes + ((int64_t)id1 * H + kvh) * VT, r);
         };
 
         auto compute = [&](const Raw& r, int i) {
-            const int st = base + i * NW;
+            const int st = base + i;
             // per-lane scales of the block holding this lane group's tokens.
             // The second block of a 16-token pair may lie past the end (its
             // staged id is 0): its tokens are masked, and its scales are
             // replaced by 0 so that stale pool contents cannot reach the sums.
-            float sk, sv, zpv;
             if constexpr (BPS == 1) {
-                sk = bits_to_f16f((uint16_t)readlane(sk_l, i)) * c2;
-                sv = bits_to_f16f((uint16_t)readlane(sv_l, i));
-                zpv = (float)readlane(zp_l, i);
+                compute_step(r, st, bits_to_f16f((uint16_t)readlane(sk_l, i)) * c2,
+                             bits_to_f16f((uint16_t)readlane(sv_l, i)), (float)readlane(zp_l, i));
             } else {
                 const bool live1 = blk0 + st * BPS + 1 < blk_end;
                 const int k0 = readlane(sk_l, 2 * i), k1 = live1 ? readlane(sk_l, 2 * i + 1) : 0;
                 const int v0 = readlane(sv_l, 2 * i), v1 = live1 ? readlane(sv_l, 2 * i + 1) : 0;
                 const int z0 = readlane(zp_l, 2 * i), z1 = live1 ? readlane(zp_l, 2 * i + 1) : 0;
-                sk = bits_to_f16f((uint16_t)(my_blk ? k1 : k0)) * c2;
-                sv = bits_to_f16f((uint16_t)(my_blk ? v1 : v0));
-                zpv = (float)(my_blk ? z1 : z0);
-            }
-
-            // ---- S^T = K_hat Q^T ----------------------------------------------
-            f32x4 sc[2];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                sc[mt] = (f32x4)0.f;
-#pragma unroll
-                for (int j = 0; j < KS; ++j) {
-                    const uint32_t u0 = r.k[mt][j / 2][2 * (j & 1)] ^ 0x80808080u;
-                    const uint32_t u1 = r.k[mt][j / 2][2 * (j & 1) + 1] ^ 0x80808080u;
-                    const uint32_t a4[4] = {__builtin_amdgcn_perm(kF16Hi, u0, kSelLo), __builtin_amdgcn_perm(kF16Hi, u0, kSelHi),
-                                            __builtin_amdgcn_perm(kF16Hi, u1, kSelLo), __builtin_amdgcn_perm(kF16Hi, u1, kSelHi)};
-                    const f16x8v aop = __builtin_bit_cast(f16x8v, a4);
-                    sc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, qop[j], sc[mt], 0, 0, 0);
-                }
-            }
-            // lane (head n16, group grp): sc[mt][i] is token 8 grp + kappa(4 mt + i)
-            float x[8];
-            float bmax = -INFINITY;
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = tok0 + 32 * st + 8 * grp + kappa<V4>(4 * mt + e);
-                    const float v = (sc[mt][e] - qbias) * sk;
-                    x[4 * mt + e] = t < tok1 ? v : -INFINITY;
-                    bmax = fmaxf(bmax, x[4 * mt + e]);
-                }
-            // every step holds at least one valid token, so bmax is finite
-            bmax = fmaxf(bmax, shfl_xor_f(bmax, 16));
-            bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
-            if (bmax > m) {   // per head; lanes of one head agree
-                const float alpha = __builtin_amdgcn_exp2f(m - bmax);
-#pragma unroll
-                for (int t = 0; t < DT; ++t) acc[t] *= alpha;
-                l *= alpha;
-                m = bmax;
-            }
-            uint32_t pw[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float p0 = __builtin_amdgcn_exp2f(x[2 * e] - m);
-                const float p1 = __builtin_amdgcn_exp2f(x[2 * e + 1] - m);
-                l += p0 + p1;
-                const f16x2 h2 = f16x2{(_Float16)(p0 * sv), (_Float16)(p1 * sv)};
-                pw[e] = __builtin_bit_cast(uint32_t, h2);
-            }
-            const f16x8v pop = __builtin_bit_cast(f16x8v, pw);
-
-            // ---- O^T += V_hat^T P^T --------------------------------------------
-            const _Float16 vo = (_Float16)((V4 ? kI4Bias : kI8Bias) + zpv);
-            const uint32_t off2 = __builtin_bit_cast(uint32_t, f16x2{vo, vo});
-#pragma unroll
-            for (int t = 0; t < DT; ++t) {
-                uint32_t a4[4];
-                if constexpr (V4) {
-                    const uint32_t wv = r.v[t][0];
-                    const uint32_t lo = wv & 0x0F0F0F0Fu, hi = (wv >> 4) & 0x0F0F0F0Fu;
-                    a4[0] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, lo, kSelLo), off2);
-                    a4[1] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, lo, kSelHi), off2);
-                    a4[2] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, hi, kSelLo), off2);
-                    a4[3] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, hi, kSelHi), off2);
-                } else {
-                    const uint32_t u0 = r.v[t][0] ^ 0x80808080u, u1 = r.v[t][1] ^ 0x80808080u;
-                    a4[0] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u0, kSelLo), off2);
-                    a4[1] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u0, kSelHi), off2);
-                    a4[2] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u1, kSelLo), off2);
-                    a4[3] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u1, kSelHi), off2);
-                }
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8v, a4), pop, acc[t], 0, 0, 0);
+                compute_step(r, st, bits_to_f16f((uint16_t)(my_blk ? k1 : k0)) * c2,
+                             bits_to_f16f((uint16_t)(my_blk ? v1 : v0)), (float)(my_blk ? z1 : z0));
             }
         };
 
@@ -699,6 +738,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
             if constexpr (V4) zp_l = a.v_zp[t];
         };
         pipelined<PBQ_GQA_DEPTH, Raw>(cnt, load, compute, scales);
+    }
+    if (FUSED && fused) {
+        __syncthreads();   // waves 0 and 1 have left the last block's tiles in LDS
+        if (w == NW - 1) {
+            // the last step: its last block from LDS; in a 16-token pair whose
+            // second block is the last one, the first block from the pool
+            const int st = nsteps - 1;
+            const int last = nblk - 1;
+            const int first = blk0 + st * BPS;            // == last when it is alone
+            const int64_t t0 = (int64_t)tab[first] * H + kvh;
+            const int8_t* lk = (const int8_t*)s_tile;
+            const uint8_t* lv = s_tile + KT;
+            const bool pair = first != last;              // block `first` comes from the pool
+            Raw r;
+            load_step(pair ? a.k_codes + t0 * KT : lk, lk, pair ? a.v_codes + t0 * VT : lv, lv, r);
+            const uint32_t ks0 = pair ? a.k_scale[t0] : s_tscale[0];
+            const uint32_t vs0 = pair ? a.v_scale[t0] : s_tscale[1];
+            const uint32_t z0 = pair ? (V4 ? a.v_zp[t0] : 0u) : s_tscale[2];
+            // a lane group's block: `first` (my_blk 0) or the block after it,
+            // which is the last block or lies past the end (masked)
+            const bool mine_last = BPS == 1 || my_blk ? true : !pair;
+            compute_step(r, st, bits_to_f16f((uint16_t)(mine_last ? s_tscale[0] : ks0)) * c2,
+                         bits_to_f16f((uint16_t)(mine_last ? s_tscale[1] : vs0)),
+                         (float)(mine_last ? s_tscale[2] : z0));
+        }
     }
     // lanes of one head split its tokens by group: sum their partial sums
     l += shfl_xor_f(l, 16);
@@ -824,16 +888,25 @@ hipError_t launch_mha(const AttnArgs& a, hipStream_t stream) {
 }
 
 // Waves per work group of the grouped-query kernel: 2 for a single pass (the
-// sequences' work groups then all fit on the GPU at once), else 4.
+// sequences' work groups then all fit on the GPU at once), else 4; the
+// single pass with the fused store uses PBQ_GQA_FUSED_WAVES.
+#ifndef PBQ_GQA_FUSED_WAVES
+#define PBQ_GQA_FUSED_WAVES 3
+#endif
 template <int BS, int D, bool V4>
 hipError_t launch_gqa(const AttnArgs& a, hipStream_t stream) {
     const int G = a.num_q_heads / a.num_kv_heads;
     const int n_ht = (G + 15) / 16;
     const dim3 grid = grid_dims(a.max_partitions, a.num_kv_heads * n_ht, a.num_seqs);
-    if (a.max_partitions == 1)
-        hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, 2>), grid, dim3(64 * 2), 0, stream, a);
-    else
-        hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, 4>), grid, dim3(64 * 4), 0, stream, a);
+    if (a.max_partitions == 1) {
+        if (a.k_new != nullptr)
+            hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, PBQ_GQA_FUSED_WAVES, true>), grid,
+                               dim3(64 * PBQ_GQA_FUSED_WAVES), 0, stream, a);
+        else
+            hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, 2, false>), grid, dim3(64 * 2), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, 4, false>), grid, dim3(64 * 4), 0, stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_partitions <= 1) return e;
     hipLaunchKernelGGL((attn_reduce<BS, D>), dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(64), 0,

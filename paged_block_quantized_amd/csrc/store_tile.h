@@ -70,10 +70,12 @@ __device__ __forceinline__ int rne_quot(float x, float s, float rcp, float half_
 // also written to lds_k / lds_v in the tile layout.  Called by a whole wave.
 // DO_K / DO_V select the tensors: the store kernel does both in one wave
 // (all rows in flight at once); the fused decode gives them to two waves,
-// which halves the registers either needs.
+// which halves the registers either needs.  With wr false nothing is written
+// to the pool (only the LDS copy), for callers that share a tile.
 template <int BS, int D, bool V4, bool LDS, bool DO_K = true, bool DO_V = true>
 __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, int slot, int c0, int sp,
-                                                 int end, int j, int phys, int8_t* lds_k, uint8_t* lds_v) {
+                                                 int end, int j, int phys, int8_t* lds_k, uint8_t* lds_v,
+                                                 bool wr = true) {
     constexpr int LPR = D / 8;     // lanes per token row
     constexpr int RPI = 64 / LPR;  // rows per wave access
     constexpr int NIT = BS / RPI;  // accesses per lane per tensor
@@ -157,10 +159,10 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
                 }
             }
             const int r = it * RPI + r_in;
-            *(u32x2*)(dst + r * D + col) = u32x2{w[0], w[1]};
+            if (wr) *(u32x2*)(dst + r * D + col) = u32x2{w[0], w[1]};
             if constexpr (LDS) *(u32x2*)(lds_k + r * D + col) = u32x2{w[0], w[1]};
         }
-        if (lane == 0) a.k_scale[tile] = s16;
+        if (wr && lane == 0) a.k_scale[tile] = s16;
         out.k_scale = s16;
     }
 
@@ -195,9 +197,11 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
                 }
             }
             uint32_t* drow = (uint32_t*)(dst + (DPL * lane + k) * BS);
+            if (wr) {
 #pragma unroll
-            for (int i = 0; i < BS / 16; ++i)
-                *(u32x4*)(drow + 4 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+                for (int i = 0; i < BS / 16; ++i)
+                    *(u32x4*)(drow + 4 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+            }
             if constexpr (LDS) {
                 uint32_t* lrow = (uint32_t*)(lds_v + (DPL * lane + k) * BS);
 #pragma unroll
@@ -205,7 +209,7 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
                     *(u32x4*)(lrow + 4 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
             }
         }
-        if (lane == 0) a.v_scale[tile] = s16;
+        if (wr && lane == 0) a.v_scale[tile] = s16;
         out.v_scale = s16;
     } else if constexpr (DO_V) {
         float lo = 0.f, hi = 0.f;  // range widened to contain 0
@@ -247,17 +251,17 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
             uint32_t* drow = (uint32_t*)(dst + (DPL * lane + k) * (BS / 2));
             uint32_t* lrow = LDS ? (uint32_t*)(lds_v + (DPL * lane + k) * (BS / 2)) : nullptr;
             if constexpr (BS == 16) {
-                *(u32x2*)drow = u32x2{w[0], w[1]};
+                if (wr) *(u32x2*)drow = u32x2{w[0], w[1]};
                 if constexpr (LDS) *(u32x2*)lrow = u32x2{w[0], w[1]};
             } else {
 #pragma unroll
                 for (int i = 0; i < BS / 32; ++i) {
-                    *(u32x4*)(drow + 4 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+                    if (wr) *(u32x4*)(drow + 4 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
                     if constexpr (LDS) *(u32x4*)(lrow + 4 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
                 }
             }
         }
-        if (lane == 0) {
+        if (wr && lane == 0) {
             a.v_scale[tile] = s16;
             a.v_zp[tile] = (uint8_t)zp;
         }
@@ -266,7 +270,7 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
     }
 
     // ---- tail slot: exact rows of a block that stays partial ----------------
-    if (end % BS != 0 && j == (end - 1) / BS) {
+    if (wr && end % BS != 0 && j == (end - 1) / BS) {
         if constexpr (DO_K) {
 #pragma unroll
             for (int it = 0; it < NIT; ++it) {

@@ -81,7 +81,7 @@ def _counter_rows(d):
 
 
 def _per_kernel(rows, counter):
-    """{kernel name: [counter value per dispatch]} in dispatch order (values
+    """{kernel name: [(dispatch id, counter value)]} in dispatch order (values
     summed over the dimensions rocprofv3 reports for one dispatch)."""
     per = {}
     for r in rows:
@@ -90,8 +90,8 @@ def _per_kernel(rows, counter):
         key = (r["Kernel_Name"], int(r.get("Dispatch_Id") or r.get("Correlation_Id")))
         per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
     out = {}
-    for (name, _), v in sorted(per.items(), key=lambda kv: kv[0][1]):
-        out.setdefault(name, []).append(v)
+    for (name, did), v in sorted(per.items(), key=lambda kv: kv[0][1]):
+        out.setdefault(name, []).append((did, v))
     return out
 
 
@@ -103,6 +103,23 @@ def _copy_kernel(per):
     return cands[0]
 
 
+def _step_kernels(per, calls):
+    """{kernel: median counter per step} over the dispatches of the last
+    `calls` steps: those from the first of the partition kernel's last
+    `calls` dispatches on (earlier store dispatches build the pool)."""
+    parts = [d for n, v in per.items() if "attn_partition_" in n for d, _ in v]
+    if len(parts) < calls:
+        raise SystemExit("fewer partition-kernel dispatches than steps")
+    first = sorted(parts)[-calls]
+    out = {}
+    for n, v in per.items():
+        if any(k in n for k in DECODE_KERNELS):
+            vals = [x for d, x in v if d >= first]
+            if vals:
+                out[n] = statistics.median(vals)
+    return out
+
+
 def summarize(args):
     res = {"workload": args.workload, "kernel_hash": kernel_source_hash()}
     total = 0.0
@@ -110,12 +127,9 @@ def summarize(args):
         known = COPY_BYTES
         per = _per_kernel(_counter_rows(d), counter)
         ck = _copy_kernel(per)
-        copy_val = statistics.median(per[ck])
+        copy_val = statistics.median(x for _, x in per[ck])
         scale = known / copy_val
-        # the step calls are each kernel's last `calls` dispatches (earlier
-        # store dispatches build the pool)
-        dec = {n: statistics.median(v[-args.calls:]) for n, v in per.items()
-               if any(k in n for k in DECODE_KERNELS)}
+        dec = _step_kernels(per, args.calls)
         if not dec:
             raise SystemExit("decode kernels not found")
         dec_bytes = sum(v * scale for v in dec.values())
