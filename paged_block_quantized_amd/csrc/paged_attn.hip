@@ -40,6 +40,9 @@
 
 #include <math.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "device_common.h"
 #include "pbq_internal.h"
 #include "store_tile.h"
@@ -166,7 +169,7 @@ void attn_partition_mha(AttnArgs a) {
     };
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     int p, h, s;
     grid_coords(p, h, s);
     const int H = a.num_kv_heads;
@@ -440,8 +443,10 @@ void attn_partition_mha(AttnArgs a) {
 // for matrix cores: per 32-token step and per group of up to 16 query heads,
 // S^T[32 tok x 16 heads] = K_hat[32 x D] * Q^T[D x 16] takes 2 x D/32
 // v_mfma_f32_16x16x32_f16, and O^T[D x 16] += V_hat^T[D x 32] * P^T[32 x 16]
-// takes D/16 more.  Codes become fp16 exactly (v_perm under 0x64, offset
-// removed with v_pk_add_f16 for V); products are exact in fp32.
+// takes D/16 more.  Codes become fp16 exactly (v_perm under 0x64); the
+// constant offset of the K codes comes off each score, that of the V codes
+// (with the zero point) once per head at the end, as the weighted sum of the
+// offsets is the same for every dim.  Products are exact in fp32.
 //
 // MFMA 16x16x32 f16 lane layout (A: m = l%16, k = 8(l/16)+i; B: n = l%16,
 // k = 8(l/16)+i; C: n = l%16, m = 4(l/16)+i).  Token order inside a step is
@@ -459,6 +464,80 @@ void attn_partition_mha(AttnArgs a) {
 #define PBQ_GQA_WAVES_PER_EU 3
 #endif
 
+// Codes reach LDS by direct-to-LDS loads (global_load_lds_dwordx4: lane i's
+// 16 bytes land at the instruction's LDS base + 16 i), so every load
+// instruction reads 1 KiB of contiguous pool memory and the MFMA operands
+// are then gathered from LDS.  0 keeps the codes in registers, loaded in the
+// operand layout straight from the pool.  The kernel with the fused store
+// keeps the register path by default: with its LDS tile copy, staging would
+// leave room for three work groups per CU instead of four.
+#ifndef PBQ_GQA_STAGE
+#define PBQ_GQA_STAGE 1
+#endif
+#ifndef PBQ_GQA_STAGE_FUSED
+#define PBQ_GQA_STAGE_FUSED 0
+#endif
+#ifndef PBQ_GQA_STAGES
+#define PBQ_GQA_STAGES 2
+#endif
+
+// Waits for the direct-to-LDS loads are the kernel's own: the compiler cannot
+// tell the stages apart and would wait for every such load in flight.
+// Vector memory loads complete in issue order, so vmcnt(N) leaves only the N
+// most recent ones outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    __asm__ volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lds() {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+}
+__device__ __forceinline__ void load_to_lds(const void* src, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// LDS reads of staged codes, written as instructions the compiler does not
+// see: it would otherwise make each of them wait for every direct-to-LDS
+// load in flight, the prefetched steps included.  Their results are valid
+// after wait_lds(); lds_fence(x) then hands x back to the compiler, so no use
+// of x can be scheduled before the wait.
+template <int OFF>
+__device__ __forceinline__ void lds_read(u32x4& x, uint32_t a) {
+    __asm__ volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(x) : "v"(a), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void lds_read(u32x2& x, uint32_t a) {
+    __asm__ volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(x) : "v"(a), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void lds_read(uint32_t& x, uint32_t a) {
+    __asm__ volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(x) : "v"(a), "i"(OFF));
+}
+template <class T>
+__device__ __forceinline__ void lds_fence(T& x) {
+    __asm__ volatile("" : "+v"(x));
+}
+
+template <int I>
+using int_c = std::integral_constant<int, I>;
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(int_c<I>{}), ...);
+}
+// f(int_c<0>{}), ..., f(int_c<N - 1>{})
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// 16-byte chunk swizzle of a staged K row r (chunk c is kept at c ^ swz(r)):
+// the rows that one operand read gathers (even or odd rows, or runs of four,
+// depending on the token order) then fall in distinct bank groups.
+__device__ __forceinline__ constexpr int kswz(int r) { return ((r >> 1) ^ ((r & 1) << 1)) & 3; }
+
 template <bool V4>
 __device__ __forceinline__ int kappa(int j) {
     if constexpr (V4) return (j & 4) ? 2 * (j & 3) + 1 : 2 * (j & 3);
@@ -468,26 +547,21 @@ __device__ __forceinline__ int kappa(int j) {
 typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint32_t pk_sub_f16(uint32_t x, uint32_t off2) {
-    // exact: both operands are small integers in fp16
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, x) - __builtin_bit_cast(f16x2, off2));
-}
-
 template <int BS, int D, bool V4, int NW, bool FUSED>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA_WAVES_PER_EU))) void attn_partition_gqa(AttnArgs a) {
     static_assert(BS == 16 || BS == 32, "block size");
+    constexpr bool STAGED = FUSED ? PBQ_GQA_STAGE_FUSED : PBQ_GQA_STAGE;
     constexpr int KS = D / 32;                 // QK k-steps
     constexpr int DT = D / 16;                 // PV dim tiles
     constexpr int KCH = D / 4;                 // K bytes per lane per row
     constexpr int BPS = 32 / BS;               // blocks per 32-token step
     constexpr int SPB = 64 / BPS;              // steps whose block ids one wave stages at once
-    constexpr int VB = V4 ? 4 : 8;             // V bytes per lane per dim tile
     constexpr int VROW = V4 ? BS / 2 : BS;     // V bytes per dim row
     constexpr int KT = BS * D;
     constexpr int VT = D * VROW;
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int n16 = lane & 15;       // head (C/B layouts) or M row (A layout)
     const int grp = lane >> 4;       // lane group
     const int G = a.num_q_heads / a.num_kv_heads;
@@ -534,7 +608,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
     }
 
     const float c2 = a.sm_scale * kLog2e;
-    float m = -INFINITY, l = 0.f;
+    float m = -INFINITY, l = 0.f, zacc = 0.f;
     f32x4 acc[DT];
 #pragma unroll
     for (int t = 0; t < DT; ++t) acc[t] = (f32x4)0.f;
@@ -552,9 +626,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
     const int my_blk = (8 * grp) / BS;       // block of tokens 8grp..8grp+7
     const int vcol = ((8 * grp) % BS) / (V4 ? 2 : 1);
 
+    using VReg = std::conditional_t<V4, uint32_t, u32x2>;   // a lane's V codes of one dim tile
     struct Raw {
         u32x4 k[2][KCH / 16];
-        uint32_t v[DT][VB / 4];
+        VReg v[DT];
     };
 
     // Codes of one 32-token step: the lane's K rows and V row come from the
@@ -570,14 +645,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
         const uint8_t* vp = (BPS == 1 || !my_blk ? v0 : v1) + vcol;
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-            const uint8_t* row = vp + (16 * t + n16) * VROW;
-            if constexpr (V4) {
-                r.v[t][0] = *(const uint32_t*)row;
-            } else {
-                const u32x2 x = *(const u32x2*)row;
-                r.v[t][0] = x[0];
-                r.v[t][1] = x[1];
-            }
+            r.v[t] = *(const VReg*)(vp + (16 * t + n16) * VROW);
         }
     };
 
@@ -601,16 +669,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
         }
         // lane (head n16, group grp): sc[mt][i] is token 8 grp + kappa(4 mt + i)
         float x[8];
-        float bmax = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = tok0 + 32 * st + 8 * grp + kappa<V4>(4 * mt + e);
-                const float v = (sc[mt][e] - qbias) * sk;
-                x[4 * mt + e] = t < tok1 ? v : -INFINITY;
-                bmax = fmaxf(bmax, x[4 * mt + e]);
-            }
+            for (int e = 0; e < 4; ++e) x[4 * mt + e] = (sc[mt][e] - qbias) * sk;
+        if (tok0 + 32 * (st + 1) > tok1) {   // the partition's last step: mask its end
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (tok0 + 32 * st + 8 * grp + kappa<V4>(j) >= tok1) x[j] = -INFINITY;
+        }
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bmax = fmaxf(bmax, x[j]);
         // every step holds at least one valid token, so bmax is finite
         bmax = fmaxf(bmax, shfl_xor_f(bmax, 16));
         bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
@@ -619,9 +689,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
 #pragma unroll
             for (int t = 0; t < DT; ++t) acc[t] *= alpha;
             l *= alpha;
+            zacc *= alpha;
             m = bmax;
         }
         uint32_t pw[4];
+        float psum = 0.f;   // sum of the fp16 weights the MFMA takes
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float p0 = __builtin_amdgcn_exp2f(x[2 * e] - m);
@@ -629,28 +701,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
             l += p0 + p1;
             const f16x2 h2 = f16x2{(_Float16)(p0 * sv), (_Float16)(p1 * sv)};
             pw[e] = __builtin_bit_cast(uint32_t, h2);
+            psum = __builtin_amdgcn_fdot2(h2, f16x2{(_Float16)1, (_Float16)1}, psum, false);
         }
         const f16x8v pop = __builtin_bit_cast(f16x8v, pw);
+        // the codes enter the MFMA as bias + u (exact fp16); the weighted
+        // bias and zero point, (bias + zp) times the weights' sum, are the
+        // same for every dim and come off once, at the end
+        zacc = __builtin_fmaf((V4 ? kI4Bias : kI8Bias) + zpv, psum, zacc);
 
-        // ---- O^T += V_hat^T P^T --------------------------------------------
-        const _Float16 vo = (_Float16)((V4 ? kI4Bias : kI8Bias) + zpv);
-        const uint32_t off2 = __builtin_bit_cast(uint32_t, f16x2{vo, vo});
+        // ---- O^T += (bias + V codes)^T P^T ---------------------------------
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
             uint32_t a4[4];
             if constexpr (V4) {
-                const uint32_t wv = r.v[t][0];
+                const uint32_t wv = r.v[t];
                 const uint32_t lo = wv & 0x0F0F0F0Fu, hi = (wv >> 4) & 0x0F0F0F0Fu;
-                a4[0] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, lo, kSelLo), off2);
-                a4[1] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, lo, kSelHi), off2);
-                a4[2] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, hi, kSelLo), off2);
-                a4[3] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, hi, kSelHi), off2);
+                a4[0] = __builtin_amdgcn_perm(kF16Hi, lo, kSelLo);
+                a4[1] = __builtin_amdgcn_perm(kF16Hi, lo, kSelHi);
+                a4[2] = __builtin_amdgcn_perm(kF16Hi, hi, kSelLo);
+                a4[3] = __builtin_amdgcn_perm(kF16Hi, hi, kSelHi);
             } else {
                 const uint32_t u0 = r.v[t][0] ^ 0x80808080u, u1 = r.v[t][1] ^ 0x80808080u;
-                a4[0] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u0, kSelLo), off2);
-                a4[1] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u0, kSelHi), off2);
-                a4[2] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u1, kSelLo), off2);
-                a4[3] = pk_sub_f16(__builtin_amdgcn_perm(kF16Hi, u1, kSelHi), off2);
+                a4[0] = __builtin_amdgcn_perm(kF16Hi, u0, kSelLo);
+                a4[1] = __builtin_amdgcn_perm(kF16Hi, u0, kSelHi);
+                a4[2] = __builtin_amdgcn_perm(kF16Hi, u1, kSelLo);
+                a4[3] = __builtin_amdgcn_perm(kF16Hi, u1, kSelHi);
             }
             acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8v, a4), pop, acc[t], 0, 0, 0);
         }
@@ -682,6 +757,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
                 s_tscale[2] = ts.v_zp;
             }
         }
+        // the staged loads' waits count on loads alone: let the stores drain
+        if constexpr (STAGED) wait_vmem<0>();
     }
 
     // Each wave takes a contiguous run of the steps (the last one excluded in
@@ -694,6 +771,87 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
     const int q = (n_loop + 2 * hc) / NW, rem = (n_loop + 2 * hc) % NW;
     const int w_start = w * q + min(w, rem) - min(w, 2) * hc;
     const int w_stop = w_start + q + (w < rem ? 1 : 0) - (w < 2 ? hc : 0);
+
+    // Staging area of the direct-to-LDS path, per wave and stage: the step's
+    // 32 K rows as 1 KiB loads (RPR rows each, chunks swizzled by kswz,
+    // padded by 64 bytes), then its BPS V tiles as in the pool.
+    constexpr int SD = PBQ_GQA_STAGES;
+    constexpr int CPR = D / 16;                // 16-byte chunks per K row
+    constexpr int RPR = 1024 / D;              // K rows per load
+    constexpr int NKL = 32 * D / 1024;         // K loads per step
+    constexpr int KREG = 1024 + 64;
+    constexpr int NVL = BPS * VT / 1024;       // V loads per step
+    constexpr int NI = NKL + NVL;
+    constexpr int STG = NKL * KREG + BPS * VT;
+    static_assert(SD == 2 || SD == 3, "stages");
+    static_assert(BPS * VT % 1024 == 0 && (VT % 1024 == 0 || (BPS == 2 && VT == 512)), "V tile loads");
+    constexpr int STAGE_BYTES = STAGED ? NW * SD * STG : 16;
+    constexpr int ACC_BYTES = NW * 16 * (D + 4) * 4;
+    __shared__ __align__(16) uint8_t s_stage[STAGE_BYTES > ACC_BYTES ? STAGE_BYTES : ACC_BYTES];
+    uint8_t* const my_stage = s_stage + w * SD * STG;   // w is wave-uniform
+    // lane offsets: where this lane's 16 bytes of a K load come from (row
+    // lane / CPR of the load), and where its operands sit in a stage
+    // (unsigned: a uniform base plus a 32-bit lane offset is the
+    // instruction's scalar-base form)
+    const int dma_r = lane / CPR;
+    const uint32_t dma_k = (uint32_t)(dma_r * D + 16 * ((lane % CPR) ^ kswz(dma_r)));
+    const uint32_t dma_v = 16u * (uint32_t)lane;
+    int ko[2][KCH / 16];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        const int R = kblk[mt] * BS + krow[mt];   // row within the step
+#pragma unroll
+        for (int c = 0; c < KCH / 16; ++c)
+            ko[mt][c] = (R / RPR) * KREG + (R % RPR) * D + 16 * ((grp + 4 * c) ^ kswz(R % RPR));
+    }
+    const int vo = NKL * KREG + my_blk * VT + vcol + n16 * VROW;
+
+    // direct-to-LDS loads of one step (blocks id0, id1) into stage `buf`
+    auto stage_step = [&](int id0, int id1, int buf) {
+        uint8_t* sb = my_stage + buf * STG;
+        const int8_t* kb0 = a.k_codes + ((int64_t)id0 * H + kvh) * KT;
+        const int8_t* kb1 = a.k_codes + ((int64_t)id1 * H + kvh) * KT;
+#pragma unroll
+        for (int g = 0; g < NKL; ++g) {
+            const int row0 = g * RPR;             // a load lies in one block
+            load_to_lds((row0 / BS ? kb1 : kb0) + (row0 % BS) * D + dma_k, sb + g * KREG);
+        }
+        const uint8_t* vb0 = a.v_codes + ((int64_t)id0 * H + kvh) * VT;
+        const uint8_t* vb1 = a.v_codes + ((int64_t)id1 * H + kvh) * VT;
+#pragma unroll
+        for (int g = 0; g < NVL; ++g) {
+            const uint8_t* src;
+            if constexpr (VT >= 1024) src = ((1024 * g) / VT ? vb1 : vb0) + (1024 * g) % VT + dma_v;
+            else src = (lane < 32 ? vb0 : vb1) + (dma_v & 511u);
+            load_to_lds(src, sb + NKL * KREG + 1024 * g);
+        }
+    };
+    // the lane's operands of the step in stage B (K rows: the second chunk
+    // of a row is 64 bytes after the first, as kswz leaves bit 2 alone)
+    const uint32_t la_k0 = lds_addr(my_stage) + (uint32_t)ko[0][0];
+    const uint32_t la_k1 = lds_addr(my_stage) + (uint32_t)ko[1][0];
+    const uint32_t la_v = lds_addr(my_stage) + (uint32_t)vo;
+    auto read_stage = [&](auto bc, Raw& r) {
+        constexpr int B = decltype(bc)::value;
+        static_for<KCH / 16>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            lds_read<B * STG + 64 * c>(r.k[0][c], la_k0);
+            lds_read<B * STG + 64 * c>(r.k[1][c], la_k1);
+        });
+        static_for<DT>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            lds_read<B * STG + 16 * t * VROW>(r.v[t], la_v);
+        });
+        wait_lds();
+#pragma unroll
+        for (int c = 0; c < KCH / 16; ++c) {
+            lds_fence(r.k[0][c]);
+            lds_fence(r.k[1][c]);
+        }
+#pragma unroll
+        for (int t = 0; t < DT; ++t) lds_fence(r.v[t]);
+    };
+
     for (int base = w_start; base < w_stop; base += SPB) {
         const int st_l = base + lane / BPS;
         const int blk_l = blk0 + st_l * BPS + lane % BPS;
@@ -737,7 +895,38 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
             sv_l = a.v_scale[t];
             if constexpr (V4) zp_l = a.v_zp[t];
         };
-        pipelined<PBQ_GQA_DEPTH, Raw>(cnt, load, compute, scales);
+        if constexpr (STAGED) {
+            // SD stages: step i + SD is loaded into step i's stage once its
+            // operands are in registers, so SD steps are in flight while one
+            // is computed.  Each wait leaves outstanding only the loads issued
+            // after the step's own (the scale loads come first).
+            auto stage = [&](int i, int buf) {
+                stage_step(readlane(id_l, i * BPS), readlane(id_l, i * BPS + BPS - 1), buf);
+            };
+            scales();
+            stage(0, 0);
+#pragma unroll
+            for (int k = 1; k < SD; ++k)
+                if (k < cnt) stage(k, k);
+            auto one = [&](auto bc, int i) {
+                constexpr int B = decltype(bc)::value;
+                const int ahead = cnt - 1 - i;   // steps staged after step i
+                if (SD == 3 && ahead >= 2) wait_vmem<(SD - 1) * NI>();
+                else if (ahead >= 1) wait_vmem<NI>();
+                else wait_vmem<0>();
+                Raw r;
+                read_stage(bc, r);
+                if (i + SD < cnt) stage(i + SD, B);
+                compute(r, i);
+            };
+            for (int i = 0; i < cnt; i += SD) {
+                static_for<SD>([&](auto bc) {
+                    if (i + decltype(bc)::value < cnt) one(bc, i + decltype(bc)::value);
+                });
+            }
+        } else {
+            pipelined<PBQ_GQA_DEPTH, Raw>(cnt, load, compute, scales);
+        }
     }
     if (FUSED && fused) {
         __syncthreads();   // waves 0 and 1 have left the last block's tiles in LDS
@@ -764,15 +953,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
                          (float)(mine_last ? s_tscale[2] : z0));
         }
     }
-    // lanes of one head split its tokens by group: sum their partial sums
+    // lanes of one head split its tokens by group: sum their partial sums,
+    // and take the weighted code bias off every dim
     l += shfl_xor_f(l, 16);
     l += shfl_xor_f(l, 32);
+    zacc += shfl_xor_f(zacc, 16);
+    zacc += shfl_xor_f(zacc, 32);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) acc[t] -= zacc;
 
-    // Merge the waves' partial results in LDS.  Rows are padded by 4 floats
-    // so that the 16-byte writes of one instruction spread over the banks.
+    // Merge the waves' partial results in LDS (over the staging area, once
+    // every wave is done with it).  Rows are padded by 4 floats so that the
+    // 16-byte writes of one instruction spread over the banks.
     constexpr int DP = D + 4;
-    __shared__ float s_acc[NW][16][DP];
+    float (*s_acc)[16][DP] = reinterpret_cast<float (*)[16][DP]>(s_stage);
     __shared__ float s_ml[NW][16][2];
+    if constexpr (STAGED) __syncthreads();
     if (n16 < nheads) {
         // acc[t] holds dims 16t + 4 grp .. +3 of head n16
 #pragma unroll
@@ -893,6 +1089,9 @@ hipError_t launch_mha(const AttnArgs& a, hipStream_t stream) {
 #ifndef PBQ_GQA_FUSED_WAVES
 #define PBQ_GQA_FUSED_WAVES 3
 #endif
+#ifndef PBQ_GQA_SINGLE_WAVES
+#define PBQ_GQA_SINGLE_WAVES 2
+#endif
 template <int BS, int D, bool V4>
 hipError_t launch_gqa(const AttnArgs& a, hipStream_t stream) {
     const int G = a.num_q_heads / a.num_kv_heads;
@@ -903,7 +1102,8 @@ hipError_t launch_gqa(const AttnArgs& a, hipStream_t stream) {
             hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, PBQ_GQA_FUSED_WAVES, true>), grid,
                                dim3(64 * PBQ_GQA_FUSED_WAVES), 0, stream, a);
         else
-            hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, 2, false>), grid, dim3(64 * 2), 0, stream, a);
+            hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, PBQ_GQA_SINGLE_WAVES, false>), grid,
+                               dim3(64 * PBQ_GQA_SINGLE_WAVES), 0, stream, a);
     } else {
         hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, 4, false>), grid, dim3(64 * 4), 0, stream, a);
     }

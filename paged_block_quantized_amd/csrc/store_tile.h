@@ -19,12 +19,9 @@
 // starting at l * D/64 of every row, so each fp16 row read and the lane's
 // code rows are contiguous.
 //
-// Exact codes without a per-element division: n = rint(x * (1/s)) is within
-// one of the answer; the remainder x - n*s is exact in one FMA (x and s are
-// fp16 values, |n| <= 255), and comparing |rem| with s/2 (also exact) decides
-// the nearest integer and the tie, so the result equals round-half-even of
-// the exact quotient, which is what a correctly rounded fp32 division
-// followed by rint gives for fp16 operands.
+// Exact codes without a per-element division (Quantizer below): a fast
+// pass that is exact except on ties, which send the wave through an exact
+// routine whose result equals round-half-even of the exact quotient.
 #pragma once
 
 #include "device_common.h"
@@ -50,17 +47,40 @@ struct TileScales {
     uint32_t k_scale, v_scale, v_zp;
 };
 
-// Round-half-even of x / s + zp for s > 0, x and s fp16 values held in fp32.
-__device__ __forceinline__ int rne_quot(float x, float s, float rcp, float half_s, int zp) {
-    const float n = __builtin_rintf(x * rcp);
-    const float rem = __builtin_fmaf(-n, s, x);  // exact
-    const float arem = __builtin_fabsf(rem);
-    const int dir = rem > 0.f ? 1 : -1;
-    int q = (int)n + zp;
-    q += arem > half_s ? dir : 0;                     // n was one off
-    q += (arem == half_s && (q & 1)) ? dir : 0;       // exact tie -> even
-    return q;
-}
+// Codes of one tile with scale s (an fp16 value; s == 0 for an all-zero
+// tile).  exact(): round-half-even of x / s + zp for fp16 x, without a
+// division: n = rint(x * (1/s)) is within one of the answer, the remainder
+// x - n*s is exact in one FMA, and comparing |rem| with s/2 (also exact)
+// decides the nearest integer and the tie.  fast(): rint(x * (1/s) + off),
+// clamped, as a float.  For fp16 x and s the quotient x / s is either exactly
+// halfway between two integers or at least 2^-12 away from every halfway
+// point (x / s - k - 1/2 is a multiple of 2^min(a+1, b) over 2 S 2^b, for
+// x = X 2^a, s = S 2^b, S < 2^11), while the fused x * (1/s) + off is within
+// 2^-15 of x / s + off for results up to 256 (1/s and the FMA each round
+// once), so fast() agrees with exact() everywhere except on exact ties,
+// which it flags (remainder of exactly s/2) for the caller to redo with
+// exact().
+struct Quantizer {
+    float s, rcp, half_s;
+    __device__ __forceinline__ explicit Quantizer(float sc)
+        : s(sc), rcp(sc > 0.f ? 1.0f / sc : 0.f), half_s(sc > 0.f ? 0.5f * sc : -1.f) {}
+    __device__ __forceinline__ int exact(float x, int zp) const {
+        const float n = __builtin_rintf(x * rcp);
+        const float rem = __builtin_fmaf(-n, s, x);
+        const float arem = __builtin_fabsf(rem);
+        const int dir = rem > 0.f ? 1 : -1;
+        int q = (int)n + zp;
+        q += arem > half_s ? dir : 0;                     // n was one off
+        q += (arem == half_s && (q & 1)) ? dir : 0;       // exact tie -> even
+        return q;
+    }
+    __device__ __forceinline__ float fast(float x, float off, float lo, float hi, bool& tie) const {
+        const float u = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(__builtin_fmaf(x, rcp, off)), lo), hi);
+        const float rem = __builtin_fmaf(-(u - off), s, x);   // exact
+        tie |= __builtin_fabsf(rem) == half_s;
+        return u;
+    }
+};
 
 // Quantize block j (physical id phys) of head g of a sequence whose rows
 // before position sp sit in tail slot `slot` and whose rows sp .. end-1 are
@@ -143,17 +163,24 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
         amax = wave_max_u32_uniform(amax);
         const float absmax = bits_to_f16f((uint16_t)amax);
         const uint16_t s16 = f32_to_f16_bits(absmax / 127.0f);
-        const float sc = bits_to_f16f(s16);
-        const float rcp = sc > 0.f ? 1.0f / sc : 0.f;
-        const float half_s = 0.5f * sc;
+        const Quantizer qz(bits_to_f16f(s16));
         int8_t* dst = a.k_codes + tile * (BS * D);
+        // one access's 8 codes at a time (registers stay few); a tie anywhere
+        // in the wave sends those codes through the exact routine
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             uint32_t w[2] = {0u, 0u};
-            if (sc > 0.f) {
+            bool tie = false;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                w[e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(qz.fast((float)kx[it][e], 128.f, 1.f, 255.f, tie), e & 3, w[e >> 2]);
+            w[0] ^= 0x80808080u;   // offset-128 bytes -> two's complement codes
+            w[1] ^= 0x80808080u;
+            if (__builtin_amdgcn_ballot_w64(tie) != 0) {
+                w[0] = w[1] = 0u;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    int q = rne_quot((float)kx[it][e], sc, rcp, half_s, 0);
+                    int q = qz.exact((float)kx[it][e], 0);
                     q = q > 127 ? 127 : (q < -127 ? -127 : q);
                     w[e >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (e & 3));
                 }
@@ -179,74 +206,90 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
         amax = wave_max_u32_uniform(amax);
         const float absmax = bits_to_f16f((uint16_t)amax);
         const uint16_t s16 = f32_to_f16_bits(absmax / 127.0f);
-        const float sc = bits_to_f16f(s16);
-        const float rcp = sc > 0.f ? 1.0f / sc : 0.f;
-        const float half_s = 0.5f * sc;
+        const Quantizer qz(bits_to_f16f(s16));
         uint8_t* dst = a.v_codes + tile * (BS * D);
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) {
+        for (int k = 0; k < DPL; ++k) {   // one dim row of codes at a time
             uint32_t w[BS / 4];
 #pragma unroll
-            for (int i = 0; i < BS / 4; ++i) w[i] = 0u;
-            if (sc > 0.f) {
+            for (int i = 0; i < BS / 4; ++i) {   // four codes, then their tie check
+                uint32_t x = 0u;
+                bool tie = false;
 #pragma unroll
-                for (int r = 0; r < BS; ++r) {
-                    int q = rne_quot(vx(k, r), sc, rcp, half_s, 0);
-                    q = q > 127 ? 127 : (q < -127 ? -127 : q);
-                    w[r >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (r & 3));
+                for (int b = 0; b < 4; ++b)
+                    x = __builtin_amdgcn_cvt_pk_u8_f32(qz.fast(vx(k, 4 * i + b), 128.f, 1.f, 255.f, tie), b, x);
+                x ^= 0x80808080u;
+                if (__builtin_amdgcn_ballot_w64(tie) != 0) {
+                    x = 0u;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        int q = qz.exact(vx(k, 4 * i + b), 0);
+                        q = q > 127 ? 127 : (q < -127 ? -127 : q);
+                        x |= ((uint32_t)q & 0xFFu) << (8 * b);
+                    }
                 }
+                w[i] = x;
             }
             uint32_t* drow = (uint32_t*)(dst + (DPL * lane + k) * BS);
-            if (wr) {
+            uint32_t* lrow = LDS ? (uint32_t*)(lds_v + (DPL * lane + k) * BS) : nullptr;
 #pragma unroll
-                for (int i = 0; i < BS / 16; ++i)
-                    *(u32x4*)(drow + 4 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-            }
-            if constexpr (LDS) {
-                uint32_t* lrow = (uint32_t*)(lds_v + (DPL * lane + k) * BS);
-#pragma unroll
-                for (int i = 0; i < BS / 16; ++i)
-                    *(u32x4*)(lrow + 4 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+            for (int i = 0; i < BS / 16; ++i) {
+                const u32x4 x = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+                if (wr) *(u32x4*)(drow + 4 * i) = x;
+                if constexpr (LDS) *(u32x4*)(lrow + 4 * i) = x;
             }
         }
         if (wr && lane == 0) a.v_scale[tile] = s16;
         out.v_scale = s16;
     } else if constexpr (DO_V) {
-        float lo = 0.f, hi = 0.f;  // range widened to contain 0
+        // range widened to contain 0, over packed fp16 pairs (exact)
+        f16x2 lo2 = f16x2{(_Float16)0, (_Float16)0}, hi2 = lo2;
 #pragma unroll
-        for (int k = 0; k < DPL; ++k)
-#pragma unroll
-            for (int r = 0; r < BS; ++r) {
-                const float x = vx(k, r);
-                lo = fminf(lo, x);
-                hi = fmaxf(hi, x);
-            }
+        for (int r = 0; r < BS; ++r) {
+            const f16x2 x = __builtin_bit_cast(f16x2, vw[r]);
+            lo2 = __builtin_elementwise_min(lo2, x);
+            hi2 = __builtin_elementwise_max(hi2, x);
+        }
+        float lo = fminf((float)lo2[0], DPL == 2 ? (float)lo2[1] : 0.f);
+        float hi = fmaxf((float)hi2[0], DPL == 2 ? (float)hi2[1] : 0.f);
         lo = wave_min_uniform(lo);
         hi = wave_max_uniform(hi);
         const uint16_t s16 = f32_to_f16_bits((hi - lo) / 15.0f);
-        const float sc = bits_to_f16f(s16);
+        const Quantizer qz(bits_to_f16f(s16));
         int zp = 0;
-        if (sc > 0.f) {
-            const float z = __builtin_rintf(-lo / sc);
+        if (qz.s > 0.f) {
+            const float z = __builtin_rintf(-lo / qz.s);
             zp = z > 15.f ? 15 : (z < 0.f ? 0 : (int)z);
         }
-        const float rcp = sc > 0.f ? 1.0f / sc : 0.f;
-        const float half_s = 0.5f * sc;
+        const float zf = (float)zp;
+        // two nibbles per byte (even row low): byte = u_even + 16 u_odd; rows
+        // not yet held (zero inputs, code zp) are masked to zero nibbles
         uint8_t* dst = a.v_codes + tile * (BS * D / 2);
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) {
+        for (int k = 0; k < DPL; ++k) {   // one dim row of codes at a time
             uint32_t w[BS / 8];
 #pragma unroll
-            for (int i = 0; i < BS / 8; ++i) w[i] = 0u;
-            if (sc > 0.f) {
+            for (int i = 0; i < BS / 8; ++i) {   // eight codes, then their tie check
+                uint32_t x = 0u;
+                bool tie = false;
 #pragma unroll
-                for (int r = 0; r < BS; ++r) {
-                    if (r < valid) {
-                        int q = rne_quot(vx(k, r), sc, rcp, half_s, zp);
+                for (int b = 0; b < 4; ++b) {
+                    const int r = 8 * i + 2 * b;
+                    const float u0 = qz.fast(vx(k, r), zf, 0.f, 15.f, tie);
+                    const float u1 = qz.fast(vx(k, r + 1), zf, 0.f, 15.f, tie);
+                    x = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(u1, 16.f, u0), b, x);
+                }
+                if (__builtin_amdgcn_ballot_w64(tie) != 0) {
+                    x = 0u;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        int q = qz.exact(vx(k, 8 * i + e), zp);
                         q = q > 15 ? 15 : (q < 0 ? 0 : q);
-                        w[r >> 3] |= (uint32_t)q << (4 * (r & 7));
+                        x |= (uint32_t)q << (4 * e);
                     }
                 }
+                const int held = min(max(valid - 8 * i, 0), 8);   // uniform
+                w[i] = held == 8 ? x : x & ((1u << (4 * held)) - 1u);
             }
             uint32_t* drow = (uint32_t*)(dst + (DPL * lane + k) * (BS / 2));
             uint32_t* lrow = LDS ? (uint32_t*)(lds_v + (DPL * lane + k) * (BS / 2)) : nullptr;
@@ -256,8 +299,9 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
             } else {
 #pragma unroll
                 for (int i = 0; i < BS / 32; ++i) {
-                    if (wr) *(u32x4*)(drow + 4 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-                    if constexpr (LDS) *(u32x4*)(lrow + 4 * i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+                    const u32x4 x = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+                    if (wr) *(u32x4*)(drow + 4 * i) = x;
+                    if constexpr (LDS) *(u32x4*)(lrow + 4 * i) = x;
                 }
             }
         }
