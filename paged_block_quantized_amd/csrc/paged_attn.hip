@@ -185,9 +185,11 @@ void attn_partition_mha(AttnArgs a) {
     // Fused store of the current token (position ctx - 1): in the sequence's
     // last partition, waves 0 and 1 first re-quantize the last block's K and
     // V tiles from the tail-slot rows and the new row (store_tile, the code
-    // of the store kernel), leaving LDS copies of the codes and scales, and
-    // take correspondingly fewer of the other blocks; after a barrier, wave
-    // NW - 1 adds the last block's contribution from the LDS copy.
+    // of the store kernel) into LDS copies of the codes and scales, and take
+    // correspondingly fewer of the other blocks; after a barrier, wave NW - 1
+    // adds the last block's contribution from the LDS copy while waves 0 and
+    // 1 write the tiles to the pool (writes mixed into the bulk of the reads
+    // cost several times their size).
     __shared__ __align__(16) uint8_t s_tile[FUSED ? KT + VT : 16];
     __shared__ uint32_t s_tscale[3];
     const bool fused = FUSED && p == nparts - 1 && nblk > 0;   // uniform in the group
@@ -199,11 +201,11 @@ void attn_partition_mha(AttnArgs a) {
         const int slot = a.tail_slots[s], phys = tab[last];
         if (w == 0) {
             const TileScales ts = store_tile<BS, D, V4, true, true, false>(
-                t, h, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT);
+                t, h, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, false);
             if (lane == 0) s_tscale[0] = ts.k_scale;
         } else {
             const TileScales ts = store_tile<BS, D, V4, true, false, true>(
-                t, h, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT);
+                t, h, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, false);
             if (lane == 0) {
                 s_tscale[1] = ts.v_scale;
                 s_tscale[2] = ts.v_zp;
@@ -389,6 +391,13 @@ void attn_partition_mha(AttnArgs a) {
     }
     if (FUSED && fused) {
         __syncthreads();   // waves 0 and 1 have left the tiles in LDS
+        if (w < 2) {
+            const TileStoreArgs t{const_cast<int8_t*>(a.k_codes), const_cast<uint8_t*>(a.v_codes),
+                                  const_cast<uint16_t*>(a.k_scale), const_cast<uint16_t*>(a.v_scale),
+                                  const_cast<uint8_t*>(a.v_zp), a.tail_k, a.tail_v, a.k_new, a.v_new, H};
+            write_stored_tile<BS, D, V4>(t, w, h, a.tail_slots[s], s, ctx - 1, tab[nblk - 1], s_tile, s_tile + KT,
+                                         s_tscale);
+        }
         if (w == NW - 1) {
             Regs r;
             load_tile((const int8_t*)s_tile, s_tile + KT, r);
@@ -733,9 +742,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
 
     // Fused store of the current token (position ctx - 1), single-partition
     // launches: waves 0 and 1 re-quantize the last block's K and V tiles
-    // (store_tile; only the first 16-head tile of a KV head writes the pool),
-    // leave LDS copies, and take fewer of the other steps; after a barrier,
-    // wave NW - 1 computes the last step with the last block read from LDS.
+    // (store_tile) into LDS copies and take fewer of the other steps; after a
+    // barrier, wave NW - 1 computes the last step with the last block read
+    // from LDS while waves 0 and 1 write the tiles to the pool (only the first
+    // 16-head tile of a KV head writes).
     __shared__ __align__(16) uint8_t s_tile[FUSED ? KT + VT : 16];
     __shared__ uint32_t s_tscale[3];
     const bool fused = FUSED && nblk > 0;   // one partition: this group holds the last block
@@ -747,11 +757,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
         const int slot = a.tail_slots[s], phys = tab[last];
         if (w == 0) {
             const TileScales ts = store_tile<BS, D, V4, true, true, false>(
-                t, kvh, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, ht == 0);
+                t, kvh, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, false);
             if (lane == 0) s_tscale[0] = ts.k_scale;
         } else {
             const TileScales ts = store_tile<BS, D, V4, true, false, true>(
-                t, kvh, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, ht == 0);
+                t, kvh, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, false);
             if (lane == 0) {
                 s_tscale[1] = ts.v_scale;
                 s_tscale[2] = ts.v_zp;
@@ -930,6 +940,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
     }
     if (FUSED && fused) {
         __syncthreads();   // waves 0 and 1 have left the last block's tiles in LDS
+        if (w < 2 && ht == 0) {   // the first 16-head tile of a KV head writes the pool
+            const TileStoreArgs t{const_cast<int8_t*>(a.k_codes), const_cast<uint8_t*>(a.v_codes),
+                                  const_cast<uint16_t*>(a.k_scale), const_cast<uint16_t*>(a.v_scale),
+                                  const_cast<uint8_t*>(a.v_zp), a.tail_k, a.tail_v, a.k_new, a.v_new, H};
+            write_stored_tile<BS, D, V4>(t, w, kvh, a.tail_slots[s], s, ctx - 1, tab[nblk - 1], s_tile, s_tile + KT,
+                                         s_tscale);
+        }
         if (w == NW - 1) {
             // the last step: its last block from LDS; in a 16-token pair whose
             // second block is the last one, the first block from the pool

@@ -334,4 +334,42 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
     return out;
 }
 
+// Pool writes of a tile that store_tile quantized with wr false (codes left
+// in LDS at lds_k / lds_v, scale bits and zero point in `sc`): wave 0 writes
+// the K codes and scale, wave 1 the V codes, scale and zero point, each also
+// the new row at position pos to the tail slot when its block stays
+// partial.  The fused decode calls it after its loop, so that these writes
+// do not meet the bulk of the pool reads.  new_row is the row of a.k / a.v
+// that holds position pos.
+template <int BS, int D, bool V4>
+__device__ __forceinline__ void write_stored_tile(const TileStoreArgs& a, int w, int g, int slot, int new_row, int pos,
+                                                  int phys, const uint8_t* lds_k, const uint8_t* lds_v,
+                                                  const uint32_t* sc) {
+    constexpr int KT = BS * D;
+    constexpr int VT = V4 ? BS * D / 2 : BS * D;
+    const int lane = threadIdx.x & 63;
+    const int H = a.num_kv_heads;
+    const int64_t tile = (int64_t)phys * H + g;
+    const bool tail = (pos + 1) % BS != 0;   // the block stays partial
+    const int64_t trow = (((int64_t)slot * H + g) * BS + pos % BS) * D;
+    const int64_t nrow = ((int64_t)new_row * H + g) * D;
+    if (w == 0) {
+#pragma unroll
+        for (int c = 0; c < KT / 1024; ++c)
+            *(u32x4*)(a.k_codes + tile * KT + 1024 * c + 16 * lane) = *(const u32x4*)(lds_k + 1024 * c + 16 * lane);
+        if (lane == 0) a.k_scale[tile] = (uint16_t)sc[0];
+        if (tail && lane < D / 8) *(u32x4*)(a.tail_k + trow + 8 * lane) = *(const u32x4*)(a.k + nrow + 8 * lane);
+    } else if (w == 1) {
+#pragma unroll
+        for (int c = 0; c < (VT + 1023) / 1024; ++c)
+            if (VT % 1024 == 0 || 1024 * c + 16 * lane < VT)
+                *(u32x4*)(a.v_codes + tile * VT + 1024 * c + 16 * lane) = *(const u32x4*)(lds_v + 1024 * c + 16 * lane);
+        if (lane == 0) {
+            a.v_scale[tile] = (uint16_t)sc[1];
+            if constexpr (V4) a.v_zp[tile] = (uint8_t)sc[2];
+        }
+        if (tail && lane < D / 8) *(u32x4*)(a.tail_v + trow + 8 * lane) = *(const u32x4*)(a.v + nrow + 8 * lane);
+    }
+}
+
 }  // namespace pbq
