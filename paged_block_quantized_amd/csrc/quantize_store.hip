@@ -16,12 +16,13 @@
 //  are zero bytes; a partially filled block is re-quantized from the exact
 //  fp16 rows kept in its sequence's tail slot.
 //
-// Mapping: one wavefront per (sequence, touched block, KV head); a workgroup
-// of four waves takes four consecutive heads of one block, so each token row
-// is read as 4 x D x 2 contiguous bytes.  The per-sequence scalars are loaded
-// together, then store_tile (store_tile.h: lane layout, exact rounding)
-// loads every fp16 row of the tile at once, reduces with DPP and readlane,
-// and writes the codes.
+// Mapping: one wavefront per (sequence, touched block, KV head, tensor); a
+// workgroup of four waves takes K and V of two consecutive heads of one
+// block, so each token row is read as 2 x D x 2 contiguous bytes and no wave
+// carries both tensors' rows.  The per-sequence scalars are loaded together,
+// then store_tile (store_tile.h: lane layout, exact rounding) loads every
+// fp16 row of the wave's tensor at once, reduces with DPP and readlane, and
+// writes the codes.
 
 #include "device_common.h"
 #include "pbq_internal.h"
@@ -32,7 +33,8 @@ namespace {
 
 template <int BS, int D, bool V4>
 __global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
-    const int g = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = blockIdx.x * 2 + (wv >> 1);
     const int jj = blockIdx.y;
     const int s = blockIdx.z;   // < num_seqs by the grid
 
@@ -59,14 +61,15 @@ __global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
     if (g >= H || n_new <= 0 || j * BS >= end) return;
     const int phys = a.block_tables[(int64_t)s * a.max_blocks_per_seq + j];
     const TileStoreArgs t{a.k_codes, a.v_codes, a.k_scale, a.v_scale, a.v_zp, a.tail_k, a.tail_v, a.k, a.v, H};
-    store_tile<BS, D, V4, false>(t, g, slot, c0, sp, end, j, phys, nullptr, nullptr);
+    if (wv & 1) store_tile<BS, D, V4, false, false, true>(t, g, slot, c0, sp, end, j, phys, nullptr, nullptr);
+    else store_tile<BS, D, V4, false, true, false>(t, g, slot, c0, sp, end, j, phys, nullptr, nullptr);
 }
 
-// Grid: x = groups of four KV heads, y = blocks a sequence's new tokens can
-// touch, z = sequences.
+// Grid: x = pairs of KV heads, y = blocks a sequence's new tokens can touch,
+// z = sequences.
 template <int BS, int D, bool V4>
 hipError_t launch_qs(const QuantStoreArgs& a, hipStream_t stream) {
-    dim3 grid((unsigned)((a.num_kv_heads + 3) / 4), (unsigned)a.tiles_per_seq, (unsigned)a.num_seqs);
+    dim3 grid((unsigned)((a.num_kv_heads + 1) / 2), (unsigned)a.tiles_per_seq, (unsigned)a.num_seqs);
     hipLaunchKernelGGL((quantize_store_kernel<BS, D, V4>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }

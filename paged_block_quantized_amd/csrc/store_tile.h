@@ -88,10 +88,10 @@ struct Quantizer {
 // Writes codes, scales, zero point, and -- when the sequence's last block
 // stays partial -- its new rows to the tail slot.  With LDS set, the codes are
 // also written to lds_k / lds_v in the tile layout.  Called by a whole wave.
-// DO_K / DO_V select the tensors: the store kernel does both in one wave
-// (all rows in flight at once); the fused decode gives them to two waves,
-// which halves the registers either needs.  With wr false nothing is written
-// to the pool (only the LDS copy), for callers that share a tile.
+// DO_K / DO_V select the tensors: the store kernel and the fused decode give
+// them to two waves, which halves the registers and the arithmetic on
+// either's path.  With wr false nothing is written to the pool (only the LDS
+// copy; write_stored_tile writes it later).
 template <int BS, int D, bool V4, bool LDS, bool DO_K = true, bool DO_V = true>
 __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, int slot, int c0, int sp,
                                                  int end, int j, int phys, int8_t* lds_k, uint8_t* lds_v,
