@@ -287,6 +287,37 @@ kv_status paged_attn_decode_append(const kv_pool_desc* desc, const kv_pool_mem* 
                                    int32_t partition_size, void* workspace_dev,
                                    size_t workspace_bytes, void* stream);
 
+/* paged_attn_decode (k_new_dev, v_new_dev, tail_slots_dev all NULL) or
+ * paged_attn_decode_append (all set) for a call whose sequences share a
+ * prefix: the first shared_tokens tokens of every sequence sit in the same
+ * physical blocks (block_tables[s][j] equal for every s and
+ * j < shared_tokens / block_size, as kv_seq_fork leaves them; a caller
+ * contract, not checked).  The same outputs, with the prefix's tiles read
+ * once per KV head and 16 queries instead of once per sequence: the prefix
+ * partitions run as one matrix-core launch whose queries are all the
+ * call's sequences x query heads of a KV head (sequence 0's block table),
+ * then the remaining partitions per sequence, then the log-sum-exp reduce.
+ * [yunthe] "prefix caching" (blocks shared between requests); the shared
+ * pass itself is a scheduling of the same sums.  partition_size must be
+ * given (not 0) and a multiple of 32; shared_tokens a positive multiple of
+ * it, below max_context_len; every context must exceed shared_tokens.
+ * Workspace as paged_attn_workspace_bytes for these sizes.  Errors as
+ * paged_attn_decode, plus KV_ERR_INVALID for a bad shared_tokens, a mix of
+ * NULL and non-NULL append pointers, or more than 65535 x 16 queries per KV
+ * head. */
+kv_status paged_attn_decode_shared_prefix(const kv_pool_desc* desc, const kv_pool_mem* mem,
+                                          const uint16_t* k_new_dev, const uint16_t* v_new_dev,
+                                          const int32_t* tail_slots_dev,
+                                          const uint16_t* q_dev, uint16_t* out_dev,
+                                          int32_t num_seqs, int32_t num_q_heads,
+                                          const int32_t* block_tables_dev,
+                                          int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens_dev,
+                                          int32_t max_context_len, float sm_scale,
+                                          int32_t partition_size, int32_t shared_tokens,
+                                          void* workspace_dev, size_t workspace_bytes,
+                                          void* stream);
+
 /* Partition size (tokens) paged_attn_decode uses when given 0: a single
  * pass when num_seqs x (heads, or KV heads x 16-head tiles) gives at least
  * four work groups per compute unit of the current device and every context

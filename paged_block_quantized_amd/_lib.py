@@ -60,7 +60,8 @@ EXPORTS = [
     "kv_seq_fork", "kv_seq_append", "kv_seq_free", "kv_seq_table",
     "kv_batch_tables", "kv_pool_stats", "kv_pool_free_list", "kv_copy_blocks",
     "kv_quantize_store", "paged_attn_workspace_bytes", "paged_attn_decode",
-    "paged_attn_decode_append", "paged_attn_default_partition", "kv_last_error",
+    "paged_attn_decode_append", "paged_attn_decode_shared_prefix",
+    "paged_attn_default_partition", "kv_last_error",
 ]
 
 _lib = None
@@ -98,6 +99,9 @@ def lib():
             "paged_attn_decode_append": (st, [P(kv_pool_desc), P(kv_pool_mem), VP, VP, VP, VP, VP,
                                               I32, I32, VP, I32, VP, I32, ctypes.c_float, I32, VP,
                                               SZ, VP]),
+            "paged_attn_decode_shared_prefix": (st, [P(kv_pool_desc), P(kv_pool_mem), VP, VP, VP, VP,
+                                                     VP, I32, I32, VP, I32, VP, I32, ctypes.c_float,
+                                                     I32, I32, VP, SZ, VP]),
             "paged_attn_default_partition": (I32, [P(kv_pool_desc), I32, I32, I32]),
             "kv_last_error": (ctypes.c_char_p, []),
         }
@@ -264,3 +268,14 @@ def paged_attn_decode_append(desc, mem, k_new, v_new, tail_slots, q, out, num_se
                                           int(max_context_len), float(sm_scale),
                                           int(partition_size), _ptr(workspace),
                                           int(workspace_bytes), _stream(stream)))
+
+
+def paged_attn_decode_shared_prefix(desc, mem, k_new, v_new, tail_slots, q, out, num_seqs,
+                                    num_q_heads, block_tables, max_blocks_per_seq, context_lens,
+                                    max_context_len, sm_scale, partition_size, shared_tokens,
+                                    workspace=None, workspace_bytes=0, stream=None):
+    _check(lib().paged_attn_decode_shared_prefix(
+        ctypes.byref(desc), ctypes.byref(mem), _ptr(k_new), _ptr(v_new), _ptr(tail_slots), _ptr(q),
+        _ptr(out), int(num_seqs), int(num_q_heads), _ptr(block_tables), int(max_blocks_per_seq),
+        _ptr(context_lens), int(max_context_len), float(sm_scale), int(partition_size),
+        int(shared_tokens), _ptr(workspace), int(workspace_bytes), _stream(stream)))

@@ -100,7 +100,7 @@ kv_status decode_impl(const kv_pool_desc* d, const kv_pool_mem* m, const AppendA
                             int32_t num_q_heads, const int32_t* block_tables,
                             int32_t max_blocks_per_seq, const int32_t* context_lens,
                             int32_t max_context_len, float sm_scale,
-                            int32_t partition_size, void* workspace,
+                            int32_t partition_size, int32_t shared_tokens, void* workspace,
                             size_t workspace_bytes, void* stream) {
     kv_status st = pbq::check_device_desc(d);
     if (st != KV_OK) return st;
@@ -133,6 +133,18 @@ kv_status decode_impl(const kv_pool_desc* d, const kv_pool_mem* m, const AppendA
         return fail(KV_ERR_INVALID, "grouped-query partition_size must be a multiple of 32 tokens");
     const int32_t max_parts = max_context_len > 0 ? pbq::ceil_div(max_context_len, part) : 1;
     if (max_parts > 65535) return fail(KV_ERR_INVALID, "too many partitions; use a larger partition_size");
+    if (shared_tokens < 0) return fail(KV_ERR_INVALID, "shared_tokens must be >= 0");
+    if (shared_tokens > 0) {
+        if (partition_size == 0 || part % 32 != 0)
+            return fail(KV_ERR_INVALID, "a shared prefix needs an explicit partition_size, a multiple of 32");
+        if (shared_tokens % part != 0)
+            return fail(KV_ERR_INVALID, "shared_tokens must be a multiple of partition_size");
+        if (shared_tokens >= max_context_len)
+            return fail(KV_ERR_INVALID, "shared_tokens must be below max_context_len");
+        const int64_t nq = (int64_t)num_seqs * (num_q_heads / d->num_kv_heads);
+        if ((int64_t)d->num_kv_heads * ((nq + 15) / 16) > 65535)
+            return fail(KV_ERR_INVALID, "too many queries per KV head for the shared-prefix launch");
+    }
     const size_t need = paged_attn_workspace_bytes(d, num_seqs, num_q_heads, max_context_len, part);
     if (workspace_bytes < need) return fail(KV_ERR_INVALID, "workspace too small");
     if (need > 0 && (!workspace || !pbq::aligned16(workspace)))
@@ -157,6 +169,8 @@ kv_status decode_impl(const kv_pool_desc* d, const kv_pool_mem* m, const AppendA
     a.sm_scale = sm_scale;
     a.partition_blocks = part / d->block_size;
     a.max_partitions = max_parts;
+    a.shared_tokens = shared_tokens;
+    a.shared_parts = shared_tokens / part;
     const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
     a.ws_out = need ? (float*)workspace : nullptr;
     a.ws_ml = need ? (float*)((char*)workspace + rows * (size_t)d->head_dim * 4) : nullptr;
@@ -332,7 +346,7 @@ kv_status paged_attn_decode(const kv_pool_desc* d, const kv_pool_mem* m,
                             int32_t partition_size, void* workspace,
                             size_t workspace_bytes, void* stream) {
     return decode_impl(d, m, nullptr, q, out, num_seqs, num_q_heads, block_tables, max_blocks_per_seq,
-                       context_lens, max_context_len, sm_scale, partition_size, workspace, workspace_bytes,
+                       context_lens, max_context_len, sm_scale, partition_size, 0, workspace, workspace_bytes,
                        stream);
 }
 
@@ -346,8 +360,24 @@ kv_status paged_attn_decode_append(const kv_pool_desc* d, const kv_pool_mem* m,
                                    size_t workspace_bytes, void* stream) {
     const AppendArgs app{k_new, v_new, tail_slots};
     return decode_impl(d, m, &app, q, out, num_seqs, num_q_heads, block_tables, max_blocks_per_seq,
-                       context_lens, max_context_len, sm_scale, partition_size, workspace, workspace_bytes,
+                       context_lens, max_context_len, sm_scale, partition_size, 0, workspace, workspace_bytes,
                        stream);
+}
+
+kv_status paged_attn_decode_shared_prefix(const kv_pool_desc* d, const kv_pool_mem* m,
+                                          const uint16_t* k_new, const uint16_t* v_new,
+                                          const int32_t* tail_slots, const uint16_t* q, uint16_t* out,
+                                          int32_t num_seqs, int32_t num_q_heads,
+                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t max_context_len,
+                                          float sm_scale, int32_t partition_size, int32_t shared_tokens,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+    if (!k_new && (v_new || tail_slots))
+        return fail(KV_ERR_INVALID, "k_new, v_new and tail_slots are all NULL (plain decode) or all set");
+    const AppendArgs app{k_new, v_new, tail_slots};
+    return decode_impl(d, m, k_new ? &app : nullptr, q, out, num_seqs, num_q_heads, block_tables,
+                       max_blocks_per_seq, context_lens, max_context_len, sm_scale, partition_size,
+                       shared_tokens, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

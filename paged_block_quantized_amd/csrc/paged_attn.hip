@@ -172,6 +172,7 @@ void attn_partition_mha(AttnArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     int p, h, s;
     grid_coords(p, h, s);
+    p += a.shared_parts;   // partitions of a shared prefix ran in their own launch
     const int H = a.num_kv_heads;
     const int ctx = a.context_lens[s];
     const int nblk = (ctx + BS - 1) / BS;
@@ -556,8 +557,15 @@ __device__ __forceinline__ int kappa(int j) {
 typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int BS, int D, bool V4, int NW, bool FUSED>
+// SHARED: the partitions of a prefix that every sequence of the call holds in
+// the same physical blocks (sequence 0's table); the queries sharing a KV
+// head are then all sequences' query heads of that group, 16 to a work
+// group (query i: sequence i / G, head kvh * G + i % G), so each of the
+// prefix's tiles is read once per 16 queries instead of once per sequence.
+// Results always go to the workspace, for the reduce.
+template <int BS, int D, bool V4, int NW, bool FUSED, bool SHARED = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA_WAVES_PER_EU))) void attn_partition_gqa(AttnArgs a) {
+    static_assert(!(FUSED && SHARED), "the shared prefix holds no current token");
     static_assert(BS == 16 || BS == 32, "block size");
     constexpr bool STAGED = FUSED ? PBQ_GQA_STAGE_FUSED : PBQ_GQA_STAGE;
     constexpr int KS = D / 32;                 // QK k-steps
@@ -574,13 +582,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
     const int n16 = lane & 15;       // head (C/B layouts) or M row (A layout)
     const int grp = lane >> 4;       // lane group
     const int G = a.num_q_heads / a.num_kv_heads;
-    const int n_ht = (G + 15) / 16;
+    const int NQ = SHARED ? a.num_seqs * G : G;   // queries that share a KV head's tiles
+    const int n_ht = (NQ + 15) / 16;
     int p, tile, s;
     grid_coords(p, tile, s);
+    if constexpr (!SHARED) p += a.shared_parts;   // shared partitions ran in their own launch
     const int kvh = tile / n_ht;
     const int ht = tile % n_ht;
     const int H = a.num_kv_heads;
-    const int ctx = a.context_lens[s];
+    const int ctx = SHARED ? a.shared_tokens : a.context_lens[s];
     const int nblk = (ctx + BS - 1) / BS;
     const int PB = a.partition_blocks;
     const int nparts = max(1, (nblk + PB - 1) / PB);
@@ -588,8 +598,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
     const int tok0 = p * PB * BS;
     const int tok1 = min(tok0 + PB * BS, ctx);
     const int nsteps = (tok1 - tok0 + 31) / 32;
-    const int head_base = kvh * G + ht * 16;
-    const int nheads = min(16, G - ht * 16);
+    const int nheads = min(16, NQ - ht * 16);
+    // sequence and query head of query ht * 16 + i
+    auto query = [&](int i, int& qs, int& qh) {
+        const int qi = ht * 16 + i;
+        qs = SHARED ? qi / G : s;
+        qh = SHARED ? kvh * G + qi % G : kvh * G + qi;
+    };
     const int blk0 = tok0 / BS;
     const int blk_end = (tok1 + BS - 1) / BS;
 
@@ -602,7 +617,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
     {
         float qs = 0.f;
         const bool live = n16 < nheads;
-        const uint16_t* qp = a.q + ((int64_t)s * a.num_q_heads + head_base + n16) * D + 16 * grp;
+        int qs_, qh_;
+        query(n16, qs_, qh_);
+        const uint16_t* qp = a.q + ((int64_t)qs_ * a.num_q_heads + qh_) * D + 16 * grp;
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
             f16x8v x = (f16x8v)(_Float16)0;
@@ -1009,8 +1026,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
             o = __builtin_fmaf(s_acc[k][hh][d], f, o);
         }
         const float res = L > 0.f ? o / L : 0.f;
-        const int64_t row = (int64_t)s * a.num_q_heads + head_base + hh;
-        if (nparts == 1) {
+        int qs_, qh_;
+        query(hh, qs_, qh_);
+        const int64_t row = (int64_t)qs_ * a.num_q_heads + qh_;
+        if (nparts == 1 && !SHARED) {
             a.out[row * D + d] = f32_to_f16_bits(res);
         } else {
             const int64_t prow = row * a.max_partitions + p;
@@ -1084,7 +1103,7 @@ __global__ __launch_bounds__(64) void attn_reduce(AttnArgs a) {
 // 64 blocks, else 4, so that each wave still streams several blocks.
 template <int BS, int D, bool V4>
 hipError_t launch_mha(const AttnArgs& a, hipStream_t stream) {
-    const dim3 grid = grid_dims(a.max_partitions, a.num_q_heads, a.num_seqs);
+    const dim3 grid = grid_dims(a.max_partitions - a.shared_parts, a.num_q_heads, a.num_seqs);
     const bool fused = a.k_new != nullptr;
     if (a.partition_blocks >= 64) {
         if (fused) hipLaunchKernelGGL((attn_partition_mha<BS, D, V4, 8, true>), grid, dim3(64 * 8), 0, stream, a);
@@ -1113,7 +1132,7 @@ template <int BS, int D, bool V4>
 hipError_t launch_gqa(const AttnArgs& a, hipStream_t stream) {
     const int G = a.num_q_heads / a.num_kv_heads;
     const int n_ht = (G + 15) / 16;
-    const dim3 grid = grid_dims(a.max_partitions, a.num_kv_heads * n_ht, a.num_seqs);
+    const dim3 grid = grid_dims(a.max_partitions - a.shared_parts, a.num_kv_heads * n_ht, a.num_seqs);
     if (a.max_partitions == 1) {
         if (a.k_new != nullptr)
             hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, PBQ_GQA_FUSED_WAVES, true>), grid,
@@ -1133,11 +1152,26 @@ hipError_t launch_gqa(const AttnArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// The partitions of a prefix shared by every sequence: one grouped launch
+// over (shared partition, KV head x 16-query tile), before the per-sequence
+// partitions.
+template <int BS, int D, bool V4>
+hipError_t launch_shared(const AttnArgs& a, hipStream_t stream) {
+    const int NQ = a.num_seqs * (a.num_q_heads / a.num_kv_heads);
+    const dim3 grid = grid_dims(a.shared_parts, a.num_kv_heads * ((NQ + 15) / 16), 1);
+    hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, 2, false, true>), grid, dim3(64 * 2), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_paged_attn(const AttnArgs& a, hipStream_t stream) {
     const bool v4 = a.v_codec == KV_CODEC_I4_ASYM;
     const bool gqa = a.num_q_heads != a.num_kv_heads;
 #define PBQ_ATTN(BS, D)                                                                        \
     if (a.block_size == BS && a.head_dim == D) {                                               \
+        if (a.shared_parts > 0) {                                                              \
+            const hipError_t e = v4 ? launch_shared<BS, D, true>(a, stream) : launch_shared<BS, D, false>(a, stream); \
+            if (e != hipSuccess) return e;                                                     \
+        }                                                                                      \
         if (gqa) return v4 ? launch_gqa<BS, D, true>(a, stream) : launch_gqa<BS, D, false>(a, stream); \
         return v4 ? launch_mha<BS, D, true>(a, stream) : launch_mha<BS, D, false>(a, stream);  \
     }

@@ -62,6 +62,11 @@ struct AttnArgs {
     const int32_t* tail_slots;
     uint16_t* tail_k;
     uint16_t* tail_v;
+    // prefix shared by all sequences (0 for none): its first shared_parts
+    // partitions (shared_tokens tokens, sequence 0's block table) run as one
+    // grouped launch over every query; the per-sequence grid starts after them
+    int32_t shared_tokens;
+    int32_t shared_parts;
 };
 
 struct CopyArgs {

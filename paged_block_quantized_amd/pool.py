@@ -152,3 +152,20 @@ class KVPool:
                                    context_lens, max_context_len, sm_scale, partition_size,
                                    workspace, nbytes, stream)
         return workspace
+
+    def decode_shared_prefix(self, q, out, block_tables, context_lens, max_context_len, sm_scale,
+                             partition_size, shared_tokens, k_new=None, v_new=None,
+                             tail_slots=None, workspace=None, stream=None, mem=None):
+        """decode (k_new None) or decode_append for sequences whose first
+        shared_tokens tokens sit in the same physical blocks."""
+        S, Hq, _ = q.shape
+        need = self.workspace_bytes(S, Hq, max_context_len, partition_size)
+        if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        L.paged_attn_decode_shared_prefix(self.desc, self.mem if mem is None else mem, k_new, v_new,
+                                          tail_slots, q, out, S, Hq, block_tables,
+                                          block_tables.shape[1], context_lens, max_context_len,
+                                          sm_scale, partition_size, shared_tokens, workspace,
+                                          nbytes, stream)
+        return workspace

@@ -7,7 +7,8 @@ A decode step for one layer stores the current token of every sequence
 (re-quantizing its block from the tail slot) and runs the fused dequantizing
 attention over the whole context, current token included: one call of
 paged_attn_decode_append, or (step_separate) kv_quantize_store followed by
-paged_attn_decode.
+paged_attn_decode.  Sequences forked from one prefix use
+paged_attn_decode_shared_prefix, which reads the shared blocks once.
 """
 
 from dataclasses import dataclass
@@ -47,6 +48,7 @@ class DecodeSetup:
     sm_scale: float
     partition: int
     replicas: list = None       # [(kv_pool_mem, arrays)] copies of the pool
+    shared: int = 0             # tokens of the prefix all sequences share (read once), 0: none
 
     def add_replicas(self, n):
         """n more copies of the pool arrays at other addresses (each the same
@@ -71,7 +73,18 @@ class DecodeSetup:
         self.attend(stream, r)
 
     def step(self, stream=None, r=0):
-        """The step as one call: paged_attn_decode_append (store fused in)."""
+        """The step as one call: paged_attn_decode_append (store fused in), or
+        paged_attn_decode_shared_prefix when the sequences share a prefix."""
+        if self.shared:
+            self.pool.decode_shared_prefix(self.q, self.out, self.tables, self.ctx_dev, self.max_ctx,
+                                           self.sm_scale, self.partition, self.shared, self.k_new,
+                                           self.v_new, self.slots, self.workspace, stream,
+                                           mem=self._mem(r))
+        else:
+            self.step_unshared(stream, r)
+
+    def step_unshared(self, stream=None, r=0):
+        """paged_attn_decode_append, which reads a shared prefix per sequence."""
         self.pool.decode_append(self.k_new, self.v_new, self.slots, self.q, self.out, self.tables,
                                 self.ctx_dev, self.max_ctx, self.sm_scale, self.partition,
                                 self.workspace, stream, mem=self._mem(r))
@@ -151,7 +164,16 @@ def setup_decode(w: W.Workload, device="cuda", chunk_seqs=8, partition=None) -> 
         cu_step=torch.arange(S + 1, dtype=torch.int32, device=device),
         k_new=torch.cat(k_new).contiguous(), v_new=torch.cat(v_new).contiguous(),
         q=q, out=out, workspace=workspace, max_ctx=max_ctx,
-        sm_scale=1.0 / float(np.sqrt(w.head_dim)), partition=part)
+        sm_scale=1.0 / float(np.sqrt(w.head_dim)), partition=part,
+        shared=shared_prefix_tokens(w, part))
+
+
+def shared_prefix_tokens(w: W.Workload, partition: int) -> int:
+    """Tokens of the workload's shared prefix that the shared-prefix decode
+    reads once: whole partitions of it (0 when it has none)."""
+    if not w.prefix or partition % 32:
+        return 0
+    return (w.prefix // partition) * partition
 
 
 def sequence_history(setup: DecodeSetup, s: int, device="cuda"):

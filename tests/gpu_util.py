@@ -107,3 +107,42 @@ def normal_case(ctx, hq, hkv, d, bs, v_codec, seed, extra_blocks=3, perm=True):
     n_blocks = sum((c + bs - 1) // bs for c in ctx) + extra_blocks
     order = rng.permutation(n_blocks) if perm else None
     return SmallCase(hk, hv, q, hq, hkv, d, bs, v_codec, n_blocks, order)
+
+
+def gathered_pool(setup, s):
+    """This sequence's blocks as stored on the GPU, in logical order (a
+    runner.DecodeSetup)."""
+    pool = setup.pool
+    nb = (int(setup.ctx[s]) + pool.block_size - 1) // pool.block_size
+    table = setup.tables[s, :nb].long()
+    g = paged.PoolArrays(nb, pool.num_kv_heads, pool.block_size, pool.head_dim, pool.v_int4)
+    g.k_codes = pool.k_codes[table].cpu().numpy()
+    g.v_codes = pool.v_codes[table].cpu().numpy()
+    g.k_scale = pool.k_scale[table].cpu().numpy()
+    g.v_scale = pool.v_scale[table].cpu().numpy()
+    if pool.v_int4:
+        g.v_zp = pool.v_zp[table].cpu().numpy()
+    return g
+
+
+def check_sequence(setup, s, out, what=None):
+    """Sequence s of a runner.DecodeSetup against the oracle: its blocks bit
+    for bit (re-quantized from the seeded history), out[s] within tolerance."""
+    from paged_block_quantized_amd import runner
+    w = setup.w
+    ctx = int(setup.ctx[s])
+    hk, hv = runner.sequence_history(setup, s)
+    nb = (ctx + w.block_size - 1) // w.block_size
+    ref_pool = paged.PoolArrays(nb, w.num_kv_heads, w.block_size, w.head_dim, w.v_codec == "i4")
+    paged.store_range(ref_pool, list(range(nb)), hk, hv, 0, ctx)
+    g = gathered_pool(setup, s)
+    assert np.array_equal(g.k_codes, ref_pool.k_codes), f"seq {s}: K codes"
+    assert np.array_equal(g.v_codes.view(np.uint8), ref_pool.v_codes.view(np.uint8)), f"seq {s}: V codes"
+    assert np.array_equal(g.k_scale.view(np.uint16), ref_pool.k_scale.view(np.uint16)), f"seq {s}: K scales"
+    assert np.array_equal(g.v_scale.view(np.uint16), ref_pool.v_scale.view(np.uint16)), f"seq {s}: V scales"
+    if ref_pool.v_int4:
+        assert np.array_equal(g.v_zp, ref_pool.v_zp), f"seq {s}: zero points"
+    khat, vhat = paged.gather_dequant(ref_pool, list(range(nb)), ctx)
+    q = setup.q[s].cpu().numpy()
+    ref = attention.decode_attention(q, khat, vhat, setup.sm_scale)
+    return assert_close(out[s], ref, f"{what or w.name} seq {s}")

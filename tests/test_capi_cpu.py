@@ -175,6 +175,20 @@ def test_device_calls_validate_before_launch(lib):
     with pytest.raises(L.PBQError, match="multiple of num_kv_heads"):
         L.paged_attn_decode_append(desc, mem, base, base, base, base, base, 1, 3, base, 4, base,
                                    64, 0.1, 0, None, 0, 0)
+    # the shared-prefix form checks its prefix and partition arguments
+    sp = L.paged_attn_decode_shared_prefix
+    with pytest.raises(L.PBQError, match="shared_tokens must be >= 0"):
+        sp(desc, mem, None, None, None, base, base, 1, 2, base, 8, base, 128, 0.1, 64, -64, None, 0, 0)
+    with pytest.raises(L.PBQError, match="explicit partition_size"):
+        sp(desc, mem, None, None, None, base, base, 1, 2, base, 8, base, 128, 0.1, 0, 64, None, 0, 0)
+    with pytest.raises(L.PBQError, match="multiple of 32"):
+        sp(desc, mem, None, None, None, base, base, 1, 2, base, 8, base, 128, 0.1, 48, 96, None, 0, 0)
+    with pytest.raises(L.PBQError, match="multiple of partition_size"):
+        sp(desc, mem, None, None, None, base, base, 1, 2, base, 8, base, 128, 0.1, 64, 96, None, 0, 0)
+    with pytest.raises(L.PBQError, match="below max_context_len"):
+        sp(desc, mem, None, None, None, base, base, 1, 2, base, 8, base, 128, 0.1, 64, 128, None, 0, 0)
+    with pytest.raises(L.PBQError, match="all NULL"):
+        sp(desc, mem, None, base, None, base, base, 1, 2, base, 8, base, 128, 0.1, 64, 64, None, 0, 0)
     # zero-sized work is a no-op that succeeds without touching the device
     L.kv_quantize_store(desc, mem, base, base, 0, base, base, base, 4, base, 0, 0)
     L.paged_attn_decode_append(desc, mem, base, base, base, base, base, 0, 2, base, 4, base, 64,

@@ -7,47 +7,11 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention, paged
+from oracle import paged
 
-from gpu_util import announce, assert_close
+from gpu_util import announce, check_sequence
 
 pytestmark = pytest.mark.gpu
-
-
-def _gathered_pool(setup, s):
-    """This sequence's blocks as stored on the GPU, in logical order."""
-    pool = setup.pool
-    nb = (int(setup.ctx[s]) + pool.block_size - 1) // pool.block_size
-    table = setup.tables[s, :nb].long()
-    g = paged.PoolArrays(nb, pool.num_kv_heads, pool.block_size, pool.head_dim, pool.v_int4)
-    g.k_codes = pool.k_codes[table].cpu().numpy()
-    g.v_codes = pool.v_codes[table].cpu().numpy()
-    g.k_scale = pool.k_scale[table].cpu().numpy()
-    g.v_scale = pool.v_scale[table].cpu().numpy()
-    if pool.v_int4:
-        g.v_zp = pool.v_zp[table].cpu().numpy()
-    return g
-
-
-def _check_sequence(setup, s, out):
-    from paged_block_quantized_amd import runner
-    w = setup.w
-    ctx = int(setup.ctx[s])
-    hk, hv = runner.sequence_history(setup, s)
-    nb = (ctx + w.block_size - 1) // w.block_size
-    ref_pool = paged.PoolArrays(nb, w.num_kv_heads, w.block_size, w.head_dim, w.v_codec == "i4")
-    paged.store_range(ref_pool, list(range(nb)), hk, hv, 0, ctx)
-    g = _gathered_pool(setup, s)
-    assert np.array_equal(g.k_codes, ref_pool.k_codes), f"seq {s}: K codes"
-    assert np.array_equal(g.v_codes.view(np.uint8), ref_pool.v_codes.view(np.uint8)), f"seq {s}: V codes"
-    assert np.array_equal(g.k_scale.view(np.uint16), ref_pool.k_scale.view(np.uint16)), f"seq {s}: K scales"
-    assert np.array_equal(g.v_scale.view(np.uint16), ref_pool.v_scale.view(np.uint16)), f"seq {s}: V scales"
-    if ref_pool.v_int4:
-        assert np.array_equal(g.v_zp, ref_pool.v_zp), f"seq {s}: zero points"
-    khat, vhat = paged.gather_dequant(ref_pool, list(range(nb)), ctx)
-    q = setup.q[s].cpu().numpy()
-    ref = attention.decode_attention(q, khat, vhat, setup.sm_scale)
-    return assert_close(out[s], ref, f"{w.name} seq {s}")
 
 
 def _run(name, samples):
@@ -62,7 +26,7 @@ def _run(name, samples):
     assert np.all(np.isfinite(out))
     for s in samples:
         announce("full", name, "oracle seq", s)
-        _check_sequence(setup, s, out)
+        check_sequence(setup, s, out)
     # the step is idempotent: a second step gives bitwise the same output
     setup.step()
     torch.cuda.synchronize()
@@ -75,9 +39,23 @@ def test_llama7b_full():
 
 
 def test_shared_prefix_full():
+    """The step reads the 4096-token prefix once (paged_attn_decode_shared_prefix);
+    the per-sequence path (paged_attn_decode_append) gives the same pool bit
+    for bit and outputs within tolerance of it."""
     setup = _run("shared_prefix", samples=[0, 31])
+    assert setup.shared == 4096
     st = setup.pool.stats()
     assert st["used"] == 28800 and st["shared"] == 128 and st["free"] == 0
+    shared_out = setup.out.clone()
+    codes = (setup.pool.k_codes.clone(), setup.pool.v_codes.clone())
+    announce("full shared_prefix per-sequence path")
+    setup.step_unshared()
+    torch.cuda.synchronize()
+    assert torch.equal(codes[0], setup.pool.k_codes) and torch.equal(codes[1], setup.pool.v_codes)
+    for s in (0, 17, 31):
+        check_sequence(setup, s, setup.out.cpu().numpy(), "shared_prefix per-sequence")
+    diff = (setup.out.float() - shared_out.float()).abs().max().item()
+    assert diff <= 4e-3, diff
 
 
 def test_prefill_store_full():

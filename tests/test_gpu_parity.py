@@ -348,3 +348,57 @@ def test_decode_append_equals_store_then_decode(bs, d, vc, g):
         assert_pool_equal(pb, opool)
         assert_close(out_a.cpu().numpy(), ref, f"store+decode part {part}")
         assert_close(out_b.cpu().numpy(), ref, f"decode_append part {part}")
+
+
+SHARED_SHAPES = [
+    # (block_size, head_dim, v codec, query heads per KV head, KV heads, sequences, partition)
+    (16, 64, "i8", 1, 2, 5, 64),
+    (16, 128, "i4", 1, 2, 20, 128),
+    (32, 64, "i4", 1, 3, 5, 64),
+    (32, 128, "i8", 1, 2, 5, 128),
+    (32, 128, "i4", 8, 2, 5, 64),
+    (16, 64, "i8", 4, 1, 5, 96),
+]
+
+
+@pytest.mark.parametrize("bs,d,vc,g,hkv,S,part", SHARED_SHAPES)
+def test_shared_prefix_decode(bs, d, vc, g, hkv, S, part):
+    """Sequences forked from one prefix of two partitions, then ragged
+    continuations.  paged_attn_decode_shared_prefix (prefix tiles read once,
+    on matrix cores, for all sequences' queries) with the current token's
+    store: every sequence's blocks bit-exact and outputs within tolerance of
+    the oracle; the per-sequence path leaves the same pool bit for bit; the
+    plain (no store) form gives the oracle's outputs too.  Two 16-query tiles
+    when sequences x group exceed 16."""
+    import dataclasses
+    from paged_block_quantized_amd import runner, workloads as W
+    from gpu_util import check_sequence
+    announce("shared-prefix", bs, d, vc, g, hkv, S, part)
+    prefix = 2 * part
+    ctx = tuple(prefix + x for x in [1, bs, bs + 1, 3 * bs + 5, 300, 2, 5 * bs, 77, 1, 33,
+                                     bs - 1, 64, 129, 9, 40, 500, 3, 17, 250, 6][:S])
+    w = dataclasses.replace(W.WORKLOADS["shared_prefix"], name="shared_small", num_seqs=S,
+                            num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                            v_codec=vc, ctx_kind="list", ctx=ctx, prefix=prefix, partition=part,
+                            seed=11 * bs + d + g + S)
+    setup = runner.setup_decode(w)
+    assert setup.shared == prefix
+    setup.step()
+    torch.cuda.synchronize()
+    out_shared = setup.out.cpu().numpy()
+    for s in range(S):
+        check_sequence(setup, s, out_shared, "shared-prefix step")
+    snap = {n: t.clone() for n, t in setup.pool.arrays.items()}
+    setup.step_unshared()
+    torch.cuda.synchronize()
+    for n, t in snap.items():
+        assert torch.equal(t, setup.pool.arrays[n]), f"{n} differs between the two step paths"
+    for s in range(S):
+        check_sequence(setup, s, setup.out.cpu().numpy(), "per-sequence step")
+    # plain decode over the same (now stored) contexts
+    out = torch.empty_like(setup.q)
+    setup.pool.decode_shared_prefix(setup.q, out, setup.tables, setup.ctx_dev, setup.max_ctx,
+                                    setup.sm_scale, part, prefix)
+    torch.cuda.synchronize()
+    for s in range(S):
+        check_sequence(setup, s, out.cpu().numpy(), "shared-prefix decode")
