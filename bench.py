@@ -1,8 +1,9 @@
 """Benchmark: one decode step of a block-quantized paged KV cache on one
 MI355X -- store each sequence's current token (re-quantizing its block) and
 run the fused dequantizing split-K attention plus its log-sum-exp reduce, as
-one paged_attn_decode_append call; the same step as two calls
-(kv_quantize_store, paged_attn_decode) is timed beside it.
+one paged_attn_decode_append call (paged_attn_decode_shared_prefix when the
+sequences share a prefix); the same step as two calls (kv_quantize_store,
+paged_attn_decode) is timed beside it.
 
 Prints ONE JSON line.  ``value`` is the step's algorithmic HBM bytes per
 second (GB/s = 1e9 B/s) with all inputs resident in HBM; the line also gives
@@ -197,23 +198,19 @@ def main():
             fl.append(a.elapsed_time(b))
         del flush
 
-    # context: a plain streaming read of the same size (torch's sum over int32
-    # words), cycling through four buffers, as a practical read ceiling
-    ceiling = None
-    if not args.only_timed:
-        words = max(1, min(dbytes, 1 << 30) // 4)
-        bufs = [torch.ones(words, dtype=torch.int32, device="cuda") for _ in range(4)]
-        for b in bufs:
-            b.sum()
-        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # context: with a shared prefix, the per-sequence step (the prefix read
+    # by every sequence) for comparison with the shared-prefix call
+    unshared = float("nan")
+    if setup.shared:
+        ua, ub = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_u = min(K, 20)
         torch.cuda.synchronize()
-        ea.record(stream)
-        for i in range(20):
-            bufs[i % 4].sum()
-        eb.record(stream)
+        ua.record(stream)
+        for i in range(n_u):
+            setup.step_unshared(r=i % R)
+        ub.record(stream)
         torch.cuda.synchronize()
-        ceiling = round(words * 4 * 20 / (ea.elapsed_time(eb) * 1e-3) / 1e9, 1)
-        del bufs
+        unshared = ua.elapsed_time(ub) / n_u
 
     step_bytes = dbytes + sbytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -242,7 +239,6 @@ def main():
             "pool_copies_rotated": R,
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "plain_read_gbs": ceiling,
         "tokens_per_s_per_layer": round(S / (ms_step * 1e-3), 1),
         "step_bytes": step_bytes,
         "kernels_ms": {"paged_attn_decode_append": round(step_call_ms, 5),
@@ -253,10 +249,14 @@ def main():
                        "separate_quantize_store_1tok": round(store_ms, 5),
                        "separate_paged_attn_decode": round(dec_ms, 5),
                        "paged_attn_decode_append_same_pool_back_to_back": _r5(np.mean(dec_same)),
-                       "paged_attn_decode_after_1GiB_flush": _r5(np.median(fl))},
+                       "paged_attn_decode_after_1GiB_flush": _r5(np.median(fl)),
+                       "per_sequence_step_without_shared_prefix": _r5(unshared)},
         "roofline": {
-            "kernel": ("paged_attn_decode_append: the current token's store fused into the split-K "
-                       "decode (plus the reduce kernel when partitions are split), one call"),
+            "kernel": (("paged_attn_decode_shared_prefix: the prefix's partitions once for all sequences "
+                        "(grouped kernel), the store kernel, the per-sequence partitions, the reduce; one call")
+                       if setup.shared else
+                       ("paged_attn_decode_append: the current token's store fused into the split-K "
+                        "decode (plus the reduce kernel when partitions are split), one call")),
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,

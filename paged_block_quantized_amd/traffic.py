@@ -41,7 +41,7 @@ DECODE_KERNELS = ("attn_partition_", "attn_reduce", "quantize_store")
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("paged_attn.hip", "device_common.h"):
+    for f in ("paged_attn.hip", "quantize_store.hip", "store_tile.h", "device_common.h"):
         with open(os.path.join(ROOT, "paged_block_quantized_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -104,13 +104,13 @@ def _copy_kernel(per):
 
 
 def _step_kernels(per, calls):
-    """{kernel: median counter per step} over the dispatches of the last
-    `calls` steps: those from the first of the partition kernel's last
-    `calls` dispatches on (earlier store dispatches build the pool)."""
+    """{kernel: median counter per step} over the dispatches of the steps:
+    those from the first partition-kernel dispatch on (the pool is built by
+    store dispatches alone; a step may hold several partition kernels)."""
     parts = [d for n, v in per.items() if "attn_partition_" in n for d, _ in v]
     if len(parts) < calls:
         raise SystemExit("fewer partition-kernel dispatches than steps")
-    first = sorted(parts)[-calls]
+    first = min(parts)
     out = {}
     for n, v in per.items():
         if any(k in n for k in DECODE_KERNELS):
