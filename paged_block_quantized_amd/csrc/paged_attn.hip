@@ -192,7 +192,7 @@ void attn_partition_mha(AttnArgs a) {
     // 1 write the tiles to the pool (writes mixed into the bulk of the reads
     // cost several times their size).
     __shared__ __align__(16) uint8_t s_tile[FUSED ? KT + VT : 16];
-    __shared__ uint32_t s_tscale[3];
+    __shared__ uint32_t s_tscale[5];
     const bool fused = FUSED && p == nparts - 1 && nblk > 0;   // uniform in the group
     if (fused && w < 2) {
         const TileStoreArgs t{const_cast<int8_t*>(a.k_codes), const_cast<uint8_t*>(a.v_codes),
@@ -203,13 +203,17 @@ void attn_partition_mha(AttnArgs a) {
         if (w == 0) {
             const TileScales ts = store_tile<BS, D, V4, true, true, false>(
                 t, h, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, false);
-            if (lane == 0) s_tscale[0] = ts.k_scale;
+            if (lane == 0) {
+                s_tscale[0] = ts.k_scale;
+                s_tscale[3] = ts.prev;
+            }
         } else {
             const TileScales ts = store_tile<BS, D, V4, true, false, true>(
                 t, h, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, false);
             if (lane == 0) {
                 s_tscale[1] = ts.v_scale;
                 s_tscale[2] = ts.v_zp;
+                s_tscale[4] = ts.prev;
             }
         }
     }
@@ -764,7 +768,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
     // from LDS while waves 0 and 1 write the tiles to the pool (only the first
     // 16-head tile of a KV head writes).
     __shared__ __align__(16) uint8_t s_tile[FUSED ? KT + VT : 16];
-    __shared__ uint32_t s_tscale[3];
+    __shared__ uint32_t s_tscale[5];
     const bool fused = FUSED && nblk > 0;   // one partition: this group holds the last block
     if (fused && w < 2) {
         const TileStoreArgs t{const_cast<int8_t*>(a.k_codes), const_cast<uint8_t*>(a.v_codes),
@@ -775,13 +779,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
         if (w == 0) {
             const TileScales ts = store_tile<BS, D, V4, true, true, false>(
                 t, kvh, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, false);
-            if (lane == 0) s_tscale[0] = ts.k_scale;
+            if (lane == 0) {
+                s_tscale[0] = ts.k_scale;
+                s_tscale[3] = ts.prev;
+            }
         } else {
             const TileScales ts = store_tile<BS, D, V4, true, false, true>(
                 t, kvh, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, false);
             if (lane == 0) {
                 s_tscale[1] = ts.v_scale;
                 s_tscale[2] = ts.v_zp;
+                s_tscale[4] = ts.prev;
             }
         }
         // the staged loads' waits count on loads alone: let the stores drain

@@ -42,9 +42,11 @@ struct TileStoreArgs {
     int32_t num_kv_heads;
 };
 
-// Raw bits of the scales (and zero point) a tile store wrote.
+// Raw bits of the scales (and zero point) a tile store wrote; with LDS set,
+// also what the pool held for the tile before (prev: K scale, or V scale |
+// zero point << 16), for write_stored_tile.
 struct TileScales {
-    uint32_t k_scale, v_scale, v_zp;
+    uint32_t k_scale, v_scale, v_zp, prev;
 };
 
 // Codes of one tile with scale s (an fp16 value; s == 0 for an all-zero
@@ -127,6 +129,11 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
 #pragma unroll
         for (int it = 0; it < NIT; ++it) kx[it] = *(const f16x8*)(row_src(a.tail_k, a.k, it * RPI + r_in) + col);
     }
+    const int64_t tile = (int64_t)phys * H + g;
+    if constexpr (LDS) {   // the pool's scale bits before this store, loaded with the rows
+        if constexpr (DO_K) out.prev = a.k_scale[tile];
+        else out.prev = a.v_scale[tile] | (V4 ? (uint32_t)a.v_zp[tile] << 16 : 0u);
+    }
     uint32_t vw[DO_V ? BS : 1];   // V row r: dims DPL*lane .. +DPL-1 (fp16 bits)
     if constexpr (DO_V) {
 #pragma unroll
@@ -149,8 +156,6 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
     auto vx = [&](int k, int r) -> float {
         return bits_to_f16f((uint16_t)(k ? vw[r] >> 16 : vw[r] & 0xFFFFu));
     };
-
-    const int64_t tile = (int64_t)phys * H + g;
 
     // ---- K: INT8 symmetric -------------------------------------------------
     if constexpr (DO_K) {
@@ -335,38 +340,53 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
 }
 
 // Pool writes of a tile that store_tile quantized with wr false (codes left
-// in LDS at lds_k / lds_v, scale bits and zero point in `sc`): wave 0 writes
-// the K codes and scale, wave 1 the V codes, scale and zero point, each also
-// the new row at position pos to the tail slot when its block stays
-// partial.  The fused decode calls it after its loop, so that these writes
-// do not meet the bulk of the pool reads.  new_row is the row of a.k / a.v
-// that holds position pos.
+// in LDS at lds_k / lds_v; sc: K scale, V scale and zero point bits, then
+// the K and the V `prev` of store_tile): wave 0 writes K, wave 1 V, each also
+// the new row at position pos to the tail slot when its block stays partial.
+// When the block already held rows (pos % bs > 0) and its scale (and zero
+// point) did not change, the earlier rows' codes are unchanged -- the same
+// exact rows under the same scale -- and only the new token's codes are
+// written: its K row (D bytes), and its byte of every V dim row.  The fused
+// decode calls it after its loop.  new_row is the row of a.k / a.v that holds
+// position pos.
 template <int BS, int D, bool V4>
 __device__ __forceinline__ void write_stored_tile(const TileStoreArgs& a, int w, int g, int slot, int new_row, int pos,
                                                   int phys, const uint8_t* lds_k, const uint8_t* lds_v,
                                                   const uint32_t* sc) {
     constexpr int KT = BS * D;
-    constexpr int VT = V4 ? BS * D / 2 : BS * D;
+    constexpr int VROW = V4 ? BS / 2 : BS;
+    constexpr int VT = D * VROW;
     const int lane = threadIdx.x & 63;
     const int H = a.num_kv_heads;
     const int64_t tile = (int64_t)phys * H + g;
-    const bool tail = (pos + 1) % BS != 0;   // the block stays partial
-    const int64_t trow = (((int64_t)slot * H + g) * BS + pos % BS) * D;
+    const int r = pos % BS;
+    const bool tail = r != BS - 1;   // the block stays partial
+    const int64_t trow = (((int64_t)slot * H + g) * BS + r) * D;
     const int64_t nrow = ((int64_t)new_row * H + g) * D;
     if (w == 0) {
+        if (r == 0 || sc[3] != sc[0]) {
 #pragma unroll
-        for (int c = 0; c < KT / 1024; ++c)
-            *(u32x4*)(a.k_codes + tile * KT + 1024 * c + 16 * lane) = *(const u32x4*)(lds_k + 1024 * c + 16 * lane);
-        if (lane == 0) a.k_scale[tile] = (uint16_t)sc[0];
+            for (int c = 0; c < KT / 1024; ++c)
+                *(u32x4*)(a.k_codes + tile * KT + 1024 * c + 16 * lane) = *(const u32x4*)(lds_k + 1024 * c + 16 * lane);
+            if (lane == 0) a.k_scale[tile] = (uint16_t)sc[0];
+        } else if (lane < D / 16) {
+            *(u32x4*)(a.k_codes + tile * KT + r * D + 16 * lane) = *(const u32x4*)(lds_k + r * D + 16 * lane);
+        }
         if (tail && lane < D / 8) *(u32x4*)(a.tail_k + trow + 8 * lane) = *(const u32x4*)(a.k + nrow + 8 * lane);
     } else if (w == 1) {
+        if (r == 0 || sc[4] != (sc[1] | (V4 ? sc[2] << 16 : 0u))) {
 #pragma unroll
-        for (int c = 0; c < (VT + 1023) / 1024; ++c)
-            if (VT % 1024 == 0 || 1024 * c + 16 * lane < VT)
-                *(u32x4*)(a.v_codes + tile * VT + 1024 * c + 16 * lane) = *(const u32x4*)(lds_v + 1024 * c + 16 * lane);
-        if (lane == 0) {
-            a.v_scale[tile] = (uint16_t)sc[1];
-            if constexpr (V4) a.v_zp[tile] = (uint8_t)sc[2];
+            for (int c = 0; c < (VT + 1023) / 1024; ++c)
+                if (VT % 1024 == 0 || 1024 * c + 16 * lane < VT)
+                    *(u32x4*)(a.v_codes + tile * VT + 1024 * c + 16 * lane) = *(const u32x4*)(lds_v + 1024 * c + 16 * lane);
+            if (lane == 0) {
+                a.v_scale[tile] = (uint16_t)sc[1];
+                if constexpr (V4) a.v_zp[tile] = (uint8_t)sc[2];
+            }
+        } else {
+            const int b = V4 ? r / 2 : r;   // the new token's byte of each dim row
+#pragma unroll
+            for (int d = lane; d < D; d += 64) a.v_codes[tile * VT + d * VROW + b] = lds_v[d * VROW + b];
         }
         if (tail && lane < D / 8) *(u32x4*)(a.tail_v + trow + 8 * lane) = *(const u32x4*)(a.v + nrow + 8 * lane);
     }
