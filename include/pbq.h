@@ -128,6 +128,7 @@ typedef struct kv_pool_stats_t {
     int32_t used;   /* blocks with refcount > 0 */
     int32_t shared; /* blocks with refcount > 1 */
     int32_t seqs;   /* live sequences */
+    int32_t cached; /* full blocks in the prefix-cache index */
 } kv_pool_stats_t;
 
 typedef struct kv_pool kv_pool; /* opaque host state */
@@ -151,6 +152,23 @@ void kv_pool_destroy(kv_pool* pool); /* NULL is ignored */
  * KV_ERR_NO_SLOTS leave the pool unchanged; KV_ERR_STATE if seq exists;
  * KV_ERR_INVALID if num_tokens < 0. */
 kv_status kv_seq_alloc(kv_pool* pool, int64_t seq, int32_t num_tokens);
+
+/* kv_seq_alloc for a request whose token ids are known ([yunthe] "prefix
+ * caching": blocks of the pool that already hold the request's prefix are
+ * mapped instead of recomputed).  Full blocks j = 0, 1, ... are looked up in
+ * order, each by (the physical block before it, its block_size token ids),
+ * until the first miss; hits are shared (refcount + 1).  The remaining blocks
+ * come from the free stack as in kv_seq_alloc, and each fresh full block is
+ * entered in the index at once; the partial last block is private.  A block
+ * leaves the index when its count reaches zero.  *cached_tokens (may be NULL)
+ * receives the number of leading tokens whose codes are already in the pool
+ * (hits x block_size): the caller stores positions cached_tokens ..
+ * num_tokens - 1 (kv_quantize_store with start_pos = cached_tokens) before
+ * any decode reads this or another sequence's fresh blocks.  token_ids:
+ * host int32 [num_tokens] (NULL when 0).  Errors as kv_seq_alloc, all-or-
+ * nothing. */
+kv_status kv_seq_alloc_prefix(kv_pool* pool, int64_t seq, const int32_t* token_ids,
+                              int32_t num_tokens, int32_t* cached_tokens);
 
 /* child shares every block of parent (refcount + 1 each) and takes the lowest
  * free tail slot.  If parent's last block is partial, one KV_COPY_SLOT

@@ -42,6 +42,21 @@ Readings where the pages are silent or disagree
   slot copy (parent slot -> child slot).
 * Error kinds: unknown sequence, sequence already present, no free blocks,
   no free slot, bad argument.  A failed call leaves the state unchanged.
+
+Prefix caching (yunthe.com "prefix caching": a new request first looks for
+blocks of the pool that already hold its prefix and, on a hit, maps them
+instead of recomputing; the page gives no matching rule or lifetime):
+* Only full blocks are matched, in order from the first; the lookup stops at
+  the first block that is not found.  A block's identity is its parent block
+  (the physical block before it, or none) and its own bs token ids, so a hit
+  means the whole prefix up to and including the block is equal.
+* Hits are shared (refcount + 1); the other blocks come from the free stack
+  as in ``alloc``, and each fresh full block is entered in the index at
+  once (its codes are the caller's to store before anything reads them).
+  The partial last block is private and never entered.
+* A block leaves the index when its count reaches zero (a freed block's
+  codes may be overwritten by its next owner): hits are blocks some live
+  sequence holds.
 """
 
 from dataclasses import dataclass, field
@@ -90,6 +105,8 @@ class BlockPoolModel:
     free: list = field(init=False)
     refcount: list = field(init=False)
     seqs: dict = field(init=False)
+    index: dict = field(init=False)     # (parent block or -1, token ids) -> block
+    key_of: dict = field(init=False)    # block -> its index key
 
     def __post_init__(self):
         if self.num_blocks <= 0 or self.block_size <= 0 or self.max_seqs <= 0:
@@ -101,6 +118,8 @@ class BlockPoolModel:
         self.free = order
         self.refcount = [0] * self.num_blocks
         self.seqs = {}
+        self.index = {}
+        self.key_of = {}
 
     # -- helpers ---------------------------------------------------------
     def _lowest_free_slot(self):
@@ -130,6 +149,40 @@ class BlockPoolModel:
             table.append(b)
         self.seqs[seq] = SeqState(table, num_tokens, slot)
         return list(table)
+
+    def alloc_prefix(self, seq: int, tokens):
+        """alloc for len(tokens) tokens that reuses the indexed blocks of the
+        longest matching full-block prefix; returns (table, cached tokens)."""
+        tokens = [int(t) for t in tokens]
+        n = len(tokens)
+        if seq in self.seqs:
+            raise BadState("sequence already present")
+        slot = self._lowest_free_slot()
+        bs = self.block_size
+        need = self._blocks_for(n)
+        hits = []
+        parent = -1
+        for j in range(n // bs):
+            b = self.index.get((parent, tuple(tokens[j * bs:(j + 1) * bs])))
+            if b is None:
+                break
+            hits.append(b)
+            parent = b
+        if need - len(hits) > len(self.free):
+            raise NoBlocks("not enough free blocks")
+        table = list(hits)
+        for b in hits:
+            self.refcount[b] += 1
+        for j in range(len(hits), need):
+            b = self.free.pop()
+            self.refcount[b] = 1
+            table.append(b)
+            if (j + 1) * bs <= n:
+                key = (table[j - 1] if j > 0 else -1, tuple(tokens[j * bs:(j + 1) * bs]))
+                self.index[key] = b
+                self.key_of[b] = key
+        self.seqs[seq] = SeqState(table, n, slot)
+        return list(table), len(hits) * bs
 
     def fork(self, parent: int, child: int):
         if parent not in self.seqs:
@@ -183,6 +236,8 @@ class BlockPoolModel:
             self.refcount[b] -= 1
             if self.refcount[b] == 0:
                 self.free.append(b)
+                if b in self.key_of:
+                    del self.index[self.key_of.pop(b)]
 
     def table(self, seq: int):
         if seq not in self.seqs:
@@ -194,7 +249,7 @@ class BlockPoolModel:
         used = sum(1 for r in self.refcount if r > 0)
         shared = sum(1 for r in self.refcount if r > 1)
         return dict(total=self.num_blocks, free=len(self.free), used=used,
-                    shared=shared, seqs=len(self.seqs))
+                    shared=shared, seqs=len(self.seqs), cached=len(self.index))
 
     def check_invariants(self):
         """Each block is either on the free stack or referenced; counts equal
@@ -214,3 +269,9 @@ class BlockPoolModel:
         slots = [st.slot for st in self.seqs.values()]
         assert len(set(slots)) == len(slots)
         assert all(0 <= s < self.max_seqs for s in slots)
+        # indexed blocks are held, their parents too, and the maps agree
+        assert len(self.index) == len(self.key_of)
+        for key, b in self.index.items():
+            assert self.key_of[b] == key and self.refcount[b] > 0
+            assert key[0] == -1 or self.refcount[key[0]] > 0
+            assert len(key[1]) == self.block_size

@@ -52,11 +52,11 @@ class kv_copy(ctypes.Structure):
 
 
 class kv_pool_stats_t(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("total", "free", "used", "shared", "seqs")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("total", "free", "used", "shared", "seqs", "cached")]
 
 
 EXPORTS = [
-    "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_seq_alloc",
+    "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_seq_alloc", "kv_seq_alloc_prefix",
     "kv_seq_fork", "kv_seq_append", "kv_seq_free", "kv_seq_table",
     "kv_batch_tables", "kv_pool_stats", "kv_pool_free_list", "kv_copy_blocks",
     "kv_quantize_store", "paged_attn_workspace_bytes", "paged_attn_decode",
@@ -83,6 +83,7 @@ def lib():
             "kv_pool_create": (st, [P(kv_pool_desc), P(I32), P(VP)]),
             "kv_pool_destroy": (None, [VP]),
             "kv_seq_alloc": (st, [VP, I64, I32]),
+            "kv_seq_alloc_prefix": (st, [VP, I64, P(I32), I32, P(I32)]),
             "kv_seq_fork": (st, [VP, I64, I64, P(kv_copy), I32, P(I32)]),
             "kv_seq_append": (st, [VP, I64, I32, P(kv_copy), I32, P(I32)]),
             "kv_seq_free": (st, [VP, I64]),
@@ -164,6 +165,16 @@ def kv_pool_destroy(handle):
 
 def kv_seq_alloc(handle, seq, num_tokens):
     _check(lib().kv_seq_alloc(handle, int(seq), int(num_tokens)))
+
+
+def kv_seq_alloc_prefix(handle, seq, token_ids):
+    """Returns the number of leading tokens already held by shared blocks."""
+    ids = [int(t) for t in token_ids]
+    arr = (ctypes.c_int32 * max(1, len(ids)))(*ids)
+    cached = ctypes.c_int32()
+    _check(lib().kv_seq_alloc_prefix(handle, int(seq), arr if ids else None, len(ids),
+                                     ctypes.byref(cached)))
+    return cached.value
 
 
 def _copies_out(fn, *args):

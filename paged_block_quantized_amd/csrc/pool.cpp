@@ -17,6 +17,13 @@
 //    sequence owns an fp16 slot with the exact rows of its partially filled
 //    last block, so the block can be re-quantized from exact values; a
 //    sequence takes the lowest free slot.
+//  * yunthe.com "prefix caching": a new request first looks for pool blocks
+//    that already hold its prefix and maps them on a hit.  Readings: full
+//    blocks only, matched in order from the first until the first miss; a
+//    block is identified by its parent block and its own token ids (so a hit
+//    means the whole prefix is equal, with no hash collisions to fear); fresh
+//    full blocks enter the index when allocated; a block leaves it when its
+//    count reaches zero.
 // The pool is single-threaded per handle; no call touches device memory.
 
 #include <stdint.h>
@@ -36,12 +43,28 @@ struct SeqState {
     int32_t slot = 0;
 };
 
+// Prefix-cache key: the block before (-1 for the first) and the block's ids.
+struct PrefixKey {
+    int32_t parent;
+    std::vector<int32_t> tokens;
+    bool operator==(const PrefixKey& o) const { return parent == o.parent && tokens == o.tokens; }
+};
+struct PrefixKeyHash {
+    size_t operator()(const PrefixKey& k) const {
+        uint64_t h = 1469598103934665603ull ^ (uint32_t)k.parent;   // FNV-1a over the words
+        for (int32_t t : k.tokens) h = (h ^ (uint32_t)t) * 1099511628211ull;
+        return (size_t)h;
+    }
+};
+
 struct kv_pool {
     kv_pool_desc desc{};
     std::vector<int32_t> free_stack;  // popped from the back
     std::vector<int32_t> refcount;
     std::unordered_map<int64_t, SeqState> seqs;
     std::set<int32_t> free_slots;
+    std::unordered_map<PrefixKey, int32_t, PrefixKeyHash> prefix_index;
+    std::unordered_map<int32_t, PrefixKey> prefix_key_of;
 };
 
 namespace {
@@ -117,6 +140,49 @@ kv_status kv_seq_alloc(kv_pool* pool, int64_t seq, int32_t num_tokens) {
     return KV_OK;
 }
 
+kv_status kv_seq_alloc_prefix(kv_pool* pool, int64_t seq, const int32_t* token_ids,
+                              int32_t num_tokens, int32_t* cached_tokens) {
+    if (!pool) return pbq::fail(KV_ERR_INVALID, "pool is NULL");
+    if (num_tokens < 0) return pbq::fail(KV_ERR_INVALID, "num_tokens < 0");
+    if (num_tokens > 0 && !token_ids) return pbq::fail(KV_ERR_INVALID, "token_ids is NULL");
+    if (pool->seqs.count(seq)) return pbq::fail(KV_ERR_STATE, "sequence already present");
+    if (pool->free_slots.empty()) return pbq::fail(KV_ERR_NO_SLOTS, "no free tail slot");
+    const int64_t bs = pool->desc.block_size;
+    const int64_t need = blocks_for(num_tokens, bs);
+    std::vector<int32_t> hits;
+    PrefixKey key{-1, {}};
+    for (int64_t j = 0; j < num_tokens / bs; ++j) {
+        key.tokens.assign(token_ids + j * bs, token_ids + (j + 1) * bs);
+        auto it = pool->prefix_index.find(key);
+        if (it == pool->prefix_index.end()) break;
+        hits.push_back(it->second);
+        key.parent = it->second;
+    }
+    if (need - (int64_t)hits.size() > (int64_t)pool->free_stack.size())
+        return pbq::fail(KV_ERR_NO_BLOCKS, "not enough free blocks");
+    SeqState st;
+    st.table = hits;
+    for (int32_t b : hits) pool->refcount[b] += 1;
+    for (int64_t j = (int64_t)hits.size(); j < need; ++j) {
+        int32_t b = pool->free_stack.back();
+        pool->free_stack.pop_back();
+        pool->refcount[b] = 1;
+        if ((j + 1) * bs <= num_tokens) {   // a full block enters the index
+            PrefixKey k{j > 0 ? st.table[j - 1] : -1,
+                        std::vector<int32_t>(token_ids + j * bs, token_ids + (j + 1) * bs)};
+            pool->prefix_index.emplace(k, b);
+            pool->prefix_key_of.emplace(b, std::move(k));
+        }
+        st.table.push_back(b);
+    }
+    st.num_tokens = num_tokens;
+    st.slot = *pool->free_slots.begin();
+    pool->free_slots.erase(pool->free_slots.begin());
+    pool->seqs.emplace(seq, std::move(st));
+    if (cached_tokens) *cached_tokens = (int32_t)(hits.size() * bs);
+    return KV_OK;
+}
+
 kv_status kv_seq_fork(kv_pool* pool, int64_t parent, int64_t child,
                       kv_copy* copies, int32_t cap, int32_t* n_copies) {
     if (!pool) return pbq::fail(KV_ERR_INVALID, "pool is NULL");
@@ -186,7 +252,14 @@ kv_status kv_seq_free(kv_pool* pool, int64_t seq) {
     if (it == pool->seqs.end()) return pbq::fail(KV_ERR_UNKNOWN_SEQ, "unknown sequence");
     for (int32_t b : it->second.table) {
         pool->refcount[b] -= 1;
-        if (pool->refcount[b] == 0) pool->free_stack.push_back(b);
+        if (pool->refcount[b] == 0) {
+            pool->free_stack.push_back(b);
+            auto k = pool->prefix_key_of.find(b);
+            if (k != pool->prefix_key_of.end()) {
+                pool->prefix_index.erase(k->second);
+                pool->prefix_key_of.erase(k);
+            }
+        }
     }
     pool->free_slots.insert(it->second.slot);
     pool->seqs.erase(it);
@@ -246,6 +319,7 @@ kv_status kv_pool_stats(const kv_pool* pool, kv_pool_stats_t* out) {
     out->used = used;
     out->shared = shared;
     out->seqs = (int32_t)pool->seqs.size();
+    out->cached = (int32_t)pool->prefix_index.size();
     return KV_OK;
 }
 

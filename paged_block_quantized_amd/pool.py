@@ -71,6 +71,11 @@ class KVPool:
         L.kv_seq_alloc(self.handle, seq, num_tokens)
         return self.table(seq)[0]
 
+    def alloc_prefix(self, seq, token_ids):
+        """alloc through the prefix cache; returns (block table, cached tokens)."""
+        cached = L.kv_seq_alloc_prefix(self.handle, seq, token_ids)
+        return self.table(seq)[0], cached
+
     def fork(self, parent, child):
         return L.kv_seq_fork(self.handle, parent, child)
 

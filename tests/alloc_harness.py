@@ -49,17 +49,27 @@ def run_golden_trace(make_pool, errors):
             assert [list(c) for c in res] == st["expect_copies"], st
         if "expect_free" in st:
             assert pool.free_list() == st["expect_free"], st
-    assert pool.stats() == g["final_stats"]
+    stats = pool.stats()
+    assert {k: stats[k] for k in g["final_stats"]} == g["final_stats"]
 
 
-def random_ops(rng, n_ops, max_seq_id=12, max_tokens=40):
+def random_ops(rng, n_ops, max_seq_id=12, max_tokens=40, prefix=False):
     """A seeded list of (op, args) tuples mixing every operation, including
-    ones that must fail (unknown sequences, over-allocation)."""
+    ones that must fail (unknown sequences, over-allocation).  With prefix,
+    a quarter of the allocations go through the prefix cache with token ids
+    that share prefixes of three seeded prompts (vocabulary of 3, so that
+    different prompts also share blocks)."""
+    prompts = [list(rng.integers(0, 3, max_tokens)) for _ in range(3)]
     ops = []
     for _ in range(n_ops):
         r = rng.random()
         a = int(rng.integers(0, max_seq_id))
-        if r < 0.3:
+        if prefix and r < 0.12:
+            n = int(rng.integers(0, max_tokens))
+            k = int(rng.integers(0, n + 1))
+            toks = prompts[int(rng.integers(0, 3))][:k] + list(rng.integers(0, 3, n - k))
+            ops.append(("prefix", a, [int(t) for t in toks]))
+        elif r < 0.3:
             ops.append(("alloc", a, int(rng.integers(0, max_tokens))))
         elif r < 0.45:
             ops.append(("fork", a, int(rng.integers(0, max_seq_id))))
@@ -75,6 +85,8 @@ def apply_op(pool, op, errors):
     try:
         if op[0] == "alloc":
             res = pool.alloc(op[1], op[2])
+        elif op[0] == "prefix":
+            res = pool.alloc_prefix(op[1], op[2])
         elif op[0] == "fork":
             res = [tuple(c) for c in pool.fork(op[1], op[2])]
         elif op[0] == "append":

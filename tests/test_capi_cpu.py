@@ -53,6 +53,10 @@ class CAdapter:
         L.kv_seq_alloc(self.h, s, n)
         return L.kv_seq_table(self.h, s)[0]
 
+    def alloc_prefix(self, s, toks):
+        cached = L.kv_seq_alloc_prefix(self.h, s, toks)
+        return L.kv_seq_table(self.h, s)[0], cached
+
     def fork(self, p, c):
         return L.kv_seq_fork(self.h, p, c)
 
@@ -83,11 +87,12 @@ def test_golden_trace_c(lib):
 @given(seed=hst.integers(0, 2 ** 31 - 1), n_blocks=hst.integers(1, 24),
        bs=hst.sampled_from([1, 2, 4, 16, 32]))
 def test_c_allocator_matches_model(lib, seed, n_blocks, bs):
+    """Every operation, prefix-cached allocation included, bit for bit."""
     rng = np.random.default_rng(seed)
     perm = rng.permutation(n_blocks)
     model = A.BlockPoolModel(n_blocks, bs, 6, perm)
     c = CAdapter(n_blocks, bs, 6, perm)
-    for op in random_ops(rng, 120):
+    for op in random_ops(rng, 120, prefix=True):
         a = apply_op(model, op, A.AllocError)
         b = apply_op(c, op, L.PBQError)
         assert a == b, op

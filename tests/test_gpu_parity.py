@@ -402,3 +402,63 @@ def test_shared_prefix_decode(bs, d, vc, g, hkv, S, part):
     torch.cuda.synchronize()
     for s in range(S):
         check_sequence(setup, s, out.cpu().numpy(), "shared-prefix decode")
+
+
+@pytest.mark.parametrize("bs,vc", [(16, "i8"), (32, "i4")])
+def test_prefix_cache_end_to_end(bs, vc):
+    """kv_seq_alloc_prefix: requests whose token ids share prefixes map the
+    cached blocks and store only their uncached positions; the pool equals
+    the oracle's (model allocator + store of the same ranges) bit for bit,
+    shared blocks are not rewritten, and decode over the full contexts
+    matches the oracle.  K/V rows are a seeded function of (token id,
+    position), as a model's would be, so equal prefixes have equal rows."""
+    announce("prefix-cache", bs, vc)
+    from paged_block_quantized_amd import KVPool
+    h, d, hq = 2, 64, 4
+    rng = np.random.default_rng(77 + bs)
+    vocab = 5
+    table_k = rng.standard_normal((vocab, 4096, h, d)).astype(np.float16)
+    table_v = rng.standard_normal((vocab, 4096, h, d)).astype(np.float16)
+    base = [int(t) for t in rng.integers(0, vocab, 8 * bs)]
+    reqs = [base[:5 * bs + 3], base[:3 * bs] + [0] * (bs + 1), base[:5 * bs + 3],
+            base[:2 * bs], [1] * (2 * bs + 7), base[:4 * bs] + [2] * (2 * bs)]
+    N = 64
+    order = rng.permutation(N)
+    pool = KVPool(N, bs, h, d, vc, max_seqs=len(reqs), free_order=order)
+    model = A.BlockPoolModel(N, bs, len(reqs), order)
+    opool = paged.PoolArrays(N, h, bs, d, vc == "i4")
+    shared_before = {}
+    for s, ids in enumerate(reqs):
+        tab, cached = pool.alloc_prefix(s, ids)
+        assert (tab, cached) == model.alloc_prefix(s, ids)
+        assert cached % bs == 0 and cached <= len(ids)
+        hk = np.stack([table_k[t, p] for p, t in enumerate(ids)])
+        hv = np.stack([table_v[t, p] for p, t in enumerate(ids)])
+        n = len(ids)
+        if cached:
+            assert np.array_equal(pool.k_codes[tab[0]].cpu().numpy(), opool.k_codes[tab[0]])
+            shared_before[s] = pool.k_codes[torch.tensor(tab[:cached // bs])].clone()
+        if n > cached:
+            t, _, sl = pool.batch_tables([s], max(1, len(tab)))
+            k = torch.from_numpy(hk[cached:]).cuda()
+            v = torch.from_numpy(hv[cached:]).cuda()
+            cu = torch.tensor([0, n - cached], dtype=torch.int32, device="cuda")
+            st = torch.tensor([cached], dtype=torch.int32, device="cuda")
+            pool.quantize_store(k, v, cu, st, t.cuda(), sl.cuda(), n - cached)
+            paged.store_range(opool, tab, hk, hv, cached, n)
+        torch.cuda.synchronize()
+    assert_pool_equal(pool, opool)
+    for s, codes in shared_before.items():   # shared blocks were not rewritten
+        tab = model.table(s)[0]
+        assert torch.equal(pool.k_codes[torch.tensor(tab[:codes.shape[0]])], codes)
+    assert model.stats() == pool.stats()
+    S = len(reqs)
+    tables, ctx_h, _ = pool.batch_tables(list(range(S)), 8)
+    q = rng.standard_normal((S, hq, d)).astype(np.float16)
+    qd = torch.from_numpy(q).cuda()
+    out = torch.empty_like(qd)
+    pool.decode(qd, out, tables.cuda(), ctx_h.cuda(), int(ctx_h.max()), 1 / np.sqrt(d), 0)
+    torch.cuda.synchronize()
+    ref = attention.paged_decode(opool, [model.table(s)[0] for s in range(S)], ctx_h.numpy(), q,
+                                 1 / np.sqrt(d))
+    assert_close(out.cpu().numpy(), ref, "prefix-cache decode")

@@ -22,6 +22,9 @@ class ModelAdapter:
     def alloc(self, s, n):
         return self.m.alloc(s, n)
 
+    def alloc_prefix(self, s, toks):
+        return self.m.alloc_prefix(s, toks)
+
     def fork(self, p, c):
         return self.m.fork(p, c)
 
@@ -134,3 +137,76 @@ def test_random_ops_keep_invariants(seed, n_blocks, bs):
     for op in random_ops(rng, 80):
         apply_op(m, op, A.AllocError)
         m.check_invariants()
+
+
+def test_prefix_cache_hand_worked():
+    """yunthe "prefix caching", as read: full blocks matched from the first,
+    keyed by (parent block, token ids); hits shared; fresh full blocks
+    indexed; the partial block private; index entries leave with the block."""
+    m = A.BlockPoolModel(16, 4, 8)          # free stack 0..15, popped from 15
+    a = [1, 1, 1, 1, 2, 2, 2, 2, 3, 3]
+    assert m.alloc_prefix(0, a) == ([15, 14, 13], 0)
+    assert m.stats()["cached"] == 2         # blocks 15 and 14; 13 is partial
+    b = [1, 1, 1, 1, 2, 2, 2, 2, 4, 4, 4, 4, 5]
+    assert m.alloc_prefix(1, b) == ([15, 14, 12, 11], 8)
+    assert m.refcount[15] == 2 and m.refcount[14] == 2
+    assert m.alloc_prefix(2, [1, 1, 1, 1, 9, 9, 9, 9]) == ([15, 10], 4)
+    # the same ids without the same parent are no hit
+    assert m.alloc_prefix(3, [2, 2, 2, 2]) == ([9], 0)
+    # the same prompt again: both full blocks hit, the partial one is fresh
+    assert m.alloc_prefix(4, a) == ([15, 14, 8], 8)
+    assert m.stats()["cached"] == 5         # 15, 14, 12, 10, 9
+    m.release(1)                            # 12 and 11 reach zero; 12 leaves the index
+    assert m.stats()["cached"] == 4
+    # its third block left the index with block 12: recomputed into a fresh
+    # block (11, pushed last), the partial one takes 12
+    assert m.alloc_prefix(5, b) == ([15, 14, 11, 12], 8)
+    # an empty request and a request shorter than a block: nothing to match
+    assert m.alloc_prefix(6, []) == ([], 0)
+    m.check_invariants()
+    for s in list(m.seqs):
+        m.release(s)
+    assert m.stats()["cached"] == 0 and m.index == {} and m.stats()["free"] == 16
+    m.check_invariants()
+
+
+def test_prefix_cache_failure_leaves_state_unchanged():
+    m = A.BlockPoolModel(3, 2, 4)
+    m.alloc_prefix(0, [7, 7, 8, 8])
+    snap = (list(m.free), list(m.refcount), dict(m.index))
+    with pytest.raises(A.NoBlocks):
+        m.alloc_prefix(1, [7, 7, 9, 9, 9, 9])   # one hit, two fresh, one free
+    with pytest.raises(A.BadState):
+        m.alloc_prefix(0, [7, 7])
+    assert snap == (list(m.free), list(m.refcount), dict(m.index))
+
+
+@settings(max_examples=60, deadline=None)
+@given(seed=hst.integers(0, 2 ** 31 - 1), n_blocks=hst.integers(1, 24),
+       bs=hst.sampled_from([1, 2, 4, 8]))
+def test_prefix_cache_hits_are_equal_prefixes(seed, n_blocks, bs):
+    """Brute force: after any op sequence, every cached block's parent chain
+    spells a token prefix, and every sequence allocated through the cache
+    holds, at each indexed position, the block that spells its own prefix."""
+    rng = np.random.default_rng(seed)
+    m = A.BlockPoolModel(n_blocks, bs, 6, rng.permutation(n_blocks))
+    toks = {}
+    for op in random_ops(rng, 80, prefix=True):
+        rec = apply_op(m, op, A.AllocError)
+        if rec[0] == "ok" and op[0] == "prefix":
+            toks[op[1]] = op[2]
+        elif rec[0] == "ok" and op[0] in ("alloc", "free"):
+            toks.pop(op[1], None)
+        m.check_invariants()
+
+        def spelled(b):
+            parent, ids = m.key_of[b]
+            return (spelled(parent) if parent != -1 else []) + list(ids)
+
+        for s, ids in toks.items():
+            if s not in m.seqs:
+                continue
+            table = m.seqs[s].table
+            for j, blk in enumerate(table[:len(ids) // bs]):
+                if blk in m.key_of:
+                    assert spelled(blk) == ids[:(j + 1) * bs]
