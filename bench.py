@@ -212,6 +212,26 @@ def main():
         torch.cuda.synchronize()
         unshared = ua.elapsed_time(ub) / n_u
 
+    # context: host cost of a prefix-cached allocation (kv_seq_alloc_prefix) of
+    # one of this workload's requests while the shared prefix is held
+    host_prefix_us = None
+    if w.prefix:
+        from paged_block_quantized_amd import KVPool
+        n_tok = int(setup.ctx.max())
+        hp = KVPool(setup.pool.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.v_codec,
+                    max_seqs=4, device=None)
+        ids = np.random.default_rng(0).integers(0, 32000, n_tok).astype(np.int32)
+        hp.alloc_prefix(0, ids[:w.prefix])
+        reps = 20
+        t0 = time.perf_counter()
+        from paged_block_quantized_amd import _lib as L
+        for i in range(reps):
+            cached = L.kv_seq_alloc_prefix(hp.handle, 1, ids)
+            L.kv_seq_free(hp.handle, 1)
+        host_prefix_us = round((time.perf_counter() - t0) * 1e6 / reps, 1)
+        assert cached == w.prefix
+        hp.close()
+
     step_bytes = dbytes + sbytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = step_bytes / (step_call_ms * 1e-3) / 1e9
@@ -251,6 +271,7 @@ def main():
                        "paged_attn_decode_append_same_pool_back_to_back": _r5(np.mean(dec_same)),
                        "paged_attn_decode_after_1GiB_flush": _r5(np.median(fl)),
                        "per_sequence_step_without_shared_prefix": _r5(unshared)},
+        "host_us": {"kv_seq_alloc_prefix_plus_free": host_prefix_us},
         "roofline": {
             "kernel": (("paged_attn_decode_shared_prefix: the prefix's partitions once for all sequences "
                         "(grouped kernel), the store kernel, the per-sequence partitions, the reduce; one call")

@@ -169,11 +169,11 @@ def kv_seq_alloc(handle, seq, num_tokens):
 
 def kv_seq_alloc_prefix(handle, seq, token_ids):
     """Returns the number of leading tokens already held by shared blocks."""
-    ids = [int(t) for t in token_ids]
-    arr = (ctypes.c_int32 * max(1, len(ids)))(*ids)
+    import numpy as np
+    ids = np.ascontiguousarray(token_ids, dtype=np.int32)
     cached = ctypes.c_int32()
-    _check(lib().kv_seq_alloc_prefix(handle, int(seq), arr if ids else None, len(ids),
-                                     ctypes.byref(cached)))
+    ptr = ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if ids.size else None
+    _check(lib().kv_seq_alloc_prefix(handle, int(seq), ptr, int(ids.size), ctypes.byref(cached)))
     return cached.value
 
 

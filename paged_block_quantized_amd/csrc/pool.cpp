@@ -43,19 +43,14 @@ struct SeqState {
     int32_t slot = 0;
 };
 
-// Prefix-cache key: the block before (-1 for the first) and the block's ids.
-struct PrefixKey {
-    int32_t parent;
-    std::vector<int32_t> tokens;
-    bool operator==(const PrefixKey& o) const { return parent == o.parent && tokens == o.tokens; }
-};
-struct PrefixKeyHash {
-    size_t operator()(const PrefixKey& k) const {
-        uint64_t h = 1469598103934665603ull ^ (uint32_t)k.parent;   // FNV-1a over the words
-        for (int32_t t : k.tokens) h = (h ^ (uint32_t)t) * 1099511628211ull;
-        return (size_t)h;
-    }
-};
+// Prefix-cache key of a block: the block before it (-1 for the first) and
+// its bs token ids.  The index maps a hash of the key to candidate blocks;
+// a candidate is a hit only if its stored key is equal.
+uint64_t prefix_hash(int32_t parent, const int32_t* ids, int64_t n) {
+    uint64_t h = 1469598103934665603ull ^ (uint32_t)parent;   // FNV-1a over the words
+    for (int64_t i = 0; i < n; ++i) h = (h ^ (uint32_t)ids[i]) * 1099511628211ull;
+    return h;
+}
 
 struct kv_pool {
     kv_pool_desc desc{};
@@ -63,8 +58,42 @@ struct kv_pool {
     std::vector<int32_t> refcount;
     std::unordered_map<int64_t, SeqState> seqs;
     std::set<int32_t> free_slots;
-    std::unordered_map<PrefixKey, int32_t, PrefixKeyHash> prefix_index;
-    std::unordered_map<int32_t, PrefixKey> prefix_key_of;
+    std::unordered_multimap<uint64_t, int32_t> prefix_index;   // key hash -> block
+    std::vector<uint8_t> indexed;     // per block: in the index
+    std::vector<int32_t> key_parent;  // per block: key parent
+    std::vector<int32_t> key_ids;     // per block: bs key ids
+    std::vector<uint64_t> key_hash;   // per block: key hash
+    int32_t n_indexed = 0;
+
+    bool key_equal(int32_t b, int32_t parent, const int32_t* ids) const {
+        const int64_t bs = desc.block_size;
+        return key_parent[b] == parent && std::equal(ids, ids + bs, key_ids.begin() + b * bs);
+    }
+    int32_t find(int32_t parent, const int32_t* ids) const {
+        auto r = prefix_index.equal_range(prefix_hash(parent, ids, desc.block_size));
+        for (auto it = r.first; it != r.second; ++it)
+            if (key_equal(it->second, parent, ids)) return it->second;
+        return -1;
+    }
+    void enter(int32_t b, int32_t parent, const int32_t* ids) {
+        const int64_t bs = desc.block_size;
+        key_parent[b] = parent;
+        std::copy(ids, ids + bs, key_ids.begin() + b * bs);
+        key_hash[b] = prefix_hash(parent, ids, bs);
+        prefix_index.emplace(key_hash[b], b);
+        indexed[b] = 1;
+        ++n_indexed;
+    }
+    void leave(int32_t b) {
+        auto r = prefix_index.equal_range(key_hash[b]);
+        for (auto it = r.first; it != r.second; ++it)
+            if (it->second == b) {
+                prefix_index.erase(it);
+                break;
+            }
+        indexed[b] = 0;
+        --n_indexed;
+    }
 };
 
 namespace {
@@ -110,6 +139,11 @@ kv_status kv_pool_create(const kv_pool_desc* desc, const int32_t* free_order,
     p->desc = *desc;
     p->free_stack = std::move(order);
     p->refcount.assign(n, 0);
+    p->indexed.assign(n, 0);
+    p->key_parent.assign(n, -1);
+    p->key_ids.assign((size_t)n * desc->block_size, 0);
+    p->key_hash.assign(n, 0);
+    p->prefix_index.reserve(n);
     for (int32_t s = 0; s < desc->max_seqs; ++s) p->free_slots.insert(s);
     *out = p;
     return KV_OK;
@@ -150,13 +184,12 @@ kv_status kv_seq_alloc_prefix(kv_pool* pool, int64_t seq, const int32_t* token_i
     const int64_t bs = pool->desc.block_size;
     const int64_t need = blocks_for(num_tokens, bs);
     std::vector<int32_t> hits;
-    PrefixKey key{-1, {}};
+    int32_t parent = -1;
     for (int64_t j = 0; j < num_tokens / bs; ++j) {
-        key.tokens.assign(token_ids + j * bs, token_ids + (j + 1) * bs);
-        auto it = pool->prefix_index.find(key);
-        if (it == pool->prefix_index.end()) break;
-        hits.push_back(it->second);
-        key.parent = it->second;
+        const int32_t b = pool->find(parent, token_ids + j * bs);
+        if (b < 0) break;
+        hits.push_back(b);
+        parent = b;
     }
     if (need - (int64_t)hits.size() > (int64_t)pool->free_stack.size())
         return pbq::fail(KV_ERR_NO_BLOCKS, "not enough free blocks");
@@ -167,12 +200,8 @@ kv_status kv_seq_alloc_prefix(kv_pool* pool, int64_t seq, const int32_t* token_i
         int32_t b = pool->free_stack.back();
         pool->free_stack.pop_back();
         pool->refcount[b] = 1;
-        if ((j + 1) * bs <= num_tokens) {   // a full block enters the index
-            PrefixKey k{j > 0 ? st.table[j - 1] : -1,
-                        std::vector<int32_t>(token_ids + j * bs, token_ids + (j + 1) * bs)};
-            pool->prefix_index.emplace(k, b);
-            pool->prefix_key_of.emplace(b, std::move(k));
-        }
+        if ((j + 1) * bs <= num_tokens)   // a full block enters the index
+            pool->enter(b, j > 0 ? st.table[j - 1] : -1, token_ids + j * bs);
         st.table.push_back(b);
     }
     st.num_tokens = num_tokens;
@@ -254,11 +283,7 @@ kv_status kv_seq_free(kv_pool* pool, int64_t seq) {
         pool->refcount[b] -= 1;
         if (pool->refcount[b] == 0) {
             pool->free_stack.push_back(b);
-            auto k = pool->prefix_key_of.find(b);
-            if (k != pool->prefix_key_of.end()) {
-                pool->prefix_index.erase(k->second);
-                pool->prefix_key_of.erase(k);
-            }
+            if (pool->indexed[b]) pool->leave(b);
         }
     }
     pool->free_slots.insert(it->second.slot);
@@ -319,7 +344,7 @@ kv_status kv_pool_stats(const kv_pool* pool, kv_pool_stats_t* out) {
     out->used = used;
     out->shared = shared;
     out->seqs = (int32_t)pool->seqs.size();
-    out->cached = (int32_t)pool->prefix_index.size();
+    out->cached = pool->n_indexed;
     return KV_OK;
 }
 
