@@ -57,12 +57,56 @@ instead of recomputing; the page gives no matching rule or lifetime):
 * A block leaves the index when its count reaches zero (a freed block's
   codes may be overwritten by its next owner): hits are blocks some live
   sequence holds.
+
+Swap (deepinsea.top "Swap": when GPU memory runs short, KV-cache blocks are
+moved to a CPU swap space sized in GB, at the price of host-device transfer
+time; the page gives no policy):
+* The swap space is a second pool of ``host_blocks`` blocks with the device
+  blocks' layout, plus ``host_slots`` tail slots, with its own free stack
+  (popped from its end, starting 0..H-1) and reference counts.
+* A group of live, resident sequences is swapped out together (forked
+  sequences share blocks; a shared block moves once).  A block moves only
+  if every reference to it comes from the group: only then does moving it
+  free device memory, so blocks also held outside the group stay where they
+  are and the group keeps its references to them.  Moved blocks take host
+  blocks in first-seen order (sequences in the given order, each table in
+  order), keep the group's count on the host side, and go back on the device
+  free stack in that order (leaving the prefix index).  Each sequence then
+  gives up its device slot for the lowest free host slot; the rows of a
+  partial last block are copied with it.
+* Swapping a group in takes a fresh device block for every host block its
+  tables name (first-seen order) with the group's count; host blocks whose
+  count reaches zero go back on the host free stack.  A host block that
+  sequences outside the group still hold stays for them (they get their own
+  device copy when they come back).  Blocks that come back are not
+  re-entered in the prefix index.  Each sequence takes the lowest free
+  device slot.
+* Both calls are all-or-nothing: slots are checked first, then blocks.  A
+  swapped sequence may only be freed or swapped in: fork, append and the
+  decode's batch tables refuse it.
+* Tables of swapped sequences name host block h as -1 - h, and their slot
+  is -1 - (host slot).
+* Each call returns its copy plan: (kind, src, dst, rows) with kinds
+  SWAP_BLOCK_OUT / SWAP_BLOCK_IN (one whole block: codes, scales, zero
+  points) and SWAP_SLOT_OUT / SWAP_SLOT_IN (the first ``rows`` fp16 rows of
+  each head of a tail slot, K and V; only for a partial last block).  Block
+  entries come first, then slot entries, each in the order above.
 """
 
 from dataclasses import dataclass, field
 
 COPY_BLOCK = 0  # copy codes, scales and zero points of one physical block
 COPY_SLOT = 1   # copy one fp16 tail slot
+
+SWAP_BLOCK_OUT = 0  # device block -> host block
+SWAP_BLOCK_IN = 1   # host block -> device block
+SWAP_SLOT_OUT = 2   # device tail slot -> host slot (first `rows` rows)
+SWAP_SLOT_IN = 3    # host slot -> device tail slot
+
+
+def host_id(h):
+    """Table entry (or slot) naming host block (or host slot) h."""
+    return -1 - h
 
 
 class AllocError(Exception):
@@ -94,6 +138,7 @@ class SeqState:
     table: list
     num_tokens: int
     slot: int
+    swapped: bool = False
 
 
 @dataclass
@@ -107,6 +152,10 @@ class BlockPoolModel:
     seqs: dict = field(init=False)
     index: dict = field(init=False)     # (parent block or -1, token ids) -> block
     key_of: dict = field(init=False)    # block -> its index key
+    host_blocks: int = field(init=False, default=0)
+    host_slots: int = field(init=False, default=0)
+    host_free: list = field(init=False)
+    host_refcount: list = field(init=False)
 
     def __post_init__(self):
         if self.num_blocks <= 0 or self.block_size <= 0 or self.max_seqs <= 0:
@@ -120,14 +169,43 @@ class BlockPoolModel:
         self.seqs = {}
         self.index = {}
         self.key_of = {}
+        self.host_free = []
+        self.host_refcount = []
 
     # -- helpers ---------------------------------------------------------
     def _lowest_free_slot(self):
-        used = {s.slot for s in self.seqs.values()}
+        used = {s.slot for s in self.seqs.values() if not s.swapped}
         for k in range(self.max_seqs):
             if k not in used:
                 return k
         raise NoSlots("no free tail slot")
+
+    def _free_host_slots(self):
+        used = {host_id(s.slot) for s in self.seqs.values() if s.swapped}
+        return [k for k in range(self.host_slots) if k not in used]
+
+    def _resident(self, seq):
+        if self.seqs[seq].swapped:
+            raise BadState("sequence is swapped out")
+        return self.seqs[seq]
+
+    def _group(self, seqs):
+        seqs = [int(s) for s in seqs]
+        if len(set(seqs)) != len(seqs):
+            raise BadArg("a sequence is named twice")
+        for s in seqs:
+            if s not in self.seqs:
+                raise UnknownSeq("unknown sequence")
+        return seqs
+
+    def _release_block(self, b, n=1):
+        """Drop n references to device block b; at zero it goes back on the
+        free stack and leaves the prefix index."""
+        self.refcount[b] -= n
+        if self.refcount[b] == 0:
+            self.free.append(b)
+            if b in self.key_of:
+                del self.index[self.key_of.pop(b)]
 
     def _blocks_for(self, n):
         return (n + self.block_size - 1) // self.block_size
@@ -189,8 +267,8 @@ class BlockPoolModel:
             raise UnknownSeq("unknown parent")
         if child in self.seqs:
             raise BadState("child already present")
+        p = self._resident(parent)
         slot = self._lowest_free_slot()
-        p = self.seqs[parent]
         for b in p.table:
             self.refcount[b] += 1
         self.seqs[child] = SeqState(list(p.table), p.num_tokens, slot)
@@ -204,7 +282,7 @@ class BlockPoolModel:
             raise BadArg("n < 0")
         if seq not in self.seqs:
             raise UnknownSeq("unknown sequence")
-        st = self.seqs[seq]
+        st = self._resident(seq)
         bs = self.block_size
         cow = (n > 0 and st.num_tokens % bs != 0
                and self.refcount[st.table[-1]] > 1)
@@ -233,11 +311,99 @@ class BlockPoolModel:
             raise UnknownSeq("unknown sequence")
         st = self.seqs.pop(seq)
         for b in st.table:
-            self.refcount[b] -= 1
-            if self.refcount[b] == 0:
-                self.free.append(b)
-                if b in self.key_of:
-                    del self.index[self.key_of.pop(b)]
+            if b >= 0:
+                self._release_block(b)
+            else:
+                h = host_id(b)
+                self.host_refcount[h] -= 1
+                if self.host_refcount[h] == 0:
+                    self.host_free.append(h)
+
+    # -- swap ------------------------------------------------------------
+    def set_swap_space(self, host_blocks: int, host_slots: int):
+        if host_blocks < 0 or host_slots < 0:
+            raise BadArg("swap space sizes must be >= 0")
+        if any(s.swapped for s in self.seqs.values()):
+            raise BadState("sequences are swapped out")
+        self.host_blocks, self.host_slots = host_blocks, host_slots
+        self.host_free = list(range(host_blocks))
+        self.host_refcount = [0] * host_blocks
+
+    def swap_out(self, seqs):
+        """Move the blocks only this group holds, and the group's tail slots,
+        to the swap space; returns the copy plan."""
+        seqs = self._group(seqs)
+        for s in seqs:
+            self._resident(s)
+        count, order = {}, []
+        for s in seqs:
+            for b in self.seqs[s].table:
+                if b not in count:
+                    order.append(b)
+                count[b] = count.get(b, 0) + 1
+        moving = [b for b in order if count[b] == self.refcount[b]]
+        if len(self._free_host_slots()) < len(seqs):
+            raise NoSlots("no free host slot")
+        if len(moving) > len(self.host_free):
+            raise NoBlocks("not enough free host blocks")
+        plan, where = [], {}
+        for b in moving:
+            h = self.host_free.pop()
+            self.host_refcount[h] = count[b]
+            self._release_block(b, count[b])
+            where[b] = h
+            plan.append((SWAP_BLOCK_OUT, b, h, 0))
+        for s in seqs:
+            st = self.seqs[s]
+            hs = self._free_host_slots()[0]
+            rows = st.num_tokens % self.block_size
+            if rows:
+                plan.append((SWAP_SLOT_OUT, st.slot, hs, rows))
+            st.table = [host_id(where[b]) if b in where else b for b in st.table]
+            st.slot = host_id(hs)
+            st.swapped = True
+        return plan
+
+    def swap_in(self, seqs):
+        """Bring a swapped group back into fresh device blocks and slots;
+        returns the copy plan."""
+        seqs = self._group(seqs)
+        for s in seqs:
+            if not self.seqs[s].swapped:
+                raise BadState("sequence is not swapped out")
+        count, order = {}, []
+        for s in seqs:
+            for b in self.seqs[s].table:
+                if b < 0:
+                    if b not in count:
+                        order.append(b)
+                    count[b] = count.get(b, 0) + 1
+        used = {s.slot for s in self.seqs.values() if not s.swapped}
+        if self.max_seqs - len(used) < len(seqs):
+            raise NoSlots("no free tail slot")
+        if len(order) > len(self.free):
+            raise NoBlocks("not enough free blocks")
+        plan, where = [], {}
+        for e in order:
+            h = host_id(e)
+            d = self.free.pop()
+            self.refcount[d] = count[e]
+            self.host_refcount[h] -= count[e]
+            if self.host_refcount[h] == 0:
+                self.host_free.append(h)
+            where[e] = d
+            plan.append((SWAP_BLOCK_IN, h, d, 0))
+        for s in seqs:
+            st = self.seqs[s]
+            hs = host_id(st.slot)
+            slot = self._lowest_free_slot()
+            st.swapped = False
+            rows = st.num_tokens % self.block_size
+            if rows:
+                plan.append((SWAP_SLOT_IN, hs, slot, rows))
+            st.table = [where[b] if b < 0 else b for b in st.table]
+            st.slot = slot
+        return plan
 
     def table(self, seq: int):
         if seq not in self.seqs:
@@ -249,26 +415,41 @@ class BlockPoolModel:
         used = sum(1 for r in self.refcount if r > 0)
         shared = sum(1 for r in self.refcount if r > 1)
         return dict(total=self.num_blocks, free=len(self.free), used=used,
-                    shared=shared, seqs=len(self.seqs), cached=len(self.index))
+                    shared=shared, seqs=len(self.seqs), cached=len(self.index),
+                    host_total=self.host_blocks, host_free=len(self.host_free),
+                    swapped=sum(1 for s in self.seqs.values() if s.swapped))
 
     def check_invariants(self):
         """Each block is either on the free stack or referenced; counts equal
         the number of table references; the stack has no duplicates; every
         table has ceil(tokens / bs) entries; slots are distinct."""
         refs = [0] * self.num_blocks
+        host_refs = [0] * self.host_blocks
         for st in self.seqs.values():
             assert len(st.table) == self._blocks_for(st.num_tokens)
             for b in st.table:
-                refs[b] += 1
+                assert b >= 0 or st.swapped
+                if b >= 0:
+                    refs[b] += 1
+                else:
+                    host_refs[host_id(b)] += 1
         assert refs == self.refcount
+        assert host_refs == self.host_refcount
+        assert len(set(self.host_free)) == len(self.host_free)
+        hfree = set(self.host_free)
+        for h in range(self.host_blocks):
+            assert (h in hfree) != (self.host_refcount[h] > 0)
         assert len(set(self.free)) == len(self.free)
         free = set(self.free)
         for b in range(self.num_blocks):
             assert (b in free) != (self.refcount[b] > 0)
         assert len(self.free) + sum(1 for r in refs if r > 0) == self.num_blocks
-        slots = [st.slot for st in self.seqs.values()]
+        slots = [st.slot for st in self.seqs.values() if not st.swapped]
         assert len(set(slots)) == len(slots)
         assert all(0 <= s < self.max_seqs for s in slots)
+        hslots = [host_id(st.slot) for st in self.seqs.values() if st.swapped]
+        assert len(set(hslots)) == len(hslots)
+        assert all(0 <= s < self.host_slots for s in hslots)
         # indexed blocks are held, their parents too, and the maps agree
         assert len(self.index) == len(self.key_of)
         for key, b in self.index.items():

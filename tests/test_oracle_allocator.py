@@ -12,7 +12,7 @@ from hypothesis import given, settings, strategies as hst
 from oracle import allocator as A
 from oracle import kv_size
 
-from alloc_harness import GOLDEN, apply_op, random_ops, run_golden_trace
+from alloc_harness import GOLDEN, ContentSim, apply_op, random_ops, run_golden_trace
 
 
 class ModelAdapter:
@@ -33,6 +33,12 @@ class ModelAdapter:
 
     def release(self, s):
         return self.m.release(s)
+
+    def swap_out(self, seqs):
+        return self.m.swap_out(seqs)
+
+    def swap_in(self, seqs):
+        return self.m.swap_in(seqs)
 
     def table(self, s):
         return self.m.table(s)
@@ -210,3 +216,96 @@ def test_prefix_cache_hits_are_equal_prefixes(seed, n_blocks, bs):
             for j, blk in enumerate(table[:len(ids) // bs]):
                 if blk in m.key_of:
                     assert spelled(blk) == ids[:(j + 1) * bs]
+
+
+def test_swap_hand_worked():
+    """deepinsea "Swap", as read: a group moves the blocks only it holds (a
+    block shared with a sequence outside the group stays on the device), its
+    slots move with the rows of a partial last block; swap-in takes fresh
+    device blocks and the lowest free slot; both are all-or-nothing."""
+    O, I, SO, SI = A.SWAP_BLOCK_OUT, A.SWAP_BLOCK_IN, A.SWAP_SLOT_OUT, A.SWAP_SLOT_IN
+    m = A.BlockPoolModel(8, 4, 3)             # free stack 0..7, popped from 7
+    m.set_swap_space(4, 2)                    # host stack 0..3, popped from 3
+    assert m.alloc(1, 10) == [7, 6, 5]        # two rows in the partial block
+    assert m.fork(1, 2) == [(A.COPY_SLOT, 0, 1)]
+    assert m.append(2, 1) == [(A.COPY_BLOCK, 5, 4)]
+    assert m.alloc(3, 4) == [3]
+    # 7 and 6 are also held by sequence 2: only 5 moves
+    assert m.swap_out([1]) == [(O, 5, 3, 0), (SO, 0, 0, 2)]
+    assert m.table(1) == ([7, 6, -4], 10, -1)
+    assert m.free == [0, 1, 2, 5]
+    assert {k: m.stats()[k] for k in ("free", "host_free", "swapped")} == \
+        dict(free=4, host_free=3, swapped=1)
+    with pytest.raises(A.BadState):
+        m.append(1, 1)
+    with pytest.raises(A.BadState):
+        m.fork(1, 9)
+    with pytest.raises(A.BadState):
+        m.swap_out([1])
+    assert m.alloc(4, 8) == [5, 2]            # slot 0, freed by the swap
+    with pytest.raises(A.NoSlots):            # slots 0, 1, 2 all held
+        m.swap_in([1])
+    m.release(3)
+    assert m.swap_in([1]) == [(I, 3, 3, 0), (SI, 0, 2, 2)]
+    assert m.table(1) == ([7, 6, 3], 10, 2)
+    # both forks together: every block is the group's own, shared ones once
+    assert m.swap_out([1, 2]) == [(O, 7, 3, 0), (O, 6, 2, 0), (O, 3, 1, 0), (O, 4, 0, 0),
+                                  (SO, 2, 0, 2), (SO, 1, 1, 3)]
+    assert m.table(1) == ([-4, -3, -2], 10, -1)
+    assert m.table(2) == ([-4, -3, -1], 11, -2)
+    assert m.free == [0, 1, 7, 6, 3, 4]
+    # one of them back: the host blocks it shares stay for the other
+    assert m.swap_in([2]) == [(I, 3, 4, 0), (I, 2, 3, 0), (I, 0, 6, 0), (SI, 1, 1, 3)]
+    assert m.table(2) == ([4, 3, 6], 11, 1)
+    assert m.host_free == [0] and m.host_refcount == [0, 1, 1, 1]
+    m.release(1)
+    assert m.host_free == [0, 3, 2, 1]
+    st = m.stats()
+    assert (st["free"], st["used"], st["host_free"], st["swapped"], st["seqs"]) == (3, 5, 4, 0, 2)
+    m.check_invariants()
+
+
+def test_swap_failure_leaves_state_unchanged():
+    m = A.BlockPoolModel(6, 2, 3)
+    m.set_swap_space(2, 1)
+    m.alloc(0, 6)
+    m.alloc(1, 1)
+
+    def snap():
+        return (list(m.free), list(m.refcount), list(m.host_free), list(m.host_refcount),
+                {k: (list(v.table), v.num_tokens, v.slot, v.swapped) for k, v in m.seqs.items()})
+
+    before = snap()
+    with pytest.raises(A.NoBlocks):           # three blocks, two host blocks
+        m.swap_out([0])
+    with pytest.raises(A.NoSlots):            # two sequences, one host slot
+        m.swap_out([1, 0])
+    with pytest.raises(A.BadArg):
+        m.swap_out([1, 1])
+    with pytest.raises(A.UnknownSeq):
+        m.swap_out([1, 5])
+    with pytest.raises(A.BadState):
+        m.swap_in([1])
+    assert snap() == before
+    m.swap_out([1])
+    with pytest.raises(A.BadState):           # resize while a sequence is out
+        m.set_swap_space(4, 4)
+    m.check_invariants()
+
+
+@settings(max_examples=80, deadline=None)
+@given(seed=hst.integers(0, 2 ** 31 - 1), n_blocks=hst.integers(1, 24),
+       bs=hst.sampled_from([1, 2, 4, 8]), host_blocks=hst.integers(0, 16))
+def test_tables_and_plans_keep_every_sequence_data(seed, n_blocks, bs, host_blocks):
+    """Brute force over random op sequences (prefix-cached allocations and
+    swaps included): running each op's copies and swap plans on stamped
+    blocks leaves every sequence's data where its table and slot point, and
+    a prefix hit always finds the block holding that very token prefix."""
+    rng = np.random.default_rng(seed)
+    m = A.BlockPoolModel(n_blocks, bs, 6, rng.permutation(n_blocks))
+    m.set_swap_space(host_blocks, 3)
+    sim = ContentSim(bs)
+    for op in random_ops(rng, 160, max_seq_id=6, prefix=True, swap=True):
+        rec = apply_op(m, op, A.AllocError)
+        sim.apply(m, op, rec)
+        m.check_invariants()
