@@ -88,6 +88,80 @@ def cpu_baseline(setup, seconds):
     }
 
 
+def swap_plan_bytes(pool, plan):
+    """Bytes a swap plan moves: whole blocks (codes, scales, zero points) and
+    the held rows of each head of the tail slots (K and V, fp16)."""
+    H, bs, D = pool.num_kv_heads, pool.block_size, pool.head_dim
+    kb = H * bs * D
+    block = kb + (kb // 2 if pool.v_int4 else kb) + 4 * H + (H if pool.v_int4 else 0)
+    total = 0
+    for kind, _, _, rows in plan:
+        total += block if kind < 2 else 4 * H * rows * D
+    return total
+
+
+def measure_swap(setup, reps):
+    """A quarter of the batch swapped out to pinned host memory and back in,
+    reps times: the swap kernel's rate per direction (HIP events around
+    kv_swap_blocks on its stream), the host allocator's time per call, and
+    the DMA engines' rate for one contiguous copy of the same size (torch
+    copy_ between device and pinned host memory) as the link's practical
+    peak.  Leaves the pool's tables changed: run it last."""
+    import numpy as np
+    import torch
+
+    from paged_block_quantized_amd import _lib as L
+    pool, w = setup.pool, setup.w
+    group = list(range(0, w.num_seqs, 4))
+    n_blocks = sum(len(pool.table(s)[0]) for s in group)
+    pool.set_swap_space(n_blocks, len(group))
+    stream = torch.cuda.current_stream()
+    plan = torch.zeros((L.swap_plan_cap(pool.handle, group), 4), dtype=torch.int32, pin_memory=True)
+    ms = {"out": [], "in": []}
+    host_us = {"out": [], "in": []}
+    nbytes = {}
+    for i in range(reps + 1):
+        for d, fn in (("out", L.kv_seq_swap_out), ("in", L.kv_seq_swap_in)):
+            t0 = time.perf_counter()
+            n = fn(pool.handle, group, plan)
+            t1 = time.perf_counter()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            L.kv_swap_blocks(pool.desc, pool.mem, pool.host_desc, pool.host_mem, plan, n, stream)
+            b.record(stream)
+            torch.cuda.synchronize()          # the plan buffer is reused
+            nbytes[d] = swap_plan_bytes(pool, plan[:n].tolist())
+            if i:
+                ms[d].append(a.elapsed_time(b))
+                host_us[d].append((t1 - t0) * 1e6)
+    size = nbytes["out"]
+    dev = torch.empty(size, dtype=torch.uint8, device="cuda")
+    host = torch.empty(size, dtype=torch.uint8, pin_memory=True)
+    dma = {"d2h": [], "h2d": []}
+    for i in range(reps + 1):
+        for d, (dst, src) in (("d2h", (host, dev)), ("h2d", (dev, host))):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            dst.copy_(src, non_blocking=True)
+            b.record(stream)
+            torch.cuda.synchronize()
+            if i:
+                dma[d].append(a.elapsed_time(b))
+    gbs = {d: nbytes[d] / (float(np.median(ms[d])) * 1e-3) / 1e9 for d in ms}
+    dgbs = {d: size / (float(np.median(dma[d])) * 1e-3) / 1e9 for d in dma}
+    return {
+        "kernel": "kv_swap_blocks (one launch per plan; the device reads or writes pinned host memory)",
+        "sequences": len(group), "blocks": n_blocks, "bytes_per_direction": size,
+        "out_ms": round(float(np.median(ms["out"])), 4), "in_ms": round(float(np.median(ms["in"])), 4),
+        "out_gbs": round(gbs["out"], 2), "in_gbs": round(gbs["in"], 2),
+        "dma_d2h_gbs": round(dgbs["d2h"], 2), "dma_h2d_gbs": round(dgbs["h2d"], 2),
+        "out_frac_of_dma": round(gbs["out"] / dgbs["d2h"], 4),
+        "in_frac_of_dma": round(gbs["in"] / dgbs["h2d"], 4),
+        "host_us_kv_seq_swap_out": round(float(np.median(host_us["out"])), 1),
+        "host_us_kv_seq_swap_in": round(float(np.median(host_us["in"])), 1),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +364,10 @@ def main():
     if not args.no_cpu_baseline:
         print("cpu baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(setup, args.cpu_seconds)
+    if not args.only_timed:
+        # context, not the step: swapping a quarter of the batch to host memory
+        print("swap", file=sys.stderr, flush=True)
+        line["swap"] = measure_swap(setup, 5)
     print(json.dumps(line), flush=True)
 
 

@@ -122,13 +122,32 @@ typedef struct kv_copy {
     int32_t dst;
 } kv_copy;
 
+/* One entry of a swap plan (kv_seq_swap_out / kv_seq_swap_in write them,
+ * kv_swap_blocks performs them):
+ *   KV_SWAP_BLOCK_OUT: device block src -> host block dst (codes, scales,
+ *                      zero points; rows 0)
+ *   KV_SWAP_BLOCK_IN : host block src -> device block dst (rows 0)
+ *   KV_SWAP_SLOT_OUT : the first `rows` fp16 rows of every head of device
+ *                      tail slot src -> host slot dst (K and V)
+ *   KV_SWAP_SLOT_IN  : the same from host slot src to device tail slot dst */
+enum { KV_SWAP_BLOCK_OUT = 0, KV_SWAP_BLOCK_IN = 1, KV_SWAP_SLOT_OUT = 2, KV_SWAP_SLOT_IN = 3 };
+typedef struct kv_swap {
+    int32_t kind;
+    int32_t src;
+    int32_t dst;
+    int32_t rows;
+} kv_swap;
+
 typedef struct kv_pool_stats_t {
-    int32_t total;  /* N */
-    int32_t free;   /* blocks on the free stack */
-    int32_t used;   /* blocks with refcount > 0 */
-    int32_t shared; /* blocks with refcount > 1 */
-    int32_t seqs;   /* live sequences */
-    int32_t cached; /* full blocks in the prefix-cache index */
+    int32_t total;      /* N */
+    int32_t free;       /* blocks on the free stack */
+    int32_t used;       /* blocks with refcount > 0 */
+    int32_t shared;     /* blocks with refcount > 1 */
+    int32_t seqs;       /* live sequences (resident and swapped) */
+    int32_t cached;     /* full blocks in the prefix-cache index */
+    int32_t host_total; /* blocks of the swap space */
+    int32_t host_free;  /* swap-space blocks on its free stack */
+    int32_t swapped;    /* sequences swapped out */
 } kv_pool_stats_t;
 
 typedef struct kv_pool kv_pool; /* opaque host state */
@@ -209,6 +228,47 @@ kv_status kv_pool_stats(const kv_pool* pool, kv_pool_stats_t* out);
 kv_status kv_pool_free_list(const kv_pool* pool, int32_t* out, int32_t cap,
                             int32_t* n);
 
+/* ---- swap space ([deepinsea] "Swap": KV blocks move to CPU memory when the
+ * GPU's runs short; the swap space is sized in GB) ---------------------------
+ * The swap space is a host-memory copy of the pool's layout: host_blocks
+ * blocks and host_slots tail slots, with arrays sized by kv_pool_bytes for a
+ * desc whose num_blocks = host_blocks and max_seqs = host_slots (the caller
+ * allocates them as pinned memory, hipHostMalloc).  Its blocks have their own
+ * free stack, popped from its end and starting as 0..host_blocks-1.  Sizing
+ * resets it; KV_ERR_STATE while any sequence is swapped out. */
+kv_status kv_pool_set_swap_space(kv_pool* pool, int32_t host_blocks, int32_t host_slots);
+
+/* Swap a group of resident sequences out (forks share blocks: swap them
+ * together so that their shared blocks move, once).  Blocks every reference
+ * to which comes from the group move to host blocks (first-seen order over
+ * the group's tables, in the order given) and return to the device free
+ * stack (leaving the prefix index); blocks also held outside the group stay
+ * on the device (moving them would free nothing) and the group keeps them.
+ * Each sequence trades its device tail slot for the lowest free host slot.
+ * plan (host, cap entries) receives the copies, block entries first, and
+ * *n_plan their number; at most (distinct blocks + n) entries.  The copies
+ * must run (kv_swap_blocks, for every layer's pool) before anything writes
+ * the freed blocks or slots.  While swapped, kv_seq_table names host block h
+ * as -1 - h and the slot as -1 - host slot; fork, append and
+ * kv_batch_tables refuse the sequence (KV_ERR_STATE); kv_seq_free releases
+ * it.  All-or-nothing: KV_ERR_INVALID (a repeated sequence, cap too small),
+ * KV_ERR_UNKNOWN_SEQ, KV_ERR_STATE (already swapped), KV_ERR_NO_SLOTS (host
+ * slots), then KV_ERR_NO_BLOCKS (host blocks). */
+kv_status kv_seq_swap_out(kv_pool* pool, const int64_t* seqs, int32_t n, kv_swap* plan,
+                          int32_t cap, int32_t* n_plan);
+
+/* Bring a group of swapped sequences back: every host block the group's
+ * tables name takes a fresh device block from the free stack (first-seen
+ * order) with the group's count of references; a host block whose count
+ * reaches zero returns to the host free stack (one still held by a
+ * sequence outside the group stays for it).  Returned blocks are not
+ * re-entered in the prefix index.  Each sequence takes the lowest free
+ * device slot.  Plan and errors as kv_seq_swap_out (KV_ERR_STATE if a
+ * sequence is not swapped out; KV_ERR_NO_SLOTS / KV_ERR_NO_BLOCKS for the
+ * device side).  The copies must run before the sequences are read. */
+kv_status kv_seq_swap_in(kv_pool* pool, const int64_t* seqs, int32_t n, kv_swap* plan,
+                         int32_t cap, int32_t* n_plan);
+
 /* ---- device calls -------------------------------------------------------- */
 
 /* Perform n copies (copies_dev: device array of kv_copy) on stream.  Block
@@ -216,6 +276,21 @@ kv_status kv_pool_free_list(const kv_pool* pool, int32_t* out, int32_t cap,
  * Destinations must be distinct and not also sources in the same call. */
 kv_status kv_copy_blocks(const kv_pool_desc* desc, const kv_pool_mem* mem,
                          const kv_copy* copies_dev, int32_t n, void* stream);
+
+/* Perform a swap plan between one layer's device pool (desc, mem) and its
+ * swap space (host_desc: the same block_size, num_kv_heads, head_dim and
+ * codecs, num_blocks = host blocks, max_seqs = host slots; host_mem: its
+ * arrays in pinned host memory, hipHostMalloc).  plan: n entries in pinned
+ * host memory; the library checks them on the host (kinds, ranges, rows <=
+ * block_size, no destination written twice or also read in the call) and a
+ * kernel reads them directly, so the plan must stay unchanged until the
+ * stream has run the copy.  One launch moves every entry: the device reads
+ * or writes the host arrays over the host link, no staging buffer.  Tail
+ * arrays are needed only for slot entries.  KV_ERR_INVALID for a bad entry,
+ * geometry or alignment, or host memory that is not pinned. */
+kv_status kv_swap_blocks(const kv_pool_desc* desc, const kv_pool_mem* mem,
+                         const kv_pool_desc* host_desc, const kv_pool_mem* host_mem,
+                         const kv_swap* plan, int32_t n, void* stream);
 
 /* Quantize and store new K/V tokens ([tbr8] §4 store_kv, per (block, head)
  * as the scale tensor's shape gives; [yunthe] Q(x)).

@@ -21,6 +21,7 @@ STATUS_NAMES = {KV_OK: "ok", KV_ERR_INVALID: "invalid", KV_ERR_NO_BLOCKS: "no_bl
                 KV_ERR_NO_SLOTS: "no_slots", KV_ERR_HIP: "hip"}
 KV_CODEC_I8_SYM, KV_CODEC_I4_ASYM = 0, 1
 KV_COPY_BLOCK, KV_COPY_SLOT = 0, 1
+KV_SWAP_BLOCK_OUT, KV_SWAP_BLOCK_IN, KV_SWAP_SLOT_OUT, KV_SWAP_SLOT_IN = range(4)
 
 
 class PBQError(RuntimeError):
@@ -51,14 +52,21 @@ class kv_copy(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("src", ctypes.c_int32), ("dst", ctypes.c_int32)]
 
 
+class kv_swap(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("src", ctypes.c_int32), ("dst", ctypes.c_int32),
+                ("rows", ctypes.c_int32)]
+
+
 class kv_pool_stats_t(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("total", "free", "used", "shared", "seqs", "cached")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("total", "free", "used", "shared", "seqs", "cached",
+                                              "host_total", "host_free", "swapped")]
 
 
 EXPORTS = [
     "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "kv_seq_alloc", "kv_seq_alloc_prefix",
     "kv_seq_fork", "kv_seq_append", "kv_seq_free", "kv_seq_table",
-    "kv_batch_tables", "kv_pool_stats", "kv_pool_free_list", "kv_copy_blocks",
+    "kv_batch_tables", "kv_pool_stats", "kv_pool_free_list", "kv_pool_set_swap_space",
+    "kv_seq_swap_out", "kv_seq_swap_in", "kv_swap_blocks", "kv_copy_blocks",
     "kv_quantize_store", "paged_attn_workspace_bytes", "paged_attn_decode",
     "paged_attn_decode_append", "paged_attn_decode_shared_prefix",
     "paged_attn_default_partition", "kv_last_error",
@@ -91,6 +99,11 @@ def lib():
             "kv_batch_tables": (st, [VP, P(I64), I32, P(I32), I32, P(I32), P(I32)]),
             "kv_pool_stats": (st, [VP, P(kv_pool_stats_t)]),
             "kv_pool_free_list": (st, [VP, P(I32), I32, P(I32)]),
+            "kv_pool_set_swap_space": (st, [VP, I32, I32]),
+            "kv_seq_swap_out": (st, [VP, P(I64), I32, P(kv_swap), I32, P(I32)]),
+            "kv_seq_swap_in": (st, [VP, P(I64), I32, P(kv_swap), I32, P(I32)]),
+            "kv_swap_blocks": (st, [P(kv_pool_desc), P(kv_pool_mem), P(kv_pool_desc),
+                                    P(kv_pool_mem), VP, I32, VP]),
             "kv_copy_blocks": (st, [P(kv_pool_desc), P(kv_pool_mem), VP, I32, VP]),
             "kv_quantize_store": (st, [P(kv_pool_desc), P(kv_pool_mem), VP, VP, I32, VP, VP,
                                        VP, I32, VP, I32, VP]),
@@ -233,6 +246,53 @@ def kv_pool_free_list(handle):
     out = (ctypes.c_int32 * max(1, n.value))()
     _check(lib().kv_pool_free_list(handle, out, n.value, None))
     return list(out)[:n.value]
+
+
+def kv_pool_set_swap_space(handle, host_blocks, host_slots):
+    _check(lib().kv_pool_set_swap_space(handle, int(host_blocks), int(host_slots)))
+
+
+def swap_plan_cap(handle, seqs):
+    """Plan entries a swap of these sequences can need: their table lengths
+    plus one slot entry each (unknown sequences count 0; the call reports them)."""
+    cap = len(seqs)
+    for s in seqs:
+        try:
+            cap += len(kv_seq_table(handle, s)[0])
+        except PBQError:
+            pass
+    return cap
+
+
+def _swap(fn, handle, seqs, plan):
+    n = len(seqs)
+    sq = (ctypes.c_int64 * max(1, n))(*[int(s) for s in seqs])
+    cnt = ctypes.c_int32()
+    if plan is None:
+        cap = swap_plan_cap(handle, seqs)
+        buf = (kv_swap * max(1, cap))()
+        _check(fn(handle, sq, n, buf, cap, ctypes.byref(cnt)))
+        return [(buf[i].kind, buf[i].src, buf[i].dst, buf[i].rows) for i in range(cnt.value)]
+    assert plan.dtype == torch.int32 and plan.dim() == 2 and plan.shape[1] == 4 and plan.is_contiguous()
+    _check(fn(handle, sq, n, ctypes.cast(plan.data_ptr(), ctypes.POINTER(kv_swap)), plan.shape[0],
+              ctypes.byref(cnt)))
+    return cnt.value
+
+
+def kv_seq_swap_out(handle, seqs, plan=None):
+    """Without ``plan``: returns the plan as (kind, src, dst, rows) tuples.
+    With ``plan`` (int32 [cap, 4] CPU tensor, e.g. pinned): writes it there
+    and returns the number of entries."""
+    return _swap(lib().kv_seq_swap_out, handle, seqs, plan)
+
+
+def kv_seq_swap_in(handle, seqs, plan=None):
+    return _swap(lib().kv_seq_swap_in, handle, seqs, plan)
+
+
+def kv_swap_blocks(desc, mem, host_desc, host_mem, plan, n, stream=None):
+    _check(lib().kv_swap_blocks(ctypes.byref(desc), ctypes.byref(mem), ctypes.byref(host_desc),
+                                ctypes.byref(host_mem), _ptr(plan), int(n), _stream(stream)))
 
 
 def kv_copy_blocks(desc, mem, copies_dev, n, stream=None):

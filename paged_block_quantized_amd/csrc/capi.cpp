@@ -8,6 +8,8 @@
 #include <atomic>
 #include <cmath>
 #include <string>
+#include <vector>
+#include <algorithm>
 
 #include "pbq_internal.h"
 
@@ -52,6 +54,65 @@ kv_status hip_status(hipError_t e, const char* what) {
 }
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+// Device address of pinned host memory [p, p + bytes): KV_ERR_INVALID unless
+// HIP knows both ends as host memory mapped contiguously for the device.
+kv_status pinned_device_ptr(const void* p, size_t bytes, const char* what, char** dev) {
+    hipPointerAttribute_t at{}, end{};
+    if (!p || hipPointerGetAttributes(&at, p) != hipSuccess || at.type != hipMemoryTypeHost ||
+        !at.devicePointer ||
+        hipPointerGetAttributes(&end, (const char*)p + bytes - 1) != hipSuccess ||
+        end.type != hipMemoryTypeHost ||
+        (const char*)end.devicePointer != (const char*)at.devicePointer + bytes - 1) {
+        (void)hipGetLastError();
+        return fail(KV_ERR_INVALID, std::string(what) + " must be pinned host memory (hipHostMalloc)");
+    }
+    *dev = (char*)at.devicePointer;
+    return KV_OK;
+}
+
+// Checks a swap plan on the host: kinds, index ranges, rows, and that no
+// destination is written twice or also read within the call (the entries
+// run concurrently).  Returns the largest entry's byte count in *max_bytes.
+kv_status check_swap_plan(const kv_pool_desc* d, const kv_pool_desc* h, const kv_swap* plan,
+                          int32_t n, bool* has_slots, int64_t* max_bytes) {
+    const int64_t tile = (int64_t)d->block_size * d->head_dim;
+    const int64_t kb = tile * d->num_kv_heads;
+    const int64_t block_bytes = kb + (d->v_codec == KV_CODEC_I4_ASYM ? kb / 2 : kb);
+    // spaces: device blocks, host blocks, device slots, host slots
+    const int32_t size[4] = {d->num_blocks, h->num_blocks, d->max_seqs, h->max_seqs};
+    std::vector<uint8_t> mark[4];
+    for (int i = 0; i < 4; ++i) mark[i].assign(size[i], 0);
+    *has_slots = false;
+    *max_bytes = 0;
+    for (int pass = 0; pass < 2; ++pass)
+        for (int32_t i = 0; i < n; ++i) {
+            const kv_swap& c = plan[i];
+            int from, to;
+            switch (c.kind) {
+                case KV_SWAP_BLOCK_OUT: from = 0, to = 1; break;
+                case KV_SWAP_BLOCK_IN: from = 1, to = 0; break;
+                case KV_SWAP_SLOT_OUT: from = 2, to = 3; break;
+                case KV_SWAP_SLOT_IN: from = 3, to = 2; break;
+                default: return fail(KV_ERR_INVALID, "swap plan: unknown kind");
+            }
+            if (c.src < 0 || c.src >= size[from] || c.dst < 0 || c.dst >= size[to])
+                return fail(KV_ERR_INVALID, "swap plan: index out of range");
+            const bool slot = from >= 2;
+            if (slot ? (c.rows < 1 || c.rows > d->block_size) : c.rows != 0)
+                return fail(KV_ERR_INVALID, "swap plan: rows must be 1..block_size for slots, 0 for blocks");
+            if (pass == 0) {
+                mark[from][c.src] |= 1;
+                *has_slots |= slot;
+                *max_bytes = std::max(*max_bytes, slot ? 4 * tile / d->block_size * c.rows * d->num_kv_heads
+                                                       : block_bytes);
+            } else {
+                if (mark[to][c.dst]) return fail(KV_ERR_INVALID, "swap plan: a destination is written twice or also read");
+                mark[to][c.dst] = 2;
+            }
+        }
+    return KV_OK;
+}
 
 // Compute units of the current device, cached per device; 256 (MI355X) when
 // no device can be queried.
@@ -255,6 +316,61 @@ kv_status kv_copy_blocks(const kv_pool_desc* d, const kv_pool_mem* m,
     a.copies = copies_dev;
     a.n = n;
     return pbq::hip_status(pbq::launch_copy_blocks(a, (hipStream_t)stream), "kv_copy_blocks launch");
+}
+
+kv_status kv_swap_blocks(const kv_pool_desc* d, const kv_pool_mem* m, const kv_pool_desc* hd,
+                         const kv_pool_mem* hm, const kv_swap* plan, int32_t n, void* stream) {
+    kv_status st = pbq::check_device_desc(d);
+    if (st != KV_OK) return st;
+    if ((st = pbq::check_device_desc(hd)) != KV_OK) return st;
+    if (hd->block_size != d->block_size || hd->num_kv_heads != d->num_kv_heads ||
+        hd->head_dim != d->head_dim || hd->k_codec != d->k_codec || hd->v_codec != d->v_codec)
+        return fail(KV_ERR_INVALID, "host_desc must have the pool's block_size, heads, head_dim and codecs");
+    if (n < 0) return fail(KV_ERR_INVALID, "n < 0");
+    if (n == 0) return KV_OK;
+    if (!plan) return fail(KV_ERR_INVALID, "plan is NULL");
+    bool has_slots = false;
+    int64_t max_bytes = 0;
+    if ((st = pbq::check_swap_plan(d, hd, plan, n, &has_slots, &max_bytes)) != KV_OK) return st;
+    if ((st = pbq::check_mem(d, m, has_slots)) != KV_OK) return st;
+    if ((st = pbq::check_mem(hd, hm, has_slots)) != KV_OK) return st;
+    const int64_t chunks = (max_bytes + pbq::kSwapChunk - 1) / pbq::kSwapChunk;
+    if (chunks > 65535) return fail(KV_ERR_INVALID, "a swap entry is too large for the launch grid");
+    kv_pool_sizes hs{};
+    if ((st = kv_pool_bytes(hd, &hs)) != KV_OK) return st;
+    pbq::SwapArgs a{};
+    char* dp = nullptr;
+    if ((st = pbq::pinned_device_ptr(plan, sizeof(kv_swap) * (size_t)n, "plan", &dp)) != KV_OK) return st;
+    a.plan = (const kv_swap*)dp;
+    struct {
+        void* p;
+        size_t bytes;
+        char** out;
+        const char* name;
+    } host[] = {
+        {hm->k_codes, hs.k_codes, &a.host.k_codes, "host k_codes"},
+        {hm->v_codes, hs.v_codes, &a.host.v_codes, "host v_codes"},
+        {hm->k_scale, hs.k_scale, (char**)&a.host.k_scale, "host k_scale"},
+        {hm->v_scale, hs.v_scale, (char**)&a.host.v_scale, "host v_scale"},
+        {hm->v_zp, hs.v_zp, (char**)&a.host.v_zp, "host v_zp"},
+        {has_slots ? hm->tail_k : nullptr, hs.tail_k, &a.host.tail_k, "host tail_k"},
+        {has_slots ? hm->tail_v : nullptr, hs.tail_v, &a.host.tail_v, "host tail_v"},
+    };
+    for (auto& e : host)
+        if (e.p && e.bytes && (st = pbq::pinned_device_ptr(e.p, e.bytes, e.name, e.out)) != KV_OK) return st;
+    a.dev = pbq::SwapSide{(char*)m->k_codes, (char*)m->v_codes, (uint16_t*)m->k_scale,
+                          (uint16_t*)m->v_scale, (uint8_t*)m->v_zp, (char*)m->tail_k, (char*)m->tail_v};
+    a.n = n;
+    a.block_size = d->block_size;
+    a.num_kv_heads = d->num_kv_heads;
+    a.head_dim = d->head_dim;
+    a.v_codec = d->v_codec;
+    a.dev_blocks = d->num_blocks;
+    a.dev_slots = d->max_seqs;
+    a.host_blocks = hd->num_blocks;
+    a.host_slots = hd->max_seqs;
+    a.chunks = (int32_t)chunks;
+    return pbq::hip_status(pbq::launch_swap_blocks(a, (hipStream_t)stream), "kv_swap_blocks launch");
 }
 
 kv_status kv_quantize_store(const kv_pool_desc* d, const kv_pool_mem* m,

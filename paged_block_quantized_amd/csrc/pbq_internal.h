@@ -82,8 +82,33 @@ struct CopyArgs {
     int32_t n;
 };
 
+// One side of a swap: a pool's arrays (device memory, or the device's
+// addresses of pinned host memory).
+struct SwapSide {
+    char* k_codes;
+    char* v_codes;
+    uint16_t* k_scale;
+    uint16_t* v_scale;
+    uint8_t* v_zp;
+    char* tail_k;
+    char* tail_v;
+};
+
+struct SwapArgs {
+    SwapSide dev, host;
+    const kv_swap* plan;  // device address of the pinned host plan
+    int32_t n;
+    int32_t block_size, num_kv_heads, head_dim, v_codec;
+    int32_t dev_blocks, dev_slots, host_blocks, host_slots;
+    int32_t chunks;       // work groups per entry (grid y)
+};
+
+// Bytes one swap work group moves (256 threads x 4 x 16 bytes).
+constexpr int64_t kSwapChunk = 256 * 4 * 16;
+
 hipError_t launch_quantize_store(const QuantStoreArgs& a, hipStream_t stream);
 hipError_t launch_paged_attn(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
+hipError_t launch_swap_blocks(const SwapArgs& a, hipStream_t stream);
 
 }  // namespace pbq

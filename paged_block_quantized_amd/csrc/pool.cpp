@@ -24,6 +24,15 @@
 //    means the whole prefix is equal, with no hash collisions to fear); fresh
 //    full blocks enter the index when allocated; a block leaves it when its
 //    count reaches zero.
+//  * deepinsea.top "Swap": when device memory runs short, KV blocks move to
+//    a CPU swap space sized in GB.  Readings: the swap space is a second
+//    block pool (own free stack popped from its end, own counts) plus host
+//    tail slots; a group of sequences swaps out together and moves only the
+//    blocks that no sequence outside the group holds (moving any other frees
+//    nothing), each once, in first-seen order; swap-in takes fresh device
+//    blocks; both are all-or-nothing.  Swapped tables name host block h as
+//    -1 - h (and the host slot likewise).  Each call returns the copy plan
+//    that kv_swap_blocks runs.
 // The pool is single-threaded per handle; no call touches device memory.
 
 #include <stdint.h>
@@ -38,10 +47,13 @@
 #include "pbq_internal.h"
 
 struct SeqState {
-    std::vector<int32_t> table;
+    std::vector<int32_t> table;  // device block b >= 0, host block h as -1 - h
     int32_t num_tokens = 0;
-    int32_t slot = 0;
+    int32_t slot = 0;            // device slot, or -1 - host slot when swapped
+    bool swapped = false;
 };
+
+inline int32_t host_id(int32_t h) { return -1 - h; }
 
 // Prefix-cache key of a block: the block before it (-1 for the first) and
 // its bs token ids.  The index maps a hash of the key to candidate blocks;
@@ -64,6 +76,21 @@ struct kv_pool {
     std::vector<int32_t> key_ids;     // per block: bs key ids
     std::vector<uint64_t> key_hash;   // per block: key hash
     int32_t n_indexed = 0;
+    // swap space
+    std::vector<int32_t> host_free_stack;
+    std::vector<int32_t> host_refcount;
+    std::set<int32_t> host_free_slots;
+    int32_t n_swapped = 0;
+
+    // drop n references to device block b; at zero it goes back on the free
+    // stack and leaves the prefix index
+    void release_block(int32_t b, int32_t n) {
+        refcount[b] -= n;
+        if (refcount[b] == 0) {
+            free_stack.push_back(b);
+            if (indexed[b]) leave(b);
+        }
+    }
 
     bool key_equal(int32_t b, int32_t parent, const int32_t* ids) const {
         const int64_t bs = desc.block_size;
@@ -218,6 +245,7 @@ kv_status kv_seq_fork(kv_pool* pool, int64_t parent, int64_t child,
     auto it = pool->seqs.find(parent);
     if (it == pool->seqs.end()) return pbq::fail(KV_ERR_UNKNOWN_SEQ, "unknown parent");
     if (pool->seqs.count(child)) return pbq::fail(KV_ERR_STATE, "child already present");
+    if (it->second.swapped) return pbq::fail(KV_ERR_STATE, "parent is swapped out");
     if (pool->free_slots.empty()) return pbq::fail(KV_ERR_NO_SLOTS, "no free tail slot");
     const SeqState& p = it->second;
     const bool partial = p.num_tokens % pool->desc.block_size != 0;
@@ -243,6 +271,7 @@ kv_status kv_seq_append(kv_pool* pool, int64_t seq, int32_t n_tokens,
     auto it = pool->seqs.find(seq);
     if (it == pool->seqs.end()) return pbq::fail(KV_ERR_UNKNOWN_SEQ, "unknown sequence");
     SeqState& st = it->second;
+    if (st.swapped) return pbq::fail(KV_ERR_STATE, "sequence is swapped out");
     const int64_t bs = pool->desc.block_size;
     const int64_t ntok = st.num_tokens;
     if (ntok + (int64_t)n_tokens > INT32_MAX)
@@ -280,13 +309,18 @@ kv_status kv_seq_free(kv_pool* pool, int64_t seq) {
     auto it = pool->seqs.find(seq);
     if (it == pool->seqs.end()) return pbq::fail(KV_ERR_UNKNOWN_SEQ, "unknown sequence");
     for (int32_t b : it->second.table) {
-        pool->refcount[b] -= 1;
-        if (pool->refcount[b] == 0) {
-            pool->free_stack.push_back(b);
-            if (pool->indexed[b]) pool->leave(b);
+        if (b >= 0) {
+            pool->release_block(b, 1);
+        } else if (--pool->host_refcount[host_id(b)] == 0) {
+            pool->host_free_stack.push_back(host_id(b));
         }
     }
-    pool->free_slots.insert(it->second.slot);
+    if (it->second.swapped) {
+        pool->host_free_slots.insert(host_id(it->second.slot));
+        pool->n_swapped -= 1;
+    } else {
+        pool->free_slots.insert(it->second.slot);
+    }
     pool->seqs.erase(it);
     return KV_OK;
 }
@@ -318,6 +352,7 @@ kv_status kv_batch_tables(const kv_pool* pool, const int64_t* seqs, int32_t n,
     for (int32_t i = 0; i < n; ++i) {  // validate first: no partial output
         auto it = pool->seqs.find(seqs[i]);
         if (it == pool->seqs.end()) return pbq::fail(KV_ERR_UNKNOWN_SEQ, "unknown sequence");
+        if (it->second.swapped) return pbq::fail(KV_ERR_STATE, "sequence is swapped out");
         if ((int64_t)it->second.table.size() > max_blocks)
             return pbq::fail(KV_ERR_INVALID, "a table needs more than max_blocks entries");
     }
@@ -345,6 +380,9 @@ kv_status kv_pool_stats(const kv_pool* pool, kv_pool_stats_t* out) {
     out->shared = shared;
     out->seqs = (int32_t)pool->seqs.size();
     out->cached = pool->n_indexed;
+    out->host_total = (int32_t)pool->host_refcount.size();
+    out->host_free = (int32_t)pool->host_free_stack.size();
+    out->swapped = pool->n_swapped;
     return KV_OK;
 }
 
@@ -357,6 +395,149 @@ kv_status kv_pool_free_list(const kv_pool* pool, int32_t* out, int32_t cap,
         std::copy(pool->free_stack.begin(), pool->free_stack.end(), out);
     }
     if (n) *n = sz;
+    return KV_OK;
+}
+
+kv_status kv_pool_set_swap_space(kv_pool* pool, int32_t host_blocks, int32_t host_slots) {
+    if (!pool) return pbq::fail(KV_ERR_INVALID, "pool is NULL");
+    if (host_blocks < 0 || host_slots < 0)
+        return pbq::fail(KV_ERR_INVALID, "swap space sizes must be >= 0");
+    if (pool->n_swapped > 0) return pbq::fail(KV_ERR_STATE, "sequences are swapped out");
+    pool->host_free_stack.resize(host_blocks);
+    for (int32_t h = 0; h < host_blocks; ++h) pool->host_free_stack[h] = h;
+    pool->host_refcount.assign(host_blocks, 0);
+    pool->host_free_slots.clear();
+    for (int32_t k = 0; k < host_slots; ++k) pool->host_free_slots.insert(k);
+    return KV_OK;
+}
+
+namespace {
+
+// Checks a swap group: no repeats, every sequence known and in the wanted
+// place (resident for swap-out, swapped for swap-in).
+kv_status check_group(const kv_pool* pool, const int64_t* seqs, int32_t n, bool want_swapped,
+                      int32_t* plan_cap, kv_swap* plan) {
+    if (n < 0 || (n > 0 && !seqs)) return pbq::fail(KV_ERR_INVALID, "bad sequence list");
+    if (*plan_cap < 0 || (*plan_cap > 0 && !plan)) return pbq::fail(KV_ERR_INVALID, "bad plan buffer");
+    std::vector<int64_t> sorted(seqs, seqs + n);
+    std::sort(sorted.begin(), sorted.end());
+    if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
+        return pbq::fail(KV_ERR_INVALID, "a sequence is named twice");
+    for (int32_t i = 0; i < n; ++i)
+        if (!pool->seqs.count(seqs[i])) return pbq::fail(KV_ERR_UNKNOWN_SEQ, "unknown sequence");
+    for (int32_t i = 0; i < n; ++i)
+        if (pool->seqs.find(seqs[i])->second.swapped != want_swapped)
+            return pbq::fail(KV_ERR_STATE, want_swapped ? "sequence is not swapped out"
+                                                        : "sequence is swapped out");
+    return KV_OK;
+}
+
+// Distinct table entries of the group in first-seen order with the number
+// of references the group holds to each: host entries (< 0) when `host`,
+// device entries otherwise.
+void group_refs(const kv_pool* pool, const int64_t* seqs, int32_t n, bool host,
+                std::vector<int32_t>& order, std::unordered_map<int32_t, int32_t>& count) {
+    for (int32_t i = 0; i < n; ++i)
+        for (int32_t b : pool->seqs.find(seqs[i])->second.table) {
+            if ((b < 0) != host) continue;
+            auto r = count.emplace(b, 0);
+            if (r.second) order.push_back(b);
+            r.first->second += 1;
+        }
+}
+
+}  // namespace
+
+kv_status kv_seq_swap_out(kv_pool* pool, const int64_t* seqs, int32_t n, kv_swap* plan,
+                          int32_t cap, int32_t* n_plan) {
+    if (!pool) return pbq::fail(KV_ERR_INVALID, "pool is NULL");
+    kv_status st = check_group(pool, seqs, n, false, &cap, plan);
+    if (st != KV_OK) return st;
+    std::vector<int32_t> order;
+    std::unordered_map<int32_t, int32_t> count;
+    group_refs(pool, seqs, n, false, order, count);
+    std::vector<int32_t> moving;
+    for (int32_t b : order)
+        if (count[b] == pool->refcount[b]) moving.push_back(b);
+    if ((int64_t)pool->host_free_slots.size() < n)
+        return pbq::fail(KV_ERR_NO_SLOTS, "no free host slot");
+    if (moving.size() > pool->host_free_stack.size())
+        return pbq::fail(KV_ERR_NO_BLOCKS, "not enough free host blocks");
+    const int32_t bs = pool->desc.block_size;
+    int64_t entries = (int64_t)moving.size();
+    for (int32_t i = 0; i < n; ++i) entries += pool->seqs.find(seqs[i])->second.num_tokens % bs != 0;
+    if (entries > cap) return pbq::fail(KV_ERR_INVALID, "plan buffer too small (cap)");
+    int32_t k = 0;
+    std::unordered_map<int32_t, int32_t> where;
+    for (int32_t b : moving) {
+        const int32_t h = pool->host_free_stack.back();
+        pool->host_free_stack.pop_back();
+        pool->host_refcount[h] = count[b];
+        pool->release_block(b, count[b]);
+        where[b] = h;
+        plan[k++] = kv_swap{KV_SWAP_BLOCK_OUT, b, h, 0};
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        SeqState& s = pool->seqs.find(seqs[i])->second;
+        const int32_t hs = *pool->host_free_slots.begin();
+        pool->host_free_slots.erase(pool->host_free_slots.begin());
+        const int32_t rows = s.num_tokens % bs;
+        if (rows) plan[k++] = kv_swap{KV_SWAP_SLOT_OUT, s.slot, hs, rows};
+        pool->free_slots.insert(s.slot);
+        for (int32_t& b : s.table) {
+            auto w = where.find(b);
+            if (w != where.end()) b = host_id(w->second);
+        }
+        s.slot = host_id(hs);
+        s.swapped = true;
+        pool->n_swapped += 1;
+    }
+    if (n_plan) *n_plan = k;
+    return KV_OK;
+}
+
+kv_status kv_seq_swap_in(kv_pool* pool, const int64_t* seqs, int32_t n, kv_swap* plan,
+                         int32_t cap, int32_t* n_plan) {
+    if (!pool) return pbq::fail(KV_ERR_INVALID, "pool is NULL");
+    kv_status st = check_group(pool, seqs, n, true, &cap, plan);
+    if (st != KV_OK) return st;
+    std::vector<int32_t> order;
+    std::unordered_map<int32_t, int32_t> count;
+    group_refs(pool, seqs, n, true, order, count);
+    if ((int64_t)pool->free_slots.size() < n) return pbq::fail(KV_ERR_NO_SLOTS, "no free tail slot");
+    if (order.size() > pool->free_stack.size())
+        return pbq::fail(KV_ERR_NO_BLOCKS, "not enough free blocks");
+    const int32_t bs = pool->desc.block_size;
+    int64_t entries = (int64_t)order.size();
+    for (int32_t i = 0; i < n; ++i) entries += pool->seqs.find(seqs[i])->second.num_tokens % bs != 0;
+    if (entries > cap) return pbq::fail(KV_ERR_INVALID, "plan buffer too small (cap)");
+    int32_t k = 0;
+    std::unordered_map<int32_t, int32_t> where;
+    for (int32_t e : order) {
+        const int32_t h = host_id(e);
+        const int32_t d = pool->free_stack.back();
+        pool->free_stack.pop_back();
+        pool->refcount[d] = count[e];
+        pool->host_refcount[h] -= count[e];
+        if (pool->host_refcount[h] == 0) pool->host_free_stack.push_back(h);
+        where[e] = d;
+        plan[k++] = kv_swap{KV_SWAP_BLOCK_IN, h, d, 0};
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        SeqState& s = pool->seqs.find(seqs[i])->second;
+        const int32_t hs = host_id(s.slot);
+        const int32_t slot = *pool->free_slots.begin();
+        pool->free_slots.erase(pool->free_slots.begin());
+        const int32_t rows = s.num_tokens % bs;
+        if (rows) plan[k++] = kv_swap{KV_SWAP_SLOT_IN, hs, slot, rows};
+        pool->host_free_slots.insert(hs);
+        for (int32_t& b : s.table)
+            if (b < 0) b = where[b];
+        s.slot = slot;
+        s.swapped = false;
+        pool->n_swapped -= 1;
+    }
+    if (n_plan) *n_plan = k;
     return KV_OK;
 }
 

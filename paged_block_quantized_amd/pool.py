@@ -97,6 +97,61 @@ class KVPool:
     def free_list(self):
         return L.kv_pool_free_list(self.handle)
 
+    # ---- swap space (deepinsea.top "Swap") ----------------------------------
+    def set_swap_space(self, host_blocks, host_slots):
+        """Size the swap space and allocate its arrays, the device arrays'
+        layout for host_blocks blocks and host_slots slots, in pinned host
+        memory."""
+        L.kv_pool_set_swap_space(self.handle, host_blocks, host_slots)
+        nb, ns = max(1, host_blocks), max(1, host_slots)
+        self.host_desc = L.make_desc(nb, self.block_size, self.num_kv_heads, self.head_dim,
+                                     self.desc.v_codec, ns)
+        self.host_arrays = {}
+        self.host_mem = None
+        if self.device is None:
+            return
+        H, bs, D = self.num_kv_heads, self.block_size, self.head_dim
+
+        def pinned(shape, dtype):
+            return torch.zeros(shape, dtype=dtype, pin_memory=True)
+
+        self.host_arrays = {
+            "k_codes": pinned((nb, H, bs, D), torch.int8),
+            "v_codes": pinned((nb, H, D, bs // 2 if self.v_int4 else bs),
+                              torch.uint8 if self.v_int4 else torch.int8),
+            "k_scale": pinned((nb, H), torch.float16),
+            "v_scale": pinned((nb, H), torch.float16),
+            "v_zp": pinned((nb, H) if self.v_int4 else (1,), torch.uint8),
+            "tail_k": pinned((ns, H, bs, D), torch.float16),
+            "tail_v": pinned((ns, H, bs, D), torch.float16),
+        }
+        self.host_mem = L.kv_pool_mem(*[
+            None if (n == "v_zp" and not self.v_int4) else self.host_arrays[n].data_ptr()
+            for n in ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "tail_k", "tail_v")])
+
+    def _run_plan(self, fn, seqs, stream, mem):
+        cap = L.swap_plan_cap(self.handle, seqs)
+        plan = torch.zeros((max(1, cap), 4), dtype=torch.int32, pin_memory=True)
+        n = fn(self.handle, seqs, plan)
+        if n:
+            L.kv_swap_blocks(self.desc, self.mem if mem is None else mem, self.host_desc,
+                             self.host_mem, plan, n, stream)
+        # the kernel reads the plan from host memory: keep it until the stream
+        # has passed the copy
+        ev = torch.cuda.Event()
+        ev.record(stream if stream is not None else torch.cuda.current_stream())
+        self._plans = [(e, p) for e, p in getattr(self, "_plans", []) if not e.query()]
+        self._plans.append((ev, plan))
+        return [tuple(r) for r in plan[:n].tolist()]
+
+    def swap_out(self, seqs, stream=None, mem=None):
+        """Swap a group of sequences out and enqueue the copies on stream;
+        returns the plan as (kind, src, dst, rows) tuples."""
+        return self._run_plan(L.kv_seq_swap_out, seqs, stream, mem)
+
+    def swap_in(self, seqs, stream=None, mem=None):
+        return self._run_plan(L.kv_seq_swap_in, seqs, stream, mem)
+
     # ---- device calls ------------------------------------------------------
     def copy_blocks(self, copies, stream=None):
         """Perform (kind, src, dst) copies returned by fork/append."""

@@ -66,6 +66,15 @@ class CAdapter:
     def release(self, s):
         return L.kv_seq_free(self.h, s)
 
+    def set_swap_space(self, hb, hs):
+        L.kv_pool_set_swap_space(self.h, hb, hs)
+
+    def swap_out(self, seqs):
+        return L.kv_seq_swap_out(self.h, seqs)
+
+    def swap_in(self, seqs):
+        return L.kv_seq_swap_in(self.h, seqs)
+
     def table(self, s):
         return L.kv_seq_table(self.h, s)
 
@@ -102,7 +111,94 @@ def test_c_allocator_matches_model(lib, seed, n_blocks, bs):
         assert (st.table, st.num_tokens, st.slot) == tuple(c.table(sid))
 
 
-def test_batch_tables(lib):
+@settings(max_examples=80, deadline=None)
+@given(seed=hst.integers(0, 2 ** 31 - 1), n_blocks=hst.integers(1, 24),
+       bs=hst.sampled_from([1, 2, 4, 16]), host_blocks=hst.integers(0, 16))
+def test_c_swap_matches_model(lib, seed, n_blocks, bs, host_blocks):
+    """Swap-out / swap-in plans, tables (host blocks as -1 - h), slots, free
+    stacks and stats equal the model's after every op, failures included."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(n_blocks)
+    model = A.BlockPoolModel(n_blocks, bs, 6, perm)
+    c = CAdapter(n_blocks, bs, 6, perm)
+    model.set_swap_space(host_blocks, 3)
+    c.set_swap_space(host_blocks, 3)
+    for op in random_ops(rng, 160, max_seq_id=6, prefix=True, swap=True):
+        a = apply_op(model, op, A.AllocError)
+        b = apply_op(c, op, L.PBQError)
+        assert a == b, op
+        assert model.free == c.free_list()
+        assert model.stats() == c.stats()
+        for sid, st in model.seqs.items():
+            assert (st.table, st.num_tokens, st.slot) == tuple(c.table(sid))
+
+
+def test_swap_allocator_errors(lib):
+    c = CAdapter(8, 4, 2, None)
+    c.set_swap_space(2, 1)
+    c.alloc(0, 5)
+    with pytest.raises(L.PBQError) as e:
+        c.swap_in([0])
+    assert e.value.kind == "state"
+    buf = (L.kv_swap * 1)()
+    n = ctypes.c_int32()
+    sq = (ctypes.c_int64 * 1)(0)
+    with pytest.raises(L.PBQError, match="cap"):       # two blocks and a slot need 3 entries
+        L._check(L.lib().kv_seq_swap_out(c.h, sq, 1, buf, 1, ctypes.byref(n)))
+    assert c.stats()["swapped"] == 0
+    assert c.swap_out([0]) == [(L.KV_SWAP_BLOCK_OUT, 7, 1, 0), (L.KV_SWAP_BLOCK_OUT, 6, 0, 0),
+                               (L.KV_SWAP_SLOT_OUT, 0, 0, 1)]
+    with pytest.raises(L.PBQError) as e:
+        L.kv_batch_tables(c.h, [0], 4)
+    assert e.value.kind == "state"
+    with pytest.raises(L.PBQError) as e:
+        c.set_swap_space(4, 4)
+    assert e.value.kind == "state"
+    assert c.table(0) == ([-2, -1], 5, -1)
+    c.release(0)
+    assert c.stats()["host_free"] == 2 and c.stats()["swapped"] == 0
+
+
+def test_swap_blocks_validates_plan_on_host(lib):
+    """kv_swap_blocks checks every plan entry before anything reaches HIP;
+    host memory that HIP does not know as pinned is refused."""
+    desc = L.make_desc(8, 16, 2, 64, max_seqs=2)
+    hdesc = L.make_desc(4, 16, 2, 64, max_seqs=1)
+    buf = ctypes.create_string_buffer(1 << 16)
+    base = (ctypes.addressof(buf) + 15) & ~15
+    mem = L.kv_pool_mem(base, base, base, base, None, base, base)
+
+    def run(entries, hd=hdesc):
+        plan = (L.kv_swap * max(1, len(entries)))(*[L.kv_swap(*e) for e in entries])
+        L.kv_swap_blocks(desc, mem, hd, mem, ctypes.addressof(plan), len(entries), 0)
+
+    O, I, SO, SI = L.KV_SWAP_BLOCK_OUT, L.KV_SWAP_BLOCK_IN, L.KV_SWAP_SLOT_OUT, L.KV_SWAP_SLOT_IN
+    with pytest.raises(L.PBQError, match="unknown kind"):
+        run([(7, 0, 0, 0)])
+    with pytest.raises(L.PBQError, match="out of range"):
+        run([(O, 8, 0, 0)])                  # device block 8 of 8
+    with pytest.raises(L.PBQError, match="out of range"):
+        run([(O, 0, 4, 0)])                  # host block 4 of 4
+    with pytest.raises(L.PBQError, match="out of range"):
+        run([(SI, 1, 0, 3)])                 # host slot 1 of 1
+    with pytest.raises(L.PBQError, match="rows"):
+        run([(SO, 0, 0, 0)])
+    with pytest.raises(L.PBQError, match="rows"):
+        run([(SO, 0, 0, 17)])
+    with pytest.raises(L.PBQError, match="rows"):
+        run([(O, 0, 0, 1)])
+    with pytest.raises(L.PBQError, match="written twice"):
+        run([(O, 0, 1, 0), (O, 2, 1, 0)])
+    with pytest.raises(L.PBQError, match="written twice or also read"):
+        run([(O, 3, 1, 0), (I, 2, 3, 0)])    # device block 3 read and written
+    with pytest.raises(L.PBQError, match="written twice or also read"):
+        run([(SO, 1, 0, 2), (SI, 0, 1, 2)])  # host slot 0 written, then read
+    with pytest.raises(L.PBQError, match="host_desc"):
+        run([(O, 0, 0, 0)], L.make_desc(4, 32, 2, 64, max_seqs=1))
+    with pytest.raises(L.PBQError, match="pinned"):
+        run([(O, 0, 0, 0), (I, 1, 2, 0), (SO, 0, 0, 5)])
+    run([])                                  # nothing to do: no device work
+
     c = CAdapter(16, 4, 4, None)
     c.alloc(7, 9)
     c.alloc(3, 1)

@@ -129,3 +129,44 @@ def test_prefill_store_full():
 def test_gqa70b_full():
     setup = _run("gqa70b", samples=[0, 64, 127])
     assert setup.w.num_q_heads // setup.w.num_kv_heads == 8
+
+
+def test_llama7b_swap_round_trip_full():
+    """A quarter of the llama7b batch (8 sequences x 4096 tokens: 2048
+    blocks of 128 KiB) swapped out to pinned host memory, its device blocks
+    overwritten by another owner, and swapped back into other blocks: the
+    decode over the stored tokens is bitwise unchanged and the swapped
+    sequences still match the oracle."""
+    from oracle import allocator as A
+    from paged_block_quantized_amd import runner, workloads as W
+    w = W.WORKLOADS["llama7b"]
+    announce("full swap llama7b", "setup")
+    setup = runner.setup_decode(w)
+    setup.step()
+    setup.attend()
+    torch.cuda.synchronize()
+    out0 = setup.out.clone()
+    pool = setup.pool
+    group = list(range(0, w.num_seqs, 4))
+    nb = 4096 // w.block_size
+    pool.set_swap_space(len(group) * nb, len(group))
+    announce("full swap llama7b", "out")
+    plan = pool.swap_out(group)
+    srcs = [e[1] for e in plan if e[0] == A.SWAP_BLOCK_OUT]
+    assert len(srcs) == len(group) * nb and len(plan) == len(srcs)   # full blocks: no slot rows
+    idx = torch.tensor(srcs, device="cuda")
+    pool.k_codes[idx] = 0
+    pool.v_codes[idx] = 0
+    pool.k_scale[idx] = 0
+    announce("full swap llama7b", "in")
+    pool.swap_in(group)
+    tables, _, slots = pool.batch_tables(list(range(w.num_seqs)), setup.tables.shape[1])
+    assert not torch.equal(tables[group].cuda(), setup.tables[group])
+    setup.tables, setup.slots = tables.cuda(), slots.cuda()
+    setup.attend()
+    torch.cuda.synchronize()
+    assert torch.equal(setup.out.view(torch.int16), out0.view(torch.int16))
+    out = setup.out.cpu().numpy()
+    for s in (group[1], group[-1]):
+        announce("full swap llama7b", "oracle seq", s)
+        check_sequence(setup, s, out, "llama7b after swap")

@@ -462,3 +462,166 @@ def test_prefix_cache_end_to_end(bs, vc):
     ref = attention.paged_decode(opool, [model.table(s)[0] for s in range(S)], ctx_h.numpy(), q,
                                  1 / np.sqrt(d))
     assert_close(out.cpu().numpy(), ref, "prefix-cache decode")
+
+
+# ---- swap to host memory (deepinsea "Swap") --------------------------------
+
+_POOL_ARRAYS = ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "tail_k", "tail_v")
+
+
+def _fill_random(rng, arrays, skip_zp):
+    """Seeded random bytes in every array (device or pinned host tensors);
+    returns numpy uint8 copies shaped [rows, bytes per row]."""
+    exp = {}
+    for n in _POOL_ARRAYS:
+        if n == "v_zp" and skip_zp:
+            continue
+        t = arrays[n]
+        b = rng.integers(0, 256, t.numel() * t.element_size(), dtype=np.uint8)
+        t.view(torch.uint8).reshape(-1).copy_(torch.from_numpy(b))
+        exp[n] = b.reshape(t.shape[0], -1)
+    return exp
+
+
+def _apply_plan(plan, dev, host, h, bs):
+    """The plan's definition on numpy byte arrays: whole rows of the block
+    arrays; the first `rows` token rows of each head of a tail slot."""
+    block = ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp")
+    for kind, src, dst, rows in plan:
+        out = kind in (A.SWAP_BLOCK_OUT, A.SWAP_SLOT_OUT)
+        a, b = (dev, host) if out else (host, dev)
+        if kind in (A.SWAP_BLOCK_OUT, A.SWAP_BLOCK_IN):
+            for n in block:
+                if n in a:
+                    b[n][dst] = a[n][src]
+        else:
+            for n in ("tail_k", "tail_v"):
+                b[n][dst].reshape(h, bs, -1)[:, :rows] = a[n][src].reshape(h, bs, -1)[:, :rows]
+
+
+SWAP_SHAPES = [(16, 2, 64, "i8"), (32, 3, 128, "i4"), (16, 32, 128, "i8"), (32, 8, 64, "i4")]
+
+
+@pytest.mark.parametrize("bs,h,d,vc", SWAP_SHAPES)
+def test_swap_moves_bytes_exactly(bs, h, d, vc):
+    """kv_seq_swap_out / kv_seq_swap_in plans equal the oracle model's, and
+    kv_swap_blocks moves exactly the bytes they name: every device and host
+    array equals seeded random contents with the plans applied by numpy,
+    bit for bit, through forks, reuse of freed blocks, and partial groups."""
+    announce("swap-bytes", bs, h, d, vc)
+    from paged_block_quantized_amd import KVPool
+    rng = np.random.default_rng(1000 + bs + h + d)
+    N, S = 40, 8
+    order = rng.permutation(N)
+    pool = KVPool(N, bs, h, d, vc, max_seqs=S, free_order=order)
+    model = A.BlockPoolModel(N, bs, S, order)
+    pool.set_swap_space(24, 4)
+    model.set_swap_space(24, 4)
+    dev = _fill_random(rng, pool.arrays, vc == "i8")
+    host = _fill_random(rng, pool.host_arrays, vc == "i8")
+    for s, n in {0: 3 * bs + 5, 1: 2 * bs, 2: 1, 3: 4 * bs - 1, 4: bs + 2}.items():
+        assert pool.alloc(s, n) == model.alloc(s, n)
+    copies = model.fork(0, 5)
+    assert pool.fork(0, 5) == copies
+    pool.copy_blocks(copies)
+    for _, src, dst in copies:                       # a slot copy: whole slot
+        for n in ("tail_k", "tail_v"):
+            dev[n][dst] = dev[n][src]
+
+    def swap(direction, group):
+        plan = getattr(pool, direction)(group)
+        assert plan == getattr(model, direction)(group)
+        _apply_plan(plan, dev, host, h, bs)
+        return plan
+
+    plan = swap("swap_out", [0, 5])                  # a fork pair: shared blocks once
+    assert sum(1 for e in plan if e[0] == A.SWAP_SLOT_OUT) == 2
+    # a new sequence takes freed blocks and a freed slot and writes them
+    tab = pool.alloc(6, 3 * bs)
+    assert tab == model.alloc(6, 3 * bs)
+    slot6 = pool.table(6)[2]
+    for n in ("k_codes", "v_codes", "k_scale", "v_scale"):
+        fresh = rng.integers(0, 256, dev[n][tab].shape, dtype=np.uint8)
+        dev[n][tab] = fresh
+        pool.arrays[n].view(torch.uint8).reshape(N, -1)[torch.tensor(tab)] = \
+            torch.from_numpy(fresh).cuda()
+    fresh = rng.integers(0, 256, dev["tail_k"][slot6].shape, dtype=np.uint8)
+    dev["tail_k"][slot6] = fresh
+    pool.arrays["tail_k"].view(torch.uint8).reshape(S, -1)[slot6] = torch.from_numpy(fresh).cuda()
+    swap("swap_out", [2])                            # one token: one block, one row
+    swap("swap_in", [0, 5])
+    pool.release(6)
+    model.release(6)
+    swap("swap_in", [2])
+    swap("swap_out", [3, 1])
+    swap("swap_in", [1])                             # 3 stays out
+    torch.cuda.synchronize()
+    for n in dev:
+        got = pool.arrays[n].view(torch.uint8).reshape(dev[n].shape).cpu().numpy()
+        assert np.array_equal(got, dev[n]), f"device {n}"
+    for n in host:
+        got = pool.host_arrays[n].view(torch.uint8).reshape(host[n].shape).numpy()
+        assert np.array_equal(got, host[n]), f"host {n}"
+    for s in model.seqs:
+        assert pool.table(s) == model.table(s)
+    assert pool.stats() == model.stats()
+
+
+@pytest.mark.parametrize("bs,vc", [(16, "i8"), (32, "i4")])
+def test_swap_then_decode_append_end_to_end(bs, vc):
+    """Sequences swapped out (their freed blocks overwritten by another
+    owner) and back in decode as before, bit for bit; their next token's
+    fused store re-quantizes the partial block from the tail rows that came
+    back, so the pool equals the oracle's quantization of each full history
+    through the final tables, and the decode matches the oracle."""
+    announce("swap-e2e", bs, vc)
+    h, d, hq = 2, 64, 4
+    ctx = [2 * bs + 3, 1, 5 * bs, 3 * bs + bs - 1, bs]
+    case = normal_case(ctx, hq, h, d, bs, vc, seed=31 + bs, extra_blocks=12)
+    case.store_all()
+    out0 = case.decode()
+    assert_close(out0, case.reference(), "swap-e2e before")
+    pool, model = case.pool, case.model
+    pool.set_swap_space(16, 3)
+    model.set_swap_space(16, 3)
+    rng = np.random.default_rng(5)
+    assert pool.swap_out([1, 3]) == model.swap_out([1, 3])
+    tab = pool.alloc(9, 4 * bs)
+    assert tab == model.alloc(9, 4 * bs)
+    idx = torch.tensor(tab)
+    pool.k_codes[idx] = torch.randint(-127, 128, pool.k_codes[idx].shape, dtype=torch.int8).cuda()
+    pool.v_codes.view(torch.uint8)[idx] = torch.randint(0, 256, pool.v_codes[idx].shape,
+                                                       dtype=torch.uint8).cuda()
+    pool.tail_k[pool.table(9)[2]] = torch.randn(pool.tail_k.shape[1:]).half().cuda()
+    pool.release(9)
+    model.release(9)
+    assert pool.swap_in([3, 1]) == model.swap_in([3, 1])
+    S = len(ctx)
+    tables, ctx_h, slots = pool.batch_tables(list(range(S)), case.max_blocks + 1)
+    case.tables, case.slots = tables.cuda(), slots.cuda()
+    out1 = case.decode()
+    assert np.array_equal(out1.view(np.uint16), out0.view(np.uint16))
+    # the next token of every sequence, stored by the fused decode
+    for s in range(S):
+        assert pool.append(s, 1) == model.append(s, 1)
+    new_k = rng.standard_normal((S, h, d)).astype(np.float16)
+    new_v = rng.standard_normal((S, h, d)).astype(np.float16)
+    q = rng.standard_normal((S, hq, d)).astype(np.float16)
+    tables, ctx_h, slots = pool.batch_tables(list(range(S)), case.max_blocks + 1)
+    qd = torch.from_numpy(q).cuda()
+    out = torch.empty_like(qd)
+    pool.decode_append(torch.from_numpy(new_k).cuda(), torch.from_numpy(new_v).cuda(), slots.cuda(),
+                       qd, out, tables.cuda(), ctx_h.cuda(), int(ctx_h.max()), 1 / np.sqrt(d))
+    torch.cuda.synchronize()
+    ref_pool = paged.PoolArrays(pool.num_blocks, h, bs, d, vc == "i4")
+    tabs = []
+    for s in range(S):
+        hk = np.concatenate([case.hist_k[s], new_k[s:s + 1]])
+        hv = np.concatenate([case.hist_v[s], new_v[s:s + 1]])
+        t = model.table(s)[0]
+        paged.store_range(ref_pool, t, hk, hv, 0, ctx[s] + 1)
+        tabs.append(t)
+    used = sorted(b for t in tabs for b in t)
+    assert_pool_equal(pool, ref_pool, used)
+    ref = attention.paged_decode(ref_pool, tabs, [c + 1 for c in ctx], q, 1 / np.sqrt(d))
+    assert_close(out.cpu().numpy(), ref, "swap-e2e after")
