@@ -27,6 +27,10 @@ Readings
   [num_blocks, heads, head_dim, block_size / 2] bytes holding two consecutive
   tokens per byte (the earlier token in the low nibble), with a u8 zero point
   per (block, head).
+* Codecs by name: K "i8" (INT8 symmetric) or "fp8" (E4M3); V "i8", "i4"
+  (INT4 asymmetric), "i8a" (INT8 asymmetric, u8 codes) or "fp8".  FP8 and
+  INT8-asymmetric tiles are u8 arrays of the INT8 tiles' shape; the
+  asymmetric codecs keep their zero point in ``v_zp``.
 """
 
 import numpy as np
@@ -38,20 +42,53 @@ class PoolArrays:
     """Host mirror of the device pool arrays, same shapes and dtypes."""
 
     def __init__(self, num_blocks, num_kv_heads, block_size, head_dim,
-                 v_int4=False):
+                 v_int4=False, k_codec="i8", v_codec=None):
         self.num_blocks = num_blocks
         self.num_kv_heads = num_kv_heads
         self.block_size = block_size
         self.head_dim = head_dim
-        self.v_int4 = v_int4
-        self.k_codes = np.zeros((num_blocks, num_kv_heads, block_size, head_dim), np.int8)
-        if v_int4:
+        self.k_codec = k_codec
+        self.v_codec = v_codec if v_codec is not None else ("i4" if v_int4 else "i8")
+        assert self.k_codec in ("i8", "fp8") and self.v_codec in ("i8", "i4", "i8a", "fp8")
+        self.v_int4 = self.v_codec == "i4"
+        self.k_codes = np.zeros((num_blocks, num_kv_heads, block_size, head_dim),
+                                np.int8 if k_codec == "i8" else np.uint8)
+        if self.v_int4:
             self.v_codes = np.zeros((num_blocks, num_kv_heads, head_dim, block_size // 2), np.uint8)
         else:
-            self.v_codes = np.zeros((num_blocks, num_kv_heads, head_dim, block_size), np.int8)
+            self.v_codes = np.zeros((num_blocks, num_kv_heads, head_dim, block_size),
+                                    np.int8 if self.v_codec == "i8" else np.uint8)
         self.k_scale = np.zeros((num_blocks, num_kv_heads), np.float16)
         self.v_scale = np.zeros((num_blocks, num_kv_heads), np.float16)
         self.v_zp = np.zeros((num_blocks, num_kv_heads), np.uint8)
+
+
+def quantize_tile(codec: str, x16):
+    """(codes, scale, zero point) of one tile's rows under a codec name."""
+    if codec == "i8":
+        c, s = quant.quantize_int8_sym(x16)
+        return c, s, np.uint8(0)
+    if codec == "fp8":
+        c, s = quant.quantize_fp8_e4m3(x16)
+        return c, s, np.uint8(0)
+    if codec == "i4":
+        return quant.quantize_int4_asym(x16)
+    if codec == "i8a":
+        return quant.quantize_int8_asym(x16)
+    raise ValueError(codec)
+
+
+def dequantize_tile(codec: str, codes, scale, zero_point):
+    """float64 values of codes under a codec name (zero point for i4/i8a)."""
+    if codec == "i8":
+        return quant.dequantize_int8_sym(codes, scale)
+    if codec == "fp8":
+        return quant.dequantize_fp8_e4m3(codes, scale)
+    if codec == "i4":
+        return quant.dequantize_int4_asym(codes, scale, zero_point)
+    if codec == "i8a":
+        return quant.dequantize_int8_asym(codes, scale, zero_point)
+    raise ValueError(codec)
 
 
 def store_block(pool: PoolArrays, phys: int, k_rows, v_rows):
@@ -62,23 +99,16 @@ def store_block(pool: PoolArrays, phys: int, k_rows, v_rows):
     n = k_rows.shape[0]
     assert 1 <= n <= pool.block_size
     for h in range(pool.num_kv_heads):
-        kc, ks = quant.quantize_int8_sym(k_rows[:, h, :])
+        kc, ks, _ = quantize_tile(pool.k_codec, k_rows[:, h, :])
         pool.k_codes[phys, h] = 0
         pool.k_codes[phys, h, :n] = kc
         pool.k_scale[phys, h] = ks
-        # V tile, dim-major: codes[d, t]; tokens >= n stay zero
-        if pool.v_int4:
-            vc, vs, vz = quant.quantize_int4_asym(v_rows[:, h, :])
-            tile = np.zeros((pool.head_dim, pool.block_size), np.uint8)
-            tile[:, :n] = vc.T
-            pool.v_codes[phys, h] = quant.pack_int4(tile)
-            pool.v_zp[phys, h] = vz
-        else:
-            vc, vs = quant.quantize_int8_sym(v_rows[:, h, :])
-            tile = np.zeros((pool.head_dim, pool.block_size), np.int8)
-            tile[:, :n] = vc.T
-            pool.v_codes[phys, h] = tile
-            pool.v_zp[phys, h] = 0
+        # V tile, dim-major: codes[d, t]; tokens >= n stay zero bytes
+        vc, vs, vz = quantize_tile(pool.v_codec, v_rows[:, h, :])
+        tile = np.zeros((pool.head_dim, pool.block_size), vc.dtype)
+        tile[:, :n] = vc.T
+        pool.v_codes[phys, h] = quant.pack_int4(tile) if pool.v_int4 else tile
+        pool.v_zp[phys, h] = vz
         pool.v_scale[phys, h] = vs
 
 
@@ -101,33 +131,33 @@ def gather_dequant(pool: PoolArrays, table, ctx: int):
     t = np.arange(ctx)
     phys = np.asarray(table, np.int64)[t // bs]
     row = t % bs
-    kc = pool.k_codes[phys, :, row, :].astype(np.float64)        # [ctx, H, D]
-    ks = pool.k_scale[phys, :].astype(np.float64)                # [ctx, H]
-    khat = kc * ks[:, :, None]
+    kc = pool.k_codes[phys, :, row, :]                            # [ctx, H, D]
+    ks = pool.k_scale[phys, :]                                    # [ctx, H]
+    khat = np.stack([dequantize_tile(pool.k_codec, kc[:, h], ks[:, h][:, None], 0)
+                     for h in range(pool.num_kv_heads)], axis=1)
     if pool.v_int4:
-        tiles = quant.unpack_int4(pool.v_codes[phys])                # [ctx, H, D, bs]
-        vc = tiles[np.arange(ctx), :, :, row].astype(np.float64)      # [ctx, H, D]
-        vz = pool.v_zp[phys, :].astype(np.float64)
-        vhat = (vc - vz[:, :, None]) * pool.v_scale[phys, :].astype(np.float64)[:, :, None]
+        tiles = quant.unpack_int4(pool.v_codes[phys])             # [ctx, H, D, bs]
     else:
-        vc = pool.v_codes[phys][np.arange(ctx), :, :, row].astype(np.float64)
-        vhat = vc * pool.v_scale[phys, :].astype(np.float64)[:, :, None]
+        tiles = pool.v_codes[phys]
+    vc = tiles[np.arange(ctx), :, :, row]                         # [ctx, H, D]
+    vz = pool.v_zp[phys, :]
+    vs = pool.v_scale[phys, :]
+    vhat = np.stack([dequantize_tile(pool.v_codec, vc[:, h], vs[:, h][:, None],
+                                     vz[:, h][:, None].astype(np.float64))
+                     for h in range(pool.num_kv_heads)], axis=1)
     return khat.transpose(1, 0, 2), vhat.transpose(1, 0, 2)
 
 
-def quantize_contiguous(x16, block_size: int, int4: bool = False):
+def quantize_contiguous(x16, block_size: int, int4: bool = False, codec=None):
     """Quantize a contiguous [H, ctx, D] fp16 tensor in row chunks of
     ``block_size`` and return the dequantized float64 values."""
+    codec = codec or ("i4" if int4 else "i8")
     x16 = np.asarray(x16, np.float16)
     H, ctx, D = x16.shape
     out = np.zeros((H, ctx, D), np.float64)
     for h in range(H):
         for lo in range(0, ctx, block_size):
             hi = min(lo + block_size, ctx)
-            if int4:
-                c, s, z = quant.quantize_int4_asym(x16[h, lo:hi])
-                out[h, lo:hi] = quant.dequantize_int4_asym(c, s, z)
-            else:
-                c, s = quant.quantize_int8_sym(x16[h, lo:hi])
-                out[h, lo:hi] = quant.dequantize_int8_sym(c, s)
+            c, s, z = quantize_tile(codec, x16[h, lo:hi])
+            out[h, lo:hi] = dequantize_tile(codec, c, s, z)
     return out

@@ -12,8 +12,8 @@ from oracle import allocator as A
 from oracle import attention, paged, quant
 
 
-def _fill(rng, ctx_lens, hkv, d, bs, n_blocks, v_int4, perm):
-    pool = paged.PoolArrays(n_blocks, hkv, bs, d, v_int4)
+def _fill(rng, ctx_lens, hkv, d, bs, n_blocks, v_int4, perm, k_codec="i8", v_codec=None):
+    pool = paged.PoolArrays(n_blocks, hkv, bs, d, v_int4, k_codec, v_codec)
     m = A.BlockPoolModel(n_blocks, bs, len(ctx_lens), perm)
     tables, hist = [], []
     for s, c in enumerate(ctx_lens):
@@ -26,16 +26,26 @@ def _fill(rng, ctx_lens, hkv, d, bs, n_blocks, v_int4, perm):
     return pool, tables, hist
 
 
-@pytest.mark.parametrize("v_int4", [False, True])
-def test_gather_equals_contiguous(v_int4):
+@pytest.mark.parametrize("kc,vc", [("i8", "i8"), ("i8", "i4"), ("i8", "i8a"), ("fp8", "fp8")])
+def test_gather_equals_contiguous(kc, vc):
     rng = np.random.default_rng(0)
     ctx = [1, 17, 50, 100]
-    pool, tables, hist = _fill(rng, ctx, 2, 64, 16, 64, v_int4, rng.permutation(64))
+    pool, tables, hist = _fill(rng, ctx, 2, 64, 16, 64, False, rng.permutation(64), kc, vc)
     for s, c in enumerate(ctx):
         kh, vh = paged.gather_dequant(pool, tables[s], c)
         k, v = hist[s]
-        assert np.array_equal(kh, paged.quantize_contiguous(k.transpose(1, 0, 2), 16))
-        assert np.array_equal(vh, paged.quantize_contiguous(v.transpose(1, 0, 2), 16, v_int4))
+        assert np.array_equal(kh, paged.quantize_contiguous(k.transpose(1, 0, 2), 16, codec=kc))
+        assert np.array_equal(vh, paged.quantize_contiguous(v.transpose(1, 0, 2), 16, codec=vc))
+        # and every tile by hand: codes of the rows, zero bytes past them
+        for j, b in enumerate(tables[s]):
+            n = min(16, c - 16 * j)
+            for h in range(2):
+                rows = v[16 * j:16 * j + n, h]
+                codes = (quant.quantize_int8_asym(rows)[0] if vc == "i8a" else
+                         quant.quantize_fp8_e4m3(rows)[0] if vc == "fp8" else None)
+                if codes is not None:
+                    assert np.array_equal(pool.v_codes[b, h][:, :n], codes.T)
+                    assert not pool.v_codes[b, h][:, n:].any()
 
 
 def test_rows_beyond_context_are_zero_and_ignored():

@@ -231,3 +231,120 @@ def test_page_literal_rule_differs_from_reading():
         e_rne += np.abs(codes * float(s) - t.astype(np.float64)).mean()
     assert diff / tiles.size > 0.3
     assert e_lit > 1.5 * e_rne
+
+
+# ------------------------------------------------------------ FP8 E4M3 ---
+
+def test_e4m3_table_hand_values_and_torch():
+    """Code values from the format's definition at hand-checked points, and
+    the whole table equal to torch's float8_e4m3fn decoding."""
+    import torch
+    T = quant.E4M3_TABLE
+    assert T[0x38] == 1.0 and T[0x7E] == 448.0 and T[0x01] == 2.0 ** -9
+    assert T[0x08] == 2.0 ** -6 and T[0x07] == 7 * 2.0 ** -9 and T[0x39] == 1.125
+    assert T[0xB8] == -1.0 and T[0x80] == 0.0 and np.signbit(T[0x80])
+    assert np.isnan(T[0x7F]) and np.isnan(T[0xFF])
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.nan_to_num(ref, nan=7.0), np.nan_to_num(T, nan=7.0))
+    pos = T[:0x7F]
+    assert np.all(np.diff(pos) > 0)                     # codes 0..0x7E increase
+
+
+def test_e4m3_hand_examples():
+    """Ties go to the even code, beyond 448 saturates, the sign of zero stays."""
+    cases = [(1.0625, 0x38),        # halfway 1 (0x38) / 1.125 (0x39): even 0x38
+             (1.1875, 0x3A),        # halfway 1.125 / 1.25: even 0x3A
+             (2.0 ** -10, 0x00),    # halfway 0 / 2^-9: even 0x00
+             (3 * 2.0 ** -10, 0x02),   # halfway 2^-9 / 2^-8: even 0x02
+             (432.0, 0x7E),         # halfway 416 (0x7D) / 448 (0x7E): even 0x7E
+             (440.0, 0x7E), (500.0, 0x7E), (1e6, 0x7E), (-1e6, 0xFE),
+             (-0.0, 0x80), (0.0, 0x00), (-1.0, 0xB8), (2.0 ** -11, 0x00), (-(2.0 ** -11), 0x80)]
+    for x, c in cases:
+        assert int(quant.e4m3_codes(np.float32(x))) == c, x
+
+
+def test_e4m3_codes_match_torch_and_exact_nearest():
+    """Every fp16 value in [-448, 448] and random fp32 quotients: the code
+    equals torch's float8_e4m3fn cast (round to nearest even), and on a
+    sample equals the nearest value found with exact rationals."""
+    import torch
+    xs = np.concatenate([ALL_FP16_BITS.view(np.float16), (ALL_FP16_BITS[1:] | 0x8000).view(np.float16)])
+    xs = xs[np.abs(xs.astype(np.float32)) <= 448].astype(np.float32)
+    r = np.random.default_rng(3).uniform(-448, 448, 200000).astype(np.float32)
+    for x in (xs, r):
+        want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(quant.e4m3_codes(x), want)
+    vals = [Fraction(v) for v in quant.E4M3_TABLE[:0x7F].tolist()]
+    for x in r[:3000].tolist():
+        a = abs(Fraction(x))
+        best = min(range(0x7F), key=lambda c: (abs(vals[c] - a), c % 2))
+        assert quant.e4m3_codes(np.float32(x)) & 0x7F == best, x
+
+
+def test_fp8_tile_range_and_roundtrip_bound():
+    """The tile's largest element maps to +-448; |x_hat - x| is at most half
+    a step of the E4M3 grid at x / s (2^-4 relative, 2^-10 absolute below
+    2^-6) times s, plus the fp32 quotient's rounding."""
+    rng = np.random.default_rng(5)
+    for spread in (1.0, 1e-3, 300.0):
+        for tile in _rand_tiles(rng, 40, 16, 64, spread):
+            codes, s = quant.quantize_fp8_e4m3(tile)
+            x = tile.astype(np.float64)
+            assert float(s) > 0
+            vmax = np.max(np.abs(quant.E4M3_TABLE[codes]))
+            assert vmax == 448.0
+            xh = quant.dequantize_fp8_e4m3(codes, s)
+            t = np.abs(x) / float(s)
+            bound = float(s) * np.maximum(t * 2.0 ** -4, 2.0 ** -10) + np.abs(x) * 2.0 ** -22
+            assert np.all(np.abs(xh - x) <= bound)
+
+
+def test_fp8_zero_and_tiny_tiles():
+    z = np.zeros((4, 8), np.float16)
+    codes, s = quant.quantize_fp8_e4m3(z)
+    assert float(s) == 0 and not codes.any()
+    tiny = np.full((2, 8), np.float16(2.0 ** -24))      # absmax/448 rounds to fp16 zero
+    codes, s = quant.quantize_fp8_e4m3(tiny)
+    assert float(s) == 0 and not codes.any()
+    # a scale that rounds down makes |x| / s exceed 448: saturated, not NaN
+    x = np.array([[449.0, 1.0]], np.float16)
+    codes, s = quant.quantize_fp8_e4m3(x)
+    assert float(x[0, 0]) / float(s) > 448 and int(codes[0, 0]) == 0x7E
+
+
+# ------------------------------------------------------- INT8 asymmetric ---
+
+@pytest.mark.parametrize("zp", [0, 1, 100, 128, 255])
+def test_int8_asym_element_map_exact(zp):
+    """clamp(RNE(exact x/s + zp), 0, 255) for sampled scales and every fp16 x,
+    by exact integer arithmetic (the fp32 route rounds only where it cannot
+    change the result)."""
+    scales = _scale_sample()[1::2]
+    xs = np.concatenate([ALL_FP16_BITS.view(np.float16),
+                         (ALL_FP16_BITS[1:] | 0x8000).view(np.float16)])
+    xi = _fp16_to_int24(xs)
+    for s in scales:
+        si = _fp16_to_int24(np.array([s], np.float16))[0]
+        expect = np.clip(_rne_div_int(xi + zp * si, np.full_like(xi, si)), 0, 255)
+        got = quant.int8_asym_codes(xs.astype(np.float32), s, zp).astype(np.int64)
+        assert np.array_equal(got, expect), (float(s), zp)
+
+
+def test_int8_asym_scale_zero_point_and_bound():
+    """scale = fp16 of the widened range / 255 (exact rationals), zero point
+    = RNE(-lo / s), 0 maps to the zero point exactly, and every in-range
+    value comes back within s / 2."""
+    rng = np.random.default_rng(9)
+    for spread, shift in ((1.0, 0.0), (0.01, 0.5), (50.0, -20.0), (1.0, 3.0)):
+        for tile in (rng.standard_normal((30, 16, 64)) * spread + shift).astype(np.float16):
+            codes, s, zp = quant.quantize_int8_asym(tile)
+            x = tile.astype(np.float64)
+            lo, hi = min(0.0, x.min()), max(0.0, x.max())
+            assert Fraction(float(s)) == _fp16_rne((Fraction(hi) - Fraction(lo)) / 255)
+            assert int(zp) == int(np.clip(_rne_div_int(np.array([_fp16_to_int24(np.array([-lo], np.float16))[0]]),
+                                                        _fp16_to_int24(np.array([s], np.float16)))[0], 0, 255))
+            assert int(quant.int8_asym_codes(np.float32([0.0]), s, zp)[0]) == int(zp)
+            xh = quant.dequantize_int8_asym(codes, s, zp)
+            inside = (x / float(s) + int(zp) >= -0.5) & (x / float(s) + int(zp) <= 255.5)
+            assert np.all(np.abs(xh - x)[inside] <= float(s) / 2 * (1 + 2.0 ** -10))
+            assert inside.mean() > 0.99
