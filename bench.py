@@ -52,7 +52,7 @@ def cpu_baseline(setup, seconds):
     from threadpoolctl import threadpool_limits
 
     from oracle import attention, paged
-    from paged_block_quantized_amd import runner
+    from paged_block_quantized_amd import runner, workloads as W
 
     w = setup.w
     bs = w.block_size
@@ -62,7 +62,8 @@ def cpu_baseline(setup, seconds):
         ctx = int(setup.ctx[s])
         hk, hv = runner.sequence_history(setup, s)
         nb = (ctx + bs - 1) // bs
-        pool = paged.PoolArrays(nb, w.num_kv_heads, bs, w.head_dim, w.v_codec == "i4")
+        pool = paged.PoolArrays(nb, w.num_kv_heads, bs, w.head_dim, k_codec=W.k_codec_of(w),
+                                v_codec=w.v_codec)
         paged.store_range(pool, list(range(nb)), hk, hv, 0, ctx - 1)
         prepared.append((s, ctx, nb, pool, hk, hv, setup.q[s].cpu().numpy()))
     with threadpool_limits(limits=1):
@@ -93,7 +94,7 @@ def swap_plan_bytes(pool, plan):
     the held rows of each head of the tail slots (K and V, fp16)."""
     H, bs, D = pool.num_kv_heads, pool.block_size, pool.head_dim
     kb = H * bs * D
-    block = kb + (kb // 2 if pool.v_int4 else kb) + 4 * H + (H if pool.v_int4 else 0)
+    block = kb + (kb // 2 if pool.v_int4 else kb) + 4 * H + (H if pool.v_zp_used else 0)
     total = 0
     for kind, _, _, rows in plan:
         total += block if kind < 2 else 4 * H * rows * D
@@ -327,8 +328,9 @@ def main():
             "workload": w.name, "layers": 1, "num_seqs": S,
             "context": int(setup.ctx.max()) if w.ctx_kind == "fixed" else [int(setup.ctx.min()), int(setup.ctx.max())],
             "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-            "block_size": w.block_size, "k_codec": "int8_sym",
-            "v_codec": "int4_asym" if w.v_codec == "i4" else "int8_sym",
+            "block_size": w.block_size,
+            "k_codec": {"i8": "int8_sym", "fp8": "fp8_e4m3"}[W.k_codec_of(w)],
+            "v_codec": {"i8": "int8_sym", "i4": "int4_asym", "i8a": "int8_asym", "fp8": "fp8_e4m3"}[w.v_codec],
             "partition": setup.partition, "shared_prefix": w.prefix,
             "pool_copies_rotated": R,
         },

@@ -54,6 +54,8 @@ typedef enum kv_status {
 } kv_status;
 
 /* Codecs, one per (block, head) tile of block_size x head_dim values.
+ * Supported (k_codec, v_codec) pairs: (I8_SYM, I8_SYM), (I8_SYM, I4_ASYM),
+ * (I8_SYM, I8_ASYM) and (FP8_E4M3, FP8_E4M3).
  * INT4 packing is along the tile's contiguous axis: tokens for V (see the
  * layout under kv_pool_sizes).
  *   KV_CODEC_I8_SYM : int8 codes in [-127, 127], fp16 scale = fp16(absmax/127)
@@ -69,8 +71,22 @@ typedef enum kv_status {
  *                     ([yunthe] Q(x) with bits = 4).
  *   A block whose statistics give scale 0 stores scale 0, zero point 0 and
  *   all-zero codes.  Rows a block does not hold yet are zero bytes.
+ *   KV_CODEC_FP8_E4M3: OCP FP8 E4M3 bytes (4 exponent bits of bias 7, 3
+ *                     mantissa bits, largest finite 448) with an fp16 scale
+ *                     = fp16(absmax / 448) over the rows held; code = E4M3 of
+ *                     the fp32 quotient x / scale, nearest with ties to the
+ *                     even code, saturated at +-448; x_hat = value * scale.
+ *                     [yunthe] "vLLM deployment" names the format for the
+ *                     cache; the scale granularity is this library's.
+ *   KV_CODEC_I8_ASYM : u8 codes in [0, 255] with scale and zero point as
+ *                     I4_ASYM with 255 levels ([yunthe] Q(x), bits = 8); V only.
  *   Dequantization is ([yunthe]) x_hat = (code - zero point) * scale. */
-typedef enum kv_codec { KV_CODEC_I8_SYM = 0, KV_CODEC_I4_ASYM = 1 } kv_codec;
+typedef enum kv_codec {
+    KV_CODEC_I8_SYM = 0,
+    KV_CODEC_I4_ASYM = 1,
+    KV_CODEC_FP8_E4M3 = 2,
+    KV_CODEC_I8_ASYM = 3
+} kv_codec;
 
 /* Shape of one layer's block pool ([tbr8] §4 PagedKVCacheManager.__init__). */
 typedef struct kv_pool_desc {
@@ -78,21 +94,23 @@ typedef struct kv_pool_desc {
     int32_t block_size;   /* tokens per block: 16 or 32 ([tbr8] §2) */
     int32_t num_kv_heads; /* Hkv >= 1 */
     int32_t head_dim;     /* D: 64 or 128 */
-    int32_t k_codec;      /* must be KV_CODEC_I8_SYM ([tbr8] §5: K in INT8) */
-    int32_t v_codec;      /* KV_CODEC_I8_SYM or KV_CODEC_I4_ASYM */
+    int32_t k_codec;      /* KV_CODEC_I8_SYM ([tbr8] §5: K in INT8) or FP8_E4M3 */
+    int32_t v_codec;      /* I8_SYM, I4_ASYM, I8_ASYM or FP8_E4M3 (pairs above) */
     int32_t max_seqs;     /* tail slots = most sequences alive at once, >= 1 */
 } kv_pool_desc;
 
 /* Byte sizes of the device arrays of one pool (all row-major):
- *   k_codes  int8  [N, Hkv, bs, D]      token-major K tiles ([tbr8] §4)
- *   v_codes  int8  [N, Hkv, D, bs]      (I8_SYM) dim-major V tiles
+ *   k_codes  int8  [N, Hkv, bs, D]      token-major K tiles ([tbr8] §4;
+ *                                        u8 E4M3 bytes for FP8_E4M3)
+ *   v_codes  int8  [N, Hkv, D, bs]      (I8_SYM; u8 for I8_ASYM and FP8_E4M3)
+ *                                        dim-major V tiles
  *            uint8 [N, Hkv, D, bs / 2]  (I4_ASYM, two consecutive tokens per
  *                                        byte, the earlier in the low nibble)
  *            The pages show only the K pool; V is stored dim-major so that a
  *            sum over a block's tokens reads one contiguous row per dim.
  *   k_scale  fp16  [N, Hkv]
  *   v_scale  fp16  [N, Hkv]
- *   v_zp     uint8 [N, Hkv]  (0 bytes unless I4_ASYM)
+ *   v_zp     uint8 [N, Hkv]  (0 bytes unless I4_ASYM or I8_ASYM)
  *   tail_k   fp16  [max_seqs, Hkv, bs, D]  exact rows of each sequence's
  *   tail_v   fp16  [max_seqs, Hkv, bs, D]  partially filled last block
  * Every array must be 16-byte aligned. */
@@ -100,7 +118,8 @@ typedef struct kv_pool_sizes {
     size_t k_codes, v_codes, k_scale, v_scale, v_zp, tail_k, tail_v;
 } kv_pool_sizes;
 
-/* Device pointers to the arrays above (v_zp may be NULL for I8_SYM V). */
+/* Device pointers to the arrays above (v_zp may be NULL when V has no zero
+ * point). */
 typedef struct kv_pool_mem {
     void* k_codes;
     void* v_codes;

@@ -19,7 +19,7 @@ KV_OK, KV_ERR_INVALID, KV_ERR_NO_BLOCKS, KV_ERR_UNKNOWN_SEQ, KV_ERR_STATE, \
 STATUS_NAMES = {KV_OK: "ok", KV_ERR_INVALID: "invalid", KV_ERR_NO_BLOCKS: "no_blocks",
                 KV_ERR_UNKNOWN_SEQ: "unknown_seq", KV_ERR_STATE: "state",
                 KV_ERR_NO_SLOTS: "no_slots", KV_ERR_HIP: "hip"}
-KV_CODEC_I8_SYM, KV_CODEC_I4_ASYM = 0, 1
+KV_CODEC_I8_SYM, KV_CODEC_I4_ASYM, KV_CODEC_FP8_E4M3, KV_CODEC_I8_ASYM = 0, 1, 2, 3
 KV_COPY_BLOCK, KV_COPY_SLOT = 0, 1
 KV_SWAP_BLOCK_OUT, KV_SWAP_BLOCK_IN, KV_SWAP_SLOT_OUT, KV_SWAP_SLOT_IN = range(4)
 

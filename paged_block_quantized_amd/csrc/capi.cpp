@@ -30,9 +30,9 @@ kv_status check_device_desc(const kv_pool_desc* d) {
     if (d->num_kv_heads < 1 || d->num_kv_heads > 65535)
         return fail(KV_ERR_INVALID, "num_kv_heads must be in [1, 65535]");
     if (d->max_seqs < 1) return fail(KV_ERR_INVALID, "max_seqs must be >= 1");
-    if (d->k_codec != KV_CODEC_I8_SYM) return fail(KV_ERR_INVALID, "k_codec must be KV_CODEC_I8_SYM");
-    if (d->v_codec != KV_CODEC_I8_SYM && d->v_codec != KV_CODEC_I4_ASYM)
-        return fail(KV_ERR_INVALID, "v_codec must be KV_CODEC_I8_SYM or KV_CODEC_I4_ASYM");
+    if (!codec_pair_supported(d->k_codec, d->v_codec))
+        return fail(KV_ERR_INVALID, "unsupported (k_codec, v_codec): use (I8_SYM, I8_SYM | I4_ASYM | I8_ASYM) "
+                                    "or (FP8_E4M3, FP8_E4M3)");
     return KV_OK;
 }
 
@@ -41,8 +41,8 @@ kv_status check_mem(const kv_pool_desc* d, const kv_pool_mem* m, bool need_tail)
     const void* req[] = {m->k_codes, m->v_codes, m->k_scale, m->v_scale};
     for (const void* p : req)
         if (!p || !aligned16(p)) return fail(KV_ERR_INVALID, "pool arrays must be non-NULL and 16-byte aligned");
-    if (d->v_codec == KV_CODEC_I4_ASYM && (!m->v_zp || !aligned16(m->v_zp)))
-        return fail(KV_ERR_INVALID, "v_zp must be non-NULL and 16-byte aligned for INT4 V");
+    if (codec_has_zp(d->v_codec) && (!m->v_zp || !aligned16(m->v_zp)))
+        return fail(KV_ERR_INVALID, "v_zp must be non-NULL and 16-byte aligned for an asymmetric V codec");
     if (need_tail && (!m->tail_k || !m->tail_v || !aligned16(m->tail_k) || !aligned16(m->tail_v)))
         return fail(KV_ERR_INVALID, "tail slots must be non-NULL and 16-byte aligned");
     return KV_OK;
@@ -78,7 +78,7 @@ kv_status check_swap_plan(const kv_pool_desc* d, const kv_pool_desc* h, const kv
                           int32_t n, bool* has_slots, int64_t* max_bytes) {
     const int64_t tile = (int64_t)d->block_size * d->head_dim;
     const int64_t kb = tile * d->num_kv_heads;
-    const int64_t block_bytes = kb + (d->v_codec == KV_CODEC_I4_ASYM ? kb / 2 : kb);
+    const int64_t block_bytes = kb + (codec_packed4(d->v_codec) ? kb / 2 : kb);
     // spaces: device blocks, host blocks, device slots, host slots
     const int32_t size[4] = {d->num_blocks, h->num_blocks, d->max_seqs, h->max_seqs};
     std::vector<uint8_t> mark[4];
@@ -215,6 +215,7 @@ kv_status decode_impl(const kv_pool_desc* d, const kv_pool_mem* m, const AppendA
     a.num_kv_heads = d->num_kv_heads;
     a.head_dim = d->head_dim;
     a.v_codec = d->v_codec;
+    a.k_codec = d->k_codec;
     a.k_codes = (const int8_t*)m->k_codes;
     a.v_codes = (const uint8_t*)m->v_codes;
     a.k_scale = (const uint16_t*)m->k_scale;
@@ -244,6 +245,7 @@ kv_status decode_impl(const kv_pool_desc* d, const kv_pool_mem* m, const AppendA
         sa.num_kv_heads = d->num_kv_heads;
         sa.head_dim = d->head_dim;
         sa.v_codec = d->v_codec;
+        sa.k_codec = d->k_codec;
         sa.k_codes = (int8_t*)m->k_codes;
         sa.v_codes = (uint8_t*)m->v_codes;
         sa.k_scale = (uint16_t*)m->k_scale;
@@ -284,10 +286,10 @@ kv_status kv_pool_bytes(const kv_pool_desc* d, kv_pool_sizes* out) {
     const size_t tile = (size_t)d->block_size * d->head_dim;
     const size_t bh = (size_t)d->num_blocks * d->num_kv_heads;
     out->k_codes = bh * tile;
-    out->v_codes = d->v_codec == KV_CODEC_I4_ASYM ? bh * tile / 2 : bh * tile;
+    out->v_codes = pbq::codec_packed4(d->v_codec) ? bh * tile / 2 : bh * tile;
     out->k_scale = bh * 2;
     out->v_scale = bh * 2;
-    out->v_zp = d->v_codec == KV_CODEC_I4_ASYM ? bh : 0;
+    out->v_zp = pbq::codec_has_zp(d->v_codec) ? bh : 0;
     out->tail_k = (size_t)d->max_seqs * d->num_kv_heads * tile * 2;
     out->tail_v = out->tail_k;
     return KV_OK;
@@ -306,6 +308,7 @@ kv_status kv_copy_blocks(const kv_pool_desc* d, const kv_pool_mem* m,
     a.num_kv_heads = d->num_kv_heads;
     a.head_dim = d->head_dim;
     a.v_codec = d->v_codec;
+    a.k_codec = d->k_codec;
     a.k_codes = (int8_t*)m->k_codes;
     a.v_codes = (uint8_t*)m->v_codes;
     a.k_scale = (uint16_t*)m->k_scale;
@@ -365,6 +368,7 @@ kv_status kv_swap_blocks(const kv_pool_desc* d, const kv_pool_mem* m, const kv_p
     a.num_kv_heads = d->num_kv_heads;
     a.head_dim = d->head_dim;
     a.v_codec = d->v_codec;
+    a.k_codec = d->k_codec;
     a.dev_blocks = d->num_blocks;
     a.dev_slots = d->max_seqs;
     a.host_blocks = hd->num_blocks;
@@ -395,6 +399,7 @@ kv_status kv_quantize_store(const kv_pool_desc* d, const kv_pool_mem* m,
     a.num_kv_heads = d->num_kv_heads;
     a.head_dim = d->head_dim;
     a.v_codec = d->v_codec;
+    a.k_codec = d->k_codec;
     a.k_codes = (int8_t*)m->k_codes;
     a.v_codes = (uint8_t*)m->v_codes;
     a.k_scale = (uint16_t*)m->k_scale;

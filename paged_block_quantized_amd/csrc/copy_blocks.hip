@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyArgs a) {
     const int tid = threadIdx.x;
     const int H = a.num_kv_heads;
     const int64_t tile = (int64_t)a.block_size * a.head_dim;
-    const bool v4 = a.v_codec == KV_CODEC_I4_ASYM;
+    const bool v4 = codec_packed4(a.v_codec), zp = codec_has_zp(a.v_codec);
     if (c.kind == KV_COPY_BLOCK) {
         const int64_t kb = tile * H;
         const int64_t vb = v4 ? kb / 2 : kb;
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyArgs a) {
         for (int g = tid; g < H; g += blockDim.x) {
             a.k_scale[(int64_t)c.dst * H + g] = a.k_scale[(int64_t)c.src * H + g];
             a.v_scale[(int64_t)c.dst * H + g] = a.v_scale[(int64_t)c.src * H + g];
-            if (v4) a.v_zp[(int64_t)c.dst * H + g] = a.v_zp[(int64_t)c.src * H + g];
+            if (zp) a.v_zp[(int64_t)c.dst * H + g] = a.v_zp[(int64_t)c.src * H + g];
         }
     } else if (c.kind == KV_COPY_SLOT) {
         const int64_t sb = tile * H * 2;

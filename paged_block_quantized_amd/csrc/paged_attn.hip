@@ -68,6 +68,44 @@ __device__ __forceinline__ f16x2 as_h2(uint32_t x) { return __builtin_bit_cast(f
 __device__ __forceinline__ f16x2 perm_lo(uint32_t w) { return as_h2(__builtin_amdgcn_perm(kF16Hi, w, kSelLo)); }
 __device__ __forceinline__ f16x2 perm_hi(uint32_t w) { return as_h2(__builtin_amdgcn_perm(kF16Hi, w, kSelHi)); }
 
+// Byte codes of the other codecs, four to a dword, become fp16 pairs the
+// same way, each pair affine in its codes with a unit and a bias that come
+// off outside the inner products: x_hat = unit * (pair - bias) * scale.
+//   I8_SYM  : 1152 + c (c xor 0x80 under 0x64), unit 1, bias 1152
+//   I8_ASYM : 1024 + u (u under 0x64), unit 1, bias 1024 + zero point
+//   FP8_E4M3: value(c) * 2^-8 exactly, unit 256, bias 0: the byte placed in
+//             the high byte of a half, shifted right by one with its sign
+//             kept and bit 14 cleared, puts E4M3's exponent (bias 7) and
+//             mantissa into fp16's fields (bias 15), subnormals included.
+constexpr uint32_t kSelF8Lo = 0x010C000Cu;   // bytes 0,1 -> high bytes of two halves
+constexpr uint32_t kSelF8Hi = 0x030C020Cu;   // bytes 2,3
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f8_pair(uint32_t w, uint32_t sel) {
+    const s16x2 t = __builtin_bit_cast(s16x2, __builtin_amdgcn_perm(0u, w, sel)) >> (s16x2){1, 1};
+    return __builtin_bit_cast(uint32_t, t) & 0xBFFFBFFFu;
+}
+template <int C>
+__device__ __forceinline__ uint32_t pair_lo(uint32_t w) {   // bytes 0, 1
+    if constexpr (C == KV_CODEC_FP8_E4M3) return f8_pair(w, kSelF8Lo);
+    else if constexpr (C == KV_CODEC_I8_SYM) return __builtin_amdgcn_perm(kF16Hi, w ^ 0x80808080u, kSelLo);
+    else return __builtin_amdgcn_perm(kF16Hi, w, kSelLo);
+}
+template <int C>
+__device__ __forceinline__ uint32_t pair_hi(uint32_t w) {   // bytes 2, 3
+    if constexpr (C == KV_CODEC_FP8_E4M3) return f8_pair(w, kSelF8Hi);
+    else if constexpr (C == KV_CODEC_I8_SYM) return __builtin_amdgcn_perm(kF16Hi, w ^ 0x80808080u, kSelHi);
+    else return __builtin_amdgcn_perm(kF16Hi, w, kSelHi);
+}
+template <int C>
+constexpr float code_unit() { return C == KV_CODEC_FP8_E4M3 ? 256.f : 1.f; }
+// bias of a pair given the block's zero point (asymmetric codecs)
+template <int C>
+__device__ __forceinline__ float code_bias(float zp) {
+    if constexpr (C == KV_CODEC_FP8_E4M3) return 0.f;
+    else if constexpr (C == KV_CODEC_I8_SYM) return kI8Bias;
+    else return kI4Bias + zp;   // INT4 nibbles and INT8 asymmetric bytes: 1024 + u
+}
+
 #ifndef PBQ_MHA_WAVES_PER_EU
 #define PBQ_MHA_WAVES_PER_EU 1
 #endif
@@ -151,9 +189,12 @@ inline dim3 grid_dims(int parts, int heads, int seqs) {
 // row of the block's tokens.  The softmax weights of a block (times its V
 // scale) are broadcast to scalar registers with readlane and every lane
 // accumulates its own dims, so no lane combination is needed for V.
-template <int BS, int D, bool V4, int NW, bool FUSED>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(FUSED ? (BS == 16 ? 5 : (V4 ? 4 : 3)) : PBQ_MHA_WAVES_PER_EU)))
+template <int BS, int D, int CP, int NW, bool FUSED>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(FUSED ? (BS == 16 ? 5 : (codec_packed4(CP % 4) ? 4 : 3)) : PBQ_MHA_WAVES_PER_EU)))
 void attn_partition_mha(AttnArgs a) {
+    constexpr int KC = CP / 4, VC = CP % 4;
+    constexpr bool V4 = codec_packed4(VC);
+    constexpr bool VZP = codec_has_zp(VC);
     constexpr int LPR = D / 16;    // K: lanes per token row (16 dims each)
     constexpr int RPI = 64 / LPR;  // K: token rows per wave access
     constexpr int NR = BS / RPI;   // K: rows per lane per block
@@ -201,14 +242,14 @@ void attn_partition_mha(AttnArgs a) {
         const int last = nblk - 1;
         const int slot = a.tail_slots[s], phys = tab[last];
         if (w == 0) {
-            const TileScales ts = store_tile<BS, D, V4, true, true, false>(
+            const TileScales ts = store_tile<BS, D, CP, true, true, false>(
                 t, h, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, false);
             if (lane == 0) {
                 s_tscale[0] = ts.k_scale;
                 s_tscale[3] = ts.prev;
             }
         } else {
-            const TileScales ts = store_tile<BS, D, V4, true, false, true>(
+            const TileScales ts = store_tile<BS, D, CP, true, false, true>(
                 t, h, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, false);
             if (lane == 0) {
                 s_tscale[1] = ts.v_scale;
@@ -232,10 +273,11 @@ void attn_partition_mha(AttnArgs a) {
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) qs += (float)q0[e] + (float)q1[e];
-        qbias = kI8Bias * qs;
+        qbias = code_bias<KC>(0.f) * qs;
     }
 
-    const float c2 = a.sm_scale * kLog2e;
+    const float c2 = a.sm_scale * kLog2e * code_unit<KC>();
+    constexpr float vunit = code_unit<VC>();
     float m = -INFINITY, l = 0.f, zacc = 0.f;
     float acc[DPL][2];
 #pragma unroll
@@ -251,9 +293,8 @@ void attn_partition_mha(AttnArgs a) {
             float d = 0.f;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const uint32_t u = r.k[j][k] ^ 0x80808080u;
-                d = __builtin_amdgcn_fdot2(perm_lo(u), q2[2 * k], d, false);
-                d = __builtin_amdgcn_fdot2(perm_hi(u), q2[2 * k + 1], d, false);
+                d = __builtin_amdgcn_fdot2(as_h2(pair_lo<KC>(r.k[j][k])), q2[2 * k], d, false);
+                d = __builtin_amdgcn_fdot2(as_h2(pair_hi<KC>(r.k[j][k])), q2[2 * k + 1], d, false);
             }
             sc[j] = d - qbias;
         }
@@ -313,8 +354,7 @@ void attn_partition_mha(AttnArgs a) {
             } else {
 #pragma unroll
                 for (int c = 0; c < VW; ++c) {   // tokens 4c .. 4c+3
-                    const uint32_t u = r.v[k][c] ^ 0x80808080u;
-                    const f16x2 a0 = perm_lo(u), a1 = perm_hi(u);
+                    const f16x2 a0 = as_h2(pair_lo<VC>(r.v[k][c])), a1 = as_h2(pair_hi<VC>(r.v[k][c]));
                     const int t = 4 * c;
                     acc[k][0] = __builtin_fmaf(sp[t + 0], (float)a0[0], acc[k][0]);
                     acc[k][1] = __builtin_fmaf(sp[t + 1], (float)a0[1], acc[k][1]);
@@ -379,8 +419,8 @@ void attn_partition_mha(AttnArgs a) {
 
         auto compute = [&](const Regs& r, int i) {
             compute_blk(r, base + i, bits_to_f16f((uint16_t)readlane(sk, i)) * c2,
-                        bits_to_f16f((uint16_t)readlane(sv, i)),
-                        V4 ? kI4Bias + (float)readlane(zp, i) : kI8Bias);
+                        bits_to_f16f((uint16_t)readlane(sv, i)) * vunit,
+                        code_bias<VC>((float)readlane(zp, i)));
         };
 
         // scale bits of the staged blocks, issued after the first codes; only
@@ -390,7 +430,7 @@ void attn_partition_mha(AttnArgs a) {
             const int64_t t = (int64_t)id * H + h;
             sk = a.k_scale[t];
             sv = a.v_scale[t];
-            if constexpr (V4) zp = a.v_zp[t];
+            if constexpr (VZP) zp = a.v_zp[t];
         };
         pipelined<PBQ_MHA_DEPTH, Regs>(cnt, load, compute, scales);
     }
@@ -400,14 +440,14 @@ void attn_partition_mha(AttnArgs a) {
             const TileStoreArgs t{const_cast<int8_t*>(a.k_codes), const_cast<uint8_t*>(a.v_codes),
                                   const_cast<uint16_t*>(a.k_scale), const_cast<uint16_t*>(a.v_scale),
                                   const_cast<uint8_t*>(a.v_zp), a.tail_k, a.tail_v, a.k_new, a.v_new, H};
-            write_stored_tile<BS, D, V4>(t, w, h, a.tail_slots[s], s, ctx - 1, tab[nblk - 1], s_tile, s_tile + KT,
+            write_stored_tile<BS, D, CP>(t, w, h, a.tail_slots[s], s, ctx - 1, tab[nblk - 1], s_tile, s_tile + KT,
                                          s_tscale);
         }
         if (w == NW - 1) {
             Regs r;
             load_tile((const int8_t*)s_tile, s_tile + KT, r);
-            compute_blk(r, b_end, bits_to_f16f((uint16_t)s_tscale[0]) * c2, bits_to_f16f((uint16_t)s_tscale[1]),
-                        V4 ? kI4Bias + (float)s_tscale[2] : kI8Bias);
+            compute_blk(r, b_end, bits_to_f16f((uint16_t)s_tscale[0]) * c2,
+                        bits_to_f16f((uint16_t)s_tscale[1]) * vunit, code_bias<VC>((float)s_tscale[2]));
         }
     }
 
@@ -567,8 +607,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // group (query i: sequence i / G, head kvh * G + i % G), so each of the
 // prefix's tiles is read once per 16 queries instead of once per sequence.
 // Results always go to the workspace, for the reduce.
-template <int BS, int D, bool V4, int NW, bool FUSED, bool SHARED = false>
+template <int BS, int D, int CP, int NW, bool FUSED, bool SHARED = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA_WAVES_PER_EU))) void attn_partition_gqa(AttnArgs a) {
+    constexpr int KC = CP / 4, VC = CP % 4;
+    constexpr bool V4 = codec_packed4(VC);
+    constexpr bool VZP = codec_has_zp(VC);
     static_assert(!(FUSED && SHARED), "the shared prefix holds no current token");
     static_assert(BS == 16 || BS == 32, "block size");
     constexpr bool STAGED = FUSED ? PBQ_GQA_STAGE_FUSED : PBQ_GQA_STAGE;
@@ -634,10 +677,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
         }
         qs += shfl_xor_f(qs, 16);
         qs += shfl_xor_f(qs, 32);
-        qbias = kI8Bias * qs;
+        qbias = code_bias<KC>(0.f) * qs;
     }
 
-    const float c2 = a.sm_scale * kLog2e;
+    const float c2 = a.sm_scale * kLog2e * code_unit<KC>();
+    constexpr float vunit = code_unit<VC>();
     float m = -INFINITY, l = 0.f, zacc = 0.f;
     f32x4 acc[DT];
 #pragma unroll
@@ -689,10 +733,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
             sc[mt] = (f32x4)0.f;
 #pragma unroll
             for (int j = 0; j < KS; ++j) {
-                const uint32_t u0 = r.k[mt][j / 2][2 * (j & 1)] ^ 0x80808080u;
-                const uint32_t u1 = r.k[mt][j / 2][2 * (j & 1) + 1] ^ 0x80808080u;
-                const uint32_t a4[4] = {__builtin_amdgcn_perm(kF16Hi, u0, kSelLo), __builtin_amdgcn_perm(kF16Hi, u0, kSelHi),
-                                        __builtin_amdgcn_perm(kF16Hi, u1, kSelLo), __builtin_amdgcn_perm(kF16Hi, u1, kSelHi)};
+                const uint32_t w0 = r.k[mt][j / 2][2 * (j & 1)];
+                const uint32_t w1 = r.k[mt][j / 2][2 * (j & 1) + 1];
+                const uint32_t a4[4] = {pair_lo<KC>(w0), pair_hi<KC>(w0), pair_lo<KC>(w1), pair_hi<KC>(w1)};
                 const f16x8v aop = __builtin_bit_cast(f16x8v, a4);
                 sc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, qop[j], sc[mt], 0, 0, 0);
             }
@@ -737,7 +780,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
         // the codes enter the MFMA as bias + u (exact fp16); the weighted
         // bias and zero point, (bias + zp) times the weights' sum, are the
         // same for every dim and come off once, at the end
-        zacc = __builtin_fmaf((V4 ? kI4Bias : kI8Bias) + zpv, psum, zacc);
+        if constexpr (VC != KV_CODEC_FP8_E4M3) zacc = __builtin_fmaf(code_bias<VC>(zpv), psum, zacc);
 
         // ---- O^T += (bias + V codes)^T P^T ---------------------------------
 #pragma unroll
@@ -751,11 +794,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
                 a4[2] = __builtin_amdgcn_perm(kF16Hi, hi, kSelLo);
                 a4[3] = __builtin_amdgcn_perm(kF16Hi, hi, kSelHi);
             } else {
-                const uint32_t u0 = r.v[t][0] ^ 0x80808080u, u1 = r.v[t][1] ^ 0x80808080u;
-                a4[0] = __builtin_amdgcn_perm(kF16Hi, u0, kSelLo);
-                a4[1] = __builtin_amdgcn_perm(kF16Hi, u0, kSelHi);
-                a4[2] = __builtin_amdgcn_perm(kF16Hi, u1, kSelLo);
-                a4[3] = __builtin_amdgcn_perm(kF16Hi, u1, kSelHi);
+                a4[0] = pair_lo<VC>(r.v[t][0]);
+                a4[1] = pair_hi<VC>(r.v[t][0]);
+                a4[2] = pair_lo<VC>(r.v[t][1]);
+                a4[3] = pair_hi<VC>(r.v[t][1]);
             }
             acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8v, a4), pop, acc[t], 0, 0, 0);
         }
@@ -777,14 +819,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
         const int last = nblk - 1;
         const int slot = a.tail_slots[s], phys = tab[last];
         if (w == 0) {
-            const TileScales ts = store_tile<BS, D, V4, true, true, false>(
+            const TileScales ts = store_tile<BS, D, CP, true, true, false>(
                 t, kvh, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, false);
             if (lane == 0) {
                 s_tscale[0] = ts.k_scale;
                 s_tscale[3] = ts.prev;
             }
         } else {
-            const TileScales ts = store_tile<BS, D, V4, true, false, true>(
+            const TileScales ts = store_tile<BS, D, CP, true, false, true>(
                 t, kvh, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, false);
             if (lane == 0) {
                 s_tscale[1] = ts.v_scale;
@@ -913,14 +955,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
             // replaced by 0 so that stale pool contents cannot reach the sums.
             if constexpr (BPS == 1) {
                 compute_step(r, st, bits_to_f16f((uint16_t)readlane(sk_l, i)) * c2,
-                             bits_to_f16f((uint16_t)readlane(sv_l, i)), (float)readlane(zp_l, i));
+                             bits_to_f16f((uint16_t)readlane(sv_l, i)) * vunit, (float)readlane(zp_l, i));
             } else {
                 const bool live1 = blk0 + st * BPS + 1 < blk_end;
                 const int k0 = readlane(sk_l, 2 * i), k1 = live1 ? readlane(sk_l, 2 * i + 1) : 0;
                 const int v0 = readlane(sv_l, 2 * i), v1 = live1 ? readlane(sv_l, 2 * i + 1) : 0;
                 const int z0 = readlane(zp_l, 2 * i), z1 = live1 ? readlane(zp_l, 2 * i + 1) : 0;
                 compute_step(r, st, bits_to_f16f((uint16_t)(my_blk ? k1 : k0)) * c2,
-                             bits_to_f16f((uint16_t)(my_blk ? v1 : v0)), (float)(my_blk ? z1 : z0));
+                             bits_to_f16f((uint16_t)(my_blk ? v1 : v0)) * vunit, (float)(my_blk ? z1 : z0));
             }
         };
 
@@ -928,7 +970,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
             const int64_t t = (int64_t)id_l * H + kvh;
             sk_l = a.k_scale[t];
             sv_l = a.v_scale[t];
-            if constexpr (V4) zp_l = a.v_zp[t];
+            if constexpr (VZP) zp_l = a.v_zp[t];
         };
         if constexpr (STAGED) {
             // SD stages: step i + SD is loaded into step i's stage once its
@@ -969,7 +1011,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
             const TileStoreArgs t{const_cast<int8_t*>(a.k_codes), const_cast<uint8_t*>(a.v_codes),
                                   const_cast<uint16_t*>(a.k_scale), const_cast<uint16_t*>(a.v_scale),
                                   const_cast<uint8_t*>(a.v_zp), a.tail_k, a.tail_v, a.k_new, a.v_new, H};
-            write_stored_tile<BS, D, V4>(t, w, kvh, a.tail_slots[s], s, ctx - 1, tab[nblk - 1], s_tile, s_tile + KT,
+            write_stored_tile<BS, D, CP>(t, w, kvh, a.tail_slots[s], s, ctx - 1, tab[nblk - 1], s_tile, s_tile + KT,
                                          s_tscale);
         }
         if (w == NW - 1) {
@@ -986,12 +1028,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
             load_step(pair ? a.k_codes + t0 * KT : lk, lk, pair ? a.v_codes + t0 * VT : lv, lv, r);
             const uint32_t ks0 = pair ? a.k_scale[t0] : s_tscale[0];
             const uint32_t vs0 = pair ? a.v_scale[t0] : s_tscale[1];
-            const uint32_t z0 = pair ? (V4 ? a.v_zp[t0] : 0u) : s_tscale[2];
+            const uint32_t z0 = pair ? (VZP ? a.v_zp[t0] : 0u) : s_tscale[2];
             // a lane group's block: `first` (my_blk 0) or the block after it,
             // which is the last block or lies past the end (masked)
             const bool mine_last = BPS == 1 || my_blk ? true : !pair;
             compute_step(r, st, bits_to_f16f((uint16_t)(mine_last ? s_tscale[0] : ks0)) * c2,
-                         bits_to_f16f((uint16_t)(mine_last ? s_tscale[1] : vs0)),
+                         bits_to_f16f((uint16_t)(mine_last ? s_tscale[1] : vs0)) * vunit,
                          (float)(mine_last ? s_tscale[2] : z0));
         }
     }
@@ -1109,16 +1151,16 @@ __global__ __launch_bounds__(64) void attn_reduce(AttnArgs a) {
 
 // Waves per work group of the MHA kernel: 8 when a partition holds at least
 // 64 blocks, else 4, so that each wave still streams several blocks.
-template <int BS, int D, bool V4>
+template <int BS, int D, int CP>
 hipError_t launch_mha(const AttnArgs& a, hipStream_t stream) {
     const dim3 grid = grid_dims(a.max_partitions - a.shared_parts, a.num_q_heads, a.num_seqs);
     const bool fused = a.k_new != nullptr;
     if (a.partition_blocks >= 64) {
-        if (fused) hipLaunchKernelGGL((attn_partition_mha<BS, D, V4, 8, true>), grid, dim3(64 * 8), 0, stream, a);
-        else hipLaunchKernelGGL((attn_partition_mha<BS, D, V4, 8, false>), grid, dim3(64 * 8), 0, stream, a);
+        if (fused) hipLaunchKernelGGL((attn_partition_mha<BS, D, CP, 8, true>), grid, dim3(64 * 8), 0, stream, a);
+        else hipLaunchKernelGGL((attn_partition_mha<BS, D, CP, 8, false>), grid, dim3(64 * 8), 0, stream, a);
     } else {
-        if (fused) hipLaunchKernelGGL((attn_partition_mha<BS, D, V4, 4, true>), grid, dim3(64 * 4), 0, stream, a);
-        else hipLaunchKernelGGL((attn_partition_mha<BS, D, V4, 4, false>), grid, dim3(64 * 4), 0, stream, a);
+        if (fused) hipLaunchKernelGGL((attn_partition_mha<BS, D, CP, 4, true>), grid, dim3(64 * 4), 0, stream, a);
+        else hipLaunchKernelGGL((attn_partition_mha<BS, D, CP, 4, false>), grid, dim3(64 * 4), 0, stream, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_partitions <= 1) return e;
@@ -1136,20 +1178,20 @@ hipError_t launch_mha(const AttnArgs& a, hipStream_t stream) {
 #ifndef PBQ_GQA_SINGLE_WAVES
 #define PBQ_GQA_SINGLE_WAVES 2
 #endif
-template <int BS, int D, bool V4>
+template <int BS, int D, int CP>
 hipError_t launch_gqa(const AttnArgs& a, hipStream_t stream) {
     const int G = a.num_q_heads / a.num_kv_heads;
     const int n_ht = (G + 15) / 16;
     const dim3 grid = grid_dims(a.max_partitions - a.shared_parts, a.num_kv_heads * n_ht, a.num_seqs);
     if (a.max_partitions == 1) {
         if (a.k_new != nullptr)
-            hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, PBQ_GQA_FUSED_WAVES, true>), grid,
+            hipLaunchKernelGGL((attn_partition_gqa<BS, D, CP, PBQ_GQA_FUSED_WAVES, true>), grid,
                                dim3(64 * PBQ_GQA_FUSED_WAVES), 0, stream, a);
         else
-            hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, PBQ_GQA_SINGLE_WAVES, false>), grid,
+            hipLaunchKernelGGL((attn_partition_gqa<BS, D, CP, PBQ_GQA_SINGLE_WAVES, false>), grid,
                                dim3(64 * PBQ_GQA_SINGLE_WAVES), 0, stream, a);
     } else {
-        hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, 4, false>), grid, dim3(64 * 4), 0, stream, a);
+        hipLaunchKernelGGL((attn_partition_gqa<BS, D, CP, 4, false>), grid, dim3(64 * 4), 0, stream, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_partitions <= 1) return e;
@@ -1163,26 +1205,29 @@ hipError_t launch_gqa(const AttnArgs& a, hipStream_t stream) {
 // The partitions of a prefix shared by every sequence: one grouped launch
 // over (shared partition, KV head x 16-query tile), before the per-sequence
 // partitions.
-template <int BS, int D, bool V4>
+template <int BS, int D, int CP>
 hipError_t launch_shared(const AttnArgs& a, hipStream_t stream) {
     const int NQ = a.num_seqs * (a.num_q_heads / a.num_kv_heads);
     const dim3 grid = grid_dims(a.shared_parts, a.num_kv_heads * ((NQ + 15) / 16), 1);
-    hipLaunchKernelGGL((attn_partition_gqa<BS, D, V4, 2, false, true>), grid, dim3(64 * 2), 0, stream, a);
+    hipLaunchKernelGGL((attn_partition_gqa<BS, D, CP, 2, false, true>), grid, dim3(64 * 2), 0, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_paged_attn(const AttnArgs& a, hipStream_t stream) {
-    const bool v4 = a.v_codec == KV_CODEC_I4_ASYM;
-    const bool gqa = a.num_q_heads != a.num_kv_heads;
-#define PBQ_ATTN(BS, D)                                                                        \
-    if (a.block_size == BS && a.head_dim == D) {                                               \
-        if (a.shared_parts > 0) {                                                              \
-            const hipError_t e = v4 ? launch_shared<BS, D, true>(a, stream) : launch_shared<BS, D, false>(a, stream); \
-            if (e != hipSuccess) return e;                                                     \
-        }                                                                                      \
-        if (gqa) return v4 ? launch_gqa<BS, D, true>(a, stream) : launch_gqa<BS, D, false>(a, stream); \
-        return v4 ? launch_mha<BS, D, true>(a, stream) : launch_mha<BS, D, false>(a, stream);  \
+template <int BS, int D, int CP>
+hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
+    if (a.shared_parts > 0) {
+        const hipError_t e = launch_shared<BS, D, CP>(a, stream);
+        if (e != hipSuccess) return e;
     }
+    if (a.num_q_heads != a.num_kv_heads) return launch_gqa<BS, D, CP>(a, stream);
+    return launch_mha<BS, D, CP>(a, stream);
+}
+
+hipError_t launch_paged_attn(const AttnArgs& a, hipStream_t stream) {
+#define PBQ_ATTN(BS, D)                                                       \
+    if (a.block_size == BS && a.head_dim == D)                                \
+        return with_codec_pair(a.k_codec, a.v_codec,                          \
+                               [&](auto cp) { return launch_attn<BS, D, decltype(cp)::value>(a, stream); });
     PBQ_ATTN(16, 64)
     PBQ_ATTN(16, 128)
     PBQ_ATTN(32, 64)

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <string>
+#include <type_traits>
 
 #include "pbq.h"
 
@@ -14,8 +15,37 @@ namespace pbq {
 // Records a message for kv_last_error() on this thread and returns st.
 kv_status fail(kv_status st, const std::string& msg);
 
+// Codec facts shared by host and device code.  The kernels are instantiated
+// per (K codec, V codec) pair, named by codec_pair(k, v).
+constexpr bool codec_has_zp(int c) { return c == KV_CODEC_I4_ASYM || c == KV_CODEC_I8_ASYM; }
+constexpr bool codec_packed4(int c) { return c == KV_CODEC_I4_ASYM; }
+constexpr int codec_pair(int k, int v) { return 4 * k + v; }
+// the pairs the kernels are built for
+constexpr bool codec_pair_supported(int k, int v) {
+    return (k == KV_CODEC_I8_SYM && (v == KV_CODEC_I8_SYM || v == KV_CODEC_I4_ASYM || v == KV_CODEC_I8_ASYM)) ||
+           (k == KV_CODEC_FP8_E4M3 && v == KV_CODEC_FP8_E4M3);
+}
+
+// f(std::integral_constant<int, codec_pair(k, v)>{}) for a supported pair;
+// hipErrorInvalidValue otherwise.
+template <class F>
+hipError_t with_codec_pair(int k, int v, F&& f) {
+    switch (codec_pair(k, v)) {
+        case codec_pair(KV_CODEC_I8_SYM, KV_CODEC_I8_SYM):
+            return f(std::integral_constant<int, codec_pair(KV_CODEC_I8_SYM, KV_CODEC_I8_SYM)>{});
+        case codec_pair(KV_CODEC_I8_SYM, KV_CODEC_I4_ASYM):
+            return f(std::integral_constant<int, codec_pair(KV_CODEC_I8_SYM, KV_CODEC_I4_ASYM)>{});
+        case codec_pair(KV_CODEC_I8_SYM, KV_CODEC_I8_ASYM):
+            return f(std::integral_constant<int, codec_pair(KV_CODEC_I8_SYM, KV_CODEC_I8_ASYM)>{});
+        case codec_pair(KV_CODEC_FP8_E4M3, KV_CODEC_FP8_E4M3):
+            return f(std::integral_constant<int, codec_pair(KV_CODEC_FP8_E4M3, KV_CODEC_FP8_E4M3)>{});
+        default:
+            return hipErrorInvalidValue;
+    }
+}
+
 struct QuantStoreArgs {
-    int32_t block_size, num_kv_heads, head_dim, v_codec;
+    int32_t block_size, num_kv_heads, head_dim, v_codec, k_codec;
     int8_t* k_codes;
     uint8_t* v_codes;
     uint16_t* k_scale;
@@ -38,7 +68,7 @@ struct QuantStoreArgs {
 };
 
 struct AttnArgs {
-    int32_t block_size, num_kv_heads, head_dim, v_codec;
+    int32_t block_size, num_kv_heads, head_dim, v_codec, k_codec;
     const int8_t* k_codes;
     const uint8_t* v_codes;
     const uint16_t* k_scale;
@@ -70,7 +100,7 @@ struct AttnArgs {
 };
 
 struct CopyArgs {
-    int32_t block_size, num_kv_heads, head_dim, v_codec;
+    int32_t block_size, num_kv_heads, head_dim, v_codec, k_codec;
     int8_t* k_codes;
     uint8_t* v_codes;
     uint16_t* k_scale;
@@ -98,7 +128,7 @@ struct SwapArgs {
     SwapSide dev, host;
     const kv_swap* plan;  // device address of the pinned host plan
     int32_t n;
-    int32_t block_size, num_kv_heads, head_dim, v_codec;
+    int32_t block_size, num_kv_heads, head_dim, v_codec, k_codec;
     int32_t dev_blocks, dev_slots, host_blocks, host_slots;
     int32_t chunks;       // work groups per entry (grid y)
 };

@@ -8,8 +8,9 @@
 //    tensor [num_blocks, num_heads, 1, 1] has it.
 //  * yunthe.com "KV-cache quantization and PagedAttention", "quantization
 //    principle": Q(x) = clamp(round(x / scale + zero_point), 0, 2^bits - 1),
-//    used here for the INT4 V codec (bits = 4) and, with zero point 128 and a
-//    signed store, for INT8.
+//    used here for the INT4 and INT8 asymmetric V codecs (bits = 4, 8) and,
+//    with zero point 128 and a signed store, for INT8; "vLLM deployment":
+//    the cache may also be kept in FP8 E4M3.
 //  Readings: rounding is to nearest with ties to even on the exact quotient;
 //  the statistics cover only the rows a block holds; the INT4 range is
 //  widened to contain 0 and its zero point is an integer; rows not yet held
@@ -31,7 +32,7 @@
 namespace pbq {
 namespace {
 
-template <int BS, int D, bool V4>
+template <int BS, int D, int CP>
 __global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = blockIdx.x * 2 + (wv >> 1);
@@ -61,26 +62,26 @@ __global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
     if (g >= H || n_new <= 0 || j * BS >= end) return;
     const int phys = a.block_tables[(int64_t)s * a.max_blocks_per_seq + j];
     const TileStoreArgs t{a.k_codes, a.v_codes, a.k_scale, a.v_scale, a.v_zp, a.tail_k, a.tail_v, a.k, a.v, H};
-    if (wv & 1) store_tile<BS, D, V4, false, false, true>(t, g, slot, c0, sp, end, j, phys, nullptr, nullptr);
-    else store_tile<BS, D, V4, false, true, false>(t, g, slot, c0, sp, end, j, phys, nullptr, nullptr);
+    if (wv & 1) store_tile<BS, D, CP, false, false, true>(t, g, slot, c0, sp, end, j, phys, nullptr, nullptr);
+    else store_tile<BS, D, CP, false, true, false>(t, g, slot, c0, sp, end, j, phys, nullptr, nullptr);
 }
 
 // Grid: x = pairs of KV heads, y = blocks a sequence's new tokens can touch,
 // z = sequences.
-template <int BS, int D, bool V4>
+template <int BS, int D, int CP>
 hipError_t launch_qs(const QuantStoreArgs& a, hipStream_t stream) {
     dim3 grid((unsigned)((a.num_kv_heads + 1) / 2), (unsigned)a.tiles_per_seq, (unsigned)a.num_seqs);
-    hipLaunchKernelGGL((quantize_store_kernel<BS, D, V4>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((quantize_store_kernel<BS, D, CP>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_quantize_store(const QuantStoreArgs& a, hipStream_t stream) {
-    const bool v4 = a.v_codec == KV_CODEC_I4_ASYM;
-#define PBQ_QS(BS, D)                                                          \
-    if (a.block_size == BS && a.head_dim == D)                                 \
-        return v4 ? launch_qs<BS, D, true>(a, stream) : launch_qs<BS, D, false>(a, stream);
+#define PBQ_QS(BS, D)                                                                         \
+    if (a.block_size == BS && a.head_dim == D)                                                \
+        return with_codec_pair(a.k_codec, a.v_codec,                                          \
+                               [&](auto cp) { return launch_qs<BS, D, decltype(cp)::value>(a, stream); });
     PBQ_QS(16, 64)
     PBQ_QS(16, 128)
     PBQ_QS(32, 64)

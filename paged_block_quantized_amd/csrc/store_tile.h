@@ -22,9 +22,16 @@
 // Exact codes without a per-element division (Quantizer below): a fast
 // pass that is exact except on ties, which send the wave through an exact
 // routine whose result equals round-half-even of the exact quotient.
+//
+// Further codecs: FP8 E4M3 (yunthe.com "vLLM deployment" names the format)
+// with an fp16 absmax/448 scale per (block, head), each code the E4M3 of the
+// correctly rounded fp32 quotient x / scale, clamped to +-448 and converted
+// by v_cvt_pk_fp8_f32 (round to nearest even); and INT8 asymmetric, the INT4
+// recipe with 255 levels and byte codes.
 #pragma once
 
 #include "device_common.h"
+#include "pbq_internal.h"
 
 namespace pbq {
 
@@ -84,6 +91,15 @@ struct Quantizer {
     }
 };
 
+// Four values (already divided by the scale) -> four E4M3 bytes, the first
+// in the low byte; the clamp keeps a quotient the scale's rounding pushed
+// past 448 at the largest finite code.
+__device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
+    auto cl = [](float x) { return __builtin_fminf(__builtin_fmaxf(x, -448.f), 448.f); };
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
+}
+
 // Quantize block j (physical id phys) of head g of a sequence whose rows
 // before position sp sit in tail slot `slot` and whose rows sp .. end-1 are
 // the new rows c0 .. c0 + end - sp - 1 of a.k / a.v.  Requires j * BS < end.
@@ -94,7 +110,7 @@ struct Quantizer {
 // them to two waves, which halves the registers and the arithmetic on
 // either's path.  With wr false nothing is written to the pool (only the LDS
 // copy; write_stored_tile writes it later).
-template <int BS, int D, bool V4, bool LDS, bool DO_K = true, bool DO_V = true>
+template <int BS, int D, int CP, bool LDS, bool DO_K = true, bool DO_V = true>
 __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, int slot, int c0, int sp,
                                                  int end, int j, int phys, int8_t* lds_k, uint8_t* lds_v,
                                                  bool wr = true) {
@@ -102,6 +118,9 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
     constexpr int RPI = 64 / LPR;  // rows per wave access
     constexpr int NIT = BS / RPI;  // accesses per lane per tensor
     constexpr int DPL = D / 64;    // V: dims per lane
+    constexpr int KC = CP / 4, VC = CP % 4;
+    constexpr bool V4 = codec_packed4(VC);
+    constexpr bool VZP = codec_has_zp(VC);
     const int lane = threadIdx.x & 63;
     const int H = a.num_kv_heads;
     TileScales out{};
@@ -132,7 +151,7 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
     const int64_t tile = (int64_t)phys * H + g;
     if constexpr (LDS) {   // the pool's scale bits before this store, loaded with the rows
         if constexpr (DO_K) out.prev = a.k_scale[tile];
-        else out.prev = a.v_scale[tile] | (V4 ? (uint32_t)a.v_zp[tile] << 16 : 0u);
+        else out.prev = a.v_scale[tile] | (VZP ? (uint32_t)a.v_zp[tile] << 16 : 0u);
     }
     uint32_t vw[DO_V ? BS : 1];   // V row r: dims DPL*lane .. +DPL-1 (fp16 bits)
     if constexpr (DO_V) {
@@ -157,8 +176,37 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
         return bits_to_f16f((uint16_t)(k ? vw[r] >> 16 : vw[r] & 0xFFFFu));
     };
 
+    // ---- K: FP8 E4M3 ----------------------------------------------------------
+    if constexpr (DO_K && KC == KV_CODEC_FP8_E4M3) {
+        uint32_t amax = 0;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const uint32_t b = absmax_bits_f16x8(kx[it]);
+            amax = amax > b ? amax : b;
+        }
+        amax = wave_max_u32_uniform(amax);
+        const float absmax = bits_to_f16f((uint16_t)amax);
+        const uint16_t s16 = f32_to_f16_bits(absmax / 448.0f);
+        const float sc = bits_to_f16f(s16);
+        int8_t* dst = a.k_codes + tile * (BS * D);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            uint32_t w[2] = {0u, 0u};
+            if (sc > 0.f) {   // uniform
+                const f16x8 x = kx[it];
+                w[0] = pack4_fp8((float)x[0] / sc, (float)x[1] / sc, (float)x[2] / sc, (float)x[3] / sc);
+                w[1] = pack4_fp8((float)x[4] / sc, (float)x[5] / sc, (float)x[6] / sc, (float)x[7] / sc);
+            }
+            const int r = it * RPI + r_in;
+            if (wr) *(u32x2*)(dst + r * D + col) = u32x2{w[0], w[1]};
+            if constexpr (LDS) *(u32x2*)(lds_k + r * D + col) = u32x2{w[0], w[1]};
+        }
+        if (wr && lane == 0) a.k_scale[tile] = s16;
+        out.k_scale = s16;
+    }
+
     // ---- K: INT8 symmetric -------------------------------------------------
-    if constexpr (DO_K) {
+    if constexpr (DO_K && KC == KV_CODEC_I8_SYM) {
         uint32_t amax = 0;
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
@@ -198,8 +246,41 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
         out.k_scale = s16;
     }
 
-    // ---- V (dim-major tile): INT8 symmetric or INT4 asymmetric ----------------
-    if constexpr (DO_V && !V4) {
+    // ---- V (dim-major tile): INT8 symmetric, FP8, INT4 or INT8 asymmetric ------
+    if constexpr (DO_V && VC == KV_CODEC_FP8_E4M3) {
+        uint32_t amax = 0;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k)
+#pragma unroll
+            for (int r = 0; r < BS; ++r) {
+                const uint32_t b = (k ? vw[r] >> 16 : vw[r]) & 0x7FFFu;
+                amax = amax > b ? amax : b;
+            }
+        amax = wave_max_u32_uniform(amax);
+        const float absmax = bits_to_f16f((uint16_t)amax);
+        const uint16_t s16 = f32_to_f16_bits(absmax / 448.0f);
+        const float sc = bits_to_f16f(s16);
+        uint8_t* dst = a.v_codes + tile * (BS * D);
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) {   // one dim row of codes at a time
+            uint32_t w[BS / 4];
+#pragma unroll
+            for (int i = 0; i < BS / 4; ++i)
+                w[i] = sc > 0.f ? pack4_fp8(vx(k, 4 * i) / sc, vx(k, 4 * i + 1) / sc, vx(k, 4 * i + 2) / sc,
+                                            vx(k, 4 * i + 3) / sc)
+                                : 0u;
+            uint32_t* drow = (uint32_t*)(dst + (DPL * lane + k) * BS);
+            uint32_t* lrow = LDS ? (uint32_t*)(lds_v + (DPL * lane + k) * BS) : nullptr;
+#pragma unroll
+            for (int i = 0; i < BS / 16; ++i) {
+                const u32x4 x = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+                if (wr) *(u32x4*)(drow + 4 * i) = x;
+                if constexpr (LDS) *(u32x4*)(lrow + 4 * i) = x;
+            }
+        }
+        if (wr && lane == 0) a.v_scale[tile] = s16;
+        out.v_scale = s16;
+    } else if constexpr (DO_V && VC == KV_CODEC_I8_SYM) {
         uint32_t amax = 0;
 #pragma unroll
         for (int k = 0; k < DPL; ++k)
@@ -247,7 +328,9 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
         if (wr && lane == 0) a.v_scale[tile] = s16;
         out.v_scale = s16;
     } else if constexpr (DO_V) {
-        // range widened to contain 0, over packed fp16 pairs (exact)
+        // INT4 or INT8 asymmetric: range widened to contain 0, over packed
+        // fp16 pairs (exact)
+        constexpr int QMAX = V4 ? 15 : 255;
         f16x2 lo2 = f16x2{(_Float16)0, (_Float16)0}, hi2 = lo2;
 #pragma unroll
         for (int r = 0; r < BS; ++r) {
@@ -259,54 +342,91 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
         float hi = fmaxf((float)hi2[0], DPL == 2 ? (float)hi2[1] : 0.f);
         lo = wave_min_uniform(lo);
         hi = wave_max_uniform(hi);
-        const uint16_t s16 = f32_to_f16_bits((hi - lo) / 15.0f);
+        const uint16_t s16 = f32_to_f16_bits((hi - lo) / (float)QMAX);
         const Quantizer qz(bits_to_f16f(s16));
         int zp = 0;
         if (qz.s > 0.f) {
             const float z = __builtin_rintf(-lo / qz.s);
-            zp = z > 15.f ? 15 : (z < 0.f ? 0 : (int)z);
+            zp = z > (float)QMAX ? QMAX : (z < 0.f ? 0 : (int)z);
         }
         const float zf = (float)zp;
-        // two nibbles per byte (even row low): byte = u_even + 16 u_odd; rows
-        // not yet held (zero inputs, code zp) are masked to zero nibbles
-        uint8_t* dst = a.v_codes + tile * (BS * D / 2);
+        if constexpr (!V4) {
+            // INT8 asymmetric: byte codes in dim rows, rows not yet held
+            // (zero inputs, code zp) masked to zero bytes
+            uint8_t* dst = a.v_codes + tile * (BS * D);
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) {   // one dim row of codes at a time
-            uint32_t w[BS / 8];
+            for (int k = 0; k < DPL; ++k) {
+                uint32_t w[BS / 4];
 #pragma unroll
-            for (int i = 0; i < BS / 8; ++i) {   // eight codes, then their tie check
-                uint32_t x = 0u;
-                bool tie = false;
+                for (int i = 0; i < BS / 4; ++i) {   // four codes, then their tie check
+                    uint32_t x = 0u;
+                    bool tie = false;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int r = 8 * i + 2 * b;
-                    const float u0 = qz.fast(vx(k, r), zf, 0.f, 15.f, tie);
-                    const float u1 = qz.fast(vx(k, r + 1), zf, 0.f, 15.f, tie);
-                    x = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(u1, 16.f, u0), b, x);
-                }
-                if (__builtin_amdgcn_ballot_w64(tie) != 0) {
-                    x = 0u;
+                    for (int b = 0; b < 4; ++b)
+                        x = __builtin_amdgcn_cvt_pk_u8_f32(qz.fast(vx(k, 4 * i + b), zf, 0.f, 255.f, tie), b, x);
+                    if (__builtin_amdgcn_ballot_w64(tie) != 0) {
+                        x = 0u;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        int q = qz.exact(vx(k, 8 * i + e), zp);
-                        q = q > 15 ? 15 : (q < 0 ? 0 : q);
-                        x |= (uint32_t)q << (4 * e);
+                        for (int b = 0; b < 4; ++b) {
+                            int q = qz.exact(vx(k, 4 * i + b), zp);
+                            q = q > 255 ? 255 : (q < 0 ? 0 : q);
+                            x |= (uint32_t)q << (8 * b);
+                        }
                     }
+                    const int held = min(max(valid - 4 * i, 0), 4);   // uniform
+                    w[i] = held == 4 ? x : x & ((1u << (8 * held)) - 1u);
                 }
-                const int held = min(max(valid - 8 * i, 0), 8);   // uniform
-                w[i] = held == 8 ? x : x & ((1u << (4 * held)) - 1u);
-            }
-            uint32_t* drow = (uint32_t*)(dst + (DPL * lane + k) * (BS / 2));
-            uint32_t* lrow = LDS ? (uint32_t*)(lds_v + (DPL * lane + k) * (BS / 2)) : nullptr;
-            if constexpr (BS == 16) {
-                if (wr) *(u32x2*)drow = u32x2{w[0], w[1]};
-                if constexpr (LDS) *(u32x2*)lrow = u32x2{w[0], w[1]};
-            } else {
+                uint32_t* drow = (uint32_t*)(dst + (DPL * lane + k) * BS);
+                uint32_t* lrow = LDS ? (uint32_t*)(lds_v + (DPL * lane + k) * BS) : nullptr;
 #pragma unroll
-                for (int i = 0; i < BS / 32; ++i) {
+                for (int i = 0; i < BS / 16; ++i) {
                     const u32x4 x = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
                     if (wr) *(u32x4*)(drow + 4 * i) = x;
                     if constexpr (LDS) *(u32x4*)(lrow + 4 * i) = x;
+                }
+            }
+        } else {
+            // two nibbles per byte (even row low): byte = u_even + 16 u_odd; rows
+            // not yet held (zero inputs, code zp) are masked to zero nibbles
+            uint8_t* dst = a.v_codes + tile * (BS * D / 2);
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) {   // one dim row of codes at a time
+                uint32_t w[BS / 8];
+#pragma unroll
+                for (int i = 0; i < BS / 8; ++i) {   // eight codes, then their tie check
+                    uint32_t x = 0u;
+                    bool tie = false;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const int r = 8 * i + 2 * b;
+                        const float u0 = qz.fast(vx(k, r), zf, 0.f, 15.f, tie);
+                        const float u1 = qz.fast(vx(k, r + 1), zf, 0.f, 15.f, tie);
+                        x = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(u1, 16.f, u0), b, x);
+                    }
+                    if (__builtin_amdgcn_ballot_w64(tie) != 0) {
+                        x = 0u;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            int q = qz.exact(vx(k, 8 * i + e), zp);
+                            q = q > 15 ? 15 : (q < 0 ? 0 : q);
+                            x |= (uint32_t)q << (4 * e);
+                        }
+                    }
+                    const int held = min(max(valid - 8 * i, 0), 8);   // uniform
+                    w[i] = held == 8 ? x : x & ((1u << (4 * held)) - 1u);
+                }
+                uint32_t* drow = (uint32_t*)(dst + (DPL * lane + k) * (BS / 2));
+                uint32_t* lrow = LDS ? (uint32_t*)(lds_v + (DPL * lane + k) * (BS / 2)) : nullptr;
+                if constexpr (BS == 16) {
+                    if (wr) *(u32x2*)drow = u32x2{w[0], w[1]};
+                    if constexpr (LDS) *(u32x2*)lrow = u32x2{w[0], w[1]};
+                } else {
+#pragma unroll
+                    for (int i = 0; i < BS / 32; ++i) {
+                        const u32x4 x = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+                        if (wr) *(u32x4*)(drow + 4 * i) = x;
+                        if constexpr (LDS) *(u32x4*)(lrow + 4 * i) = x;
+                    }
                 }
             }
         }
@@ -349,11 +469,13 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
 // written: its K row (D bytes), and its byte of every V dim row.  The fused
 // decode calls it after its loop.  new_row is the row of a.k / a.v that holds
 // position pos.
-template <int BS, int D, bool V4>
+template <int BS, int D, int CP>
 __device__ __forceinline__ void write_stored_tile(const TileStoreArgs& a, int w, int g, int slot, int new_row, int pos,
                                                   int phys, const uint8_t* lds_k, const uint8_t* lds_v,
                                                   const uint32_t* sc) {
     constexpr int KT = BS * D;
+    constexpr bool V4 = codec_packed4(CP % 4);
+    constexpr bool VZP = codec_has_zp(CP % 4);
     constexpr int VROW = V4 ? BS / 2 : BS;
     constexpr int VT = D * VROW;
     const int lane = threadIdx.x & 63;
@@ -374,14 +496,14 @@ __device__ __forceinline__ void write_stored_tile(const TileStoreArgs& a, int w,
         }
         if (tail && lane < D / 8) *(u32x4*)(a.tail_k + trow + 8 * lane) = *(const u32x4*)(a.k + nrow + 8 * lane);
     } else if (w == 1) {
-        if (r == 0 || sc[4] != (sc[1] | (V4 ? sc[2] << 16 : 0u))) {
+        if (r == 0 || sc[4] != (sc[1] | (VZP ? sc[2] << 16 : 0u))) {
 #pragma unroll
             for (int c = 0; c < (VT + 1023) / 1024; ++c)
                 if (VT % 1024 == 0 || 1024 * c + 16 * lane < VT)
                     *(u32x4*)(a.v_codes + tile * VT + 1024 * c + 16 * lane) = *(const u32x4*)(lds_v + 1024 * c + 16 * lane);
             if (lane == 0) {
                 a.v_scale[tile] = (uint16_t)sc[1];
-                if constexpr (V4) a.v_zp[tile] = (uint8_t)sc[2];
+                if constexpr (VZP) a.v_zp[tile] = (uint8_t)sc[2];
             }
         } else {
             const int b = V4 ? r / 2 : r;   // the new token's byte of each dim row

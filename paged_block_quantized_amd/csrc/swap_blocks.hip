@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kThreads) void swap_kernel(SwapArgs a) {
         const int32_t src_n = out ? a.dev_blocks : a.host_blocks;
         const int32_t dst_n = out ? a.host_blocks : a.dev_blocks;
         if (c.src < 0 || c.src >= src_n || c.dst < 0 || c.dst >= dst_n) return;
-        const bool v4 = a.v_codec == KV_CODEC_I4_ASYM;
+        const bool v4 = codec_packed4(a.v_codec), zp = codec_has_zp(a.v_codec);
         const int64_t kb = tile * H, vb = v4 ? kb / 2 : kb;
         const int64_t ku = kb / 16, units = (kb + vb) / 16;
         const char* sk = from.k_codes + c.src * kb;
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void swap_kernel(SwapArgs a) {
             for (int g = tid; g < H; g += kThreads) {
                 to.k_scale[(int64_t)c.dst * H + g] = from.k_scale[(int64_t)c.src * H + g];
                 to.v_scale[(int64_t)c.dst * H + g] = from.v_scale[(int64_t)c.src * H + g];
-                if (v4) to.v_zp[(int64_t)c.dst * H + g] = from.v_zp[(int64_t)c.src * H + g];
+                if (zp) to.v_zp[(int64_t)c.dst * H + g] = from.v_zp[(int64_t)c.src * H + g];
             }
     } else {
         const int32_t src_n = out ? a.dev_slots : a.host_slots;

@@ -11,17 +11,25 @@ class KVPool:
     """Host allocator (``kv_pool_create``) + device arrays sized by
     ``kv_pool_bytes``.
 
-    v_codec: "i8" (INT8 symmetric V) or "i4" (INT4 asymmetric V).
+    v_codec: "i8" (INT8 symmetric), "i4" (INT4 asymmetric), "i8a" (INT8
+    asymmetric) or "fp8" (FP8 E4M3) V; k_codec: "i8" or "fp8", by default
+    "fp8" exactly when V is FP8 (the supported pairs).
     free_order: initial free stack (a permutation of 0..N-1) or None.
     """
 
+    CODECS = {"i8": L.KV_CODEC_I8_SYM, "i4": L.KV_CODEC_I4_ASYM, "fp8": L.KV_CODEC_FP8_E4M3,
+              "i8a": L.KV_CODEC_I8_ASYM}
+
     def __init__(self, num_blocks, block_size, num_kv_heads, head_dim, v_codec="i8",
-                 max_seqs=1, free_order=None, device="cuda"):
-        codec = {"i8": L.KV_CODEC_I8_SYM, "i4": L.KV_CODEC_I4_ASYM}[v_codec]
-        self.desc = L.make_desc(num_blocks, block_size, num_kv_heads, head_dim, codec, max_seqs)
+                 max_seqs=1, free_order=None, device="cuda", k_codec=None):
+        k_codec = k_codec or ("fp8" if v_codec == "fp8" else "i8")
+        self.desc = L.make_desc(num_blocks, block_size, num_kv_heads, head_dim, self.CODECS[v_codec],
+                                max_seqs, k_codec=self.CODECS[k_codec])
         self.num_blocks, self.block_size = num_blocks, block_size
         self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
+        self.k_codec, self.v_codec = k_codec, v_codec
         self.v_int4 = v_codec == "i4"
+        self.v_zp_used = v_codec in ("i4", "i8a")
         self.max_seqs = max_seqs
         self.handle = L.kv_pool_create(self.desc, free_order)
         self.sizes = L.kv_pool_bytes(self.desc)
@@ -30,24 +38,33 @@ class KVPool:
         if device is not None:
             N, H, bs, D = num_blocks, num_kv_heads, block_size, head_dim
             dev = torch.device(device)
-            self.arrays = {
-                "k_codes": torch.zeros((N, H, bs, D), dtype=torch.int8, device=dev),
-                # V tiles are dim-major: [D, bs] codes per (block, head)
-                "v_codes": torch.zeros((N, H, D, bs // 2 if self.v_int4 else bs),
-                                       dtype=torch.uint8 if self.v_int4 else torch.int8, device=dev),
-                "k_scale": torch.zeros((N, H), dtype=torch.float16, device=dev),
-                "v_scale": torch.zeros((N, H), dtype=torch.float16, device=dev),
-                "v_zp": torch.zeros((N, H) if self.v_int4 else (1,), dtype=torch.uint8, device=dev),
-                "tail_k": torch.zeros((max_seqs, H, bs, D), dtype=torch.float16, device=dev),
-                "tail_v": torch.zeros((max_seqs, H, bs, D), dtype=torch.float16, device=dev),
-            }
+            self.arrays = self._arrays(N, max_seqs, lambda shape, dtype: torch.zeros(shape, dtype=dtype, device=dev))
             for name, t in self.arrays.items():
-                if name == "v_zp" and not self.v_int4:
+                if name == "v_zp" and not self.v_zp_used:
                     continue
                 assert t.numel() * t.element_size() == self.sizes[name], name
-            self.mem = L.kv_pool_mem(*[
-                None if (n == "v_zp" and not self.v_int4) else self.arrays[n].data_ptr()
-                for n in ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "tail_k", "tail_v")])
+            self.mem = self._mem(self.arrays)
+
+    def _arrays(self, nb, ns, make):
+        """The pool's arrays for nb blocks and ns tail slots (layout as
+        kv_pool_bytes gives it), each from make(shape, dtype)."""
+        H, bs, D = self.num_kv_heads, self.block_size, self.head_dim
+        return {
+            "k_codes": make((nb, H, bs, D), torch.int8 if self.k_codec == "i8" else torch.uint8),
+            # V tiles are dim-major: [D, bs] codes per (block, head)
+            "v_codes": make((nb, H, D, bs // 2 if self.v_int4 else bs),
+                            torch.int8 if self.v_codec == "i8" else torch.uint8),
+            "k_scale": make((nb, H), torch.float16),
+            "v_scale": make((nb, H), torch.float16),
+            "v_zp": make((nb, H) if self.v_zp_used else (1,), torch.uint8),
+            "tail_k": make((ns, H, bs, D), torch.float16),
+            "tail_v": make((ns, H, bs, D), torch.float16),
+        }
+
+    def _mem(self, arrays):
+        return L.kv_pool_mem(*[
+            None if (n == "v_zp" and not self.v_zp_used) else arrays[n].data_ptr()
+            for n in ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "tail_k", "tail_v")])
 
     def __getattr__(self, name):
         arrays = self.__dict__.get("arrays", {})
@@ -105,29 +122,14 @@ class KVPool:
         L.kv_pool_set_swap_space(self.handle, host_blocks, host_slots)
         nb, ns = max(1, host_blocks), max(1, host_slots)
         self.host_desc = L.make_desc(nb, self.block_size, self.num_kv_heads, self.head_dim,
-                                     self.desc.v_codec, ns)
+                                     self.desc.v_codec, ns, k_codec=self.desc.k_codec)
         self.host_arrays = {}
         self.host_mem = None
         if self.device is None:
             return
-        H, bs, D = self.num_kv_heads, self.block_size, self.head_dim
-
-        def pinned(shape, dtype):
-            return torch.zeros(shape, dtype=dtype, pin_memory=True)
-
-        self.host_arrays = {
-            "k_codes": pinned((nb, H, bs, D), torch.int8),
-            "v_codes": pinned((nb, H, D, bs // 2 if self.v_int4 else bs),
-                              torch.uint8 if self.v_int4 else torch.int8),
-            "k_scale": pinned((nb, H), torch.float16),
-            "v_scale": pinned((nb, H), torch.float16),
-            "v_zp": pinned((nb, H) if self.v_int4 else (1,), torch.uint8),
-            "tail_k": pinned((ns, H, bs, D), torch.float16),
-            "tail_v": pinned((ns, H, bs, D), torch.float16),
-        }
-        self.host_mem = L.kv_pool_mem(*[
-            None if (n == "v_zp" and not self.v_int4) else self.host_arrays[n].data_ptr()
-            for n in ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "tail_k", "tail_v")])
+        self.host_arrays = self._arrays(nb, ns, lambda shape, dtype: torch.zeros(shape, dtype=dtype,
+                                                                                pin_memory=True))
+        self.host_mem = self._mem(self.host_arrays)
 
     def _run_plan(self, fn, seqs, stream, mem):
         cap = L.swap_plan_cap(self.handle, seqs)
@@ -165,12 +167,9 @@ class KVPool:
         """A copy of the pool's code, scale and zero-point arrays in fresh
         device memory (tail slots shared), as a kv_pool_mem: the same cache
         contents at other addresses, e.g. to stand for another layer's pool."""
-        keep = {n: (t if n.startswith("tail") or (n == "v_zp" and not self.v_int4) else t.clone())
+        keep = {n: (t if n.startswith("tail") or (n == "v_zp" and not self.v_zp_used) else t.clone())
                 for n, t in self.arrays.items()}
-        mem = L.kv_pool_mem(*[
-            None if (n == "v_zp" and not self.v_int4) else keep[n].data_ptr()
-            for n in ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "tail_k", "tail_v")])
-        return mem, keep
+        return self._mem(keep), keep
 
     def quantize_store(self, k, v, cu_seqlens, start_pos, block_tables, tail_slots,
                        max_new_tokens, stream=None, mem=None):

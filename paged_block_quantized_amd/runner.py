@@ -193,7 +193,7 @@ def decode_bytes(w: W.Workload, ctx: np.ndarray) -> int:
     the context lengths; a shared prefix counted once."""
     S, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
     vbits = 4 if w.v_codec == "i4" else 8
-    meta = 2 + 2 + (1 if w.v_codec == "i4" else 0)
+    meta = 2 + 2 + (1 if w.v_codec in ("i4", "i8a") else 0)
     tokens = int(np.sum(ctx))
     blocks = int(np.sum((ctx + bs - 1) // bs))
     if w.prefix:
@@ -212,7 +212,7 @@ def store_step_bytes(w: W.Workload, ctx: np.ndarray) -> int:
     and the per-sequence index arrays."""
     Hkv, D, bs = w.num_kv_heads, w.head_dim, w.block_size
     vbits = 4 if w.v_codec == "i4" else 8
-    meta = 2 + 2 + (1 if w.v_codec == "i4" else 0)
+    meta = 2 + 2 + (1 if w.v_codec in ("i4", "i8a") else 0)
     rows = (ctx - 1) % bs + 1                    # rows the block holds after the store
     read = int(np.sum(rows)) * Hkv * D * 2 * 2
     write = len(ctx) * Hkv * (bs * D * (8 + vbits) // 8 + meta)

@@ -27,6 +27,9 @@ caching"):
 * ``shared_prefix``  32 sequences of 32768 tokens whose first 4096 are one
                      shared prefix, bs 32, 32 heads x D 128, INT8 K / INT4 V,
                      N(0,1), 512-token split-K partitions.
+* ``llama7b_fp8``, ``gqa70b_fp8``  the same shapes and draws with FP8 E4M3 K
+                     and V (the cache dtype yunthe.com "vLLM deployment"
+                     names); ``llama7b_i8a`` with INT8 asymmetric V.
 """
 
 from dataclasses import dataclass, field
@@ -43,7 +46,7 @@ class Workload:
     num_kv_heads: int
     head_dim: int
     block_size: int
-    v_codec: str                   # "i8" or "i4"
+    v_codec: str                   # "i8", "i4", "i8a" or "fp8" (K is FP8 exactly when V is)
     ctx_kind: str                  # "fixed", "list", "uniform"
     ctx: tuple = ()                # fixed: (n,), list: lengths, uniform: (lo, hi)
     channel_sigma: float = 0.0     # LogNormal sigma of per-(head, dim) factors
@@ -67,7 +70,19 @@ WORKLOADS = {
                               pool_blocks=16384, seed=4),
     "shared_prefix": Workload("shared_prefix", 32, 32, 32, 128, 32, "i4", "fixed", (32768,),
                               prefix=4096, partition=512, seed=5),
+    "llama7b_fp8": Workload("llama7b_fp8", 32, 32, 32, 128, 16, "fp8", "fixed", (4096,),
+                            channel_sigma=0.5, seed=2),
+    "llama7b_i8a": Workload("llama7b_i8a", 32, 32, 32, 128, 16, "i8a", "fixed", (4096,),
+                            channel_sigma=0.5, seed=2),
+    "gqa70b_fp8": Workload("gqa70b_fp8", 128, 64, 8, 128, 32, "fp8", "uniform", (500, 2000),
+                           outlier_frac=0.01, outlier_mult=8.0, seed=3),
 }
+
+
+def k_codec_of(w: Workload) -> str:
+    """The K codec paired with the workload's V codec (FP8 K with FP8 V,
+    INT8 symmetric K otherwise)."""
+    return "fp8" if w.v_codec == "fp8" else "i8"
 
 
 def context_lengths(w: Workload) -> np.ndarray:

@@ -32,7 +32,7 @@ def assert_close(gpu, ref, what=""):
 
 def pool_numpy(pool):
     out = {n: pool.arrays[n].cpu().numpy() for n in ("k_codes", "v_codes", "k_scale", "v_scale")}
-    out["v_zp"] = pool.arrays["v_zp"].cpu().numpy() if pool.v_int4 else None
+    out["v_zp"] = pool.arrays["v_zp"].cpu().numpy() if pool.v_zp_used else None
     return out
 
 
@@ -40,11 +40,11 @@ def assert_pool_equal(gpu_pool, opool, blocks=None):
     """Bit-exact comparison of codes, fp16 scale bits and zero points."""
     g = pool_numpy(gpu_pool)
     sel = slice(None) if blocks is None else np.asarray(blocks)
-    assert np.array_equal(g["k_codes"][sel], opool.k_codes[sel]), "K codes differ"
+    assert np.array_equal(g["k_codes"][sel].view(np.uint8), opool.k_codes[sel].view(np.uint8)), "K codes differ"
     assert np.array_equal(g["v_codes"][sel].view(np.uint8), opool.v_codes[sel].view(np.uint8)), "V codes differ"
     assert np.array_equal(g["k_scale"][sel].view(np.uint16), opool.k_scale[sel].view(np.uint16)), "K scales differ"
     assert np.array_equal(g["v_scale"][sel].view(np.uint16), opool.v_scale[sel].view(np.uint16)), "V scales differ"
-    if gpu_pool.v_int4:
+    if gpu_pool.v_zp_used:
         assert np.array_equal(g["v_zp"][sel], opool.v_zp[sel]), "V zero points differ"
 
 
@@ -64,7 +64,7 @@ class SmallCase:
         self.pool = KVPool(n_blocks, bs, hkv, d, v_codec, max_seqs=self.S,
                            free_order=free_order, device=device)
         self.model = A.BlockPoolModel(n_blocks, bs, self.S, free_order)
-        self.opool = paged.PoolArrays(n_blocks, hkv, bs, d, self.v_int4)
+        self.opool = paged.PoolArrays(n_blocks, hkv, bs, d, k_codec=self.pool.k_codec, v_codec=v_codec)
         for s, c in enumerate(self.ctx):
             t_gpu = self.pool.alloc(s, c)
             t_ref = self.model.alloc(s, c)
@@ -99,6 +99,11 @@ class SmallCase:
         return attention.paged_decode(self.opool, tables, self.ctx, self.q, sm)
 
 
+def opool_for(n_blocks, hkv, bs, d, vc):
+    """The oracle's pool for a V codec name (K is FP8 exactly when V is)."""
+    return paged.PoolArrays(n_blocks, hkv, bs, d, k_codec="fp8" if vc == "fp8" else "i8", v_codec=vc)
+
+
 def normal_case(ctx, hq, hkv, d, bs, v_codec, seed, extra_blocks=3, perm=True):
     rng = np.random.default_rng(seed)
     hk = [rng.standard_normal((c, hkv, d)).astype(np.float16) for c in ctx]
@@ -115,12 +120,13 @@ def gathered_pool(setup, s):
     pool = setup.pool
     nb = (int(setup.ctx[s]) + pool.block_size - 1) // pool.block_size
     table = setup.tables[s, :nb].long()
-    g = paged.PoolArrays(nb, pool.num_kv_heads, pool.block_size, pool.head_dim, pool.v_int4)
+    g = paged.PoolArrays(nb, pool.num_kv_heads, pool.block_size, pool.head_dim, k_codec=pool.k_codec,
+                         v_codec=pool.v_codec)
     g.k_codes = pool.k_codes[table].cpu().numpy()
     g.v_codes = pool.v_codes[table].cpu().numpy()
     g.k_scale = pool.k_scale[table].cpu().numpy()
     g.v_scale = pool.v_scale[table].cpu().numpy()
-    if pool.v_int4:
+    if pool.v_zp_used:
         g.v_zp = pool.v_zp[table].cpu().numpy()
     return g
 
@@ -133,14 +139,16 @@ def check_sequence(setup, s, out, what=None):
     ctx = int(setup.ctx[s])
     hk, hv = runner.sequence_history(setup, s)
     nb = (ctx + w.block_size - 1) // w.block_size
-    ref_pool = paged.PoolArrays(nb, w.num_kv_heads, w.block_size, w.head_dim, w.v_codec == "i4")
+    from paged_block_quantized_amd import workloads as W
+    ref_pool = paged.PoolArrays(nb, w.num_kv_heads, w.block_size, w.head_dim, k_codec=W.k_codec_of(w),
+                                v_codec=w.v_codec)
     paged.store_range(ref_pool, list(range(nb)), hk, hv, 0, ctx)
     g = gathered_pool(setup, s)
-    assert np.array_equal(g.k_codes, ref_pool.k_codes), f"seq {s}: K codes"
+    assert np.array_equal(g.k_codes.view(np.uint8), ref_pool.k_codes.view(np.uint8)), f"seq {s}: K codes"
     assert np.array_equal(g.v_codes.view(np.uint8), ref_pool.v_codes.view(np.uint8)), f"seq {s}: V codes"
     assert np.array_equal(g.k_scale.view(np.uint16), ref_pool.k_scale.view(np.uint16)), f"seq {s}: K scales"
     assert np.array_equal(g.v_scale.view(np.uint16), ref_pool.v_scale.view(np.uint16)), f"seq {s}: V scales"
-    if ref_pool.v_int4:
+    if ref_pool.v_codec in ("i4", "i8a"):
         assert np.array_equal(g.v_zp, ref_pool.v_zp), f"seq {s}: zero points"
     khat, vhat = paged.gather_dequant(ref_pool, list(range(nb)), ctx)
     q = setup.q[s].cpu().numpy()

@@ -233,6 +233,23 @@ def test_create_rejects_bad_arguments(lib):
         L.kv_pool_bytes(L.make_desc(4, 16, 1, 96))     # head_dim 96 has no kernel
     with pytest.raises(L.PBQError):
         L.kv_pool_bytes(L.make_desc(4, 16, 1, 64, v_codec=7))
+    # codec pairs: FP8 K goes with FP8 V only, FP8 V with FP8 K only
+    for kc, vc in ((L.KV_CODEC_I8_SYM, L.KV_CODEC_FP8_E4M3), (L.KV_CODEC_FP8_E4M3, L.KV_CODEC_I4_ASYM),
+                   (L.KV_CODEC_I4_ASYM, L.KV_CODEC_I4_ASYM), (L.KV_CODEC_I8_ASYM, L.KV_CODEC_I8_ASYM)):
+        with pytest.raises(L.PBQError, match="unsupported"):
+            L.kv_pool_bytes(L.make_desc(4, 16, 1, 64, v_codec=vc, k_codec=kc))
+
+
+def test_codec_pair_sizes(lib):
+    """Byte codecs (FP8, INT8 asymmetric) take one byte per value; the
+    asymmetric ones add a zero point per (block, head)."""
+    N, H, bs, D = 10, 3, 32, 128
+    f8 = L.kv_pool_bytes(L.make_desc(N, bs, H, D, L.KV_CODEC_FP8_E4M3, 2, k_codec=L.KV_CODEC_FP8_E4M3))
+    i8a = L.kv_pool_bytes(L.make_desc(N, bs, H, D, L.KV_CODEC_I8_ASYM, 2))
+    for sz in (f8, i8a):
+        assert sz["k_codes"] == sz["v_codes"] == N * H * bs * D
+        assert sz["k_scale"] == sz["v_scale"] == N * H * 2
+    assert f8["v_zp"] == 0 and i8a["v_zp"] == N * H
 
 
 def test_device_calls_validate_before_launch(lib):

@@ -38,6 +38,13 @@ def test_llama7b_full():
     _run("llama7b", samples=[0, 13, 31])
 
 
+@pytest.mark.parametrize("name", ["llama7b_fp8", "llama7b_i8a", "gqa70b_fp8"])
+def test_codec_variants_full(name):
+    """The FP8 and INT8-asymmetric workloads at full size, sampled sequences
+    against the oracle."""
+    _run(name, samples=[0, 17] if name.startswith("llama") else [0, 77, 127])
+
+
 def test_shared_prefix_full():
     """The step reads the 4096-token prefix once (paged_attn_decode_shared_prefix);
     the per-sequence path (paged_attn_decode_append) gives the same pool bit

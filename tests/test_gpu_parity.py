@@ -9,7 +9,7 @@ import torch
 from oracle import allocator as A
 from oracle import attention, paged
 
-from gpu_util import SmallCase, announce, assert_close, assert_pool_equal, normal_case
+from gpu_util import SmallCase, announce, assert_close, assert_pool_equal, normal_case, opool_for
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +43,7 @@ def test_tiny_workload(partition):
     assert np.array_equal(out[0], vrow.astype(np.float16))
 
 
-SHAPES = [(bs, d, vc) for bs in (16, 32) for d in (64, 128) for vc in ("i8", "i4")]
+SHAPES = [(bs, d, vc) for bs in (16, 32) for d in (64, 128) for vc in ("i8", "i4", "i8a", "fp8")]
 
 
 @pytest.mark.parametrize("bs,d,vc", SHAPES)
@@ -70,7 +70,7 @@ def test_zero_context_and_zero_blocks():
     hv[2][16:32] = 0           # an all-zero V block between non-zero ones
     hk[2][:16] = np.float16(0.5)  # a constant K block
     q = rng.standard_normal((3, 1, d)).astype(np.float16)
-    for vc in ("i8", "i4"):
+    for vc in ("i8", "i4", "i8a", "fp8"):
         case = SmallCase(hk, hv, q, 1, 1, d, bs, vc, 8, rng.permutation(8))
         case.store_all()
         assert_pool_equal(case.pool, case.opool)
@@ -93,9 +93,17 @@ def test_rounding_ties():
     k = np.array(rows, np.float16)[:, None, :]
     v = np.array(rows, np.float16)[::-1][:, None, :].copy()
     v4 = np.array([[-5.0, 10.0, 2.5, -0.5, 3.5] * 12 + [0.5, 1.5, -4.5, 7.5]] * bs, np.float16)[:, None, :]
+    # INT8 asymmetric: range 8 - (-7.9375) = 255/16, so scale 1/16 and zero
+    # point 127; (m + 1/2)/16 lands x/s + zp on half-integers
+    v8 = np.array([[8.0, -7.9375] + [(m + 0.5) / 16 for m in range(-31, 31)]] * bs, np.float16)[:, None, :]
+    # FP8: absmax 448 gives scale 1; midpoints of the E4M3 grid, normal and
+    # subnormal, and the 416/448 midpoint
+    mids = [1.0625, 1.1875, -1.3125, 3 * 2.0 ** -10, 2.0 ** -10, -5 * 2.0 ** -10, 432.0, 2.25, -2.75, 0.15625]
+    f8 = np.array([[448.0] + mids * 6 + [0.0, -0.0, 1.0]] * bs, np.float16)[:, None, :]
+    k8 = f8.copy()
     q = np.ones((2, 1, d), np.float16)
-    for vc, vv in (("i8", v), ("i4", v4)):
-        case = SmallCase([k, k[:7]], [vv, vv[:7]], q, 1, 1, d, bs, vc, 4, None)
+    for vc, kk, vv in (("i8", k, v), ("i4", k, v4), ("i8a", k, v8), ("fp8", k8, f8)):
+        case = SmallCase([kk, kk[:7]], [vv, vv[:7]], q, 1, 1, d, bs, vc, 4, None)
         case.store_all()
         assert_pool_equal(case.pool, case.opool)
 
@@ -133,7 +141,7 @@ def _store_chunk(pool, k, v, s, start, tables, slots):
                         tables[s:s + 1], slots[s:s + 1], k.shape[0])
 
 
-@pytest.mark.parametrize("vc", ["i8", "i4"])
+@pytest.mark.parametrize("vc", ["i8", "i4", "i8a", "fp8"])
 def test_append_requantize_from_tail(vc):
     """One-token appends re-quantize the partial block from the exact rows in
     the tail slot; the result equals the oracle's quantization of the rows."""
@@ -146,7 +154,7 @@ def test_append_requantize_from_tail(vc):
     hv = rng.standard_normal((total, h, d)).astype(np.float16)
     pool = KVPool(8, bs, h, d, vc, max_seqs=2, free_order=rng.permutation(8))
     model = A.BlockPoolModel(8, bs, 2, pool.free_list())
-    opool = paged.PoolArrays(8, h, bs, d, vc == "i4")
+    opool = opool_for(8, h, bs, d, vc)
     pool.alloc(0, 3)
     model.alloc(0, 3)
     tables, _, slots = pool.batch_tables([0], 3)
@@ -168,12 +176,12 @@ def test_append_requantize_from_tail(vc):
     assert np.array_equal(tk[:, :n_tail].transpose(1, 0, 2).view(np.uint16),
                           hk[total - n_tail:].view(np.uint16))
     # append-built blocks equal a prefill of the same rows
-    pre = paged.PoolArrays(8, h, bs, d, vc == "i4")
+    pre = opool_for(8, h, bs, d, vc)
     paged.store_range(pre, model.table(0)[0], hk, hv, 0, total)
     assert_pool_equal(pool, pre)
 
 
-@pytest.mark.parametrize("vc", ["i8", "i4"])
+@pytest.mark.parametrize("vc", ["i8", "i4", "i8a", "fp8"])
 def test_fork_copy_on_write(vc):
     """An unaligned shared prefix: fork copies the tail slot; each child's
     first append copies only the shared partial block; shared prefix blocks
@@ -189,7 +197,7 @@ def test_fork_copy_on_write(vc):
     order = rng.permutation(N)
     pool = KVPool(N, bs, h, d, vc, max_seqs=4, free_order=order)
     model = A.BlockPoolModel(N, bs, 4, order)
-    opool = paged.PoolArrays(N, h, bs, d, vc == "i4")
+    opool = opool_for(N, h, bs, d, vc)
     parent = 9
     pool.alloc(parent, pre)
     model.alloc(parent, pre)
@@ -228,7 +236,7 @@ def test_fork_copy_on_write(vc):
     # the shared blocks were not modified by the children's stores
     shared = [b for b in model.table(parent)[0] if model.refcount[b] > 1]
     assert len(shared) == 2
-    ref_parent = paged.PoolArrays(N, h, bs, d, vc == "i4")
+    ref_parent = opool_for(N, h, bs, d, vc)
     paged.store_range(ref_parent, model.table(parent)[0], hp_k, hp_v, 0, pre)
     assert_pool_equal(pool, ref_parent, blocks=model.table(parent)[0])
 
@@ -241,6 +249,10 @@ GQA_SHAPES = [
     (16, 64, "i4", 2, 3),
     (32, 128, "i8", 32, 1),
     (16, 128, "i4", 7, 2),
+    (32, 128, "fp8", 8, 2),
+    (16, 64, "fp8", 4, 1),
+    (32, 128, "i8a", 8, 2),
+    (16, 128, "i8a", 7, 2),
 ]
 
 
@@ -268,8 +280,9 @@ def test_gqa_rejects_partition_not_multiple_of_32():
         case.decode(16)
 
 
-APPEND_SHAPES = [(bs, d, vc, 1) for bs in (16, 32) for d in (64, 128) for vc in ("i8", "i4")] + [
-    (32, 128, "i4", 8), (16, 128, "i8", 4)]
+APPEND_SHAPES = [(bs, d, vc, 1) for bs in (16, 32) for d in (64, 128) for vc in ("i8", "i4", "i8a", "fp8")] + [
+    (32, 128, "i4", 8), (16, 128, "i8", 4), (32, 128, "fp8", 8), (16, 64, "fp8", 4), (32, 128, "i8a", 8),
+    (16, 128, "i8a", 2)]
 
 
 @pytest.mark.parametrize("bs,d,vc,g", APPEND_SHAPES)
@@ -319,7 +332,7 @@ def test_decode_append_equals_store_then_decode(bs, d, vc, g):
     qd = torch.from_numpy(q).to(dev)
     # the oracle: every row stored, tables from the allocator model
     model = A.BlockPoolModel(n_blocks, bs, S, order)
-    opool = paged.PoolArrays(n_blocks, hkv, bs, d, vc == "i4")
+    opool = opool_for(n_blocks, hkv, bs, d, vc)
     for s, c in enumerate(ctx):          # the same call order as build()
         model.alloc(s, c - 1)
     for s, c in enumerate(ctx):
@@ -338,7 +351,7 @@ def test_decode_append_equals_store_then_decode(bs, d, vc, g):
         out_b = torch.empty_like(qd)
         pb.decode_append(k_new, v_new, sb, qd, out_b, tb, cb, max(ctx), sm, part)
         torch.cuda.synchronize()
-        for name in ("k_codes", "v_codes", "k_scale", "v_scale", "tail_k", "tail_v") + (("v_zp",) if vc == "i4" else ()):
+        for name in ("k_codes", "v_codes", "k_scale", "v_scale", "tail_k", "tail_v") + (("v_zp",) if vc in ("i4", "i8a") else ()):
             x, y = pa.arrays[name].cpu().numpy(), pb.arrays[name].cpu().numpy()
             assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f"{name} differs (part {part})"
         g_k = pb.k_codes.cpu().numpy()
@@ -358,6 +371,9 @@ SHARED_SHAPES = [
     (32, 128, "i8", 1, 2, 5, 128),
     (32, 128, "i4", 8, 2, 5, 64),
     (16, 64, "i8", 4, 1, 5, 96),
+    (32, 128, "fp8", 8, 2, 5, 64),
+    (16, 128, "fp8", 1, 2, 5, 128),
+    (32, 64, "i8a", 1, 2, 5, 64),
 ]
 
 
@@ -426,7 +442,7 @@ def test_prefix_cache_end_to_end(bs, vc):
     order = rng.permutation(N)
     pool = KVPool(N, bs, h, d, vc, max_seqs=len(reqs), free_order=order)
     model = A.BlockPoolModel(N, bs, len(reqs), order)
-    opool = paged.PoolArrays(N, h, bs, d, vc == "i4")
+    opool = opool_for(N, h, bs, d, vc)
     shared_before = {}
     for s, ids in enumerate(reqs):
         tab, cached = pool.alloc_prefix(s, ids)
@@ -499,7 +515,8 @@ def _apply_plan(plan, dev, host, h, bs):
                 b[n][dst].reshape(h, bs, -1)[:, :rows] = a[n][src].reshape(h, bs, -1)[:, :rows]
 
 
-SWAP_SHAPES = [(16, 2, 64, "i8"), (32, 3, 128, "i4"), (16, 32, 128, "i8"), (32, 8, 64, "i4")]
+SWAP_SHAPES = [(16, 2, 64, "i8"), (32, 3, 128, "i4"), (16, 32, 128, "i8"), (32, 8, 64, "i4"),
+               (16, 4, 128, "fp8"), (32, 2, 64, "i8a")]
 
 
 @pytest.mark.parametrize("bs,h,d,vc", SWAP_SHAPES)
@@ -517,8 +534,8 @@ def test_swap_moves_bytes_exactly(bs, h, d, vc):
     model = A.BlockPoolModel(N, bs, S, order)
     pool.set_swap_space(24, 4)
     model.set_swap_space(24, 4)
-    dev = _fill_random(rng, pool.arrays, vc == "i8")
-    host = _fill_random(rng, pool.host_arrays, vc == "i8")
+    dev = _fill_random(rng, pool.arrays, not pool.v_zp_used)
+    host = _fill_random(rng, pool.host_arrays, not pool.v_zp_used)
     for s, n in {0: 3 * bs + 5, 1: 2 * bs, 2: 1, 3: 4 * bs - 1, 4: bs + 2}.items():
         assert pool.alloc(s, n) == model.alloc(s, n)
     copies = model.fork(0, 5)
@@ -613,7 +630,7 @@ def test_swap_then_decode_append_end_to_end(bs, vc):
     pool.decode_append(torch.from_numpy(new_k).cuda(), torch.from_numpy(new_v).cuda(), slots.cuda(),
                        qd, out, tables.cuda(), ctx_h.cuda(), int(ctx_h.max()), 1 / np.sqrt(d))
     torch.cuda.synchronize()
-    ref_pool = paged.PoolArrays(pool.num_blocks, h, bs, d, vc == "i4")
+    ref_pool = opool_for(pool.num_blocks, h, bs, d, vc)
     tabs = []
     for s in range(S):
         hk = np.concatenate([case.hist_k[s], new_k[s:s + 1]])
