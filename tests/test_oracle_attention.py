@@ -183,3 +183,28 @@ def test_v_tile_layout_dim_major():
     assert float(pool4.v_scale[0, 0]) == 1.0 and int(pool4.v_zp[0, 0]) == 0
     assert pool4.v_codes[0, 0, 5].tolist() == [(2 * j) | ((2 * j + 1) << 4) for j in range(bs // 2)]
     assert not pool4.v_codes[0, 0, 4].any()
+
+
+@pytest.mark.parametrize("n,ctx,hq,hkv", [(5, 5, 2, 2), (7, 20, 4, 2), (1, 9, 3, 1), (16, 16, 8, 1)])
+def test_multi_query_matches_torch_causal_sdpa(n, ctx, hq, hkv):
+    """The last n tokens attending causally equal torch's float64 SDPA with
+    a causal mask shifted by ctx - n (is_causal itself when n == ctx)."""
+    rng = np.random.default_rng(n * 100 + ctx)
+    d = 32
+    k = rng.standard_normal((hkv, ctx, d))
+    v = rng.standard_normal((hkv, ctx, d))
+    q = rng.standard_normal((n, hq, d)).astype(np.float16)
+    sm = 0.3
+    got = attention.multi_query_attention(q, k, v, sm)
+    g = hq // hkv
+    qt = torch.from_numpy(q.astype(np.float64)).permute(1, 0, 2)              # [Hq, n, D]
+    kt = torch.from_numpy(k).repeat_interleave(g, 0)
+    vt = torch.from_numpy(v).repeat_interleave(g, 0)
+    mask = torch.ones(n, ctx, dtype=torch.bool).tril(diagonal=ctx - n)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=sm)
+    assert np.allclose(got, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+    if n == ctx:
+        ref2 = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=sm)
+        assert np.allclose(got, ref2.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+    # the last query sees everything: the single-query definition
+    assert np.allclose(got[-1], attention.decode_attention(q[-1], k, v, sm), rtol=0, atol=0)
