@@ -430,6 +430,43 @@ kv_status paged_attn_decode_shared_prefix(const kv_pool_desc* desc, const kv_poo
                                           void* workspace_dev, size_t workspace_bytes,
                                           void* stream);
 
+/* Attention of several query tokens per sequence over the quantized cache:
+ * chunked prefill over a cached prefix ([yunthe] "prefix caching": once the
+ * prefix's blocks are in the pool only the new tokens are computed), or
+ * several candidate / draft tokens of one sequence.  Sequence s's queries
+ * are rows cu_seqlens[s] .. cu_seqlens[s+1] - 1 of q_dev and out_dev (fp16
+ * [num_tokens, num_q_heads, D], token-major); they are its last
+ * n_s = cu_seqlens[s+1] - cu_seqlens[s] stored tokens (store them first,
+ * kv_quantize_store), and query i attends causally to tokens
+ * 0 .. context_lens[s] - n_s + i:
+ *   out[r, h, :] = sum_{t <= pos} softmax_t(sm_scale <q[r,h], K_hat[s,g,t]>)
+ *                  V_hat[s, g, t, :],  g = h / (num_q_heads / Hkv).
+ * cu_seqlens_dev int32 [num_seqs + 1] (cu[0] = 0, cu[num_seqs] = num_tokens);
+ * max_q_len >= every n_s and <= max_context_len (sizes the grid); n_s <=
+ * context_lens[s] is the caller's contract (a query that sees no token gives
+ * a zero row).  All query heads of a KV head and 16 (token, head) pairs at a
+ * time run on the matrix cores, for any group size.  partition_size: a
+ * multiple of 32 and of block_size, or 0 for the library's choice; a query
+ * merges only the partitions its position reaches.  Workspace:
+ * paged_attn_multi_query_workspace_bytes.  Errors as paged_attn_decode,
+ * plus KV_ERR_INVALID for a bad max_q_len or more than 65535 (token, head)
+ * tiles per KV head and sequence. */
+kv_status paged_attn_multi_query(const kv_pool_desc* desc, const kv_pool_mem* mem,
+                                 const uint16_t* q_dev, uint16_t* out_dev, int32_t num_seqs,
+                                 int32_t num_q_heads, const int32_t* cu_seqlens_dev,
+                                 int32_t num_tokens, int32_t max_q_len,
+                                 const int32_t* block_tables_dev, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens_dev, int32_t max_context_len,
+                                 float sm_scale, int32_t partition_size, void* workspace_dev,
+                                 size_t workspace_bytes, void* stream);
+
+/* Workspace bytes paged_attn_multi_query needs (fp32 partial outputs and
+ * (max, sum) per query token, head and partition; 0 for one partition). */
+size_t paged_attn_multi_query_workspace_bytes(const kv_pool_desc* desc, int32_t num_seqs,
+                                              int32_t num_tokens, int32_t num_q_heads,
+                                              int32_t max_q_len, int32_t max_context_len,
+                                              int32_t partition_size);
+
 /* Partition size (tokens) paged_attn_decode uses when given 0: a single
  * pass when num_seqs x (heads, or KV heads x 16-head tiles) gives at least
  * four work groups per compute unit of the current device and every context

@@ -68,7 +68,8 @@ EXPORTS = [
     "kv_batch_tables", "kv_pool_stats", "kv_pool_free_list", "kv_pool_set_swap_space",
     "kv_seq_swap_out", "kv_seq_swap_in", "kv_swap_blocks", "kv_copy_blocks",
     "kv_quantize_store", "paged_attn_workspace_bytes", "paged_attn_decode",
-    "paged_attn_decode_append", "paged_attn_decode_shared_prefix",
+    "paged_attn_decode_append", "paged_attn_decode_shared_prefix", "paged_attn_multi_query",
+    "paged_attn_multi_query_workspace_bytes",
     "paged_attn_default_partition", "kv_last_error",
 ]
 
@@ -116,6 +117,9 @@ def lib():
             "paged_attn_decode_shared_prefix": (st, [P(kv_pool_desc), P(kv_pool_mem), VP, VP, VP, VP,
                                                      VP, I32, I32, VP, I32, VP, I32, ctypes.c_float,
                                                      I32, I32, VP, SZ, VP]),
+            "paged_attn_multi_query": (st, [P(kv_pool_desc), P(kv_pool_mem), VP, VP, I32, I32, VP, I32, I32,
+                                            VP, I32, VP, I32, ctypes.c_float, I32, VP, SZ, VP]),
+            "paged_attn_multi_query_workspace_bytes": (SZ, [P(kv_pool_desc), I32, I32, I32, I32, I32, I32]),
             "paged_attn_default_partition": (I32, [P(kv_pool_desc), I32, I32, I32]),
             "kv_last_error": (ctypes.c_char_p, []),
         }
@@ -350,3 +354,20 @@ def paged_attn_decode_shared_prefix(desc, mem, k_new, v_new, tail_slots, q, out,
         _ptr(out), int(num_seqs), int(num_q_heads), _ptr(block_tables), int(max_blocks_per_seq),
         _ptr(context_lens), int(max_context_len), float(sm_scale), int(partition_size),
         int(shared_tokens), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def paged_attn_multi_query_workspace_bytes(desc, num_seqs, num_tokens, num_q_heads, max_q_len,
+                                           max_context_len, partition_size=0):
+    return lib().paged_attn_multi_query_workspace_bytes(ctypes.byref(desc), int(num_seqs), int(num_tokens),
+                                                        int(num_q_heads), int(max_q_len),
+                                                        int(max_context_len), int(partition_size))
+
+
+def paged_attn_multi_query(desc, mem, q, out, num_seqs, num_q_heads, cu_seqlens, num_tokens, max_q_len,
+                           block_tables, max_blocks_per_seq, context_lens, max_context_len, sm_scale,
+                           partition_size=0, workspace=None, workspace_bytes=0, stream=None):
+    _check(lib().paged_attn_multi_query(
+        ctypes.byref(desc), ctypes.byref(mem), _ptr(q), _ptr(out), int(num_seqs), int(num_q_heads),
+        _ptr(cu_seqlens), int(num_tokens), int(max_q_len), _ptr(block_tables), int(max_blocks_per_seq),
+        _ptr(context_lens), int(max_context_len), float(sm_scale), int(partition_size), _ptr(workspace),
+        int(workspace_bytes), _stream(stream)))

@@ -425,14 +425,12 @@ kv_status kv_quantize_store(const kv_pool_desc* d, const kv_pool_mem* m,
     return pbq::hip_status(pbq::launch_quantize_store(a, (hipStream_t)stream), "kv_quantize_store launch");
 }
 
-int32_t paged_attn_default_partition(const kv_pool_desc* d, int32_t num_seqs,
-                                     int32_t num_q_heads, int32_t max_context_len) {
-    if (!d || d->block_size < 1 || d->num_kv_heads < 1 || num_seqs < 1 || num_q_heads < 1) return 0;
-    // Work groups: one per (sequence, head) for one query head per KV head,
-    // one per (sequence, KV head, tile of 16 query heads) otherwise.
-    const int64_t group = num_q_heads / d->num_kv_heads;
-    const int64_t units = (int64_t)num_seqs *
-                          (group == 1 ? num_q_heads : (int64_t)d->num_kv_heads * pbq::ceil_div(group, 16));
+}  // extern "C"
+
+namespace {
+
+// The partition policy over `units` work groups per partition.
+int32_t partition_for_units(int64_t units, int32_t max_context_len) {
     const int64_t target = 4 * (int64_t)pbq::device_cu_count();
     const int32_t ctx = max_context_len > 0 ? max_context_len : 1;
     // A single pass (no reduce kernel, no workspace) when the units alone give
@@ -445,6 +443,118 @@ int32_t paged_attn_default_partition(const kv_pool_desc* d, int32_t num_seqs,
     return part;
 }
 
+// Multi-query work groups per partition: sequences x KV heads x tiles of 16
+// (query token, group head) pairs.
+int32_t multi_default_partition(const kv_pool_desc* d, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t max_q_len, int32_t max_context_len) {
+    if (!d || d->num_kv_heads < 1 || num_seqs < 1 || num_q_heads < 1 || max_q_len < 1) return 0;
+    const int64_t group = num_q_heads / d->num_kv_heads;
+    return partition_for_units((int64_t)num_seqs * d->num_kv_heads * pbq::ceil_div(max_q_len * group, 16),
+                               max_context_len);
+}
+
+size_t workspace_rows_bytes(const kv_pool_desc* d, int64_t rows_per_part, int32_t max_context_len,
+                            int32_t part) {
+    if (part <= 0) return 0;
+    const int32_t max_parts = max_context_len > 0 ? pbq::ceil_div(max_context_len, part) : 1;
+    if (max_parts <= 1) return 0;
+    const size_t rows = (size_t)rows_per_part * max_parts;
+    return rows * (size_t)d->head_dim * 4 + rows * 8;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t paged_attn_default_partition(const kv_pool_desc* d, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t max_context_len) {
+    if (!d || d->block_size < 1 || d->num_kv_heads < 1 || num_seqs < 1 || num_q_heads < 1) return 0;
+    // Work groups: one per (sequence, head) for one query head per KV head,
+    // one per (sequence, KV head, tile of 16 query heads) otherwise.
+    const int64_t group = num_q_heads / d->num_kv_heads;
+    const int64_t units = (int64_t)num_seqs *
+                          (group == 1 ? num_q_heads : (int64_t)d->num_kv_heads * pbq::ceil_div(group, 16));
+    return partition_for_units(units, max_context_len);
+}
+
+size_t paged_attn_multi_query_workspace_bytes(const kv_pool_desc* d, int32_t num_seqs, int32_t num_tokens,
+                                              int32_t num_q_heads, int32_t max_q_len,
+                                              int32_t max_context_len, int32_t partition_size) {
+    if (!d || num_seqs <= 0 || num_tokens <= 0 || num_q_heads <= 0 || max_context_len < 0 || d->head_dim <= 0)
+        return 0;
+    const int32_t part = partition_size > 0
+                             ? partition_size
+                             : multi_default_partition(d, num_seqs, num_q_heads, max_q_len, max_context_len);
+    return workspace_rows_bytes(d, (int64_t)num_tokens * num_q_heads, max_context_len, part);
+}
+
+kv_status paged_attn_multi_query(const kv_pool_desc* d, const kv_pool_mem* m, const uint16_t* q,
+                                 uint16_t* out, int32_t num_seqs, int32_t num_q_heads,
+                                 const int32_t* cu_seqlens, int32_t num_tokens, int32_t max_q_len,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t max_context_len, float sm_scale,
+                                 int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    kv_status st = pbq::check_device_desc(d);
+    if (st != KV_OK) return st;
+    if ((st = pbq::check_mem(d, m, false)) != KV_OK) return st;
+    if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0 || max_context_len < 0 || max_blocks_per_seq < 0)
+        return fail(KV_ERR_INVALID, "negative size argument");
+    if (num_q_heads < 1 || num_q_heads % d->num_kv_heads != 0)
+        return fail(KV_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
+    const int32_t group = num_q_heads / d->num_kv_heads;
+    if (num_seqs == 0 || num_tokens == 0) return KV_OK;
+    if (max_q_len < 1 || max_q_len > max_context_len)
+        return fail(KV_ERR_INVALID, "max_q_len must be in [1, max_context_len]");
+    if (num_seqs > 65535 || num_q_heads > 65535 || max_q_len > 65535)
+        return fail(KV_ERR_INVALID, "num_seqs, num_q_heads and max_q_len must stay below 65536");
+    if ((int64_t)d->num_kv_heads * pbq::ceil_div((int64_t)max_q_len * group, 16) > 65535)
+        return fail(KV_ERR_INVALID, "too many (query token, head) tiles per sequence for the launch grid");
+    if (!q || !out || !pbq::aligned16(q) || !pbq::aligned16(out))
+        return fail(KV_ERR_INVALID, "q and out must be non-NULL and 16-byte aligned");
+    if (!cu_seqlens || !block_tables || !context_lens) return fail(KV_ERR_INVALID, "index arrays must be non-NULL");
+    if ((int64_t)max_blocks_per_seq * d->block_size < max_context_len)
+        return fail(KV_ERR_INVALID, "max_blocks_per_seq * block_size < max_context_len");
+    if (!std::isfinite(sm_scale)) return fail(KV_ERR_INVALID, "sm_scale must be finite");
+    int32_t part = partition_size;
+    if (part == 0) part = multi_default_partition(d, num_seqs, num_q_heads, max_q_len, max_context_len);
+    if (part <= 0 || part % d->block_size != 0 || part % 32 != 0)
+        return fail(KV_ERR_INVALID, "partition_size must be a positive multiple of 32 and of block_size (or 0)");
+    const int32_t max_parts = pbq::ceil_div(max_context_len, part);
+    if (max_parts > 65535) return fail(KV_ERR_INVALID, "too many partitions; use a larger partition_size");
+    const size_t need = workspace_rows_bytes(d, (int64_t)num_tokens * num_q_heads, max_context_len, part);
+    if (workspace_bytes < need) return fail(KV_ERR_INVALID, "workspace too small");
+    if (need > 0 && (!workspace || !pbq::aligned16(workspace)))
+        return fail(KV_ERR_INVALID, "workspace must be non-NULL and 16-byte aligned");
+    pbq::AttnArgs a{};
+    a.block_size = d->block_size;
+    a.num_kv_heads = d->num_kv_heads;
+    a.head_dim = d->head_dim;
+    a.v_codec = d->v_codec;
+    a.k_codec = d->k_codec;
+    a.k_codes = (const int8_t*)m->k_codes;
+    a.v_codes = (const uint8_t*)m->v_codes;
+    a.k_scale = (const uint16_t*)m->k_scale;
+    a.v_scale = (const uint16_t*)m->v_scale;
+    a.v_zp = (const uint8_t*)m->v_zp;
+    a.q = q;
+    a.out = out;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.sm_scale = sm_scale;
+    a.partition_blocks = part / d->block_size;
+    a.max_partitions = max_parts;
+    a.cu_q = cu_seqlens;
+    a.max_q_len = max_q_len;
+    const size_t rows = (size_t)num_tokens * num_q_heads * max_parts;
+    a.ws_out = need ? (float*)workspace : nullptr;
+    a.ws_ml = need ? (float*)((char*)workspace + rows * (size_t)d->head_dim * 4) : nullptr;
+    return pbq::hip_status(pbq::launch_paged_attn(a, (hipStream_t)stream), "paged_attn_multi_query launch");
+}
+
 size_t paged_attn_workspace_bytes(const kv_pool_desc* d, int32_t num_seqs,
                                   int32_t num_q_heads, int32_t max_context_len,
                                   int32_t partition_size) {
@@ -452,11 +562,7 @@ size_t paged_attn_workspace_bytes(const kv_pool_desc* d, int32_t num_seqs,
         return 0;
     int32_t part = partition_size > 0 ? partition_size
                                       : paged_attn_default_partition(d, num_seqs, num_q_heads, max_context_len);
-    if (part <= 0) return 0;
-    int32_t max_parts = max_context_len > 0 ? pbq::ceil_div(max_context_len, part) : 1;
-    if (max_parts <= 1) return 0;
-    size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
-    return rows * (size_t)d->head_dim * 4 + rows * 8;
+    return workspace_rows_bytes(d, (int64_t)num_seqs * num_q_heads, max_context_len, part);
 }
 
 kv_status paged_attn_decode(const kv_pool_desc* d, const kv_pool_mem* m,

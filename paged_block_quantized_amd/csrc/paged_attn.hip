@@ -607,12 +607,19 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // group (query i: sequence i / G, head kvh * G + i % G), so each of the
 // prefix's tiles is read once per 16 queries instead of once per sequence.
 // Results always go to the workspace, for the reduce.
-template <int BS, int D, int CP, int NW, bool FUSED, bool SHARED = false>
+//
+// MULTI: several query tokens per sequence, the last n of its stored tokens
+// (rows cu_q[s] .. cu_q[s+1] - 1 of q), each attending causally up to its
+// own position.  Query i of a sequence's tiles is token i / G with head
+// kvh * G + i % G; a tile reads only the tokens its last query can see, and
+// the steps past its first query's position mask per query.
+template <int BS, int D, int CP, int NW, bool FUSED, bool SHARED = false, bool MULTI = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA_WAVES_PER_EU))) void attn_partition_gqa(AttnArgs a) {
     constexpr int KC = CP / 4, VC = CP % 4;
     constexpr bool V4 = codec_packed4(VC);
     constexpr bool VZP = codec_has_zp(VC);
     static_assert(!(FUSED && SHARED), "the shared prefix holds no current token");
+    static_assert(!(MULTI && (FUSED || SHARED)), "multi-query launches store nothing and share nothing");
     static_assert(BS == 16 || BS == 32, "block size");
     constexpr bool STAGED = FUSED ? PBQ_GQA_STAGE_FUSED : PBQ_GQA_STAGE;
     constexpr int KS = D / 32;                 // QK k-steps
@@ -629,29 +636,47 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
     const int n16 = lane & 15;       // head (C/B layouts) or M row (A layout)
     const int grp = lane >> 4;       // lane group
     const int G = a.num_q_heads / a.num_kv_heads;
-    const int NQ = SHARED ? a.num_seqs * G : G;   // queries that share a KV head's tiles
-    const int n_ht = (NQ + 15) / 16;
     int p, tile, s;
     grid_coords(p, tile, s);
-    if constexpr (!SHARED) p += a.shared_parts;   // shared partitions ran in their own launch
-    const int kvh = tile / n_ht;
-    const int ht = tile % n_ht;
+    if constexpr (!SHARED && !MULTI) p += a.shared_parts;   // shared partitions ran in their own launch
+    const int q_row0 = MULTI ? a.cu_q[s] : 0;               // the sequence's first query row
+    const int n_tok = MULTI ? a.cu_q[s + 1] - q_row0 : 1;   // its query tokens
+    // queries that share a KV head's tiles
+    const int NQ = SHARED ? a.num_seqs * G : n_tok * G;
+    const int n_ht = (NQ + 15) / 16;
+    const int n_ht_grid = MULTI ? (a.max_q_len * G + 15) / 16 : n_ht;
+    const int kvh = tile / n_ht_grid;
+    const int ht = tile % n_ht_grid;
+    if (MULTI && ht >= n_ht) return;
     const int H = a.num_kv_heads;
-    const int ctx = SHARED ? a.shared_tokens : a.context_lens[s];
+    const int ctx_seq = SHARED ? a.shared_tokens : a.context_lens[s];
+    // position of query token 0, and the tokens this tile's last query sees
+    const int pos0 = ctx_seq - n_tok;
+    const int ctx = MULTI ? pos0 + (min(NQ, ht * 16 + 16) - 1) / G + 1 : ctx_seq;
     const int nblk = (ctx + BS - 1) / BS;
     const int PB = a.partition_blocks;
     const int nparts = max(1, (nblk + PB - 1) / PB);
     if (p >= nparts) return;
+    // the partial results go to the workspace unless the sequence has a
+    // single partition (the reduce merges by sequence)
+    const int nblk_seq = (ctx_seq + BS - 1) / BS;
+    const bool direct = SHARED ? false : (MULTI ? nblk_seq <= PB : nparts == 1);
     const int tok0 = p * PB * BS;
     const int tok1 = min(tok0 + PB * BS, ctx);
     const int nsteps = (tok1 - tok0 + 31) / 32;
     const int nheads = min(16, NQ - ht * 16);
-    // sequence and query head of query ht * 16 + i
-    auto query = [&](int i, int& qs, int& qh) {
+    // row of query ht * 16 + i in q and out ([rows, Hq, D])
+    auto query_row = [&](int i) -> int64_t {
         const int qi = ht * 16 + i;
-        qs = SHARED ? qi / G : s;
-        qh = SHARED ? kvh * G + qi % G : kvh * G + qi;
+        if constexpr (SHARED) return (int64_t)(qi / G) * a.num_q_heads + kvh * G + qi % G;
+        else if constexpr (MULTI) return (int64_t)(q_row0 + qi / G) * a.num_q_heads + kvh * G + qi % G;
+        else return (int64_t)s * a.num_q_heads + kvh * G + qi;
     };
+    // MULTI: the last token this lane's query sees (lanes without a query
+    // see the whole tile, so that their scores stay finite), and the first
+    // token that some query of the tile does not see
+    const int qlim = MULTI && n16 < nheads ? pos0 + (ht * 16 + n16) / G : ctx - 1;
+    const int mask_from = MULTI ? pos0 + (ht * 16) / G + 1 : ctx;
     const int blk0 = tok0 / BS;
     const int blk_end = (tok1 + BS - 1) / BS;
 
@@ -664,9 +689,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
     {
         float qs = 0.f;
         const bool live = n16 < nheads;
-        int qs_, qh_;
-        query(n16, qs_, qh_);
-        const uint16_t* qp = a.q + ((int64_t)qs_ * a.num_q_heads + qh_) * D + 16 * grp;
+        const uint16_t* qp = a.q + query_row(live ? n16 : 0) * D + 16 * grp;
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
             f16x8v x = (f16x8v)(_Float16)0;
@@ -746,7 +769,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[4 * mt + e] = (sc[mt][e] - qbias) * sk;
-        if (tok0 + 32 * (st + 1) > tok1) {   // the partition's last step: mask its end
+        if constexpr (MULTI) {
+            if (tok0 + 32 * (st + 1) > mask_from) {   // causal mask, per query
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (tok0 + 32 * st + 8 * grp + kappa<V4>(j) > qlim) x[j] = -INFINITY;
+            }
+        } else if (tok0 + 32 * (st + 1) > tok1) {   // the partition's last step: mask its end
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 if (tok0 + 32 * st + 8 * grp + kappa<V4>(j) >= tok1) x[j] = -INFINITY;
@@ -754,7 +783,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
         float bmax = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 8; ++j) bmax = fmaxf(bmax, x[j]);
-        // every step holds at least one valid token, so bmax is finite
+        // every step holds a token each query sees (MULTI: not always, see
+        // mref below), so bmax is finite
         bmax = fmaxf(bmax, shfl_xor_f(bmax, 16));
         bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
         if (bmax > m) {   // per head; lanes of one head agree
@@ -767,10 +797,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
         }
         uint32_t pw[4];
         float psum = 0.f;   // sum of the fp16 weights the MFMA takes
+        // a query that has seen no token yet (MULTI: all masked so far) keeps
+        // m = -inf; its weights are 0, not exp2(-inf + inf)
+        const float mref = MULTI && m == -INFINITY ? 0.f : m;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(x[2 * e] - m);
-            const float p1 = __builtin_amdgcn_exp2f(x[2 * e + 1] - m);
+            const float p0 = __builtin_amdgcn_exp2f(x[2 * e] - mref);
+            const float p1 = __builtin_amdgcn_exp2f(x[2 * e + 1] - mref);
             l += p0 + p1;
             const f16x2 h2 = f16x2{(_Float16)(p0 * sv), (_Float16)(p1 * sv)};
             pw[e] = __builtin_bit_cast(uint32_t, h2);
@@ -1076,10 +1109,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
             o = __builtin_fmaf(s_acc[k][hh][d], f, o);
         }
         const float res = L > 0.f ? o / L : 0.f;
-        int qs_, qh_;
-        query(hh, qs_, qh_);
-        const int64_t row = (int64_t)qs_ * a.num_q_heads + qh_;
-        if (nparts == 1 && !SHARED) {
+        const int64_t row = query_row(hh);
+        if (direct) {
             a.out[row * D + d] = f32_to_f16_bits(res);
         } else {
             const int64_t prow = row * a.max_partitions + p;
@@ -1092,22 +1123,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
     }
 }
 
-// One wavefront per (query head, sequence): merges the partitions of
-// sequences that have more than one.  Lane p holds partition p's (max, sum)
-// and weight; the partial outputs are read eight partitions at a time so that
-// their loads are in flight together.
-template <int BS, int D>
-__global__ __launch_bounds__(64) void attn_reduce(AttnArgs a) {
+// Merges partitions 0 .. nparts-1 of workspace row `row` into out (one
+// wavefront).  Lane p holds partition p's (max, sum) and weight; the partial
+// outputs are read eight partitions at a time so that their loads are in
+// flight together.
+template <int D>
+__device__ __forceinline__ void merge_partitions(const AttnArgs& a, int64_t row, int nparts) {
     constexpr int PER = D / 64;
     constexpr int BATCH = 8;
     const int lane = threadIdx.x;
-    const int h = blockIdx.x;
-    const int s = blockIdx.y;
-    const int ctx = a.context_lens[s];
-    const int nblk = (ctx + BS - 1) / BS;
-    const int nparts = max(1, (nblk + a.partition_blocks - 1) / a.partition_blocks);
-    if (nparts == 1) return;
-    const int64_t row = (int64_t)s * a.num_q_heads + h;
     const int64_t prow0 = row * a.max_partitions;
     const float* ml = a.ws_ml + prow0 * 2;
     const float* op = a.ws_out + prow0 * D + lane;
@@ -1147,6 +1171,36 @@ __global__ __launch_bounds__(64) void attn_reduce(AttnArgs a) {
     L = group_sum<64>(L);
 #pragma unroll
     for (int k = 0; k < PER; ++k) a.out[row * D + lane + 64 * k] = f32_to_f16_bits(L > 0.f ? o[k] / L : 0.f);
+}
+
+// One wavefront per (query head, sequence): merges the partitions of
+// sequences that have more than one.
+template <int BS, int D>
+__global__ __launch_bounds__(64) void attn_reduce(AttnArgs a) {
+    const int h = blockIdx.x;
+    const int s = blockIdx.y;
+    const int ctx = a.context_lens[s];
+    const int nblk = (ctx + BS - 1) / BS;
+    const int nparts = max(1, (nblk + a.partition_blocks - 1) / a.partition_blocks);
+    if (nparts == 1) return;
+    merge_partitions<D>(a, (int64_t)s * a.num_q_heads + h, nparts);
+}
+
+// Multi-query form: one wavefront per (query head, query token, sequence);
+// a query at position pos merges the partitions that hold tokens 0 .. pos.
+template <int BS, int D>
+__global__ __launch_bounds__(64) void attn_reduce_multi(AttnArgs a) {
+    const int h = blockIdx.x;
+    const int i = blockIdx.y;
+    const int s = blockIdx.z;
+    const int r0 = a.cu_q[s];
+    const int n = a.cu_q[s + 1] - r0;
+    if (i >= n) return;
+    const int ctx = a.context_lens[s];
+    const int PB = a.partition_blocks;
+    if ((ctx + BS - 1) / BS <= PB) return;   // one partition: written directly
+    const int pos = ctx - n + i;
+    merge_partitions<D>(a, (int64_t)(r0 + i) * a.num_q_heads + h, (pos / BS) / PB + 1);
 }
 
 // Waves per work group of the MHA kernel: 8 when a partition holds at least
@@ -1213,8 +1267,28 @@ hipError_t launch_shared(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Several query tokens per sequence: the grouped-query kernel for any group
+// size (MHA included: its 16-query tiles are then 16 tokens of one head),
+// over (partition, KV head x query tile, sequence), then the per-query reduce.
+template <int BS, int D, int CP>
+hipError_t launch_multi(const AttnArgs& a, hipStream_t stream) {
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int n_ht = (a.max_q_len * G + 15) / 16;
+    const dim3 grid = grid_dims(a.max_partitions, a.num_kv_heads * n_ht, a.num_seqs);
+    if (a.max_partitions == 1)
+        hipLaunchKernelGGL((attn_partition_gqa<BS, D, CP, 2, false, false, true>), grid, dim3(64 * 2), 0, stream, a);
+    else
+        hipLaunchKernelGGL((attn_partition_gqa<BS, D, CP, 4, false, false, true>), grid, dim3(64 * 4), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.max_partitions <= 1) return e;
+    hipLaunchKernelGGL((attn_reduce_multi<BS, D>), dim3((unsigned)a.num_q_heads, (unsigned)a.max_q_len,
+                                                        (unsigned)a.num_seqs), dim3(64), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int BS, int D, int CP>
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
+    if (a.cu_q) return launch_multi<BS, D, CP>(a, stream);
     if (a.shared_parts > 0) {
         const hipError_t e = launch_shared<BS, D, CP>(a, stream);
         if (e != hipSuccess) return e;

@@ -97,6 +97,11 @@ struct AttnArgs {
     // grouped launch over every query; the per-sequence grid starts after them
     int32_t shared_tokens;
     int32_t shared_parts;
+    // several query tokens per sequence (NULL for one): q and out rows
+    // cu_q[s] .. cu_q[s+1] - 1 are sequence s's last tokens; the workspace
+    // then has one row per query token and head
+    const int32_t* cu_q;
+    int32_t max_q_len;
 };
 
 struct CopyArgs {

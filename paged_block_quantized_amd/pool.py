@@ -212,6 +212,23 @@ class KVPool:
                                    workspace, nbytes, stream)
         return workspace
 
+    def multi_query(self, q, out, cu_seqlens, max_q_len, block_tables, context_lens, max_context_len,
+                    sm_scale, partition_size=0, workspace=None, stream=None, mem=None):
+        """Several query tokens per sequence (q, out [T, Hq, D]; sequence s's
+        rows cu_seqlens[s] .. cu_seqlens[s+1]-1 are its last stored tokens),
+        each attending causally."""
+        T, Hq, _ = q.shape
+        S = cu_seqlens.numel() - 1
+        need = L.paged_attn_multi_query_workspace_bytes(self.desc, S, T, Hq, max_q_len, max_context_len,
+                                                        partition_size)
+        if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        L.paged_attn_multi_query(self.desc, self.mem if mem is None else mem, q, out, S, Hq, cu_seqlens, T,
+                                 max_q_len, block_tables, block_tables.shape[1], context_lens, max_context_len,
+                                 sm_scale, partition_size, workspace, nbytes, stream)
+        return workspace
+
     def decode_shared_prefix(self, q, out, block_tables, context_lens, max_context_len, sm_scale,
                              partition_size, shared_tokens, k_new=None, v_new=None,
                              tail_slots=None, workspace=None, stream=None, mem=None):

@@ -642,3 +642,70 @@ def test_swap_then_decode_append_end_to_end(bs, vc):
     assert_pool_equal(pool, ref_pool, used)
     ref = attention.paged_decode(ref_pool, tabs, [c + 1 for c in ctx], q, 1 / np.sqrt(d))
     assert_close(out.cpu().numpy(), ref, "swap-e2e after")
+
+
+# ---- several query tokens per sequence (chunked prefill, candidates) --------
+
+MULTI_SHAPES = [
+    # (block_size, head_dim, v codec, query heads per KV head, KV heads)
+    (16, 128, "i8", 1, 2),
+    (32, 64, "i4", 1, 3),
+    (32, 128, "i4", 8, 2),
+    (16, 64, "i8", 4, 1),
+    (16, 128, "fp8", 2, 2),
+    (32, 128, "i8a", 8, 1),
+    (32, 64, "i8", 16, 1),
+    (16, 128, "i4", 7, 2),
+]
+
+
+@pytest.mark.parametrize("bs,d,vc,g,hkv", MULTI_SHAPES)
+def test_multi_query_ragged(bs, d, vc, g, hkv):
+    """paged_attn_multi_query: each sequence's last n stored tokens attend
+    causally (full prefills, chunks after a prefix, single tokens, chunks
+    across partitions and blocks), every partition size, against the oracle;
+    a one-token query equals the decode's output within tolerance."""
+    announce("multi", bs, d, vc, g, hkv)
+    seqs = [(1, 1), (17, 5), (100, 100), (700, 64), (33, 32), (2100, 17), (300, 1), (64, 40)]
+    ctx = [c for c, _ in seqs]
+    ns = [n for _, n in seqs]
+    hq = g * hkv
+    case = normal_case(ctx, hq, hkv, d, bs, vc, seed=11 * bs + d + g + hkv)
+    case.store_all()
+    assert_pool_equal(case.pool, case.opool)
+    rng = np.random.default_rng(bs + d + g)
+    T = sum(ns)
+    q_rows = rng.standard_normal((T, hq, d)).astype(np.float16)
+    # the last query of each sequence is the decode query
+    cu = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    for s in range(len(seqs)):
+        q_rows[cu[s + 1] - 1] = case.q[s]
+    sm = 1 / np.sqrt(d)
+    ref = attention.paged_multi_query(case.opool, [case.model.table(s)[0] for s in range(len(seqs))], ctx,
+                                      q_rows, cu, sm)
+    qd = torch.from_numpy(q_rows).cuda()
+    cud = torch.from_numpy(cu).cuda()
+    dec = case.decode()
+    for part in (0, 32, 96, 256, 2048):
+        out = torch.full_like(qd, float("nan"))
+        case.pool.multi_query(qd, out, cud, max(ns), case.tables, case.ctx_dev, max(ctx), sm, part)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert_close(got, ref, f"multi bs{bs} d{d} {vc} g{g} part{part}")
+        assert_close(got[cu[1:] - 1], dec.astype(np.float64), f"multi vs decode part{part}")
+
+
+def test_multi_query_validates():
+    from paged_block_quantized_amd import _lib as L
+    from paged_block_quantized_amd import KVPool
+    pool = KVPool(8, 16, 2, 64, "i8", max_seqs=1)
+    q = torch.zeros((4, 2, 64), dtype=torch.float16, device="cuda")
+    t = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
+    c = torch.tensor([40], dtype=torch.int32, device="cuda")
+    cu = torch.tensor([0, 4], dtype=torch.int32, device="cuda")
+    with pytest.raises(L.PBQError, match="max_q_len"):
+        L.paged_attn_multi_query(pool.desc, pool.mem, q, q, 1, 2, cu, 4, 0, t, 4, c, 40, 0.1)
+    with pytest.raises(L.PBQError, match="multiple of 32"):
+        L.paged_attn_multi_query(pool.desc, pool.mem, q, q, 1, 2, cu, 4, 4, t, 4, c, 40, 0.1, 16)
+    with pytest.raises(L.PBQError, match="workspace"):
+        L.paged_attn_multi_query(pool.desc, pool.mem, q, q, 1, 2, cu, 4, 4, t, 4, c, 40, 0.1, 32)
