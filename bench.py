@@ -163,6 +163,95 @@ def measure_swap(setup, reps):
     }
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def cpu_baseline_multi(setup, seconds):
+    """The oracle's multi-query attention on a bounded sample: sequence 0's
+    stored tokens quantized by the oracle, then its queries from the last one
+    backwards, single-threaded, until `seconds` have passed."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention, paged
+    from paged_block_quantized_amd import runner, workloads as W
+
+    w = setup.w
+    bs, n = w.block_size, w.q_len
+    ctx = int(setup.ctx[0])
+    k, v = W.kv_tokens(w, 0, ctx, "cpu")
+    nb = (ctx + bs - 1) // bs
+    pool = paged.PoolArrays(nb, w.num_kv_heads, bs, w.head_dim, k_codec=W.k_codec_of(w), v_codec=w.v_codec)
+    paged.store_range(pool, list(range(nb)), k.numpy(), v.numpy(), 0, ctx)
+    q = setup.q[:n].cpu().numpy()
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        khat, vhat = paged.gather_dequant(pool, list(range(nb)), ctx)
+        flops, done = 0, 0
+        while time.perf_counter() - t0 < seconds and done < n:
+            i = n - 1 - done
+            pos = ctx - n + i
+            attention.decode_attention(q[i], khat[:, :pos + 1], vhat[:, :pos + 1], setup.sm_scale)
+            flops += 4 * w.head_dim * w.num_q_heads * (pos + 1)
+            done += 1
+        dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"sequence 0 ({ctx} tokens stored): its last {done} of {n} queries, float64 "
+                      f"numpy, dequantization included, {dt:.1f} s"}
+
+
+def bench_multi(w, args):
+    """Multi-query (chunked prefill) attention: K timed calls of
+    paged_attn_multi_query over the workload's pool."""
+    import numpy as np
+    import torch
+
+    from paged_block_quantized_amd import runner, workloads as W
+    print(f"setup {w.name}", file=sys.stderr, flush=True)
+    setup = runner.setup_multi(w, partition=args.partition or 0)
+    flops = runner.multi_flops(w, setup.ctx)
+    nbytes = runner.multi_bytes(w, setup.ctx)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        setup.run()
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(K):
+        setup.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    call_ms = e0.elapsed_time(e1) / K
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (call_ms * 1e-3) / 1e12
+    T = w.num_seqs * w.q_len
+    line = {
+        "metric": "multi-query attention over the quantized paged cache, TFLOP/s (+ query tokens/s)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8" if w.v_codec != "fp8" else "fp8", "data": "synthetic",
+        "config": {"workload": w.name, "layers": 1, "num_seqs": w.num_seqs, "context": int(setup.ctx.max()),
+                   "query_tokens_per_seq": w.q_len, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size,
+                   "k_codec": W.k_codec_of(w), "v_codec": w.v_codec,
+                   "partition": setup.partition or "library default"},
+        "query_tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "unique_bytes_gbs": round(nbytes / (ms_step * 1e-3) / 1e9, 2),
+        "roofline": {"kernel": "paged_attn_multi_query (grouped-query MFMA kernel, multi-query mode; "
+                               "plus the per-query reduce when partitions are split)",
+                     "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops, "bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        print("cpu baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline_multi(setup, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,6 +284,9 @@ def main():
     from paged_block_quantized_amd import runner, workloads as W
 
     w = W.WORKLOADS[args.workload]
+    if w.q_len:
+        bench_multi(w, args)
+        return
     print(f"setup {w.name}", file=sys.stderr, flush=True)
     setup = runner.setup_decode(w, partition=args.partition)
     S = w.num_seqs

@@ -218,3 +218,77 @@ def store_step_bytes(w: W.Workload, ctx: np.ndarray) -> int:
     write = len(ctx) * Hkv * (bs * D * (8 + vbits) // 8 + meta)
     tail_write = int(np.sum(rows < bs)) * Hkv * D * 2 * 2
     return read + write + tail_write + len(ctx) * 4 * 4
+
+
+@dataclass
+class MultiSetup:
+    """A multi-query workload: every token stored, the last q_len of each
+    sequence as queries."""
+    w: W.Workload
+    pool: KVPool
+    ctx: np.ndarray
+    tables: torch.Tensor
+    ctx_dev: torch.Tensor
+    cu: torch.Tensor            # int32 [S+1]
+    q: torch.Tensor             # fp16 [S * q_len, Hq, D]
+    out: torch.Tensor
+    workspace: torch.Tensor
+    max_ctx: int
+    sm_scale: float
+    partition: int
+
+    def run(self, stream=None):
+        self.pool.multi_query(self.q, self.out, self.cu, self.w.q_len, self.tables, self.ctx_dev,
+                              self.max_ctx, self.sm_scale, self.partition, self.workspace, stream)
+
+
+def setup_multi(w: W.Workload, device="cuda", chunk_seqs=8, partition=0) -> MultiSetup:
+    """Build the pool for multi-query workload ``w`` with all its tokens
+    stored (the queries' own K/V included) and allocate the call's tensors."""
+    from . import _lib as L
+    ctx = W.context_lengths(w)
+    S, bs = w.num_seqs, w.block_size
+    N = blocks_needed(w, ctx)
+    pool = KVPool(N, bs, w.num_kv_heads, w.head_dim, w.v_codec, max_seqs=S,
+                  free_order=W.free_order(w, N), device=device)
+    for c0 in range(0, S, chunk_seqs):
+        ids = list(range(c0, min(S, c0 + chunk_seqs)))
+        ks, vs = [], []
+        for s in ids:
+            pool.alloc(s, int(ctx[s]))
+            k, v = W.kv_tokens(w, s, int(ctx[s]), device)
+            ks.append(k)
+            vs.append(v)
+        _store(pool, ks, vs, ids, [0] * len(ids), device)
+    max_blocks = int(np.max((ctx + bs - 1) // bs))
+    tables, ctx_h, _ = pool.batch_tables(list(range(S)), max_blocks)
+    q = W.multi_queries(w, device)
+    cu = torch.arange(0, S + 1, dtype=torch.int32, device=device) * w.q_len
+    max_ctx = int(ctx.max())
+    ws = L.paged_attn_multi_query_workspace_bytes(pool.desc, S, S * w.q_len, w.num_q_heads, w.q_len,
+                                                  max_ctx, partition)
+    torch.cuda.synchronize()
+    return MultiSetup(w=w, pool=pool, ctx=ctx, tables=tables.to(device), ctx_dev=ctx_h.to(device), cu=cu,
+                      q=q, out=torch.empty_like(q), workspace=torch.empty(max(ws, 16), dtype=torch.uint8,
+                                                                          device=device),
+                      max_ctx=max_ctx, sm_scale=1.0 / float(np.sqrt(w.head_dim)), partition=partition)
+
+
+def multi_flops(w: W.Workload, ctx: np.ndarray) -> int:
+    """Algorithmic flops of one multi-query pass: per query token, query head
+    and visible token, a D-long dot product and a D-long weighted sum (2 D
+    multiply-adds)."""
+    n = w.q_len
+    vis = int(np.sum(ctx - n)) * n + len(ctx) * n * (n + 1) // 2   # sum over queries of pos + 1
+    return 4 * w.head_dim * w.num_q_heads * vis
+
+
+def multi_bytes(w: W.Workload, ctx: np.ndarray) -> int:
+    """Algorithmic HBM bytes of one multi-query pass: every stored token's
+    codes and block metadata once, the query and output rows, the tables."""
+    S, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    vbits = 4 if w.v_codec == "i4" else 8
+    meta = 2 + 2 + (1 if w.v_codec in ("i4", "i8a") else 0)
+    blocks = int(np.sum((ctx + bs - 1) // bs))
+    return (int(np.sum(ctx)) * Hkv * D * (8 + vbits) // 8 + blocks * Hkv * meta
+            + 2 * S * w.q_len * Hq * D * 2 + blocks * 4 + (2 * S + 1) * 4)

@@ -30,6 +30,14 @@ caching"):
 * ``llama7b_fp8``, ``gqa70b_fp8``  the same shapes and draws with FP8 E4M3 K
                      and V (the cache dtype yunthe.com "vLLM deployment"
                      names); ``llama7b_i8a`` with INT8 asymmetric V.
+* ``prefill_chunk``  chunked prefill over a cached prefix (yunthe.com "prefix
+                     caching": only the new tokens are computed): 32
+                     sequences of 4096 stored tokens whose last 512 are the
+                     queries, llama7b's heads, channel factors and codecs;
+                     queries N(0,1).
+* ``prefill_chunk_gqa``  the same over gqa70b's heads and codecs (64 query
+                     heads on 8 KV heads, bs 32, INT8 K / INT4 V), 16
+                     sequences of 4096 tokens, 512 queries each.
 """
 
 from dataclasses import dataclass, field
@@ -56,6 +64,7 @@ class Workload:
     pool_blocks: int = 0           # 0: exactly the blocks needed
     partition: int = 0             # split-K partition tokens (0: library default)
     seed: int = 0
+    q_len: int = 0                 # query tokens per sequence (multi-query workloads)
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
 
@@ -76,6 +85,10 @@ WORKLOADS = {
                             channel_sigma=0.5, seed=2),
     "gqa70b_fp8": Workload("gqa70b_fp8", 128, 64, 8, 128, 32, "fp8", "uniform", (500, 2000),
                            outlier_frac=0.01, outlier_mult=8.0, seed=3),
+    "prefill_chunk": Workload("prefill_chunk", 32, 32, 32, 128, 16, "i8", "fixed", (4096,),
+                              channel_sigma=0.5, q_len=512, seed=6),
+    "prefill_chunk_gqa": Workload("prefill_chunk_gqa", 16, 64, 8, 128, 32, "i4", "fixed", (4096,),
+                                  q_len=512, seed=7),
 }
 
 
@@ -141,3 +154,9 @@ def kv_tokens(w: Workload, key, n_tokens: int, device="cpu"):
 def queries(w: Workload, device="cpu", step: int = 0):
     """fp16 queries [S, Hq, D] for decode step ``step``."""
     return _draw(w, (w.num_seqs, w.num_q_heads, w.head_dim), device, (12, step))
+
+
+def multi_queries(w: Workload, device="cpu"):
+    """fp16 query rows [S * q_len, Hq, D] of a multi-query workload, sequence
+    s's at rows s * q_len .. (s + 1) * q_len - 1."""
+    return _draw(w, (w.num_seqs * w.q_len, w.num_q_heads, w.head_dim), device, (13,))

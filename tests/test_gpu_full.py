@@ -177,3 +177,40 @@ def test_llama7b_swap_round_trip_full():
     for s in (group[1], group[-1]):
         announce("full swap llama7b", "oracle seq", s)
         check_sequence(setup, s, out, "llama7b after swap")
+
+
+@pytest.mark.parametrize("name", ["prefill_chunk", "prefill_chunk_gqa"])
+def test_multi_query_full(name):
+    """Chunked prefill at full size in the benchmark's launch configuration:
+    sampled query rows (first, middle and last of sampled sequences) against
+    the oracle; a second call gives bitwise the same output."""
+    from oracle import attention
+    from paged_block_quantized_amd import runner, workloads as W
+    w = W.WORKLOADS[name]
+    announce("full multi", name, "setup")
+    setup = runner.setup_multi(w)
+    setup.run()
+    torch.cuda.synchronize()
+    out = setup.out.clone()
+    assert torch.isfinite(out.float()).all()
+    setup.run()
+    torch.cuda.synchronize()
+    assert torch.equal(setup.out.view(torch.int16), out.view(torch.int16))
+    out = out.cpu().numpy()
+    n = w.q_len
+    for s in (0, w.num_seqs - 1):
+        announce("full multi", name, "oracle seq", s)
+        ctx = int(setup.ctx[s])
+        k, v = W.kv_tokens(w, s, ctx, "cuda")
+        nb = (ctx + w.block_size - 1) // w.block_size
+        ref_pool = paged.PoolArrays(nb, w.num_kv_heads, w.block_size, w.head_dim, k_codec=W.k_codec_of(w),
+                                    v_codec=w.v_codec)
+        paged.store_range(ref_pool, list(range(nb)), k.cpu().numpy(), v.cpu().numpy(), 0, ctx)
+        khat, vhat = paged.gather_dequant(ref_pool, list(range(nb)), ctx)
+        for i in (0, n // 2, n - 1):
+            row = s * n + i
+            pos = ctx - n + i
+            ref = attention.decode_attention(setup.q[row].cpu().numpy(), khat[:, :pos + 1], vhat[:, :pos + 1],
+                                             setup.sm_scale)
+            from gpu_util import assert_close
+            assert_close(out[row], ref, f"{name} seq {s} query {i}")
