@@ -613,8 +613,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // own position.  Query i of a sequence's tiles is token i / G with head
 // kvh * G + i % G; a tile reads only the tokens its last query can see, and
 // the steps past its first query's position mask per query.
+// Byte-coded V with D = 128 stages 34 KiB of LDS per 2-wave group, which caps
+// the staged kernels at two waves per SIMD: their register budget is then
+// that of two waves (no spills into AGPRs).
+template <int D, int CP, bool FUSED, bool MULTI>
+constexpr int gqa_waves_per_eu() {
+    return MULTI || (!FUSED && D == 128 && !codec_packed4(CP % 4)) ? 2 : PBQ_GQA_WAVES_PER_EU;
+}
+
 template <int BS, int D, int CP, int NW, bool FUSED, bool SHARED = false, bool MULTI = false>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA_WAVES_PER_EU))) void attn_partition_gqa(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(gqa_waves_per_eu<D, CP, FUSED, MULTI>())))
+void attn_partition_gqa(AttnArgs a) {
     constexpr int KC = CP / 4, VC = CP % 4;
     constexpr bool V4 = codec_packed4(VC);
     constexpr bool VZP = codec_has_zp(VC);
@@ -787,7 +796,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PBQ_GQA
         // mref below), so bmax is finite
         bmax = fmaxf(bmax, shfl_xor_f(bmax, 16));
         bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
-        if (bmax > m) {   // per head; lanes of one head agree
+        // per head; lanes of one head agree.  MULTI rescales only when the
+        // maximum grows by more than 8 (base 2): the weights exp2(x - m) then
+        // stay below 256 and most steps skip the rescale of the accumulators
+        // (the final division by l uses the same m, so the result is the same
+        // softmax)
+        if (bmax > m + (MULTI ? 8.f : 0.f)) {
             const float alpha = __builtin_amdgcn_exp2f(m - bmax);
 #pragma unroll
             for (int t = 0; t < DT; ++t) acc[t] *= alpha;
