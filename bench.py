@@ -243,7 +243,8 @@ def bench_multi(w, args):
         "roofline": {"kernel": "paged_attn_multi_query (grouped-query MFMA kernel, multi-query mode; "
                                "plus the per-query reduce when partitions are split)",
                      "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name),
                      "flops_per_launch": flops, "bytes_per_launch": nbytes},
     }
     if not args.no_cpu_baseline:

@@ -54,11 +54,16 @@ def run(args):
     from paged_block_quantized_amd import runner, workloads as W
 
     w = W.WORKLOADS[args.workload]
-    setup = runner.setup_decode(w)
-    if args.rotate > 1:
-        setup.add_replicas(args.rotate - 1)
-    for i in range(args.calls):
-        setup.step(r=i % max(1, args.rotate))
+    if w.q_len:   # a multi-query workload: its calls re-read one pool
+        setup = runner.setup_multi(w)
+        for _ in range(args.calls):
+            setup.run()
+    else:
+        setup = runner.setup_decode(w)
+        if args.rotate > 1:
+            setup.add_replicas(args.rotate - 1)
+        for i in range(args.calls):
+            setup.step(r=i % max(1, args.rotate))
     torch.cuda.synchronize()
     src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
