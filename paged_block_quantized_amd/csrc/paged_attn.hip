@@ -646,7 +646,24 @@ void attn_partition_gqa(AttnArgs a) {
     const int grp = lane >> 4;       // lane group
     const int G = a.num_q_heads / a.num_kv_heads;
     int p, tile, s;
-    grid_coords(p, tile, s);
+    if constexpr (MULTI) {
+        // Work groups go to the 8 XCDs (each with its own L2) round-robin by
+        // launch order.  Renumber so that each XCD takes a contiguous range
+        // of work items, ordered partition, then query tile, then KV head,
+        // then sequence: the tiles of one (sequence, KV head), which read the
+        // same codes, then run on one XCD at about the same time and share
+        // its L2 instead of each XCD fetching them.
+        const int P = gridDim.x, NT = gridDim.y;
+        const int total = P * NT * gridDim.z;
+        const int lin = blockIdx.x + P * (blockIdx.y + NT * blockIdx.z);
+        const int xcd = lin % 8, k = lin / 8, q8 = total / 8, r8 = total % 8;
+        const int work = xcd * q8 + min(xcd, r8) + k;
+        p = work % P;
+        tile = (work / P) % NT;
+        s = work / (P * NT);
+    } else {
+        grid_coords(p, tile, s);
+    }
     if constexpr (!SHARED && !MULTI) p += a.shared_parts;   // shared partitions ran in their own launch
     const int q_row0 = MULTI ? a.cu_q[s] : 0;               // the sequence's first query row
     const int n_tok = MULTI ? a.cu_q[s + 1] - q_row0 : 1;   // its query tokens
@@ -1288,7 +1305,9 @@ template <int BS, int D, int CP>
 hipError_t launch_multi(const AttnArgs& a, hipStream_t stream) {
     const int G = a.num_q_heads / a.num_kv_heads;
     const int n_ht = (a.max_q_len * G + 15) / 16;
-    const dim3 grid = grid_dims(a.max_partitions, a.num_kv_heads * n_ht, a.num_seqs);
+    // x = partition, y = KV head x query tile, z = sequence (the kernel
+    // renumbers the work groups over the XCDs)
+    const dim3 grid((unsigned)a.max_partitions, (unsigned)(a.num_kv_heads * n_ht), (unsigned)a.num_seqs);
     if (a.max_partitions == 1)
         hipLaunchKernelGGL((attn_partition_gqa<BS, D, CP, 2, false, false, true>), grid, dim3(64 * 2), 0, stream, a);
     else
