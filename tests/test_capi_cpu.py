@@ -314,6 +314,39 @@ def test_device_calls_validate_before_launch(lib):
     L.kv_copy_blocks(desc, mem, None, 0, 0)
 
 
+def test_multi_query_validates_before_launch(lib):
+    """paged_attn_multi_query checks its sizes, pointers, partition and
+    workspace on the host; zero tokens is a no-op."""
+    desc = L.make_desc(8, 16, 2, 64)
+    buf = ctypes.create_string_buffer(1 << 16)
+    base = (ctypes.addressof(buf) + 15) & ~15
+    mem = L.kv_pool_mem(base, base, base, base, None, base, base)
+    def mq(*args):
+        args = list(args) + [0] * (15 - len(args))       # partition_size 0 by default
+        return L.paged_attn_multi_query(*args, workspace=None, workspace_bytes=0, stream=0)
+    with pytest.raises(L.PBQError, match="multiple of num_kv_heads"):
+        mq(desc, mem, base, base, 1, 3, base, 4, 4, base, 4, base, 64, 0.1)
+    with pytest.raises(L.PBQError, match="max_q_len"):
+        mq(desc, mem, base, base, 1, 2, base, 4, 0, base, 4, base, 64, 0.1)
+    with pytest.raises(L.PBQError, match="max_q_len"):
+        mq(desc, mem, base, base, 1, 2, base, 4, 65, base, 8, base, 64, 0.1)
+    with pytest.raises(L.PBQError, match="multiple of 32"):
+        mq(desc, mem, base, base, 1, 2, base, 4, 4, base, 4, base, 64, 0.1, 48)
+    with pytest.raises(L.PBQError, match="max_blocks_per_seq"):
+        mq(desc, mem, base, base, 1, 2, base, 4, 4, base, 2, base, 64, 0.1)
+    with pytest.raises(L.PBQError, match="aligned"):
+        mq(desc, mem, base + 2, base, 1, 2, base, 4, 4, base, 4, base, 64, 0.1)
+    with pytest.raises(L.PBQError, match="workspace"):
+        mq(desc, mem, base, base, 1, 2, base, 4, 4, base, 64, base, 1024, 0.1, 32)
+    with pytest.raises(L.PBQError, match="tiles"):
+        mq(L.make_desc(8, 16, 1, 64), mem, base, base, 1, 64, base, 40000, 40000, base, 2500, base,
+           40000, 0.1, 64)
+    mq(desc, mem, base, base, 1, 2, base, 0, 0, base, 4, base, 64, 0.1)   # nothing to do
+    # workspace: one row of (D + 2) floats per query token, head and partition
+    assert L.paged_attn_multi_query_workspace_bytes(desc, 2, 10, 2, 5, 1024, 256) == 10 * 2 * 4 * (64 * 4 + 8)
+    assert L.paged_attn_multi_query_workspace_bytes(desc, 2, 10, 2, 5, 256, 256) == 0
+
+
 def test_workspace_bytes(lib):
     desc = L.make_desc(8192, 16, 32, 128)
     # 32 seqs x 32 heads x 8 partitions x (128 floats + max + sum)
