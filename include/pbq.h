@@ -441,10 +441,11 @@ kv_status paged_attn_decode_shared_prefix(const kv_pool_desc* desc, const kv_poo
  * 0 .. context_lens[s] - n_s + i:
  *   out[r, h, :] = sum_{t <= pos} softmax_t(sm_scale <q[r,h], K_hat[s,g,t]>)
  *                  V_hat[s, g, t, :],  g = h / (num_q_heads / Hkv).
- * cu_seqlens_dev int32 [num_seqs + 1] (cu[0] = 0, cu[num_seqs] = num_tokens);
- * max_q_len >= every n_s and <= max_context_len (sizes the grid); n_s <=
- * context_lens[s] is the caller's contract (a query that sees no token gives
- * a zero row).  All query heads of a KV head and 16 (token, head) pairs at a
+ * cu_seqlens_dev int32 [num_seqs + 1] (cu[0] = 0, non-decreasing,
+ * cu[num_seqs] = num_tokens); max_q_len >= every n_s and <= max_context_len
+ * (sizes the grid).  Device-resident arrays are not checked: cu_seqlens as
+ * stated, block ids < N and n_s <= context_lens[s] are the caller's contract
+ * (a query that sees no token gives a zero row).  All query heads of a KV head and 16 (token, head) pairs at a
  * time run on the matrix cores, for any group size.  partition_size: a
  * multiple of 32 and of block_size, or 0 for the library's choice; a query
  * merges only the partitions its position reaches.  Workspace:
