@@ -621,7 +621,11 @@ constexpr int gqa_waves_per_eu() {
     return MULTI || (!FUSED && D == 128 && !codec_packed4(CP % 4)) ? 2 : PBQ_GQA_WAVES_PER_EU;
 }
 
-template <int BS, int D, int CP, int NW, bool FUSED, bool SHARED = false, bool MULTI = false>
+//
+// TPW: 16-query tiles per work group (MULTI only).  With two, every K and V
+// code converted to fp16 feeds the matrix products of both tiles, which
+// halves the conversion work per query; the softmax stays per tile.
+template <int BS, int D, int CP, int NW, bool FUSED, bool SHARED = false, bool MULTI = false, int TPW = 1>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(gqa_waves_per_eu<D, CP, FUSED, MULTI>())))
 void attn_partition_gqa(AttnArgs a) {
     constexpr int KC = CP / 4, VC = CP % 4;
@@ -630,6 +634,8 @@ void attn_partition_gqa(AttnArgs a) {
     static_assert(!(FUSED && SHARED), "the shared prefix holds no current token");
     static_assert(!(MULTI && (FUSED || SHARED)), "multi-query launches store nothing and share nothing");
     static_assert(BS == 16 || BS == 32, "block size");
+    static_assert(TPW == 1 || (MULTI && TPW == 2), "two tiles per work group only for multi-query launches");
+    constexpr int QT = 16 * TPW;               // queries per work group
     constexpr bool STAGED = FUSED ? PBQ_GQA_STAGE_FUSED : PBQ_GQA_STAGE;
     constexpr int KS = D / 32;                 // QK k-steps
     constexpr int DT = D / 16;                 // PV dim tiles
@@ -669,8 +675,8 @@ void attn_partition_gqa(AttnArgs a) {
     const int n_tok = MULTI ? a.cu_q[s + 1] - q_row0 : 1;   // its query tokens
     // queries that share a KV head's tiles
     const int NQ = SHARED ? a.num_seqs * G : n_tok * G;
-    const int n_ht = (NQ + 15) / 16;
-    const int n_ht_grid = MULTI ? (a.max_q_len * G + 15) / 16 : n_ht;
+    const int n_ht = (NQ + QT - 1) / QT;
+    const int n_ht_grid = MULTI ? (a.max_q_len * G + QT - 1) / QT : n_ht;
     const int kvh = tile / n_ht_grid;
     const int ht = tile % n_ht_grid;
     if (MULTI && ht >= n_ht) return;
@@ -678,7 +684,7 @@ void attn_partition_gqa(AttnArgs a) {
     const int ctx_seq = SHARED ? a.shared_tokens : a.context_lens[s];
     // position of query token 0, and the tokens this tile's last query sees
     const int pos0 = ctx_seq - n_tok;
-    const int ctx = MULTI ? pos0 + (min(NQ, ht * 16 + 16) - 1) / G + 1 : ctx_seq;
+    const int ctx = MULTI ? pos0 + (min(NQ, ht * QT + QT) - 1) / G + 1 : ctx_seq;
     const int nblk = (ctx + BS - 1) / BS;
     const int PB = a.partition_blocks;
     const int nparts = max(1, (nblk + PB - 1) / PB);
@@ -690,10 +696,10 @@ void attn_partition_gqa(AttnArgs a) {
     const int tok0 = p * PB * BS;
     const int tok1 = min(tok0 + PB * BS, ctx);
     const int nsteps = (tok1 - tok0 + 31) / 32;
-    const int nheads = min(16, NQ - ht * 16);
-    // row of query ht * 16 + i in q and out ([rows, Hq, D])
+    const int nheads = min(QT, NQ - ht * QT);   // queries of the work group (tile T: 16 T ..)
+    // row of query ht * QT + i in q and out ([rows, Hq, D])
     auto query_row = [&](int i) -> int64_t {
-        const int qi = ht * 16 + i;
+        const int qi = ht * QT + i;
         if constexpr (SHARED) return (int64_t)(qi / G) * a.num_q_heads + kvh * G + qi % G;
         else if constexpr (MULTI) return (int64_t)(q_row0 + qi / G) * a.num_q_heads + kvh * G + qi % G;
         else return (int64_t)s * a.num_q_heads + kvh * G + qi;
@@ -701,8 +707,11 @@ void attn_partition_gqa(AttnArgs a) {
     // MULTI: the last token this lane's query sees (lanes without a query
     // see the whole tile, so that their scores stay finite), and the first
     // token that some query of the tile does not see
-    const int qlim = MULTI && n16 < nheads ? pos0 + (ht * 16 + n16) / G : ctx - 1;
-    const int mask_from = MULTI ? pos0 + (ht * 16) / G + 1 : ctx;
+    int qlim[TPW];
+#pragma unroll
+    for (int T = 0; T < TPW; ++T)
+        qlim[T] = MULTI && 16 * T + n16 < nheads ? pos0 + (ht * QT + 16 * T + n16) / G : ctx - 1;
+    const int mask_from = MULTI ? pos0 + (ht * QT) / G + 1 : ctx;
     const int blk0 = tok0 / BS;
     const int blk_end = (tok1 + BS - 1) / BS;
 
@@ -710,31 +719,38 @@ void attn_partition_gqa(AttnArgs a) {
     // j, lane group grp, element i is head dim 64 (j/2) + 16 grp + 8 (j%2) + i,
     // so that a lane's K codes for two k-steps are 16 contiguous bytes and
     // the four lane groups of one row read 64 contiguous bytes.
-    f16x8v qop[KS];
-    float qbias;
-    {
+    f16x8v qop[TPW][KS];
+    float qbias[TPW];
+#pragma unroll
+    for (int T = 0; T < TPW; ++T) {
         float qs = 0.f;
-        const bool live = n16 < nheads;
-        const uint16_t* qp = a.q + query_row(live ? n16 : 0) * D + 16 * grp;
+        const bool live = 16 * T + n16 < nheads;
+        const uint16_t* qp = a.q + query_row(live ? 16 * T + n16 : 0) * D + 16 * grp;
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
             f16x8v x = (f16x8v)(_Float16)0;
             if (live) x = *(const f16x8v*)(qp + 64 * (j / 2) + 8 * (j % 2));
-            qop[j] = x;
+            qop[T][j] = x;
 #pragma unroll
             for (int i = 0; i < 8; ++i) qs += (float)x[i];
         }
         qs += shfl_xor_f(qs, 16);
         qs += shfl_xor_f(qs, 32);
-        qbias = code_bias<KC>(0.f) * qs;
+        qbias[T] = code_bias<KC>(0.f) * qs;
     }
 
     const float c2 = a.sm_scale * kLog2e * code_unit<KC>();
     constexpr float vunit = code_unit<VC>();
-    float m = -INFINITY, l = 0.f, zacc = 0.f;
-    f32x4 acc[DT];
+    float m[TPW], l[TPW], zacc[TPW];
+    f32x4 acc[TPW][DT];
 #pragma unroll
-    for (int t = 0; t < DT; ++t) acc[t] = (f32x4)0.f;
+    for (int T = 0; T < TPW; ++T) {
+        m[T] = -INFINITY;
+        l[T] = 0.f;
+        zacc[T] = 0.f;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) acc[T][t] = (f32x4)0.f;
+    }
 
     const int32_t* tab = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
     // the block (within a step) whose K row this lane loads for tile mt, and
@@ -775,78 +791,85 @@ void attn_partition_gqa(AttnArgs a) {
     // One step: scores on MFMA, online softmax, PV on MFMA.  sk, sv, zpv are
     // this lane's block's scales (sk times sm_scale log2 e) and zero point.
     auto compute_step = [&](const Raw& r, int st, float sk, float sv, float zpv) {
-        // ---- S^T = K_hat Q^T ----------------------------------------------
-        f32x4 sc[2];
+        // ---- S^T = K_hat Q^T (each converted K operand serves every tile) --
+        f32x4 sc[TPW][2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-            sc[mt] = (f32x4)0.f;
+#pragma unroll
+            for (int T = 0; T < TPW; ++T) sc[T][mt] = (f32x4)0.f;
 #pragma unroll
             for (int j = 0; j < KS; ++j) {
                 const uint32_t w0 = r.k[mt][j / 2][2 * (j & 1)];
                 const uint32_t w1 = r.k[mt][j / 2][2 * (j & 1) + 1];
                 const uint32_t a4[4] = {pair_lo<KC>(w0), pair_hi<KC>(w0), pair_lo<KC>(w1), pair_hi<KC>(w1)};
                 const f16x8v aop = __builtin_bit_cast(f16x8v, a4);
-                sc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, qop[j], sc[mt], 0, 0, 0);
+#pragma unroll
+                for (int T = 0; T < TPW; ++T)
+                    sc[T][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, qop[T][j], sc[T][mt], 0, 0, 0);
             }
         }
-        // lane (head n16, group grp): sc[mt][i] is token 8 grp + kappa(4 mt + i)
-        float x[8];
+        f16x8v pop[TPW];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int T = 0; T < TPW; ++T) {
+            // lane (head n16, group grp): sc[T][mt][i] is token 8 grp + kappa(4 mt + i)
+            float x[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[4 * mt + e] = (sc[mt][e] - qbias) * sk;
-        if constexpr (MULTI) {
-            if (tok0 + 32 * (st + 1) > mask_from) {   // causal mask, per query
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[4 * mt + e] = (sc[T][mt][e] - qbias[T]) * sk;
+            if constexpr (MULTI) {
+                if (tok0 + 32 * (st + 1) > mask_from) {   // causal mask, per query
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (tok0 + 32 * st + 8 * grp + kappa<V4>(j) > qlim[T]) x[j] = -INFINITY;
+                }
+            } else if (tok0 + 32 * (st + 1) > tok1) {   // the partition's last step: mask its end
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    if (tok0 + 32 * st + 8 * grp + kappa<V4>(j) > qlim) x[j] = -INFINITY;
+                    if (tok0 + 32 * st + 8 * grp + kappa<V4>(j) >= tok1) x[j] = -INFINITY;
             }
-        } else if (tok0 + 32 * (st + 1) > tok1) {   // the partition's last step: mask its end
+            float bmax = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (tok0 + 32 * st + 8 * grp + kappa<V4>(j) >= tok1) x[j] = -INFINITY;
+            for (int j = 0; j < 8; ++j) bmax = fmaxf(bmax, x[j]);
+            // every step holds a token each query sees (MULTI: not always, see
+            // mref below), so bmax is finite
+            bmax = fmaxf(bmax, shfl_xor_f(bmax, 16));
+            bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
+            // per head; lanes of one head agree.  MULTI rescales only when the
+            // maximum grows by more than 8 (base 2): the weights exp2(x - m) then
+            // stay below 256 and most steps skip the rescale of the accumulators
+            // (the final division by l uses the same m, so the result is the same
+            // softmax)
+            if (bmax > m[T] + (MULTI ? 8.f : 0.f)) {
+                const float alpha = __builtin_amdgcn_exp2f(m[T] - bmax);
+#pragma unroll
+                for (int t = 0; t < DT; ++t) acc[T][t] *= alpha;
+                l[T] *= alpha;
+                zacc[T] *= alpha;
+                m[T] = bmax;
+            }
+            uint32_t pw[4];
+            float psum = 0.f;   // sum of the fp16 weights the MFMA takes
+            // a query that has seen no token yet (MULTI: all masked so far) keeps
+            // m = -inf; its weights are 0, not exp2(-inf + inf)
+            const float mref = MULTI && m[T] == -INFINITY ? 0.f : m[T];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = __builtin_amdgcn_exp2f(x[2 * e] - mref);
+                const float p1 = __builtin_amdgcn_exp2f(x[2 * e + 1] - mref);
+                l[T] += p0 + p1;
+                const f16x2 h2 = f16x2{(_Float16)(p0 * sv), (_Float16)(p1 * sv)};
+                pw[e] = __builtin_bit_cast(uint32_t, h2);
+                psum = __builtin_amdgcn_fdot2(h2, f16x2{(_Float16)1, (_Float16)1}, psum, false);
+            }
+            pop[T] = __builtin_bit_cast(f16x8v, pw);
+            // the codes enter the MFMA as bias + u (exact fp16); the weighted
+            // bias and zero point, (bias + zp) times the weights' sum, are the
+            // same for every dim and come off once, at the end
+            if constexpr (VC != KV_CODEC_FP8_E4M3) zacc[T] = __builtin_fmaf(code_bias<VC>(zpv), psum, zacc[T]);
         }
-        float bmax = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) bmax = fmaxf(bmax, x[j]);
-        // every step holds a token each query sees (MULTI: not always, see
-        // mref below), so bmax is finite
-        bmax = fmaxf(bmax, shfl_xor_f(bmax, 16));
-        bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
-        // per head; lanes of one head agree.  MULTI rescales only when the
-        // maximum grows by more than 8 (base 2): the weights exp2(x - m) then
-        // stay below 256 and most steps skip the rescale of the accumulators
-        // (the final division by l uses the same m, so the result is the same
-        // softmax)
-        if (bmax > m + (MULTI ? 8.f : 0.f)) {
-            const float alpha = __builtin_amdgcn_exp2f(m - bmax);
-#pragma unroll
-            for (int t = 0; t < DT; ++t) acc[t] *= alpha;
-            l *= alpha;
-            zacc *= alpha;
-            m = bmax;
-        }
-        uint32_t pw[4];
-        float psum = 0.f;   // sum of the fp16 weights the MFMA takes
-        // a query that has seen no token yet (MULTI: all masked so far) keeps
-        // m = -inf; its weights are 0, not exp2(-inf + inf)
-        const float mref = MULTI && m == -INFINITY ? 0.f : m;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(x[2 * e] - mref);
-            const float p1 = __builtin_amdgcn_exp2f(x[2 * e + 1] - mref);
-            l += p0 + p1;
-            const f16x2 h2 = f16x2{(_Float16)(p0 * sv), (_Float16)(p1 * sv)};
-            pw[e] = __builtin_bit_cast(uint32_t, h2);
-            psum = __builtin_amdgcn_fdot2(h2, f16x2{(_Float16)1, (_Float16)1}, psum, false);
-        }
-        const f16x8v pop = __builtin_bit_cast(f16x8v, pw);
-        // the codes enter the MFMA as bias + u (exact fp16); the weighted
-        // bias and zero point, (bias + zp) times the weights' sum, are the
-        // same for every dim and come off once, at the end
-        if constexpr (VC != KV_CODEC_FP8_E4M3) zacc = __builtin_fmaf(code_bias<VC>(zpv), psum, zacc);
 
-        // ---- O^T += (bias + V codes)^T P^T ---------------------------------
+        // ---- O^T += (bias + V codes)^T P^T (each converted V operand serves every tile)
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
             uint32_t a4[4];
@@ -863,7 +886,10 @@ void attn_partition_gqa(AttnArgs a) {
                 a4[2] = pair_lo<VC>(r.v[t][1]);
                 a4[3] = pair_hi<VC>(r.v[t][1]);
             }
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8v, a4), pop, acc[t], 0, 0, 0);
+            const f16x8v vop = __builtin_bit_cast(f16x8v, a4);
+#pragma unroll
+            for (int T = 0; T < TPW; ++T)
+                acc[T][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[T], acc[T][t], 0, 0, 0);
         }
     };
 
@@ -927,7 +953,7 @@ void attn_partition_gqa(AttnArgs a) {
     static_assert(SD == 2 || SD == 3, "stages");
     static_assert(BPS * VT % 1024 == 0 && (VT % 1024 == 0 || (BPS == 2 && VT == 512)), "V tile loads");
     constexpr int STAGE_BYTES = STAGED ? NW * SD * STG : 16;
-    constexpr int ACC_BYTES = NW * 16 * (D + 4) * 4;
+    constexpr int ACC_BYTES = NW * QT * (D + 4) * 4;
     __shared__ __align__(16) uint8_t s_stage[STAGE_BYTES > ACC_BYTES ? STAGE_BYTES : ACC_BYTES];
     uint8_t* const my_stage = s_stage + w * SD * STG;   // w is wave-uniform
     // lane offsets: where this lane's 16 bytes of a K load come from (row
@@ -1103,27 +1129,34 @@ void attn_partition_gqa(AttnArgs a) {
     }
     // lanes of one head split its tokens by group: sum their partial sums,
     // and take the weighted code bias off every dim
-    l += shfl_xor_f(l, 16);
-    l += shfl_xor_f(l, 32);
-    zacc += shfl_xor_f(zacc, 16);
-    zacc += shfl_xor_f(zacc, 32);
 #pragma unroll
-    for (int t = 0; t < DT; ++t) acc[t] -= zacc;
+    for (int T = 0; T < TPW; ++T) {
+        l[T] += shfl_xor_f(l[T], 16);
+        l[T] += shfl_xor_f(l[T], 32);
+        zacc[T] += shfl_xor_f(zacc[T], 16);
+        zacc[T] += shfl_xor_f(zacc[T], 32);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) acc[T][t] -= zacc[T];
+    }
 
     // Merge the waves' partial results in LDS (over the staging area, once
     // every wave is done with it).  Rows are padded by 4 floats so that the
     // 16-byte writes of one instruction spread over the banks.
     constexpr int DP = D + 4;
-    float (*s_acc)[16][DP] = reinterpret_cast<float (*)[16][DP]>(s_stage);
-    __shared__ float s_ml[NW][16][2];
+    float (*s_acc)[QT][DP] = reinterpret_cast<float (*)[QT][DP]>(s_stage);
+    __shared__ float s_ml[NW][QT][2];
     if constexpr (STAGED) __syncthreads();
-    if (n16 < nheads) {
-        // acc[t] holds dims 16t + 4 grp .. +3 of head n16
 #pragma unroll
-        for (int t = 0; t < DT; ++t) *(f32x4*)&s_acc[w][n16][16 * t + 4 * grp] = acc[t];
-        if (grp == 0) {
-            s_ml[w][n16][0] = m;
-            s_ml[w][n16][1] = l;
+    for (int T = 0; T < TPW; ++T) {
+        const int qq = 16 * T + n16;   // the lane's query in the work group
+        if (qq < nheads) {
+            // acc[T][t] holds dims 16t + 4 grp .. +3 of query qq
+#pragma unroll
+            for (int t = 0; t < DT; ++t) *(f32x4*)&s_acc[w][qq][16 * t + 4 * grp] = acc[T][t];
+            if (grp == 0) {
+                s_ml[w][qq][0] = m[T];
+                s_ml[w][qq][1] = l[T];
+            }
         }
     }
     __syncthreads();
@@ -1298,21 +1331,34 @@ hipError_t launch_shared(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Several query tokens per sequence: the grouped-query kernel for any group
-// size (MHA included: its 16-query tiles are then 16 tokens of one head),
-// over (partition, KV head x query tile, sequence), then the per-query reduce.
-template <int BS, int D, int CP>
-hipError_t launch_multi(const AttnArgs& a, hipStream_t stream) {
+// The partition launch of a multi-query call with TPW 16-query tiles per
+// work group.
+template <int BS, int D, int CP, int TPW>
+hipError_t launch_multi_tiles(const AttnArgs& a, hipStream_t stream) {
     const int G = a.num_q_heads / a.num_kv_heads;
-    const int n_ht = (a.max_q_len * G + 15) / 16;
+    const int n_ht = (a.max_q_len * G + 16 * TPW - 1) / (16 * TPW);
     // x = partition, y = KV head x query tile, z = sequence (the kernel
     // renumbers the work groups over the XCDs)
     const dim3 grid((unsigned)a.max_partitions, (unsigned)(a.num_kv_heads * n_ht), (unsigned)a.num_seqs);
     if (a.max_partitions == 1)
-        hipLaunchKernelGGL((attn_partition_gqa<BS, D, CP, 2, false, false, true>), grid, dim3(64 * 2), 0, stream, a);
+        hipLaunchKernelGGL((attn_partition_gqa<BS, D, CP, 2, false, false, true, TPW>), grid, dim3(64 * 2), 0,
+                           stream, a);
     else
-        hipLaunchKernelGGL((attn_partition_gqa<BS, D, CP, 4, false, false, true>), grid, dim3(64 * 4), 0, stream, a);
-    hipError_t e = hipGetLastError();
+        hipLaunchKernelGGL((attn_partition_gqa<BS, D, CP, 4, false, false, true, TPW>), grid, dim3(64 * 4), 0,
+                           stream, a);
+    return hipGetLastError();
+}
+
+// Several query tokens per sequence: the grouped-query kernel for any group
+// size (MHA included: its 16-query tiles are then 16 tokens of one head),
+// over (partition, KV head x query tile, sequence), then the per-query reduce.
+// Work groups take two 16-query tiles when a sequence's queries of one KV
+// head fill more than one.
+template <int BS, int D, int CP>
+hipError_t launch_multi(const AttnArgs& a, hipStream_t stream) {
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const hipError_t e = a.max_q_len * G > 16 ? launch_multi_tiles<BS, D, CP, 2>(a, stream)
+                                              : launch_multi_tiles<BS, D, CP, 1>(a, stream);
     if (e != hipSuccess || a.max_partitions <= 1) return e;
     hipLaunchKernelGGL((attn_reduce_multi<BS, D>), dim3((unsigned)a.num_q_heads, (unsigned)a.max_q_len,
                                                         (unsigned)a.num_seqs), dim3(64), 0, stream, a);

@@ -695,6 +695,36 @@ def test_multi_query_ragged(bs, d, vc, g, hkv):
         assert_close(got[cu[1:] - 1], dec.astype(np.float64), f"multi vs decode part{part}")
 
 
+@pytest.mark.parametrize("bs,d,vc,g,hkv,ns", [
+    (16, 128, "i8", 1, 2, [1, 16, 9, 3]),
+    (32, 128, "i4", 8, 2, [2, 1, 2]),
+    (32, 64, "i8", 16, 1, [1, 1]),
+    (16, 64, "fp8", 4, 2, [4, 3, 1, 4]),
+])
+def test_multi_query_single_tile(bs, d, vc, g, hkv, ns):
+    """Calls whose queries of one (sequence, KV head) fit one 16-query tile
+    (n G <= 16) take the one-tile work groups; against the oracle at every
+    partition size."""
+    announce("multi-one-tile", bs, d, vc, g, hkv, ns)
+    ctx = [50, 700, 33, 2100][:len(ns)]
+    hq = g * hkv
+    case = normal_case(ctx, hq, hkv, d, bs, vc, seed=7 * bs + d + g)
+    case.store_all()
+    rng = np.random.default_rng(bs + d + g + 1)
+    q_rows = rng.standard_normal((sum(ns), hq, d)).astype(np.float16)
+    cu = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    sm = 1 / np.sqrt(d)
+    ref = attention.paged_multi_query(case.opool, [case.model.table(s)[0] for s in range(len(ns))], ctx,
+                                      q_rows, cu, sm)
+    qd = torch.from_numpy(q_rows).cuda()
+    cud = torch.from_numpy(cu).cuda()
+    for part in (0, 32, 256):
+        out = torch.full_like(qd, float("nan"))
+        case.pool.multi_query(qd, out, cud, max(ns), case.tables, case.ctx_dev, max(ctx), sm, part)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), ref, f"multi one tile bs{bs} d{d} {vc} g{g} part{part}")
+
+
 def test_multi_query_validates():
     from paged_block_quantized_amd import _lib as L
     from paged_block_quantized_amd import KVPool
