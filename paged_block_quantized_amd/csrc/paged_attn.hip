@@ -812,21 +812,27 @@ void attn_partition_gqa(AttnArgs a) {
 #pragma unroll
         for (int T = 0; T < TPW; ++T) {
             // lane (head n16, group grp): sc[T][mt][i] is token 8 grp + kappa(4 mt + i)
+            // (sc - qbias) sk as one rounding of sc sk plus the product -qbias sk
             float x[8];
+            const float nb = -qbias[T] * sk;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[4 * mt + e] = (sc[T][mt][e] - qbias[T]) * sk;
+                for (int e = 0; e < 4; ++e) x[4 * mt + e] = __builtin_fmaf(sc[T][mt][e], sk, nb);
+            // slot j holds token base + kappa(j) of the lane group's run
+            const int base = tok0 + 32 * st + 8 * grp;
             if constexpr (MULTI) {
                 if (tok0 + 32 * (st + 1) > mask_from) {   // causal mask, per query
+                    const int lim = qlim[T] - base;          // slots with kappa(j) > lim are masked
 #pragma unroll
                     for (int j = 0; j < 8; ++j)
-                        if (tok0 + 32 * st + 8 * grp + kappa<V4>(j) > qlim[T]) x[j] = -INFINITY;
+                        if (kappa<V4>(j) > lim) x[j] = -INFINITY;
                 }
             } else if (tok0 + 32 * (st + 1) > tok1) {   // the partition's last step: mask its end
+                const int lim = tok1 - base;
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    if (tok0 + 32 * st + 8 * grp + kappa<V4>(j) >= tok1) x[j] = -INFINITY;
+                    if (kappa<V4>(j) >= lim) x[j] = -INFINITY;
             }
             float bmax = -INFINITY;
 #pragma unroll
