@@ -253,6 +253,108 @@ def bench_multi(w, args):
     print(json.dumps(line), flush=True)
 
 
+def cpu_baseline_store(setup, seconds):
+    """The oracle's quantize-and-store of whole prompts (the same rows the
+    GPU stores), single-threaded, for up to ``seconds``."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged
+    from paged_block_quantized_amd import runner, workloads as W
+
+    w, T = setup.w, setup.tokens
+    H, D, bs = w.num_kv_heads, w.head_dim, w.block_size
+    nb = (T + bs - 1) // bs
+    per_prompt = runner.prefill_store_bytes(w) // w.num_seqs
+    done, spent = 0, 0.0
+    with threadpool_limits(1):
+        for s in range(w.num_seqs):
+            hk = setup.k[s * T:(s + 1) * T].cpu().numpy()
+            hv = setup.v[s * T:(s + 1) * T].cpu().numpy()
+            ref = paged.PoolArrays(nb, H, bs, D, w.v_codec == "i4", k_codec=W.k_codec_of(w), v_codec=w.v_codec)
+            t0 = time.perf_counter()
+            paged.store_range(ref, list(range(nb)), hk, hv, 0, T)
+            spent += time.perf_counter() - t0
+            done += 1
+            if spent >= seconds:
+                break
+    return {"value": round(done * per_prompt / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tokens_stored_per_s": round(done * T / spent, 1),
+            "sample": f"{done} of the {w.num_seqs} prompts ({T} tokens each, all KV heads) stored by the oracle, "
+                      f"{spent:.1f} s, one thread"}
+
+
+def bench_store(w, args):
+    """Quantize-and-store: K timed calls of kv_quantize_store that store every
+    prompt of the workload (re-quantizing the same blocks each call), then
+    the one-token append steps of the same workload, each timed alone."""
+    import numpy as np
+    import torch
+
+    from paged_block_quantized_amd import runner, workloads as W
+    print(f"setup {w.name}", file=sys.stderr, flush=True)
+    setup = runner.setup_prefill_store(w)
+    nbytes = runner.prefill_store_bytes(w)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        setup.run()
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(K):
+        setup.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+    call_ms = e0.elapsed_time(e1) / K
+    T = w.num_seqs * setup.tokens
+
+    # one-token appends to 64 partially filled blocks, 16 steps (every block
+    # crosses its fill point once); the host reserves the positions between
+    # the timed calls
+    print("appends", file=sys.stderr, flush=True)
+    app = runner.setup_append(w)
+    app_ms, app_bytes = [], []
+    for step in range(16):
+        args_ = app.inputs(step)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        app.pool.quantize_store(*args_, 1)
+        b.record(stream)
+        torch.cuda.synchronize()
+        app_ms.append(a.elapsed_time(b))
+        app_bytes.append(runner.store_step_bytes(w, app.fill + step + 1))
+    line = {
+        "metric": "quantize-and-store GB/s (% of HBM peak) + tokens stored/s",
+        "value": round(nbytes / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "tokens_per_prompt": setup.tokens,
+                   "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "k_codec": W.k_codec_of(w), "v_codec": w.v_codec, "pool_blocks": setup.pool.num_blocks},
+        "pct_of_hbm_peak": round(100 * nbytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "tokens_stored_per_s": round(T / (ms_step * 1e-3), 1),
+        "step_bytes": nbytes,
+        "append": {"calls": 16, "sequences": w.num_seqs, "mean_us": round(1e3 * float(np.mean(app_ms)), 2),
+                   "p10_us": round(1e3 * float(np.percentile(app_ms, 10)), 2),
+                   "p90_us": round(1e3 * float(np.percentile(app_ms, 90)), 2),
+                   "mean_bytes": int(np.mean(app_bytes)),
+                   "note": "one kv_quantize_store call per step, each timed alone with HIP events "
+                           "(launch-latency bound)"},
+        "roofline": {"kernel": "kv_quantize_store (quantize_store_kernel), one call storing every prompt",
+                     "bound": "hbm", "achieved": round(nbytes / (call_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(nbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name), "bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        print("cpu baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline_store(setup, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,6 +389,9 @@ def main():
     w = W.WORKLOADS[args.workload]
     if w.q_len:
         bench_multi(w, args)
+        return
+    if w.store_only:
+        bench_store(w, args)
         return
     print(f"setup {w.name}", file=sys.stderr, flush=True)
     setup = runner.setup_decode(w, partition=args.partition)

@@ -317,3 +317,98 @@ def multi_bytes(w: W.Workload, ctx: np.ndarray) -> int:
     blocks = int(np.sum((ctx + bs - 1) // bs))
     return (int(np.sum(ctx)) * Hkv * D * (8 + vbits) // 8 + blocks * Hkv * meta
             + 2 * S * w.q_len * Hq * D * 2 + blocks * 4 + (2 * S + 1) * 4)
+
+
+@dataclass
+class StoreSetup:
+    """A quantize-and-store workload: every sequence's prompt (fp16 K/V in
+    HBM) stored in one call into blocks the allocator took from a pool in
+    seeded random order."""
+    w: W.Workload
+    pool: KVPool
+    k: torch.Tensor             # fp16 [S * T, Hkv, D]
+    v: torch.Tensor
+    cu: torch.Tensor            # int32 [S+1]
+    start: torch.Tensor         # int32 [S] (zeros)
+    tables: torch.Tensor
+    slots: torch.Tensor
+    tokens: int                 # tokens per prompt
+
+    def run(self, stream=None):
+        self.pool.quantize_store(self.k, self.v, self.cu, self.start, self.tables, self.slots, self.tokens,
+                                 stream)
+
+
+def setup_prefill_store(w: W.Workload, device="cuda") -> StoreSetup:
+    """The pool and inputs of a store-only workload (all prompts allocated,
+    nothing stored yet)."""
+    S, T, bs = w.num_seqs, w.ctx[0], w.block_size
+    N = w.pool_blocks or S * ((T + bs - 1) // bs)
+    pool = KVPool(N, bs, w.num_kv_heads, w.head_dim, w.v_codec, max_seqs=S,
+                  free_order=W.free_order(w, N), device=device)
+    for s in range(S):
+        pool.alloc(s, T)
+    tables, _, slots = pool.batch_tables(list(range(S)), (T + bs - 1) // bs)
+    ks, vs = zip(*[W.kv_tokens(w, s, T, device) for s in range(S)])
+    k, v = torch.cat(ks), torch.cat(vs)
+    del ks, vs
+    cu = torch.arange(0, (S + 1) * T, T, dtype=torch.int32, device=device)
+    torch.cuda.synchronize()
+    return StoreSetup(w=w, pool=pool, k=k, v=v, cu=cu, start=torch.zeros(S, dtype=torch.int32, device=device),
+                      tables=tables.to(device), slots=slots.to(device), tokens=T)
+
+
+def prefill_store_bytes(w: W.Workload) -> int:
+    """Algorithmic HBM bytes of storing every prompt of a store-only
+    workload: the fp16 K and V rows read, the codes and per-(block, head)
+    metadata written, the block tables read."""
+    S, T, Hkv, D, bs = w.num_seqs, w.ctx[0], w.num_kv_heads, w.head_dim, w.block_size
+    vbits = 4 if w.v_codec == "i4" else 8
+    meta = 2 + 2 + (1 if w.v_codec in ("i4", "i8a") else 0)
+    tok = S * T
+    blocks = S * ((T + bs - 1) // bs)
+    return tok * Hkv * D * 2 * 2 + tok * Hkv * D * (8 + vbits) // 8 + blocks * Hkv * meta + blocks * 4
+
+
+@dataclass
+class AppendSetup:
+    """One-token appends to sequences whose last block is partly filled: each
+    step reserves a position per sequence on the host and stores the new
+    token, re-quantizing its block from the tail slot's exact rows."""
+    pool: KVPool
+    hist: list                  # per sequence (K, V) fp16 [fill + steps, Hkv, D] on the device
+    fill: np.ndarray            # rows stored before the first step
+
+    def inputs(self, step, device="cuda"):
+        """Reserve step `step`'s positions and return the call's arguments."""
+        S = len(self.fill)
+        for s in range(S):
+            assert self.pool.append(s, 1) == []
+        tables, _, slots = self.pool.batch_tables(list(range(S)), 2)
+        kn = torch.cat([h[0][f + step:f + step + 1] for h, f in zip(self.hist, self.fill)])
+        vn = torch.cat([h[1][f + step:f + step + 1] for h, f in zip(self.hist, self.fill)])
+        cu = torch.arange(S + 1, dtype=torch.int32, device=device)
+        st = torch.tensor(self.fill + step, dtype=torch.int32, device=device)
+        return kn, vn, cu, st, tables.to(device), slots.to(device)
+
+
+def setup_append(w: W.Workload, steps: int = 16, device="cuda") -> AppendSetup:
+    """The store workload's sequences restarted with 1..bs-1 stored rows each
+    (seeded), ready for `steps` one-token appends that carry every block
+    through its fill point."""
+    S, bs = w.num_seqs, w.block_size
+    rng = np.random.default_rng([w.seed, 7])
+    fill = rng.integers(1, bs, S)
+    pool = KVPool(w.pool_blocks or S * 2, bs, w.num_kv_heads, w.head_dim, w.v_codec, max_seqs=S,
+                  free_order=W.free_order(w, w.pool_blocks or S * 2), device=device)
+    for s in range(S):
+        pool.alloc(s, int(fill[s]))
+    hist = [W.kv_tokens(w, 100 + s, int(fill[s]) + steps, device) for s in range(S)]
+    tables, _, slots = pool.batch_tables(list(range(S)), 2)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(fill)]), dtype=torch.int32, device=device)
+    pool.quantize_store(torch.cat([h[0][:f] for h, f in zip(hist, fill)]),
+                        torch.cat([h[1][:f] for h, f in zip(hist, fill)]),
+                        cu, torch.zeros(S, dtype=torch.int32, device=device),
+                        tables.to(device), slots.to(device), int(fill.max()))
+    torch.cuda.synchronize()
+    return AppendSetup(pool=pool, hist=hist, fill=fill)

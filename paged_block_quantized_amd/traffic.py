@@ -58,6 +58,10 @@ def run(args):
         setup = runner.setup_multi(w)
         for _ in range(args.calls):
             setup.run()
+    elif w.store_only:   # quantize-and-store of every prompt, the same call repeated
+        setup = runner.setup_prefill_store(w)
+        for _ in range(args.calls):
+            setup.run()
     else:
         setup = runner.setup_decode(w)
         if args.rotate > 1:
@@ -111,11 +115,18 @@ def _copy_kernel(per):
 def _step_kernels(per, calls):
     """{kernel: median counter per step} over the dispatches of the steps:
     those from the first partition-kernel dispatch on (the pool is built by
-    store dispatches alone; a step may hold several partition kernels)."""
+    store dispatches alone; a step may hold several partition kernels), or
+    for a store-only workload its last `calls` store dispatches."""
     parts = [d for n, v in per.items() if "attn_partition_" in n for d, _ in v]
-    if len(parts) < calls:
-        raise SystemExit("fewer partition-kernel dispatches than steps")
-    first = min(parts)
+    if parts:
+        if len(parts) < calls:
+            raise SystemExit("fewer partition-kernel dispatches than steps")
+        first = min(parts)
+    else:   # a store-only workload: its last `calls` store dispatches
+        stores = sorted(d for n, v in per.items() if "quantize_store" in n for d, _ in v)
+        if len(stores) < calls:
+            raise SystemExit("fewer store dispatches than calls")
+        first = stores[-calls]
     out = {}
     for n, v in per.items():
         if any(k in n for k in DECODE_KERNELS):

@@ -65,6 +65,7 @@ class Workload:
     partition: int = 0             # split-K partition tokens (0: library default)
     seed: int = 0
     q_len: int = 0                 # query tokens per sequence (multi-query workloads)
+    store_only: bool = False       # measured as quantize-and-store (no attention)
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
 
@@ -76,7 +77,7 @@ WORKLOADS = {
     "gqa70b": Workload("gqa70b", 128, 64, 8, 128, 32, "i4", "uniform", (500, 2000),
                        outlier_frac=0.01, outlier_mult=8.0, seed=3),
     "prefill_store": Workload("prefill_store", 64, 32, 32, 128, 16, "i8", "fixed", (2048,),
-                              pool_blocks=16384, seed=4),
+                              pool_blocks=16384, seed=4, store_only=True),
     "shared_prefix": Workload("shared_prefix", 32, 32, 32, 128, 32, "i4", "fixed", (32768,),
                               prefix=4096, partition=512, seed=5),
     "llama7b_fp8": Workload("llama7b_fp8", 32, 32, 32, 128, 16, "fp8", "fixed", (4096,),
