@@ -621,9 +621,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // the steps past its first query's position mask per query.
 // Byte-coded V with D = 128 stages 34 KiB of LDS per 2-wave group, which caps
 // the staged kernels at two waves per SIMD: their register budget is then
-// that of two waves (no spills into AGPRs).
-template <int D, int CP, bool FUSED, bool MULTI>
+// that of two waves (no spills into AGPRs).  Two-wave multi-query groups
+// with INT4 V use about 26 KiB (their merge takes one wave's slot), room for
+// three waves per SIMD, and get that register budget.
+template <int D, int CP, bool FUSED, bool MULTI, int NW>
 constexpr int gqa_waves_per_eu() {
+    if (MULTI && NW == 2 && codec_packed4(CP % 4)) return 3;
     return MULTI || (!FUSED && D == 128 && !codec_packed4(CP % 4)) ? 2 : PBQ_GQA_WAVES_PER_EU;
 }
 
@@ -632,7 +635,7 @@ constexpr int gqa_waves_per_eu() {
 // code converted to fp16 feeds the matrix products of both tiles, which
 // halves the conversion work per query; the softmax stays per tile.
 template <int BS, int D, int CP, int NW, bool FUSED, bool SHARED = false, bool MULTI = false, int TPW = 1>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(gqa_waves_per_eu<D, CP, FUSED, MULTI>())))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(gqa_waves_per_eu<D, CP, FUSED, MULTI, NW>())))
 void attn_partition_gqa(AttnArgs a) {
     constexpr int KC = CP / 4, VC = CP % 4;
     constexpr bool V4 = codec_packed4(VC);
@@ -973,7 +976,11 @@ void attn_partition_gqa(AttnArgs a) {
     static_assert(SD == 2 || SD == 3, "stages");
     static_assert(BPS * VT % 1024 == 0 && (VT % 1024 == 0 || (BPS == 2 && VT == 512)), "V tile loads");
     constexpr int STAGE_BYTES = STAGED ? NW * SD * STG : 16;
-    constexpr int ACC_BYTES = NW * QT * (D + 4) * 4;
+    // two-wave multi-query groups merge through one wave's slot (the other
+    // wave merges from its registers), which leaves LDS room for a third
+    // work group of waves per SIMD
+    constexpr bool HALF = MULTI && NW == 2;
+    constexpr int ACC_BYTES = (HALF ? 1 : NW) * QT * (D + 4) * 4;
     __shared__ __align__(16) uint8_t s_stage[STAGE_BYTES > ACC_BYTES ? STAGE_BYTES : ACC_BYTES];
     uint8_t* const my_stage = s_stage + w * SD * STG;   // w is wave-uniform
     // lane offsets: where this lane's 16 bytes of a K load come from (row
@@ -1166,6 +1173,73 @@ void attn_partition_gqa(AttnArgs a) {
     float (*s_acc)[QT][DP] = reinterpret_cast<float (*)[QT][DP]>(s_stage);
     __shared__ float s_ml[NW][QT][2];
     if constexpr (STAGED) __syncthreads();
+    if constexpr (HALF) {
+        // wave 1 leaves its partial result in the slot; wave 0 combines it
+        // with its own (the same arithmetic, in the same order, as the merge
+        // over all waves below) and leaves the normalised result there, with
+        // the combined (max, sum) in s_ml[0]
+        if (w == 1) {
+#pragma unroll
+            for (int T = 0; T < TPW; ++T) {
+                const int qq = 16 * T + n16;
+                if (qq < nheads) {
+#pragma unroll
+                    for (int t = 0; t < DT; ++t) *(f32x4*)&s_acc[0][qq][16 * t + 4 * grp] = acc[T][t];
+                    if (grp == 0) {
+                        s_ml[1][qq][0] = m[T];
+                        s_ml[1][qq][1] = l[T];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (w == 0) {
+#pragma unroll
+            for (int T = 0; T < TPW; ++T) {
+                const int qq = 16 * T + n16;
+                if (qq < nheads) {
+                    const float m1 = s_ml[1][qq][0], l1 = s_ml[1][qq][1];
+                    const float M = fmaxf(m[T], m1);
+                    const float f0 = m[T] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[T] - M);
+                    const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+                    const float L = __builtin_fmaf(l1, f1, l[T] * f0);
+#pragma unroll
+                    for (int t = 0; t < DT; ++t) {
+                        f32x4* slot = (f32x4*)&s_acc[0][qq][16 * t + 4 * grp];
+                        const f32x4 o1 = *slot;
+                        f32x4 res;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float o = __builtin_fmaf(o1[i], f1, acc[T][t][i] * f0);
+                            res[i] = L > 0.f ? o / L : 0.f;
+                        }
+                        *slot = res;
+                    }
+                    if (grp == 0) {
+                        s_ml[0][qq][0] = M;
+                        s_ml[0][qq][1] = L;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < nheads * D; idx += 64 * NW) {
+            const int hh = idx / D, d = idx % D;
+            const float res = s_acc[0][hh][d];
+            const int64_t row = query_row(hh);
+            if (direct) {
+                a.out[row * D + d] = f32_to_f16_bits(res);
+            } else {
+                const int64_t prow = row * a.max_partitions + p;
+                a.ws_out[prow * D + d] = res;
+                if (d == 0) {
+                    a.ws_ml[prow * 2] = s_ml[0][hh][0];
+                    a.ws_ml[prow * 2 + 1] = s_ml[0][hh][1];
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int T = 0; T < TPW; ++T) {
         const int qq = 16 * T + n16;   // the lane's query in the work group
