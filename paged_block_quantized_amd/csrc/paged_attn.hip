@@ -534,6 +534,14 @@ void attn_partition_mha(AttnArgs a) {
 #ifndef PBQ_MULTI_BYTEV_STAGE
 #define PBQ_MULTI_BYTEV_STAGE 0
 #endif
+// Two-wave multi-query groups of two tiles per wave with INT4 V share one
+// staging area: both waves stream every step, each for its own 32 queries
+// (prefill_chunk_gqa +3 %).  With byte-coded V the staged kernels need more
+// registers than three waves per SIMD allow (spilled: -11 %; at two waves:
+// -3 %), and the register path stays.
+#ifndef PBQ_MULTI_SHARE
+#define PBQ_MULTI_SHARE 1
+#endif
 #ifndef PBQ_GQA_STAGE_FUSED
 #define PBQ_GQA_STAGE_FUSED 0
 #endif
@@ -631,9 +639,12 @@ constexpr int gqa_waves_per_eu() {
 }
 
 //
-// TPW: 16-query tiles per work group (MULTI only).  With two, every K and V
-// code converted to fp16 feeds the matrix products of both tiles, which
-// halves the conversion work per query; the softmax stays per tile.
+// TPW: 16-query tiles per wave (MULTI only).  With two, every K and V code
+// converted to fp16 feeds the matrix products of both tiles, which halves
+// the conversion work per query; the softmax stays per tile.  Two-wave
+// groups then either split the partition's steps between the waves and
+// merge them (byte-coded V), or (SHARE, INT4 V) stream every step through
+// one shared staging area, each wave for its own two tiles.
 template <int BS, int D, int CP, int NW, bool FUSED, bool SHARED = false, bool MULTI = false, int TPW = 1>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(gqa_waves_per_eu<D, CP, FUSED, MULTI, NW>())))
 void attn_partition_gqa(AttnArgs a) {
@@ -644,8 +655,12 @@ void attn_partition_gqa(AttnArgs a) {
     static_assert(!(MULTI && (FUSED || SHARED)), "multi-query launches store nothing and share nothing");
     static_assert(BS == 16 || BS == 32, "block size");
     static_assert(TPW == 1 || (MULTI && TPW == 2), "two tiles per work group only for multi-query launches");
-    constexpr int QT = 16 * TPW;               // queries per work group
-    constexpr bool STAGED = FUSED ? PBQ_GQA_STAGE_FUSED : (MULTI && !V4 ? PBQ_MULTI_BYTEV_STAGE : PBQ_GQA_STAGE);
+    constexpr int QT = 16 * TPW;               // queries per wave
+    // SHARE: both waves stream every step of the partition from one staging
+    // area, wave w for queries w QT .. of the group (no merge of waves)
+    constexpr bool SHARE = MULTI && NW == 2 && TPW == 2 && codec_packed4(CP % 4) && PBQ_MULTI_SHARE;
+    constexpr int QW = SHARE ? NW * QT : QT;   // queries per work group
+    constexpr bool STAGED = FUSED ? PBQ_GQA_STAGE_FUSED : (SHARE ? true : (MULTI && !V4 ? PBQ_MULTI_BYTEV_STAGE : PBQ_GQA_STAGE));
     constexpr int KS = D / 32;                 // QK k-steps
     constexpr int DT = D / 16;                 // PV dim tiles
     constexpr int KCH = D / 4;                 // K bytes per lane per row
@@ -684,8 +699,8 @@ void attn_partition_gqa(AttnArgs a) {
     const int n_tok = MULTI ? a.cu_q[s + 1] - q_row0 : 1;   // its query tokens
     // queries that share a KV head's tiles
     const int NQ = SHARED ? a.num_seqs * G : n_tok * G;
-    const int n_ht = (NQ + QT - 1) / QT;
-    const int n_ht_grid = MULTI ? (a.max_q_len * G + QT - 1) / QT : n_ht;
+    const int n_ht = (NQ + QW - 1) / QW;
+    const int n_ht_grid = MULTI ? (a.max_q_len * G + QW - 1) / QW : n_ht;
     const int kvh = tile / n_ht_grid;
     const int ht = tile % n_ht_grid;
     if (MULTI && ht >= n_ht) return;
@@ -693,7 +708,7 @@ void attn_partition_gqa(AttnArgs a) {
     const int ctx_seq = SHARED ? a.shared_tokens : a.context_lens[s];
     // position of query token 0, and the tokens this tile's last query sees
     const int pos0 = ctx_seq - n_tok;
-    const int ctx = MULTI ? pos0 + (min(NQ, ht * QT + QT) - 1) / G + 1 : ctx_seq;
+    const int ctx = MULTI ? pos0 + (min(NQ, ht * QW + QW) - 1) / G + 1 : ctx_seq;
     const int nblk = (ctx + BS - 1) / BS;
     const int PB = a.partition_blocks;
     const int nparts = max(1, (nblk + PB - 1) / PB);
@@ -705,10 +720,11 @@ void attn_partition_gqa(AttnArgs a) {
     const int tok0 = p * PB * BS;
     const int tok1 = min(tok0 + PB * BS, ctx);
     const int nsteps = (tok1 - tok0 + 31) / 32;
-    const int nheads = min(QT, NQ - ht * QT);   // queries of the work group (tile T: 16 T ..)
+    const int q0 = ht * QW + (SHARE ? w * QT : 0);   // the wave's first query
+    const int nheads = max(0, min(QT, NQ - q0));      // the wave's queries (tile T: 16 T ..)
     // row of query ht * QT + i in q and out ([rows, Hq, D])
     auto query_row = [&](int i) -> int64_t {
-        const int qi = ht * QT + i;
+        const int qi = q0 + i;
         if constexpr (SHARED) return (int64_t)(qi / G) * a.num_q_heads + kvh * G + qi % G;
         else if constexpr (MULTI) return (int64_t)(q_row0 + qi / G) * a.num_q_heads + kvh * G + qi % G;
         else return (int64_t)s * a.num_q_heads + kvh * G + qi;
@@ -719,8 +735,8 @@ void attn_partition_gqa(AttnArgs a) {
     int qlim[TPW];
 #pragma unroll
     for (int T = 0; T < TPW; ++T)
-        qlim[T] = MULTI && 16 * T + n16 < nheads ? pos0 + (ht * QT + 16 * T + n16) / G : ctx - 1;
-    const int mask_from = MULTI ? pos0 + (ht * QT) / G + 1 : ctx;
+        qlim[T] = MULTI && 16 * T + n16 < nheads ? pos0 + (q0 + 16 * T + n16) / G : ctx - 1;
+    const int mask_from = MULTI ? pos0 + q0 / G + 1 : ctx;
     const int blk0 = tok0 / BS;
     const int blk_end = (tok1 + BS - 1) / BS;
 
@@ -959,13 +975,13 @@ void attn_partition_gqa(AttnArgs a) {
     const int n_loop = fused ? nsteps - 1 : nsteps;
     const int hc = fused ? min(PBQ_STORE_HANDICAP_TOKENS / 32, n_loop / NW) : 0;
     const int q = (n_loop + 2 * hc) / NW, rem = (n_loop + 2 * hc) % NW;
-    const int w_start = w * q + min(w, rem) - min(w, 2) * hc;
-    const int w_stop = w_start + q + (w < rem ? 1 : 0) - (w < 2 ? hc : 0);
+    const int w_start = SHARE ? 0 : w * q + min(w, rem) - min(w, 2) * hc;
+    const int w_stop = SHARE ? n_loop : w_start + q + (w < rem ? 1 : 0) - (w < 2 ? hc : 0);
 
     // Staging area of the direct-to-LDS path, per wave and stage: the step's
     // 32 K rows as 1 KiB loads (RPR rows each, chunks swizzled by kswz,
     // padded by 64 bytes), then its BPS V tiles as in the pool.
-    constexpr int SD = PBQ_GQA_STAGES;
+    constexpr int SD = SHARE ? 3 : PBQ_GQA_STAGES;
     constexpr int CPR = D / 16;                // 16-byte chunks per K row
     constexpr int RPR = 1024 / D;              // K rows per load
     constexpr int NKL = 32 * D / 1024;         // K loads per step
@@ -975,14 +991,14 @@ void attn_partition_gqa(AttnArgs a) {
     constexpr int STG = NKL * KREG + BPS * VT;
     static_assert(SD == 2 || SD == 3, "stages");
     static_assert(BPS * VT % 1024 == 0 && (VT % 1024 == 0 || (BPS == 2 && VT == 512)), "V tile loads");
-    constexpr int STAGE_BYTES = STAGED ? NW * SD * STG : 16;
+    constexpr int STAGE_BYTES = STAGED ? (SHARE ? 1 : NW) * SD * STG : 16;
     // two-wave multi-query groups merge through one wave's slot (the other
     // wave merges from its registers), which leaves LDS room for a third
     // work group of waves per SIMD
-    constexpr bool HALF = MULTI && NW == 2;
-    constexpr int ACC_BYTES = (HALF ? 1 : NW) * QT * (D + 4) * 4;
+    constexpr bool HALF = MULTI && NW == 2 && !SHARE;
+    constexpr int ACC_BYTES = SHARE ? 16 : (HALF ? 1 : NW) * QT * (D + 4) * 4;
     __shared__ __align__(16) uint8_t s_stage[STAGE_BYTES > ACC_BYTES ? STAGE_BYTES : ACC_BYTES];
-    uint8_t* const my_stage = s_stage + w * SD * STG;   // w is wave-uniform
+    uint8_t* const my_stage = s_stage + (SHARE ? 0 : w * SD * STG);   // w is wave-uniform
     // lane offsets: where this lane's 16 bytes of a K load come from (row
     // lane / CPR of the load), and where its operands sit in a stage
     // (unsigned: a uniform base plus a 32-bit lane offset is the
@@ -1008,7 +1024,8 @@ void attn_partition_gqa(AttnArgs a) {
 #pragma unroll
         for (int g = 0; g < NKL; ++g) {
             const int row0 = g * RPR;             // a load lies in one block
-            load_to_lds((row0 / BS ? kb1 : kb0) + (row0 % BS) * D + dma_k, sb + g * KREG);
+            if (!SHARE || g % NW == w)            // SHARE: the waves take turns
+                load_to_lds((row0 / BS ? kb1 : kb0) + (row0 % BS) * D + dma_k, sb + g * KREG);
         }
         const uint8_t* vb0 = a.v_codes + ((int64_t)id0 * H + kvh) * VT;
         const uint8_t* vb1 = a.v_codes + ((int64_t)id1 * H + kvh) * VT;
@@ -1017,7 +1034,7 @@ void attn_partition_gqa(AttnArgs a) {
             const uint8_t* src;
             if constexpr (VT >= 1024) src = ((1024 * g) / VT ? vb1 : vb0) + (1024 * g) % VT + dma_v;
             else src = (lane < 32 ? vb0 : vb1) + (dma_v & 511u);
-            load_to_lds(src, sb + NKL * KREG + 1024 * g);
+            if (!SHARE || (NKL + g) % NW == w) load_to_lds(src, sb + NKL * KREG + 1024 * g);
         }
     };
     // the lane's operands of the step in stage B (K rows: the second chunk
@@ -1089,7 +1106,41 @@ void attn_partition_gqa(AttnArgs a) {
             sv_l = a.v_scale[t];
             if constexpr (VZP) zp_l = a.v_zp[t];
         };
-        if constexpr (STAGED) {
+        if constexpr (SHARE) {
+            // One staging area for both waves, three stages: step i + 2 is
+            // loaded into the stage of step i - 1 once every wave has passed
+            // the barrier of step i (so has read step i - 1), and two steps
+            // are in flight while one is computed.  Each wave issues its
+            // share of a step's loads (NIW) and waits for its own; the
+            // barrier then makes the whole step visible.
+            constexpr int NIW0 = (NI + 1) / 2, NIW1 = NI / 2;
+            auto stage = [&](int i, int buf) {
+                stage_step(readlane(id_l, i * BPS), readlane(id_l, i * BPS + BPS - 1), buf);
+            };
+            __builtin_amdgcn_s_barrier();   // the previous batch's stages are read
+            scales();
+            stage(0, 0);
+            if (1 < cnt) stage(1, 1);
+            auto one = [&](auto bc, int i) {
+                constexpr int B = decltype(bc)::value;
+                if (i + 1 < cnt) {   // step i + 1 was issued after step i
+                    if (w == 0) wait_vmem<NIW0>();
+                    else wait_vmem<NIW1>();
+                } else {
+                    wait_vmem<0>();
+                }
+                __builtin_amdgcn_s_barrier();
+                Raw r;
+                read_stage(bc, r);
+                if (i + 2 < cnt) stage(i + 2, (B + 2) % 3);
+                compute(r, i);
+            };
+            for (int i = 0; i < cnt; i += 3) {
+                static_for<3>([&](auto bc) {
+                    if (i + decltype(bc)::value < cnt) one(bc, i + decltype(bc)::value);
+                });
+            }
+        } else if constexpr (STAGED) {
             // SD stages: step i + SD is loaded into step i's stage once its
             // operands are in registers, so SD steps are in flight while one
             // is computed.  Each wait leaves outstanding only the loads issued
@@ -1173,6 +1224,38 @@ void attn_partition_gqa(AttnArgs a) {
     float (*s_acc)[QT][DP] = reinterpret_cast<float (*)[QT][DP]>(s_stage);
     __shared__ float s_ml[NW][QT][2];
     if constexpr (STAGED) __syncthreads();
+    if constexpr (SHARE) {
+        // each wave holds every token of its queries: normalise and write
+        // from the registers (lane: dims 16t + 4 grp .. +3 of query 16T + n16)
+#pragma unroll
+        for (int T = 0; T < TPW; ++T) {
+            const int qq = 16 * T + n16;
+            if (qq < nheads) {
+                const int64_t row = query_row(qq);
+                const float L = l[T];
+#pragma unroll
+                for (int t = 0; t < DT; ++t) {
+                    float res[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) res[i] = L > 0.f ? acc[T][t][i] / L : 0.f;
+                    const int d = 16 * t + 4 * grp;
+                    if (direct) {
+                        const uint32_t lo = (uint32_t)f32_to_f16_bits(res[0]) | ((uint32_t)f32_to_f16_bits(res[1]) << 16);
+                        const uint32_t hi = (uint32_t)f32_to_f16_bits(res[2]) | ((uint32_t)f32_to_f16_bits(res[3]) << 16);
+                        *(u32x2*)&a.out[row * D + d] = u32x2{lo, hi};
+                    } else {
+                        const int64_t prow = row * a.max_partitions + p;
+                        *(f32x4*)&a.ws_out[prow * D + d] = f32x4{res[0], res[1], res[2], res[3]};
+                        if (t == 0 && grp == 0) {
+                            a.ws_ml[prow * 2] = m[T];
+                            a.ws_ml[prow * 2 + 1] = L;
+                        }
+                    }
+                }
+            }
+        }
+        return;
+    }
     if constexpr (HALF) {
         // wave 1 leaves its partial result in the slot; wave 0 combines it
         // with its own (the same arithmetic, in the same order, as the merge
@@ -1430,7 +1513,10 @@ hipError_t launch_shared(const AttnArgs& a, hipStream_t stream) {
 template <int BS, int D, int CP, int TPW>
 hipError_t launch_multi_tiles(const AttnArgs& a, hipStream_t stream) {
     const int G = a.num_q_heads / a.num_kv_heads;
-    const int n_ht = (a.max_q_len * G + 16 * TPW - 1) / (16 * TPW);
+    // queries per work group: two-wave groups of two-tile waves with INT4 V
+    // share their staging and take 64 (the kernel's SHARE mode), others 16 TPW
+    const int QW = (a.max_partitions == 1 && TPW == 2 && codec_packed4(CP % 4) && PBQ_MULTI_SHARE) ? 64 : 16 * TPW;
+    const int n_ht = (a.max_q_len * G + QW - 1) / QW;
     // x = partition, y = KV head x query tile, z = sequence (the kernel
     // renumbers the work groups over the XCDs)
     const dim3 grid((unsigned)a.max_partitions, (unsigned)(a.num_kv_heads * n_ht), (unsigned)a.num_seqs);
