@@ -663,7 +663,8 @@ MULTI_SHAPES = [
 def test_multi_query_ragged(bs, d, vc, g, hkv):
     """paged_attn_multi_query: each sequence's last n stored tokens attend
     causally (full prefills, chunks after a prefix, single tokens, chunks
-    across partitions and blocks), every partition size, against the oracle;
+    across partitions and blocks), every partition size and a single pass,
+    against the oracle;
     a one-token query equals the decode's output within tolerance."""
     announce("multi", bs, d, vc, g, hkv)
     seqs = [(1, 1), (17, 5), (100, 100), (700, 64), (33, 32), (2100, 17), (300, 1), (64, 40)]
@@ -686,7 +687,9 @@ def test_multi_query_ragged(bs, d, vc, g, hkv):
     qd = torch.from_numpy(q_rows).cuda()
     cud = torch.from_numpy(cu).cuda()
     dec = case.decode()
-    for part in (0, 32, 96, 256, 2048):
+    # 4096: one pass over every context (two-wave groups: the one-slot merge,
+    # or with INT4 V the shared staging)
+    for part in (0, 32, 96, 256, 2048, 4096):
         out = torch.full_like(qd, float("nan"))
         case.pool.multi_query(qd, out, cud, max(ns), case.tables, case.ctx_dev, max(ctx), sm, part)
         torch.cuda.synchronize()
