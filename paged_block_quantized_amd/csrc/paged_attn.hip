@@ -534,11 +534,10 @@ void attn_partition_mha(AttnArgs a) {
 #ifndef PBQ_MULTI_BYTEV_STAGE
 #define PBQ_MULTI_BYTEV_STAGE 0
 #endif
-// Two-wave multi-query groups of two tiles per wave with INT4 V share one
-// staging area: both waves stream every step, each for its own 32 queries
-// (prefill_chunk_gqa +3 %).  With byte-coded V the staged kernels need more
-// registers than three waves per SIMD allow (spilled: -11 %; at two waves:
-// -3 %), and the register path stays.
+// Two-wave multi-query groups of two tiles per wave share one staging area:
+// both waves stream every step, each for its own 32 queries, reading a
+// step's V operands only after its softmax so that three waves fit per SIMD
+// (prefill_chunk 652 -> 702 TFLOP/s, prefill_chunk_gqa 741-757 -> 768-775).
 #ifndef PBQ_MULTI_SHARE
 #define PBQ_MULTI_SHARE 1
 #endif
@@ -629,12 +628,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // the steps past its first query's position mask per query.
 // Byte-coded V with D = 128 stages 34 KiB of LDS per 2-wave group, which caps
 // the staged kernels at two waves per SIMD: their register budget is then
-// that of two waves (no spills into AGPRs).  Two-wave multi-query groups
-// with INT4 V use about 26 KiB (their merge takes one wave's slot), room for
-// three waves per SIMD, and get that register budget.
+// that of two waves (no spills into AGPRs).  Two-wave multi-query groups use
+// at most about 26 KiB (a shared three-stage area, or a merge through one
+// wave's slot), room for three waves per SIMD, and get that register budget.
 template <int D, int CP, bool FUSED, bool MULTI, int NW>
 constexpr int gqa_waves_per_eu() {
-    if (MULTI && NW == 2 && codec_packed4(CP % 4)) return 3;
+    if (MULTI && NW == 2) return 3;
     return MULTI || (!FUSED && D == 128 && !codec_packed4(CP % 4)) ? 2 : PBQ_GQA_WAVES_PER_EU;
 }
 
@@ -642,9 +641,9 @@ constexpr int gqa_waves_per_eu() {
 // TPW: 16-query tiles per wave (MULTI only).  With two, every K and V code
 // converted to fp16 feeds the matrix products of both tiles, which halves
 // the conversion work per query; the softmax stays per tile.  Two-wave
-// groups then either split the partition's steps between the waves and
-// merge them (byte-coded V), or (SHARE, INT4 V) stream every step through
-// one shared staging area, each wave for its own two tiles.
+// groups (single-pass launches) stream every step through one shared
+// staging area, each wave for its own two tiles (SHARE); the four-wave
+// groups of split partitions divide the steps and merge.
 template <int BS, int D, int CP, int NW, bool FUSED, bool SHARED = false, bool MULTI = false, int TPW = 1>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(gqa_waves_per_eu<D, CP, FUSED, MULTI, NW>())))
 void attn_partition_gqa(AttnArgs a) {
@@ -658,7 +657,7 @@ void attn_partition_gqa(AttnArgs a) {
     constexpr int QT = 16 * TPW;               // queries per wave
     // SHARE: both waves stream every step of the partition from one staging
     // area, wave w for queries w QT .. of the group (no merge of waves)
-    constexpr bool SHARE = MULTI && NW == 2 && TPW == 2 && codec_packed4(CP % 4) && PBQ_MULTI_SHARE;
+    constexpr bool SHARE = MULTI && NW == 2 && TPW == 2 && PBQ_MULTI_SHARE;
     constexpr int QW = SHARE ? NW * QT : QT;   // queries per work group
     constexpr bool STAGED = FUSED ? PBQ_GQA_STAGE_FUSED : (SHARE ? true : (MULTI && !V4 ? PBQ_MULTI_BYTEV_STAGE : PBQ_GQA_STAGE));
     constexpr int KS = D / 32;                 // QK k-steps
@@ -815,7 +814,9 @@ void attn_partition_gqa(AttnArgs a) {
 
     // One step: scores on MFMA, online softmax, PV on MFMA.  sk, sv, zpv are
     // this lane's block's scales (sk times sm_scale log2 e) and zero point.
-    auto compute_step = [&](const Raw& r, int st, float sk, float sv, float zpv) {
+    // before_pv(r) runs after the softmax, before the V operands are used
+    // (the shared-staging path reads them from LDS only then).
+    auto compute_step = [&](Raw& r, int st, float sk, float sv, float zpv, auto&& before_pv) {
         // ---- S^T = K_hat Q^T (each converted K operand serves every tile) --
         // The staged multi-query kernel raises its wave's priority while it
         // issues matrix products, so that the other wave's vector work fills
@@ -906,6 +907,7 @@ void attn_partition_gqa(AttnArgs a) {
             if constexpr (VC != KV_CODEC_FP8_E4M3) zacc[T] = __builtin_fmaf(code_bias<VC>(zpv), psum, zacc[T]);
         }
 
+        before_pv(r);
         // ---- O^T += (bias + V codes)^T P^T (each converted V operand serves every tile)
         if constexpr (MULTI && STAGED) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -1042,6 +1044,30 @@ void attn_partition_gqa(AttnArgs a) {
     const uint32_t la_k0 = lds_addr(my_stage) + (uint32_t)ko[0][0];
     const uint32_t la_k1 = lds_addr(my_stage) + (uint32_t)ko[1][0];
     const uint32_t la_v = lds_addr(my_stage) + (uint32_t)vo;
+    auto read_stage_k = [&](auto bc, Raw& r) {
+        constexpr int B = decltype(bc)::value;
+        static_for<KCH / 16>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            lds_read<B * STG + 64 * c>(r.k[0][c], la_k0);
+            lds_read<B * STG + 64 * c>(r.k[1][c], la_k1);
+        });
+        wait_lds();
+#pragma unroll
+        for (int c = 0; c < KCH / 16; ++c) {
+            lds_fence(r.k[0][c]);
+            lds_fence(r.k[1][c]);
+        }
+    };
+    auto read_stage_v = [&](auto bc, Raw& r) {
+        constexpr int B = decltype(bc)::value;
+        static_for<DT>([&](auto tc) {
+            constexpr int t = decltype(tc)::value;
+            lds_read<B * STG + 16 * t * VROW>(r.v[t], la_v);
+        });
+        wait_lds();
+#pragma unroll
+        for (int t = 0; t < DT; ++t) lds_fence(r.v[t]);
+    };
     auto read_stage = [&](auto bc, Raw& r) {
         constexpr int B = decltype(bc)::value;
         static_for<KCH / 16>([&](auto cc) {
@@ -1081,7 +1107,7 @@ void attn_partition_gqa(AttnArgs a) {
                       a.v_codes + ((int64_t)id0 * H + kvh) * VT, a.v_codes + ((int64_t)id1 * H + kvh) * VT, r);
         };
 
-        auto compute = [&](const Raw& r, int i) {
+        auto compute_with = [&](Raw& r, int i, auto&& before_pv) {
             const int st = base + i;
             // per-lane scales of the block holding this lane group's tokens.
             // The second block of a 16-token pair may lie past the end (its
@@ -1089,16 +1115,18 @@ void attn_partition_gqa(AttnArgs a) {
             // replaced by 0 so that stale pool contents cannot reach the sums.
             if constexpr (BPS == 1) {
                 compute_step(r, st, bits_to_f16f((uint16_t)readlane(sk_l, i)) * c2,
-                             bits_to_f16f((uint16_t)readlane(sv_l, i)) * vunit, (float)readlane(zp_l, i));
+                             bits_to_f16f((uint16_t)readlane(sv_l, i)) * vunit, (float)readlane(zp_l, i), before_pv);
             } else {
                 const bool live1 = blk0 + st * BPS + 1 < blk_end;
                 const int k0 = readlane(sk_l, 2 * i), k1 = live1 ? readlane(sk_l, 2 * i + 1) : 0;
                 const int v0 = readlane(sv_l, 2 * i), v1 = live1 ? readlane(sv_l, 2 * i + 1) : 0;
                 const int z0 = readlane(zp_l, 2 * i), z1 = live1 ? readlane(zp_l, 2 * i + 1) : 0;
                 compute_step(r, st, bits_to_f16f((uint16_t)(my_blk ? k1 : k0)) * c2,
-                             bits_to_f16f((uint16_t)(my_blk ? v1 : v0)) * vunit, (float)(my_blk ? z1 : z0));
+                             bits_to_f16f((uint16_t)(my_blk ? v1 : v0)) * vunit, (float)(my_blk ? z1 : z0),
+                             before_pv);
             }
         };
+        auto compute = [&](Raw& r, int i) { compute_with(r, i, [](Raw&) {}); };
 
         auto scales = [&]() {
             const int64_t t = (int64_t)id_l * H + kvh;
@@ -1131,9 +1159,10 @@ void attn_partition_gqa(AttnArgs a) {
                 }
                 __builtin_amdgcn_s_barrier();
                 Raw r;
-                read_stage(bc, r);
+                read_stage_k(bc, r);
                 if (i + 2 < cnt) stage(i + 2, (B + 2) % 3);
-                compute(r, i);
+                // V operands only after the softmax: fewer registers live
+                compute_with(r, i, [&](Raw& rr) { read_stage_v(bc, rr); });
             };
             for (int i = 0; i < cnt; i += 3) {
                 static_for<3>([&](auto bc) {
@@ -1202,7 +1231,7 @@ void attn_partition_gqa(AttnArgs a) {
             const bool mine_last = BPS == 1 || my_blk ? true : !pair;
             compute_step(r, st, bits_to_f16f((uint16_t)(mine_last ? s_tscale[0] : ks0)) * c2,
                          bits_to_f16f((uint16_t)(mine_last ? s_tscale[1] : vs0)) * vunit,
-                         (float)(mine_last ? s_tscale[2] : z0));
+                         (float)(mine_last ? s_tscale[2] : z0), [](Raw&) {});
         }
     }
     // lanes of one head split its tokens by group: sum their partial sums,
@@ -1513,9 +1542,9 @@ hipError_t launch_shared(const AttnArgs& a, hipStream_t stream) {
 template <int BS, int D, int CP, int TPW>
 hipError_t launch_multi_tiles(const AttnArgs& a, hipStream_t stream) {
     const int G = a.num_q_heads / a.num_kv_heads;
-    // queries per work group: two-wave groups of two-tile waves with INT4 V
-    // share their staging and take 64 (the kernel's SHARE mode), others 16 TPW
-    const int QW = (a.max_partitions == 1 && TPW == 2 && codec_packed4(CP % 4) && PBQ_MULTI_SHARE) ? 64 : 16 * TPW;
+    // queries per work group: two-wave groups of two-tile waves share their
+    // staging and take 64 (the kernel's SHARE mode), others 16 TPW
+    const int QW = (a.max_partitions == 1 && TPW == 2 && PBQ_MULTI_SHARE) ? 64 : 16 * TPW;
     const int n_ht = (a.max_q_len * G + QW - 1) / QW;
     // x = partition, y = KV head x query tile, z = sequence (the kernel
     // renumbers the work groups over the XCDs)
