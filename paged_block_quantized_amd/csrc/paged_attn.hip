@@ -814,6 +814,16 @@ void attn_partition_gqa(AttnArgs a) {
 
     // One step: scores on MFMA, online softmax, PV on MFMA.  sk, sv, zpv are
     // this lane's block's scales (sk times sm_scale log2 e) and zero point.
+    // MULTI's lazy rescale threshold (base 2), per V codec: the fp16 weights
+    // p sv must stay finite for every fp16 input, with p up to 2^kLazy and sv
+    // the largest V scale the codec can produce (INT8: 65504 / 127 -> 516,
+    // INT8 asymmetric: 131008 / 255 -> 514, INT4: 131008 / 15 -> 8736, FP8:
+    // 65504 / 448 -> 146.25 times its unit 256): 2^6 516, 2^2 8736 and
+    // 2^0 37440 are below 65504.
+    constexpr float kLazy = !MULTI ? 0.f
+                          : VC == KV_CODEC_FP8_E4M3 ? 0.f
+                          : V4 ? 2.f
+                          : 6.f;
     // before_pv(r) runs after the softmax, before the V operands are used
     // (the shared-staging path reads them from LDS only then).
     auto compute_step = [&](Raw& r, int st, float sk, float sv, float zpv, auto&& before_pv) {
@@ -874,11 +884,11 @@ void attn_partition_gqa(AttnArgs a) {
             bmax = fmaxf(bmax, shfl_xor_f(bmax, 16));
             bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
             // per head; lanes of one head agree.  MULTI rescales only when the
-            // maximum grows by more than 8 (base 2): the weights exp2(x - m) then
-            // stay below 256 and most steps skip the rescale of the accumulators
-            // (the final division by l uses the same m, so the result is the same
-            // softmax)
-            if (bmax > m[T] + (MULTI ? 8.f : 0.f)) {
+            // maximum grows by more than kLazy (base 2): the weights
+            // exp2(x - m) then stay at most 2^kLazy and most steps skip the
+            // rescale of the accumulators (the final division by l uses the
+            // same m, so the result is the same softmax)
+            if (bmax > m[T] + kLazy) {
                 const float alpha = __builtin_amdgcn_exp2f(m[T] - bmax);
 #pragma unroll
                 for (int t = 0; t < DT; ++t) acc[T][t] *= alpha;

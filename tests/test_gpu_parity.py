@@ -728,6 +728,54 @@ def test_multi_query_single_tile(bs, d, vc, g, hkv, ns):
         assert_close(out.cpu().numpy(), ref, f"multi one tile bs{bs} d{d} {vc} g{g} part{part}")
 
 
+@pytest.mark.parametrize("vc,vmul", [("i8", 12000.0), ("i4", 1000.0), ("fp8", 200.0), ("i8a", 12000.0)])
+def test_multi_query_large_v_scales(vc, vmul):
+    """V blocks whose scales are 2^8 or more, with scores that jump by just
+    under 8 (base 2) after the first 32 tokens: the multi-query softmax,
+    which rescales only when its maximum grows by more than 8, would weight
+    those tokens by about 2^8 times their V scale, past the fp16 range.
+    Outputs stay finite and match the oracle (compared relative to the V
+    magnitude: attention is linear in V)."""
+    announce("multi-large-v", vc, vmul)
+    bs, d, hkv, g = 16, 128, 2, 1
+    ctx = [700, 333, 64]
+    ns = [64, 40, 17]
+    rng = np.random.default_rng(23)
+    hk, hv = [], []
+    for c in ctx:
+        k = rng.standard_normal((c, hkv, d)) * 0.1
+        # score 0 for the first 32 tokens, then 7.95 (base 2) for the rest
+        k[:, :, 0] = np.where(np.arange(c) >= 32, 7.95 / np.log2(np.e) * np.sqrt(d), 0.0)[:, None]
+        v = np.clip(rng.standard_normal((c, hkv, d)) * vmul, -65000, 65000)
+        hk.append(k.astype(np.float16))
+        hv.append(v.astype(np.float16))
+    q_dec = np.zeros((len(ctx), hkv * g, d), np.float16)
+    q_dec[:, :, 0] = 1
+    n_blocks = sum((c + bs - 1) // bs for c in ctx) + 2
+    case = SmallCase(hk, hv, q_dec, hkv * g, hkv, d, bs, vc, n_blocks, rng.permutation(n_blocks))
+    case.store_all()
+    assert_pool_equal(case.pool, case.opool)
+    assert float(np.max(case.opool.v_scale.astype(np.float64))) * (256 if vc == "fp8" else 1) >= 255
+    q_rows = np.zeros((sum(ns), hkv * g, d), np.float16)
+    q_rows[:, :, 0] = 1
+    cu = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    sm = 1 / np.sqrt(d)
+    ref = attention.paged_multi_query(case.opool, [case.model.table(s)[0] for s in range(len(ctx))], ctx,
+                                      q_rows, cu, sm)
+    qd = torch.from_numpy(q_rows).cuda()
+    cud = torch.from_numpy(cu).cuda()
+    for part in (0, 256, 4096):
+        out = torch.full_like(qd, float("nan"))
+        case.pool.multi_query(qd, out, cud, max(ns), case.tables, case.ctx_dev, max(ctx), sm, part)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.all(np.isfinite(got)), f"non-finite outputs, {vc} part{part}"
+        assert_close(got / vmul, ref / vmul, f"multi large V {vc} part{part}")
+    dec = case.decode()
+    assert np.all(np.isfinite(dec))
+    assert_close(dec / vmul, case.reference() / vmul, f"decode large V {vc}")
+
+
 def test_multi_query_validates():
     from paged_block_quantized_amd import _lib as L
     from paged_block_quantized_amd import KVPool
