@@ -721,7 +721,8 @@ def test_multi_query_single_tile(bs, d, vc, g, hkv, ns):
                                       q_rows, cu, sm)
     qd = torch.from_numpy(q_rows).cuda()
     cud = torch.from_numpy(cu).cuda()
-    for part in (0, 32, 256):
+    # 4096: a single pass (two-wave groups merging through one wave's slot)
+    for part in (0, 32, 256, 4096):
         out = torch.full_like(qd, float("nan"))
         case.pool.multi_query(qd, out, cud, max(ns), case.tables, case.ctx_dev, max(ctx), sm, part)
         torch.cuda.synchronize()
