@@ -1405,12 +1405,12 @@ void attn_partition_gqa(AttnArgs a) {
 
 // Merges partitions 0 .. nparts-1 of workspace row `row` into out (one
 // wavefront).  Lane p holds partition p's (max, sum) and weight; the partial
-// outputs are read eight partitions at a time so that their loads are in
+// outputs are read 32 partitions at a time so that their loads are in
 // flight together.
 template <int D>
 __device__ __forceinline__ void merge_partitions(const AttnArgs& a, int64_t row, int nparts) {
     constexpr int PER = D / 64;
-    constexpr int BATCH = 8;
+    constexpr int BATCH = 32;   // 8: 12.1 us, 32: 10.1 us for shared_prefix's 64 partitions
     const int lane = threadIdx.x;
     const int64_t prow0 = row * a.max_partitions;
     const float* ml = a.ws_ml + prow0 * 2;
