@@ -538,8 +538,8 @@ void attn_partition_mha(AttnArgs a) {
 // both waves stream every step, each for its own 32 queries, reading a
 // step's V operands only after its softmax so that three waves fit per SIMD
 // (prefill_chunk 652 -> 702 TFLOP/s, prefill_chunk_gqa 741-757 -> 768-775).
-#ifndef PBQ_MULTI_SHARE
-#define PBQ_MULTI_SHARE 1
+#ifndef PBQ_MULTI_JOINT_STAGE
+#define PBQ_MULTI_JOINT_STAGE 1
 #endif
 #ifndef PBQ_GQA_STAGE_FUSED
 #define PBQ_GQA_STAGE_FUSED 0
@@ -642,7 +642,7 @@ constexpr int gqa_waves_per_eu() {
 // converted to fp16 feeds the matrix products of both tiles, which halves
 // the conversion work per query; the softmax stays per tile.  Two-wave
 // groups (single-pass launches) stream every step through one shared
-// staging area, each wave for its own two tiles (SHARE); the four-wave
+// staging area, each wave for its own two tiles (JOINT); the four-wave
 // groups of split partitions divide the steps and merge.
 template <int BS, int D, int CP, int NW, bool FUSED, bool SHARED = false, bool MULTI = false, int TPW = 1>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(gqa_waves_per_eu<D, CP, FUSED, MULTI, NW>())))
@@ -653,13 +653,13 @@ void attn_partition_gqa(AttnArgs a) {
     static_assert(!(FUSED && SHARED), "the shared prefix holds no current token");
     static_assert(!(MULTI && (FUSED || SHARED)), "multi-query launches store nothing and share nothing");
     static_assert(BS == 16 || BS == 32, "block size");
-    static_assert(TPW == 1 || (MULTI && TPW == 2), "two tiles per work group only for multi-query launches");
+    static_assert(TPW == 1 || (MULTI && TPW == 2), "two tiles per wave only for multi-query launches");
     constexpr int QT = 16 * TPW;               // queries per wave
-    // SHARE: both waves stream every step of the partition from one staging
+    // JOINT: both waves stream every step of the partition from one staging
     // area, wave w for queries w QT .. of the group (no merge of waves)
-    constexpr bool SHARE = MULTI && NW == 2 && TPW == 2 && PBQ_MULTI_SHARE;
-    constexpr int QW = SHARE ? NW * QT : QT;   // queries per work group
-    constexpr bool STAGED = FUSED ? PBQ_GQA_STAGE_FUSED : (SHARE ? true : (MULTI && !V4 ? PBQ_MULTI_BYTEV_STAGE : PBQ_GQA_STAGE));
+    constexpr bool JOINT = MULTI && NW == 2 && TPW == 2 && PBQ_MULTI_JOINT_STAGE;
+    constexpr int QW = JOINT ? NW * QT : QT;   // queries per work group
+    constexpr bool STAGED = FUSED ? PBQ_GQA_STAGE_FUSED : (JOINT ? true : (MULTI && !V4 ? PBQ_MULTI_BYTEV_STAGE : PBQ_GQA_STAGE));
     constexpr int KS = D / 32;                 // QK k-steps
     constexpr int DT = D / 16;                 // PV dim tiles
     constexpr int KCH = D / 4;                 // K bytes per lane per row
@@ -719,7 +719,7 @@ void attn_partition_gqa(AttnArgs a) {
     const int tok0 = p * PB * BS;
     const int tok1 = min(tok0 + PB * BS, ctx);
     const int nsteps = (tok1 - tok0 + 31) / 32;
-    const int q0 = ht * QW + (SHARE ? w * QT : 0);   // the wave's first query
+    const int q0 = ht * QW + (JOINT ? w * QT : 0);   // the wave's first query
     const int nheads = max(0, min(QT, NQ - q0));      // the wave's queries (tile T: 16 T ..)
     // row of query ht * QT + i in q and out ([rows, Hq, D])
     auto query_row = [&](int i) -> int64_t {
@@ -987,13 +987,13 @@ void attn_partition_gqa(AttnArgs a) {
     const int n_loop = fused ? nsteps - 1 : nsteps;
     const int hc = fused ? min(PBQ_STORE_HANDICAP_TOKENS / 32, n_loop / NW) : 0;
     const int q = (n_loop + 2 * hc) / NW, rem = (n_loop + 2 * hc) % NW;
-    const int w_start = SHARE ? 0 : w * q + min(w, rem) - min(w, 2) * hc;
-    const int w_stop = SHARE ? n_loop : w_start + q + (w < rem ? 1 : 0) - (w < 2 ? hc : 0);
+    const int w_start = JOINT ? 0 : w * q + min(w, rem) - min(w, 2) * hc;
+    const int w_stop = JOINT ? n_loop : w_start + q + (w < rem ? 1 : 0) - (w < 2 ? hc : 0);
 
     // Staging area of the direct-to-LDS path, per wave and stage: the step's
     // 32 K rows as 1 KiB loads (RPR rows each, chunks swizzled by kswz,
     // padded by 64 bytes), then its BPS V tiles as in the pool.
-    constexpr int SD = SHARE ? 3 : PBQ_GQA_STAGES;
+    constexpr int SD = JOINT ? 3 : PBQ_GQA_STAGES;
     constexpr int CPR = D / 16;                // 16-byte chunks per K row
     constexpr int RPR = 1024 / D;              // K rows per load
     constexpr int NKL = 32 * D / 1024;         // K loads per step
@@ -1003,14 +1003,14 @@ void attn_partition_gqa(AttnArgs a) {
     constexpr int STG = NKL * KREG + BPS * VT;
     static_assert(SD == 2 || SD == 3, "stages");
     static_assert(BPS * VT % 1024 == 0 && (VT % 1024 == 0 || (BPS == 2 && VT == 512)), "V tile loads");
-    constexpr int STAGE_BYTES = STAGED ? (SHARE ? 1 : NW) * SD * STG : 16;
+    constexpr int STAGE_BYTES = STAGED ? (JOINT ? 1 : NW) * SD * STG : 16;
     // two-wave multi-query groups merge through one wave's slot (the other
     // wave merges from its registers), which leaves LDS room for a third
     // work group of waves per SIMD
-    constexpr bool HALF = MULTI && NW == 2 && !SHARE;
-    constexpr int ACC_BYTES = SHARE ? 16 : (HALF ? 1 : NW) * QT * (D + 4) * 4;
+    constexpr bool HALF = MULTI && NW == 2 && !JOINT;
+    constexpr int ACC_BYTES = JOINT ? 16 : (HALF ? 1 : NW) * QT * (D + 4) * 4;
     __shared__ __align__(16) uint8_t s_stage[STAGE_BYTES > ACC_BYTES ? STAGE_BYTES : ACC_BYTES];
-    uint8_t* const my_stage = s_stage + (SHARE ? 0 : w * SD * STG);   // w is wave-uniform
+    uint8_t* const my_stage = s_stage + (JOINT ? 0 : w * SD * STG);   // w is wave-uniform
     // lane offsets: where this lane's 16 bytes of a K load come from (row
     // lane / CPR of the load), and where its operands sit in a stage
     // (unsigned: a uniform base plus a 32-bit lane offset is the
@@ -1036,7 +1036,7 @@ void attn_partition_gqa(AttnArgs a) {
 #pragma unroll
         for (int g = 0; g < NKL; ++g) {
             const int row0 = g * RPR;             // a load lies in one block
-            if (!SHARE || g % NW == w)            // SHARE: the waves take turns
+            if (!JOINT || g % NW == w)            // JOINT: the waves take turns
                 load_to_lds((row0 / BS ? kb1 : kb0) + (row0 % BS) * D + dma_k, sb + g * KREG);
         }
         const uint8_t* vb0 = a.v_codes + ((int64_t)id0 * H + kvh) * VT;
@@ -1046,7 +1046,7 @@ void attn_partition_gqa(AttnArgs a) {
             const uint8_t* src;
             if constexpr (VT >= 1024) src = ((1024 * g) / VT ? vb1 : vb0) + (1024 * g) % VT + dma_v;
             else src = (lane < 32 ? vb0 : vb1) + (dma_v & 511u);
-            if (!SHARE || (NKL + g) % NW == w) load_to_lds(src, sb + NKL * KREG + 1024 * g);
+            if (!JOINT || (NKL + g) % NW == w) load_to_lds(src, sb + NKL * KREG + 1024 * g);
         }
     };
     // the lane's operands of the step in stage B (K rows: the second chunk
@@ -1144,7 +1144,7 @@ void attn_partition_gqa(AttnArgs a) {
             sv_l = a.v_scale[t];
             if constexpr (VZP) zp_l = a.v_zp[t];
         };
-        if constexpr (SHARE) {
+        if constexpr (JOINT) {
             // One staging area for both waves, three stages: step i + 2 is
             // loaded into the stage of step i - 1 once every wave has passed
             // the barrier of step i (so has read step i - 1), and two steps
@@ -1263,7 +1263,7 @@ void attn_partition_gqa(AttnArgs a) {
     float (*s_acc)[QT][DP] = reinterpret_cast<float (*)[QT][DP]>(s_stage);
     __shared__ float s_ml[NW][QT][2];
     if constexpr (STAGED) __syncthreads();
-    if constexpr (SHARE) {
+    if constexpr (JOINT) {
         // each wave holds every token of its queries: normalise and write
         // from the registers (lane: dims 16t + 4 grp .. +3 of query 16T + n16)
 #pragma unroll
@@ -1553,8 +1553,8 @@ template <int BS, int D, int CP, int TPW>
 hipError_t launch_multi_tiles(const AttnArgs& a, hipStream_t stream) {
     const int G = a.num_q_heads / a.num_kv_heads;
     // queries per work group: two-wave groups of two-tile waves share their
-    // staging and take 64 (the kernel's SHARE mode), others 16 TPW
-    const int QW = (a.max_partitions == 1 && TPW == 2 && PBQ_MULTI_SHARE) ? 64 : 16 * TPW;
+    // staging and take 64 (the kernel's JOINT mode), others 16 TPW
+    const int QW = (a.max_partitions == 1 && TPW == 2 && PBQ_MULTI_JOINT_STAGE) ? 64 : 16 * TPW;
     const int n_ht = (a.max_q_len * G + QW - 1) / QW;
     // x = partition, y = KV head x query tile, z = sequence (the kernel
     // renumbers the work groups over the XCDs)
