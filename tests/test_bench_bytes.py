@@ -1,0 +1,65 @@
+"""The algorithmic byte and flop counts the benchmark divides by, against
+their closed forms at the workloads' sizes (no GPU)."""
+
+import numpy as np
+
+from paged_block_quantized_amd import runner, workloads as W
+
+
+def test_llama7b_decode_bytes():
+    # 32 sequences x 4096 tokens, 32 KV heads x 128 dims, INT8 K and V:
+    # codes 2 x 32 x 4096 x 32 x 128 B, two fp16 scales per (block of 16, head),
+    # fp16 Q and O rows, one int32 table entry per block, one length per sequence
+    w = W.WORKLOADS["llama7b"]
+    ctx = W.context_lengths(w)
+    codes = 2 * 32 * 4096 * 32 * 128
+    scales = 32 * (4096 // 16) * 32 * 4
+    qo = 2 * 32 * 32 * 128 * 2
+    tables = 32 * (4096 // 16) * 4 + 32 * 4
+    assert codes + scales + qo + tables == 1_075_347_584
+    assert runner.decode_bytes(w, ctx) == 1_075_347_584
+
+
+def test_shared_prefix_decode_bytes_count_the_prefix_once():
+    # 32 x 32768 tokens, INT8 K + INT4 V (1.5 B per element), fp16 scale pair
+    # and u8 zero point per (block of 32, head); the 4096-token prefix's codes
+    # and metadata once, the tables and lengths per sequence
+    w = W.WORKLOADS["shared_prefix"]
+    ctx = W.context_lengths(w)
+    tokens = 4096 + 32 * (32768 - 4096)
+    blocks = 4096 // 32 + 32 * (32768 - 4096) // 32
+    expect = (tokens * 32 * 128 * 3 // 2 + blocks * 32 * 5 + 2 * 32 * 32 * 128 * 2
+              + 32 * (32768 // 32) * 4 + 32 * 4)
+    assert runner.decode_bytes(w, ctx) == expect == 5_667_573_888
+    per_sequence = dict(vars(w))
+    per_sequence.pop("extra", None)
+    per_sequence["prefix"] = 0
+    assert runner.decode_bytes(W.Workload(**per_sequence), ctx) == 6_448_349_312
+
+
+def test_prefill_store_bytes():
+    # 64 prompts x 2048 tokens, 32 KV heads x 128 dims: fp16 K and V read,
+    # INT8 codes written, two fp16 scales per (block of 16, head), the tables
+    w = W.WORKLOADS["prefill_store"]
+    expect = 64 * 2048 * 32 * 128 * 2 * 2 + 64 * 2048 * 32 * 128 * 2 + 64 * 128 * 32 * 4 + 64 * 128 * 4
+    assert runner.prefill_store_bytes(w) == expect == 3_222_306_816
+
+
+def test_prefill_chunk_flops():
+    # the last 512 of 4096 tokens query causally: query i (0-based) sees
+    # 3584 + i + 1 tokens; 4 x head_dim x heads flops per (query, token)
+    w = W.WORKLOADS["prefill_chunk"]
+    ctx = W.context_lengths(w)
+    seen = sum(3584 + i + 1 for i in range(512))
+    assert runner.multi_flops(w, ctx) == 32 * seen * 4 * 128 * 32 == 1_030_926_368_768
+
+
+def test_store_step_bytes_one_token():
+    # one token per sequence at position ctx - 1: the block's held rows read
+    # (fp16 K and V), the whole tile's codes and metadata written, the tail
+    # rows of a partial block written back, four int32 arrays per sequence
+    w = W.WORKLOADS["llama7b"]
+    ctx = np.array([4096] * 32)
+    rows = 16   # position 4095 fills its block
+    expect = 32 * rows * 32 * 128 * 4 + 32 * 32 * (16 * 128 * 2 + 4) + 32 * 16
+    assert runner.store_step_bytes(w, ctx) == expect
