@@ -256,7 +256,6 @@ def bench_multi(w, args):
 def cpu_baseline_store(setup, seconds):
     """The oracle's quantize-and-store of whole prompts (the same rows the
     GPU stores), single-threaded, for up to ``seconds``."""
-    import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import paged
