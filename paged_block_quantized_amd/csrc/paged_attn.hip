@@ -828,11 +828,6 @@ void attn_partition_gqa(AttnArgs a) {
     // (the shared-staging path reads them from LDS only then).
     auto compute_step = [&](Raw& r, int st, float sk, float sv, float zpv, auto&& before_pv) {
         // ---- S^T = K_hat Q^T (each converted K operand serves every tile) --
-        // The staged multi-query kernel raises its wave's priority while it
-        // issues matrix products, so that the other wave's vector work fills
-        // the gaps between them (prefill_chunk_gqa +2 %; the register-path
-        // kernel loses 1 % with it and does not).
-        if constexpr (MULTI && STAGED) __builtin_amdgcn_s_setprio(1);
         f32x4 sc[TPW][2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
@@ -849,7 +844,6 @@ void attn_partition_gqa(AttnArgs a) {
                     sc[T][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, qop[T][j], sc[T][mt], 0, 0, 0);
             }
         }
-        if constexpr (MULTI && STAGED) __builtin_amdgcn_s_setprio(0);
         f16x8v pop[TPW];
 #pragma unroll
         for (int T = 0; T < TPW; ++T) {
@@ -919,7 +913,6 @@ void attn_partition_gqa(AttnArgs a) {
 
         before_pv(r);
         // ---- O^T += (bias + V codes)^T P^T (each converted V operand serves every tile)
-        if constexpr (MULTI && STAGED) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
             uint32_t a4[4];
@@ -941,7 +934,6 @@ void attn_partition_gqa(AttnArgs a) {
             for (int T = 0; T < TPW; ++T)
                 acc[T][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[T], acc[T][t], 0, 0, 0);
         }
-        if constexpr (MULTI && STAGED) __builtin_amdgcn_s_setprio(0);
     };
 
     // Fused store of the current token (position ctx - 1), single-partition
