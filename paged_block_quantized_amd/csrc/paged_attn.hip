@@ -528,9 +528,10 @@ void attn_partition_mha(AttnArgs a) {
 #ifndef PBQ_GQA_STAGE
 #define PBQ_GQA_STAGE 1
 #endif
-// Multi-query launches with byte-coded V keep the register path too: their
-// tiles re-read codes that the L2 mostly holds, and without the staging
-// copies `prefill_chunk` runs 4 % faster (with INT4 V the two are even).
+// Multi-query groups with byte-coded V that do not stage jointly (one tile
+// per wave, or the four-wave groups of split partitions) keep the register
+// path too: their waves re-read codes the L2 mostly holds (measured before
+// joint staging existed: 4 % faster than per-wave staging on prefill_chunk).
 #ifndef PBQ_MULTI_BYTEV_STAGE
 #define PBQ_MULTI_BYTEV_STAGE 0
 #endif
@@ -624,8 +625,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // MULTI: several query tokens per sequence, the last n of its stored tokens
 // (rows cu_q[s] .. cu_q[s+1] - 1 of q), each attending causally up to its
 // own position.  Query i of a sequence's tiles is token i / G with head
-// kvh * G + i % G; a tile reads only the tokens its last query can see, and
-// the steps past its first query's position mask per query.
+// kvh * G + i % G; a work group reads only the tokens its last query can
+// see, and the steps past a wave's first query's position mask per query.
 // Byte-coded V with D = 128 stages 34 KiB of LDS per 2-wave group, which caps
 // the staged kernels at two waves per SIMD: their register budget is then
 // that of two waves (no spills into AGPRs).  Two-wave multi-query groups use
@@ -982,9 +983,10 @@ void attn_partition_gqa(AttnArgs a) {
     const int w_start = JOINT ? 0 : w * q + min(w, rem) - min(w, 2) * hc;
     const int w_stop = JOINT ? n_loop : w_start + q + (w < rem ? 1 : 0) - (w < 2 ? hc : 0);
 
-    // Staging area of the direct-to-LDS path, per wave and stage: the step's
-    // 32 K rows as 1 KiB loads (RPR rows each, chunks swizzled by kswz,
-    // padded by 64 bytes), then its BPS V tiles as in the pool.
+    // Staging area of the direct-to-LDS path, per wave (one for the group in
+    // the joint mode) and stage: the step's 32 K rows as 1 KiB loads (RPR
+    // rows each, chunks swizzled by kswz, padded by 64 bytes), then its BPS V
+    // tiles as in the pool.
     constexpr int SD = JOINT ? 3 : PBQ_GQA_STAGES;
     constexpr int CPR = D / 16;                // 16-byte chunks per K row
     constexpr int RPR = 1024 / D;              // K rows per load
