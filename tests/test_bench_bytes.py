@@ -63,3 +63,17 @@ def test_store_step_bytes_one_token():
     rows = 16   # position 4095 fills its block
     expect = 32 * rows * 32 * 128 * 4 + 32 * 32 * (16 * 128 * 2 + 4) + 32 * 16
     assert runner.store_step_bytes(w, ctx) == expect
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the benchmark measures one GPU; asking for more ends with a message and
+    # status 2 before any device is touched
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
