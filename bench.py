@@ -79,7 +79,7 @@ def cpu_baseline(setup, seconds):
         dt = time.perf_counter() - t0
     ctx_done = np.array([int(setup.ctx[s]) for s in done])
     sub = dataclasses.replace(w, num_seqs=len(done), prefix=0)
-    nbytes = runner.decode_bytes(sub, ctx_done) + runner.store_step_bytes(sub, ctx_done)
+    nbytes = runner.decode_bytes(sub, ctx_done) + runner.store_step_bytes(sub, ctx_done, rewrite_tiles=False)
     return {
         "value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
         "tokens_per_s_per_layer": round(len(done) / dt, 2),
@@ -396,7 +396,10 @@ def main():
     setup = runner.setup_decode(w, partition=args.partition)
     S = w.num_seqs
     dbytes = runner.decode_bytes(w, setup.ctx)
-    sbytes = runner.store_step_bytes(w, setup.ctx)
+    # the timed steps store the same current token again and again: the
+    # block's scale does not change after the first, so the store's
+    # algorithmic writes are the token's own codes (not the whole tile)
+    sbytes = runner.store_step_bytes(w, setup.ctx, rewrite_tiles=False)
 
     # The timed steps cycle through R copies of the pool at different
     # addresses, as the layers of a model would, so no step finds its codes in

@@ -777,6 +777,34 @@ void attn_partition_gqa(AttnArgs a) {
         for (int t = 0; t < DT; ++t) acc[T][t] = (f32x4)0.f;
     }
 
+    // V-scale normaliser.  The PV product takes the weights p sv as fp16, so
+    // a block whose fp16 V scale is tiny would give subnormal (imprecise)
+    // weights, and a large one could overflow.  The weights are therefore
+    // p sv 2^(15 - vF): vF (wave-uniform) is an fp16 exponent field that
+    // follows the largest V scale of the current step, changed only when
+    // that scale's field rises above vF or falls more than kVHyst below it,
+    // so that steady-state steps never change it.  On a change the
+    // accumulators are rescaled by the power of two (exact), and the result
+    // is multiplied back once at the end, with the codec's unit.
+    constexpr int kVHyst = 8;
+    int vF = 0;            // none yet: the first step sets it
+    float vmul = 1.f;      // 2^(15 - vF)
+    auto vnorm_step = [&](int vbits) -> float {   // vbits: fp16 bits of the step's largest V scale
+        const int f = max(1, (vbits >> 10) & 31);
+        if (f > vF || f < vF - kVHyst) {
+            const float r = __builtin_amdgcn_ldexpf(1.f, vF - f);
+#pragma unroll
+            for (int T = 0; T < TPW; ++T) {
+#pragma unroll
+                for (int t = 0; t < DT; ++t) acc[T][t] *= r;
+                zacc[T] *= r;
+            }
+            vF = f;
+            vmul = __builtin_amdgcn_ldexpf(1.f, 15 - f);
+        }
+        return vmul;
+    };
+
     const int32_t* tab = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
     // the block (within a step) whose K row this lane loads for tile mt, and
     // the row inside it: token 8(n16/4) + kappa(4mt + n16%4)
@@ -814,17 +842,12 @@ void attn_partition_gqa(AttnArgs a) {
     };
 
     // One step: scores on MFMA, online softmax, PV on MFMA.  sk, sv, zpv are
-    // this lane's block's scales (sk times sm_scale log2 e) and zero point.
-    // MULTI's lazy rescale threshold (base 2), per V codec: the fp16 weights
-    // p sv must stay finite for every fp16 input, with p up to 2^kLazy and sv
-    // the largest V scale the codec can produce (INT8: 65504 / 127 -> 516,
-    // INT8 asymmetric: 131008 / 255 -> 514, INT4: 131008 / 15 -> 8736, FP8:
-    // 65504 / 448 -> 146.25 times its unit 256): 2^6 516, 2^2 8736 and
-    // 2^0 37440 are below 65504.
-    constexpr float kLazy = !MULTI ? 0.f
-                          : VC == KV_CODEC_FP8_E4M3 ? 0.f
-                          : V4 ? 2.f
-                          : 6.f;
+    // this lane's block's scales (sk times sm_scale log2 e, sv times the
+    // V-scale normaliser 2^(15 - vF)) and zero point.
+    // MULTI's lazy rescale threshold (base 2): the fp16 weights p sv 2^(15 -
+    // vF) stay below 2^(kLazy + 1) (the normalised scale is below 2), far
+    // from fp16's largest finite value for every codec.
+    constexpr float kLazy = MULTI ? 8.f : 0.f;
     // before_pv(r) runs after the softmax, before the V operands are used
     // (the shared-staging path reads them from LDS only then).
     auto compute_step = [&](Raw& r, int st, float sk, float sv, float zpv, auto&& before_pv) {
@@ -1118,15 +1141,18 @@ void attn_partition_gqa(AttnArgs a) {
             // staged id is 0): its tokens are masked, and its scales are
             // replaced by 0 so that stale pool contents cannot reach the sums.
             if constexpr (BPS == 1) {
+                const int v0 = readlane(sv_l, i);
+                const float vm = vnorm_step(v0);
                 compute_step(r, st, bits_to_f16f((uint16_t)readlane(sk_l, i)) * c2,
-                             bits_to_f16f((uint16_t)readlane(sv_l, i)) * vunit, (float)readlane(zp_l, i), before_pv);
+                             bits_to_f16f((uint16_t)v0) * vm, (float)readlane(zp_l, i), before_pv);
             } else {
                 const bool live1 = blk0 + st * BPS + 1 < blk_end;
                 const int k0 = readlane(sk_l, 2 * i), k1 = live1 ? readlane(sk_l, 2 * i + 1) : 0;
                 const int v0 = readlane(sv_l, 2 * i), v1 = live1 ? readlane(sv_l, 2 * i + 1) : 0;
                 const int z0 = readlane(zp_l, 2 * i), z1 = live1 ? readlane(zp_l, 2 * i + 1) : 0;
+                const float vm = vnorm_step(max(v0, v1));   // fp16 bits of non-negative scales order as values
                 compute_step(r, st, bits_to_f16f((uint16_t)(my_blk ? k1 : k0)) * c2,
-                             bits_to_f16f((uint16_t)(my_blk ? v1 : v0)) * vunit, (float)(my_blk ? z1 : z0),
+                             bits_to_f16f((uint16_t)(my_blk ? v1 : v0)) * vm, (float)(my_blk ? z1 : z0),
                              before_pv);
             }
         };
@@ -1233,13 +1259,17 @@ void attn_partition_gqa(AttnArgs a) {
             // a lane group's block: `first` (my_blk 0) or the block after it,
             // which is the last block or lies past the end (masked)
             const bool mine_last = BPS == 1 || my_blk ? true : !pair;
+            const int vl = __builtin_amdgcn_readfirstlane((int)s_tscale[1]);
+            const float vm = vnorm_step(pair ? max(vl, (int)vs0) : vl);
             compute_step(r, st, bits_to_f16f((uint16_t)(mine_last ? s_tscale[0] : ks0)) * c2,
-                         bits_to_f16f((uint16_t)(mine_last ? s_tscale[1] : vs0)) * vunit,
+                         bits_to_f16f((uint16_t)(mine_last ? s_tscale[1] : vs0)) * vm,
                          (float)(mine_last ? s_tscale[2] : z0), [](Raw&) {});
         }
     }
     // lanes of one head split its tokens by group: sum their partial sums,
-    // and take the weighted code bias off every dim
+    // take the weighted code bias off every dim, and undo the V-scale
+    // normaliser (times the codec's unit)
+    const float vback = __builtin_amdgcn_ldexpf(vunit, vF - 15);
 #pragma unroll
     for (int T = 0; T < TPW; ++T) {
         l[T] += shfl_xor_f(l[T], 16);
@@ -1247,7 +1277,7 @@ void attn_partition_gqa(AttnArgs a) {
         zacc[T] += shfl_xor_f(zacc[T], 16);
         zacc[T] += shfl_xor_f(zacc[T], 32);
 #pragma unroll
-        for (int t = 0; t < DT; ++t) acc[T][t] -= zacc[T];
+        for (int t = 0; t < DT; ++t) acc[T][t] = (acc[T][t] - zacc[T]) * vback;
     }
 
     // Merge the waves' partial results in LDS (over the staging area, once
@@ -1449,15 +1479,23 @@ __device__ __forceinline__ void merge_partitions(const AttnArgs& a, int64_t row,
 
 // One wavefront per (query head, sequence): merges the partitions of
 // sequences that have more than one.
+// With a shared prefix every sequence must hold more tokens than the prefix
+// (the prefix's partitions were computed over all of it); a sequence that
+// does not gets a NaN row instead of a silently wrong one.
 template <int BS, int D>
 __global__ __launch_bounds__(64) void attn_reduce(AttnArgs a) {
     const int h = blockIdx.x;
     const int s = blockIdx.y;
     const int ctx = a.context_lens[s];
+    const int64_t row = (int64_t)s * a.num_q_heads + h;
+    if (a.shared_tokens > 0 && ctx <= a.shared_tokens) {
+        for (int d = threadIdx.x; d < D; d += 64) a.out[row * D + d] = 0x7E00u;   // fp16 NaN
+        return;
+    }
     const int nblk = (ctx + BS - 1) / BS;
     const int nparts = max(1, (nblk + a.partition_blocks - 1) / a.partition_blocks);
     if (nparts == 1) return;
-    merge_partitions<D>(a, (int64_t)s * a.num_q_heads + h, nparts);
+    merge_partitions<D>(a, row, nparts);
 }
 
 // Multi-query form: one wavefront per (query head, query token, sequence);

@@ -19,9 +19,9 @@
 // starting at l * D/64 of every row, so each fp16 row read and the lane's
 // code rows are contiguous.
 //
-// Exact codes without a per-element division (Quantizer below): a fast
-// pass that is exact except on ties, which send the wave through an exact
-// routine whose result equals round-half-even of the exact quotient.
+// Exact codes without a per-element division (Quantizer, quantizer.h): a
+// fast pass that is exact except on ties, which send the wave through an
+// exact routine whose result equals round-half-even of the exact quotient.
 //
 // Further codecs: FP8 E4M3 (yunthe.com "vLLM deployment" names the format)
 // with an fp16 absmax/448 scale per (block, head), each code the E4M3 of the
@@ -32,6 +32,7 @@
 
 #include "device_common.h"
 #include "pbq_internal.h"
+#include "quantizer.h"
 
 namespace pbq {
 
@@ -54,41 +55,6 @@ struct TileStoreArgs {
 // zero point << 16), for write_stored_tile.
 struct TileScales {
     uint32_t k_scale, v_scale, v_zp, prev;
-};
-
-// Codes of one tile with scale s (an fp16 value; s == 0 for an all-zero
-// tile).  exact(): round-half-even of x / s + zp for fp16 x, without a
-// division: n = rint(x * (1/s)) is within one of the answer, the remainder
-// x - n*s is exact in one FMA, and comparing |rem| with s/2 (also exact)
-// decides the nearest integer and the tie.  fast(): rint(x * (1/s) + off),
-// clamped, as a float.  For fp16 x and s the quotient x / s is either exactly
-// halfway between two integers or at least 2^-12 away from every halfway
-// point (x / s - k - 1/2 is a multiple of 2^min(a+1, b) over 2 S 2^b, for
-// x = X 2^a, s = S 2^b, S < 2^11), while the fused x * (1/s) + off is within
-// 2^-15 of x / s + off for results up to 256 (1/s and the FMA each round
-// once), so fast() agrees with exact() everywhere except on exact ties,
-// which it flags (remainder of exactly s/2) for the caller to redo with
-// exact().
-struct Quantizer {
-    float s, rcp, half_s;
-    __device__ __forceinline__ explicit Quantizer(float sc)
-        : s(sc), rcp(sc > 0.f ? 1.0f / sc : 0.f), half_s(sc > 0.f ? 0.5f * sc : -1.f) {}
-    __device__ __forceinline__ int exact(float x, int zp) const {
-        const float n = __builtin_rintf(x * rcp);
-        const float rem = __builtin_fmaf(-n, s, x);
-        const float arem = __builtin_fabsf(rem);
-        const int dir = rem > 0.f ? 1 : -1;
-        int q = (int)n + zp;
-        q += arem > half_s ? dir : 0;                     // n was one off
-        q += (arem == half_s && (q & 1)) ? dir : 0;       // exact tie -> even
-        return q;
-    }
-    __device__ __forceinline__ float fast(float x, float off, float lo, float hi, bool& tie) const {
-        const float u = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(__builtin_fmaf(x, rcp, off)), lo), hi);
-        const float rem = __builtin_fmaf(-(u - off), s, x);   // exact
-        tie |= __builtin_fabsf(rem) == half_s;
-        return u;
-    }
 };
 
 // Four values (already divided by the scale) -> four E4M3 bytes, the first

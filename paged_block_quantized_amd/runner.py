@@ -231,16 +231,25 @@ def decode_bytes(w: W.Workload, ctx: np.ndarray) -> int:
     return codes + meta_b + qo + tables
 
 
-def store_step_bytes(w: W.Workload, ctx: np.ndarray) -> int:
+def store_step_bytes(w: W.Workload, ctx: np.ndarray, rewrite_tiles: bool = True) -> int:
     """Algorithmic bytes of storing the current token: the block's exact rows
     read (tail slot + new row, fp16 K and V), its codes and metadata written,
-    and the per-sequence index arrays."""
+    and the per-sequence index arrays.
+
+    rewrite_tiles False: the block's scale (and zero point) is already what
+    the store computes -- as when the same token is stored again -- so the
+    earlier rows' codes are unchanged and only the token's own codes are
+    written (its K row and its entry of every V dim row), with the block's
+    metadata read instead of written."""
     Hkv, D, bs = w.num_kv_heads, w.head_dim, w.block_size
     vbits = 4 if w.v_codec == "i4" else 8
     meta = 2 + 2 + (1 if w.v_codec in ("i4", "i8a") else 0)
     rows = (ctx - 1) % bs + 1                    # rows the block holds after the store
     read = int(np.sum(rows)) * Hkv * D * 2 * 2
-    write = len(ctx) * Hkv * (bs * D * (8 + vbits) // 8 + meta)
+    if rewrite_tiles:
+        write = len(ctx) * Hkv * (bs * D * (8 + vbits) // 8 + meta)
+    else:
+        write = len(ctx) * Hkv * (D * (8 + vbits) // 8 + meta)   # metadata read, not written
     tail_write = int(np.sum(rows < bs)) * Hkv * D * 2 * 2
     return read + write + tail_write + len(ctx) * 4 * 4
 

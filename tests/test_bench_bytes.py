@@ -63,6 +63,17 @@ def test_store_step_bytes_one_token():
     rows = 16   # position 4095 fills its block
     expect = 32 * rows * 32 * 128 * 4 + 32 * 32 * (16 * 128 * 2 + 4) + 32 * 16
     assert runner.store_step_bytes(w, ctx) == expect
+    # the same token stored again (the benchmark's repeated step): the scale
+    # is unchanged, so only the token's K row and V entries are written and
+    # the metadata is read
+    expect_row = 32 * rows * 32 * 128 * 4 + 32 * 32 * (128 * 2 + 4) + 32 * 16
+    assert runner.store_step_bytes(w, ctx, rewrite_tiles=False) == expect_row
+    # INT4 V: half a byte per V code
+    w4 = W.WORKLOADS["gqa70b"]
+    ctx4 = np.array([33, 64])
+    rows4 = np.array([1, 32])
+    expect4 = (int(rows4.sum()) * 8 * 128 * 4 + 2 * 8 * (128 * 12 // 8 + 5) + 1 * 8 * 128 * 4 + 2 * 16)
+    assert runner.store_step_bytes(w4, ctx4, rewrite_tiles=False) == expect4
 
 
 def test_bench_refuses_more_than_one_gpu():

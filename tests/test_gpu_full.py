@@ -35,21 +35,21 @@ def _run(name, samples):
 
 
 def test_llama7b_full():
-    _run("llama7b", samples=[0, 13, 31])
+    _run("llama7b", samples=[0, 9, 13, 22, 31])
 
 
 @pytest.mark.parametrize("name", ["llama7b_fp8", "llama7b_i8a", "gqa70b_fp8"])
 def test_codec_variants_full(name):
     """The FP8 and INT8-asymmetric workloads at full size, sampled sequences
     against the oracle."""
-    _run(name, samples=[0, 17] if name.startswith("llama") else [0, 77, 127])
+    _run(name, samples=[0, 11, 17, 31] if name.startswith("llama") else [0, 40, 77, 127])
 
 
 def test_shared_prefix_full():
     """The step reads the 4096-token prefix once (paged_attn_decode_shared_prefix);
     the per-sequence path (paged_attn_decode_append) gives the same pool bit
     for bit and outputs within tolerance of it."""
-    setup = _run("shared_prefix", samples=[0, 31])
+    setup = _run("shared_prefix", samples=[0, 10, 21, 31])
     assert setup.shared == 4096
     st = setup.pool.stats()
     assert st["used"] == 28800 and st["shared"] == 128 and st["free"] == 0
@@ -130,11 +130,12 @@ def test_prefill_store_full():
         t = tables[s].long()
         assert np.array_equal(pool.k_codes[t].cpu().numpy(), ref.k_codes), s
         assert np.array_equal(pool.v_codes[t].cpu().numpy(), ref.v_codes), s
+        assert np.array_equal(pool.k_scale[t].cpu().numpy().view(np.uint16), ref.k_scale.view(np.uint16)), s
         assert np.array_equal(pool.v_scale[t].cpu().numpy().view(np.uint16), ref.v_scale.view(np.uint16)), s
 
 
 def test_gqa70b_full():
-    setup = _run("gqa70b", samples=[0, 64, 127])
+    setup = _run("gqa70b", samples=[0, 33, 64, 127])
     assert setup.w.num_q_heads // setup.w.num_kv_heads == 8
 
 

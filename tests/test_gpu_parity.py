@@ -420,6 +420,70 @@ def test_shared_prefix_decode(bs, d, vc, g, hkv, S, part):
         check_sequence(setup, s, out.cpu().numpy(), "shared-prefix decode")
 
 
+P9_SHAPES = [
+    # (block_size, head_dim, v codec, query heads per KV head, KV heads)
+    (32, 128, "i4", 1, 2),
+    (16, 64, "i8", 4, 1),
+    (32, 128, "fp8", 8, 2),
+    (16, 128, "i8a", 1, 2),
+]
+
+
+@pytest.mark.parametrize("bs,d,vc,g,hkv", P9_SHAPES)
+def test_shared_prefix_equals_private_copies_bitwise(bs, d, vc, g, hkv):
+    """Sequences forked from one prefix (yunthe.com "PagedAttention
+    mechanism": prefix sharing maps every sequence's prefix to the same
+    physical blocks) decode bitwise as they do when each holds a private
+    copy of the prefix blocks (kv_copy_blocks into fresh blocks, tables
+    rewritten), at several partition sizes; the shared blocks are the
+    oracle's quantization of the prefix rows after every sequence's
+    divergent tokens are stored."""
+    import dataclasses
+    from oracle import allocator as A
+    from paged_block_quantized_amd import runner, workloads as W
+    from gpu_util import check_sequence
+    announce("P9 shared vs private prefix", bs, d, vc, g, hkv)
+    S, part = 5, 64
+    prefix = 2 * part
+    ctx = tuple(prefix + x for x in [1, bs + 1, 3 * bs + 5, 300, 77])
+    w = dataclasses.replace(W.WORKLOADS["shared_prefix"], name="p9_small", num_seqs=S,
+                            num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                            v_codec=vc, ctx_kind="list", ctx=ctx, prefix=prefix, partition=part,
+                            seed=3 * bs + d + g)
+    P = prefix // bs
+    n_blocks = runner.blocks_needed(w, W.context_lengths(w)) + S * P
+    w = dataclasses.replace(w, pool_blocks=n_blocks)
+    setup = runner.setup_decode(w)
+    setup.step_unshared()          # the current tokens stored, decoded per sequence
+    torch.cuda.synchronize()
+    pool = setup.pool
+    shared_ids = setup.tables[:, :P].cpu().numpy()
+    assert (shared_ids == shared_ids[0]).all(), "every sequence maps the prefix to the same blocks"
+    for s in range(S):
+        check_sequence(setup, s, setup.out.cpu().numpy(), "P9 shared step")
+    # private copies of the prefix blocks, one set per sequence
+    dummy = S + 7
+    pool.alloc(dummy, S * prefix)
+    dtab = pool.table(dummy)[0]
+    private = setup.tables.clone()
+    copies = []
+    for s in range(S):
+        for j in range(P):
+            copies.append((A.COPY_BLOCK, int(shared_ids[s, j]), int(dtab[s * P + j])))
+            private[s, j] = int(dtab[s * P + j])
+    keep = pool.copy_blocks(copies)
+    torch.cuda.synchronize()
+    del keep
+    for p in (0, bs if g == 1 else 32, part, 4096):
+        outs = []
+        for tables in (setup.tables, private):
+            out = torch.empty_like(setup.q)
+            pool.decode(setup.q, out, tables, setup.ctx_dev, setup.max_ctx, setup.sm_scale, p)
+            torch.cuda.synchronize()
+            outs.append(out.cpu().numpy())
+        assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16)), f"partition {p}"
+
+
 @pytest.mark.parametrize("bs,vc", [(16, "i8"), (32, "i4")])
 def test_prefix_cache_end_to_end(bs, vc):
     """kv_seq_alloc_prefix: requests whose token ids share prefixes map the
@@ -791,3 +855,123 @@ def test_multi_query_validates():
         L.paged_attn_multi_query(pool.desc, pool.mem, q, q, 1, 2, cu, 4, 4, t, 4, c, 40, 0.1, 16)
     with pytest.raises(L.PBQError, match="workspace"):
         L.paged_attn_multi_query(pool.desc, pool.mem, q, q, 1, 2, cu, 4, 4, t, 4, c, 40, 0.1, 32)
+
+
+# ---- V magnitudes far from 1: the fp16 weights of the matrix-core path ------
+
+def _scaled_v_case(bs, d, vc, g, hkv, kind, seed):
+    """Histories whose V values are tiny (kind "small3": N(0, 1e-3),
+    "small4": N(0, 1e-4): fp16 V scales near or below fp16's normal range)
+    or alternate by 32-token step between N(0, 1e-3) and N(0, 10) with K
+    set so that the tiny-V tokens dominate the softmax ("mixed").  Returns
+    (hk, hv, q, sigma), sigma the magnitude of the V values that dominate
+    the output."""
+    rng = np.random.default_rng(seed)
+    ctx = [1, 40, 333, 700, 1100, 2047]
+    hq = g * hkv
+    hk, hv = [], []
+    for c in ctx:
+        k = rng.standard_normal((c, hkv, d))
+        v = rng.standard_normal((c, hkv, d))
+        if kind == "mixed":
+            small = (np.arange(c) // 32) % 2 == 0
+            v *= np.where(small, 1e-3, 10.0)[:, None, None]
+            k *= 0.05
+            k[:, :, 0] = np.where(small, 20.0 * np.sqrt(d), 0.0)[:, None]
+        else:
+            v *= 1e-3 if kind == "small3" else 1e-4
+        hk.append(k.astype(np.float16))
+        hv.append(v.astype(np.float16))
+    if kind == "mixed":
+        q = (rng.standard_normal((len(ctx), hq, d)) * 0.01).astype(np.float16)
+        q[:, :, 0] = 1.0
+    else:
+        q = rng.standard_normal((len(ctx), hq, d)).astype(np.float16)
+    sigma = 1e-4 if kind == "small4" else 1e-3
+    return ctx, hk, hv, q, sigma
+
+
+SCALED_V = [(bs, g, vc, kind) for bs, g in ((32, 8), (16, 4)) for vc in ("i8", "i4", "i8a", "fp8")
+            for kind in ("small3", "small4", "mixed")]
+
+
+@pytest.mark.parametrize("bs,g,vc,kind", SCALED_V)
+def test_gqa_decode_scaled_v(bs, g, vc, kind):
+    """Grouped-query decode with V far from unit magnitude: outputs within
+    tolerance relative to the V magnitude (attention is linear in V), for
+    the plain decode at several partition sizes and for the fused store +
+    decode (single pass).  The matrix cores take fp16 weights p * sv; they
+    are normalised by a power of two that follows the V scales, so tiny
+    scales keep full fp16 precision."""
+    announce("gqa-scaled-v", bs, g, vc, kind)
+    from paged_block_quantized_amd import KVPool
+    d, hkv = 128, 2
+    ctx, hk, hv, q, sigma = _scaled_v_case(bs, d, vc, g, hkv, kind, seed=bs + g + len(kind))
+    n_blocks = sum((c + bs - 1) // bs for c in ctx) + 2
+    order = np.random.default_rng(5).permutation(n_blocks)
+    case = SmallCase(hk, hv, q, g * hkv, hkv, d, bs, vc, n_blocks, order)
+    case.store_all()
+    assert_pool_equal(case.pool, case.opool)
+    ref = case.reference()
+    for part in (0, 32, 4096):
+        got = case.decode(part)
+        assert_close(got / sigma, ref / sigma, f"gqa scaled V {kind} {vc} bs{bs} part{part}")
+    # the fused store + decode: every token but the last stored first
+    dev = "cuda"
+    S = len(ctx)
+    pool = KVPool(n_blocks, bs, hkv, d, vc, max_seqs=S, free_order=order)
+    for s, c in enumerate(ctx):
+        pool.alloc(s, c - 1)
+    mb = max((c + bs - 1) // bs for c in ctx)
+    tables, _, slots = pool.batch_tables(list(range(S)), mb)
+    lens = [c - 1 for c in ctx]
+    kk = torch.from_numpy(np.concatenate([h[:c - 1] for h, c in zip(hk, ctx)])).to(dev)
+    vv = torch.from_numpy(np.concatenate([h[:c - 1] for h, c in zip(hv, ctx)])).to(dev)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+    pool.quantize_store(kk, vv, cu, torch.zeros(S, dtype=torch.int32, device=dev), tables.to(dev),
+                        slots.to(dev), max(max(lens), 1))
+    for s in range(S):
+        assert pool.append(s, 1) == []
+    tables, ctx_h, slots = pool.batch_tables(list(range(S)), mb)
+    k_new = torch.from_numpy(np.stack([h[c - 1] for h, c in zip(hk, ctx)])).to(dev)
+    v_new = torch.from_numpy(np.stack([h[c - 1] for h, c in zip(hv, ctx)])).to(dev)
+    qd = torch.from_numpy(q).to(dev)
+    out = torch.empty_like(qd)
+    pool.decode_append(k_new, v_new, slots.to(dev), qd, out, tables.to(dev), ctx_h.to(dev), max(ctx),
+                       1 / np.sqrt(d), 4096)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy() / sigma, ref / sigma, f"gqa fused scaled V {kind} {vc} bs{bs}")
+
+
+@pytest.mark.parametrize("bs,g,vc,kind", [(32, 8, vc, k) for vc in ("i8", "i4", "i8a", "fp8")
+                                          for k in ("small3", "small4", "mixed")] +
+                         [(16, 1, vc, k) for vc in ("i8", "i4") for k in ("small4", "mixed")])
+def test_multi_query_scaled_v(bs, g, vc, kind):
+    """Multi-query attention with V far from unit magnitude, within
+    tolerance relative to the V magnitude, one pass and split partitions."""
+    announce("multi-scaled-v", bs, g, vc, kind)
+    d, hkv = 128, 2
+    ctx, hk, hv, q_dec, sigma = _scaled_v_case(bs, d, vc, g, hkv, kind, seed=3 * bs + g + len(kind))
+    n_blocks = sum((c + bs - 1) // bs for c in ctx) + 2
+    case = SmallCase(hk, hv, q_dec, g * hkv, hkv, d, bs, vc, n_blocks,
+                     np.random.default_rng(6).permutation(n_blocks))
+    case.store_all()
+    ns = [1, 17, 64, 40, 100, 33]
+    rng = np.random.default_rng(bs + g)
+    T = sum(ns)
+    if kind == "mixed":
+        q_rows = (rng.standard_normal((T, g * hkv, d)) * 0.01).astype(np.float16)
+        q_rows[:, :, 0] = 1.0
+    else:
+        q_rows = rng.standard_normal((T, g * hkv, d)).astype(np.float16)
+    cu = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    sm = 1 / np.sqrt(d)
+    ref = attention.paged_multi_query(case.opool, [case.model.table(s)[0] for s in range(len(ctx))],
+                                      case.ctx, q_rows, cu, sm)
+    qd = torch.from_numpy(q_rows).cuda()
+    cud = torch.from_numpy(cu).cuda()
+    for part in (0, 256, 4096):
+        out = torch.full_like(qd, float("nan"))
+        case.pool.multi_query(qd, out, cud, max(ns), case.tables, case.ctx_dev, max(case.ctx), sm, part)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy() / sigma, ref / sigma, f"multi scaled V {kind} {vc} part{part}")
