@@ -45,47 +45,124 @@ def _r5(x):
     return round(x, 5) if x == x else None
 
 
-def cpu_baseline(setup, seconds):
-    """The oracle's decode step (store the current token, attend over the
-    whole context) on a bounded sample of sequences, single-threaded."""
+def host_cpu():
+    """The host's CPU model (from /proc/cpuinfo) and logical CPU count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count() or 1
+
+
+def oracle_workers():
+    """Worker processes for the oracle baseline: every host CPU, at most 16
+    (the share of a one-GPU host this benchmark may occupy)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _oracle_decode_worker(units, bs, k_codec, v_codec, sm_scale, start_evt, seconds, out_q):
+    """One worker process of the oracle baseline (spawned: imports numpy and
+    the oracle only, never touches the GPU).  Each unit is one (sequence,
+    KV head): fp16 history [ctx, D] of K and V and its query heads [G, D].
+    The history up to the current token is quantized before the timed
+    region; then, until `seconds` have passed, each unit in turn re-stores
+    its current token (re-quantizing the block) and runs float64 attention
+    over its dequantized context."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import attention, paged
+    prepared = []
+    for uid, hk, hv, q in units:
+        ctx = hk.shape[0]
+        nb = (ctx + bs - 1) // bs
+        pool = paged.PoolArrays(nb, 1, bs, hk.shape[-1], k_codec=k_codec, v_codec=v_codec)
+        paged.store_range(pool, list(range(nb)), hk[:, None], hv[:, None], 0, ctx - 1)
+        prepared.append((uid, ctx, nb, pool, hk[:, None], hv[:, None], q))
+    done = {uid: 0 for uid, *_ in units}
+    start_evt.wait()
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for uid, ctx, nb, pool, hk, hv, q in prepared:
+                paged.store_range(pool, list(range(nb)), hk, hv, ctx - 1, ctx)
+                khat, vhat = paged.gather_dequant(pool, list(range(nb)), ctx)
+                attention.decode_attention(q, khat, vhat, sm_scale)
+                done[uid] += 1
+        dt = time.perf_counter() - t0
+    out_q.put((done, dt))
+
+
+def cpu_baseline(setup, seconds):
+    """The oracle's decode step on the host's cores: (sequence, KV head)
+    units of the workload's first sequences, spread over a pool of worker
+    processes, each repeating the oracle's step (store the current token,
+    float64 attention over the dequantized context) for `seconds`.
+    Throughput is the algorithmic bytes of the unit-steps done (a unit's
+    share of its sequence's step bytes) over the slowest worker's time."""
+    import multiprocessing as mp
+
+    import numpy as np
+
     from paged_block_quantized_amd import runner, workloads as W
 
     w = setup.w
-    bs = w.block_size
-    prepared = []
-    budget_seqs = min(w.num_seqs, 4)
-    for s in range(budget_seqs):
-        ctx = int(setup.ctx[s])
+    H, G = w.num_kv_heads, w.num_q_heads // w.num_kv_heads
+    n_workers = oracle_workers()
+    # units of whole sequences first, at most about 256 MiB of fp16 history
+    unit_bytes = int(np.max(setup.ctx)) * w.head_dim * 4
+    max_units = max(n_workers, min(w.num_seqs * H, (256 << 20) // unit_bytes))
+    units, seq_of = [], {}
+    for s in range(w.num_seqs):
+        if len(units) >= max_units:
+            break
         hk, hv = runner.sequence_history(setup, s)
-        nb = (ctx + bs - 1) // bs
-        pool = paged.PoolArrays(nb, w.num_kv_heads, bs, w.head_dim, k_codec=W.k_codec_of(w),
-                                v_codec=w.v_codec)
-        paged.store_range(pool, list(range(nb)), hk, hv, 0, ctx - 1)
-        prepared.append((s, ctx, nb, pool, hk, hv, setup.q[s].cpu().numpy()))
-    with threadpool_limits(limits=1):
-        done, t0 = [], time.perf_counter()
-        while True:
-            for s, ctx, nb, pool, hk, hv, q in prepared:
-                paged.store_range(pool, list(range(nb)), hk, hv, ctx - 1, ctx)
-                khat, vhat = paged.gather_dequant(pool, list(range(nb)), ctx)
-                attention.decode_attention(q, khat, vhat, setup.sm_scale)
-                done.append(s)
-            if time.perf_counter() - t0 >= seconds:
+        q = setup.q[s].cpu().numpy()
+        for g in range(H):
+            if len(units) >= max_units:
                 break
-        dt = time.perf_counter() - t0
-    ctx_done = np.array([int(setup.ctx[s]) for s in done])
-    sub = dataclasses.replace(w, num_seqs=len(done), prefix=0)
-    nbytes = runner.decode_bytes(sub, ctx_done) + runner.store_step_bytes(sub, ctx_done, rewrite_tiles=False)
+            uid = len(units)
+            seq_of[uid] = s
+            units.append((uid, np.ascontiguousarray(hk[:, g]), np.ascontiguousarray(hv[:, g]),
+                          np.ascontiguousarray(q[g * G:(g + 1) * G])))
+    n_workers = min(n_workers, len(units))
+    ctx_mp = mp.get_context("spawn")
+    start_evt, out_q = ctx_mp.Event(), ctx_mp.Queue()
+    procs = [ctx_mp.Process(target=_oracle_decode_worker,
+                            args=(units[i::n_workers], w.block_size, W.k_codec_of(w), w.v_codec, setup.sm_scale,
+                                  start_evt, seconds, out_q), daemon=True)
+             for i in range(n_workers)]
+    for p_ in procs:
+        p_.start()
+    time.sleep(0.5)
+    start_evt.set()
+    results = [out_q.get(timeout=seconds + 600) for _ in procs]
+    for p_ in procs:
+        p_.join(timeout=60)
+    dt = max(r[1] for r in results)
+    nbytes = 0
+    steps = 0
+    for done, _ in results:
+        for uid, n in done.items():
+            ctx1 = np.array([int(setup.ctx[seq_of[uid]])])
+            sub = dataclasses.replace(w, num_seqs=1, prefix=0)
+            per_seq = runner.decode_bytes(sub, ctx1) + runner.store_step_bytes(sub, ctx1, rewrite_tiles=False)
+            nbytes += n * per_seq / H
+            steps += n
+    model, cpus = host_cpu()
+    n_seqs = len(set(seq_of.values()))
     return {
-        "value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "tokens_per_s_per_layer": round(len(done) / dt, 2),
-        "sample": (f"{len(done)} sequence-steps over the first {budget_seqs} sequences of the "
-                   f"same workload (oracle store of the current token + float64 attention), "
-                   f"{dt:.1f} s, one thread; shared prefixes counted per sequence"),
+        "value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": n_workers, "kind": "oracle",
+        "host_cpus": cpus, "cpu_model": model,
+        "tokens_per_s_per_layer": round(steps / H / dt, 2),
+        "sample": (f"{steps} (sequence, KV head) unit-steps over {len(units)} units of the first {n_seqs} "
+                   f"sequences of the same workload (oracle store of the current token + float64 attention), "
+                   f"{n_workers} worker processes, {dt:.1f} s; shared prefixes counted per sequence"),
     }
 
 
@@ -354,6 +431,65 @@ def bench_store(w, args):
     print(json.dumps(line), flush=True)
 
 
+def read_ceiling(setup, reps=10):
+    """The plain-read ceiling of the decode's access pattern, measured with
+    kv_stream_read_tiles: exactly the tiles the decode reads (per sequence
+    and KV head, its K tiles, then its V tiles, in table order; a shared
+    prefix once), rotating over the pool copies as the timed steps do, and a
+    sequential read of the same number of bytes.  GB/s over the tile bytes
+    (the tile list itself, 4 bytes per tile, is read too and not counted)."""
+    import numpy as np
+    import torch
+
+    from paged_block_quantized_amd import _lib as L
+    w = setup.w
+    H, bs, D = w.num_kv_heads, w.block_size, w.head_dim
+    k_tile = bs * D
+    v_tile = bs * D // 2 if w.v_codec == "i4" else bs * D
+    if k_tile not in (1024, 2048, 4096) or v_tile not in (1024, 2048, 4096):
+        return None
+    tables = setup.tables.cpu().numpy()
+    shared_blocks = setup.shared // bs
+    ids = []
+    for s_ in range(w.num_seqs):
+        nb = (int(setup.ctx[s_]) + bs - 1) // bs
+        first = shared_blocks if (setup.shared and s_ > 0) else 0
+        blocks = tables[s_, first:nb].astype(np.int64)
+        for h in range(H):
+            ids.append(blocks * H + h)
+    order = torch.from_numpy(np.concatenate(ids).astype(np.int32)).cuda()
+    n = int(order.numel())
+    sink = torch.empty(max(1, L.kv_stream_read_sink_words(n)), dtype=torch.int32, device="cuda")
+    copies = [setup.pool.arrays] + [arr for _, arr in (setup.replicas or [])]
+    stream = torch.cuda.current_stream()
+
+    def run(ordered):
+        ms = []
+        for i in range(reps + 1):
+            arr = copies[i % len(copies)]
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for name, tb in (("k_codes", k_tile), ("v_codes", v_tile)):
+                src = arr[name]
+                L.kv_stream_read_tiles(src, src.numel() * src.element_size() // tb, tb,
+                                       order if ordered else None, n, sink, stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            if i:
+                ms.append(a.elapsed_time(b))
+        return float(np.median(ms))
+
+    nbytes = n * (k_tile + v_tile)
+    t_tiles, t_seq = run(True), run(False)
+    return {"kernel": "kv_stream_read_tiles (one launch per code array)", "bytes": nbytes,
+            "decode_tiles_gbs": round(nbytes / (t_tiles * 1e-3) / 1e9, 1),
+            "sequential_gbs": round(nbytes / (t_seq * 1e-3) / 1e9, 1),
+            "decode_tiles_frac": round(nbytes / (t_tiles * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "sequential_frac": round(nbytes / (t_seq * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "the decode's tile list over pool copies the timed steps rotate through; context "
+                    "for roofline.frac (the decode's arithmetic made free), not a denominator"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -455,23 +591,33 @@ def main():
     # context: the same step as two calls (kv_quantize_store, paged_attn_decode)
     ms_sep, st_ms, dec = timed(min(K, 20), R, fused=False)
     store_ms, dec_ms = float(np.mean(st_ms)), float(np.mean(dec))
-    dec_same, fl = np.array([np.nan]), [np.nan]
+    dec_same, fl_w, fl_r, ceiling = np.array([np.nan]), [np.nan], [np.nan], None
     if not args.only_timed:
         # context: the same pool every step (its codes partly in the last-level cache)
         _, dec_same, _ = timed(min(K, 20), 1)
-        # context: decode after a 1 GiB cache-clearing write (outside the events);
-        # the write leaves dirty lines whose write-back slows the next reads
+        # context: decode after a 1 GiB cache-clearing pass (outside the
+        # events), once a write (torch zero_: it leaves dirty lines whose
+        # write-back competes with the next reads) and once a plain read
+        # (kv_stream_read_tiles: clean lines, so only the cache is cold)
+        from paged_block_quantized_amd import _lib as L
         flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        fl = []
-        for _ in range(10):
-            flush.zero_()
+        n_fl = (1 << 30) // 4096
+        sink = torch.empty(L.kv_stream_read_sink_words(n_fl), dtype=torch.int32, device="cuda")
+        fl_w, fl_r = [], []
+        for i in range(20):
+            if i % 2 == 0:
+                flush.zero_()
+            else:
+                L.kv_stream_read_tiles(flush, n_fl, 4096, None, n_fl, sink, stream)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             setup.attend()
             b.record(stream)
             torch.cuda.synchronize()
-            fl.append(a.elapsed_time(b))
-        del flush
+            (fl_w if i % 2 == 0 else fl_r).append(a.elapsed_time(b))
+        del flush, sink
+        print("read ceiling", file=sys.stderr, flush=True)
+        ceiling = read_ceiling(setup)
 
     # context: with a shared prefix, the per-sequence step (the prefix read
     # by every sequence) for comparison with the shared-prefix call
@@ -547,7 +693,8 @@ def main():
                        "separate_quantize_store_1tok": round(store_ms, 5),
                        "separate_paged_attn_decode": round(dec_ms, 5),
                        "paged_attn_decode_append_same_pool_back_to_back": _r5(np.mean(dec_same)),
-                       "paged_attn_decode_after_1GiB_flush": _r5(np.median(fl)),
+                       "paged_attn_decode_after_1GiB_write_flush": _r5(np.median(fl_w)),
+                       "paged_attn_decode_after_1GiB_read_flush": _r5(np.median(fl_r)),
                        "per_sequence_step_without_shared_prefix": _r5(unshared)},
         "host_us": {"kv_seq_alloc_prefix_plus_free": host_prefix_us},
         "roofline": {
@@ -563,6 +710,7 @@ def main():
             "decode_only": {"bytes_per_launch": dbytes,
                             "achieved": round(dbytes / (dec_ms * 1e-3) / 1e9, 2),
                             "frac": round(dbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "plain_read_ceiling": ceiling,
         },
     }
     if not args.no_cpu_baseline:

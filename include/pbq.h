@@ -478,6 +478,24 @@ int32_t paged_attn_default_partition(const kv_pool_desc* desc,
                                      int32_t num_seqs, int32_t num_q_heads,
                                      int32_t max_context_len);
 
+/* ---- Measurement: the plain-read ceiling of the decode's access pattern --
+ * Reads n_tiles tiles of tile_bytes bytes (1024, 2048 or 4096) from src_dev
+ * and computes nothing but an xor of them: tile i of the list is source tile
+ * order_dev[i] (a device int32 array of n_tiles ids, each in
+ * [0, n_src_tiles): the caller's contract, not checked), or source tile i
+ * when order_dev is NULL (then n_tiles <= n_src_tiles).  Each wavefront
+ * streams a contiguous run of the list with 16-byte loads contiguous across
+ * the wave, as the decode kernels read their tiles; one uint32 per work
+ * group is written to sink_dev, which must hold at least
+ * kv_stream_read_sink_words(n_tiles) words.  Asynchronous on stream.  The
+ * benchmark reports this rate beside the decode's: reading scattered 2 KiB
+ * tiles at this rate is what the decode could reach if its arithmetic cost
+ * nothing. */
+size_t kv_stream_read_sink_words(int64_t n_tiles);
+kv_status kv_stream_read_tiles(const void* src_dev, int64_t n_src_tiles, int32_t tile_bytes,
+                               const int32_t* order_dev, int64_t n_tiles, uint32_t* sink_dev,
+                               size_t sink_words, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* kv_last_error(void);
 

@@ -70,7 +70,7 @@ EXPORTS = [
     "kv_quantize_store", "paged_attn_workspace_bytes", "paged_attn_decode",
     "paged_attn_decode_append", "paged_attn_decode_shared_prefix", "paged_attn_multi_query",
     "paged_attn_multi_query_workspace_bytes",
-    "paged_attn_default_partition", "kv_last_error",
+    "paged_attn_default_partition", "kv_stream_read_sink_words", "kv_stream_read_tiles", "kv_last_error",
 ]
 
 _lib = None
@@ -121,6 +121,8 @@ def lib():
                                             VP, I32, VP, I32, ctypes.c_float, I32, VP, SZ, VP]),
             "paged_attn_multi_query_workspace_bytes": (SZ, [P(kv_pool_desc), I32, I32, I32, I32, I32, I32]),
             "paged_attn_default_partition": (I32, [P(kv_pool_desc), I32, I32, I32]),
+            "kv_stream_read_sink_words": (SZ, [I64]),
+            "kv_stream_read_tiles": (st, [VP, I64, I32, VP, I64, VP, SZ, VP]),
             "kv_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -371,3 +373,12 @@ def paged_attn_multi_query(desc, mem, q, out, num_seqs, num_q_heads, cu_seqlens,
         _ptr(cu_seqlens), int(num_tokens), int(max_q_len), _ptr(block_tables), int(max_blocks_per_seq),
         _ptr(context_lens), int(max_context_len), float(sm_scale), int(partition_size), _ptr(workspace),
         int(workspace_bytes), _stream(stream)))
+
+
+def kv_stream_read_sink_words(n_tiles):
+    return lib().kv_stream_read_sink_words(int(n_tiles))
+
+
+def kv_stream_read_tiles(src, n_src_tiles, tile_bytes, order, n_tiles, sink, stream=None):
+    _check(lib().kv_stream_read_tiles(_ptr(src), int(n_src_tiles), int(tile_bytes), _ptr(order), int(n_tiles),
+                                      _ptr(sink), int(sink.numel()), _stream(stream)))

@@ -555,6 +555,52 @@ kv_status paged_attn_multi_query(const kv_pool_desc* d, const kv_pool_mem* m, co
     return pbq::hip_status(pbq::launch_paged_attn(a, (hipStream_t)stream), "paged_attn_multi_query launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+// List entries per wavefront of the streaming read: about 16 waves per
+// compute unit over the whole list, at least 16 tiles each.
+int64_t stream_tiles_per_wave(int64_t n_tiles) {
+    const int64_t waves = 16 * (int64_t)pbq::device_cu_count();
+    return std::max<int64_t>(16, (n_tiles + waves - 1) / waves);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kv_stream_read_sink_words(int64_t n_tiles) {
+    if (n_tiles <= 0) return 0;
+    return (size_t)pbq::stream_read_groups(n_tiles, stream_tiles_per_wave(n_tiles));
+}
+
+kv_status kv_stream_read_tiles(const void* src, int64_t n_src_tiles, int32_t tile_bytes, const int32_t* order,
+                               int64_t n_tiles, uint32_t* sink, size_t sink_words, void* stream) {
+    int sh = -1;
+    if (tile_bytes == 1024) sh = 0;
+    else if (tile_bytes == 2048) sh = 1;
+    else if (tile_bytes == 4096) sh = 2;
+    if (sh < 0) return fail(KV_ERR_INVALID, "tile_bytes must be 1024, 2048 or 4096");
+    if (n_tiles < 0 || n_src_tiles < 0) return fail(KV_ERR_INVALID, "negative size argument");
+    if (n_tiles == 0) return KV_OK;
+    if (!src || !sink || !pbq::aligned16(src)) return fail(KV_ERR_INVALID, "src and sink must be non-NULL, src 16-byte aligned");
+    if (!order && n_tiles > n_src_tiles) return fail(KV_ERR_INVALID, "n_tiles exceeds n_src_tiles");
+    if (n_src_tiles > ((int64_t)1 << 40 >> (10 + sh))) return fail(KV_ERR_INVALID, "source too large");
+    const int64_t tpw = stream_tiles_per_wave(n_tiles);
+    const int64_t groups = pbq::stream_read_groups(n_tiles, tpw);
+    if (groups > 0x7FFFFFFF) return fail(KV_ERR_INVALID, "too many tiles for one launch");
+    if (sink_words < (size_t)groups) return fail(KV_ERR_INVALID, "sink too small: see kv_stream_read_sink_words");
+    pbq::StreamReadArgs a{};
+    a.src = (const uint8_t*)src;
+    a.order = order;
+    a.n_tiles = n_tiles;
+    a.tiles_per_wave = tpw;
+    a.tile_kib_log2 = sh;
+    a.sink = sink;
+    return pbq::hip_status(pbq::launch_stream_read(a, (hipStream_t)stream), "kv_stream_read_tiles launch");
+}
+
 size_t paged_attn_workspace_bytes(const kv_pool_desc* d, int32_t num_seqs,
                                   int32_t num_q_heads, int32_t max_context_len,
                                   int32_t partition_size) {

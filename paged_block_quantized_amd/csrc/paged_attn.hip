@@ -498,9 +498,10 @@ void attn_partition_mha(AttnArgs a) {
 // S^T[32 tok x 16 heads] = K_hat[32 x D] * Q^T[D x 16] takes 2 x D/32
 // v_mfma_f32_16x16x32_f16, and O^T[D x 16] += V_hat^T[D x 32] * P^T[32 x 16]
 // takes D/16 more.  Codes become fp16 exactly (v_perm under 0x64); the
-// constant offset of the K codes comes off each score, that of the V codes
-// (with the zero point) once per head at the end, as the weighted sum of the
-// offsets is the same for every dim.  Products are exact in fp32.
+// constant offset of the K codes comes off each score (Q and the K codes
+// are exact, so the offset's product is too), while the V operands are
+// turned into code - zero point by one exact packed subtraction, so the PV
+// accumulators carry no offset.  Products are exact in fp32.
 //
 // MFMA 16x16x32 f16 lane layout (A: m = l%16, k = 8(l/16)+i; B: n = l%16,
 // k = 8(l/16)+i; C: n = l%16, m = 4(l/16)+i).  Token order inside a step is
@@ -766,13 +767,12 @@ void attn_partition_gqa(AttnArgs a) {
 
     const float c2 = a.sm_scale * kLog2e * code_unit<KC>();
     constexpr float vunit = code_unit<VC>();
-    float m[TPW], l[TPW], zacc[TPW];
+    float m[TPW], l[TPW];
     f32x4 acc[TPW][DT];
 #pragma unroll
     for (int T = 0; T < TPW; ++T) {
         m[T] = -INFINITY;
         l[T] = 0.f;
-        zacc[T] = 0.f;
 #pragma unroll
         for (int t = 0; t < DT; ++t) acc[T][t] = (f32x4)0.f;
     }
@@ -780,27 +780,29 @@ void attn_partition_gqa(AttnArgs a) {
     // V-scale normaliser.  The PV product takes the weights p sv as fp16, so
     // a block whose fp16 V scale is tiny would give subnormal (imprecise)
     // weights, and a large one could overflow.  The weights are therefore
-    // p sv 2^(15 - vF): vF (wave-uniform) is an fp16 exponent field that
-    // follows the largest V scale of the current step, changed only when
-    // that scale's field rises above vF or falls more than kVHyst below it,
-    // so that steady-state steps never change it.  On a change the
-    // accumulators are rescaled by the power of two (exact), and the result
-    // is multiplied back once at the end, with the codec's unit.
+    // p sv 2^(15 + kVTop - vF): vF (wave-uniform) is an fp16 exponent field
+    // that follows the largest V scale of the current step, changed only
+    // when that scale's field rises above vF or falls more than kVHyst below
+    // it, so that steady-state steps never change it.  The largest scale's
+    // weights then lie in [2^kVTop, 2^(kVTop + 1)) times p, far above fp16's
+    // subnormal range (p <= 1 in decode; MULTI's lazy softmax lets p reach
+    // 2^kLazy, so its top is lower).  On a change the accumulators are
+    // rescaled by the power of two (exact), and the result is multiplied
+    // back once at the end, with the codec's unit.
     constexpr int kVHyst = 8;
+    constexpr int kVTop = MULTI ? 6 : 10;
     int vF = 0;            // none yet: the first step sets it
-    float vmul = 1.f;      // 2^(15 - vF)
+    float vmul = 1.f;      // 2^(15 + kVTop - vF)
     auto vnorm_step = [&](int vbits) -> float {   // vbits: fp16 bits of the step's largest V scale
         const int f = max(1, (vbits >> 10) & 31);
         if (f > vF || f < vF - kVHyst) {
             const float r = __builtin_amdgcn_ldexpf(1.f, vF - f);
 #pragma unroll
-            for (int T = 0; T < TPW; ++T) {
+            for (int T = 0; T < TPW; ++T)
 #pragma unroll
                 for (int t = 0; t < DT; ++t) acc[T][t] *= r;
-                zacc[T] *= r;
-            }
             vF = f;
-            vmul = __builtin_amdgcn_ldexpf(1.f, 15 - f);
+            vmul = __builtin_amdgcn_ldexpf(1.f, 15 + kVTop - f);
         }
         return vmul;
     };
@@ -844,9 +846,10 @@ void attn_partition_gqa(AttnArgs a) {
     // One step: scores on MFMA, online softmax, PV on MFMA.  sk, sv, zpv are
     // this lane's block's scales (sk times sm_scale log2 e, sv times the
     // V-scale normaliser 2^(15 - vF)) and zero point.
-    // MULTI's lazy rescale threshold (base 2): the fp16 weights p sv 2^(15 -
-    // vF) stay below 2^(kLazy + 1) (the normalised scale is below 2), far
-    // from fp16's largest finite value for every codec.
+    // MULTI's lazy rescale threshold (base 2): the fp16 weights p sv 2^(15 +
+    // kVTop - vF) stay below 2^(kLazy + kVTop + 1) = 2^15 (the normalised
+    // scale is below 2^(kVTop + 1)), inside fp16's finite range for every
+    // codec.
     constexpr float kLazy = MULTI ? 8.f : 0.f;
     // before_pv(r) runs after the softmax, before the V operands are used
     // (the shared-staging path reads them from LDS only then).
@@ -911,11 +914,9 @@ void attn_partition_gqa(AttnArgs a) {
 #pragma unroll
                 for (int t = 0; t < DT; ++t) acc[T][t] *= alpha;
                 l[T] *= alpha;
-                zacc[T] *= alpha;
                 m[T] = bmax;
             }
             uint32_t pw[4];
-            float psum = 0.f;   // sum of the fp16 weights the MFMA takes
             // a query that has seen no token yet (MULTI: all masked so far) keeps
             // m = -inf; its weights are 0, not exp2(-inf + inf)
             const float mref = MULTI && m[T] == -INFINITY ? 0.f : m[T];
@@ -926,17 +927,19 @@ void attn_partition_gqa(AttnArgs a) {
                 l[T] += p0 + p1;
                 const f16x2 h2 = f16x2{(_Float16)(p0 * sv), (_Float16)(p1 * sv)};
                 pw[e] = __builtin_bit_cast(uint32_t, h2);
-                psum = __builtin_amdgcn_fdot2(h2, f16x2{(_Float16)1, (_Float16)1}, psum, false);
             }
             pop[T] = __builtin_bit_cast(f16x8v, pw);
-            // the codes enter the MFMA as bias + u (exact fp16); the weighted
-            // bias and zero point, (bias + zp) times the weights' sum, are the
-            // same for every dim and come off once, at the end
-            if constexpr (VC != KV_CODEC_FP8_E4M3) zacc[T] = __builtin_fmaf(code_bias<VC>(zpv), psum, zacc[T]);
         }
 
         before_pv(r);
-        // ---- O^T += (bias + V codes)^T P^T (each converted V operand serves every tile)
+        // ---- O^T += (V codes - zero point)^T P^T (each converted V operand
+        // serves every tile).  v_perm gives bias + u; one packed fp16
+        // subtraction of bias + zp (both integers below 2048: exact) leaves
+        // u - zp, so no constant offset is carried through the accumulators
+        // and cancelled at the end (its weights' sum would have to match the
+        // matrix core's treatment of every fp16 weight, subnormals included).
+        const _Float16 nb = (_Float16)(-code_bias<VC>(zpv));
+        const f16x2 nb2 = f16x2{nb, nb};
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
             uint32_t a4[4];
@@ -952,6 +955,10 @@ void attn_partition_gqa(AttnArgs a) {
                 a4[1] = pair_hi<VC>(r.v[t][0]);
                 a4[2] = pair_lo<VC>(r.v[t][1]);
                 a4[3] = pair_hi<VC>(r.v[t][1]);
+            }
+            if constexpr (VC != KV_CODEC_FP8_E4M3) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a4[i] = __builtin_bit_cast(uint32_t, as_h2(a4[i]) + nb2);
             }
             const f16x8v vop = __builtin_bit_cast(f16x8v, a4);
 #pragma unroll
@@ -1267,17 +1274,14 @@ void attn_partition_gqa(AttnArgs a) {
         }
     }
     // lanes of one head split its tokens by group: sum their partial sums,
-    // take the weighted code bias off every dim, and undo the V-scale
-    // normaliser (times the codec's unit)
-    const float vback = __builtin_amdgcn_ldexpf(vunit, vF - 15);
+    // and undo the V-scale normaliser (times the codec's unit)
+    const float vback = __builtin_amdgcn_ldexpf(vunit, vF - 15 - kVTop);
 #pragma unroll
     for (int T = 0; T < TPW; ++T) {
         l[T] += shfl_xor_f(l[T], 16);
         l[T] += shfl_xor_f(l[T], 32);
-        zacc[T] += shfl_xor_f(zacc[T], 16);
-        zacc[T] += shfl_xor_f(zacc[T], 32);
 #pragma unroll
-        for (int t = 0; t < DT; ++t) acc[T][t] = (acc[T][t] - zacc[T]) * vback;
+        for (int t = 0; t < DT; ++t) acc[T][t] *= vback;
     }
 
     // Merge the waves' partial results in LDS (over the staging area, once

@@ -141,7 +141,21 @@ struct SwapArgs {
 // Bytes one swap work group moves (256 threads x 4 x 16 bytes).
 constexpr int64_t kSwapChunk = 256 * 4 * 16;
 
+// Plain streaming read of tiles (the measured ceiling of the decode's
+// access pattern): tiles of 2^tile_kib_log2 KiB, each wave a contiguous run
+// of tiles_per_wave list entries; one xor word per work group to sink.
+struct StreamReadArgs {
+    const uint8_t* src;
+    const int32_t* order;   // NULL: tile i of the list is source tile i
+    int64_t n_tiles;
+    int64_t tiles_per_wave;
+    int32_t tile_kib_log2;
+    uint32_t* sink;
+};
+
 hipError_t launch_quantize_store(const QuantStoreArgs& a, hipStream_t stream);
+hipError_t launch_stream_read(const StreamReadArgs& a, hipStream_t stream);
+int64_t stream_read_groups(int64_t n_tiles, int64_t tiles_per_wave);
 hipError_t launch_paged_attn(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_swap_blocks(const SwapArgs& a, hipStream_t stream);

@@ -376,3 +376,22 @@ def test_default_partition_policy(lib):
     p = L.paged_attn_default_partition(gqa, 128, 64, 1968)
     assert p == (1984 if 128 * 8 >= target else p) and p % 32 == 0
     assert lib.paged_attn_default_partition(None, 1, 1, 1) == 0
+
+
+def test_stream_read_validates_before_launch(lib):
+    """kv_stream_read_tiles checks tile size, sizes, pointers and the sink on
+    the host; zero tiles is a no-op."""
+    buf = ctypes.create_string_buffer(1 << 14)
+    base = (ctypes.addressof(buf) + 15) & ~15
+    f = lib.kv_stream_read_tiles
+    assert f(base, 4, 3000, None, 4, base, 1024, None) == L.KV_ERR_INVALID
+    assert "tile_bytes" in lib.kv_last_error().decode()
+    assert f(base, 4, 2048, None, 5, base, 1024, None) == L.KV_ERR_INVALID
+    assert "n_src_tiles" in lib.kv_last_error().decode()
+    assert f(base + 4, 4, 2048, None, 4, base, 1024, None) == L.KV_ERR_INVALID
+    assert f(base, 4, 2048, None, 4, None, 1024, None) == L.KV_ERR_INVALID
+    assert f(base, 4, 2048, None, 4, base, 0, None) == L.KV_ERR_INVALID
+    assert "sink" in lib.kv_last_error().decode()
+    assert f(base, 4, 2048, None, 0, base, 0, None) == L.KV_OK
+    assert lib.kv_stream_read_sink_words(0) == 0
+    assert lib.kv_stream_read_sink_words(1) >= 1

@@ -975,3 +975,25 @@ def test_multi_query_scaled_v(bs, g, vc, kind):
         case.pool.multi_query(qd, out, cud, max(ns), case.tables, case.ctx_dev, max(case.ctx), sm, part)
         torch.cuda.synchronize()
         assert_close(out.cpu().numpy() / sigma, ref / sigma, f"multi scaled V {kind} {vc} part{part}")
+
+
+# ---- the plain-read ceiling kernel -------------------------------------------
+
+@pytest.mark.parametrize("tile_bytes,n_src,n,ordered", [(2048, 3000, 3000, True), (4096, 700, 313, True),
+                                                      (1024, 5000, 4999, False), (2048, 64, 1, True)])
+def test_stream_read_reads_every_listed_tile(tile_bytes, n_src, n, ordered):
+    """kv_stream_read_tiles reads exactly the listed tiles: the xor of its
+    sink words equals the xor of every 32-bit word of those tiles."""
+    announce("stream-read", tile_bytes, n_src, n, ordered)
+    from paged_block_quantized_amd import _lib as L
+    rng = np.random.default_rng(tile_bytes + n)
+    src = rng.integers(0, 2 ** 32, n_src * tile_bytes // 4, dtype=np.uint32)
+    ids = rng.permutation(n_src)[:n].astype(np.int32) if ordered else np.arange(n, dtype=np.int32)
+    expect = np.bitwise_xor.reduce(src.reshape(n_src, -1)[ids].ravel())
+    src_d = torch.from_numpy(src.view(np.int32)).cuda()
+    order_d = torch.from_numpy(ids).cuda() if ordered else None
+    sink = torch.full((L.kv_stream_read_sink_words(n),), 0x55, dtype=torch.int32, device="cuda")
+    L.kv_stream_read_tiles(src_d, n_src, tile_bytes, order_d, n, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == expect
