@@ -24,8 +24,13 @@ __global__ __launch_bounds__(64 * kWaves) void stream_read_kernel(StreamReadArgs
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t wave = (int64_t)blockIdx.x * kWaves + w;
-    const int64_t t0 = wave * a.tiles_per_wave;
-    const int64_t t1 = min(t0 + a.tiles_per_wave, a.n_tiles);
+    const int64_t n_waves = (int64_t)gridDim.x * kWaves;
+    // a list: the wave's contiguous run of it.  No list: the k-th tile of
+    // the wave is tile wave + k n_waves, so that the waves together sweep
+    // memory front to back (the sequential read)
+    const int64_t t0 = a.order ? wave * a.tiles_per_wave : 0;
+    const int64_t t1 = a.order ? min(t0 + a.tiles_per_wave, a.n_tiles)
+                               : (wave < a.n_tiles ? (a.n_tiles - wave + n_waves - 1) / n_waves : 0);
     const int sh = a.tile_kib_log2;
     u32x4 acc = {0u, 0u, 0u, 0u};
     for (int64_t base = t0; base < t1; base += 64) {
@@ -38,7 +43,7 @@ __global__ __launch_bounds__(64 * kWaves) void stream_read_kernel(StreamReadArgs
             for (int k = 0; k < kInflight; ++k) {
                 const int cc = min(c + k, nch - 1);   // the last batch re-reads its final chunk
                 const int ti = cc >> sh;
-                const int64_t tile = a.order ? (int64_t)readlane(id, ti) : base + ti;
+                const int64_t tile = a.order ? (int64_t)readlane(id, ti) : wave + (base + ti) * n_waves;
                 v[k] = *(const u32x4*)(a.src + (((tile << sh) + (cc & ((1 << sh) - 1))) << 10) + 16 * lane);
             }
 #pragma unroll
