@@ -27,10 +27,16 @@ Readings
   [num_blocks, heads, head_dim, block_size / 2] bytes holding two consecutive
   tokens per byte (the earlier token in the low nibble), with a u8 zero point
   per (block, head).
-* Codecs by name: K "i8" (INT8 symmetric) or "fp8" (E4M3); V "i8", "i4"
-  (INT4 asymmetric), "i8a" (INT8 asymmetric, u8 codes) or "fp8".  FP8 and
-  INT8-asymmetric tiles are u8 arrays of the INT8 tiles' shape; the
-  asymmetric codecs keep their zero point in ``v_zp``.
+* Codecs by name: K "i8" (INT8 symmetric), "fp8" (E4M3) or "i4" (INT4
+  asymmetric); V "i8", "i4" (INT4 asymmetric), "i8a" (INT8 asymmetric, u8
+  codes) or "fp8".  FP8 and INT8-asymmetric tiles are u8 arrays of the INT8
+  tiles' shape; the asymmetric V codecs keep their zero point in ``v_zp``.
+* INT4 K (tbr8.org §3: blocks may be quantized to INT8 or even INT4;
+  yunthe.com "quantization principle": Q(x) with bits = 4): the same
+  per-(block, head) affine recipe as INT4 V, applied to the K tile; K tiles
+  stay token-major, so the two codes of a byte are consecutive head dims of
+  one token (the even dim in the low nibble): [num_blocks, heads,
+  block_size, head_dim / 2] bytes, with the zero point in ``k_zp``.
 """
 
 import numpy as np
@@ -49,10 +55,14 @@ class PoolArrays:
         self.head_dim = head_dim
         self.k_codec = k_codec
         self.v_codec = v_codec if v_codec is not None else ("i4" if v_int4 else "i8")
-        assert self.k_codec in ("i8", "fp8") and self.v_codec in ("i8", "i4", "i8a", "fp8")
+        assert self.k_codec in ("i8", "fp8", "i4") and self.v_codec in ("i8", "i4", "i8a", "fp8")
         self.v_int4 = self.v_codec == "i4"
-        self.k_codes = np.zeros((num_blocks, num_kv_heads, block_size, head_dim),
-                                np.int8 if k_codec == "i8" else np.uint8)
+        self.k_int4 = self.k_codec == "i4"
+        if self.k_int4:
+            self.k_codes = np.zeros((num_blocks, num_kv_heads, block_size, head_dim // 2), np.uint8)
+        else:
+            self.k_codes = np.zeros((num_blocks, num_kv_heads, block_size, head_dim),
+                                    np.int8 if k_codec == "i8" else np.uint8)
         if self.v_int4:
             self.v_codes = np.zeros((num_blocks, num_kv_heads, head_dim, block_size // 2), np.uint8)
         else:
@@ -61,6 +71,7 @@ class PoolArrays:
         self.k_scale = np.zeros((num_blocks, num_kv_heads), np.float16)
         self.v_scale = np.zeros((num_blocks, num_kv_heads), np.float16)
         self.v_zp = np.zeros((num_blocks, num_kv_heads), np.uint8)
+        self.k_zp = np.zeros((num_blocks, num_kv_heads), np.uint8)
 
 
 def quantize_tile(codec: str, x16):
@@ -99,10 +110,12 @@ def store_block(pool: PoolArrays, phys: int, k_rows, v_rows):
     n = k_rows.shape[0]
     assert 1 <= n <= pool.block_size
     for h in range(pool.num_kv_heads):
-        kc, ks, _ = quantize_tile(pool.k_codec, k_rows[:, h, :])
+        kc, ks, kz = quantize_tile(pool.k_codec, k_rows[:, h, :])
         pool.k_codes[phys, h] = 0
-        pool.k_codes[phys, h, :n] = kc
+        # INT4 K: two consecutive head dims of a token per byte
+        pool.k_codes[phys, h, :n] = quant.pack_int4(kc) if pool.k_int4 else kc
         pool.k_scale[phys, h] = ks
+        pool.k_zp[phys, h] = kz
         # V tile, dim-major: codes[d, t]; tokens >= n stay zero bytes
         vc, vs, vz = quantize_tile(pool.v_codec, v_rows[:, h, :])
         tile = np.zeros((pool.head_dim, pool.block_size), vc.dtype)
@@ -131,9 +144,13 @@ def gather_dequant(pool: PoolArrays, table, ctx: int):
     t = np.arange(ctx)
     phys = np.asarray(table, np.int64)[t // bs]
     row = t % bs
-    kc = pool.k_codes[phys, :, row, :]                            # [ctx, H, D]
+    kc = pool.k_codes[phys, :, row, :]                            # [ctx, H, D] (INT4: D / 2 bytes)
+    if pool.k_int4:
+        kc = quant.unpack_int4(kc)
     ks = pool.k_scale[phys, :]                                    # [ctx, H]
-    khat = np.stack([dequantize_tile(pool.k_codec, kc[:, h], ks[:, h][:, None], 0)
+    kz = pool.k_zp[phys, :]
+    khat = np.stack([dequantize_tile(pool.k_codec, kc[:, h], ks[:, h][:, None],
+                                     kz[:, h][:, None].astype(np.float64))
                      for h in range(pool.num_kv_heads)], axis=1)
     if pool.v_int4:
         tiles = quant.unpack_int4(pool.v_codes[phys])             # [ctx, H, D, bs]

@@ -54,6 +54,10 @@ bits = 8 and a free zero point for INT8 asymmetric):
   all codes 0.  x_hat = value(code) * scale.
 * INT8 asymmetric: the INT4 asymmetric recipe with 255 in place of 15, codes
   0..255 stored as u8, the zero point u8 beside them.
+
+INT4 K (tbr8.org §3: a block may go to INT8 or even INT4; yunthe.com Q(x)
+with bits = 4): K tiles use ``quantize_int4_asym`` unchanged; only their
+packing differs (paged.py: along head_dim, K tiles being token-major).
 """
 
 import numpy as np

@@ -26,7 +26,8 @@ def _fill(rng, ctx_lens, hkv, d, bs, n_blocks, v_int4, perm, k_codec="i8", v_cod
     return pool, tables, hist
 
 
-@pytest.mark.parametrize("kc,vc", [("i8", "i8"), ("i8", "i4"), ("i8", "i8a"), ("fp8", "fp8")])
+@pytest.mark.parametrize("kc,vc", [("i8", "i8"), ("i8", "i4"), ("i8", "i8a"), ("fp8", "fp8"),
+                                   ("i4", "i4"), ("i4", "i8")])
 def test_gather_equals_contiguous(kc, vc):
     rng = np.random.default_rng(0)
     ctx = [1, 17, 50, 100]
@@ -46,6 +47,55 @@ def test_gather_equals_contiguous(kc, vc):
                 if codes is not None:
                     assert np.array_equal(pool.v_codes[b, h][:, :n], codes.T)
                     assert not pool.v_codes[b, h][:, n:].any()
+
+
+def test_int4_k_tile_hand_example_and_layout():
+    """INT4 K: the hand-worked tile of tests/golden/quant_examples.json stored
+    through the pool -- codes packed along head_dim (two consecutive dims of
+    one token per byte, even dim low), scale and zero point -- rows past the
+    tile zero bytes, and gathered back as (code - zp) * scale."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "quant_examples.json")))["int4_k_tile"]
+    x = np.array(g["x"], np.float16)
+    k = x[:, None, :]
+    v = np.zeros_like(k)
+    pool = paged.PoolArrays(3, 1, 16, 4, k_codec="i4", v_codec="i8")
+    paged.store_block(pool, 2, k, v)
+    assert float(pool.k_scale[2, 0]) == g["scale"] and int(pool.k_zp[2, 0]) == g["zero_point"]
+    assert pool.k_codes.shape == (3, 1, 16, 2)
+    assert pool.k_codes[2, 0, :2].tolist() == g["bytes"]
+    assert not pool.k_codes[2, 0, 2:].any()
+    kh, _ = paged.gather_dequant(pool, [2], 2)
+    expect = (np.array(g["codes"], np.float64) - g["zero_point"]) * g["scale"]
+    assert np.array_equal(kh[0], expect)
+
+
+@pytest.mark.parametrize("kc,vc", [("i4", "i4"), ("i4", "i8")])
+def test_int4_k_permutation_invariance_and_append(kc, vc):
+    """INT4 K pools: outputs unchanged under a permuted pool, and one-token
+    appends from exact rows end with the bytes of one prefill."""
+    rng = np.random.default_rng(12)
+    ctx = [3, 40, 33]
+    q = rng.standard_normal((3, 4, 64)).astype(np.float16)
+    outs = []
+    for perm_seed in (10, 11):
+        r2 = np.random.default_rng(5)
+        pool, tables, _ = _fill(r2, ctx, 2, 64, 16, 16, False,
+                                np.random.default_rng(perm_seed).permutation(16), kc, vc)
+        outs.append(attention.paged_decode(pool, tables, ctx, q, 0.125))
+    assert np.array_equal(outs[0], outs[1])
+    k = rng.standard_normal((40, 2, 64)).astype(np.float16)
+    v = rng.standard_normal((40, 2, 64)).astype(np.float16)
+    pre = paged.PoolArrays(8, 2, 16, 64, k_codec=kc, v_codec=vc)
+    app = paged.PoolArrays(8, 2, 16, 64, k_codec=kc, v_codec=vc)
+    table = [4, 1, 6]
+    paged.store_range(pre, table, k, v, 0, 40)
+    paged.store_range(app, table, k, v, 0, 3)
+    for p in range(3, 40):
+        paged.store_range(app, table, k, v, p, p + 1)
+    for arr in ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "k_zp"):
+        assert np.array_equal(getattr(pre, arr), getattr(app, arr)), arr
 
 
 def test_rows_beyond_context_are_zero_and_ignored():
