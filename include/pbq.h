@@ -478,6 +478,27 @@ int32_t paged_attn_default_partition(const kv_pool_desc* desc,
                                      int32_t num_seqs, int32_t num_q_heads,
                                      int32_t max_context_len);
 
+/* paged_attn_decode_append without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * or harnesses that forbid hipMalloc).  The split-K partial results go to
+ * the library's own scratch: a device array of 64 MiB (67,108,864 bytes)
+ * per GPU, held from library load until the process ends.  A call whose
+ * workspace (paged_attn_workspace_bytes with the same arguments) exceeds it
+ * fails with KV_ERR_INVALID before any device work.  The call allocates
+ * nothing.  Its first call on a device looks up that device's scratch
+ * address (a HIP runtime query; KV_ERR_HIP if it fails).  Every call on one
+ * GPU shares that GPU's scratch: calls that overlap on one GPU (other
+ * streams, or other threads) race and must be ordered by the caller.
+ * Otherwise identical to paged_attn_decode_append (arguments, layouts,
+ * results bit for bit). */
+kv_status paged_attn_decode_append_noalloc(const kv_pool_desc* desc, const kv_pool_mem* mem,
+                                           const uint16_t* k_new_dev, const uint16_t* v_new_dev,
+                                           const int32_t* tail_slots_dev, const uint16_t* q_dev,
+                                           uint16_t* out_dev, int32_t num_seqs, int32_t num_q_heads,
+                                           const int32_t* block_tables_dev, int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens_dev, int32_t max_context_len,
+                                           float sm_scale, int32_t partition_size, void* stream);
+
 /* ---- Measurement: the plain-read ceiling of the decode's access pattern --
  * Reads n_tiles tiles of tile_bytes bytes (1024, 2048 or 4096) from src_dev
  * and computes nothing but an xor of them: tile i of the list is source tile

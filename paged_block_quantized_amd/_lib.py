@@ -68,7 +68,7 @@ EXPORTS = [
     "kv_batch_tables", "kv_pool_stats", "kv_pool_free_list", "kv_pool_set_swap_space",
     "kv_seq_swap_out", "kv_seq_swap_in", "kv_swap_blocks", "kv_copy_blocks",
     "kv_quantize_store", "paged_attn_workspace_bytes", "paged_attn_decode",
-    "paged_attn_decode_append", "paged_attn_decode_shared_prefix", "paged_attn_multi_query",
+    "paged_attn_decode_append", "paged_attn_decode_append_noalloc", "paged_attn_decode_shared_prefix", "paged_attn_multi_query",
     "paged_attn_multi_query_workspace_bytes",
     "paged_attn_default_partition", "kv_stream_read_sink_words", "kv_stream_read_tiles", "kv_last_error",
 ]
@@ -114,6 +114,8 @@ def lib():
             "paged_attn_decode_append": (st, [P(kv_pool_desc), P(kv_pool_mem), VP, VP, VP, VP, VP,
                                               I32, I32, VP, I32, VP, I32, ctypes.c_float, I32, VP,
                                               SZ, VP]),
+            "paged_attn_decode_append_noalloc": (st, [P(kv_pool_desc), P(kv_pool_mem), VP, VP, VP, VP, VP,
+                                                      I32, I32, VP, I32, VP, I32, ctypes.c_float, I32, VP]),
             "paged_attn_decode_shared_prefix": (st, [P(kv_pool_desc), P(kv_pool_mem), VP, VP, VP, VP,
                                                      VP, I32, I32, VP, I32, VP, I32, ctypes.c_float,
                                                      I32, I32, VP, SZ, VP]),
@@ -345,6 +347,17 @@ def paged_attn_decode_append(desc, mem, k_new, v_new, tail_slots, q, out, num_se
                                           int(max_context_len), float(sm_scale),
                                           int(partition_size), _ptr(workspace),
                                           int(workspace_bytes), _stream(stream)))
+
+
+def paged_attn_decode_append_noalloc(desc, mem, k_new, v_new, tail_slots, q, out, num_seqs, num_q_heads,
+                                     block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                                     sm_scale, partition_size=0, stream=None):
+    _check(lib().paged_attn_decode_append_noalloc(ctypes.byref(desc), ctypes.byref(mem), _ptr(k_new),
+                                                  _ptr(v_new), _ptr(tail_slots), _ptr(q), _ptr(out),
+                                                  int(num_seqs), int(num_q_heads), _ptr(block_tables),
+                                                  int(max_blocks_per_seq), _ptr(context_lens),
+                                                  int(max_context_len), float(sm_scale),
+                                                  int(partition_size), _stream(stream)))
 
 
 def paged_attn_decode_shared_prefix(desc, mem, k_new, v_new, tail_slots, q, out, num_seqs,

@@ -15,7 +15,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libpbq.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-HIP_SOURCES = ["quantize_store.hip", "paged_attn.hip", "copy_blocks.hip", "swap_blocks.hip", "stream_read.hip"]
+HIP_SOURCES = ["quantize_store.hip", "paged_attn.hip", "copy_blocks.hip", "swap_blocks.hip", "stream_read.hip", "scratch.hip"]
 CPP_SOURCES = ["capi.cpp", "pool.cpp"]
 
 # -packed-fp32-ops: no packed fp32 VALU instructions are generated.

@@ -156,13 +156,15 @@ struct AppendArgs {
     const int32_t* tail_slots;
 };
 
+// use_scratch: the workspace is the library's own scratch (workspace and
+// workspace_bytes are ignored), looked up only after every argument check.
 kv_status decode_impl(const kv_pool_desc* d, const kv_pool_mem* m, const AppendArgs* app,
                             const uint16_t* q, uint16_t* out, int32_t num_seqs,
                             int32_t num_q_heads, const int32_t* block_tables,
                             int32_t max_blocks_per_seq, const int32_t* context_lens,
                             int32_t max_context_len, float sm_scale,
                             int32_t partition_size, int32_t shared_tokens, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            size_t workspace_bytes, void* stream, bool use_scratch = false) {
     kv_status st = pbq::check_device_desc(d);
     if (st != KV_OK) return st;
     if ((st = pbq::check_mem(d, m, app != nullptr)) != KV_OK) return st;
@@ -207,6 +209,20 @@ kv_status decode_impl(const kv_pool_desc* d, const kv_pool_mem* m, const AppendA
             return fail(KV_ERR_INVALID, "too many queries per KV head for the shared-prefix launch");
     }
     const size_t need = paged_attn_workspace_bytes(d, num_seqs, num_q_heads, max_context_len, part);
+    if (use_scratch) {
+        if (need > pbq::kScratchBytes)
+            return fail(KV_ERR_INVALID, "the call needs " + std::to_string(need) +
+                                            " bytes of workspace, more than the library's scratch (" +
+                                            std::to_string(pbq::kScratchBytes) +
+                                            " bytes); use paged_attn_decode_append");
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (need > 0) {
+            st = pbq::hip_status(pbq::scratch_address(&workspace), "paged_attn_decode_append_noalloc scratch");
+            if (st != KV_OK) return st;
+            workspace_bytes = pbq::kScratchBytes;
+        }
+    }
     if (workspace_bytes < need) return fail(KV_ERR_INVALID, "workspace too small");
     if (need > 0 && (!workspace || !pbq::aligned16(workspace)))
         return fail(KV_ERR_INVALID, "workspace must be non-NULL and 16-byte aligned");
@@ -635,6 +651,19 @@ kv_status paged_attn_decode_append(const kv_pool_desc* d, const kv_pool_mem* m,
     return decode_impl(d, m, &app, q, out, num_seqs, num_q_heads, block_tables, max_blocks_per_seq,
                        context_lens, max_context_len, sm_scale, partition_size, 0, workspace, workspace_bytes,
                        stream);
+}
+
+kv_status paged_attn_decode_append_noalloc(const kv_pool_desc* d, const kv_pool_mem* m,
+                                           const uint16_t* k_new, const uint16_t* v_new,
+                                           const int32_t* tail_slots, const uint16_t* q, uint16_t* out,
+                                           int32_t num_seqs, int32_t num_q_heads,
+                                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, int32_t max_context_len,
+                                           float sm_scale, int32_t partition_size, void* stream) {
+    const AppendArgs app{k_new, v_new, tail_slots};
+    return decode_impl(d, m, &app, q, out, num_seqs, num_q_heads, block_tables, max_blocks_per_seq,
+                       context_lens, max_context_len, sm_scale, partition_size, 0, nullptr, 0, stream,
+                       /*use_scratch=*/true);
 }
 
 kv_status paged_attn_decode_shared_prefix(const kv_pool_desc* d, const kv_pool_mem* m,

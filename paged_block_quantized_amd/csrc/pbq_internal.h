@@ -153,6 +153,12 @@ struct StreamReadArgs {
     uint32_t* sink;
 };
 
+// The library's device scratch (scratch.hip): kScratchBytes per device for
+// the allocation-free decode; scratch_address gives the current device's
+// copy (looked up once per device).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+hipError_t scratch_address(void** out);
+
 hipError_t launch_quantize_store(const QuantStoreArgs& a, hipStream_t stream);
 hipError_t launch_stream_read(const StreamReadArgs& a, hipStream_t stream);
 int64_t stream_read_groups(int64_t n_tiles, int64_t tiles_per_wave);

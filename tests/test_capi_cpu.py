@@ -395,3 +395,25 @@ def test_stream_read_validates_before_launch(lib):
     assert f(base, 4, 2048, None, 0, base, 0, None) == L.KV_OK
     assert lib.kv_stream_read_sink_words(0) == 0
     assert lib.kv_stream_read_sink_words(1) >= 1
+
+
+def test_noalloc_validates_before_touching_the_device(lib):
+    """paged_attn_decode_append_noalloc checks its arguments, and that the
+    call's workspace fits the library's 64 MiB scratch, before it looks up
+    the scratch or launches anything; zero sequences is a no-op."""
+    desc = L.make_desc(8, 16, 2, 64)
+    buf = ctypes.create_string_buffer(1 << 16)
+    base = (ctypes.addressof(buf) + 15) & ~15
+    mem = L.kv_pool_mem(base, base, base, base, None, base, base)
+    f = L.paged_attn_decode_append_noalloc
+    with pytest.raises(L.PBQError, match="multiple of num_kv_heads"):
+        f(desc, mem, base, base, base, base, base, 1, 3, base, 4, base, 64, 0.1, 0, 0)
+    with pytest.raises(L.PBQError, match="k_new"):
+        f(desc, mem, None, base, base, base, base, 1, 2, base, 4, base, 64, 0.1, 0, 0)
+    with pytest.raises(L.PBQError, match="partition_size"):
+        f(desc, mem, base, base, base, base, base, 1, 2, base, 4, base, 64, 0.1, 24, 0)
+    # 4096 sequences x 2 heads x 256 partitions x (64 x 4 + 8) bytes > 64 MiB
+    assert L.paged_attn_workspace_bytes(desc, 4096, 2, 65536, 256) > 64 << 20
+    with pytest.raises(L.PBQError, match="scratch"):
+        f(desc, mem, base, base, base, base, base, 4096, 2, base, 4096, base, 65536, 0.1, 256, 0)
+    f(desc, mem, base, base, base, base, base, 0, 2, base, 4, base, 64, 0.1, 0, 0)
