@@ -640,6 +640,7 @@ def main():
         from paged_block_quantized_amd import KVPool
         n_tok = int(setup.ctx.max())
         hp = KVPool(setup.pool.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.v_codec,
+                    k_codec=W.k_codec_of(w),
                     max_seqs=4, device=None)
         ids = np.random.default_rng(0).integers(0, 32000, n_tok).astype(np.int32)
         hp.alloc_prefix(0, ids[:w.prefix])

@@ -55,9 +55,11 @@ typedef enum kv_status {
 
 /* Codecs, one per (block, head) tile of block_size x head_dim values.
  * Supported (k_codec, v_codec) pairs: (I8_SYM, I8_SYM), (I8_SYM, I4_ASYM),
- * (I8_SYM, I8_ASYM) and (FP8_E4M3, FP8_E4M3).
- * INT4 packing is along the tile's contiguous axis: tokens for V (see the
- * layout under kv_pool_sizes).
+ * (I8_SYM, I8_ASYM), (FP8_E4M3, FP8_E4M3), (I4_ASYM, I4_ASYM) and
+ * (I4_ASYM, I8_SYM).
+ * INT4 packing is along the tile's contiguous axis: tokens for V, head dims
+ * for K (see the layout under kv_pool_sizes).  INT4 K follows [tbr8] §3 (a
+ * block may go to INT8 or even INT4) with [yunthe] Q(x), bits = 4.
  *   KV_CODEC_I8_SYM : int8 codes in [-127, 127], fp16 scale = fp16(absmax/127)
  *                     over the rows the block holds; code = round-half-even
  *                     of the fp32 quotient x / scale, clamped.  This is
@@ -94,7 +96,7 @@ typedef struct kv_pool_desc {
     int32_t block_size;   /* tokens per block: 16 or 32 ([tbr8] §2) */
     int32_t num_kv_heads; /* Hkv >= 1 */
     int32_t head_dim;     /* D: 64 or 128 */
-    int32_t k_codec;      /* KV_CODEC_I8_SYM ([tbr8] §5: K in INT8) or FP8_E4M3 */
+    int32_t k_codec;      /* KV_CODEC_I8_SYM ([tbr8] §5: K in INT8), FP8_E4M3 or I4_ASYM */
     int32_t v_codec;      /* I8_SYM, I4_ASYM, I8_ASYM or FP8_E4M3 (pairs above) */
     int32_t max_seqs;     /* tail slots = most sequences alive at once, >= 1 */
 } kv_pool_desc;
@@ -102,6 +104,9 @@ typedef struct kv_pool_desc {
 /* Byte sizes of the device arrays of one pool (all row-major):
  *   k_codes  int8  [N, Hkv, bs, D]      token-major K tiles ([tbr8] §4;
  *                                        u8 E4M3 bytes for FP8_E4M3)
+ *            uint8 [N, Hkv, bs, D / 2]  (I4_ASYM K: two consecutive head
+ *                                        dims of a token per byte, the even
+ *                                        dim in the low nibble)
  *   v_codes  int8  [N, Hkv, D, bs]      (I8_SYM; u8 for I8_ASYM and FP8_E4M3)
  *                                        dim-major V tiles
  *            uint8 [N, Hkv, D, bs / 2]  (I4_ASYM, two consecutive tokens per
@@ -113,13 +118,14 @@ typedef struct kv_pool_desc {
  *   v_zp     uint8 [N, Hkv]  (0 bytes unless I4_ASYM or I8_ASYM)
  *   tail_k   fp16  [max_seqs, Hkv, bs, D]  exact rows of each sequence's
  *   tail_v   fp16  [max_seqs, Hkv, bs, D]  partially filled last block
+ *   k_zp     uint8 [N, Hkv]  (0 bytes unless K is I4_ASYM)
  * Every array must be 16-byte aligned. */
 typedef struct kv_pool_sizes {
-    size_t k_codes, v_codes, k_scale, v_scale, v_zp, tail_k, tail_v;
+    size_t k_codes, v_codes, k_scale, v_scale, v_zp, tail_k, tail_v, k_zp;
 } kv_pool_sizes;
 
-/* Device pointers to the arrays above (v_zp may be NULL when V has no zero
- * point). */
+/* Device pointers to the arrays above (v_zp and k_zp may be NULL when V,
+ * or K, has no zero point). */
 typedef struct kv_pool_mem {
     void* k_codes;
     void* v_codes;
@@ -128,6 +134,7 @@ typedef struct kv_pool_mem {
     void* v_zp;
     void* tail_k;
     void* tail_v;
+    void* k_zp;
 } kv_pool_mem;
 
 /* A copy the caller must perform on the device before writing new tokens

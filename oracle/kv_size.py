@@ -36,9 +36,10 @@ def kv_bytes_dense(num_layers: int, num_kv_heads: int, head_dim: int,
     return 2 * num_layers * per_tensor
 
 
-def meta_bytes_per_block_head(v_asymmetric: bool) -> int:
-    """fp16 K scale + fp16 V scale (+ one u8 zero point for asymmetric V)."""
-    return 2 + 2 + (1 if v_asymmetric else 0)
+def meta_bytes_per_block_head(v_asymmetric: bool, k_asymmetric: bool = False) -> int:
+    """fp16 K scale + fp16 V scale (+ one u8 zero point for asymmetric V, and
+    one for asymmetric K)."""
+    return 2 + 2 + (1 if v_asymmetric else 0) + (1 if k_asymmetric else 0)
 
 
 def kv_bytes_block_quantized(seq_len: int, batch: int, num_kv_heads: int,
@@ -57,10 +58,10 @@ def kv_bytes_block_quantized(seq_len: int, batch: int, num_kv_heads: int,
 
 
 def pool_block_bytes(num_kv_heads: int, head_dim: int, block_size: int,
-                     k_bits: int, v_bits: int, v_asymmetric: bool) -> int:
+                     k_bits: int, v_bits: int, v_asymmetric: bool, k_asymmetric: bool = False) -> int:
     """Bytes one physical pool block occupies over all KV heads."""
     codes = block_size * head_dim * (k_bits + v_bits) // 8
-    return num_kv_heads * (codes + meta_bytes_per_block_head(v_asymmetric))
+    return num_kv_heads * (codes + meta_bytes_per_block_head(v_asymmetric, k_asymmetric))
 
 
 def pool_num_blocks(budget_bytes: int, num_kv_heads: int, head_dim: int,

@@ -38,14 +38,15 @@ class kv_pool_desc(ctypes.Structure):
                 ("max_seqs", ctypes.c_int32)]
 
 
+POOL_ARRAYS = ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "tail_k", "tail_v", "k_zp")
+
+
 class kv_pool_sizes(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in
-                ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "tail_k", "tail_v")]
+    _fields_ = [(n, ctypes.c_size_t) for n in POOL_ARRAYS]
 
 
 class kv_pool_mem(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in
-                ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "tail_k", "tail_v")]
+    _fields_ = [(n, ctypes.c_void_p) for n in POOL_ARRAYS]
 
 
 class kv_copy(ctypes.Structure):

@@ -31,8 +31,8 @@ kv_status check_device_desc(const kv_pool_desc* d) {
         return fail(KV_ERR_INVALID, "num_kv_heads must be in [1, 65535]");
     if (d->max_seqs < 1) return fail(KV_ERR_INVALID, "max_seqs must be >= 1");
     if (!codec_pair_supported(d->k_codec, d->v_codec))
-        return fail(KV_ERR_INVALID, "unsupported (k_codec, v_codec): use (I8_SYM, I8_SYM | I4_ASYM | I8_ASYM) "
-                                    "or (FP8_E4M3, FP8_E4M3)");
+        return fail(KV_ERR_INVALID, "unsupported (k_codec, v_codec): use (I8_SYM, I8_SYM | I4_ASYM | I8_ASYM), "
+                                    "(FP8_E4M3, FP8_E4M3) or (I4_ASYM, I4_ASYM | I8_SYM)");
     return KV_OK;
 }
 
@@ -43,6 +43,8 @@ kv_status check_mem(const kv_pool_desc* d, const kv_pool_mem* m, bool need_tail)
         if (!p || !aligned16(p)) return fail(KV_ERR_INVALID, "pool arrays must be non-NULL and 16-byte aligned");
     if (codec_has_zp(d->v_codec) && (!m->v_zp || !aligned16(m->v_zp)))
         return fail(KV_ERR_INVALID, "v_zp must be non-NULL and 16-byte aligned for an asymmetric V codec");
+    if (codec_has_zp(d->k_codec) && (!m->k_zp || !aligned16(m->k_zp)))
+        return fail(KV_ERR_INVALID, "k_zp must be non-NULL and 16-byte aligned for an asymmetric K codec");
     if (need_tail && (!m->tail_k || !m->tail_v || !aligned16(m->tail_k) || !aligned16(m->tail_v)))
         return fail(KV_ERR_INVALID, "tail slots must be non-NULL and 16-byte aligned");
     return KV_OK;
@@ -78,7 +80,7 @@ kv_status check_swap_plan(const kv_pool_desc* d, const kv_pool_desc* h, const kv
                           int32_t n, bool* has_slots, int64_t* max_bytes) {
     const int64_t tile = (int64_t)d->block_size * d->head_dim;
     const int64_t kb = tile * d->num_kv_heads;
-    const int64_t block_bytes = kb + (codec_packed4(d->v_codec) ? kb / 2 : kb);
+    const int64_t block_bytes = (codec_packed4(d->k_codec) ? kb / 2 : kb) + (codec_packed4(d->v_codec) ? kb / 2 : kb);
     // spaces: device blocks, host blocks, device slots, host slots
     const int32_t size[4] = {d->num_blocks, h->num_blocks, d->max_seqs, h->max_seqs};
     std::vector<uint8_t> mark[4];
@@ -237,6 +239,7 @@ kv_status decode_impl(const kv_pool_desc* d, const kv_pool_mem* m, const AppendA
     a.k_scale = (const uint16_t*)m->k_scale;
     a.v_scale = (const uint16_t*)m->v_scale;
     a.v_zp = (const uint8_t*)m->v_zp;
+    a.k_zp = (const uint8_t*)m->k_zp;
     a.q = q;
     a.out = out;
     a.num_seqs = num_seqs;
@@ -267,6 +270,7 @@ kv_status decode_impl(const kv_pool_desc* d, const kv_pool_mem* m, const AppendA
         sa.k_scale = (uint16_t*)m->k_scale;
         sa.v_scale = (uint16_t*)m->v_scale;
         sa.v_zp = (uint8_t*)m->v_zp;
+        sa.k_zp = (uint8_t*)m->k_zp;
         sa.tail_k = (uint16_t*)m->tail_k;
         sa.tail_v = (uint16_t*)m->tail_v;
         sa.k = app->k_new;
@@ -301,11 +305,12 @@ kv_status kv_pool_bytes(const kv_pool_desc* d, kv_pool_sizes* out) {
     if (st != KV_OK) return st;
     const size_t tile = (size_t)d->block_size * d->head_dim;
     const size_t bh = (size_t)d->num_blocks * d->num_kv_heads;
-    out->k_codes = bh * tile;
+    out->k_codes = pbq::codec_packed4(d->k_codec) ? bh * tile / 2 : bh * tile;
     out->v_codes = pbq::codec_packed4(d->v_codec) ? bh * tile / 2 : bh * tile;
     out->k_scale = bh * 2;
     out->v_scale = bh * 2;
     out->v_zp = pbq::codec_has_zp(d->v_codec) ? bh : 0;
+    out->k_zp = pbq::codec_has_zp(d->k_codec) ? bh : 0;
     out->tail_k = (size_t)d->max_seqs * d->num_kv_heads * tile * 2;
     out->tail_v = out->tail_k;
     return KV_OK;
@@ -330,6 +335,7 @@ kv_status kv_copy_blocks(const kv_pool_desc* d, const kv_pool_mem* m,
     a.k_scale = (uint16_t*)m->k_scale;
     a.v_scale = (uint16_t*)m->v_scale;
     a.v_zp = (uint8_t*)m->v_zp;
+    a.k_zp = (uint8_t*)m->k_zp;
     a.tail_k = (uint16_t*)m->tail_k;
     a.tail_v = (uint16_t*)m->tail_v;
     a.copies = copies_dev;
@@ -372,13 +378,15 @@ kv_status kv_swap_blocks(const kv_pool_desc* d, const kv_pool_mem* m, const kv_p
         {hm->k_scale, hs.k_scale, (char**)&a.host.k_scale, "host k_scale"},
         {hm->v_scale, hs.v_scale, (char**)&a.host.v_scale, "host v_scale"},
         {hm->v_zp, hs.v_zp, (char**)&a.host.v_zp, "host v_zp"},
+        {hm->k_zp, hs.k_zp, (char**)&a.host.k_zp, "host k_zp"},
         {has_slots ? hm->tail_k : nullptr, hs.tail_k, &a.host.tail_k, "host tail_k"},
         {has_slots ? hm->tail_v : nullptr, hs.tail_v, &a.host.tail_v, "host tail_v"},
     };
     for (auto& e : host)
         if (e.p && e.bytes && (st = pbq::pinned_device_ptr(e.p, e.bytes, e.name, e.out)) != KV_OK) return st;
     a.dev = pbq::SwapSide{(char*)m->k_codes, (char*)m->v_codes, (uint16_t*)m->k_scale,
-                          (uint16_t*)m->v_scale, (uint8_t*)m->v_zp, (char*)m->tail_k, (char*)m->tail_v};
+                          (uint16_t*)m->v_scale, (uint8_t*)m->v_zp, (uint8_t*)m->k_zp, (char*)m->tail_k,
+                          (char*)m->tail_v};
     a.n = n;
     a.block_size = d->block_size;
     a.num_kv_heads = d->num_kv_heads;
@@ -421,6 +429,7 @@ kv_status kv_quantize_store(const kv_pool_desc* d, const kv_pool_mem* m,
     a.k_scale = (uint16_t*)m->k_scale;
     a.v_scale = (uint16_t*)m->v_scale;
     a.v_zp = (uint8_t*)m->v_zp;
+    a.k_zp = (uint8_t*)m->k_zp;
     a.tail_k = (uint16_t*)m->tail_k;
     a.tail_v = (uint16_t*)m->tail_v;
     a.k = k;
@@ -553,6 +562,7 @@ kv_status paged_attn_multi_query(const kv_pool_desc* d, const kv_pool_mem* m, co
     a.k_scale = (const uint16_t*)m->k_scale;
     a.v_scale = (const uint16_t*)m->v_scale;
     a.v_zp = (const uint8_t*)m->v_zp;
+    a.k_zp = (const uint8_t*)m->k_zp;
     a.q = q;
     a.out = out;
     a.num_seqs = num_seqs;

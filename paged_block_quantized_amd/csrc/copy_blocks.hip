@@ -3,7 +3,7 @@
 // deepinsea.top "PagedAttention memory management in depth", "Copy-on-Write":
 // sequences share prefix blocks and only the block about to be modified is
 // copied.  A block copy moves a physical block's codes (all heads; they are
-// contiguous in the [N, Hkv, bs, D] layout), scales and zero points; a slot
+// contiguous in the pool layout), scales and zero points; a slot
 // copy moves a sequence's fp16 tail rows (K and V).
 //
 // One workgroup per copy, 16-byte accesses for the bulk data.
@@ -26,15 +26,18 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyArgs a) {
     const int H = a.num_kv_heads;
     const int64_t tile = (int64_t)a.block_size * a.head_dim;
     const bool v4 = codec_packed4(a.v_codec), zp = codec_has_zp(a.v_codec);
+    const bool k4 = codec_packed4(a.k_codec), kzp = codec_has_zp(a.k_codec);
     if (c.kind == KV_COPY_BLOCK) {
-        const int64_t kb = tile * H;
-        const int64_t vb = v4 ? kb / 2 : kb;
+        const int64_t codes = tile * H;
+        const int64_t kb = k4 ? codes / 2 : codes;
+        const int64_t vb = v4 ? codes / 2 : codes;
         copy16(a.k_codes + c.src * kb, a.k_codes + c.dst * kb, kb, tid, blockDim.x);
         copy16(a.v_codes + c.src * vb, a.v_codes + c.dst * vb, vb, tid, blockDim.x);
         for (int g = tid; g < H; g += blockDim.x) {
             a.k_scale[(int64_t)c.dst * H + g] = a.k_scale[(int64_t)c.src * H + g];
             a.v_scale[(int64_t)c.dst * H + g] = a.v_scale[(int64_t)c.src * H + g];
             if (zp) a.v_zp[(int64_t)c.dst * H + g] = a.v_zp[(int64_t)c.src * H + g];
+            if (kzp) a.k_zp[(int64_t)c.dst * H + g] = a.k_zp[(int64_t)c.src * H + g];
         }
     } else if (c.kind == KV_COPY_SLOT) {
         const int64_t sb = tile * H * 2;

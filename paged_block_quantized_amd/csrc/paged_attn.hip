@@ -106,6 +106,14 @@ __device__ __forceinline__ float code_bias(float zp) {
     else return kI4Bias + zp;   // INT4 nibbles and INT8 asymmetric bytes: 1024 + u
 }
 
+// The pool arrays and new rows the fused store of a decode call writes.
+__device__ __forceinline__ TileStoreArgs fused_store_args(const AttnArgs& a) {
+    return TileStoreArgs{const_cast<int8_t*>(a.k_codes), const_cast<uint8_t*>(a.v_codes),
+                         const_cast<uint16_t*>(a.k_scale), const_cast<uint16_t*>(a.v_scale),
+                         const_cast<uint8_t*>(a.v_zp), const_cast<uint8_t*>(a.k_zp), a.tail_k, a.tail_v,
+                         a.k_new, a.v_new, a.num_kv_heads};
+}
+
 #ifndef PBQ_MHA_WAVES_PER_EU
 #define PBQ_MHA_WAVES_PER_EU 1
 #endif
@@ -195,17 +203,22 @@ void attn_partition_mha(AttnArgs a) {
     constexpr int KC = CP / 4, VC = CP % 4;
     constexpr bool V4 = codec_packed4(VC);
     constexpr bool VZP = codec_has_zp(VC);
+    constexpr bool K4 = codec_packed4(KC);   // INT4 K: two head dims per byte
+    constexpr bool KZP = codec_has_zp(KC);
     constexpr int LPR = D / 16;    // K: lanes per token row (16 dims each)
     constexpr int RPI = 64 / LPR;  // K: token rows per wave access
     constexpr int NR = BS / RPI;   // K: rows per lane per block
-    constexpr int KT = BS * D;     // K tile bytes
+    constexpr int KB = K4 ? 8 : 16;          // K bytes per lane and row (16 dims)
+    constexpr int KACC = 64 * KB;            // K bytes per wave access
+    constexpr int KT = BS * D * KB / 16;     // K tile bytes
     constexpr int DPL = D / 64;    // V: dims per lane
     constexpr int VROW = V4 ? BS / 2 : BS;  // V: bytes per dim row
     constexpr int VT = D * VROW;   // V tile bytes
     constexpr int VW = VROW / 4;   // V: dwords per dim row
 
+    using KReg = std::conditional_t<K4, u32x2, u32x4>;
     struct Regs {
-        u32x4 k[NR];
+        KReg k[NR];
         uint32_t v[DPL][VW];
     };
 
@@ -236,9 +249,7 @@ void attn_partition_mha(AttnArgs a) {
     __shared__ uint32_t s_tscale[5];
     const bool fused = FUSED && p == nparts - 1 && nblk > 0;   // uniform in the group
     if (fused && w < 2) {
-        const TileStoreArgs t{const_cast<int8_t*>(a.k_codes), const_cast<uint8_t*>(a.v_codes),
-                              const_cast<uint16_t*>(a.k_scale), const_cast<uint16_t*>(a.v_scale),
-                              const_cast<uint8_t*>(a.v_zp), a.tail_k, a.tail_v, a.k_new, a.v_new, H};
+        const TileStoreArgs t = fused_store_args(a);
         const int last = nblk - 1;
         const int slot = a.tail_slots[s], phys = tab[last];
         if (w == 0) {
@@ -260,21 +271,31 @@ void attn_partition_mha(AttnArgs a) {
     }
 
     const int dl = (lane % LPR) * 16;
+    // the lane's 16 query dims as fp16 pairs in the order the K codes come
+    // out of a dword: byte codes give dims (4k, 4k+1), (4k+2, 4k+3); INT4
+    // nibbles of dims 8c .. 8c+7 give (0, 2), (4, 6), (1, 3), (5, 7)
     f16x2 q2[8];
-    float qbias;
+    float qs = 0.f;   // sum of the lane's query dims: the K code offset's weight
     {
         const f16x8* qp = (const f16x8*)(a.q + ((int64_t)s * a.num_q_heads + h) * D + dl);
         const f16x8 q0 = qp[0], q1 = qp[1];
-        float qs = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            q2[e] = f16x2{q0[2 * e], q0[2 * e + 1]};
-            q2[4 + e] = f16x2{q1[2 * e], q1[2 * e + 1]};
+        for (int c = 0; c < 2; ++c) {
+            const f16x8 x = c ? q1 : q0;
+            if constexpr (K4) {
+                q2[4 * c + 0] = f16x2{x[0], x[2]};
+                q2[4 * c + 1] = f16x2{x[4], x[6]};
+                q2[4 * c + 2] = f16x2{x[1], x[3]};
+                q2[4 * c + 3] = f16x2{x[5], x[7]};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) q2[4 * c + e] = f16x2{x[2 * e], x[2 * e + 1]};
+            }
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) qs += (float)q0[e] + (float)q1[e];
-        qbias = code_bias<KC>(0.f) * qs;
     }
+    const float qbias = code_bias<KC>(0.f) * qs;   // the K offset's share (INT4 K: per block)
 
     const float c2 = a.sm_scale * kLog2e * code_unit<KC>();
     constexpr float vunit = code_unit<VC>();
@@ -286,17 +307,30 @@ void attn_partition_mha(AttnArgs a) {
     const int row_lane = lane / LPR;
 
     // One block's contribution: scores, online softmax update, weighted V.
-    auto compute_blk = [&](const Regs& r, int blk, float skc, float svv, float vbias) {
+    // kzp: the block's K zero point (INT4 K; unused otherwise).
+    auto compute_blk = [&](const Regs& r, int blk, float skc, float svv, float vbias, float kzp) {
         float sc[NR];
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
             float d = 0.f;
+            if constexpr (K4) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                d = __builtin_amdgcn_fdot2(as_h2(pair_lo<KC>(r.k[j][k])), q2[2 * k], d, false);
-                d = __builtin_amdgcn_fdot2(as_h2(pair_hi<KC>(r.k[j][k])), q2[2 * k + 1], d, false);
+                for (int c = 0; c < 2; ++c) {   // dims 8c .. 8c+7 of the lane's 16
+                    const uint32_t lo = r.k[j][c] & 0x0F0F0F0Fu, hi = (r.k[j][c] >> 4) & 0x0F0F0F0Fu;
+                    d = __builtin_amdgcn_fdot2(perm_lo(lo), q2[4 * c + 0], d, false);
+                    d = __builtin_amdgcn_fdot2(perm_hi(lo), q2[4 * c + 1], d, false);
+                    d = __builtin_amdgcn_fdot2(perm_lo(hi), q2[4 * c + 2], d, false);
+                    d = __builtin_amdgcn_fdot2(perm_hi(hi), q2[4 * c + 3], d, false);
+                }
+                sc[j] = d - code_bias<KC>(kzp) * qs;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    d = __builtin_amdgcn_fdot2(as_h2(pair_lo<KC>(r.k[j][k])), q2[2 * k], d, false);
+                    d = __builtin_amdgcn_fdot2(as_h2(pair_hi<KC>(r.k[j][k])), q2[2 * k + 1], d, false);
+                }
+                sc[j] = d - qbias;
             }
-            sc[j] = d - qbias;
         }
 #pragma unroll
         for (int j = 0; j < NR; ++j) sc[j] = group_sum<LPR>(sc[j]);
@@ -368,9 +402,9 @@ void attn_partition_mha(AttnArgs a) {
     // Codes of one (block, head) tile: K from kp (the tile's first byte), V
     // from vp; either may point into the pool or into the LDS copy of a tile.
     auto load_tile = [&](const int8_t* kp, const uint8_t* vp, Regs& r) {
-        kp += lane * 16;
+        kp += lane * KB;
 #pragma unroll
-        for (int j = 0; j < NR; ++j) r.k[j] = *(const u32x4*)(kp + j * 1024);
+        for (int j = 0; j < NR; ++j) r.k[j] = *(const KReg*)(kp + j * KACC);
 #pragma unroll
         for (int k = 0; k < DPL; ++k) {
             const uint8_t* row = vp + (lane + 64 * k) * VROW;
@@ -410,7 +444,7 @@ void attn_partition_mha(AttnArgs a) {
         // raw fp16 scale bits and zero point, converted where they are used
         // (any arithmetic here would make the first step's wait cover the
         // prefetched codes too)
-        int sk = 0, sv = 0, zp = 0;
+        int sk = 0, sv = 0, zp = 0, kz = 0;
 
         auto load = [&](int i, Regs& r) {
             const int64_t t = (int64_t)readlane(id, i) * H + h;
@@ -420,7 +454,7 @@ void attn_partition_mha(AttnArgs a) {
         auto compute = [&](const Regs& r, int i) {
             compute_blk(r, base + i, bits_to_f16f((uint16_t)readlane(sk, i)) * c2,
                         bits_to_f16f((uint16_t)readlane(sv, i)) * vunit,
-                        code_bias<VC>((float)readlane(zp, i)));
+                        code_bias<VC>((float)readlane(zp, i)), (float)readlane(kz, i));
         };
 
         // scale bits of the staged blocks, issued after the first codes; only
@@ -431,15 +465,14 @@ void attn_partition_mha(AttnArgs a) {
             sk = a.k_scale[t];
             sv = a.v_scale[t];
             if constexpr (VZP) zp = a.v_zp[t];
+            if constexpr (KZP) kz = a.k_zp[t];
         };
         pipelined<PBQ_MHA_DEPTH, Regs>(cnt, load, compute, scales);
     }
     if (FUSED && fused) {
         __syncthreads();   // waves 0 and 1 have left the tiles in LDS
         if (w < 2) {
-            const TileStoreArgs t{const_cast<int8_t*>(a.k_codes), const_cast<uint8_t*>(a.v_codes),
-                                  const_cast<uint16_t*>(a.k_scale), const_cast<uint16_t*>(a.v_scale),
-                                  const_cast<uint8_t*>(a.v_zp), a.tail_k, a.tail_v, a.k_new, a.v_new, H};
+            const TileStoreArgs t = fused_store_args(a);
             write_stored_tile<BS, D, CP>(t, w, h, a.tail_slots[s], s, ctx - 1, tab[nblk - 1], s_tile, s_tile + KT,
                                          s_tscale);
         }
@@ -447,7 +480,8 @@ void attn_partition_mha(AttnArgs a) {
             Regs r;
             load_tile((const int8_t*)s_tile, s_tile + KT, r);
             compute_blk(r, b_end, bits_to_f16f((uint16_t)s_tscale[0]) * c2,
-                        bits_to_f16f((uint16_t)s_tscale[1]) * vunit, code_bias<VC>((float)s_tscale[2]));
+                        bits_to_f16f((uint16_t)s_tscale[1]) * vunit, code_bias<VC>((float)s_tscale[2]),
+                        (float)(s_tscale[0] >> 16));
         }
     }
 
@@ -652,6 +686,8 @@ void attn_partition_gqa(AttnArgs a) {
     constexpr int KC = CP / 4, VC = CP % 4;
     constexpr bool V4 = codec_packed4(VC);
     constexpr bool VZP = codec_has_zp(VC);
+    constexpr bool K4 = codec_packed4(KC);   // INT4 K: two head dims per byte
+    constexpr bool KZP = codec_has_zp(KC);
     static_assert(!(FUSED && SHARED), "the shared prefix holds no current token");
     static_assert(!(MULTI && (FUSED || SHARED)), "multi-query launches store nothing and share nothing");
     static_assert(BS == 16 || BS == 32, "block size");
@@ -659,16 +695,22 @@ void attn_partition_gqa(AttnArgs a) {
     constexpr int QT = 16 * TPW;               // queries per wave
     // JOINT: both waves stream every step of the partition from one staging
     // area, wave w for queries w QT .. of the group (no merge of waves)
-    constexpr bool JOINT = MULTI && NW == 2 && TPW == 2 && PBQ_MULTI_JOINT_STAGE;
+    // (INT4 K rows are not staged: their codes stay on the register path)
+    constexpr bool JOINT = MULTI && NW == 2 && TPW == 2 && PBQ_MULTI_JOINT_STAGE && !K4;
     constexpr int QW = JOINT ? NW * QT : QT;   // queries per work group
-    constexpr bool STAGED = FUSED ? PBQ_GQA_STAGE_FUSED : (JOINT ? true : (MULTI && !V4 ? PBQ_MULTI_BYTEV_STAGE : PBQ_GQA_STAGE));
+    constexpr bool STAGED = K4 ? false
+                          : FUSED ? PBQ_GQA_STAGE_FUSED
+                          : (JOINT ? true : (MULTI && !V4 ? PBQ_MULTI_BYTEV_STAGE : PBQ_GQA_STAGE));
     constexpr int KS = D / 32;                 // QK k-steps
     constexpr int DT = D / 16;                 // PV dim tiles
-    constexpr int KCH = D / 4;                 // K bytes per lane per row
+    constexpr int KROW = K4 ? D / 2 : D;       // K bytes per token row
+    constexpr int KCH = KROW / 4;              // K bytes per lane per row
+    constexpr int NKC = KCH >= 16 ? KCH / 16 : 1;   // their 16-byte chunks (INT4 K, D 64: one of 8 bytes)
+    using KChunk = std::conditional_t<(KCH >= 16), u32x4, u32x2>;
     constexpr int BPS = 32 / BS;               // blocks per 32-token step
     constexpr int SPB = 64 / BPS;              // steps whose block ids one wave stages at once
     constexpr int VROW = V4 ? BS / 2 : BS;     // V bytes per dim row
-    constexpr int KT = BS * D;
+    constexpr int KT = BS * KROW;
     constexpr int VT = D * VROW;
 
     const int lane = threadIdx.x & 63;
@@ -741,28 +783,33 @@ void attn_partition_gqa(AttnArgs a) {
     const int blk0 = tok0 / BS;
     const int blk_end = (tok1 + BS - 1) / BS;
 
-    // Q as the B operand of the QK product.  The contraction index of k-step
-    // j, lane group grp, element i is head dim 64 (j/2) + 16 grp + 8 (j%2) + i,
-    // so that a lane's K codes for two k-steps are 16 contiguous bytes and
-    // the four lane groups of one row read 64 contiguous bytes.
+    // Q as the B operand of the QK product.  Byte-coded K: the contraction
+    // index of k-step j, lane group grp, element i is head dim 64 (j/2) +
+    // 16 grp + 8 (j%2) + i, so that a lane's K codes for two k-steps are 16
+    // contiguous bytes and the four lane groups of one row read 64
+    // contiguous bytes.  INT4 K: lane group grp holds the row's dims
+    // 2 KCH grp .. + 2 KCH - 1 (KCH contiguous bytes), k-step j its dword j,
+    // whose nibbles come out as dims 8j + (0, 2, 4, 6, 1, 3, 5, 7).
     f16x8v qop[TPW][KS];
-    float qbias[TPW];
+    float qsum[TPW], qbias[TPW];
 #pragma unroll
     for (int T = 0; T < TPW; ++T) {
         float qs = 0.f;
         const bool live = 16 * T + n16 < nheads;
-        const uint16_t* qp = a.q + query_row(live ? 16 * T + n16 : 0) * D + 16 * grp;
+        const uint16_t* qp = a.q + query_row(live ? 16 * T + n16 : 0) * D + (K4 ? 2 * KCH : 16) * grp;
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
             f16x8v x = (f16x8v)(_Float16)0;
-            if (live) x = *(const f16x8v*)(qp + 64 * (j / 2) + 8 * (j % 2));
-            qop[T][j] = x;
+            if (live) x = *(const f16x8v*)(qp + (K4 ? 8 * j : 64 * (j / 2) + 8 * (j % 2)));
+            if constexpr (K4) qop[T][j] = __builtin_shufflevector(x, x, 0, 2, 4, 6, 1, 3, 5, 7);
+            else qop[T][j] = x;
 #pragma unroll
             for (int i = 0; i < 8; ++i) qs += (float)x[i];
         }
         qs += shfl_xor_f(qs, 16);
         qs += shfl_xor_f(qs, 32);
-        qbias[T] = code_bias<KC>(0.f) * qs;
+        qsum[T] = qs;
+        qbias[T] = code_bias<KC>(0.f) * qs;   // INT4 K: per block, from its zero point
     }
 
     const float c2 = a.sm_scale * kLog2e * code_unit<KC>();
@@ -822,7 +869,7 @@ void attn_partition_gqa(AttnArgs a) {
 
     using VReg = std::conditional_t<V4, uint32_t, u32x2>;   // a lane's V codes of one dim tile
     struct Raw {
-        u32x4 k[2][KCH / 16];
+        KChunk k[2][NKC];
         VReg v[DT];
     };
 
@@ -832,9 +879,9 @@ void attn_partition_gqa(AttnArgs a) {
     auto load_step = [&](const int8_t* k0, const int8_t* k1, const uint8_t* v0, const uint8_t* v1, Raw& r) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-            const int8_t* kp = (BPS == 1 || !kblk[mt] ? k0 : k1) + krow[mt] * D + 16 * grp;
+            const int8_t* kp = (BPS == 1 || !kblk[mt] ? k0 : k1) + krow[mt] * KROW + (K4 ? KCH : 16) * grp;
 #pragma unroll
-            for (int c = 0; c < KCH / 16; ++c) r.k[mt][c] = *(const u32x4*)(kp + 64 * c);
+            for (int c = 0; c < NKC; ++c) r.k[mt][c] = *(const KChunk*)(kp + 64 * c);
         }
         const uint8_t* vp = (BPS == 1 || !my_blk ? v0 : v1) + vcol;
 #pragma unroll
@@ -845,7 +892,8 @@ void attn_partition_gqa(AttnArgs a) {
 
     // One step: scores on MFMA, online softmax, PV on MFMA.  sk, sv, zpv are
     // this lane's block's scales (sk times sm_scale log2 e, sv times the
-    // V-scale normaliser 2^(15 - vF)) and zero point.
+    // V-scale normaliser 2^(15 - vF)) and V zero point, kzv its K zero
+    // point (INT4 K).
     // MULTI's lazy rescale threshold (base 2): the fp16 weights p sv 2^(15 +
     // kVTop - vF) stay below 2^(kLazy + kVTop + 1) = 2^15 (the normalised
     // scale is below 2^(kVTop + 1)), inside fp16's finite range for every
@@ -853,7 +901,7 @@ void attn_partition_gqa(AttnArgs a) {
     constexpr float kLazy = MULTI ? 8.f : 0.f;
     // before_pv(r) runs after the softmax, before the V operands are used
     // (the shared-staging path reads them from LDS only then).
-    auto compute_step = [&](Raw& r, int st, float sk, float sv, float zpv, auto&& before_pv) {
+    auto compute_step = [&](Raw& r, int st, float sk, float sv, float zpv, float kzv, auto&& before_pv) {
         // ---- S^T = K_hat Q^T (each converted K operand serves every tile) --
         f32x4 sc[TPW][2];
 #pragma unroll
@@ -862,9 +910,22 @@ void attn_partition_gqa(AttnArgs a) {
             for (int T = 0; T < TPW; ++T) sc[T][mt] = (f32x4)0.f;
 #pragma unroll
             for (int j = 0; j < KS; ++j) {
-                const uint32_t w0 = r.k[mt][j / 2][2 * (j & 1)];
-                const uint32_t w1 = r.k[mt][j / 2][2 * (j & 1) + 1];
-                const uint32_t a4[4] = {pair_lo<KC>(w0), pair_hi<KC>(w0), pair_lo<KC>(w1), pair_hi<KC>(w1)};
+                uint32_t a4[4];
+                if constexpr (K4) {   // dword j: dims 8j + (0, 2, 4, 6 | 1, 3, 5, 7)
+                    const uint32_t w = r.k[mt][0][j];
+                    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+                    a4[0] = __builtin_amdgcn_perm(kF16Hi, lo, kSelLo);
+                    a4[1] = __builtin_amdgcn_perm(kF16Hi, lo, kSelHi);
+                    a4[2] = __builtin_amdgcn_perm(kF16Hi, hi, kSelLo);
+                    a4[3] = __builtin_amdgcn_perm(kF16Hi, hi, kSelHi);
+                } else {
+                    const uint32_t w0 = r.k[mt][j / 2][2 * (j & 1)];
+                    const uint32_t w1 = r.k[mt][j / 2][2 * (j & 1) + 1];
+                    a4[0] = pair_lo<KC>(w0);
+                    a4[1] = pair_hi<KC>(w0);
+                    a4[2] = pair_lo<KC>(w1);
+                    a4[3] = pair_hi<KC>(w1);
+                }
                 const f16x8v aop = __builtin_bit_cast(f16x8v, a4);
 #pragma unroll
                 for (int T = 0; T < TPW; ++T)
@@ -877,7 +938,7 @@ void attn_partition_gqa(AttnArgs a) {
             // lane (head n16, group grp): sc[T][mt][i] is token 8 grp + kappa(4 mt + i)
             // (sc - qbias) sk as one rounding of sc sk plus the product -qbias sk
             float x[8];
-            const float nb = -qbias[T] * sk;
+            const float nb = -(K4 ? code_bias<KC>(kzv) * qsum[T] : qbias[T]) * sk;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -977,9 +1038,7 @@ void attn_partition_gqa(AttnArgs a) {
     __shared__ uint32_t s_tscale[5];
     const bool fused = FUSED && nblk > 0;   // one partition: this group holds the last block
     if (fused && w < 2) {
-        const TileStoreArgs t{const_cast<int8_t*>(a.k_codes), const_cast<uint8_t*>(a.v_codes),
-                              const_cast<uint16_t*>(a.k_scale), const_cast<uint16_t*>(a.v_scale),
-                              const_cast<uint8_t*>(a.v_zp), a.tail_k, a.tail_v, a.k_new, a.v_new, H};
+        const TileStoreArgs t = fused_store_args(a);
         const int last = nblk - 1;
         const int slot = a.tail_slots[s], phys = tab[last];
         if (w == 0) {
@@ -1042,12 +1101,12 @@ void attn_partition_gqa(AttnArgs a) {
     const int dma_r = lane / CPR;
     const uint32_t dma_k = (uint32_t)(dma_r * D + 16 * ((lane % CPR) ^ kswz(dma_r)));
     const uint32_t dma_v = 16u * (uint32_t)lane;
-    int ko[2][KCH / 16];
+    int ko[2][NKC];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
         const int R = kblk[mt] * BS + krow[mt];   // row within the step
 #pragma unroll
-        for (int c = 0; c < KCH / 16; ++c)
+        for (int c = 0; c < NKC; ++c)
             ko[mt][c] = (R / RPR) * KREG + (R % RPR) * D + 16 * ((grp + 4 * c) ^ kswz(R % RPR));
     }
     const int vo = NKL * KREG + my_blk * VT + vcol + n16 * VROW;
@@ -1080,14 +1139,14 @@ void attn_partition_gqa(AttnArgs a) {
     const uint32_t la_v = lds_addr(my_stage) + (uint32_t)vo;
     auto read_stage_k = [&](auto bc, Raw& r) {
         constexpr int B = decltype(bc)::value;
-        static_for<KCH / 16>([&](auto cc) {
+        static_for<NKC>([&](auto cc) {
             constexpr int c = decltype(cc)::value;
             lds_read<B * STG + 64 * c>(r.k[0][c], la_k0);
             lds_read<B * STG + 64 * c>(r.k[1][c], la_k1);
         });
         wait_lds();
 #pragma unroll
-        for (int c = 0; c < KCH / 16; ++c) {
+        for (int c = 0; c < NKC; ++c) {
             lds_fence(r.k[0][c]);
             lds_fence(r.k[1][c]);
         }
@@ -1104,7 +1163,7 @@ void attn_partition_gqa(AttnArgs a) {
     };
     auto read_stage = [&](auto bc, Raw& r) {
         constexpr int B = decltype(bc)::value;
-        static_for<KCH / 16>([&](auto cc) {
+        static_for<NKC>([&](auto cc) {
             constexpr int c = decltype(cc)::value;
             lds_read<B * STG + 64 * c>(r.k[0][c], la_k0);
             lds_read<B * STG + 64 * c>(r.k[1][c], la_k1);
@@ -1115,7 +1174,7 @@ void attn_partition_gqa(AttnArgs a) {
         });
         wait_lds();
 #pragma unroll
-        for (int c = 0; c < KCH / 16; ++c) {
+        for (int c = 0; c < NKC; ++c) {
             lds_fence(r.k[0][c]);
             lds_fence(r.k[1][c]);
         }
@@ -1129,7 +1188,7 @@ void attn_partition_gqa(AttnArgs a) {
         const bool ok_l = st_l < w_stop && blk_l < blk_end;
         const int id_l = ok_l ? tab[blk_l] : 0;
         const int cnt = min(SPB, w_stop - base);
-        int sk_l, sv_l, zp_l = 0;   // raw scale bits and zero point (converted at use)
+        int sk_l, sv_l, zp_l = 0, kz_l = 0;   // raw scale bits and zero points (converted at use)
 
         // Loads are unconditional: a block past the partition's end has id 0
         // (any valid block); its tokens are masked, so its codes only meet
@@ -1151,16 +1210,18 @@ void attn_partition_gqa(AttnArgs a) {
                 const int v0 = readlane(sv_l, i);
                 const float vm = vnorm_step(v0);
                 compute_step(r, st, bits_to_f16f((uint16_t)readlane(sk_l, i)) * c2,
-                             bits_to_f16f((uint16_t)v0) * vm, (float)readlane(zp_l, i), before_pv);
+                             bits_to_f16f((uint16_t)v0) * vm, (float)readlane(zp_l, i),
+                             (float)readlane(kz_l, i), before_pv);
             } else {
                 const bool live1 = blk0 + st * BPS + 1 < blk_end;
                 const int k0 = readlane(sk_l, 2 * i), k1 = live1 ? readlane(sk_l, 2 * i + 1) : 0;
                 const int v0 = readlane(sv_l, 2 * i), v1 = live1 ? readlane(sv_l, 2 * i + 1) : 0;
                 const int z0 = readlane(zp_l, 2 * i), z1 = live1 ? readlane(zp_l, 2 * i + 1) : 0;
+                const int kz0 = readlane(kz_l, 2 * i), kz1 = live1 ? readlane(kz_l, 2 * i + 1) : 0;
                 const float vm = vnorm_step(max(v0, v1));   // fp16 bits of non-negative scales order as values
                 compute_step(r, st, bits_to_f16f((uint16_t)(my_blk ? k1 : k0)) * c2,
                              bits_to_f16f((uint16_t)(my_blk ? v1 : v0)) * vm, (float)(my_blk ? z1 : z0),
-                             before_pv);
+                             (float)(my_blk ? kz1 : kz0), before_pv);
             }
         };
         auto compute = [&](Raw& r, int i) { compute_with(r, i, [](Raw&) {}); };
@@ -1170,6 +1231,7 @@ void attn_partition_gqa(AttnArgs a) {
             sk_l = a.k_scale[t];
             sv_l = a.v_scale[t];
             if constexpr (VZP) zp_l = a.v_zp[t];
+            if constexpr (KZP) kz_l = a.k_zp[t];
         };
         if constexpr (JOINT) {
             // One staging area for both waves, three stages: step i + 2 is
@@ -1242,9 +1304,7 @@ void attn_partition_gqa(AttnArgs a) {
     if (FUSED && fused) {
         __syncthreads();   // waves 0 and 1 have left the last block's tiles in LDS
         if (w < 2 && ht == 0) {   // the first 16-head tile of a KV head writes the pool
-            const TileStoreArgs t{const_cast<int8_t*>(a.k_codes), const_cast<uint8_t*>(a.v_codes),
-                                  const_cast<uint16_t*>(a.k_scale), const_cast<uint16_t*>(a.v_scale),
-                                  const_cast<uint8_t*>(a.v_zp), a.tail_k, a.tail_v, a.k_new, a.v_new, H};
+            const TileStoreArgs t = fused_store_args(a);
             write_stored_tile<BS, D, CP>(t, w, kvh, a.tail_slots[s], s, ctx - 1, tab[nblk - 1], s_tile, s_tile + KT,
                                          s_tscale);
         }
@@ -1260,9 +1320,10 @@ void attn_partition_gqa(AttnArgs a) {
             const bool pair = first != last;              // block `first` comes from the pool
             Raw r;
             load_step(pair ? a.k_codes + t0 * KT : lk, lk, pair ? a.v_codes + t0 * VT : lv, lv, r);
-            const uint32_t ks0 = pair ? a.k_scale[t0] : s_tscale[0];
+            const uint32_t ks0 = pair ? a.k_scale[t0] : s_tscale[0] & 0xFFFFu;
             const uint32_t vs0 = pair ? a.v_scale[t0] : s_tscale[1];
             const uint32_t z0 = pair ? (VZP ? a.v_zp[t0] : 0u) : s_tscale[2];
+            const uint32_t kz0 = pair ? (KZP ? a.k_zp[t0] : 0u) : s_tscale[0] >> 16;
             // a lane group's block: `first` (my_blk 0) or the block after it,
             // which is the last block or lies past the end (masked)
             const bool mine_last = BPS == 1 || my_blk ? true : !pair;
@@ -1270,7 +1331,8 @@ void attn_partition_gqa(AttnArgs a) {
             const float vm = vnorm_step(pair ? max(vl, (int)vs0) : vl);
             compute_step(r, st, bits_to_f16f((uint16_t)(mine_last ? s_tscale[0] : ks0)) * c2,
                          bits_to_f16f((uint16_t)(mine_last ? s_tscale[1] : vs0)) * vm,
-                         (float)(mine_last ? s_tscale[2] : z0), [](Raw&) {});
+                         (float)(mine_last ? s_tscale[2] : z0), (float)(mine_last ? s_tscale[0] >> 16 : kz0),
+                         [](Raw&) {});
         }
     }
     // lanes of one head split its tokens by group: sum their partial sums,
@@ -1590,7 +1652,8 @@ hipError_t launch_multi_tiles(const AttnArgs& a, hipStream_t stream) {
     const int G = a.num_q_heads / a.num_kv_heads;
     // queries per work group: two-wave groups of two-tile waves share their
     // staging and take 64 (the kernel's JOINT mode), others 16 TPW
-    const int QW = (a.max_partitions == 1 && TPW == 2 && PBQ_MULTI_JOINT_STAGE) ? 64 : 16 * TPW;
+    const int QW = (a.max_partitions == 1 && TPW == 2 && PBQ_MULTI_JOINT_STAGE && !codec_packed4(CP / 4))
+                       ? 64 : 16 * TPW;
     const int n_ht = (a.max_q_len * G + QW - 1) / QW;
     // x = partition, y = KV head x query tile, z = sequence (the kernel
     // renumbers the work groups over the XCDs)

@@ -23,7 +23,8 @@ constexpr int codec_pair(int k, int v) { return 4 * k + v; }
 // the pairs the kernels are built for
 constexpr bool codec_pair_supported(int k, int v) {
     return (k == KV_CODEC_I8_SYM && (v == KV_CODEC_I8_SYM || v == KV_CODEC_I4_ASYM || v == KV_CODEC_I8_ASYM)) ||
-           (k == KV_CODEC_FP8_E4M3 && v == KV_CODEC_FP8_E4M3);
+           (k == KV_CODEC_FP8_E4M3 && v == KV_CODEC_FP8_E4M3) ||
+           (k == KV_CODEC_I4_ASYM && (v == KV_CODEC_I4_ASYM || v == KV_CODEC_I8_SYM));
 }
 
 // f(std::integral_constant<int, codec_pair(k, v)>{}) for a supported pair;
@@ -39,6 +40,10 @@ hipError_t with_codec_pair(int k, int v, F&& f) {
             return f(std::integral_constant<int, codec_pair(KV_CODEC_I8_SYM, KV_CODEC_I8_ASYM)>{});
         case codec_pair(KV_CODEC_FP8_E4M3, KV_CODEC_FP8_E4M3):
             return f(std::integral_constant<int, codec_pair(KV_CODEC_FP8_E4M3, KV_CODEC_FP8_E4M3)>{});
+        case codec_pair(KV_CODEC_I4_ASYM, KV_CODEC_I4_ASYM):
+            return f(std::integral_constant<int, codec_pair(KV_CODEC_I4_ASYM, KV_CODEC_I4_ASYM)>{});
+        case codec_pair(KV_CODEC_I4_ASYM, KV_CODEC_I8_SYM):
+            return f(std::integral_constant<int, codec_pair(KV_CODEC_I4_ASYM, KV_CODEC_I8_SYM)>{});
         default:
             return hipErrorInvalidValue;
     }
@@ -51,6 +56,7 @@ struct QuantStoreArgs {
     uint16_t* k_scale;
     uint16_t* v_scale;
     uint8_t* v_zp;
+    uint8_t* k_zp;
     uint16_t* tail_k;
     uint16_t* tail_v;
     const uint16_t* k;
@@ -74,6 +80,7 @@ struct AttnArgs {
     const uint16_t* k_scale;
     const uint16_t* v_scale;
     const uint8_t* v_zp;
+    const uint8_t* k_zp;
     const uint16_t* q;
     uint16_t* out;
     int32_t num_seqs, num_q_heads;
@@ -111,6 +118,7 @@ struct CopyArgs {
     uint16_t* k_scale;
     uint16_t* v_scale;
     uint8_t* v_zp;
+    uint8_t* k_zp;
     uint16_t* tail_k;
     uint16_t* tail_v;
     const kv_copy* copies;
@@ -125,6 +133,7 @@ struct SwapSide {
     uint16_t* k_scale;
     uint16_t* v_scale;
     uint8_t* v_zp;
+    uint8_t* k_zp;
     char* tail_k;
     char* tail_v;
 };

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void quantize_store_kernel(QuantStoreArgs a) {
     const int j = sp / BS + jj;
     if (g >= H || n_new <= 0 || j * BS >= end) return;
     const int phys = a.block_tables[(int64_t)s * a.max_blocks_per_seq + j];
-    const TileStoreArgs t{a.k_codes, a.v_codes, a.k_scale, a.v_scale, a.v_zp, a.tail_k, a.tail_v, a.k, a.v, H};
+    const TileStoreArgs t{a.k_codes, a.v_codes, a.k_scale, a.v_scale, a.v_zp, a.k_zp, a.tail_k, a.tail_v, a.k, a.v, H};
     if (wv & 1) store_tile<BS, D, CP, false, false, true>(t, g, slot, c0, sp, end, j, phys, nullptr, nullptr);
     else store_tile<BS, D, CP, false, true, false>(t, g, slot, c0, sp, end, j, phys, nullptr, nullptr);
 }

@@ -26,8 +26,10 @@
 // Further codecs: FP8 E4M3 (yunthe.com "vLLM deployment" names the format)
 // with an fp16 absmax/448 scale per (block, head), each code the E4M3 of the
 // correctly rounded fp32 quotient x / scale, clamped to +-448 and converted
-// by v_cvt_pk_fp8_f32 (round to nearest even); and INT8 asymmetric, the INT4
-// recipe with 255 levels and byte codes.
+// by v_cvt_pk_fp8_f32 (round to nearest even); INT8 asymmetric, the INT4
+// recipe with 255 levels and byte codes; and INT4 K (tbr8.org §3: blocks may
+// go to INT4), the INT4 recipe on the token-major K tile, two consecutive
+// head dims of a token per byte (the even dim in the low nibble).
 #pragma once
 
 #include "device_common.h"
@@ -43,6 +45,7 @@ struct TileStoreArgs {
     uint16_t* k_scale;
     uint16_t* v_scale;
     uint8_t* v_zp;
+    uint8_t* k_zp;
     uint16_t* tail_k;      // [max_seqs, H, bs, D] fp16
     uint16_t* tail_v;
     const uint16_t* k;     // new rows, token-major [T, H, D] fp16
@@ -50,9 +53,10 @@ struct TileStoreArgs {
     int32_t num_kv_heads;
 };
 
-// Raw bits of the scales (and zero point) a tile store wrote; with LDS set,
-// also what the pool held for the tile before (prev: K scale, or V scale |
-// zero point << 16), for write_stored_tile.
+// Raw bits of the scales (and zero point) a tile store wrote -- k_scale
+// carries the K zero point in its upper half for INT4 K; with LDS set, also
+// what the pool held for the tile before (prev: K scale (| K zero point <<
+// 16), or V scale | zero point << 16), for write_stored_tile.
 struct TileScales {
     uint32_t k_scale, v_scale, v_zp, prev;
 };
@@ -115,8 +119,9 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
         for (int it = 0; it < NIT; ++it) kx[it] = *(const f16x8*)(row_src(a.tail_k, a.k, it * RPI + r_in) + col);
     }
     const int64_t tile = (int64_t)phys * H + g;
+    constexpr bool KZP = codec_has_zp(KC);
     if constexpr (LDS) {   // the pool's scale bits before this store, loaded with the rows
-        if constexpr (DO_K) out.prev = a.k_scale[tile];
+        if constexpr (DO_K) out.prev = a.k_scale[tile] | (KZP ? (uint32_t)a.k_zp[tile] << 16 : 0u);
         else out.prev = a.v_scale[tile] | (VZP ? (uint32_t)a.v_zp[tile] << 16 : 0u);
     }
     uint32_t vw[DO_V ? BS : 1];   // V row r: dims DPL*lane .. +DPL-1 (fp16 bits)
@@ -210,6 +215,61 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
         }
         if (wr && lane == 0) a.k_scale[tile] = s16;
         out.k_scale = s16;
+    }
+
+    // ---- K: INT4 asymmetric (token-major, two head dims per byte) -----------
+    if constexpr (DO_K && KC == KV_CODEC_I4_ASYM) {
+        // range widened to contain 0, over packed fp16 pairs (exact); rows
+        // not held are zeros, which the widened range contains anyway
+        f16x2 lo2 = f16x2{(_Float16)0, (_Float16)0}, hi2 = lo2;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const f16x2 x = f16x2{kx[it][2 * e], kx[it][2 * e + 1]};
+                lo2 = __builtin_elementwise_min(lo2, x);
+                hi2 = __builtin_elementwise_max(hi2, x);
+            }
+        const float lo = wave_min_uniform(fminf((float)lo2[0], (float)lo2[1]));
+        const float hi = wave_max_uniform(fmaxf((float)hi2[0], (float)hi2[1]));
+        const uint16_t s16 = f32_to_f16_bits((hi - lo) / 15.0f);
+        const Quantizer qz(bits_to_f16f(s16));
+        int zp = 0;
+        if (qz.s > 0.f) {
+            const float z = __builtin_rintf(-lo / qz.s);
+            zp = z > 15.f ? 15 : (z < 0.f ? 0 : (int)z);
+        }
+        const float zf = (float)zp;
+        uint8_t* dst = (uint8_t*)a.k_codes + tile * (BS * D / 2);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {   // a lane's 8 dims of one row: 4 bytes
+            uint32_t x = 0u;
+            bool tie = false;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float u0 = qz.fast((float)kx[it][2 * b], zf, 0.f, 15.f, tie);
+                const float u1 = qz.fast((float)kx[it][2 * b + 1], zf, 0.f, 15.f, tie);
+                x = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(u1, 16.f, u0), b, x);
+            }
+            if (__builtin_amdgcn_ballot_w64(tie) != 0) {
+                x = 0u;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    int q = qz.exact((float)kx[it][e], zp);
+                    q = q > 15 ? 15 : (q < 0 ? 0 : q);
+                    x |= (uint32_t)q << (4 * e);
+                }
+            }
+            const int r = it * RPI + r_in;
+            x = r < valid ? x : 0u;   // rows not held are zero bytes (their code would be zp)
+            if (wr) *(uint32_t*)(dst + r * (D / 2) + col / 2) = x;
+            if constexpr (LDS) *(uint32_t*)(lds_k + r * (D / 2) + col / 2) = x;
+        }
+        if (wr && lane == 0) {
+            a.k_scale[tile] = s16;
+            a.k_zp[tile] = (uint8_t)zp;
+        }
+        out.k_scale = (uint32_t)s16 | ((uint32_t)zp << 16);
     }
 
     // ---- V (dim-major tile): INT8 symmetric, FP8, INT4 or INT8 asymmetric ------
@@ -426,20 +486,25 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
 }
 
 // Pool writes of a tile that store_tile quantized with wr false (codes left
-// in LDS at lds_k / lds_v; sc: K scale, V scale and zero point bits, then
-// the K and the V `prev` of store_tile): wave 0 writes K, wave 1 V, each also
+// in LDS at lds_k / lds_v; sc: K scale (| K zero point << 16), V scale and
+// zero point bits, then the K and the V `prev` of store_tile): wave 0 writes
+// K, wave 1 V, each also
 // the new row at position pos to the tail slot when its block stays partial.
 // When the block already held rows (pos % bs > 0) and its scale (and zero
 // point) did not change, the earlier rows' codes are unchanged -- the same
 // exact rows under the same scale -- and only the new token's codes are
-// written: its K row (D bytes), and its byte of every V dim row.  The fused
+// written: its K row (D bytes, D / 2 for INT4), and its byte of every V dim
+// row.  The fused
 // decode calls it after its loop.  new_row is the row of a.k / a.v that holds
 // position pos.
 template <int BS, int D, int CP>
 __device__ __forceinline__ void write_stored_tile(const TileStoreArgs& a, int w, int g, int slot, int new_row, int pos,
                                                   int phys, const uint8_t* lds_k, const uint8_t* lds_v,
                                                   const uint32_t* sc) {
-    constexpr int KT = BS * D;
+    constexpr bool K4 = codec_packed4(CP / 4);
+    constexpr bool KZP = codec_has_zp(CP / 4);
+    constexpr int KROW = K4 ? D / 2 : D;   // K bytes per token row
+    constexpr int KT = BS * KROW;
     constexpr bool V4 = codec_packed4(CP % 4);
     constexpr bool VZP = codec_has_zp(CP % 4);
     constexpr int VROW = V4 ? BS / 2 : BS;
@@ -454,11 +519,15 @@ __device__ __forceinline__ void write_stored_tile(const TileStoreArgs& a, int w,
     if (w == 0) {
         if (r == 0 || sc[3] != sc[0]) {
 #pragma unroll
-            for (int c = 0; c < KT / 1024; ++c)
-                *(u32x4*)(a.k_codes + tile * KT + 1024 * c + 16 * lane) = *(const u32x4*)(lds_k + 1024 * c + 16 * lane);
-            if (lane == 0) a.k_scale[tile] = (uint16_t)sc[0];
-        } else if (lane < D / 16) {
-            *(u32x4*)(a.k_codes + tile * KT + r * D + 16 * lane) = *(const u32x4*)(lds_k + r * D + 16 * lane);
+            for (int c = 0; c < (KT + 1023) / 1024; ++c)
+                if (KT % 1024 == 0 || 1024 * c + 16 * lane < KT)
+                    *(u32x4*)(a.k_codes + tile * KT + 1024 * c + 16 * lane) = *(const u32x4*)(lds_k + 1024 * c + 16 * lane);
+            if (lane == 0) {
+                a.k_scale[tile] = (uint16_t)sc[0];
+                if constexpr (KZP) a.k_zp[tile] = (uint8_t)(sc[0] >> 16);
+            }
+        } else if (lane < KROW / 16) {
+            *(u32x4*)(a.k_codes + tile * KT + r * KROW + 16 * lane) = *(const u32x4*)(lds_k + r * KROW + 16 * lane);
         }
         if (tail && lane < D / 8) *(u32x4*)(a.tail_k + trow + 8 * lane) = *(const u32x4*)(a.k + nrow + 8 * lane);
     } else if (w == 1) {

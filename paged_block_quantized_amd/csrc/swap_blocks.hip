@@ -41,7 +41,8 @@ __global__ __launch_bounds__(kThreads) void swap_kernel(SwapArgs a) {
         const int32_t dst_n = out ? a.host_blocks : a.dev_blocks;
         if (c.src < 0 || c.src >= src_n || c.dst < 0 || c.dst >= dst_n) return;
         const bool v4 = codec_packed4(a.v_codec), zp = codec_has_zp(a.v_codec);
-        const int64_t kb = tile * H, vb = v4 ? kb / 2 : kb;
+        const bool k4 = codec_packed4(a.k_codec), kzp = codec_has_zp(a.k_codec);
+        const int64_t kb = k4 ? tile * H / 2 : tile * H, vb = v4 ? tile * H / 2 : tile * H;
         const int64_t ku = kb / 16, units = (kb + vb) / 16;
         const char* sk = from.k_codes + c.src * kb;
         const char* sv = from.v_codes + c.src * vb - kb;
@@ -63,6 +64,7 @@ __global__ __launch_bounds__(kThreads) void swap_kernel(SwapArgs a) {
                 to.k_scale[(int64_t)c.dst * H + g] = from.k_scale[(int64_t)c.src * H + g];
                 to.v_scale[(int64_t)c.dst * H + g] = from.v_scale[(int64_t)c.src * H + g];
                 if (zp) to.v_zp[(int64_t)c.dst * H + g] = from.v_zp[(int64_t)c.src * H + g];
+                if (kzp) to.k_zp[(int64_t)c.dst * H + g] = from.k_zp[(int64_t)c.src * H + g];
             }
     } else {
         const int32_t src_n = out ? a.dev_slots : a.host_slots;

@@ -12,8 +12,8 @@ class KVPool:
     ``kv_pool_bytes``.
 
     v_codec: "i8" (INT8 symmetric), "i4" (INT4 asymmetric), "i8a" (INT8
-    asymmetric) or "fp8" (FP8 E4M3) V; k_codec: "i8" or "fp8", by default
-    "fp8" exactly when V is FP8 (the supported pairs).
+    asymmetric) or "fp8" (FP8 E4M3) V; k_codec: "i8", "fp8" or "i4" (INT4
+    asymmetric, with V "i4" or "i8"), by default "fp8" exactly when V is FP8.
     free_order: initial free stack (a permutation of 0..N-1) or None.
     """
 
@@ -30,6 +30,8 @@ class KVPool:
         self.k_codec, self.v_codec = k_codec, v_codec
         self.v_int4 = v_codec == "i4"
         self.v_zp_used = v_codec in ("i4", "i8a")
+        self.k_int4 = k_codec == "i4"
+        self.k_zp_used = k_codec == "i4"
         self.max_seqs = max_seqs
         self.handle = L.kv_pool_create(self.desc, free_order)
         self.sizes = L.kv_pool_bytes(self.desc)
@@ -40,17 +42,24 @@ class KVPool:
             dev = torch.device(device)
             self.arrays = self._arrays(N, max_seqs, lambda shape, dtype: torch.zeros(shape, dtype=dtype, device=dev))
             for name, t in self.arrays.items():
-                if name == "v_zp" and not self.v_zp_used:
+                if not self._used(name):
                     continue
                 assert t.numel() * t.element_size() == self.sizes[name], name
             self.mem = self._mem(self.arrays)
+
+    def _used(self, name):
+        """False for a zero-point array the codecs do not use."""
+        return not ((name == "v_zp" and not self.v_zp_used) or (name == "k_zp" and not self.k_zp_used))
 
     def _arrays(self, nb, ns, make):
         """The pool's arrays for nb blocks and ns tail slots (layout as
         kv_pool_bytes gives it), each from make(shape, dtype)."""
         H, bs, D = self.num_kv_heads, self.block_size, self.head_dim
         return {
-            "k_codes": make((nb, H, bs, D), torch.int8 if self.k_codec == "i8" else torch.uint8),
+            # K tiles are token-major: [bs, D] codes per (block, head); INT4
+            # packs two consecutive head dims per byte
+            "k_codes": make((nb, H, bs, D // 2 if self.k_int4 else D),
+                            torch.int8 if self.k_codec == "i8" else torch.uint8),
             # V tiles are dim-major: [D, bs] codes per (block, head)
             "v_codes": make((nb, H, D, bs // 2 if self.v_int4 else bs),
                             torch.int8 if self.v_codec == "i8" else torch.uint8),
@@ -59,12 +68,11 @@ class KVPool:
             "v_zp": make((nb, H) if self.v_zp_used else (1,), torch.uint8),
             "tail_k": make((ns, H, bs, D), torch.float16),
             "tail_v": make((ns, H, bs, D), torch.float16),
+            "k_zp": make((nb, H) if self.k_zp_used else (1,), torch.uint8),
         }
 
     def _mem(self, arrays):
-        return L.kv_pool_mem(*[
-            None if (n == "v_zp" and not self.v_zp_used) else arrays[n].data_ptr()
-            for n in ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "tail_k", "tail_v")])
+        return L.kv_pool_mem(*[arrays[n].data_ptr() if self._used(n) else None for n in L.POOL_ARRAYS])
 
     def __getattr__(self, name):
         arrays = self.__dict__.get("arrays", {})
@@ -167,7 +175,7 @@ class KVPool:
         """A copy of the pool's code, scale and zero-point arrays in fresh
         device memory (tail slots shared), as a kv_pool_mem: the same cache
         contents at other addresses, e.g. to stand for another layer's pool."""
-        keep = {n: (t if n.startswith("tail") or (n == "v_zp" and not self.v_zp_used) else t.clone())
+        keep = {n: (t if n.startswith("tail") or not self._used(n) else t.clone())
                 for n, t in self.arrays.items()}
         return self._mem(keep), keep
 

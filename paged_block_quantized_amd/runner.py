@@ -134,7 +134,7 @@ def setup_decode(w: W.Workload, device="cuda", chunk_seqs=8, partition=None, ord
     ctx = ctx_w[order]
     S, bs = w.num_seqs, w.block_size
     N = w.pool_blocks or blocks_needed(w, ctx)
-    pool = KVPool(N, bs, w.num_kv_heads, w.head_dim, w.v_codec, max_seqs=S + 1,
+    pool = KVPool(N, bs, w.num_kv_heads, w.head_dim, w.v_codec, k_codec=W.k_codec_of(w), max_seqs=S + 1,
                   free_order=W.free_order(w, N), device=device)
     if w.prefix:
         parent = S
@@ -283,7 +283,7 @@ def setup_multi(w: W.Workload, device="cuda", chunk_seqs=8, partition=0) -> Mult
     ctx = W.context_lengths(w)
     S, bs = w.num_seqs, w.block_size
     N = blocks_needed(w, ctx)
-    pool = KVPool(N, bs, w.num_kv_heads, w.head_dim, w.v_codec, max_seqs=S,
+    pool = KVPool(N, bs, w.num_kv_heads, w.head_dim, w.v_codec, k_codec=W.k_codec_of(w), max_seqs=S,
                   free_order=W.free_order(w, N), device=device)
     for c0 in range(0, S, chunk_seqs):
         ids = list(range(c0, min(S, c0 + chunk_seqs)))
@@ -353,7 +353,7 @@ def setup_prefill_store(w: W.Workload, device="cuda") -> StoreSetup:
     nothing stored yet)."""
     S, T, bs = w.num_seqs, w.ctx[0], w.block_size
     N = w.pool_blocks or S * ((T + bs - 1) // bs)
-    pool = KVPool(N, bs, w.num_kv_heads, w.head_dim, w.v_codec, max_seqs=S,
+    pool = KVPool(N, bs, w.num_kv_heads, w.head_dim, w.v_codec, k_codec=W.k_codec_of(w), max_seqs=S,
                   free_order=W.free_order(w, N), device=device)
     for s in range(S):
         pool.alloc(s, T)
@@ -408,7 +408,7 @@ def setup_append(w: W.Workload, steps: int = 16, device="cuda") -> AppendSetup:
     S, bs = w.num_seqs, w.block_size
     rng = np.random.default_rng([w.seed, 7])
     fill = rng.integers(1, bs, S)
-    pool = KVPool(w.pool_blocks or S * 2, bs, w.num_kv_heads, w.head_dim, w.v_codec, max_seqs=S,
+    pool = KVPool(w.pool_blocks or S * 2, bs, w.num_kv_heads, w.head_dim, w.v_codec, k_codec=W.k_codec_of(w), max_seqs=S,
                   free_order=W.free_order(w, w.pool_blocks or S * 2), device=device)
     for s in range(S):
         pool.alloc(s, int(fill[s]))

@@ -54,7 +54,7 @@ class Workload:
     num_kv_heads: int
     head_dim: int
     block_size: int
-    v_codec: str                   # "i8", "i4", "i8a" or "fp8" (K is FP8 exactly when V is)
+    v_codec: str                   # "i8", "i4", "i8a" or "fp8" (K: see k_codec)
     ctx_kind: str                  # "fixed", "list", "uniform"
     ctx: tuple = ()                # fixed: (n,), list: lengths, uniform: (lo, hi)
     channel_sigma: float = 0.0     # LogNormal sigma of per-(head, dim) factors
@@ -66,6 +66,7 @@ class Workload:
     seed: int = 0
     q_len: int = 0                 # query tokens per sequence (multi-query workloads)
     store_only: bool = False       # measured as quantize-and-store (no attention)
+    k_codec: str = ""              # "" : FP8 with FP8 V, else INT8; or "i4" (INT4 K, V "i4" or "i8")
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
 
@@ -90,12 +91,22 @@ WORKLOADS = {
                               channel_sigma=0.5, q_len=512, seed=6),
     "prefill_chunk_gqa": Workload("prefill_chunk_gqa", 16, 64, 8, 128, 32, "i4", "fixed", (4096,),
                                   q_len=512, seed=7),
+    # INT4 K (tbr8.org §3: blocks in INT8 or even INT4): the llama7b and
+    # gqa70b shapes with INT4 K and INT4 or INT8 V, the same draws
+    "llama7b_k4v4": Workload("llama7b_k4v4", 32, 32, 32, 128, 16, "i4", "fixed", (4096,),
+                             channel_sigma=0.5, seed=2, k_codec="i4"),
+    "llama7b_k4v8": Workload("llama7b_k4v8", 32, 32, 32, 128, 16, "i8", "fixed", (4096,),
+                             channel_sigma=0.5, seed=2, k_codec="i4"),
+    "gqa70b_k4": Workload("gqa70b_k4", 128, 64, 8, 128, 32, "i4", "uniform", (500, 2000),
+                          outlier_frac=0.01, outlier_mult=8.0, seed=3, k_codec="i4"),
 }
 
 
 def k_codec_of(w: Workload) -> str:
-    """The K codec paired with the workload's V codec (FP8 K with FP8 V,
-    INT8 symmetric K otherwise)."""
+    """The workload's K codec: its own when set, else FP8 with FP8 V and
+    INT8 symmetric otherwise."""
+    if w.k_codec:
+        return w.k_codec
     return "fp8" if w.v_codec == "fp8" else "i8"
 
 

@@ -12,6 +12,27 @@ from oracle import attention, paged
 ATOL, RTOL = 2e-3, 1e-2   # |gpu - ref| <= ATOL + RTOL * |ref|, fp32 accumulate
 
 
+def codecs(spec):
+    """(K codec, V codec) of a test's codec name: "k4i4" and "k4i8" are INT4 K
+    with INT4 or INT8 V, "fp8" is FP8 K and V, any other name is INT8 K with
+    that V codec."""
+    if spec.startswith("k4"):
+        return "i4", spec[2:]
+    return ("fp8" if spec == "fp8" else "i8"), spec
+
+
+def zp_arrays(spec):
+    """Names of the zero-point arrays a codec pair uses."""
+    kc, vc = codecs(spec)
+    return (("v_zp",) if vc in ("i4", "i8a") else ()) + (("k_zp",) if kc == "i4" else ())
+
+
+def make_pool(n_blocks, bs, hkv, d, spec, **kw):
+    from paged_block_quantized_amd import KVPool
+    kc, vc = codecs(spec)
+    return KVPool(n_blocks, bs, hkv, d, vc, k_codec=kc, **kw)
+
+
 def announce(*what):
     print("CASE", *what, flush=True)
     sys.stdout.flush()
@@ -33,6 +54,7 @@ def assert_close(gpu, ref, what=""):
 def pool_numpy(pool):
     out = {n: pool.arrays[n].cpu().numpy() for n in ("k_codes", "v_codes", "k_scale", "v_scale")}
     out["v_zp"] = pool.arrays["v_zp"].cpu().numpy() if pool.v_zp_used else None
+    out["k_zp"] = pool.arrays["k_zp"].cpu().numpy() if pool.k_zp_used else None
     return out
 
 
@@ -46,6 +68,8 @@ def assert_pool_equal(gpu_pool, opool, blocks=None):
     assert np.array_equal(g["v_scale"][sel].view(np.uint16), opool.v_scale[sel].view(np.uint16)), "V scales differ"
     if gpu_pool.v_zp_used:
         assert np.array_equal(g["v_zp"][sel], opool.v_zp[sel]), "V zero points differ"
+    if gpu_pool.k_zp_used:
+        assert np.array_equal(g["k_zp"][sel], opool.k_zp[sel]), "K zero points differ"
 
 
 class SmallCase:
@@ -54,17 +78,16 @@ class SmallCase:
 
     def __init__(self, hist_k, hist_v, q, hq, hkv, d, bs, v_codec, n_blocks, free_order,
                  device="cuda"):
-        from paged_block_quantized_amd import KVPool
         self.S = len(hist_k)
         self.ctx = [int(k.shape[0]) for k in hist_k]
         self.hist_k, self.hist_v, self.q = hist_k, hist_v, q
         self.hq, self.hkv, self.d, self.bs = hq, hkv, d, bs
-        self.v_int4 = v_codec == "i4"
+        self.v_int4 = codecs(v_codec)[1] == "i4"
         self.device = device
-        self.pool = KVPool(n_blocks, bs, hkv, d, v_codec, max_seqs=self.S,
-                           free_order=free_order, device=device)
+        self.pool = make_pool(n_blocks, bs, hkv, d, v_codec, max_seqs=self.S, free_order=free_order,
+                              device=device)
         self.model = A.BlockPoolModel(n_blocks, bs, self.S, free_order)
-        self.opool = paged.PoolArrays(n_blocks, hkv, bs, d, k_codec=self.pool.k_codec, v_codec=v_codec)
+        self.opool = opool_for(n_blocks, hkv, bs, d, v_codec)
         for s, c in enumerate(self.ctx):
             t_gpu = self.pool.alloc(s, c)
             t_ref = self.model.alloc(s, c)
@@ -99,9 +122,10 @@ class SmallCase:
         return attention.paged_decode(self.opool, tables, self.ctx, self.q, sm)
 
 
-def opool_for(n_blocks, hkv, bs, d, vc):
-    """The oracle's pool for a V codec name (K is FP8 exactly when V is)."""
-    return paged.PoolArrays(n_blocks, hkv, bs, d, k_codec="fp8" if vc == "fp8" else "i8", v_codec=vc)
+def opool_for(n_blocks, hkv, bs, d, spec):
+    """The oracle's pool for a test's codec name (see codecs)."""
+    kc, vc = codecs(spec)
+    return paged.PoolArrays(n_blocks, hkv, bs, d, k_codec=kc, v_codec=vc)
 
 
 def normal_case(ctx, hq, hkv, d, bs, v_codec, seed, extra_blocks=3, perm=True):
@@ -128,6 +152,8 @@ def gathered_pool(setup, s):
     g.v_scale = pool.v_scale[table].cpu().numpy()
     if pool.v_zp_used:
         g.v_zp = pool.v_zp[table].cpu().numpy()
+    if pool.k_zp_used:
+        g.k_zp = pool.k_zp[table].cpu().numpy()
     return g
 
 
@@ -150,6 +176,8 @@ def check_sequence(setup, s, out, what=None):
     assert np.array_equal(g.v_scale.view(np.uint16), ref_pool.v_scale.view(np.uint16)), f"seq {s}: V scales"
     if ref_pool.v_codec in ("i4", "i8a"):
         assert np.array_equal(g.v_zp, ref_pool.v_zp), f"seq {s}: zero points"
+    if ref_pool.k_codec == "i4":
+        assert np.array_equal(g.k_zp, ref_pool.k_zp), f"seq {s}: K zero points"
     khat, vhat = paged.gather_dequant(ref_pool, list(range(nb)), ctx)
     q = setup.q[s].cpu().numpy()
     ref = attention.decode_attention(q, khat, vhat, setup.sm_scale)

@@ -213,12 +213,16 @@ def test_swap_blocks_validates_plan_on_host(lib):
 
 
 def test_pool_bytes_match_closed_form(lib):
-    for bs, D, H, v4, N in [(16, 128, 32, False, 8192), (32, 128, 8, True, 1000), (16, 64, 2, False, 64)]:
-        desc = L.make_desc(N, bs, H, D, L.KV_CODEC_I4_ASYM if v4 else L.KV_CODEC_I8_SYM, 3)
+    for bs, D, H, v4, k4, N in [(16, 128, 32, False, False, 8192), (32, 128, 8, True, False, 1000),
+                                (16, 64, 2, False, False, 64), (16, 128, 32, True, True, 8192),
+                                (32, 64, 3, False, True, 77)]:
+        desc = L.make_desc(N, bs, H, D, L.KV_CODEC_I4_ASYM if v4 else L.KV_CODEC_I8_SYM, 3,
+                           k_codec=L.KV_CODEC_I4_ASYM if k4 else L.KV_CODEC_I8_SYM)
         sz = L.kv_pool_bytes(desc)
-        per_block = sum(sz[n] for n in ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp")) // N
-        assert per_block == kv_size.pool_block_bytes(H, D, bs, 8, 4 if v4 else 8, v4)
+        per_block = sum(sz[n] for n in ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "k_zp")) // N
+        assert per_block == kv_size.pool_block_bytes(H, D, bs, 4 if k4 else 8, 4 if v4 else 8, v4, k4)
         assert sz["tail_k"] == sz["tail_v"] == 3 * H * bs * D * 2
+        assert sz["k_zp"] == (N * H if k4 else 0)
 
 
 def test_create_rejects_bad_arguments(lib):
@@ -233,9 +237,11 @@ def test_create_rejects_bad_arguments(lib):
         L.kv_pool_bytes(L.make_desc(4, 16, 1, 96))     # head_dim 96 has no kernel
     with pytest.raises(L.PBQError):
         L.kv_pool_bytes(L.make_desc(4, 16, 1, 64, v_codec=7))
-    # codec pairs: FP8 K goes with FP8 V only, FP8 V with FP8 K only
+    # codec pairs: FP8 K goes with FP8 V only, FP8 V with FP8 K only, INT4 K
+    # with INT4 or INT8 V
     for kc, vc in ((L.KV_CODEC_I8_SYM, L.KV_CODEC_FP8_E4M3), (L.KV_CODEC_FP8_E4M3, L.KV_CODEC_I4_ASYM),
-                   (L.KV_CODEC_I4_ASYM, L.KV_CODEC_I4_ASYM), (L.KV_CODEC_I8_ASYM, L.KV_CODEC_I8_ASYM)):
+                   (L.KV_CODEC_I4_ASYM, L.KV_CODEC_I8_ASYM), (L.KV_CODEC_I4_ASYM, L.KV_CODEC_FP8_E4M3),
+                   (L.KV_CODEC_I8_ASYM, L.KV_CODEC_I8_ASYM)):
         with pytest.raises(L.PBQError, match="unsupported"):
             L.kv_pool_bytes(L.make_desc(4, 16, 1, 64, v_codec=vc, k_codec=kc))
 

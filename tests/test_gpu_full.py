@@ -38,10 +38,11 @@ def test_llama7b_full():
     _run("llama7b", samples=[0, 9, 13, 22, 31])
 
 
-@pytest.mark.parametrize("name", ["llama7b_fp8", "llama7b_i8a", "gqa70b_fp8"])
+@pytest.mark.parametrize("name", ["llama7b_fp8", "llama7b_i8a", "gqa70b_fp8", "llama7b_k4v4", "llama7b_k4v8",
+                                  "gqa70b_k4"])
 def test_codec_variants_full(name):
-    """The FP8 and INT8-asymmetric workloads at full size, sampled sequences
-    against the oracle."""
+    """The FP8, INT8-asymmetric and INT4-K workloads at full size, sampled
+    sequences against the oracle."""
     _run(name, samples=[0, 11, 17, 31] if name.startswith("llama") else [0, 40, 77, 127])
 
 

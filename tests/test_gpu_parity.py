@@ -9,7 +9,8 @@ import torch
 from oracle import allocator as A
 from oracle import attention, paged
 
-from gpu_util import SmallCase, announce, assert_close, assert_pool_equal, normal_case, opool_for
+from gpu_util import (SmallCase, announce, assert_close, assert_pool_equal, codecs, make_pool, normal_case,
+                      opool_for, zp_arrays)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +44,7 @@ def test_tiny_workload(partition):
     assert np.array_equal(out[0], vrow.astype(np.float16))
 
 
-SHAPES = [(bs, d, vc) for bs in (16, 32) for d in (64, 128) for vc in ("i8", "i4", "i8a", "fp8")]
+SHAPES = [(bs, d, vc) for bs in (16, 32) for d in (64, 128) for vc in ("i8", "i4", "i8a", "fp8", "k4i4", "k4i8")]
 
 
 @pytest.mark.parametrize("bs,d,vc", SHAPES)
@@ -70,7 +71,7 @@ def test_zero_context_and_zero_blocks():
     hv[2][16:32] = 0           # an all-zero V block between non-zero ones
     hk[2][:16] = np.float16(0.5)  # a constant K block
     q = rng.standard_normal((3, 1, d)).astype(np.float16)
-    for vc in ("i8", "i4", "i8a", "fp8"):
+    for vc in ("i8", "i4", "i8a", "fp8", "k4i4", "k4i8"):
         case = SmallCase(hk, hv, q, 1, 1, d, bs, vc, 8, rng.permutation(8))
         case.store_all()
         assert_pool_equal(case.pool, case.opool)
@@ -102,7 +103,9 @@ def test_rounding_ties():
     f8 = np.array([[448.0] + mids * 6 + [0.0, -0.0, 1.0]] * bs, np.float16)[:, None, :]
     k8 = f8.copy()
     q = np.ones((2, 1, d), np.float16)
-    for vc, kk, vv in (("i8", k, v), ("i4", k, v4), ("i8a", k, v8), ("fp8", k8, f8)):
+    # INT4 K: the INT4 V rows as K (scale 1, zero point 5, half-integer ties)
+    for vc, kk, vv in (("i8", k, v), ("i4", k, v4), ("i8a", k, v8), ("fp8", k8, f8), ("k4i4", v4, v4),
+                       ("k4i8", v4, v)):
         case = SmallCase([kk, kk[:7]], [vv, vv[:7]], q, 1, 1, d, bs, vc, 4, None)
         case.store_all()
         assert_pool_equal(case.pool, case.opool)
@@ -141,7 +144,7 @@ def _store_chunk(pool, k, v, s, start, tables, slots):
                         tables[s:s + 1], slots[s:s + 1], k.shape[0])
 
 
-@pytest.mark.parametrize("vc", ["i8", "i4", "i8a", "fp8"])
+@pytest.mark.parametrize("vc", ["i8", "i4", "i8a", "fp8", "k4i4", "k4i8"])
 def test_append_requantize_from_tail(vc):
     """One-token appends re-quantize the partial block from the exact rows in
     the tail slot; the result equals the oracle's quantization of the rows."""
@@ -152,7 +155,7 @@ def test_append_requantize_from_tail(vc):
     total = 40
     hk = rng.standard_normal((total, h, d)).astype(np.float16)
     hv = rng.standard_normal((total, h, d)).astype(np.float16)
-    pool = KVPool(8, bs, h, d, vc, max_seqs=2, free_order=rng.permutation(8))
+    pool = make_pool(8, bs, h, d, vc, max_seqs=2, free_order=rng.permutation(8))
     model = A.BlockPoolModel(8, bs, 2, pool.free_list())
     opool = opool_for(8, h, bs, d, vc)
     pool.alloc(0, 3)
@@ -181,7 +184,7 @@ def test_append_requantize_from_tail(vc):
     assert_pool_equal(pool, pre)
 
 
-@pytest.mark.parametrize("vc", ["i8", "i4", "i8a", "fp8"])
+@pytest.mark.parametrize("vc", ["i8", "i4", "i8a", "fp8", "k4i4", "k4i8"])
 def test_fork_copy_on_write(vc):
     """An unaligned shared prefix: fork copies the tail slot; each child's
     first append copies only the shared partial block; shared prefix blocks
@@ -195,7 +198,7 @@ def test_fork_copy_on_write(vc):
     hp_v = rng.standard_normal((pre, h, d)).astype(np.float16)
     N = 16
     order = rng.permutation(N)
-    pool = KVPool(N, bs, h, d, vc, max_seqs=4, free_order=order)
+    pool = make_pool(N, bs, h, d, vc, max_seqs=4, free_order=order)
     model = A.BlockPoolModel(N, bs, 4, order)
     opool = opool_for(N, h, bs, d, vc)
     parent = 9
@@ -253,6 +256,10 @@ GQA_SHAPES = [
     (16, 64, "fp8", 4, 1),
     (32, 128, "i8a", 8, 2),
     (16, 128, "i8a", 7, 2),
+    (32, 128, "k4i4", 8, 2),
+    (16, 64, "k4i8", 4, 1),
+    (16, 128, "k4i4", 7, 2),
+    (32, 64, "k4i8", 16, 1),
 ]
 
 
@@ -280,9 +287,10 @@ def test_gqa_rejects_partition_not_multiple_of_32():
         case.decode(16)
 
 
-APPEND_SHAPES = [(bs, d, vc, 1) for bs in (16, 32) for d in (64, 128) for vc in ("i8", "i4", "i8a", "fp8")] + [
+APPEND_SHAPES = [(bs, d, vc, 1) for bs in (16, 32) for d in (64, 128)
+                 for vc in ("i8", "i4", "i8a", "fp8", "k4i4", "k4i8")] + [
     (32, 128, "i4", 8), (16, 128, "i8", 4), (32, 128, "fp8", 8), (16, 64, "fp8", 4), (32, 128, "i8a", 8),
-    (16, 128, "i8a", 2)]
+    (16, 128, "i8a", 2), (32, 128, "k4i4", 8), (16, 64, "k4i8", 4), (16, 128, "k4i4", 2)]
 
 
 @pytest.mark.parametrize("bs,d,vc,g", APPEND_SHAPES)
@@ -309,7 +317,7 @@ def test_decode_append_equals_store_then_decode(bs, d, vc, g):
     dev = torch.device("cuda")
 
     def build():
-        pool = KVPool(n_blocks, bs, hkv, d, vc, max_seqs=S, free_order=order)
+        pool = make_pool(n_blocks, bs, hkv, d, vc, max_seqs=S, free_order=order)
         for s, c in enumerate(ctx):
             pool.alloc(s, c - 1)
         tables, _, slots = pool.batch_tables(list(range(S)), max_blocks)
@@ -351,7 +359,7 @@ def test_decode_append_equals_store_then_decode(bs, d, vc, g):
         out_b = torch.empty_like(qd)
         pb.decode_append(k_new, v_new, sb, qd, out_b, tb, cb, max(ctx), sm, part)
         torch.cuda.synchronize()
-        for name in ("k_codes", "v_codes", "k_scale", "v_scale", "tail_k", "tail_v") + (("v_zp",) if vc in ("i4", "i8a") else ()):
+        for name in ("k_codes", "v_codes", "k_scale", "v_scale", "tail_k", "tail_v") + zp_arrays(vc):
             x, y = pa.arrays[name].cpu().numpy(), pb.arrays[name].cpu().numpy()
             assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f"{name} differs (part {part})"
         g_k = pb.k_codes.cpu().numpy()
@@ -374,6 +382,8 @@ SHARED_SHAPES = [
     (32, 128, "fp8", 8, 2, 5, 64),
     (16, 128, "fp8", 1, 2, 5, 128),
     (32, 64, "i8a", 1, 2, 5, 64),
+    (32, 128, "k4i4", 8, 2, 5, 64),
+    (16, 64, "k4i8", 1, 2, 5, 64),
 ]
 
 
@@ -395,7 +405,8 @@ def test_shared_prefix_decode(bs, d, vc, g, hkv, S, part):
                                      bs - 1, 64, 129, 9, 40, 500, 3, 17, 250, 6][:S])
     w = dataclasses.replace(W.WORKLOADS["shared_prefix"], name="shared_small", num_seqs=S,
                             num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d, block_size=bs,
-                            v_codec=vc, ctx_kind="list", ctx=ctx, prefix=prefix, partition=part,
+                            v_codec=codecs(vc)[1], k_codec=codecs(vc)[0], ctx_kind="list", ctx=ctx,
+                            prefix=prefix, partition=part,
                             seed=11 * bs + d + g + S)
     setup = runner.setup_decode(w)
     assert setup.shared == prefix
@@ -426,6 +437,8 @@ P9_SHAPES = [
     (16, 64, "i8", 4, 1),
     (32, 128, "fp8", 8, 2),
     (16, 128, "i8a", 1, 2),
+    (32, 128, "k4i4", 8, 2),
+    (16, 64, "k4i8", 1, 2),
 ]
 
 
@@ -448,7 +461,8 @@ def test_shared_prefix_equals_private_copies_bitwise(bs, d, vc, g, hkv):
     ctx = tuple(prefix + x for x in [1, bs + 1, 3 * bs + 5, 300, 77])
     w = dataclasses.replace(W.WORKLOADS["shared_prefix"], name="p9_small", num_seqs=S,
                             num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d, block_size=bs,
-                            v_codec=vc, ctx_kind="list", ctx=ctx, prefix=prefix, partition=part,
+                            v_codec=codecs(vc)[1], k_codec=codecs(vc)[0], ctx_kind="list", ctx=ctx,
+                            prefix=prefix, partition=part,
                             seed=3 * bs + d + g)
     P = prefix // bs
     n_blocks = runner.blocks_needed(w, W.context_lengths(w)) + S * P
@@ -484,7 +498,7 @@ def test_shared_prefix_equals_private_copies_bitwise(bs, d, vc, g, hkv):
         assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16)), f"partition {p}"
 
 
-@pytest.mark.parametrize("bs,vc", [(16, "i8"), (32, "i4")])
+@pytest.mark.parametrize("bs,vc", [(16, "i8"), (32, "i4"), (32, "k4i4")])
 def test_prefix_cache_end_to_end(bs, vc):
     """kv_seq_alloc_prefix: requests whose token ids share prefixes map the
     cached blocks and store only their uncached positions; the pool equals
@@ -504,7 +518,7 @@ def test_prefix_cache_end_to_end(bs, vc):
             base[:2 * bs], [1] * (2 * bs + 7), base[:4 * bs] + [2] * (2 * bs)]
     N = 64
     order = rng.permutation(N)
-    pool = KVPool(N, bs, h, d, vc, max_seqs=len(reqs), free_order=order)
+    pool = make_pool(N, bs, h, d, vc, max_seqs=len(reqs), free_order=order)
     model = A.BlockPoolModel(N, bs, len(reqs), order)
     opool = opool_for(N, h, bs, d, vc)
     shared_before = {}
@@ -546,15 +560,15 @@ def test_prefix_cache_end_to_end(bs, vc):
 
 # ---- swap to host memory (deepinsea "Swap") --------------------------------
 
-_POOL_ARRAYS = ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "tail_k", "tail_v")
+_POOL_ARRAYS = ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "tail_k", "tail_v", "k_zp")
 
 
-def _fill_random(rng, arrays, skip_zp):
-    """Seeded random bytes in every array (device or pinned host tensors);
-    returns numpy uint8 copies shaped [rows, bytes per row]."""
+def _fill_random(rng, arrays, used):
+    """Seeded random bytes in every array the codecs use (device or pinned
+    host tensors); returns numpy uint8 copies shaped [rows, bytes per row]."""
     exp = {}
     for n in _POOL_ARRAYS:
-        if n == "v_zp" and skip_zp:
+        if n.endswith("_zp") and n not in used:
             continue
         t = arrays[n]
         b = rng.integers(0, 256, t.numel() * t.element_size(), dtype=np.uint8)
@@ -566,7 +580,7 @@ def _fill_random(rng, arrays, skip_zp):
 def _apply_plan(plan, dev, host, h, bs):
     """The plan's definition on numpy byte arrays: whole rows of the block
     arrays; the first `rows` token rows of each head of a tail slot."""
-    block = ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp")
+    block = ("k_codes", "v_codes", "k_scale", "v_scale", "v_zp", "k_zp")
     for kind, src, dst, rows in plan:
         out = kind in (A.SWAP_BLOCK_OUT, A.SWAP_SLOT_OUT)
         a, b = (dev, host) if out else (host, dev)
@@ -580,7 +594,7 @@ def _apply_plan(plan, dev, host, h, bs):
 
 
 SWAP_SHAPES = [(16, 2, 64, "i8"), (32, 3, 128, "i4"), (16, 32, 128, "i8"), (32, 8, 64, "i4"),
-               (16, 4, 128, "fp8"), (32, 2, 64, "i8a")]
+               (16, 4, 128, "fp8"), (32, 2, 64, "i8a"), (32, 3, 128, "k4i4"), (16, 2, 64, "k4i8")]
 
 
 @pytest.mark.parametrize("bs,h,d,vc", SWAP_SHAPES)
@@ -594,12 +608,12 @@ def test_swap_moves_bytes_exactly(bs, h, d, vc):
     rng = np.random.default_rng(1000 + bs + h + d)
     N, S = 40, 8
     order = rng.permutation(N)
-    pool = KVPool(N, bs, h, d, vc, max_seqs=S, free_order=order)
+    pool = make_pool(N, bs, h, d, vc, max_seqs=S, free_order=order)
     model = A.BlockPoolModel(N, bs, S, order)
     pool.set_swap_space(24, 4)
     model.set_swap_space(24, 4)
-    dev = _fill_random(rng, pool.arrays, not pool.v_zp_used)
-    host = _fill_random(rng, pool.host_arrays, not pool.v_zp_used)
+    dev = _fill_random(rng, pool.arrays, zp_arrays(vc))
+    host = _fill_random(rng, pool.host_arrays, zp_arrays(vc))
     for s, n in {0: 3 * bs + 5, 1: 2 * bs, 2: 1, 3: 4 * bs - 1, 4: bs + 2}.items():
         assert pool.alloc(s, n) == model.alloc(s, n)
     copies = model.fork(0, 5)
@@ -648,7 +662,7 @@ def test_swap_moves_bytes_exactly(bs, h, d, vc):
     assert pool.stats() == model.stats()
 
 
-@pytest.mark.parametrize("bs,vc", [(16, "i8"), (32, "i4")])
+@pytest.mark.parametrize("bs,vc", [(16, "i8"), (32, "i4"), (16, "k4i4")])
 def test_swap_then_decode_append_end_to_end(bs, vc):
     """Sequences swapped out (their freed blocks overwritten by another
     owner) and back in decode as before, bit for bit; their next token's
@@ -670,7 +684,8 @@ def test_swap_then_decode_append_end_to_end(bs, vc):
     tab = pool.alloc(9, 4 * bs)
     assert tab == model.alloc(9, 4 * bs)
     idx = torch.tensor(tab)
-    pool.k_codes[idx] = torch.randint(-127, 128, pool.k_codes[idx].shape, dtype=torch.int8).cuda()
+    pool.k_codes.view(torch.uint8)[idx] = torch.randint(0, 256, pool.k_codes[idx].shape,
+                                                       dtype=torch.uint8).cuda()
     pool.v_codes.view(torch.uint8)[idx] = torch.randint(0, 256, pool.v_codes[idx].shape,
                                                        dtype=torch.uint8).cuda()
     pool.tail_k[pool.table(9)[2]] = torch.randn(pool.tail_k.shape[1:]).half().cuda()
@@ -720,6 +735,9 @@ MULTI_SHAPES = [
     (32, 128, "i8a", 8, 1),
     (32, 64, "i8", 16, 1),
     (16, 128, "i4", 7, 2),
+    (32, 128, "k4i4", 8, 2),
+    (16, 64, "k4i8", 1, 2),
+    (16, 128, "k4i4", 4, 1),
 ]
 
 
@@ -767,6 +785,7 @@ def test_multi_query_ragged(bs, d, vc, g, hkv):
     (32, 128, "i4", 8, 2, [2, 1, 2]),
     (32, 64, "i8", 16, 1, [1, 1]),
     (16, 64, "fp8", 4, 2, [4, 3, 1, 4]),
+    (32, 128, "k4i4", 8, 2, [2, 1, 2]),
 ])
 def test_multi_query_single_tile(bs, d, vc, g, hkv, ns):
     """Calls whose queries of one (sequence, KV head) fit one 16-query tile
@@ -919,7 +938,7 @@ def test_gqa_decode_scaled_v(bs, g, vc, kind):
     # the fused store + decode: every token but the last stored first
     dev = "cuda"
     S = len(ctx)
-    pool = KVPool(n_blocks, bs, hkv, d, vc, max_seqs=S, free_order=order)
+    pool = make_pool(n_blocks, bs, hkv, d, vc, max_seqs=S, free_order=order)
     for s, c in enumerate(ctx):
         pool.alloc(s, c - 1)
     mb = max((c + bs - 1) // bs for c in ctx)

@@ -21,14 +21,15 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import SmallCase, announce, assert_close, assert_pool_equal
+from gpu_util import SmallCase, announce, assert_close, assert_pool_equal, codecs
 
 pytestmark = pytest.mark.gpu
 
 BS, D, H = 16, 64, 8
 F16 = np.float16
-# (V codec name; K follows: FP8 exactly when V is)
-CODECS = ["i8", "i4", "i8a", "fp8"]
+# codec names (gpu_util.codecs): INT8 K with each V codec, FP8 K and V, and
+# INT4 K with INT4 or INT8 V
+CODECS = ["i8", "i4", "i8a", "fp8", "k4i4", "k4i8"]
 
 
 def _finite_positive_f16():
@@ -75,14 +76,25 @@ def _asym_tile(a, i, rng):
     return x.reshape(BS, D)
 
 
-def _absmax_case(vc, seed):
-    rng = np.random.default_rng(seed)
+def _sweep_tiles(spec, rng):
+    """One K and one V tile per positive finite fp16 absmax: symmetric tiles
+    for symmetric codecs, range-sweeping tiles for asymmetric ones."""
+    kc, vc = codecs(spec)
     amax = _finite_positive_f16()
-    ktiles = [_sym_tile(a, rng, vc != "fp8") for a in amax]
+    if kc == "i4":
+        ktiles = [_asym_tile(a, i + 1, rng) for i, a in enumerate(amax)]
+    else:
+        ktiles = [_sym_tile(a, rng, kc != "fp8") for a in amax]
     if vc in ("i4", "i8a"):
         vtiles = [_asym_tile(a, i, rng) for i, a in enumerate(amax)]
     else:
         vtiles = [_sym_tile(a, rng, vc == "i8") for a in amax]
+    return ktiles, vtiles
+
+
+def _absmax_case(vc, seed):
+    rng = np.random.default_rng(seed)
+    ktiles, vtiles = _sweep_tiles(vc, rng)
     hk, hv = _tiles_to_history(ktiles), _tiles_to_history(vtiles)
     n_blocks = hk.shape[0] // BS
     q = (rng.standard_normal((1, H, D)) * 2.0 ** -10).astype(F16)
@@ -96,17 +108,20 @@ def test_every_fp16_absmax(vc):
     case.store_all()
     assert_pool_equal(case.pool, case.opool)
     g = case.pool.k_scale.cpu().numpy().view(np.uint16)
+    kc_name, vc_name = codecs(vc)
     # the sweep reached subnormal scales and (INT8) codes clamped at +-127
     assert np.any((g > 0) & (g < 0x0400)), "no subnormal K scale"
-    if vc != "fp8":
+    if kc_name == "i8":
         kc = case.opool.k_codes
         assert np.any(np.abs(kc.astype(np.int32)) == 127)
-    if vc in ("i4", "i8a"):
+    if vc_name in ("i4", "i8a"):
         zp = case.opool.v_zp
-        top = 15 if vc == "i4" else 255
+        top = 15 if vc_name == "i4" else 255
         assert zp.min() == 0 and zp.max() == top
-        if vc == "i4":
+        if vc_name == "i4":
             assert len(np.unique(zp)) == 16, "every INT4 zero point"
+    if kc_name == "i4":
+        assert len(np.unique(case.opool.k_zp)) == 16, "every INT4 K zero point"
 
 
 @pytest.mark.parametrize("vc", CODECS)
@@ -120,12 +135,7 @@ def test_decode_over_every_absmax(vc):
     happens to be near zero)."""
     announce("absmax sweep decode", vc)
     rng = np.random.default_rng(21 + CODECS.index(vc))
-    amax = _finite_positive_f16()
-    ktiles = [_sym_tile(a, rng, vc != "fp8") for a in amax]
-    if vc in ("i4", "i8a"):
-        vtiles = [_asym_tile(a, i, rng) for i, a in enumerate(amax)]
-    else:
-        vtiles = [_sym_tile(a, rng, vc == "i8") for a in amax]
+    ktiles, vtiles = _sweep_tiles(vc, rng)
     hk, hv = _tiles_to_history(ktiles), _tiles_to_history(vtiles)
     per = 64 * BS
     n_seq = hk.shape[0] // per
@@ -180,18 +190,18 @@ def test_every_fp16_element(vc):
     """Every finite fp16 value inside tiles of fixed absmax (symmetric
     codecs) or fixed range (asymmetric), as K and as V."""
     announce("element sweep", vc)
+    kc_name, vc_name = codecs(vc)
     kind = "fp8" if vc == "fp8" else "i8"
-    ktiles = []
+    sym = []
     for a in SWEEP_ABSMAX[kind]:
-        ktiles += _element_tiles(_all_f16_upto(a), [a])
-    if vc in ("i4", "i8a"):
-        vtiles = []
-        for lo, hi in [(-1.0, 3.0), (-100.0, 1.0), (0.0, 7.5), (-2.0 ** -10, 2.0 ** -11), (-60000.0, 1000.0)]:
-            vals = _all_f16_upto(max(-lo, hi))
-            vals = vals[(vals.astype(np.float64) >= lo) & (vals.astype(np.float64) <= hi)]
-            vtiles += _element_tiles(vals, [lo, hi])
-    else:
-        vtiles = list(ktiles)
+        sym += _element_tiles(_all_f16_upto(a), [a])
+    asym = []
+    for lo, hi in [(-1.0, 3.0), (-100.0, 1.0), (0.0, 7.5), (-2.0 ** -10, 2.0 ** -11), (-60000.0, 1000.0)]:
+        vals = _all_f16_upto(max(-lo, hi))
+        vals = vals[(vals.astype(np.float64) >= lo) & (vals.astype(np.float64) <= hi)]
+        asym += _element_tiles(vals, [lo, hi])
+    ktiles = list(asym) if kc_name == "i4" else list(sym)
+    vtiles = list(asym) if vc_name in ("i4", "i8a") else list(sym)
     n = max(len(ktiles), len(vtiles))
     zero = np.zeros((BS, D), F16)
     ktiles += [zero] * (n - len(ktiles))

@@ -59,4 +59,9 @@ def test_pool_sizing():
     assert kv_size.pool_block_bytes(32, 128, 16, 8, 8, False) == 32 * 4100
     # INT4 V at bs 32: 32 * (4096 + 2048 + 5)
     assert kv_size.pool_block_bytes(32, 128, 32, 8, 4, True) == 32 * 6149
+    # INT4 K and V at bs 16, D 128: 16 x 128 x (4 + 4) / 8 = 2048 code bytes,
+    # two fp16 scales and two u8 zero points = 2054 per head; INT4 K with
+    # INT8 V: 16 x 128 x 12 / 8 = 3072 + 2 + 2 + 1 = 3077
+    assert kv_size.pool_block_bytes(32, 128, 16, 4, 4, True, True) == 32 * 2054
+    assert kv_size.pool_block_bytes(32, 128, 16, 4, 8, False, True) == 32 * 3077
     assert kv_size.pool_num_blocks(32 * 4100 * 1000 + 5, 32, 128, 16, 8, 8, False) == 1000

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import announce
+from gpu_util import announce, make_pool, zp_arrays
 
 pytestmark = pytest.mark.gpu
 
@@ -17,7 +17,6 @@ pytestmark = pytest.mark.gpu
 def _pools(bs, d, vc, hkv, ctx, seed):
     """Two pools holding the same ctx - 1 stored tokens per sequence with the
     current token reserved, plus the step's inputs."""
-    from paged_block_quantized_amd import KVPool
     S = len(ctx)
     rng = np.random.default_rng(seed)
     hk = [rng.standard_normal((c, hkv, d)).astype(np.float16) for c in ctx]
@@ -28,7 +27,7 @@ def _pools(bs, d, vc, hkv, ctx, seed):
     dev = torch.device("cuda")
     out = []
     for _ in range(2):
-        pool = KVPool(n_blocks, bs, hkv, d, vc, max_seqs=S, free_order=order)
+        pool = make_pool(n_blocks, bs, hkv, d, vc, max_seqs=S, free_order=order)
         for s, c in enumerate(ctx):
             pool.alloc(s, c - 1)
         tables, _, slots = pool.batch_tables(list(range(S)), max_blocks)
@@ -53,6 +52,8 @@ CASES = [
     (32, 128, "i4", 8),
     (32, 64, "fp8", 4),
     (16, 64, "i8a", 1),
+    (32, 128, "k4i4", 8),
+    (16, 64, "k4i8", 1),
 ]
 
 
@@ -81,8 +82,7 @@ def test_noalloc_matches_decode_append(bs, d, vc, g):
                                            cb, max(ctx), sm, part)
         torch.cuda.synchronize()
         assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16)), f"call {i}: outputs differ"
-        for name in ("k_codes", "v_codes", "k_scale", "v_scale", "tail_k", "tail_v") + \
-                (("v_zp",) if vc in ("i4", "i8a") else ()):
+        for name in ("k_codes", "v_codes", "k_scale", "v_scale", "tail_k", "tail_v") + zp_arrays(vc):
             assert torch.equal(pa.arrays[name], pb.arrays[name]), f"call {i}: {name} differs"
 
 
