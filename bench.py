@@ -171,7 +171,8 @@ def swap_plan_bytes(pool, plan):
     the held rows of each head of the tail slots (K and V, fp16)."""
     H, bs, D = pool.num_kv_heads, pool.block_size, pool.head_dim
     kb = H * bs * D
-    block = kb + (kb // 2 if pool.v_int4 else kb) + 4 * H + (H if pool.v_zp_used else 0)
+    block = ((kb // 2 if pool.k_int4 else kb) + (kb // 2 if pool.v_int4 else kb) + 4 * H
+             + (H if pool.v_zp_used else 0) + (H if pool.k_zp_used else 0))
     total = 0
     for kind, _, _, rows in plan:
         total += block if kind < 2 else 4 * H * rows * D
@@ -676,7 +677,7 @@ def main():
             "context": int(setup.ctx.max()) if w.ctx_kind == "fixed" else [int(setup.ctx.min()), int(setup.ctx.max())],
             "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
             "block_size": w.block_size,
-            "k_codec": {"i8": "int8_sym", "fp8": "fp8_e4m3"}[W.k_codec_of(w)],
+            "k_codec": {"i8": "int8_sym", "fp8": "fp8_e4m3", "i4": "int4_asym"}[W.k_codec_of(w)],
             "v_codec": {"i8": "int8_sym", "i4": "int4_asym", "i8a": "int8_asym", "fp8": "fp8_e4m3"}[w.v_codec],
             "partition": setup.partition, "shared_prefix": w.prefix,
             "pool_copies_rotated": R,

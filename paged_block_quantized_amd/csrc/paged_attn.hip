@@ -400,22 +400,24 @@ void attn_partition_mha(AttnArgs a) {
     };
 
     // Codes of one (block, head) tile: K from kp (the tile's first byte), V
-    // from vp; either may point into the pool or into the LDS copy of a tile.
-    auto load_tile = [&](const int8_t* kp, const uint8_t* vp, Regs& r) {
+    // from vp; either may point into the pool (nt: read once, non-temporal)
+    // or into the LDS copy of a tile.
+    auto load_tile = [&](auto nt, const int8_t* kp, const uint8_t* vp, Regs& r) {
+        constexpr bool NT = decltype(nt)::value;
         kp += lane * KB;
 #pragma unroll
-        for (int j = 0; j < NR; ++j) r.k[j] = *(const KReg*)(kp + j * KACC);
+        for (int j = 0; j < NR; ++j) r.k[j] = load_once<NT>((const KReg*)(kp + j * KACC));
 #pragma unroll
         for (int k = 0; k < DPL; ++k) {
             const uint8_t* row = vp + (lane + 64 * k) * VROW;
             if constexpr (VROW == 8) {
-                const u32x2 x = *(const u32x2*)row;
+                const u32x2 x = load_once<NT>((const u32x2*)row);
                 r.v[k][0] = x[0];
                 r.v[k][1] = x[1];
             } else {
 #pragma unroll
                 for (int c = 0; c < VROW / 16; ++c) {
-                    const u32x4 x = *(const u32x4*)(row + 16 * c);
+                    const u32x4 x = load_once<NT>((const u32x4*)(row + 16 * c));
                     r.v[k][4 * c + 0] = x[0];
                     r.v[k][4 * c + 1] = x[1];
                     r.v[k][4 * c + 2] = x[2];
@@ -448,7 +450,7 @@ void attn_partition_mha(AttnArgs a) {
 
         auto load = [&](int i, Regs& r) {
             const int64_t t = (int64_t)readlane(id, i) * H + h;
-            load_tile(a.k_codes + t * KT, a.v_codes + t * VT, r);
+            load_tile(std::true_type{}, a.k_codes + t * KT, a.v_codes + t * VT, r);
         };
 
         auto compute = [&](const Regs& r, int i) {
@@ -478,7 +480,7 @@ void attn_partition_mha(AttnArgs a) {
         }
         if (w == NW - 1) {
             Regs r;
-            load_tile((const int8_t*)s_tile, s_tile + KT, r);
+            load_tile(std::false_type{}, (const int8_t*)s_tile, s_tile + KT, r);
             compute_blk(r, b_end, bits_to_f16f((uint16_t)s_tscale[0]) * c2,
                         bits_to_f16f((uint16_t)s_tscale[1]) * vunit, code_bias<VC>((float)s_tscale[2]),
                         (float)(s_tscale[0] >> 16));
@@ -595,8 +597,12 @@ __device__ __forceinline__ void wait_vmem() {
 __device__ __forceinline__ void wait_lds() {
     __asm__ volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
 }
+// NT: the non-temporal cache policy (codes read once; the policy immediate
+// 2 is the instruction's nt bit)
+template <bool NT>
 __device__ __forceinline__ void load_to_lds(const void* src, void* lds_dst) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0,
+                                     NT && PBQ_NT_CODES ? 2 : 0);
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -712,6 +718,9 @@ void attn_partition_gqa(AttnArgs a) {
     constexpr int VROW = V4 ? BS / 2 : BS;     // V bytes per dim row
     constexpr int KT = BS * KROW;
     constexpr int VT = D * VROW;
+    // codes read once per call (a decode work group owns its (sequence, KV
+    // head)); multi-query and shared-prefix tiles reread them through L2
+    constexpr bool NTL = !MULTI && !SHARED;
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -876,17 +885,19 @@ void attn_partition_gqa(AttnArgs a) {
     // Codes of one 32-token step: the lane's K rows and V row come from the
     // tile of block 0 or block 1 of the step (bs 16), whose K and V tile
     // bases are given (pool or LDS copy).
-    auto load_step = [&](const int8_t* k0, const int8_t* k1, const uint8_t* v0, const uint8_t* v1, Raw& r) {
+    auto load_step = [&](auto nt, const int8_t* k0, const int8_t* k1, const uint8_t* v0, const uint8_t* v1,
+                         Raw& r) {
+        constexpr bool NT = decltype(nt)::value;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             const int8_t* kp = (BPS == 1 || !kblk[mt] ? k0 : k1) + krow[mt] * KROW + (K4 ? KCH : 16) * grp;
 #pragma unroll
-            for (int c = 0; c < NKC; ++c) r.k[mt][c] = *(const KChunk*)(kp + 64 * c);
+            for (int c = 0; c < NKC; ++c) r.k[mt][c] = load_once<NT>((const KChunk*)(kp + 64 * c));
         }
         const uint8_t* vp = (BPS == 1 || !my_blk ? v0 : v1) + vcol;
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-            r.v[t] = *(const VReg*)(vp + (16 * t + n16) * VROW);
+            r.v[t] = load_once<NT>((const VReg*)(vp + (16 * t + n16) * VROW));
         }
     };
 
@@ -1120,7 +1131,7 @@ void attn_partition_gqa(AttnArgs a) {
         for (int g = 0; g < NKL; ++g) {
             const int row0 = g * RPR;             // a load lies in one block
             if (!JOINT || g % NW == w)            // JOINT: the waves take turns
-                load_to_lds((row0 / BS ? kb1 : kb0) + (row0 % BS) * D + dma_k, sb + g * KREG);
+                load_to_lds<NTL>((row0 / BS ? kb1 : kb0) + (row0 % BS) * D + dma_k, sb + g * KREG);
         }
         const uint8_t* vb0 = a.v_codes + ((int64_t)id0 * H + kvh) * VT;
         const uint8_t* vb1 = a.v_codes + ((int64_t)id1 * H + kvh) * VT;
@@ -1129,7 +1140,7 @@ void attn_partition_gqa(AttnArgs a) {
             const uint8_t* src;
             if constexpr (VT >= 1024) src = ((1024 * g) / VT ? vb1 : vb0) + (1024 * g) % VT + dma_v;
             else src = (lane < 32 ? vb0 : vb1) + (dma_v & 511u);
-            if (!JOINT || (NKL + g) % NW == w) load_to_lds(src, sb + NKL * KREG + 1024 * g);
+            if (!JOINT || (NKL + g) % NW == w) load_to_lds<NTL>(src, sb + NKL * KREG + 1024 * g);
         }
     };
     // the lane's operands of the step in stage B (K rows: the second chunk
@@ -1196,7 +1207,8 @@ void attn_partition_gqa(AttnArgs a) {
         // wait for every outstanding load, the prefetch included.)
         auto load = [&](int i, Raw& r) {
             const int id0 = readlane(id_l, i * BPS), id1 = readlane(id_l, i * BPS + BPS - 1);
-            load_step(a.k_codes + ((int64_t)id0 * H + kvh) * KT, a.k_codes + ((int64_t)id1 * H + kvh) * KT,
+            load_step(std::integral_constant<bool, NTL>{}, a.k_codes + ((int64_t)id0 * H + kvh) * KT,
+                      a.k_codes + ((int64_t)id1 * H + kvh) * KT,
                       a.v_codes + ((int64_t)id0 * H + kvh) * VT, a.v_codes + ((int64_t)id1 * H + kvh) * VT, r);
         };
 
@@ -1319,7 +1331,7 @@ void attn_partition_gqa(AttnArgs a) {
             const uint8_t* lv = s_tile + KT;
             const bool pair = first != last;              // block `first` comes from the pool
             Raw r;
-            load_step(pair ? a.k_codes + t0 * KT : lk, lk, pair ? a.v_codes + t0 * VT : lv, lv, r);
+            load_step(std::false_type{}, pair ? a.k_codes + t0 * KT : lk, lk, pair ? a.v_codes + t0 * VT : lv, lv, r);
             const uint32_t ks0 = pair ? a.k_scale[t0] : s_tscale[0] & 0xFFFFu;
             const uint32_t vs0 = pair ? a.v_scale[t0] : s_tscale[1];
             const uint32_t z0 = pair ? (VZP ? a.v_zp[t0] : 0u) : s_tscale[2];

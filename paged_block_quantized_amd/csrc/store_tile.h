@@ -36,6 +36,16 @@
 #include "pbq_internal.h"
 #include "quantizer.h"
 
+// Cache policy of the store's row loads and code writes (1: non-temporal).
+// Off: with the decode's reads the store's mixed traffic ran slower
+// non-temporal (prefill 55 % against 62 % of the HBM peak).
+#ifndef PBQ_STORE_NT_LOADS
+#define PBQ_STORE_NT_LOADS 0
+#endif
+#ifndef PBQ_STORE_NT_WRITES
+#define PBQ_STORE_NT_WRITES 0
+#endif
+
 namespace pbq {
 
 // Pool arrays a tile store writes and the fp16 rows it reads.
@@ -116,7 +126,7 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
     f16x8 kx[DO_K ? NIT : 1];
     if constexpr (DO_K) {
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) kx[it] = *(const f16x8*)(row_src(a.tail_k, a.k, it * RPI + r_in) + col);
+        for (int it = 0; it < NIT; ++it) kx[it] = load_once<PBQ_STORE_NT_LOADS>((const f16x8*)(row_src(a.tail_k, a.k, it * RPI + r_in) + col));
     }
     const int64_t tile = (int64_t)phys * H + g;
     constexpr bool KZP = codec_has_zp(KC);
@@ -129,7 +139,7 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
 #pragma unroll
         for (int r = 0; r < BS; ++r) {
             const uint16_t* src = row_src(a.tail_v, a.v, r) + DPL * lane;
-            vw[r] = DPL == 2 ? *(const uint32_t*)src : (uint32_t)*src;
+            vw[r] = DPL == 2 ? load_once<PBQ_STORE_NT_LOADS>((const uint32_t*)src) : (uint32_t)load_once<PBQ_STORE_NT_LOADS>(src);
         }
     }
     if constexpr (DO_K) {
@@ -169,7 +179,7 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
                 w[1] = pack4_fp8((float)x[4] / sc, (float)x[5] / sc, (float)x[6] / sc, (float)x[7] / sc);
             }
             const int r = it * RPI + r_in;
-            if (wr) *(u32x2*)(dst + r * D + col) = u32x2{w[0], w[1]};
+            if (wr) store_once<PBQ_STORE_NT_WRITES>(u32x2{w[0], w[1]}, (u32x2*)(dst + r * D + col));
             if constexpr (LDS) *(u32x2*)(lds_k + r * D + col) = u32x2{w[0], w[1]};
         }
         if (wr && lane == 0) a.k_scale[tile] = s16;
@@ -210,7 +220,7 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
                 }
             }
             const int r = it * RPI + r_in;
-            if (wr) *(u32x2*)(dst + r * D + col) = u32x2{w[0], w[1]};
+            if (wr) store_once<PBQ_STORE_NT_WRITES>(u32x2{w[0], w[1]}, (u32x2*)(dst + r * D + col));
             if constexpr (LDS) *(u32x2*)(lds_k + r * D + col) = u32x2{w[0], w[1]};
         }
         if (wr && lane == 0) a.k_scale[tile] = s16;
@@ -262,7 +272,7 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
             }
             const int r = it * RPI + r_in;
             x = r < valid ? x : 0u;   // rows not held are zero bytes (their code would be zp)
-            if (wr) *(uint32_t*)(dst + r * (D / 2) + col / 2) = x;
+            if (wr) store_once<PBQ_STORE_NT_WRITES>(x, (uint32_t*)(dst + r * (D / 2) + col / 2));
             if constexpr (LDS) *(uint32_t*)(lds_k + r * (D / 2) + col / 2) = x;
         }
         if (wr && lane == 0) {
@@ -300,7 +310,7 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
 #pragma unroll
             for (int i = 0; i < BS / 16; ++i) {
                 const u32x4 x = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-                if (wr) *(u32x4*)(drow + 4 * i) = x;
+                if (wr) store_once<PBQ_STORE_NT_WRITES>(x, (u32x4*)(drow + 4 * i));
                 if constexpr (LDS) *(u32x4*)(lrow + 4 * i) = x;
             }
         }
@@ -347,7 +357,7 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
 #pragma unroll
             for (int i = 0; i < BS / 16; ++i) {
                 const u32x4 x = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-                if (wr) *(u32x4*)(drow + 4 * i) = x;
+                if (wr) store_once<PBQ_STORE_NT_WRITES>(x, (u32x4*)(drow + 4 * i));
                 if constexpr (LDS) *(u32x4*)(lrow + 4 * i) = x;
             }
         }
@@ -407,7 +417,7 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
 #pragma unroll
                 for (int i = 0; i < BS / 16; ++i) {
                     const u32x4 x = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-                    if (wr) *(u32x4*)(drow + 4 * i) = x;
+                    if (wr) store_once<PBQ_STORE_NT_WRITES>(x, (u32x4*)(drow + 4 * i));
                     if constexpr (LDS) *(u32x4*)(lrow + 4 * i) = x;
                 }
             }
@@ -444,13 +454,13 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
                 uint32_t* drow = (uint32_t*)(dst + (DPL * lane + k) * (BS / 2));
                 uint32_t* lrow = LDS ? (uint32_t*)(lds_v + (DPL * lane + k) * (BS / 2)) : nullptr;
                 if constexpr (BS == 16) {
-                    if (wr) *(u32x2*)drow = u32x2{w[0], w[1]};
+                    if (wr) store_once<PBQ_STORE_NT_WRITES>(u32x2{w[0], w[1]}, (u32x2*)drow);
                     if constexpr (LDS) *(u32x2*)lrow = u32x2{w[0], w[1]};
                 } else {
 #pragma unroll
                     for (int i = 0; i < BS / 32; ++i) {
                         const u32x4 x = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-                        if (wr) *(u32x4*)(drow + 4 * i) = x;
+                        if (wr) store_once<PBQ_STORE_NT_WRITES>(x, (u32x4*)(drow + 4 * i));
                         if constexpr (LDS) *(u32x4*)(lrow + 4 * i) = x;
                     }
                 }

@@ -7,9 +7,9 @@
 //
 // Mapping: each wavefront takes a contiguous run of the tile list and reads
 // it as a stream of 1 KiB chunks (16 bytes per lane, contiguous across the
-// wave, as the decode's loads are), eight chunks in flight per wave; the
-// tile ids of the wave's next 64 tiles are gathered into lanes once and
-// read back with readlane.
+// wave, non-temporal, as the decode's loads are), eight chunks in flight per
+// wave; the tile ids of the wave's next 64 tiles are gathered into lanes
+// once and read back with readlane.
 
 #include "device_common.h"
 #include "pbq_internal.h"
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(64 * kWaves) void stream_read_kernel(StreamReadArgs
                 const int cc = min(c + k, nch - 1);   // the last batch re-reads its final chunk
                 const int ti = cc >> sh;
                 const int64_t tile = a.order ? (int64_t)readlane(id, ti) : wave + (base + ti) * n_waves;
-                v[k] = *(const u32x4*)(a.src + (((tile << sh) + (cc & ((1 << sh) - 1))) << 10) + 16 * lane);
+                v[k] = load_once<true>((const u32x4*)(a.src + (((tile << sh) + (cc & ((1 << sh) - 1))) << 10) + 16 * lane));
             }
 #pragma unroll
             for (int k = 0; k < kInflight; ++k) acc ^= c + k < nch ? v[k] : u32x4{0u, 0u, 0u, 0u};

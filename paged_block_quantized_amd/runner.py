@@ -20,6 +20,16 @@ from . import workloads as W
 from .pool import KVPool
 
 
+def code_bits(w: W.Workload):
+    """(K bits, V bits, metadata bytes per (block, head)) of the workload's
+    codecs: two fp16 scales, plus a u8 zero point for each asymmetric codec."""
+    kc = W.k_codec_of(w)
+    kbits = 4 if kc == "i4" else 8
+    vbits = 4 if w.v_codec == "i4" else 8
+    meta = 2 + 2 + (1 if w.v_codec in ("i4", "i8a") else 0) + (1 if kc == "i4" else 0)
+    return kbits, vbits, meta
+
+
 def balanced_order(ctx: np.ndarray, block: int = 64) -> np.ndarray:
     """Batch order for a decode step: sequence ids sorted by context length,
     longest first, with every other run of `block` reversed.  The GPU hands
@@ -217,14 +227,13 @@ def decode_bytes(w: W.Workload, ctx: np.ndarray) -> int:
     valid token, the metadata of every block read, Q, O, the block tables and
     the context lengths; a shared prefix counted once."""
     S, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
-    vbits = 4 if w.v_codec == "i4" else 8
-    meta = 2 + 2 + (1 if w.v_codec in ("i4", "i8a") else 0)
+    kbits, vbits, meta = code_bits(w)
     tokens = int(np.sum(ctx))
     blocks = int(np.sum((ctx + bs - 1) // bs))
     if w.prefix:
         tokens -= (S - 1) * w.prefix
         blocks -= (S - 1) * (w.prefix // bs)
-    codes = tokens * Hkv * D * (8 + vbits) // 8
+    codes = tokens * Hkv * D * (kbits + vbits) // 8
     meta_b = blocks * Hkv * meta
     qo = 2 * S * Hq * D * 2
     tables = int(np.sum((ctx + bs - 1) // bs)) * 4 + S * 4
@@ -242,14 +251,13 @@ def store_step_bytes(w: W.Workload, ctx: np.ndarray, rewrite_tiles: bool = True)
     written (its K row and its entry of every V dim row), with the block's
     metadata read instead of written."""
     Hkv, D, bs = w.num_kv_heads, w.head_dim, w.block_size
-    vbits = 4 if w.v_codec == "i4" else 8
-    meta = 2 + 2 + (1 if w.v_codec in ("i4", "i8a") else 0)
+    kbits, vbits, meta = code_bits(w)
     rows = (ctx - 1) % bs + 1                    # rows the block holds after the store
     read = int(np.sum(rows)) * Hkv * D * 2 * 2
     if rewrite_tiles:
-        write = len(ctx) * Hkv * (bs * D * (8 + vbits) // 8 + meta)
+        write = len(ctx) * Hkv * (bs * D * (kbits + vbits) // 8 + meta)
     else:
-        write = len(ctx) * Hkv * (D * (8 + vbits) // 8 + meta)   # metadata read, not written
+        write = len(ctx) * Hkv * (D * (kbits + vbits) // 8 + meta)   # metadata read, not written
     tail_write = int(np.sum(rows < bs)) * Hkv * D * 2 * 2
     return read + write + tail_write + len(ctx) * 4 * 4
 
@@ -321,10 +329,9 @@ def multi_bytes(w: W.Workload, ctx: np.ndarray) -> int:
     """Algorithmic HBM bytes of one multi-query pass: every stored token's
     codes and block metadata once, the query and output rows, the tables."""
     S, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
-    vbits = 4 if w.v_codec == "i4" else 8
-    meta = 2 + 2 + (1 if w.v_codec in ("i4", "i8a") else 0)
+    kbits, vbits, meta = code_bits(w)
     blocks = int(np.sum((ctx + bs - 1) // bs))
-    return (int(np.sum(ctx)) * Hkv * D * (8 + vbits) // 8 + blocks * Hkv * meta
+    return (int(np.sum(ctx)) * Hkv * D * (kbits + vbits) // 8 + blocks * Hkv * meta
             + 2 * S * w.q_len * Hq * D * 2 + blocks * 4 + (2 * S + 1) * 4)
 
 
@@ -372,11 +379,10 @@ def prefill_store_bytes(w: W.Workload) -> int:
     workload: the fp16 K and V rows read, the codes and per-(block, head)
     metadata written, the block tables read."""
     S, T, Hkv, D, bs = w.num_seqs, w.ctx[0], w.num_kv_heads, w.head_dim, w.block_size
-    vbits = 4 if w.v_codec == "i4" else 8
-    meta = 2 + 2 + (1 if w.v_codec in ("i4", "i8a") else 0)
+    kbits, vbits, meta = code_bits(w)
     tok = S * T
     blocks = S * ((T + bs - 1) // bs)
-    return tok * Hkv * D * 2 * 2 + tok * Hkv * D * (8 + vbits) // 8 + blocks * Hkv * meta + blocks * 4
+    return tok * Hkv * D * 2 * 2 + tok * Hkv * D * (kbits + vbits) // 8 + blocks * Hkv * meta + blocks * 4
 
 
 @dataclass

@@ -88,3 +88,15 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_int4_k_decode_bytes():
+    # llama7b shape with INT4 K and V: 4 + 4 bits per (token, head, dim) and
+    # per block and head two fp16 scales and two u8 zero points; INT4 K with
+    # INT8 V: 12 bits and one zero point
+    ctx = np.array([4096] * 32)
+    qo_tables = 2 * 32 * 32 * 128 * 2 + 32 * 256 * 4 + 32 * 4
+    w44 = W.WORKLOADS["llama7b_k4v4"]
+    assert runner.decode_bytes(w44, ctx) == 32 * 4096 * 32 * 128 + 32 * 256 * 32 * 6 + qo_tables
+    w48 = W.WORKLOADS["llama7b_k4v8"]
+    assert runner.decode_bytes(w48, ctx) == 32 * 4096 * 32 * 192 + 32 * 256 * 32 * 5 + qo_tables
