@@ -585,6 +585,33 @@ void attn_partition_mha(AttnArgs a) {
 #ifndef PBQ_GQA_STAGES
 #define PBQ_GQA_STAGES 2
 #endif
+// Single-pass grouped-query decode in paired groups (see attn_partition_gqa).
+#ifndef PBQ_GQA_PAIR
+#define PBQ_GQA_PAIR 1
+#endif
+// Most sequences a paired group ranks by context length (each of its
+// threads ranks one sequence, or half of one's keys, against all S).
+#ifndef PBQ_PAIR_RANK_MAX
+#define PBQ_PAIR_RANK_MAX 256
+#endif
+constexpr int kPairRankMax = PBQ_PAIR_RANK_MAX;
+// Loop steps the two waves of a paired group that quantize the stored tiles
+// and take the stored steps give up to the other two.
+#ifndef PBQ_PAIR_HANDICAP
+#define PBQ_PAIR_HANDICAP 2
+#endif
+// LDS of a paired group (two per CU must fit): per wave two stages of a
+// step's codes (or a result slot, if larger), one more slot, and with the
+// fused store both sequences' stored K and V tiles
+constexpr int kPairLdsMax = 76 * 1024;   // the ranking's arrays need a few KiB more
+template <int BS, int D, int CP, bool FUSED>
+constexpr int gqa_pair_lds() {
+    constexpr bool V4 = codec_packed4(CP % 4), K4 = codec_packed4(CP / 4);
+    constexpr int stg = (32 * D / 1024) * (1024 + 64) + (32 / BS) * D * (V4 ? BS / 2 : BS);
+    constexpr int slot = 16 * (D + 4) * 4 + 16 * 8;
+    constexpr int part = ((PBQ_GQA_STAGES * stg > slot ? PBQ_GQA_STAGES * stg : slot) + 15) / 16 * 16;
+    return 4 * part + slot + (FUSED ? 2 * (BS * (K4 ? D / 2 : D) + D * (V4 ? BS / 2 : BS)) : 0);
+}
 
 // Waits for the direct-to-LDS loads are the kernel's own: the compiler cannot
 // tell the stages apart and would wait for every such load in flight.
@@ -673,8 +700,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // that of two waves (no spills into AGPRs).  Two-wave multi-query groups use
 // at most about 26 KiB (a shared three-stage area, or a merge through one
 // wave's slot), room for three waves per SIMD, and get that register budget.
-template <int D, int CP, bool FUSED, bool MULTI, int NW>
+template <int D, int CP, bool FUSED, bool MULTI, int NW, bool PAIR>
 constexpr int gqa_waves_per_eu() {
+    if (PAIR) return 2;   // two four-wave groups per CU
     if (MULTI && NW == 2) return 3;
     return MULTI || (!FUSED && D == 128 && !codec_packed4(CP % 4)) ? 2 : PBQ_GQA_WAVES_PER_EU;
 }
@@ -686,8 +714,20 @@ constexpr int gqa_waves_per_eu() {
 // groups (single-pass launches) stream every step through one shared
 // staging area, each wave for its own two tiles (JOINT); the four-wave
 // groups of split partitions divide the steps and merge.
-template <int BS, int D, int CP, int NW, bool FUSED, bool SHARED = false, bool MULTI = false, int TPW = 1>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(gqa_waves_per_eu<D, CP, FUSED, MULTI, NW>())))
+//
+// PAIR (single-pass decode): each streaming wave's rate is set by its own
+// loads in flight, so the step ends when the wave with the most steps does.
+// A four-wave group takes two sequences -- those ranked `pair` and S - 1 -
+// pair by context length (ties by index), so a long one with a short one --
+// for one (KV head, query tile), and its waves split the two sequences'
+// steps, laid end to end, into four equal runs.  The wave whose run crosses
+// from the first sequence to the second leaves its first result in LDS; at
+// the end waves 1 and 3 each merge one sequence's results and write its
+// output.  With the fused store each wave loads one tile's exact rows (K or
+// V of either sequence) before its loop and quantizes them after it.
+template <int BS, int D, int CP, int NW, bool FUSED, bool SHARED = false, bool MULTI = false, int TPW = 1,
+          bool PAIR = false>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(gqa_waves_per_eu<D, CP, FUSED, MULTI, NW, PAIR>())))
 void attn_partition_gqa(AttnArgs a) {
     constexpr int KC = CP / 4, VC = CP % 4;
     constexpr bool V4 = codec_packed4(VC);
@@ -698,6 +738,7 @@ void attn_partition_gqa(AttnArgs a) {
     static_assert(!(MULTI && (FUSED || SHARED)), "multi-query launches store nothing and share nothing");
     static_assert(BS == 16 || BS == 32, "block size");
     static_assert(TPW == 1 || (MULTI && TPW == 2), "two tiles per wave only for multi-query launches");
+    static_assert(!PAIR || (!MULTI && !SHARED && NW == 4), "paired groups: single-pass decode, four waves");
     constexpr int QT = 16 * TPW;               // queries per wave
     // JOINT: both waves stream every step of the partition from one staging
     // area, wave w for queries w QT .. of the group (no merge of waves)
@@ -705,8 +746,13 @@ void attn_partition_gqa(AttnArgs a) {
     constexpr bool JOINT = MULTI && NW == 2 && TPW == 2 && PBQ_MULTI_JOINT_STAGE && !K4;
     constexpr int QW = JOINT ? NW * QT : QT;   // queries per work group
     constexpr bool STAGED = K4 ? false
+                          : PAIR ? true
                           : FUSED ? PBQ_GQA_STAGE_FUSED
                           : (JOINT ? true : (MULTI && !V4 ? PBQ_MULTI_BYTEV_STAGE : PBQ_GQA_STAGE));
+    // PAIR with the fused store: the stored tiles have LDS of their own (the
+    // launcher pairs only when it fits)
+    constexpr bool EARLY = PAIR && FUSED;
+    static_assert(!PAIR || gqa_pair_lds<BS, D, CP, FUSED>() <= kPairLdsMax, "two paired groups per CU");
     constexpr int KS = D / 32;                 // QK k-steps
     constexpr int DT = D / 16;                 // PV dim tiles
     constexpr int KROW = K4 ? D / 2 : D;       // K bytes per token row
@@ -743,8 +789,89 @@ void attn_partition_gqa(AttnArgs a) {
         p = work % P;
         tile = (work / P) % NT;
         s = work / (P * NT);
+    } else if constexpr (PAIR) {
+        p = 0;
+        tile = blockIdx.y;
+        s = 0;   // the pair's first sequence, below
     } else {
         grid_coords(p, tile, s);
+    }
+    // PAIR: the group's sequences, those of ranks pair and S - 1 - pair when
+    // the sequences are ordered by context length, longest first (ties by
+    // index; beyond kPairRankMax sequences, the call's own order).  The
+    // first is at least as long as the second; an odd S leaves the middle
+    // rank alone (seq_b -1).
+    int seq_a = 0, seq_b = -1;
+    // PAIR: the two sequences' context lengths and (fused) tail slots
+    int pctx[2] = {0, 0}, pslot[2] = {0, 0};
+    if constexpr (PAIR) {
+        const int S = a.num_seqs, pr = blockIdx.z;
+        if (S <= kPairRankMax) {
+            // Each thread reads one sequence's length (and, fused, its tail
+            // slot) into LDS.  Keys: the length (clamped; only
+            // the pairing depends on it), then the reversed index, so that
+            // all keys differ and the rank is the number of larger keys; two
+            // threads per sequence when S <= 128, each counting over half of
+            // the keys (four at a time).
+            __shared__ int s_pair[2];
+            __shared__ __align__(16) uint32_t s_key[kPairRankMax];
+            __shared__ int s_len[kPairRankMax];
+            __shared__ int s_half[2][kPairRankMax / 2];
+            __shared__ int s_slot[FUSED ? kPairRankMax : 1];
+            const int S4 = (S + 3) & ~3;
+            for (int i = threadIdx.x; i < S4; i += 64 * NW) {
+                const int len = i < S ? a.context_lens[i] : 0;
+                s_key[i] = i < S ? ((uint32_t)min(len, (1 << 22) - 1) << 9) | (uint32_t)(511 - i) : 0u;
+                if (i < S) {
+                    s_len[i] = len;
+                    if constexpr (FUSED) s_slot[i] = a.tail_slots[i];
+                }
+            }
+            if (threadIdx.x < 2) s_pair[threadIdx.x] = -1;
+            __syncthreads();
+            const bool split = S <= 128;
+            const int i = split ? threadIdx.x & 127 : threadIdx.x;
+            const int half = split ? threadIdx.x >> 7 : 0;
+            const int j0 = split ? half * (S4 / 8) * 4 : 0;            // S4 / 2 rounded down to 4
+            const int j1 = split && half == 0 ? (S4 / 8) * 4 : S4;
+            int cnt = 0;
+            if (i < S) {
+                const uint32_t ki = s_key[i];
+#pragma unroll 4
+                for (int j = j0; j < j1; j += 4) {
+                    const u32x4 k4 = *(const u32x4*)&s_key[j];
+                    cnt += (k4[0] > ki) + (k4[1] > ki) + (k4[2] > ki) + (k4[3] > ki);
+                }
+            }
+            if (split) {
+                if (i < S) s_half[half][i] = cnt;   // i < 128
+                __syncthreads();
+                if (half == 0 && i < S) cnt += s_half[1][i];
+            }
+            if (i < S && half == 0) {
+                if (cnt == pr) s_pair[0] = i;
+                if (cnt == S - 1 - pr && cnt != pr) s_pair[1] = i;
+            }
+            __syncthreads();
+            seq_a = s_pair[0];
+            seq_b = s_pair[1];
+            pctx[0] = s_len[seq_a];
+            if (seq_b >= 0) pctx[1] = s_len[seq_b];
+            if constexpr (FUSED) {
+                pslot[0] = s_slot[seq_a];
+                if (seq_b >= 0) pslot[1] = s_slot[seq_b];
+            }
+        } else {
+            seq_a = pr;
+            seq_b = S - 1 - pr != pr ? S - 1 - pr : -1;
+            pctx[0] = a.context_lens[seq_a];
+            if (seq_b >= 0) pctx[1] = a.context_lens[seq_b];
+            if constexpr (FUSED) {
+                pslot[0] = a.tail_slots[seq_a];
+                if (seq_b >= 0) pslot[1] = a.tail_slots[seq_b];
+            }
+        }
+        s = seq_a;
     }
     if constexpr (!SHARED && !MULTI) p += a.shared_parts;   // shared partitions ran in their own launch
     const int q_row0 = MULTI ? a.cu_q[s] : 0;               // the sequence's first query row
@@ -757,11 +884,11 @@ void attn_partition_gqa(AttnArgs a) {
     const int ht = tile % n_ht_grid;
     if (MULTI && ht >= n_ht) return;
     const int H = a.num_kv_heads;
-    const int ctx_seq = SHARED ? a.shared_tokens : a.context_lens[s];
+    int ctx_seq = SHARED ? a.shared_tokens : PAIR ? pctx[0] : a.context_lens[s];
     // position of query token 0, and the tokens this tile's last query sees
     const int pos0 = ctx_seq - n_tok;
-    const int ctx = MULTI ? pos0 + (min(NQ, ht * QW + QW) - 1) / G + 1 : ctx_seq;
-    const int nblk = (ctx + BS - 1) / BS;
+    int ctx = MULTI ? pos0 + (min(NQ, ht * QW + QW) - 1) / G + 1 : ctx_seq;
+    int nblk = (ctx + BS - 1) / BS;
     const int PB = a.partition_blocks;
     const int nparts = max(1, (nblk + PB - 1) / PB);
     if (p >= nparts) return;
@@ -770,8 +897,8 @@ void attn_partition_gqa(AttnArgs a) {
     const int nblk_seq = (ctx_seq + BS - 1) / BS;
     const bool direct = SHARED ? false : (MULTI ? nblk_seq <= PB : nparts == 1);
     const int tok0 = p * PB * BS;
-    const int tok1 = min(tok0 + PB * BS, ctx);
-    const int nsteps = (tok1 - tok0 + 31) / 32;
+    int tok1 = min(tok0 + PB * BS, ctx);
+    int nsteps = (tok1 - tok0 + 31) / 32;
     const int q0 = ht * QW + (JOINT ? w * QT : 0);   // the wave's first query
     const int nheads = max(0, min(QT, NQ - q0));      // the wave's queries (tile T: 16 T ..)
     // row of query ht * QT + i in q and out ([rows, Hq, D])
@@ -790,7 +917,7 @@ void attn_partition_gqa(AttnArgs a) {
         qlim[T] = MULTI && 16 * T + n16 < nheads ? pos0 + (q0 + 16 * T + n16) / G : ctx - 1;
     const int mask_from = MULTI ? pos0 + q0 / G + 1 : ctx;
     const int blk0 = tok0 / BS;
-    const int blk_end = (tok1 + BS - 1) / BS;
+    int blk_end = (tok1 + BS - 1) / BS;
 
     // Q as the B operand of the QK product.  Byte-coded K: the contraction
     // index of k-step j, lane group grp, element i is head dim 64 (j/2) +
@@ -801,6 +928,7 @@ void attn_partition_gqa(AttnArgs a) {
     // whose nibbles come out as dims 8j + (0, 2, 4, 6, 1, 3, 5, 7).
     f16x8v qop[TPW][KS];
     float qsum[TPW], qbias[TPW];
+    auto load_q = [&]() {   // (again for a paired group's second sequence)
 #pragma unroll
     for (int T = 0; T < TPW; ++T) {
         float qs = 0.f;
@@ -820,6 +948,8 @@ void attn_partition_gqa(AttnArgs a) {
         qsum[T] = qs;
         qbias[T] = code_bias<KC>(0.f) * qs;   // INT4 K: per block, from its zero point
     }
+    };
+    load_q();
 
     const float c2 = a.sm_scale * kLog2e * code_unit<KC>();
     constexpr float vunit = code_unit<VC>();
@@ -864,6 +994,40 @@ void attn_partition_gqa(AttnArgs a) {
     };
 
     const int32_t* tab = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    // PAIR: switch the per-sequence state to sequence seq of context c (one
+    // pass: tokens 0 .. c - 1), and the online softmax state
+    auto set_unit = [&](int seq, int c) {
+        s = seq;
+        ctx_seq = ctx = c;
+        nblk = (c + BS - 1) / BS;
+        tok1 = min(tok0 + PB * BS, c);
+        nsteps = (tok1 - tok0 + 31) / 32;
+        blk_end = (tok1 + BS - 1) / BS;
+        tab = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
+    };
+    auto reset_state = [&]() {
+#pragma unroll
+        for (int T = 0; T < TPW; ++T) {
+            m[T] = -INFINITY;
+            l[T] = 0.f;
+#pragma unroll
+            for (int t = 0; t < DT; ++t) acc[T][t] = (f32x4)0.f;
+        }
+        vF = 0;
+        vmul = 1.f;
+    };
+    // lanes of one head split its tokens by group: sum their partial sums,
+    // and undo the V-scale normaliser (times the codec's unit)
+    auto finish_state = [&]() {
+        const float vb = __builtin_amdgcn_ldexpf(vunit, vF - 15 - kVTop);
+#pragma unroll
+        for (int T = 0; T < TPW; ++T) {
+            l[T] += shfl_xor_f(l[T], 16);
+            l[T] += shfl_xor_f(l[T], 32);
+#pragma unroll
+            for (int t = 0; t < DT; ++t) acc[T][t] *= vb;
+        }
+    };
     // the block (within a step) whose K row this lane loads for tile mt, and
     // the row inside it: token 8(n16/4) + kappa(4mt + n16%4)
     int krow[2], kblk[2];
@@ -1045,10 +1209,70 @@ void attn_partition_gqa(AttnArgs a) {
     // barrier, wave NW - 1 computes the last step with the last block read
     // from LDS while waves 0 and 1 write the tiles to the pool (only the first
     // 16-head tile of a KV head writes).
-    __shared__ __align__(16) uint8_t s_tile[FUSED ? KT + VT : 16];
-    __shared__ uint32_t s_tscale[5];
+    __shared__ __align__(16) uint8_t s_tile[FUSED && !PAIR ? KT + VT : 16];
+    __shared__ uint32_t s_tscale[PAIR ? 10 : 5];   // PAIR: five per sequence
+    __shared__ __align__(16) uint8_t s_ptile[EARLY ? 2 * (KT + VT) : 16];   // PAIR: each sequence's K, V tiles
     const bool fused = FUSED && nblk > 0;   // one partition: this group holds the last block
-    if (fused && w < 2) {
+    // PAIR: the second sequence, and the tile whose exact rows this wave
+    // loads now and quantizes after its loop (wave w: K for even w, else V,
+    // of the first sequence for w < 2, else of the second)
+    const int ctx_b = pctx[1];
+    const bool fused_b = FUSED && ctx_b > 0;
+    // PAIR, fused: wave 0 loads the first sequence's stored tile rows (K and
+    // V), wave 3 the second's; each quantizes them once its first steps'
+    // codes are in flight, and takes that sequence's stored step itself
+    TileRows<BS> trows_k, trows_v;
+    int t_seq = -1, t_ctx = 0, t_slot = 0, t_phys = 0;
+    if constexpr (PAIR && FUSED) {
+        const int u = w == 0 ? 0 : w == NW - 1 ? 1 : -1;
+        if (u >= 0) {
+            t_seq = u ? seq_b : seq_a;
+            t_ctx = pctx[u];
+            t_slot = pslot[u];
+        }
+        if (t_seq >= 0 && t_ctx > 0) {
+            // the rows need only the slot; the last block's id (for the
+            // pool's previous scale bits, read later) is loaded beside them
+            const TileStoreArgs t = fused_store_args(a);
+            const int last = (t_ctx - 1) / BS;
+            t_phys = a.block_tables[(int64_t)t_seq * a.max_blocks_per_seq + last];
+            trows_k = load_tile_rows<BS, D, CP, false, true>(t, kvh, t_slot, t_seq, t_ctx - 1, t_ctx, last, 0);
+            trows_v = load_tile_rows<BS, D, CP, false, false>(t, kvh, t_slot, t_seq, t_ctx - 1, t_ctx, last, 0);
+        } else {
+            t_seq = -1;
+        }
+    }
+    // PAIR: both sequences' query operands, in registers
+    const int nblk_a = nblk, nblk_b = (ctx_b + BS - 1) / BS;
+    f16x8v qop_a[TPW][KS], qop_b[TPW][KS];
+    float qsum_a[TPW], qsum_b[TPW], qbias_a[TPW], qbias_b[TPW];
+    if constexpr (PAIR) {
+#pragma unroll
+        for (int T = 0; T < TPW; ++T) {
+#pragma unroll
+            for (int k = 0; k < KS; ++k) qop_a[T][k] = qop_b[T][k] = qop[T][k];
+            qsum_a[T] = qsum_b[T] = qsum[T];
+            qbias_a[T] = qbias_b[T] = qbias[T];
+        }
+        if (seq_b >= 0) {
+            s = seq_b;
+            load_q();
+#pragma unroll
+            for (int T = 0; T < TPW; ++T) {
+#pragma unroll
+                for (int k = 0; k < KS; ++k) {
+                    qop_b[T][k] = qop[T][k];
+                    qop[T][k] = qop_a[T][k];
+                }
+                qsum_b[T] = qsum[T];
+                qbias_b[T] = qbias[T];
+                qsum[T] = qsum_a[T];
+                qbias[T] = qbias_a[T];
+            }
+            s = seq_a;
+        }
+    }
+    if (!PAIR && fused && w < 2) {
         const TileStoreArgs t = fused_store_args(a);
         const int last = nblk - 1;
         const int slot = a.tail_slots[s], phys = tab[last];
@@ -1082,6 +1306,10 @@ void attn_partition_gqa(AttnArgs a) {
     const int q = (n_loop + 2 * hc) / NW, rem = (n_loop + 2 * hc) % NW;
     const int w_start = JOINT ? 0 : w * q + min(w, rem) - min(w, 2) * hc;
     const int w_stop = JOINT ? n_loop : w_start + q + (w < rem ? 1 : 0) - (w < 2 ? hc : 0);
+    // PAIR: the loop steps of both sequences (with the fused store, each
+    // one's last step comes after the loop), laid end to end
+    const int n_a = fused ? nsteps - 1 : nsteps;
+    const int n_b = PAIR && seq_b >= 0 ? (fused_b ? (ctx_b + 31) / 32 - 1 : (ctx_b + 31) / 32) : 0;
 
     // Staging area of the direct-to-LDS path, per wave (one for the group in
     // the joint mode) and stage: the step's 32 K rows as 1 KiB loads (RPR
@@ -1097,14 +1325,21 @@ void attn_partition_gqa(AttnArgs a) {
     constexpr int STG = NKL * KREG + BPS * VT;
     static_assert(SD == 2 || SD == 3, "stages");
     static_assert(BPS * VT % 1024 == 0 && (VT % 1024 == 0 || (BPS == 2 && VT == 512)), "V tile loads");
-    constexpr int STAGE_BYTES = STAGED ? (JOINT ? 1 : NW) * SD * STG : 16;
+    // PAIR: wave w's part of the area holds its stages, then (after its
+    // loop) its result slot (QT rows of D + 4 floats, then QT (max, sum)
+    // pairs); one more slot, for the first result of the wave whose run
+    // crosses to the second sequence, follows the parts
+    constexpr int SLOT = QT * (D + 4) * 4 + QT * 8;
+    constexpr int PART_MIN = SLOT;
+    constexpr int PART = PAIR ? ((STAGED && SD * STG > PART_MIN ? SD * STG : PART_MIN) + 15) / 16 * 16 : SD * STG;
+    constexpr int STAGE_BYTES = PAIR ? NW * PART + SLOT : STAGED ? (JOINT ? 1 : NW) * SD * STG : 16;
     // two-wave multi-query groups merge through one wave's slot (the other
     // wave merges from its registers), which leaves LDS room for a third
     // work group of waves per SIMD
     constexpr bool HALF = MULTI && NW == 2 && !JOINT;
-    constexpr int ACC_BYTES = JOINT ? 16 : (HALF ? 1 : NW) * QT * (D + 4) * 4;
+    constexpr int ACC_BYTES = JOINT || PAIR ? 16 : (HALF ? 1 : NW) * QT * (D + 4) * 4;
     __shared__ __align__(16) uint8_t s_stage[STAGE_BYTES > ACC_BYTES ? STAGE_BYTES : ACC_BYTES];
-    uint8_t* const my_stage = s_stage + (JOINT ? 0 : w * SD * STG);   // w is wave-uniform
+    uint8_t* const my_stage = s_stage + (JOINT ? 0 : w * PART);   // w is wave-uniform
     // lane offsets: where this lane's 16 bytes of a K load come from (row
     // lane / CPR of the load), and where its operands sit in a stage
     // (unsigned: a uniform base plus a 32-bit lane offset is the
@@ -1193,13 +1428,46 @@ void attn_partition_gqa(AttnArgs a) {
         for (int t = 0; t < DT; ++t) lds_fence(r.v[t]);
     };
 
-    for (int base = w_start; base < w_stop; base += SPB) {
+    // A batch's block ids (lane L: sub-block L % BPS of its (L / BPS)-th
+    // step), raw scale bits and zero points (converted at use).
+    int id_l = 0, sk_l = 0, sv_l = 0, zp_l = 0, kz_l = 0;
+    auto batch_tables = [&](int base, int w_stop) {
         const int st_l = base + lane / BPS;
         const int blk_l = blk0 + st_l * BPS + lane % BPS;
         const bool ok_l = st_l < w_stop && blk_l < blk_end;
-        const int id_l = ok_l ? tab[blk_l] : 0;
+        id_l = ok_l ? tab[blk_l] : 0;
+        zp_l = 0;
+        kz_l = 0;
+    };
+    auto batch_scales = [&]() {
+        const int64_t t = (int64_t)id_l * H + kvh;
+        sk_l = a.k_scale[t];
+        sv_l = a.v_scale[t];
+        if constexpr (VZP) zp_l = a.v_zp[t];
+        if constexpr (KZP) kz_l = a.k_zp[t];
+    };
+    // direct-to-LDS loads of step i of the batch into stage buf
+    auto stage_batch_step = [&](int i, int buf) {
+        stage_step(readlane(id_l, i * BPS), readlane(id_l, i * BPS + BPS - 1), buf);
+    };
+    // The staged path's start of run [w_start, w_stop): the first batch's
+    // tables and scales, and its first SD steps in flight.  run_steps(...,
+    // true) then continues from there.
+    auto issue_first = [&](int w_start, int w_stop) {
+        batch_tables(w_start, w_stop);
+        batch_scales();
+        const int cnt = min(SPB, w_stop - w_start);
+        stage_batch_step(0, 0);
+#pragma unroll
+        for (int k = 1; k < SD; ++k)
+            if (k < cnt) stage_batch_step(k, k);
+    };
+    // steps w_start .. w_stop - 1 of the sequence (pre: issue_first ran)
+    auto run_steps = [&](int w_start, int w_stop, bool pre) {
+    for (int base = w_start; base < w_stop; base += SPB) {
+        const bool issued = pre && base == w_start;
+        if (!issued) batch_tables(base, w_stop);
         const int cnt = min(SPB, w_stop - base);
-        int sk_l, sv_l, zp_l = 0, kz_l = 0;   // raw scale bits and zero points (converted at use)
 
         // Loads are unconditional: a block past the partition's end has id 0
         // (any valid block); its tokens are masked, so its codes only meet
@@ -1238,13 +1506,7 @@ void attn_partition_gqa(AttnArgs a) {
         };
         auto compute = [&](Raw& r, int i) { compute_with(r, i, [](Raw&) {}); };
 
-        auto scales = [&]() {
-            const int64_t t = (int64_t)id_l * H + kvh;
-            sk_l = a.k_scale[t];
-            sv_l = a.v_scale[t];
-            if constexpr (VZP) zp_l = a.v_zp[t];
-            if constexpr (KZP) kz_l = a.k_zp[t];
-        };
+        auto scales = [&]() { batch_scales(); };
         if constexpr (JOINT) {
             // One staging area for both waves, three stages: step i + 2 is
             // loaded into the stage of step i - 1 once every wave has passed
@@ -1285,14 +1547,14 @@ void attn_partition_gqa(AttnArgs a) {
             // operands are in registers, so SD steps are in flight while one
             // is computed.  Each wait leaves outstanding only the loads issued
             // after the step's own (the scale loads come first).
-            auto stage = [&](int i, int buf) {
-                stage_step(readlane(id_l, i * BPS), readlane(id_l, i * BPS + BPS - 1), buf);
-            };
-            scales();
-            stage(0, 0);
+            auto stage = [&](int i, int buf) { stage_batch_step(i, buf); };
+            if (!issued) {
+                scales();
+                stage(0, 0);
 #pragma unroll
-            for (int k = 1; k < SD; ++k)
-                if (k < cnt) stage(k, k);
+                for (int k = 1; k < SD; ++k)
+                    if (k < cnt) stage(k, k);
+            }
             auto one = [&](auto bc, int i) {
                 constexpr int B = decltype(bc)::value;
                 const int ahead = cnt - 1 - i;   // steps staged after step i
@@ -1313,6 +1575,173 @@ void attn_partition_gqa(AttnArgs a) {
             pipelined<PBQ_GQA_DEPTH, Raw>(cnt, load, compute, scales);
         }
     }
+    };
+
+    // The last step of a fused single pass: its last block from the LDS copy
+    // (lk, lv; sc: that block's scale bits as s_tscale holds them); in a
+    // 16-token pair whose second block is the last one, the first block from
+    // the pool.
+    auto last_step = [&](const int8_t* lk, const uint8_t* lv, const uint32_t* sc) {
+        const int st = nsteps - 1;
+        const int last = nblk - 1;
+        const int first = blk0 + st * BPS;            // == last when it is alone
+        const int64_t t0 = (int64_t)tab[first] * H + kvh;
+        const bool from_pool = first != last;         // block `first` comes from the pool
+        Raw r;
+        load_step(std::false_type{}, from_pool ? a.k_codes + t0 * KT : lk, lk, from_pool ? a.v_codes + t0 * VT : lv,
+                  lv, r);
+        const uint32_t ks0 = from_pool ? a.k_scale[t0] : sc[0] & 0xFFFFu;
+        const uint32_t vs0 = from_pool ? a.v_scale[t0] : sc[1];
+        const uint32_t z0 = from_pool ? (VZP ? a.v_zp[t0] : 0u) : sc[2];
+        const uint32_t kz0 = from_pool ? (KZP ? a.k_zp[t0] : 0u) : sc[0] >> 16;
+        // a lane group's block: `first` (my_blk 0) or the block after it,
+        // which is the last block or lies past the end (masked)
+        const bool mine_last = BPS == 1 || my_blk ? true : !from_pool;
+        const int vl = __builtin_amdgcn_readfirstlane((int)sc[1]);
+        const float vm = vnorm_step(from_pool ? max(vl, (int)vs0) : vl);
+        compute_step(r, st, bits_to_f16f((uint16_t)(mine_last ? sc[0] : ks0)) * c2,
+                     bits_to_f16f((uint16_t)(mine_last ? sc[1] : vs0)) * vm,
+                     (float)(mine_last ? sc[2] : z0), (float)(mine_last ? sc[0] >> 16 : kz0), [](Raw&) {});
+    };
+
+    if constexpr (PAIR) {
+        static_assert(STAGED && TPW == 1, "paired groups stream through the staged path");
+        // Waves 0 and NW - 1 quantize a stored tile pair and take a stored
+        // step each (fused): they get hc fewer loop steps.  Run k of the
+        // loop steps laid end to end is [px(k), px(k + 1)).
+        const int N = n_a + n_b;
+        const int hc = FUSED ? min(PBQ_PAIR_HANDICAP, N / 4) : 0;
+        auto px = [&](int k) { return (k * (N + 2 * hc)) / NW - (k > 0 ? hc : 0) - (k == NW ? hc : 0); };
+        const bool last_a = FUSED && nblk_a > 0;                  // stored steps: wave 0 ...
+        const bool last_b = FUSED && seq_b >= 0 && nblk_b > 0;    // ... and wave NW - 1
+        auto seg_a = [&](int k) { return min(px(k + 1), n_a) > px(k) || (last_a && k == 0); };
+        auto seg_b = [&](int k) { return px(k + 1) > max(px(k), n_a) || (last_b && k == NW - 1); };
+        const int x0 = px(w), x1 = px(w + 1);
+        const bool in_a = seg_a(w), in_b = seg_b(w);
+        // a result slot: lane (n16, grp) holds dims 16t + 4 grp .. +3 of
+        // query n16, and (grp 0) its (max, sum)
+        auto write_slot = [&](uint8_t* sl) {
+            float (*sa)[D + 4] = reinterpret_cast<float (*)[D + 4]>(sl);
+            float (*sm)[2] = reinterpret_cast<float (*)[2]>(sl + QT * (D + 4) * 4);
+#pragma unroll
+            for (int t = 0; t < DT; ++t) *(f32x4*)&sa[n16][16 * t + 4 * grp] = acc[0][t];
+            if (grp == 0) {
+                sm[n16][0] = m[0];
+                sm[n16][1] = l[0];
+            }
+        };
+        auto use_q = [&](int u) {   // sequence u's query operands (uniform)
+#pragma unroll
+            for (int k = 0; k < KS; ++k) qop[0][k] = u ? qop_b[0][k] : qop_a[0][k];
+            qsum[0] = u ? qsum_b[0] : qsum_a[0];
+            qbias[0] = u ? qbias_b[0] : qbias_a[0];
+        };
+        // the wave's stored tiles (sequence w == 0 ? 0 : 1) in LDS
+        const int tu = w == 0 ? 0 : 1;
+        const int8_t* const tk = (const int8_t*)(s_ptile + tu * (KT + VT));
+        const uint8_t* const tv = s_ptile + tu * (KT + VT) + KT;
+        uint32_t* const tsc = s_tscale + 5 * tu;
+        if (!in_a && in_b) {
+            set_unit(seq_b, ctx_b);
+            use_q(1);
+        }
+        const int r0 = in_a ? x0 : max(x0, n_a) - n_a;
+        const int r1 = in_a ? min(x1, n_a) : x1 - n_a;
+        if constexpr (FUSED) {   // the pool's scale bits before the store
+            if (t_seq >= 0) {
+                const int64_t tt = (int64_t)t_phys * H + kvh;
+                trows_k.prev = a.k_scale[tt] | (KZP ? (uint32_t)a.k_zp[tt] << 16 : 0u);
+                trows_v.prev = a.v_scale[tt] | (VZP ? (uint32_t)a.v_zp[tt] << 16 : 0u);
+            }
+        }
+        if (r0 < r1) issue_first(r0, r1);   // the first run's first steps in flight ...
+        if constexpr (FUSED) {              // ... while the stored tiles are quantized
+            if (t_seq >= 0) {
+                const TileStoreArgs t = fused_store_args(a);
+                const int last = (t_ctx - 1) / BS;
+                const TileScales ks = quantize_tile_rows<BS, D, CP, true, true, false>(
+                    t, trows_k, kvh, t_slot, t_ctx - 1, t_ctx, last, t_phys, (int8_t*)tk, nullptr, false);
+                const TileScales vs = quantize_tile_rows<BS, D, CP, true, false, true>(
+                    t, trows_v, kvh, t_slot, t_ctx - 1, t_ctx, last, t_phys, nullptr, (uint8_t*)tv, false);
+                if (lane == 0) {
+                    tsc[0] = ks.k_scale;
+                    tsc[1] = vs.v_scale;
+                    tsc[2] = vs.v_zp;
+                    tsc[3] = ks.prev;
+                    tsc[4] = vs.prev;
+                }
+                wait_lds();
+                __asm__ volatile("" : : : "memory");
+            }
+        }
+        if (in_a) {
+            if (w == 0 && last_a) last_step(tk, tv, tsc);
+            run_steps(x0, min(x1, n_a), true);
+        }
+        if (in_b) {
+            if (in_a) {   // crossing: the first sequence's result goes to the extra slot
+                finish_state();
+                write_slot(s_stage + NW * PART);
+                reset_state();
+                set_unit(seq_b, ctx_b);
+                use_q(1);
+            }
+            run_steps(max(x0, n_a) - n_a, x1 - n_a, !in_a);
+            if (w == NW - 1 && last_b) last_step(tk, tv, tsc);
+        }
+        if constexpr (FUSED) {
+            if (t_seq >= 0 && ht == 0) {   // the first 16-head tile of a KV head writes the pool
+                const TileStoreArgs t = fused_store_args(a);
+                write_stored_tile<BS, D, CP>(t, 0, kvh, t_slot, t_seq, t_ctx - 1, t_phys, (const uint8_t*)tk, tv, tsc);
+                write_stored_tile<BS, D, CP>(t, 1, kvh, t_slot, t_seq, t_ctx - 1, t_phys, (const uint8_t*)tk, tv, tsc);
+            }
+        }
+        finish_state();
+        write_slot(s_stage + w * PART);   // its stages are no longer read
+        __syncthreads();
+        // Merge each sequence's results over the slots of the waves whose
+        // runs ended on it (and the crossing wave's first result), in wave
+        // order, one output element per thread.
+        bool crossed = false;
+        uint32_t tag = 0;   // bit k: wave k's result is the second sequence's
+#pragma unroll
+        for (int k = 0; k < NW; ++k) {
+            crossed |= seg_a(k) && seg_b(k);
+            tag |= (seg_b(k) ? 1u : 0u) << k;
+        }
+        const int n_out = (seq_b >= 0 ? 2 : 1) * nheads * D;
+        for (int idx = threadIdx.x; idx < n_out; idx += 64 * NW) {
+            const int u = idx / (nheads * D), hh = (idx / D) % nheads, d = idx % D;
+            float mk[NW + 1], lk[NW + 1], ok[NW + 1];
+#pragma unroll
+            for (int k = 0; k <= NW; ++k) {   // every slot is read; the unused ones are masked after
+                const uint8_t* sl = s_stage + k * PART;
+                mk[k] = reinterpret_cast<const float (*)[2]>(sl + QT * (D + 4) * 4)[hh][0];
+                lk[k] = reinterpret_cast<const float (*)[2]>(sl + QT * (D + 4) * 4)[hh][1];
+                ok[k] = reinterpret_cast<const float (*)[D + 4]>(sl)[hh][d];
+            }
+            float M = -INFINITY;
+#pragma unroll
+            for (int k = 0; k <= NW; ++k) {
+                const bool use = k < NW ? ((tag >> k) & 1u) == (uint32_t)u : (u == 0 && crossed);
+                mk[k] = use ? mk[k] : -INFINITY;   // (an unused slot may hold anything)
+                lk[k] = use ? lk[k] : 0.f;
+                ok[k] = use ? ok[k] : 0.f;
+                M = fmaxf(M, mk[k]);
+            }
+            float L = 0.f, o = 0.f;
+#pragma unroll
+            for (int k = 0; k <= NW; ++k) {
+                const float f = mk[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk[k] - M);
+                L = __builtin_fmaf(lk[k], f, L);
+                o = __builtin_fmaf(ok[k], f, o);
+            }
+            const int64_t row = (int64_t)(u ? seq_b : seq_a) * a.num_q_heads + kvh * G + q0 + hh;
+            a.out[row * D + d] = f32_to_f16_bits(L > 0.f ? o / L : 0.f);
+        }
+        return;
+    }
+    run_steps(w_start, w_stop, false);
     if (FUSED && fused) {
         __syncthreads();   // waves 0 and 1 have left the last block's tiles in LDS
         if (w < 2 && ht == 0) {   // the first 16-head tile of a KV head writes the pool
@@ -1320,32 +1749,7 @@ void attn_partition_gqa(AttnArgs a) {
             write_stored_tile<BS, D, CP>(t, w, kvh, a.tail_slots[s], s, ctx - 1, tab[nblk - 1], s_tile, s_tile + KT,
                                          s_tscale);
         }
-        if (w == NW - 1) {
-            // the last step: its last block from LDS; in a 16-token pair whose
-            // second block is the last one, the first block from the pool
-            const int st = nsteps - 1;
-            const int last = nblk - 1;
-            const int first = blk0 + st * BPS;            // == last when it is alone
-            const int64_t t0 = (int64_t)tab[first] * H + kvh;
-            const int8_t* lk = (const int8_t*)s_tile;
-            const uint8_t* lv = s_tile + KT;
-            const bool pair = first != last;              // block `first` comes from the pool
-            Raw r;
-            load_step(std::false_type{}, pair ? a.k_codes + t0 * KT : lk, lk, pair ? a.v_codes + t0 * VT : lv, lv, r);
-            const uint32_t ks0 = pair ? a.k_scale[t0] : s_tscale[0] & 0xFFFFu;
-            const uint32_t vs0 = pair ? a.v_scale[t0] : s_tscale[1];
-            const uint32_t z0 = pair ? (VZP ? a.v_zp[t0] : 0u) : s_tscale[2];
-            const uint32_t kz0 = pair ? (KZP ? a.k_zp[t0] : 0u) : s_tscale[0] >> 16;
-            // a lane group's block: `first` (my_blk 0) or the block after it,
-            // which is the last block or lies past the end (masked)
-            const bool mine_last = BPS == 1 || my_blk ? true : !pair;
-            const int vl = __builtin_amdgcn_readfirstlane((int)s_tscale[1]);
-            const float vm = vnorm_step(pair ? max(vl, (int)vs0) : vl);
-            compute_step(r, st, bits_to_f16f((uint16_t)(mine_last ? s_tscale[0] : ks0)) * c2,
-                         bits_to_f16f((uint16_t)(mine_last ? s_tscale[1] : vs0)) * vm,
-                         (float)(mine_last ? s_tscale[2] : z0), (float)(mine_last ? s_tscale[0] >> 16 : kz0),
-                         [](Raw&) {});
-        }
+        if (w == NW - 1) last_step((const int8_t*)s_tile, s_tile + KT, s_tscale);
     }
     // lanes of one head split its tokens by group: sum their partial sums,
     // and undo the V-scale normaliser (times the codec's unit)
@@ -1626,6 +2030,26 @@ template <int BS, int D, int CP>
 hipError_t launch_gqa(const AttnArgs& a, hipStream_t stream) {
     const int G = a.num_q_heads / a.num_kv_heads;
     const int n_ht = (G + 15) / 16;
+    // paired four-wave groups, (KV head x 16-query tile, pair of sequences):
+    // single passes whose contexts fit the groups' LDS block tables (INT4 K
+    // keeps its codes on the register path, which pairs do not use)
+    if constexpr (PBQ_GQA_PAIR && !codec_packed4(CP / 4)) {
+        const dim3 pg(1u, (unsigned)(a.num_kv_heads * n_ht), (unsigned)((a.num_seqs + 1) / 2));
+        if (a.max_partitions == 1 && a.shared_parts == 0) {
+            if constexpr (gqa_pair_lds<BS, D, CP, true>() <= kPairLdsMax) {
+                if (a.k_new != nullptr) {
+                    hipLaunchKernelGGL((attn_partition_gqa<BS, D, CP, 4, true, false, false, 1, true>), pg, dim3(256),
+                                       0, stream, a);
+                    return hipGetLastError();
+                }
+            }
+            if (a.k_new == nullptr) {
+                hipLaunchKernelGGL((attn_partition_gqa<BS, D, CP, 4, false, false, false, 1, true>), pg, dim3(256), 0,
+                                   stream, a);
+                return hipGetLastError();
+            }
+        }
+    }
     const dim3 grid = grid_dims(a.max_partitions - a.shared_parts, a.num_kv_heads * n_ht, a.num_seqs);
     if (a.max_partitions == 1) {
         if (a.k_new != nullptr)

@@ -80,78 +80,116 @@ __device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d
     return __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
 }
 
-// Quantize block j (physical id phys) of head g of a sequence whose rows
-// before position sp sit in tail slot `slot` and whose rows sp .. end-1 are
-// the new rows c0 .. c0 + end - sp - 1 of a.k / a.v.  Requires j * BS < end.
-// Writes codes, scales, zero point, and -- when the sequence's last block
-// stays partial -- its new rows to the tail slot.  With LDS set, the codes are
-// also written to lds_k / lds_v in the tile layout.  Called by a whole wave.
-// DO_K / DO_V select the tensors: the store kernel and the fused decode give
-// them to two waves, which halves the registers and the arithmetic on
-// either's path.  With wr false nothing is written to the pool (only the LDS
-// copy; write_stored_tile writes it later).
-template <int BS, int D, int CP, bool LDS, bool DO_K = true, bool DO_V = true>
-__device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, int slot, int c0, int sp,
-                                                 int end, int j, int phys, int8_t* lds_k, uint8_t* lds_v,
-                                                 bool wr = true) {
+// The exact fp16 rows of one tensor of a tile store, as raw bits: K access
+// `it` (8 dims of one row) in r[4 it .. 4 it + 3], or V row r's DPL dims in
+// r[r] -- BS dwords either way.  load_tile_rows issues their loads,
+// quantize_tile_rows does the rest, and store_tile is the two in a row.  The
+// fused decode issues the loads before its streaming loop and quantizes after
+// it, so that their latency hides behind the loop.
+template <int BS>
+struct TileRows {
+    uint32_t r[BS];
+    uint32_t prev;   // PREV: the pool's scale (| zero point << 16) before the store
+};
+
+// K (IS_K) or V rows of block j (physical id phys) of head g of a sequence
+// whose rows before position sp sit in tail slot `slot` and whose rows sp ..
+// end-1 are the new rows c0 .. c0 + end - sp - 1 of a.k / a.v.  Requires
+// j * BS < end.  Every row is loaded unconditionally -- rows past the block's
+// end read row 0 again and are replaced by zeros when quantized -- and the
+// source is chosen arithmetically, so that all loads are in flight together.
+// PREV: also the scale bits the pool held for the tile (write_stored_tile
+// compares them).  Called by a whole wave.
+template <int BS, int D, int CP, bool PREV, bool IS_K>
+__device__ __forceinline__ TileRows<BS> load_tile_rows(const TileStoreArgs& a, int g, int slot, int c0, int sp,
+                                                       int end, int j, int phys) {
+    constexpr int LPR = D / 8;     // lanes per token row
+    constexpr int RPI = 64 / LPR;  // rows per wave access
+    constexpr int NIT = BS / RPI;  // K accesses per lane
+    constexpr int DPL = D / 64;    // V: dims per lane
+    constexpr int KC = CP / 4, VC = CP % 4;
+    static_assert(4 * NIT <= BS, "K rows fit the raw registers");
+    const int lane = threadIdx.x & 63;
+    const int H = a.num_kv_heads;
+    TileRows<BS> t;
+    t.prev = 0u;
+    const int row0 = j * BS;
+    const int valid = min(BS, end - row0);   // >= 1
+    const int r_in = lane / LPR;
+    const int col = (lane % LPR) * 8;
+    const int64_t tail_base = ((int64_t)slot * H + g) * BS * D;
+    auto row_src = [&](const uint16_t* tail, const uint16_t* fresh, int r) -> const uint16_t* {
+        const int rr = r < valid ? r : 0;
+        const int p = row0 + rr;
+        const uintptr_t tp = (uintptr_t)(tail + tail_base + rr * D);
+        const uintptr_t f = (uintptr_t)(fresh + ((int64_t)(c0 + p - sp) * H + g) * D);
+        const uintptr_t from_tail = (uintptr_t)0 - (uintptr_t)(p < sp);
+        return (const uint16_t*)(f ^ ((tp ^ f) & from_tail));
+    };
+    const int64_t tile = (int64_t)phys * H + g;
+    if constexpr (IS_K) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const u32x4 x = load_once<PBQ_STORE_NT_LOADS>((const u32x4*)(row_src(a.tail_k, a.k, it * RPI + r_in) + col));
+#pragma unroll
+            for (int c = 0; c < 4; ++c) t.r[4 * it + c] = x[c];
+        }
+        if constexpr (PREV) t.prev = a.k_scale[tile] | (codec_has_zp(KC) ? (uint32_t)a.k_zp[tile] << 16 : 0u);
+    } else {
+        if constexpr (PREV) t.prev = a.v_scale[tile] | (codec_has_zp(VC) ? (uint32_t)a.v_zp[tile] << 16 : 0u);
+#pragma unroll
+        for (int r = 0; r < BS; ++r) {
+            const uint16_t* src = row_src(a.tail_v, a.v, r) + DPL * lane;
+            t.r[r] = DPL == 2 ? load_once<PBQ_STORE_NT_LOADS>((const uint32_t*)src)
+                              : (uint32_t)load_once<PBQ_STORE_NT_LOADS>(src);
+        }
+    }
+    return t;
+}
+
+// Quantize the rows load_tile_rows loaded (same arguments; DO_K: K rows,
+// else V rows): writes codes, scales, zero point, and -- when the sequence's
+// last block stays partial -- its new rows to the tail slot.  With LDS set,
+// the codes are also written to lds_k / lds_v in the tile layout.  Called by
+// a whole wave.  One tensor per call: the store kernel and the fused decode
+// give K and V to two waves, which halves the registers and the arithmetic
+// on either's path.  With wr false nothing is written to the pool (only the
+// LDS copy; write_stored_tile writes it later).
+template <int BS, int D, int CP, bool LDS, bool DO_K, bool DO_V>
+__device__ __forceinline__ TileScales quantize_tile_rows(const TileStoreArgs& a, const TileRows<BS>& rows, int g,
+                                                         int slot, int sp, int end, int j, int phys,
+                                                         int8_t* lds_k, uint8_t* lds_v, bool wr = true) {
     constexpr int LPR = D / 8;     // lanes per token row
     constexpr int RPI = 64 / LPR;  // rows per wave access
     constexpr int NIT = BS / RPI;  // accesses per lane per tensor
     constexpr int DPL = D / 64;    // V: dims per lane
     constexpr int KC = CP / 4, VC = CP % 4;
     constexpr bool V4 = codec_packed4(VC);
-    constexpr bool VZP = codec_has_zp(VC);
+    static_assert(DO_K != DO_V, "one tensor per call");
     const int lane = threadIdx.x & 63;
     const int H = a.num_kv_heads;
     TileScales out{};
+    out.prev = rows.prev;
     const int row0 = j * BS;
     const int valid = min(BS, end - row0);   // >= 1
     const int r_in = lane / LPR;
     const int col = (lane % LPR) * 8;
-
-    // Row r of the block comes from the tail slot (positions before sp) or
-    // from the new tokens.  Every row is loaded unconditionally -- rows past
-    // `valid` read row 0 again and are then replaced by zeros -- and the
-    // source is chosen arithmetically, so that all loads are in flight
-    // together, beside the block id's.
     const int64_t tail_base = ((int64_t)slot * H + g) * BS * D;
-    auto row_src = [&](const uint16_t* tail, const uint16_t* fresh, int r) -> const uint16_t* {
-        const int rr = r < valid ? r : 0;
-        const int p = row0 + rr;
-        const uintptr_t t = (uintptr_t)(tail + tail_base + rr * D);
-        const uintptr_t f = (uintptr_t)(fresh + ((int64_t)(c0 + p - sp) * H + g) * D);
-        const uintptr_t from_tail = (uintptr_t)0 - (uintptr_t)(p < sp);
-        return (const uint16_t*)(f ^ ((t ^ f) & from_tail));
-    };
+    const int64_t tile = (int64_t)phys * H + g;
+    // rows past `valid` become zeros; V's fp16 values stay packed (dims
+    // DPL*lane and DPL*lane + 1 in the low and high halves)
     f16x8 kx[DO_K ? NIT : 1];
+    uint32_t vw[DO_V ? BS : 1];
     if constexpr (DO_K) {
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) kx[it] = load_once<PBQ_STORE_NT_LOADS>((const f16x8*)(row_src(a.tail_k, a.k, it * RPI + r_in) + col));
-    }
-    const int64_t tile = (int64_t)phys * H + g;
-    constexpr bool KZP = codec_has_zp(KC);
-    if constexpr (LDS) {   // the pool's scale bits before this store, loaded with the rows
-        if constexpr (DO_K) out.prev = a.k_scale[tile] | (KZP ? (uint32_t)a.k_zp[tile] << 16 : 0u);
-        else out.prev = a.v_scale[tile] | (VZP ? (uint32_t)a.v_zp[tile] << 16 : 0u);
-    }
-    uint32_t vw[DO_V ? BS : 1];   // V row r: dims DPL*lane .. +DPL-1 (fp16 bits)
-    if constexpr (DO_V) {
-#pragma unroll
-        for (int r = 0; r < BS; ++r) {
-            const uint16_t* src = row_src(a.tail_v, a.v, r) + DPL * lane;
-            vw[r] = DPL == 2 ? load_once<PBQ_STORE_NT_LOADS>((const uint32_t*)src) : (uint32_t)load_once<PBQ_STORE_NT_LOADS>(src);
+        for (int it = 0; it < NIT; ++it) {
+            const u32x4 x = u32x4{rows.r[4 * it], rows.r[4 * it + 1], rows.r[4 * it + 2], rows.r[4 * it + 3]};
+            kx[it] = it * RPI + r_in < valid ? __builtin_bit_cast(f16x8, x) : (f16x8)(_Float16)0;
         }
     }
-    if constexpr (DO_K) {
-#pragma unroll
-        for (int it = 0; it < NIT; ++it)
-            if (it * RPI + r_in >= valid) kx[it] = (f16x8)(_Float16)0;
-    }
-    // rows past `valid` become zeros; the fp16 values stay packed (dims
-    // DPL*lane and DPL*lane + 1 in the low and high halves)
     if constexpr (DO_V) {
 #pragma unroll
-        for (int r = 0; r < BS; ++r) vw[r] = r < valid ? vw[r] : 0u;
+        for (int r = 0; r < BS; ++r) vw[r] = r < valid ? rows.r[r] : 0u;
     }
     auto vx = [&](int k, int r) -> float {
         return bits_to_f16f((uint16_t)(k ? vw[r] >> 16 : vw[r] & 0xFFFFu));
@@ -493,6 +531,17 @@ __device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, 
         }
     }
     return out;
+}
+
+// Quantize one tensor (DO_K or DO_V) of block j (physical id phys) of head
+// g: load_tile_rows, then quantize_tile_rows (see both).  With LDS set,
+// out.prev is the pool's scale bits before this store.
+template <int BS, int D, int CP, bool LDS, bool DO_K, bool DO_V>
+__device__ __forceinline__ TileScales store_tile(const TileStoreArgs& a, int g, int slot, int c0, int sp,
+                                                 int end, int j, int phys, int8_t* lds_k, uint8_t* lds_v,
+                                                 bool wr = true) {
+    const TileRows<BS> rows = load_tile_rows<BS, D, CP, LDS, DO_K>(a, g, slot, c0, sp, end, j, phys);
+    return quantize_tile_rows<BS, D, CP, LDS, DO_K, DO_V>(a, rows, g, slot, sp, end, j, phys, lds_k, lds_v, wr);
 }
 
 // Pool writes of a tile that store_tile quantized with wr false (codes left

@@ -301,12 +301,21 @@ def test_decode_append_equals_store_then_decode(bs, d, vc, g):
     outputs agree with the oracle.  Context lengths put the new token at the
     start, the middle and the end of a block."""
     announce("decode-append", bs, d, vc, g)
-    from paged_block_quantized_amd import KVPool
-    hkv = 2
-    hq = g * hkv
     ctx = [1, 2, bs - 1, bs, bs + 1, 2 * bs, 3 * bs + 5, 700, 1100]
+    # 2048 covers every context: one partition (the fused kernel)
+    check_decode_append(bs, d, vc, g, ctx, (0, 32 if g > 1 else bs, 1024, 2048),
+                        seed=1000 * bs + d + 7 * g + (vc == "i4"))
+
+
+def check_decode_append(bs, d, vc, g, ctx, parts, seed, hkv=2, repeat=False):
+    """Sequences of the given contexts, their last token stored two ways
+    (kv_quantize_store then paged_attn_decode, and paged_attn_decode_append)
+    for each partition size: the pools bit-identical to each other and to the
+    oracle's, both outputs within tolerance of the oracle's.  repeat: the
+    fused call runs twice on identical pools and must give identical bits."""
+    hq = g * hkv
     S = len(ctx)
-    rng = np.random.default_rng(1000 * bs + d + 7 * g + (vc == "i4"))
+    rng = np.random.default_rng(seed)
     hk = [rng.standard_normal((c, hkv, d)).astype(np.float16) for c in ctx]
     hv = [rng.standard_normal((c, hkv, d)).astype(np.float16) for c in ctx]
     q = rng.standard_normal((S, hq, d)).astype(np.float16)
@@ -326,7 +335,7 @@ def test_decode_append_equals_store_then_decode(bs, d, vc, g):
         k = torch.from_numpy(np.concatenate([h[:c - 1] for h, c in zip(hk, ctx)])).to(dev)
         v = torch.from_numpy(np.concatenate([h[:c - 1] for h, c in zip(hv, ctx)])).to(dev)
         pool.quantize_store(k, v, cu, torch.zeros(S, dtype=torch.int32, device=dev),
-                            tables.to(dev), slots.to(dev), max(lens))
+                            tables.to(dev), slots.to(dev), max(max(lens), 1))
         for s in range(S):
             assert pool.append(s, 1) == []
         tables, ctx_h, slots = pool.batch_tables(list(range(S)), max_blocks)
@@ -348,8 +357,7 @@ def test_decode_append_equals_store_then_decode(bs, d, vc, g):
         paged.store_range(opool, model.table(s)[0], hk[s], hv[s], 0, c)
     ref = attention.paged_decode(opool, [model.table(s)[0] for s in range(S)], ctx, q, sm)
 
-    # 2048 covers every context: one partition (the fused kernel for MHA)
-    for part in (0, 32 if g > 1 else bs, 1024, 2048):
+    for part in parts:
         pa, ta, ca, sa = build()
         pa.quantize_store(k_new, v_new, torch.arange(S + 1, dtype=torch.int32, device=dev),
                           ca - 1, ta, sa, 1)
@@ -369,6 +377,43 @@ def test_decode_append_equals_store_then_decode(bs, d, vc, g):
         assert_pool_equal(pb, opool)
         assert_close(out_a.cpu().numpy(), ref, f"store+decode part {part}")
         assert_close(out_b.cpu().numpy(), ref, f"decode_append part {part}")
+        if repeat:
+            pc, tc, cc, sc = build()
+            out_c = torch.empty_like(qd)
+            pc.decode_append(k_new, v_new, sc, qd, out_c, tc, cc, max(ctx), sm, part)
+            torch.cuda.synchronize()
+            assert np.array_equal(out_c.cpu().numpy().view(np.uint16), out_b.cpu().numpy().view(np.uint16)), \
+                f"decode_append not reproducible (part {part})"
+
+
+# Single-pass grouped-query calls run in paired work groups: two sequences
+# (ranked by context length, longest with shortest; beyond 256 sequences in
+# the call's order) share four waves that split their steps end to end.
+PAIR_CONTEXTS = {
+    "one": [40],
+    "stored_only": [1, 2],                 # both sequences: the stored step alone
+    "second_stored_only": [700, 20],       # the short one: its stored step alone
+    "ties": [50, 50, 7, 50, 7, 96],
+    "odd": [33, 1, 64, 500, 31],
+    "ranked_256": [int(x) for x in np.random.default_rng(17).integers(1, 200, 256)],
+    "unranked_300": [int(x) for x in np.random.default_rng(18).integers(1, 90, 300)],
+}
+
+
+@pytest.mark.parametrize("name", list(PAIR_CONTEXTS))
+@pytest.mark.parametrize("vc", ["i4", "fp8"])
+def test_paired_groups(name, vc):
+    """Paired grouped-query groups against the oracle, plain decode and fused
+    store + decode, in one pass; the fused call is reproducible bit for bit."""
+    announce("paired", name, vc)
+    ctx = PAIR_CONTEXTS[name]
+    check_decode_append(32, 128, vc, 8, ctx, (2048,), seed=len(ctx) + 3 * sum(ctx) % 1000, repeat=True)
+    case = normal_case(ctx, 8 * 2, 2, 128, 32, vc, seed=sum(ctx) % 997)
+    case.store_all()
+    ref = case.reference()
+    out = case.decode(2048)
+    assert_close(out, ref, f"paired plain decode {name} {vc}")
+    assert np.array_equal(case.decode(2048).view(np.uint16), out.view(np.uint16)), "plain decode not reproducible"
 
 
 SHARED_SHAPES = [
