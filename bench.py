@@ -681,8 +681,8 @@ def main():
             "v_codec": {"i8": "int8_sym", "i4": "int4_asym", "i8a": "int8_asym", "fp8": "fp8_e4m3"}[w.v_codec],
             "partition": setup.partition, "shared_prefix": w.prefix,
             "pool_copies_rotated": R,
-            "batch_order": ("workload order (equal lengths)" if np.all(setup.ctx == setup.ctx[0]) else
-                            "runner.balanced_order: longest first, every other run of 64 reversed"),
+            "batch_order": "the workload's own order (single-pass grouped-query launches rank the "
+                           "sequences by length inside the kernel)",
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s_per_layer": round(S / (ms_step * 1e-3), 1),

@@ -796,30 +796,45 @@ void attn_partition_gqa(AttnArgs a) {
     } else {
         grid_coords(p, tile, s);
     }
-    // PAIR: the group's sequences, those of ranks pair and S - 1 - pair when
-    // the sequences are ordered by context length, longest first (ties by
-    // index; beyond kPairRankMax sequences, the call's own order).  The
-    // first is at least as long as the second; an odd S leaves the middle
-    // rank alone (seq_b -1).
+    // Ranks by context length, longest first (ties by index; beyond
+    // kPairRankMax sequences, the call's own order).  PAIR: the group's
+    // sequences are those of ranks pair and S - 1 - pair -- the first at
+    // least as long as the second; an odd S leaves the middle rank alone
+    // (seq_b -1).  Other single passes (one sequence per group): group z
+    // takes the sequence at position z of the longest-first order with every
+    // other run of 64 reversed, so that the compute units, which receive
+    // consecutive groups in turn, each get long and short sequences.
     int seq_a = 0, seq_b = -1;
-    // PAIR: the two sequences' context lengths and (fused) tail slots
+    // the group's sequences' context lengths (the second: PAIR), and (PAIR,
+    // fused) tail slots
     int pctx[2] = {0, 0}, pslot[2] = {0, 0};
-    if constexpr (PAIR) {
-        const int S = a.num_seqs, pr = blockIdx.z;
+    bool have_ctx = false;
+    constexpr bool RANKED = !MULTI && !SHARED;
+    if (RANKED && (PAIR || a.max_partitions == 1)) {   // uniform
+        constexpr int NT = 64 * NW, HT = NT / 2;
+        const int S = a.num_seqs;
+        int want0, want1 = -1;
+        if constexpr (PAIR) {
+            want0 = blockIdx.z;
+            want1 = S - 1 - (int)blockIdx.z != (int)blockIdx.z ? S - 1 - (int)blockIdx.z : -1;
+        } else {
+            const int b = s, start = b / 64 * 64, size = min(64, S - start);
+            want0 = (b / 64) % 2 == 0 ? b : start + size - 1 - b % 64;
+        }
         if (S <= kPairRankMax) {
-            // Each thread reads one sequence's length (and, fused, its tail
-            // slot) into LDS.  Keys: the length (clamped; only
-            // the pairing depends on it), then the reversed index, so that
-            // all keys differ and the rank is the number of larger keys; two
-            // threads per sequence when S <= 128, each counting over half of
-            // the keys (four at a time).
+            // Each thread reads one sequence's length (and, paired and fused,
+            // its tail slot) into LDS.  Keys: the length (clamped; only the
+            // order depends on it), then the reversed index, so that all keys
+            // differ and the rank is the number of larger keys; two threads
+            // per sequence when S <= NT / 2, each counting over half of the
+            // keys (four at a time).
             __shared__ int s_pair[2];
             __shared__ __align__(16) uint32_t s_key[kPairRankMax];
             __shared__ int s_len[kPairRankMax];
-            __shared__ int s_half[2][kPairRankMax / 2];
+            __shared__ int s_half[2][kPairRankMax / 2];   // (row 1 used)
             __shared__ int s_slot[FUSED ? kPairRankMax : 1];
             const int S4 = (S + 3) & ~3;
-            for (int i = threadIdx.x; i < S4; i += 64 * NW) {
+            for (int i = threadIdx.x; i < S4; i += NT) {
                 const int len = i < S ? a.context_lens[i] : 0;
                 s_key[i] = i < S ? ((uint32_t)min(len, (1 << 22) - 1) << 9) | (uint32_t)(511 - i) : 0u;
                 if (i < S) {
@@ -829,49 +844,51 @@ void attn_partition_gqa(AttnArgs a) {
             }
             if (threadIdx.x < 2) s_pair[threadIdx.x] = -1;
             __syncthreads();
-            const bool split = S <= 128;
-            const int i = split ? threadIdx.x & 127 : threadIdx.x;
-            const int half = split ? threadIdx.x >> 7 : 0;
-            const int j0 = split ? half * (S4 / 8) * 4 : 0;            // S4 / 2 rounded down to 4
-            const int j1 = split && half == 0 ? (S4 / 8) * 4 : S4;
-            int cnt = 0;
-            if (i < S) {
+            auto count = [&](int i, int j0, int j1) {   // keys j0 .. j1 - 1 above sequence i's
                 const uint32_t ki = s_key[i];
+                int cnt = 0;
 #pragma unroll 4
                 for (int j = j0; j < j1; j += 4) {
                     const u32x4 k4 = *(const u32x4*)&s_key[j];
                     cnt += (k4[0] > ki) + (k4[1] > ki) + (k4[2] > ki) + (k4[3] > ki);
                 }
-            }
-            if (split) {
-                if (i < S) s_half[half][i] = cnt;   // i < 128
+                return cnt;
+            };
+            auto found = [&](int i, int rank) {
+                if (rank == want0) s_pair[0] = i;
+                if (rank == want1) s_pair[1] = i;
+            };
+            if (S <= HT) {   // uniform
+                const int i = (int)threadIdx.x % HT, half = (int)threadIdx.x / HT;
+                const int mid = (S4 / 8) * 4;   // S4 / 2 rounded down to 4
+                const int cnt = i < S ? count(i, half ? mid : 0, half ? S4 : mid) : 0;
+                if (half == 1 && i < S) s_half[1][i] = cnt;   // i < NT / 2 <= kPairRankMax / 2
                 __syncthreads();
-                if (half == 0 && i < S) cnt += s_half[1][i];
-            }
-            if (i < S && half == 0) {
-                if (cnt == pr) s_pair[0] = i;
-                if (cnt == S - 1 - pr && cnt != pr) s_pair[1] = i;
+                if (half == 0 && i < S) found(i, cnt + s_half[1][i]);
+            } else {
+                for (int i = threadIdx.x; i < S; i += NT) found(i, count(i, 0, S4));
             }
             __syncthreads();
             seq_a = s_pair[0];
             seq_b = s_pair[1];
             pctx[0] = s_len[seq_a];
-            if (seq_b >= 0) pctx[1] = s_len[seq_b];
-            if constexpr (FUSED) {
-                pslot[0] = s_slot[seq_a];
-                if (seq_b >= 0) pslot[1] = s_slot[seq_b];
+            if constexpr (FUSED) pslot[0] = s_slot[seq_a];
+            if constexpr (PAIR) {
+                if (seq_b >= 0) pctx[1] = s_len[seq_b];
+                if (FUSED && seq_b >= 0) pslot[1] = s_slot[seq_b];
             }
         } else {
-            seq_a = pr;
-            seq_b = S - 1 - pr != pr ? S - 1 - pr : -1;
+            seq_a = PAIR ? want0 : s;
+            seq_b = want1;
             pctx[0] = a.context_lens[seq_a];
-            if (seq_b >= 0) pctx[1] = a.context_lens[seq_b];
-            if constexpr (FUSED) {
-                pslot[0] = a.tail_slots[seq_a];
-                if (seq_b >= 0) pslot[1] = a.tail_slots[seq_b];
+            if constexpr (FUSED) pslot[0] = a.tail_slots[seq_a];
+            if constexpr (PAIR) {
+                if (seq_b >= 0) pctx[1] = a.context_lens[seq_b];
+                if (FUSED && seq_b >= 0) pslot[1] = a.tail_slots[seq_b];
             }
         }
         s = seq_a;
+        have_ctx = true;
     }
     if constexpr (!SHARED && !MULTI) p += a.shared_parts;   // shared partitions ran in their own launch
     const int q_row0 = MULTI ? a.cu_q[s] : 0;               // the sequence's first query row
@@ -884,7 +901,7 @@ void attn_partition_gqa(AttnArgs a) {
     const int ht = tile % n_ht_grid;
     if (MULTI && ht >= n_ht) return;
     const int H = a.num_kv_heads;
-    int ctx_seq = SHARED ? a.shared_tokens : PAIR ? pctx[0] : a.context_lens[s];
+    int ctx_seq = SHARED ? a.shared_tokens : have_ctx ? pctx[0] : a.context_lens[s];
     // position of query token 0, and the tokens this tile's last query sees
     const int pos0 = ctx_seq - n_tok;
     int ctx = MULTI ? pos0 + (min(NQ, ht * QW + QW) - 1) / G + 1 : ctx_seq;
@@ -1275,7 +1292,7 @@ void attn_partition_gqa(AttnArgs a) {
     if (!PAIR && fused && w < 2) {
         const TileStoreArgs t = fused_store_args(a);
         const int last = nblk - 1;
-        const int slot = a.tail_slots[s], phys = tab[last];
+        const int slot = have_ctx ? pslot[0] : a.tail_slots[s], phys = tab[last];
         if (w == 0) {
             const TileScales ts = store_tile<BS, D, CP, true, true, false>(
                 t, kvh, slot, s, ctx - 1, ctx, last, phys, (int8_t*)s_tile, s_tile + KT, false);
@@ -1746,8 +1763,8 @@ void attn_partition_gqa(AttnArgs a) {
         __syncthreads();   // waves 0 and 1 have left the last block's tiles in LDS
         if (w < 2 && ht == 0) {   // the first 16-head tile of a KV head writes the pool
             const TileStoreArgs t = fused_store_args(a);
-            write_stored_tile<BS, D, CP>(t, w, kvh, a.tail_slots[s], s, ctx - 1, tab[nblk - 1], s_tile, s_tile + KT,
-                                         s_tscale);
+            write_stored_tile<BS, D, CP>(t, w, kvh, have_ctx ? pslot[0] : a.tail_slots[s], s, ctx - 1, tab[nblk - 1],
+                                         s_tile, s_tile + KT, s_tscale);
         }
         if (w == NW - 1) last_step((const int8_t*)s_tile, s_tile + KT, s_tscale);
     }

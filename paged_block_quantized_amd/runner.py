@@ -30,26 +30,6 @@ def code_bits(w: W.Workload):
     return kbits, vbits, meta
 
 
-def balanced_order(ctx: np.ndarray, block: int = 64) -> np.ndarray:
-    """Batch order for a decode step: sequence ids sorted by context length,
-    longest first, with every other run of `block` reversed.  The GPU hands
-    work groups to its 8 XCDs in turn and, within an XCD, to its compute
-    units in turn, so consecutive sequences land on different units; the
-    alternating runs give every unit a mix of long and short sequences.
-    (gqa70b's step: 61.6 us in the workload's order, 56.8 us longest first,
-    54.7 us with this order.)  Equal lengths keep their order."""
-    ctx = np.asarray(ctx)
-    if np.all(ctx == ctx[0]):
-        return np.arange(len(ctx))
-    srt = np.argsort(-ctx, kind="stable")
-    pos = np.arange(len(ctx))
-    run, off = pos // block, pos % block
-    start = run * block
-    size = np.minimum(block, len(ctx) - start)
-    rank = np.where(run % 2 == 0, pos, start + size - 1 - off)
-    return srt[rank]
-
-
 def blocks_needed(w: W.Workload, ctx: np.ndarray) -> int:
     bs = w.block_size
     per_seq = (ctx + bs - 1) // bs
@@ -138,9 +118,10 @@ def setup_decode(w: W.Workload, device="cuda", chunk_seqs=8, partition=None, ord
     """Build the pool for workload ``w`` holding ctx-1 tokens per sequence,
     reserve the current token's position, and allocate the step's tensors.
     The batch is laid out in ``order`` (workload sequence ids; by default
-    balanced_order of the lengths): batch index b is sequence order[b]."""
+    the workload's own order -- the library balances ragged batches over the
+    GPU itself): batch index b is sequence order[b]."""
     ctx_w = W.context_lengths(w)
-    order = balanced_order(ctx_w) if order is None else np.asarray(order)
+    order = np.arange(len(ctx_w)) if order is None else np.asarray(order)
     ctx = ctx_w[order]
     S, bs = w.num_seqs, w.block_size
     N = w.pool_blocks or blocks_needed(w, ctx)

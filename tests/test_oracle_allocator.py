@@ -309,21 +309,3 @@ def test_tables_and_plans_keep_every_sequence_data(seed, n_blocks, bs, host_bloc
         rec = apply_op(m, op, A.AllocError)
         sim.apply(m, op, rec)
         m.check_invariants()
-
-
-def test_balanced_batch_order():
-    """The decode runner's batch order is a permutation, keeps equal lengths
-    in place, puts the longest sequence first and reverses every other run
-    of 64 of the length-sorted order."""
-    from paged_block_quantized_amd import runner
-    rng = np.random.default_rng(3)
-    for n in (1, 5, 64, 100, 128, 300):
-        ctx = rng.integers(1, 5000, n)
-        o = runner.balanced_order(ctx)
-        assert sorted(o.tolist()) == list(range(n))
-        srt = ctx[np.argsort(-ctx, kind="stable")]
-        got = ctx[o]
-        for b in range(0, n, 64):
-            run = srt[b:b + 64]
-            assert list(got[b:b + 64]) == (list(run) if (b // 64) % 2 == 0 else list(run[::-1]))
-    assert runner.balanced_order(np.full(7, 42)).tolist() == list(range(7))
