@@ -596,9 +596,11 @@ void attn_partition_mha(AttnArgs a) {
 #endif
 constexpr int kPairRankMax = PBQ_PAIR_RANK_MAX;
 // Loop steps the two waves of a paired group that quantize the stored tiles
-// and take the stored steps give up to the other two.
+// and take the stored steps give up to the other two (their quantize of a K
+// and a V tile keeps them from streaming for about as long as six steps take
+// on gqa70b's shapes).
 #ifndef PBQ_PAIR_HANDICAP
-#define PBQ_PAIR_HANDICAP 2
+#define PBQ_PAIR_HANDICAP 6
 #endif
 // LDS of a paired group (two per CU must fit): per wave two stages of a
 // step's codes (or a result slot, if larger), one more slot, and with the
@@ -809,7 +811,8 @@ void attn_partition_gqa(AttnArgs a) {
     // fused) tail slots
     int pctx[2] = {0, 0}, pslot[2] = {0, 0};
     bool have_ctx = false;
-    constexpr bool RANKED = !MULTI && !SHARED;
+    // (four-wave groups without PAIR serve split partitions only: no ranking, no LDS for it)
+    constexpr bool RANKED = !MULTI && !SHARED && (PAIR || NW != 4);
     if (RANKED && (PAIR || a.max_partitions == 1)) {   // uniform
         constexpr int NT = 64 * NW, HT = NT / 2;
         const int S = a.num_seqs;
@@ -945,28 +948,44 @@ void attn_partition_gqa(AttnArgs a) {
     // whose nibbles come out as dims 8j + (0, 2, 4, 6, 1, 3, 5, 7).
     f16x8v qop[TPW][KS];
     float qsum[TPW], qbias[TPW];
-    auto load_q = [&]() {   // (again for a paired group's second sequence)
+    // the loads of sequence `seq`'s query operands (PAIR: of either sequence)
+    auto load_q_into = [&](f16x8v (&dst)[TPW][KS], int seq) {
 #pragma unroll
-    for (int T = 0; T < TPW; ++T) {
-        float qs = 0.f;
-        const bool live = 16 * T + n16 < nheads;
-        const uint16_t* qp = a.q + query_row(live ? 16 * T + n16 : 0) * D + (K4 ? 2 * KCH : 16) * grp;
+        for (int T = 0; T < TPW; ++T) {
+            const bool live = 16 * T + n16 < nheads;
+            const int s_saved = s;
+            s = seq;
+            const uint16_t* qp = a.q + query_row(live ? 16 * T + n16 : 0) * D + (K4 ? 2 * KCH : 16) * grp;
+            s = s_saved;
 #pragma unroll
-        for (int j = 0; j < KS; ++j) {
-            f16x8v x = (f16x8v)(_Float16)0;
-            if (live) x = *(const f16x8v*)(qp + (K4 ? 8 * j : 64 * (j / 2) + 8 * (j % 2)));
-            if constexpr (K4) qop[T][j] = __builtin_shufflevector(x, x, 0, 2, 4, 6, 1, 3, 5, 7);
-            else qop[T][j] = x;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) qs += (float)x[i];
+            for (int j = 0; j < KS; ++j) {
+                f16x8v x = (f16x8v)(_Float16)0;
+                if (live) x = *(const f16x8v*)(qp + (K4 ? 8 * j : 64 * (j / 2) + 8 * (j % 2)));
+                if constexpr (K4) dst[T][j] = __builtin_shufflevector(x, x, 0, 2, 4, 6, 1, 3, 5, 7);
+                else dst[T][j] = x;
+            }
         }
-        qs += shfl_xor_f(qs, 16);
-        qs += shfl_xor_f(qs, 32);
-        qsum[T] = qs;
-        qbias[T] = code_bias<KC>(0.f) * qs;   // INT4 K: per block, from its zero point
-    }
     };
-    load_q();
+    // the sum of each query's elements (the K codes' offset times it is
+    // taken off the scores), once the loads above have landed
+    auto q_sums = [&](const f16x8v (&qq)[TPW][KS], float (&qs_out)[TPW], float (&qb_out)[TPW]) {
+#pragma unroll
+        for (int T = 0; T < TPW; ++T) {
+            float qs = 0.f;
+#pragma unroll
+            for (int j = 0; j < KS; ++j)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) qs += (float)qq[T][j][i];
+            qs += shfl_xor_f(qs, 16);
+            qs += shfl_xor_f(qs, 32);
+            qs_out[T] = qs;
+            qb_out[T] = code_bias<KC>(0.f) * qs;   // INT4 K: per block, from its zero point
+        }
+    };
+    if constexpr (!PAIR) {
+        load_q_into(qop, s);
+        q_sums(qop, qsum, qbias);
+    }
 
     const float c2 = a.sm_scale * kLog2e * code_unit<KC>();
     constexpr float vunit = code_unit<VC>();
@@ -1240,6 +1259,7 @@ void attn_partition_gqa(AttnArgs a) {
     // codes are in flight, and takes that sequence's stored step itself
     TileRows<BS> trows_k, trows_v;
     int t_seq = -1, t_ctx = 0, t_slot = 0, t_phys = 0;
+    uint32_t prev_k = 0u, prev_v = 0u;
     if constexpr (PAIR && FUSED) {
         const int u = w == 0 ? 0 : w == NW - 1 ? 1 : -1;
         if (u >= 0) {
@@ -1248,13 +1268,9 @@ void attn_partition_gqa(AttnArgs a) {
             t_slot = pslot[u];
         }
         if (t_seq >= 0 && t_ctx > 0) {
-            // the rows need only the slot; the last block's id (for the
-            // pool's previous scale bits, read later) is loaded beside them
-            const TileStoreArgs t = fused_store_args(a);
-            const int last = (t_ctx - 1) / BS;
-            t_phys = a.block_tables[(int64_t)t_seq * a.max_blocks_per_seq + last];
-            trows_k = load_tile_rows<BS, D, CP, false, true>(t, kvh, t_slot, t_seq, t_ctx - 1, t_ctx, last, 0);
-            trows_v = load_tile_rows<BS, D, CP, false, false>(t, kvh, t_slot, t_seq, t_ctx - 1, t_ctx, last, 0);
+            // the last block's id, for the pool's previous scale bits (the
+            // rows are loaded after the first steps' block ids)
+            t_phys = a.block_tables[(int64_t)t_seq * a.max_blocks_per_seq + (t_ctx - 1) / BS];
         } else {
             t_seq = -1;
         }
@@ -1263,31 +1279,11 @@ void attn_partition_gqa(AttnArgs a) {
     const int nblk_a = nblk, nblk_b = (ctx_b + BS - 1) / BS;
     f16x8v qop_a[TPW][KS], qop_b[TPW][KS];
     float qsum_a[TPW], qsum_b[TPW], qbias_a[TPW], qbias_b[TPW];
-    if constexpr (PAIR) {
+    if constexpr (PAIR) {   // (loads only: their sums are taken once the first steps are in flight)
+        load_q_into(qop_a, seq_a);
 #pragma unroll
-        for (int T = 0; T < TPW; ++T) {
-#pragma unroll
-            for (int k = 0; k < KS; ++k) qop_a[T][k] = qop_b[T][k] = qop[T][k];
-            qsum_a[T] = qsum_b[T] = qsum[T];
-            qbias_a[T] = qbias_b[T] = qbias[T];
-        }
-        if (seq_b >= 0) {
-            s = seq_b;
-            load_q();
-#pragma unroll
-            for (int T = 0; T < TPW; ++T) {
-#pragma unroll
-                for (int k = 0; k < KS; ++k) {
-                    qop_b[T][k] = qop[T][k];
-                    qop[T][k] = qop_a[T][k];
-                }
-                qsum_b[T] = qsum[T];
-                qbias_b[T] = qbias[T];
-                qsum[T] = qsum_a[T];
-                qbias[T] = qbias_a[T];
-            }
-            s = seq_a;
-        }
+        for (int k = 0; k < KS; ++k) qop_b[0][k] = (f16x8v)(_Float16)0;
+        if (seq_b >= 0) load_q_into(qop_b, seq_b);
     }
     if (!PAIR && fused && w < 2) {
         const TileStoreArgs t = fused_store_args(a);
@@ -1470,8 +1466,8 @@ void attn_partition_gqa(AttnArgs a) {
     // The staged path's start of run [w_start, w_stop): the first batch's
     // tables and scales, and its first SD steps in flight.  run_steps(...,
     // true) then continues from there.
-    auto issue_first = [&](int w_start, int w_stop) {
-        batch_tables(w_start, w_stop);
+    auto issue_first = [&](int w_start, int w_stop, bool have_tables) {
+        if (!have_tables) batch_tables(w_start, w_stop);
         batch_scales();
         const int cnt = min(SPB, w_stop - w_start);
         stage_batch_step(0, 0);
@@ -1658,21 +1654,34 @@ void attn_partition_gqa(AttnArgs a) {
         const int8_t* const tk = (const int8_t*)(s_ptile + tu * (KT + VT));
         const uint8_t* const tv = s_ptile + tu * (KT + VT) + KT;
         uint32_t* const tsc = s_tscale + 5 * tu;
-        if (!in_a && in_b) {
-            set_unit(seq_b, ctx_b);
-            use_q(1);
-        }
+        if (!in_a && in_b) set_unit(seq_b, ctx_b);
         const int r0 = in_a ? x0 : max(x0, n_a) - n_a;
         const int r1 = in_a ? min(x1, n_a) : x1 - n_a;
-        if constexpr (FUSED) {   // the pool's scale bits before the store
+        // The first run's block ids, then (waves 0 and NW - 1) the stored
+        // tiles' rows, then the first steps' scales and codes: loads complete
+        // in issue order, so the rows must not come before what the first
+        // steps wait for.  The tiles are quantized while those are in flight.
+        if (r0 < r1) batch_tables(r0, r1);
+        if constexpr (FUSED) {
             if (t_seq >= 0) {
-                const int64_t tt = (int64_t)t_phys * H + kvh;
-                trows_k.prev = a.k_scale[tt] | (KZP ? (uint32_t)a.k_zp[tt] << 16 : 0u);
-                trows_v.prev = a.v_scale[tt] | (VZP ? (uint32_t)a.v_zp[tt] << 16 : 0u);
+                const TileStoreArgs t = fused_store_args(a);
+                const int last = (t_ctx - 1) / BS;
+                trows_k = load_tile_rows<BS, D, CP, false, true>(t, kvh, t_slot, t_seq, t_ctx - 1, t_ctx, last, 0);
+                trows_v = load_tile_rows<BS, D, CP, false, false>(t, kvh, t_slot, t_seq, t_ctx - 1, t_ctx, last, 0);
             }
         }
-        if (r0 < r1) issue_first(r0, r1);   // the first run's first steps in flight ...
-        if constexpr (FUSED) {              // ... while the stored tiles are quantized
+        if (r0 < r1) issue_first(r0, r1, true);
+        if constexpr (FUSED) {   // the pool's scale bits before the store (used after the loop)
+            if (t_seq >= 0) {
+                const int64_t tt = (int64_t)t_phys * H + kvh;
+                prev_k = a.k_scale[tt] | (KZP ? (uint32_t)a.k_zp[tt] << 16 : 0u);
+                prev_v = a.v_scale[tt] | (VZP ? (uint32_t)a.v_zp[tt] << 16 : 0u);
+            }
+        }
+        q_sums(qop_a, qsum_a, qbias_a);
+        if (seq_b >= 0) q_sums(qop_b, qsum_b, qbias_b);
+        use_q(in_a ? 0 : 1);
+        if constexpr (FUSED) {
             if (t_seq >= 0) {
                 const TileStoreArgs t = fused_store_args(a);
                 const int last = (t_ctx - 1) / BS;
@@ -1684,8 +1693,6 @@ void attn_partition_gqa(AttnArgs a) {
                     tsc[0] = ks.k_scale;
                     tsc[1] = vs.v_scale;
                     tsc[2] = vs.v_zp;
-                    tsc[3] = ks.prev;
-                    tsc[4] = vs.prev;
                 }
                 wait_lds();
                 __asm__ volatile("" : : : "memory");
@@ -1709,6 +1716,11 @@ void attn_partition_gqa(AttnArgs a) {
         if constexpr (FUSED) {
             if (t_seq >= 0 && ht == 0) {   // the first 16-head tile of a KV head writes the pool
                 const TileStoreArgs t = fused_store_args(a);
+                if (lane == 0) {   // the pool's scale bits before the store (loaded at the start)
+                    tsc[3] = prev_k;
+                    tsc[4] = prev_v;
+                }
+                wait_lds();
                 write_stored_tile<BS, D, CP>(t, 0, kvh, t_slot, t_seq, t_ctx - 1, t_phys, (const uint8_t*)tk, tv, tsc);
                 write_stored_tile<BS, D, CP>(t, 1, kvh, t_slot, t_seq, t_ctx - 1, t_phys, (const uint8_t*)tk, tv, tsc);
             }
@@ -1718,7 +1730,8 @@ void attn_partition_gqa(AttnArgs a) {
         __syncthreads();
         // Merge each sequence's results over the slots of the waves whose
         // runs ended on it (and the crossing wave's first result), in wave
-        // order, one output element per thread.
+        // order: a thread takes 8 dims of one query row -- the row's weights
+        // once, then 8 outputs, written as 16 bytes.
         bool crossed = false;
         uint32_t tag = 0;   // bit k: wave k's result is the second sequence's
 #pragma unroll
@@ -1726,35 +1739,48 @@ void attn_partition_gqa(AttnArgs a) {
             crossed |= seg_a(k) && seg_b(k);
             tag |= (seg_b(k) ? 1u : 0u) << k;
         }
-        const int n_out = (seq_b >= 0 ? 2 : 1) * nheads * D;
-        for (int idx = threadIdx.x; idx < n_out; idx += 64 * NW) {
-            const int u = idx / (nheads * D), hh = (idx / D) % nheads, d = idx % D;
-            float mk[NW + 1], lk[NW + 1], ok[NW + 1];
+        constexpr int CPR8 = D / 8;   // 8-dim chunks per row
+        const int n_chunks = (seq_b >= 0 ? 2 : 1) * nheads * CPR8;
+        for (int c = threadIdx.x; c < n_chunks; c += 64 * NW) {
+            const int row_i = c / CPR8, d0 = (c % CPR8) * 8;
+            const int u = row_i >= nheads ? 1 : 0, hh = row_i - (u ? nheads : 0);
+            float mk[NW + 1], lk[NW + 1];
 #pragma unroll
             for (int k = 0; k <= NW; ++k) {   // every slot is read; the unused ones are masked after
-                const uint8_t* sl = s_stage + k * PART;
-                mk[k] = reinterpret_cast<const float (*)[2]>(sl + QT * (D + 4) * 4)[hh][0];
-                lk[k] = reinterpret_cast<const float (*)[2]>(sl + QT * (D + 4) * 4)[hh][1];
-                ok[k] = reinterpret_cast<const float (*)[D + 4]>(sl)[hh][d];
+                const float (*sm)[2] = reinterpret_cast<const float (*)[2]>(s_stage + k * PART + QT * (D + 4) * 4);
+                const bool use = k < NW ? ((tag >> k) & 1u) == (uint32_t)u : (u == 0 && crossed);
+                mk[k] = use ? sm[hh][0] : -INFINITY;   // (an unused slot may hold anything)
+                lk[k] = use ? sm[hh][1] : 0.f;
             }
             float M = -INFINITY;
 #pragma unroll
-            for (int k = 0; k <= NW; ++k) {
-                const bool use = k < NW ? ((tag >> k) & 1u) == (uint32_t)u : (u == 0 && crossed);
-                mk[k] = use ? mk[k] : -INFINITY;   // (an unused slot may hold anything)
-                lk[k] = use ? lk[k] : 0.f;
-                ok[k] = use ? ok[k] : 0.f;
-                M = fmaxf(M, mk[k]);
-            }
-            float L = 0.f, o = 0.f;
+            for (int k = 0; k <= NW; ++k) M = fmaxf(M, mk[k]);
+            float f[NW + 1], L = 0.f;
 #pragma unroll
             for (int k = 0; k <= NW; ++k) {
-                const float f = mk[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk[k] - M);
-                L = __builtin_fmaf(lk[k], f, L);
-                o = __builtin_fmaf(ok[k], f, o);
+                f[k] = mk[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk[k] - M);
+                L = __builtin_fmaf(lk[k], f[k], L);
+            }
+            const float rl = L > 0.f ? 1.f / L : 0.f;
+            f32x4 o0 = (f32x4)0.f, o1 = (f32x4)0.f;
+#pragma unroll
+            for (int k = 0; k <= NW; ++k) {
+                const float* sa = reinterpret_cast<const float*>(s_stage + k * PART) + hh * (D + 4) + d0;
+                const f32x4 x0 = *(const f32x4*)sa, x1 = *(const f32x4*)(sa + 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {   // a masked slot's values meet f = 0 only if finite: select
+                    o0[i] = __builtin_fmaf(f[k] > 0.f ? x0[i] : 0.f, f[k], o0[i]);
+                    o1[i] = __builtin_fmaf(f[k] > 0.f ? x1[i] : 0.f, f[k], o1[i]);
+                }
+            }
+            uint32_t h[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                h[i] = (uint32_t)f32_to_f16_bits(o0[2 * i] * rl) | ((uint32_t)f32_to_f16_bits(o0[2 * i + 1] * rl) << 16);
+                h[2 + i] = (uint32_t)f32_to_f16_bits(o1[2 * i] * rl) | ((uint32_t)f32_to_f16_bits(o1[2 * i + 1] * rl) << 16);
             }
             const int64_t row = (int64_t)(u ? seq_b : seq_a) * a.num_q_heads + kvh * G + q0 + hh;
-            a.out[row * D + d] = f32_to_f16_bits(L > 0.f ? o / L : 0.f);
+            *(u32x4*)&a.out[row * D + d0] = u32x4{h[0], h[1], h[2], h[3]};
         }
         return;
     }
