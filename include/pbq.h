@@ -527,6 +527,21 @@ kv_status kv_stream_read_tiles(const void* src_dev, int64_t n_src_tiles, int32_t
 /* Message of the last failed call on this thread ("" if none). */
 const char* kv_last_error(void);
 
+/* Debug checks of the callers' contracts (returns the previous setting;
+ * until the first call the environment variable PBQ_DEBUG_CHECKS, set to
+ * anything but "0", turns them on).  Before launching, kv_quantize_store,
+ * paged_attn_decode_append (and _noalloc) and paged_attn_decode_shared_prefix
+ * with a store then copy their index arrays to the host and fail with
+ * KV_ERR_INVALID when one call would write a physical block for two
+ * sequences, or a tail slot twice (tiles of one call are written
+ * concurrently: shared blocks must be copied first, deepinsea.top
+ * "PagedAttention memory management in depth", "Copy-on-Write"); and
+ * paged_attn_decode_shared_prefix fails when a sequence's table does not
+ * hold sequence 0's blocks for the shared positions or its context does not
+ * extend past them.  The copies synchronize the stream: for debugging, not
+ * for timed runs.  Process-wide; thread-safe. */
+int32_t kv_set_debug_checks(int32_t on);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,7 +12,8 @@ import os
 import torch  # loads the HIP runtime the library then shares
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpbq.so")
+# PBQ_LIB_PATH selects another build of the library (the sanitizer test's)
+LIB_PATH = os.environ.get("PBQ_LIB_PATH") or os.path.join(_HERE, "libpbq.so")
 
 KV_OK, KV_ERR_INVALID, KV_ERR_NO_BLOCKS, KV_ERR_UNKNOWN_SEQ, KV_ERR_STATE, \
     KV_ERR_NO_SLOTS, KV_ERR_HIP = range(7)
@@ -72,6 +73,7 @@ EXPORTS = [
     "paged_attn_decode_append", "paged_attn_decode_append_noalloc", "paged_attn_decode_shared_prefix", "paged_attn_multi_query",
     "paged_attn_multi_query_workspace_bytes",
     "paged_attn_default_partition", "kv_stream_read_sink_words", "kv_stream_read_tiles", "kv_last_error",
+    "kv_set_debug_checks",
 ]
 
 _lib = None
@@ -127,6 +129,7 @@ def lib():
             "kv_stream_read_sink_words": (SZ, [I64]),
             "kv_stream_read_tiles": (st, [VP, I64, I32, VP, I64, VP, SZ, VP]),
             "kv_last_error": (ctypes.c_char_p, []),
+            "kv_set_debug_checks": (I32, [I32]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -396,3 +399,9 @@ def kv_stream_read_sink_words(n_tiles):
 def kv_stream_read_tiles(src, n_src_tiles, tile_bytes, order, n_tiles, sink, stream=None):
     _check(lib().kv_stream_read_tiles(_ptr(src), int(n_src_tiles), int(tile_bytes), _ptr(order), int(n_tiles),
                                       _ptr(sink), int(sink.numel()), _stream(stream)))
+
+
+def kv_set_debug_checks(on):
+    """Turns the library's debug checks of caller contracts on or off;
+    returns the previous setting."""
+    return int(lib().kv_set_debug_checks(1 if on else 0))

@@ -7,6 +7,8 @@
 
 #include <atomic>
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 #include <vector>
 #include <algorithm>
@@ -138,6 +140,67 @@ int device_cu_count() {
     return n;
 }
 
+// ---- debug checks of caller contracts ------------------------------------
+// On when kv_set_debug_checks(1) was called, or (until then) when the
+// environment variable PBQ_DEBUG_CHECKS is set to anything but "0".  They
+// copy the calls' index arrays to the host (after synchronizing the stream),
+// so they are for debugging, not for timed runs.
+std::atomic<int> g_debug_checks{-1};
+
+bool debug_checks() {
+    int v = g_debug_checks.load(std::memory_order_relaxed);
+    if (v < 0) {
+        const char* e = std::getenv("PBQ_DEBUG_CHECKS");
+        v = e && *e && std::strcmp(e, "0") != 0 ? 1 : 0;
+        int expected = -1;
+        g_debug_checks.compare_exchange_strong(expected, v);
+        v = g_debug_checks.load(std::memory_order_relaxed);
+    }
+    return v > 0;
+}
+
+template <class T>
+kv_status fetch(const T* dev, size_t n, std::vector<T>& out, hipStream_t stream) {
+    out.assign(n, T{});
+    if (n == 0) return KV_OK;
+    kv_status st = hip_status(hipStreamSynchronize(stream), "debug check: stream synchronize");
+    if (st != KV_OK) return st;
+    return hip_status(hipMemcpy(out.data(), dev, n * sizeof(T), hipMemcpyDeviceToHost), "debug check: copy");
+}
+
+// The tiles one store call writes run concurrently: no physical block may be
+// written for two sequences, and no tail slot may be written twice (rows are
+// kept in a sequence's slot while its last block stays partial).  Sequence
+// s writes positions first[s] .. end[s] - 1 through its table row.
+kv_status check_disjoint_writes(const kv_pool_desc* d, const char* call, const std::vector<int32_t>& tables,
+                                int32_t max_blocks, const std::vector<int32_t>& first,
+                                const std::vector<int32_t>& end, const std::vector<int32_t>& slots) {
+    const int32_t bs = d->block_size;
+    std::vector<int32_t> owner_block(d->num_blocks, -1), owner_slot(d->max_seqs, -1);
+    for (size_t s = 0; s < first.size(); ++s) {
+        if (end[s] <= first[s]) continue;
+        for (int32_t j = first[s] / bs; j <= (end[s] - 1) / bs; ++j) {
+            if (j >= max_blocks) return fail(KV_ERR_INVALID, std::string(call) + ": a store runs past its table row");
+            const int32_t b = tables[s * (size_t)max_blocks + j];
+            if (b < 0 || b >= d->num_blocks) return fail(KV_ERR_INVALID, std::string(call) + ": block id out of range");
+            if (owner_block[b] >= 0 && owner_block[b] != (int32_t)s)
+                return fail(KV_ERR_INVALID, std::string(call) + ": block " + std::to_string(b) + " is written for sequences " +
+                                                std::to_string(owner_block[b]) + " and " + std::to_string(s) +
+                                                " in one call (copy-on-write first)");
+            owner_block[b] = (int32_t)s;
+        }
+        if (end[s] % bs != 0) {   // the last block stays partial: its rows go to the slot
+            const int32_t sl = slots[s];
+            if (sl < 0 || sl >= d->max_seqs) return fail(KV_ERR_INVALID, std::string(call) + ": tail slot out of range");
+            if (owner_slot[sl] >= 0)
+                return fail(KV_ERR_INVALID, std::string(call) + ": tail slot " + std::to_string(sl) +
+                                                " is written for two sequences in one call");
+            owner_slot[sl] = (int32_t)s;
+        }
+    }
+    return KV_OK;
+}
+
 }  // namespace
 
 kv_status fail(kv_status st, const std::string& msg) {
@@ -209,6 +272,36 @@ kv_status decode_impl(const kv_pool_desc* d, const kv_pool_mem* m, const AppendA
         const int64_t nq = (int64_t)num_seqs * (num_q_heads / d->num_kv_heads);
         if ((int64_t)d->num_kv_heads * ((nq + 15) / 16) > 65535)
             return fail(KV_ERR_INVALID, "too many queries per KV head for the shared-prefix launch");
+    }
+    if (pbq::debug_checks() && (app || shared_tokens > 0)) {
+        std::vector<int32_t> ctx, tab, sl;
+        const hipStream_t s = (hipStream_t)stream;
+        if ((st = pbq::fetch(context_lens, num_seqs, ctx, s)) != KV_OK ||
+            (st = pbq::fetch(block_tables, (size_t)num_seqs * max_blocks_per_seq, tab, s)) != KV_OK)
+            return st;
+        if (app) {   // each sequence stores its current token (position ctx - 1)
+            if ((st = pbq::fetch(app->tail_slots, num_seqs, sl, s)) != KV_OK) return st;
+            std::vector<int32_t> first(num_seqs);
+            for (int32_t i = 0; i < num_seqs; ++i) {
+                if (ctx[i] < 1 || ctx[i] > max_context_len)
+                    return fail(KV_ERR_INVALID, "decode with append: context_lens must be in [1, max_context_len]");
+                first[i] = ctx[i] - 1;
+            }
+            if ((st = pbq::check_disjoint_writes(d, "paged_attn_decode_append", tab, max_blocks_per_seq, first, ctx,
+                                                 sl)) != KV_OK)
+                return st;
+        }
+        if (shared_tokens > 0) {   // the prefix's blocks are sequence 0's for every sequence
+            const int32_t nb = shared_tokens / d->block_size;
+            for (int32_t i = 0; i < num_seqs; ++i) {
+                if (ctx[i] <= shared_tokens)
+                    return fail(KV_ERR_INVALID, "shared prefix: a context_lens entry does not exceed shared_tokens");
+                for (int32_t j = 0; j < nb; ++j)
+                    if (tab[i * (size_t)max_blocks_per_seq + j] != tab[j])
+                        return fail(KV_ERR_INVALID, "shared prefix: sequence " + std::to_string(i) + "'s block " +
+                                                        std::to_string(j) + " differs from sequence 0's");
+            }
+        }
     }
     const size_t need = paged_attn_workspace_bytes(d, num_seqs, num_q_heads, max_context_len, part);
     if (use_scratch) {
@@ -298,6 +391,11 @@ kv_status decode_impl(const kv_pool_desc* d, const kv_pool_mem* m, const AppendA
 extern "C" {
 
 const char* kv_last_error(void) { return pbq::g_last_error.c_str(); }
+
+int32_t kv_set_debug_checks(int32_t on) {
+    pbq::debug_checks();   // settle the environment default first
+    return pbq::g_debug_checks.exchange(on ? 1 : 0);
+}
 
 kv_status kv_pool_bytes(const kv_pool_desc* d, kv_pool_sizes* out) {
     if (!out) return fail(KV_ERR_INVALID, "out is NULL");
@@ -418,6 +516,19 @@ kv_status kv_quantize_store(const kv_pool_desc* d, const kv_pool_mem* m,
     if (!cu_seqlens || !start_pos || !block_tables || !tail_slots)
         return fail(KV_ERR_INVALID, "index arrays must be non-NULL");
     if (max_blocks_per_seq < 1) return fail(KV_ERR_INVALID, "max_blocks_per_seq must be >= 1");
+    if (pbq::debug_checks()) {
+        std::vector<int32_t> cu, sp, tab, sl;
+        const hipStream_t s = (hipStream_t)stream;
+        if ((st = pbq::fetch(cu_seqlens, num_seqs + 1, cu, s)) != KV_OK ||
+            (st = pbq::fetch(start_pos, num_seqs, sp, s)) != KV_OK ||
+            (st = pbq::fetch(block_tables, (size_t)num_seqs * max_blocks_per_seq, tab, s)) != KV_OK ||
+            (st = pbq::fetch(tail_slots, num_seqs, sl, s)) != KV_OK)
+            return st;
+        std::vector<int32_t> end(num_seqs);
+        for (int32_t i = 0; i < num_seqs; ++i) end[i] = sp[i] + (cu[i + 1] - cu[i]);
+        if ((st = pbq::check_disjoint_writes(d, "kv_quantize_store", tab, max_blocks_per_seq, sp, end, sl)) != KV_OK)
+            return st;
+    }
     pbq::QuantStoreArgs a{};
     a.block_size = d->block_size;
     a.num_kv_heads = d->num_kv_heads;

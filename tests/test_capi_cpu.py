@@ -423,3 +423,13 @@ def test_noalloc_validates_before_touching_the_device(lib):
     with pytest.raises(L.PBQError, match="scratch"):
         f(desc, mem, base, base, base, base, base, 4096, 2, base, 4096, base, 65536, 0.1, 256, 0)
     f(desc, mem, base, base, base, base, base, 0, 2, base, 4, base, 64, 0.1, 0, 0)
+
+
+def test_debug_checks_toggle(lib):
+    """kv_set_debug_checks returns the previous setting; the checks are off
+    unless PBQ_DEBUG_CHECKS asks for them."""
+    env_on = os.environ.get("PBQ_DEBUG_CHECKS", "0") not in ("", "0")
+    first = L.kv_set_debug_checks(True)
+    assert first == (1 if env_on else 0)
+    assert L.kv_set_debug_checks(False) == 1
+    assert L.kv_set_debug_checks(first) == 0

@@ -1061,3 +1061,52 @@ def test_stream_read_reads_every_listed_tile(tile_bytes, n_src, n, ordered):
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == expect
+
+
+def test_debug_checks_catch_contract_violations():
+    """With the library's debug checks on, a store or a decode with the
+    current token's store that would write one physical block for two
+    sequences fails before launching, and so does a shared-prefix decode whose
+    tables do not hold the same prefix blocks; valid calls go through (and
+    with the checks off the same calls are not inspected)."""
+    announce("debug-checks")
+    from paged_block_quantized_amd import PBQError, _lib as L
+    bs, hkv, d, hq = 16, 2, 64, 4
+    n = 3 * bs
+    dev = torch.device("cuda")
+    prev = L.kv_set_debug_checks(True)
+    try:
+        pool = make_pool(32, bs, hkv, d, "i8", max_seqs=4)
+        pool.alloc(0, n)                 # three full blocks
+        assert pool.fork(0, 1) == []     # sequence 1 shares them (aligned: no copy)
+        pool.alloc(2, bs + 4)            # a sequence of its own
+        rows = torch.zeros((3, hkv, d), dtype=torch.float16, device=dev)
+        # one token at position n - 1 of sequences 0 and 1: both in their shared block 2
+        tables, _, slots = pool.batch_tables([0, 1, 2], 4)
+        cu = torch.tensor([0, 1, 2, 3], dtype=torch.int32, device=dev)
+        start = torch.tensor([n - 1, n - 1, bs + 3], dtype=torch.int32, device=dev)
+        with pytest.raises(PBQError, match="written for sequences 0 and 1"):
+            pool.quantize_store(rows, rows, cu, start, tables.to(dev), slots.to(dev), 1)
+        # the same token of sequences 0 and 2 only: disjoint blocks, accepted
+        t02, _, s02 = pool.batch_tables([0, 2], 4)
+        pool.quantize_store(rows[:2], rows[:2], cu[:3], start[[0, 2]].contiguous(), t02.to(dev), s02.to(dev), 1)
+        torch.cuda.synchronize()
+        # the fused store of the current token (position n - 1) of sequences 0 and 1
+        q = torch.zeros((2, hq, d), dtype=torch.float16, device=dev)
+        out = torch.empty_like(q)
+        ctx01 = torch.tensor([n, n], dtype=torch.int32, device=dev)
+        t01, _, s01 = pool.batch_tables([0, 1], 4)
+        with pytest.raises(PBQError, match="paged_attn_decode_append: block"):
+            pool.decode_append(rows[:2], rows[:2], s01.to(dev), q, out, t01.to(dev), ctx01, n, 0.125, 2048)
+        # a shared prefix of two blocks, which sequence 1's table does not hold
+        bad = t01.clone()
+        bad[1, 0] = int(t02[1, 0])
+        with pytest.raises(PBQError, match="differs from sequence 0's"):
+            pool.decode_shared_prefix(q, out, bad.to(dev), ctx01, n, 0.125, 32, 32)
+        pool.decode_shared_prefix(q, out, t01.to(dev), ctx01, n, 0.125, 32, 32)   # the real tables
+        torch.cuda.synchronize()
+        assert L.kv_set_debug_checks(False) == 1
+        pool.decode_shared_prefix(q, out, t01.to(dev), ctx01, n, 0.125, 32, 32)
+        torch.cuda.synchronize()
+    finally:
+        L.kv_set_debug_checks(prev)
