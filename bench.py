@@ -445,7 +445,8 @@ def read_ceiling(setup, reps=10):
     from paged_block_quantized_amd import _lib as L
     w = setup.w
     H, bs, D = w.num_kv_heads, w.block_size, w.head_dim
-    k_tile = bs * D
+    from paged_block_quantized_amd import workloads as W
+    k_tile = bs * D // 2 if W.k_codec_of(w) == "i4" else bs * D
     v_tile = bs * D // 2 if w.v_codec == "i4" else bs * D
     if k_tile not in (1024, 2048, 4096) or v_tile not in (1024, 2048, 4096):
         return None
