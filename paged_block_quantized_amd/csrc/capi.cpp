@@ -348,10 +348,11 @@ kv_status decode_impl(const kv_pool_desc* d, const kv_pool_mem* m, const AppendA
     const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
     a.ws_out = need ? (float*)workspace : nullptr;
     a.ws_ml = need ? (float*)((char*)workspace + rows * (size_t)d->head_dim * 4) : nullptr;
-    if (app && max_parts > 1) {
-        // split partitions: the store kernel in one-token append mode, then
-        // the decode (all but one work group per sequence and head would
-        // carry the fused store's registers for nothing)
+    if (app && max_parts > 1 && !pbq::split_store_fused(a)) {
+        // split partitions whose fused kernel would lose occupancy: the store
+        // kernel in one-token append mode, then the decode (all but one work
+        // group per sequence and head would carry the fused store's
+        // registers for nothing)
         pbq::QuantStoreArgs sa{};
         sa.block_size = d->block_size;
         sa.num_kv_heads = d->num_kv_heads;

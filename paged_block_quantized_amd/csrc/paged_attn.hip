@@ -15,11 +15,13 @@
 //
 // Arithmetic: the per-(block, head) scales factor out of the inner products,
 // score_t = (sm_scale * s_k) * sum_d q_d * code_td and
-// acc_d += (p_t * s_v) * (code_td - zp); codes convert to fp32 exactly and all
-// accumulation is fp32.  Softmax is online, in base 2 (scores are
-// pre-multiplied by log2 e), with a running maximum that is uniform across the
-// wavefront so that rescaling is a uniform branch taken only when a block
-// raises the maximum.
+// acc_d += s_v * sum_t p_t * (code_td - zp); codes become fp16 exactly, the
+// products are exact and all accumulation is fp32.  The weights p_t (at
+// most 1, relative to the running maximum) enter the V products as fp16,
+// and the normaliser sums the same rounded values.  Softmax is online, in
+// base 2 (scores are pre-multiplied by log2 e), with a running maximum that
+// is uniform across the wavefront so that rescaling is a uniform branch
+// taken only when a block raises the maximum.
 //
 // MHA partition kernel (one query head per KV head): one workgroup per
 // (partition, head, sequence); each of its NW wavefronts takes a contiguous
@@ -40,8 +42,11 @@
 
 #include <math.h>
 
+#include <memory>
+#include <mutex>
 #include <type_traits>
 #include <utility>
+#include <vector>
 
 #include "device_common.h"
 #include "pbq_internal.h"
@@ -353,49 +358,52 @@ void attn_partition_mha(AttnArgs a) {
             zacc *= alpha;
             m = bmax;
         }
-        float pv[NR];
+        // The block's weights 2^(score - max), in (0, 1], rounded to fp16:
+        // both the V contraction (v_dot2_f32_f16 over pairs of tokens, the
+        // weights from scalar registers) and the normaliser use the rounded
+        // values, and the V scale applies to the block's sums in fp32, so
+        // that no weight leaves fp16's normal range because of the scale.
+        uint32_t ph[NR];
+        float ps = 0.f;   // the lane's sum of its rounded weights
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
-            const float pr = __builtin_amdgcn_exp2f(sc[j] - m);
-            l += pr;
-            pv[j] = pr * svv;
-            zacc = __builtin_fmaf(pv[j], vbias, zacc);
+            const _Float16 h = (_Float16)__builtin_amdgcn_exp2f(sc[j] - m);
+            ph[j] = (uint32_t)__builtin_bit_cast(uint16_t, h);
+            ps += (float)h;
         }
-        // weights of all tokens of the block, uniform across the wave
-        float sp[BS];
+        l += ps;
+        zacc = __builtin_fmaf(svv * vbias, ps, zacc);
+        // weights of all tokens of the block, uniform across the wave, as
+        // fp16 pairs in the token order of the V operands
+        uint32_t sw[BS];
 #pragma unroll
-        for (int t = 0; t < BS; ++t) sp[t] = readlane(pv[t / RPI], (t % RPI) * LPR);
+        for (int t = 0; t < BS; ++t) sw[t] = (uint32_t)readlane((int)ph[t / RPI], (t % RPI) * LPR);
+        auto wpair = [&](int t0, int t1) { return as_h2(sw[t0] | (sw[t1] << 16)); };
 #pragma unroll
         for (int k = 0; k < DPL; ++k) {
+            float b0 = 0.f, b1 = 0.f;
             if constexpr (V4) {
 #pragma unroll
                 for (int c = 0; c < VW; ++c) {   // tokens 8c .. 8c+7
                     const uint32_t wv = r.v[k][c];
                     const uint32_t lo = wv & 0x0F0F0F0Fu;         // tokens 0,2,4,6
                     const uint32_t hi = (wv >> 4) & 0x0F0F0F0Fu;  // tokens 1,3,5,7
-                    const f16x2 e0 = perm_lo(lo), e1 = perm_hi(lo);
-                    const f16x2 o0 = perm_lo(hi), o1 = perm_hi(hi);
                     const int t = 8 * c;
-                    acc[k][0] = __builtin_fmaf(sp[t + 0], (float)e0[0], acc[k][0]);
-                    acc[k][1] = __builtin_fmaf(sp[t + 1], (float)o0[0], acc[k][1]);
-                    acc[k][0] = __builtin_fmaf(sp[t + 2], (float)e0[1], acc[k][0]);
-                    acc[k][1] = __builtin_fmaf(sp[t + 3], (float)o0[1], acc[k][1]);
-                    acc[k][0] = __builtin_fmaf(sp[t + 4], (float)e1[0], acc[k][0]);
-                    acc[k][1] = __builtin_fmaf(sp[t + 5], (float)o1[0], acc[k][1]);
-                    acc[k][0] = __builtin_fmaf(sp[t + 6], (float)e1[1], acc[k][0]);
-                    acc[k][1] = __builtin_fmaf(sp[t + 7], (float)o1[1], acc[k][1]);
+                    b0 = __builtin_amdgcn_fdot2(perm_lo(lo), wpair(t + 0, t + 2), b0, false);
+                    b1 = __builtin_amdgcn_fdot2(perm_lo(hi), wpair(t + 1, t + 3), b1, false);
+                    b0 = __builtin_amdgcn_fdot2(perm_hi(lo), wpair(t + 4, t + 6), b0, false);
+                    b1 = __builtin_amdgcn_fdot2(perm_hi(hi), wpair(t + 5, t + 7), b1, false);
                 }
             } else {
 #pragma unroll
                 for (int c = 0; c < VW; ++c) {   // tokens 4c .. 4c+3
-                    const f16x2 a0 = as_h2(pair_lo<VC>(r.v[k][c])), a1 = as_h2(pair_hi<VC>(r.v[k][c]));
                     const int t = 4 * c;
-                    acc[k][0] = __builtin_fmaf(sp[t + 0], (float)a0[0], acc[k][0]);
-                    acc[k][1] = __builtin_fmaf(sp[t + 1], (float)a0[1], acc[k][1]);
-                    acc[k][0] = __builtin_fmaf(sp[t + 2], (float)a1[0], acc[k][0]);
-                    acc[k][1] = __builtin_fmaf(sp[t + 3], (float)a1[1], acc[k][1]);
+                    b0 = __builtin_amdgcn_fdot2(as_h2(pair_lo<VC>(r.v[k][c])), wpair(t, t + 1), b0, false);
+                    b1 = __builtin_amdgcn_fdot2(as_h2(pair_hi<VC>(r.v[k][c])), wpair(t + 2, t + 3), b1, false);
                 }
             }
+            acc[k][0] = __builtin_fmaf(b0, svv, acc[k][0]);
+            acc[k][1] = __builtin_fmaf(b1, svv, acc[k][1]);
         }
     };
 
@@ -2042,8 +2050,10 @@ __global__ __launch_bounds__(64) void attn_reduce_multi(AttnArgs a) {
 
 // Waves per work group of the MHA kernel: 8 when a partition holds at least
 // 64 blocks, else 4, so that each wave still streams several blocks.
+// join: an event the reduce waits for (the shared prefix's partitions on the
+// side stream), or nullptr.
 template <int BS, int D, int CP>
-hipError_t launch_mha(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_mha(const AttnArgs& a, hipStream_t stream, hipEvent_t join) {
     const dim3 grid = grid_dims(a.max_partitions - a.shared_parts, a.num_q_heads, a.num_seqs);
     const bool fused = a.k_new != nullptr;
     if (a.partition_blocks >= 64) {
@@ -2055,9 +2065,32 @@ hipError_t launch_mha(const AttnArgs& a, hipStream_t stream) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_partitions <= 1) return e;
+    if (join && (e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return e;
     hipLaunchKernelGGL((attn_reduce<BS, D>), dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(64), 0,
                        stream, a);
     return hipGetLastError();
+}
+
+// Work groups of one kernel that fit a compute unit at once (0 if unknown).
+int groups_per_cu(const void* kernel, int threads) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return n;
+}
+
+// Whether the MHA kernel carrying the fused store fits as many work groups
+// per compute unit as the plain one (looked up once per instantiation).
+template <int BS, int D, int CP, int NW>
+bool mha_fused_keeps_occupancy() {
+    static const bool same = [] {
+        const int f = groups_per_cu((const void*)&attn_partition_mha<BS, D, CP, NW, true>, 64 * NW);
+        const int p = groups_per_cu((const void*)&attn_partition_mha<BS, D, CP, NW, false>, 64 * NW);
+        return f > 0 && f == p;
+    }();
+    return same;
 }
 
 // Waves per work group of the grouped-query kernel: 2 for a single pass (the
@@ -2070,7 +2103,7 @@ hipError_t launch_mha(const AttnArgs& a, hipStream_t stream) {
 #define PBQ_GQA_SINGLE_WAVES 2
 #endif
 template <int BS, int D, int CP>
-hipError_t launch_gqa(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_gqa(const AttnArgs& a, hipStream_t stream, hipEvent_t join) {
     const int G = a.num_q_heads / a.num_kv_heads;
     const int n_ht = (G + 15) / 16;
     // paired four-wave groups, (KV head x 16-query tile, pair of sequences):
@@ -2106,6 +2139,7 @@ hipError_t launch_gqa(const AttnArgs& a, hipStream_t stream) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_partitions <= 1) return e;
+    if (join && (e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return e;
     hipLaunchKernelGGL((attn_reduce<BS, D>), dim3((unsigned)a.num_q_heads, (unsigned)a.num_seqs), dim3(64), 0,
                        stream, a);
     return hipGetLastError();
@@ -2162,15 +2196,97 @@ hipError_t launch_multi(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// A second stream per device for a shared prefix's partitions, which then
+// run beside the per-sequence partitions: forked from the caller's stream
+// and joined back before the reduce with events, so that a captured call
+// stays one graph.  Created on first use and kept until the process ends;
+// when it cannot be created the prefix's partitions run on the caller's
+// stream first.  The mutex keeps one call's record / wait pairs together
+// when several host threads launch at once.
+#ifndef PBQ_SIDE_STREAM
+#define PBQ_SIDE_STREAM 1
+#endif
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    std::mutex mu;
+};
+
+SideStream* side_stream() {
+    static std::mutex mu;
+    static std::vector<std::unique_ptr<SideStream>> per_device;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)per_device.size() <= dev) per_device.resize(dev + 1);
+    if (!per_device[dev]) {
+        auto ss = std::make_unique<SideStream>();
+        if (hipStreamCreateWithFlags(&ss->s, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&ss->join, hipEventDisableTiming) != hipSuccess) {
+            (void)hipGetLastError();
+            ss->s = nullptr;
+        }
+        per_device[dev] = std::move(ss);
+    }
+    return per_device[dev]->s ? per_device[dev].get() : nullptr;
+}
+
+template <int BS, int D, int CP>
+hipError_t launch_per_sequence(const AttnArgs& a, hipStream_t stream, hipEvent_t join) {
+    if (a.num_q_heads != a.num_kv_heads) return launch_gqa<BS, D, CP>(a, stream, join);
+    return launch_mha<BS, D, CP>(a, stream, join);
+}
+
 template <int BS, int D, int CP>
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
     if (a.cu_q) return launch_multi<BS, D, CP>(a, stream);
-    if (a.shared_parts > 0) {
+    if (a.shared_parts == 0) return launch_per_sequence<BS, D, CP>(a, stream, nullptr);
+    SideStream* ss = PBQ_SIDE_STREAM ? side_stream() : nullptr;
+    if (!ss) {
         const hipError_t e = launch_shared<BS, D, CP>(a, stream);
-        if (e != hipSuccess) return e;
+        return e != hipSuccess ? e : launch_per_sequence<BS, D, CP>(a, stream, nullptr);
     }
-    if (a.num_q_heads != a.num_kv_heads) return launch_gqa<BS, D, CP>(a, stream);
-    return launch_mha<BS, D, CP>(a, stream);
+    std::lock_guard<std::mutex> lock(ss->mu);
+    hipError_t e;
+    if ((e = hipEventRecord(ss->fork, stream)) != hipSuccess ||
+        (e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess ||
+        (e = launch_shared<BS, D, CP>(a, ss->s)) != hipSuccess || (e = hipEventRecord(ss->join, ss->s)) != hipSuccess)
+        return e;
+    return launch_per_sequence<BS, D, CP>(a, stream, ss->join);
+}
+
+// Whether a split-partition decode with the current token's store fuses the
+// store into its partition kernel: for MHA launches whose fused kernel keeps
+// the plain kernel's occupancy (otherwise the store kernel runs first).
+#ifndef PBQ_SPLIT_STORE_FUSED
+#define PBQ_SPLIT_STORE_FUSED 1
+#endif
+bool split_store_fused(const AttnArgs& a) {
+    if (!PBQ_SPLIT_STORE_FUSED || a.cu_q || a.num_q_heads != a.num_kv_heads) return false;
+    auto pick = [&](auto bs, auto d) {
+        constexpr int BS = decltype(bs)::value, D = decltype(d)::value;
+        bool same = false;
+        (void)with_codec_pair(a.k_codec, a.v_codec, [&](auto cp) {
+            constexpr int CP = decltype(cp)::value;
+            same = a.partition_blocks >= 64 ? mha_fused_keeps_occupancy<BS, D, CP, 8>()
+                                            : mha_fused_keeps_occupancy<BS, D, CP, 4>();
+            return hipSuccess;
+        });
+        return same;
+    };
+    using I16 = std::integral_constant<int, 16>;
+    using I32 = std::integral_constant<int, 32>;
+    using I64 = std::integral_constant<int, 64>;
+    using I128 = std::integral_constant<int, 128>;
+    if (a.block_size == 16 && a.head_dim == 64) return pick(I16{}, I64{});
+    if (a.block_size == 16 && a.head_dim == 128) return pick(I16{}, I128{});
+    if (a.block_size == 32 && a.head_dim == 64) return pick(I32{}, I64{});
+    if (a.block_size == 32 && a.head_dim == 128) return pick(I32{}, I128{});
+    return false;
 }
 
 hipError_t launch_paged_attn(const AttnArgs& a, hipStream_t stream) {

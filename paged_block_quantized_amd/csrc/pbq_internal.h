@@ -172,6 +172,9 @@ hipError_t launch_quantize_store(const QuantStoreArgs& a, hipStream_t stream);
 hipError_t launch_stream_read(const StreamReadArgs& a, hipStream_t stream);
 int64_t stream_read_groups(int64_t n_tiles, int64_t tiles_per_wave);
 hipError_t launch_paged_attn(const AttnArgs& a, hipStream_t stream);
+// whether a split-partition decode fuses the current token's store into its
+// partition kernel (else the store kernel runs first)
+bool split_store_fused(const AttnArgs& a);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_swap_blocks(const SwapArgs& a, hipStream_t stream);
 

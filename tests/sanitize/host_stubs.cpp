@@ -21,6 +21,7 @@ int64_t stream_read_groups(int64_t n_tiles, int64_t tiles_per_wave) {
     return (waves + 3) / 4;
 }
 hipError_t launch_paged_attn(const AttnArgs&, hipStream_t) { return hipErrorNotSupported; }
+bool split_store_fused(const AttnArgs&) { return false; }
 hipError_t launch_copy_blocks(const CopyArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_swap_blocks(const SwapArgs&, hipStream_t) { return hipErrorNotSupported; }
 

@@ -955,19 +955,20 @@ def _scaled_v_case(bs, d, vc, g, hkv, kind, seed):
     return ctx, hk, hv, q, sigma
 
 
-SCALED_V = [(bs, g, vc, kind) for bs, g in ((32, 8), (16, 4)) for vc in ("i8", "i4", "i8a", "fp8")
-            for kind in ("small3", "small4", "mixed")]
+SCALED_V = [(bs, g, vc, kind) for bs, g in ((32, 8), (16, 4), (32, 1), (16, 1))
+            for vc in ("i8", "i4", "i8a", "fp8") for kind in ("small3", "small4", "mixed")]
 
 
 @pytest.mark.parametrize("bs,g,vc,kind", SCALED_V)
-def test_gqa_decode_scaled_v(bs, g, vc, kind):
-    """Grouped-query decode with V far from unit magnitude: outputs within
-    tolerance relative to the V magnitude (attention is linear in V), for
-    the plain decode at several partition sizes and for the fused store +
-    decode (single pass).  The matrix cores take fp16 weights p * sv; they
-    are normalised by a power of two that follows the V scales, so tiny
-    scales keep full fp16 precision."""
-    announce("gqa-scaled-v", bs, g, vc, kind)
+def test_decode_scaled_v(bs, g, vc, kind):
+    """Decode with V far from unit magnitude, grouped-query (g > 1) and MHA
+    (g = 1): outputs within tolerance relative to the V magnitude (attention
+    is linear in V), for the plain decode at several partition sizes and for
+    the fused store + decode (single pass).  Both kernels weight V with fp16
+    values: the matrix cores take p * sv normalised by a power of two that
+    follows the V scales, the MHA kernel takes p alone and applies the V
+    scale per block in fp32, so tiny scales keep full fp16 precision."""
+    announce("scaled-v", bs, g, vc, kind)
     from paged_block_quantized_amd import KVPool
     d, hkv = 128, 2
     ctx, hk, hv, q, sigma = _scaled_v_case(bs, d, vc, g, hkv, kind, seed=bs + g + len(kind))
@@ -979,7 +980,7 @@ def test_gqa_decode_scaled_v(bs, g, vc, kind):
     ref = case.reference()
     for part in (0, 32, 4096):
         got = case.decode(part)
-        assert_close(got / sigma, ref / sigma, f"gqa scaled V {kind} {vc} bs{bs} part{part}")
+        assert_close(got / sigma, ref / sigma, f"scaled V g{g} {kind} {vc} bs{bs} part{part}")
     # the fused store + decode: every token but the last stored first
     dev = "cuda"
     S = len(ctx)
@@ -1004,7 +1005,7 @@ def test_gqa_decode_scaled_v(bs, g, vc, kind):
     pool.decode_append(k_new, v_new, slots.to(dev), qd, out, tables.to(dev), ctx_h.to(dev), max(ctx),
                        1 / np.sqrt(d), 4096)
     torch.cuda.synchronize()
-    assert_close(out.cpu().numpy() / sigma, ref / sigma, f"gqa fused scaled V {kind} {vc} bs{bs}")
+    assert_close(out.cpu().numpy() / sigma, ref / sigma, f"fused scaled V g{g} {kind} {vc} bs{bs}")
 
 
 @pytest.mark.parametrize("bs,g,vc,kind", [(32, 8, vc, k) for vc in ("i8", "i4", "i8a", "fp8")
