@@ -710,10 +710,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // that of two waves (no spills into AGPRs).  Two-wave multi-query groups use
 // at most about 26 KiB (a shared three-stage area, or a merge through one
 // wave's slot), room for three waves per SIMD, and get that register budget.
+#ifndef PBQ_MULTI_WAVES_PER_EU
+#define PBQ_MULTI_WAVES_PER_EU 3
+#endif
 template <int D, int CP, bool FUSED, bool MULTI, int NW, bool PAIR>
 constexpr int gqa_waves_per_eu() {
     if (PAIR) return 2;   // two four-wave groups per CU
-    if (MULTI && NW == 2) return 3;
+    if (MULTI && NW == 2) return PBQ_MULTI_WAVES_PER_EU;
     return MULTI || (!FUSED && D == 128 && !codec_packed4(CP % 4)) ? 2 : PBQ_GQA_WAVES_PER_EU;
 }
 
