@@ -2202,10 +2202,12 @@ hipError_t launch_multi(const AttnArgs& a, hipStream_t stream) {
 // A second stream per device for a shared prefix's partitions, which then
 // run beside the per-sequence partitions: forked from the caller's stream
 // and joined back before the reduce with events, so that a captured call
-// stays one graph.  Created on first use and kept until the process ends;
-// when it cannot be created the prefix's partitions run on the caller's
-// stream first.  The mutex keeps one call's record / wait pairs together
-// when several host threads launch at once.
+// stays one graph.  Created on first use outside a stream capture (creating
+// it while the caller's stream captures could end the capture) and kept
+// until the process ends; until then, or when it cannot be created, the
+// prefix's partitions run on the caller's stream first.  The mutex keeps one
+// call's record / wait pairs together when several host threads launch at
+// once.
 #ifndef PBQ_SIDE_STREAM
 #define PBQ_SIDE_STREAM 1
 #endif
@@ -2215,7 +2217,7 @@ struct SideStream {
     std::mutex mu;
 };
 
-SideStream* side_stream() {
+SideStream* side_stream(hipStream_t caller) {
     static std::mutex mu;
     static std::vector<std::unique_ptr<SideStream>> per_device;
     int dev = 0;
@@ -2226,6 +2228,11 @@ SideStream* side_stream() {
     std::lock_guard<std::mutex> lock(mu);
     if ((int)per_device.size() <= dev) per_device.resize(dev + 1);
     if (!per_device[dev]) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
         auto ss = std::make_unique<SideStream>();
         if (hipStreamCreateWithFlags(&ss->s, hipStreamNonBlocking) != hipSuccess ||
             hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming) != hipSuccess ||
@@ -2248,7 +2255,7 @@ template <int BS, int D, int CP>
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
     if (a.cu_q) return launch_multi<BS, D, CP>(a, stream);
     if (a.shared_parts == 0) return launch_per_sequence<BS, D, CP>(a, stream, nullptr);
-    SideStream* ss = PBQ_SIDE_STREAM ? side_stream() : nullptr;
+    SideStream* ss = PBQ_SIDE_STREAM ? side_stream(stream) : nullptr;
     if (!ss) {
         const hipError_t e = launch_shared<BS, D, CP>(a, stream);
         return e != hipSuccess ? e : launch_per_sequence<BS, D, CP>(a, stream, nullptr);
