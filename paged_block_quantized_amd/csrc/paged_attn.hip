@@ -604,11 +604,14 @@ void attn_partition_mha(AttnArgs a) {
 #endif
 constexpr int kPairRankMax = PBQ_PAIR_RANK_MAX;
 // Loop steps the two waves of a paired group that quantize the stored tiles
-// and take the stored steps give up to the other two (their quantize of a K
-// and a V tile keeps them from streaming for about as long as six steps take
-// on gqa70b's shapes).
+// and take the stored steps give up to the other two, measured best on
+// gqa70b's shapes: 9 of its 32-token steps (6 and 12 were slower), and 12
+// of the shorter INT4 K steps.
 #ifndef PBQ_PAIR_HANDICAP
-#define PBQ_PAIR_HANDICAP 6
+#define PBQ_PAIR_HANDICAP 9
+#endif
+#ifndef PBQ_PAIR_HANDICAP_K4
+#define PBQ_PAIR_HANDICAP_K4 12
 #endif
 // LDS of a paired group (two per CU must fit): per wave two stages of a
 // step's codes (or a result slot, if larger), one more slot, and with the
@@ -617,7 +620,7 @@ constexpr int kPairLdsMax = 76 * 1024;   // the ranking's arrays need a few KiB 
 template <int BS, int D, int CP, bool FUSED>
 constexpr int gqa_pair_lds() {
     constexpr bool V4 = codec_packed4(CP % 4), K4 = codec_packed4(CP / 4);
-    constexpr int stg = (32 * D / 1024) * (1024 + 64) + (32 / BS) * D * (V4 ? BS / 2 : BS);
+    constexpr int stg = (32 * (K4 ? D / 2 : D) / 1024) * (1024 + 64) + (32 / BS) * D * (V4 ? BS / 2 : BS);
     constexpr int slot = 16 * (D + 4) * 4 + 16 * 8;
     constexpr int part = ((PBQ_GQA_STAGES * stg > slot ? PBQ_GQA_STAGES * stg : slot) + 15) / 16 * 16;
     return 4 * part + slot + (FUSED ? 2 * (BS * (K4 ? D / 2 : D) + D * (V4 ? BS / 2 : BS)) : 0);
@@ -758,7 +761,9 @@ void attn_partition_gqa(AttnArgs a) {
     // (INT4 K rows are not staged: their codes stay on the register path)
     constexpr bool JOINT = MULTI && NW == 2 && TPW == 2 && PBQ_MULTI_JOINT_STAGE && !K4;
     constexpr int QW = JOINT ? NW * QT : QT;   // queries per work group
-    constexpr bool STAGED = K4 ? false
+    // INT4 K is staged in paired groups (D 128: 64-byte rows, four chunks);
+    // other INT4 K launches keep its codes on the register path
+    constexpr bool STAGED = K4 ? (PAIR && D == 128)
                           : PAIR ? true
                           : FUSED ? PBQ_GQA_STAGE_FUSED
                           : (JOINT ? true : (MULTI && !V4 ? PBQ_MULTI_BYTEV_STAGE : PBQ_GQA_STAGE));
@@ -841,20 +846,18 @@ void attn_partition_gqa(AttnArgs a) {
             // order depends on it), then the reversed index, so that all keys
             // differ and the rank is the number of larger keys; two threads
             // per sequence when S <= NT / 2, each counting over half of the
-            // keys (four at a time).
+            // keys (four at a time).  A length below the clamp is read back
+            // from its key.
             __shared__ int s_pair[2];
             __shared__ __align__(16) uint32_t s_key[kPairRankMax];
-            __shared__ int s_len[kPairRankMax];
-            __shared__ int s_half[2][kPairRankMax / 2];   // (row 1 used)
+            __shared__ int s_half[kPairRankMax / 2];   // the second half's counts
             __shared__ int s_slot[FUSED ? kPairRankMax : 1];
             const int S4 = (S + 3) & ~3;
             for (int i = threadIdx.x; i < S4; i += NT) {
                 const int len = i < S ? a.context_lens[i] : 0;
                 s_key[i] = i < S ? ((uint32_t)min(len, (1 << 22) - 1) << 9) | (uint32_t)(511 - i) : 0u;
-                if (i < S) {
-                    s_len[i] = len;
-                    if constexpr (FUSED) s_slot[i] = a.tail_slots[i];
-                }
+                if constexpr (FUSED)
+                    if (i < S) s_slot[i] = a.tail_slots[i];
             }
             if (threadIdx.x < 2) s_pair[threadIdx.x] = -1;
             __syncthreads();
@@ -876,19 +879,23 @@ void attn_partition_gqa(AttnArgs a) {
                 const int i = (int)threadIdx.x % HT, half = (int)threadIdx.x / HT;
                 const int mid = (S4 / 8) * 4;   // S4 / 2 rounded down to 4
                 const int cnt = i < S ? count(i, half ? mid : 0, half ? S4 : mid) : 0;
-                if (half == 1 && i < S) s_half[1][i] = cnt;   // i < NT / 2 <= kPairRankMax / 2
+                if (half == 1 && i < S) s_half[i] = cnt;   // i < NT / 2 <= kPairRankMax / 2
                 __syncthreads();
-                if (half == 0 && i < S) found(i, cnt + s_half[1][i]);
+                if (half == 0 && i < S) found(i, cnt + s_half[i]);
             } else {
                 for (int i = threadIdx.x; i < S; i += NT) found(i, count(i, 0, S4));
             }
             __syncthreads();
             seq_a = s_pair[0];
             seq_b = s_pair[1];
-            pctx[0] = s_len[seq_a];
+            auto len_of = [&](int i) {
+                const int k = (int)(s_key[i] >> 9);
+                return k < (1 << 22) - 1 ? k : a.context_lens[i];
+            };
+            pctx[0] = len_of(seq_a);
             if constexpr (FUSED) pslot[0] = s_slot[seq_a];
             if constexpr (PAIR) {
-                if (seq_b >= 0) pctx[1] = s_len[seq_b];
+                if (seq_b >= 0) pctx[1] = len_of(seq_b);
                 if (FUSED && seq_b >= 0) pslot[1] = s_slot[seq_b];
             }
         } else {
@@ -1340,9 +1347,9 @@ void attn_partition_gqa(AttnArgs a) {
     // rows each, chunks swizzled by kswz, padded by 64 bytes), then its BPS V
     // tiles as in the pool.
     constexpr int SD = JOINT ? 3 : PBQ_GQA_STAGES;
-    constexpr int CPR = D / 16;                // 16-byte chunks per K row
-    constexpr int RPR = 1024 / D;              // K rows per load
-    constexpr int NKL = 32 * D / 1024;         // K loads per step
+    constexpr int CPR = KROW / 16;             // 16-byte chunks per K row
+    constexpr int RPR = 1024 / KROW;           // K rows per load
+    constexpr int NKL = 32 * KROW / 1024;      // K loads per step
     constexpr int KREG = 1024 + 64;
     constexpr int NVL = BPS * VT / 1024;       // V loads per step
     constexpr int NI = NKL + NVL;
@@ -1369,7 +1376,7 @@ void attn_partition_gqa(AttnArgs a) {
     // (unsigned: a uniform base plus a 32-bit lane offset is the
     // instruction's scalar-base form)
     const int dma_r = lane / CPR;
-    const uint32_t dma_k = (uint32_t)(dma_r * D + 16 * ((lane % CPR) ^ kswz(dma_r)));
+    const uint32_t dma_k = (uint32_t)(dma_r * KROW + 16 * ((lane % CPR) ^ kswz(dma_r)));
     const uint32_t dma_v = 16u * (uint32_t)lane;
     int ko[2][NKC];
 #pragma unroll
@@ -1377,7 +1384,7 @@ void attn_partition_gqa(AttnArgs a) {
         const int R = kblk[mt] * BS + krow[mt];   // row within the step
 #pragma unroll
         for (int c = 0; c < NKC; ++c)
-            ko[mt][c] = (R / RPR) * KREG + (R % RPR) * D + 16 * ((grp + 4 * c) ^ kswz(R % RPR));
+            ko[mt][c] = (R / RPR) * KREG + (R % RPR) * KROW + 16 * ((grp + 4 * c) ^ kswz(R % RPR));
     }
     const int vo = NKL * KREG + my_blk * VT + vcol + n16 * VROW;
 
@@ -1390,7 +1397,7 @@ void attn_partition_gqa(AttnArgs a) {
         for (int g = 0; g < NKL; ++g) {
             const int row0 = g * RPR;             // a load lies in one block
             if (!JOINT || g % NW == w)            // JOINT: the waves take turns
-                load_to_lds<NTL>((row0 / BS ? kb1 : kb0) + (row0 % BS) * D + dma_k, sb + g * KREG);
+                load_to_lds<NTL>((row0 / BS ? kb1 : kb0) + (row0 % BS) * KROW + dma_k, sb + g * KREG);
         }
         const uint8_t* vb0 = a.v_codes + ((int64_t)id0 * H + kvh) * VT;
         const uint8_t* vb1 = a.v_codes + ((int64_t)id1 * H + kvh) * VT;
@@ -1634,7 +1641,7 @@ void attn_partition_gqa(AttnArgs a) {
         // step each (fused): they get hc fewer loop steps.  Run k of the
         // loop steps laid end to end is [px(k), px(k + 1)).
         const int N = n_a + n_b;
-        const int hc = FUSED ? min(PBQ_PAIR_HANDICAP, N / 4) : 0;
+        const int hc = FUSED ? min(K4 ? PBQ_PAIR_HANDICAP_K4 : PBQ_PAIR_HANDICAP, N / 4) : 0;
         auto px = [&](int k) { return (k * (N + 2 * hc)) / NW - (k > 0 ? hc : 0) - (k == NW ? hc : 0); };
         const bool last_a = FUSED && nblk_a > 0;                  // stored steps: wave 0 ...
         const bool last_b = FUSED && seq_b >= 0 && nblk_b > 0;    // ... and wave NW - 1
@@ -1821,7 +1828,7 @@ void attn_partition_gqa(AttnArgs a) {
     // 16-byte writes of one instruction spread over the banks.
     constexpr int DP = D + 4;
     float (*s_acc)[QT][DP] = reinterpret_cast<float (*)[QT][DP]>(s_stage);
-    __shared__ float s_ml[NW][QT][2];
+    __shared__ float s_ml[PAIR ? 1 : NW][QT][2];   // (paired groups merge in their slots)
     if constexpr (STAGED) __syncthreads();
     if constexpr (JOINT) {
         // each wave holds every token of its queries: normalise and write
@@ -2111,8 +2118,9 @@ hipError_t launch_gqa(const AttnArgs& a, hipStream_t stream, hipEvent_t join) {
     const int n_ht = (G + 15) / 16;
     // paired four-wave groups, (KV head x 16-query tile, pair of sequences):
     // single passes whose contexts fit the groups' LDS block tables (INT4 K
-    // keeps its codes on the register path, which pairs do not use)
-    if constexpr (PBQ_GQA_PAIR && !codec_packed4(CP / 4)) {
+    // at head_dim 64 keeps its codes on the register path, which pairs do
+    // not use)
+    if constexpr (PBQ_GQA_PAIR && (!codec_packed4(CP / 4) || D == 128)) {
         const dim3 pg(1u, (unsigned)(a.num_kv_heads * n_ht), (unsigned)((a.num_seqs + 1) / 2));
         if (a.max_partitions == 1 && a.shared_parts == 0) {
             if constexpr (gqa_pair_lds<BS, D, CP, true>() <= kPairLdsMax) {

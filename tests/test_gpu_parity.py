@@ -401,10 +401,11 @@ PAIR_CONTEXTS = {
 
 
 @pytest.mark.parametrize("name", list(PAIR_CONTEXTS))
-@pytest.mark.parametrize("vc", ["i4", "fp8"])
+@pytest.mark.parametrize("vc", ["i4", "fp8", "k4i4", "k4i8"])
 def test_paired_groups(name, vc):
     """Paired grouped-query groups against the oracle, plain decode and fused
-    store + decode, in one pass; the fused call is reproducible bit for bit."""
+    store + decode, in one pass; the fused call is reproducible bit for bit.
+    INT4 K (k4i4, k4i8) stages its 64-byte rows through LDS like byte K."""
     announce("paired", name, vc)
     ctx = PAIR_CONTEXTS[name]
     check_decode_append(32, 128, vc, 8, ctx, (2048,), seed=len(ctx) + 3 * sum(ctx) % 1000, repeat=True)
