@@ -604,11 +604,11 @@ void attn_partition_mha(AttnArgs a) {
 #endif
 constexpr int kPairRankMax = PBQ_PAIR_RANK_MAX;
 // Loop steps the two waves of a paired group that quantize the stored tiles
-// and take the stored steps give up to the other two, measured best on
-// gqa70b's shapes: 9 of its 32-token steps (6 and 12 were slower), and 12
-// of the shorter INT4 K steps.
+// and take the stored steps give up to the other two, measured on gqa70b's
+// shapes: 6 of its 32-token steps (3 was slower, 9 within the noise), and
+// 12 of the shorter INT4 K steps (against 6: 1-2 us less).
 #ifndef PBQ_PAIR_HANDICAP
-#define PBQ_PAIR_HANDICAP 9
+#define PBQ_PAIR_HANDICAP 6
 #endif
 #ifndef PBQ_PAIR_HANDICAP_K4
 #define PBQ_PAIR_HANDICAP_K4 12
