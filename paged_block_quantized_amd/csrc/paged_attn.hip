@@ -122,6 +122,13 @@ __device__ __forceinline__ TileStoreArgs fused_store_args(const AttnArgs& a) {
 #ifndef PBQ_MHA_WAVES_PER_EU
 #define PBQ_MHA_WAVES_PER_EU 1
 #endif
+// Cache policy of the split-K partial results (1: non-temporal): written
+// once in the middle of the codes' read stream and read once by the reduce,
+// they cost the stream less non-temporal (shared_prefix's 512-token
+// partitions: 2-4 % on the step).
+#ifndef PBQ_WS_NT
+#define PBQ_WS_NT 1
+#endif
 
 // Software pipeline over cnt >= 1 steps: the codes of the next DEPTH-1 steps
 // are in flight while one step is computed.  Every load outside the short
@@ -526,10 +533,10 @@ void attn_partition_mha(AttnArgs a) {
             a.out[row * D + tid] = f32_to_f16_bits(res);
         } else {
             const int64_t prow = row * a.max_partitions + p;
-            a.ws_out[prow * D + tid] = res;
+            store_once<PBQ_WS_NT>(res, &a.ws_out[prow * D + tid]);
             if (tid == 0) {
-                a.ws_ml[prow * 2] = M;
-                a.ws_ml[prow * 2 + 1] = L;
+                store_once<PBQ_WS_NT>(M, &a.ws_ml[prow * 2]);
+                store_once<PBQ_WS_NT>(L, &a.ws_ml[prow * 2 + 1]);
             }
         }
     }
@@ -1851,10 +1858,10 @@ void attn_partition_gqa(AttnArgs a) {
                         *(u32x2*)&a.out[row * D + d] = u32x2{lo, hi};
                     } else {
                         const int64_t prow = row * a.max_partitions + p;
-                        *(f32x4*)&a.ws_out[prow * D + d] = f32x4{res[0], res[1], res[2], res[3]};
+                        store_once<PBQ_WS_NT>(f32x4{res[0], res[1], res[2], res[3]}, (f32x4*)&a.ws_out[prow * D + d]);
                         if (t == 0 && grp == 0) {
-                            a.ws_ml[prow * 2] = m[T];
-                            a.ws_ml[prow * 2 + 1] = L;
+                            store_once<PBQ_WS_NT>(m[T], &a.ws_ml[prow * 2]);
+                            store_once<PBQ_WS_NT>(L, &a.ws_ml[prow * 2 + 1]);
                         }
                     }
                 }
@@ -1920,10 +1927,10 @@ void attn_partition_gqa(AttnArgs a) {
                 a.out[row * D + d] = f32_to_f16_bits(res);
             } else {
                 const int64_t prow = row * a.max_partitions + p;
-                a.ws_out[prow * D + d] = res;
+                store_once<PBQ_WS_NT>(res, &a.ws_out[prow * D + d]);
                 if (d == 0) {
-                    a.ws_ml[prow * 2] = s_ml[0][hh][0];
-                    a.ws_ml[prow * 2 + 1] = s_ml[0][hh][1];
+                    store_once<PBQ_WS_NT>(s_ml[0][hh][0], &a.ws_ml[prow * 2]);
+                    store_once<PBQ_WS_NT>(s_ml[0][hh][1], &a.ws_ml[prow * 2 + 1]);
                 }
             }
         }
@@ -1961,10 +1968,10 @@ void attn_partition_gqa(AttnArgs a) {
             a.out[row * D + d] = f32_to_f16_bits(res);
         } else {
             const int64_t prow = row * a.max_partitions + p;
-            a.ws_out[prow * D + d] = res;
+            store_once<PBQ_WS_NT>(res, &a.ws_out[prow * D + d]);
             if (d == 0) {
-                a.ws_ml[prow * 2] = M;
-                a.ws_ml[prow * 2 + 1] = L;
+                store_once<PBQ_WS_NT>(M, &a.ws_ml[prow * 2]);
+                store_once<PBQ_WS_NT>(L, &a.ws_ml[prow * 2 + 1]);
             }
         }
     }
