@@ -124,8 +124,8 @@ __device__ __forceinline__ TileStoreArgs fused_store_args(const AttnArgs& a) {
 #endif
 // Cache policy of the split-K partial results (1: non-temporal): written
 // once in the middle of the codes' read stream and read once by the reduce,
-// they cost the stream less non-temporal (shared_prefix's 512-token
-// partitions: 2-4 % on the step).
+// they cost the stream less non-temporal (the 512-token partitions of 32
+// sequences x 32768 tokens over a shared prefix: 2-4 % on the step).
 #ifndef PBQ_WS_NT
 #define PBQ_WS_NT 1
 #endif
@@ -583,14 +583,16 @@ void attn_partition_mha(AttnArgs a) {
 // Multi-query groups with byte-coded V that do not stage jointly (one tile
 // per wave, or the four-wave groups of split partitions) keep the register
 // path too: their waves re-read codes the L2 mostly holds (measured before
-// joint staging existed: 4 % faster than per-wave staging on prefill_chunk).
+// joint staging existed: 4 % faster than per-wave staging on 512-query
+// chunks over 4096 tokens, MHA, INT8).
 #ifndef PBQ_MULTI_BYTEV_STAGE
 #define PBQ_MULTI_BYTEV_STAGE 0
 #endif
 // Two-wave multi-query groups of two tiles per wave share one staging area:
 // both waves stream every step, each for its own 32 queries, reading a
 // step's V operands only after its softmax so that three waves fit per SIMD
-// (prefill_chunk 652 -> 702 TFLOP/s, prefill_chunk_gqa 741-757 -> 768-775).
+// (512-query chunks over 4096 tokens: MHA with INT8 652 -> 702 TFLOP/s, 64
+// query heads over 8 with INT8 K / INT4 V 741-757 -> 768-775).
 #ifndef PBQ_MULTI_JOINT_STAGE
 #define PBQ_MULTI_JOINT_STAGE 1
 #endif
@@ -611,9 +613,10 @@ void attn_partition_mha(AttnArgs a) {
 #endif
 constexpr int kPairRankMax = PBQ_PAIR_RANK_MAX;
 // Loop steps the two waves of a paired group that quantize the stored tiles
-// and take the stored steps give up to the other two, measured on gqa70b's
-// shapes: 6 of its 32-token steps (3 was slower, 9 within the noise), and
-// 12 of the shorter INT4 K steps (against 6: 1-2 us less).
+// and take the stored steps give up to the other two, measured on a layer
+// of 64 query heads over 8 KV heads with 128 sequences of 500-2000 tokens:
+// 6 of its 32-token steps (3 was slower, 9 within the noise), and 12 of the
+// shorter INT4 K steps (against 6: 1-2 us less).
 #ifndef PBQ_PAIR_HANDICAP
 #define PBQ_PAIR_HANDICAP 6
 #endif
@@ -1984,7 +1987,7 @@ void attn_partition_gqa(AttnArgs a) {
 template <int D>
 __device__ __forceinline__ void merge_partitions(const AttnArgs& a, int64_t row, int nparts) {
     constexpr int PER = D / 64;
-    constexpr int BATCH = 32;   // 8: 12.1 us, 32: 10.1 us for shared_prefix's 64 partitions
+    constexpr int BATCH = 32;   // 8: 12.1 us, 32: 10.1 us for 32 sequences x 32 heads x 64 partitions
     const int lane = threadIdx.x;
     const int64_t prow0 = row * a.max_partitions;
     const float* ml = a.ws_ml + prow0 * 2;
