@@ -390,8 +390,11 @@ kv_status paged_attn_decode(const kv_pool_desc* desc, const kv_pool_mem* mem,
  * block may not be shared with another sequence of the call.  With a single
  * partition per sequence, the last block's store runs inside the attention
  * kernel (two of the work group's waves quantize its K and V tiles, which
- * the attention then reads from LDS): one launch.  With split partitions,
- * the store kernel runs first, then the decode.  Arguments and errors otherwise as paged_attn_decode; the pool's
+ * the attention then reads from LDS): one launch.  With split partitions
+ * and one query head per KV head the same happens in each sequence's last
+ * partition when that kernel keeps the plain kernel's occupancy; otherwise
+ * (and for grouped query heads) the store kernel runs first, then the
+ * decode.  Arguments and errors otherwise as paged_attn_decode; the pool's
  * tail slots must be set in mem.  [tbr8] §4 store_kv and §5 point 2;
  * [yunthe] Q(x) and x_hat. */
 kv_status paged_attn_decode_append(const kv_pool_desc* desc, const kv_pool_mem* mem,
@@ -415,7 +418,13 @@ kv_status paged_attn_decode_append(const kv_pool_desc* desc, const kv_pool_mem* 
  * once per KV head and 16 queries instead of once per sequence: the prefix
  * partitions run as one matrix-core launch whose queries are all the
  * call's sequences x query heads of a KV head (sequence 0's block table),
- * then the remaining partitions per sequence, then the log-sum-exp reduce.
+ * beside the remaining partitions per sequence, then the log-sum-exp
+ * reduce.  The prefix's launch runs on a second stream of the library's
+ * (one per device, created by the first such call outside a stream capture
+ * and kept until the process ends), forked from `stream` and joined back
+ * to it before the reduce with events: the call stays ordered on `stream`,
+ * and a captured call records both streams' kernels in the graph.  Calls
+ * from several host threads are serialized at the fork.
  * [yunthe] "prefix caching" (blocks shared between requests); the shared
  * pass itself is a scheduling of the same sums.  partition_size must be
  * given (not 0) and a multiple of 32; shared_tokens a positive multiple of

@@ -349,10 +349,11 @@ kv_status decode_impl(const kv_pool_desc* d, const kv_pool_mem* m, const AppendA
     a.ws_out = need ? (float*)workspace : nullptr;
     a.ws_ml = need ? (float*)((char*)workspace + rows * (size_t)d->head_dim * 4) : nullptr;
     if (app && max_parts > 1 && !pbq::split_store_fused(a)) {
-        // split partitions whose fused kernel would lose occupancy: the store
-        // kernel in one-token append mode, then the decode (all but one work
-        // group per sequence and head would carry the fused store's
-        // registers for nothing)
+        // split partitions the partition kernels do not fuse the store into
+        // (grouped query heads, or an MHA kernel that would lose occupancy:
+        // all but one work group per sequence and head would carry the fused
+        // store's registers for nothing): the store kernel in one-token
+        // append mode, then the decode
         pbq::QuantStoreArgs sa{};
         sa.block_size = d->block_size;
         sa.num_kv_heads = d->num_kv_heads;
