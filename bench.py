@@ -426,10 +426,44 @@ def bench_store(w, args):
                      "unit": "GB/s", "frac": round(nbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name), "bytes_per_launch": nbytes},
     }
+    if not args.only_timed:
+        print("elementwise ceiling", file=sys.stderr, flush=True)
+        line["roofline"]["plain_elementwise_ceiling"] = elementwise_ceiling(nbytes)
     if not args.no_cpu_baseline:
         print("cpu baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline_store(setup, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def elementwise_ceiling(nbytes, reps=10):
+    """Context for the store: a plain contiguous elementwise kernel with the
+    store's traffic mix (two bytes read per byte written), torch.add of two
+    fp16 arrays into a third, moving the store call's bytes per call, over
+    two sets of buffers used in turn (each larger than the last-level
+    cache).  It does no scattering and no arithmetic beyond the add."""
+    import numpy as np
+    import torch
+
+    n = nbytes // 6   # fp16 elements: 2 n B read twice, 2 n B written
+    bufs = [[torch.randn(n, dtype=torch.float16, device="cuda") for _ in range(3)] for _ in range(2)]
+    stream = torch.cuda.current_stream()
+    ms = []
+    for i in range(reps + 2):
+        x, y, z = bufs[i % 2]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        torch.add(x, y, out=z)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            ms.append(a.elapsed_time(b))
+    del bufs
+    t = float(np.median(ms))
+    moved = 6 * n
+    return {"kernel": "torch.add (fp16, a + b -> c), contiguous", "bytes": moved,
+            "gbs": round(moved / (t * 1e-3) / 1e9, 1), "frac": round(moved / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "context for roofline.frac: the store's 2:1 read:write mix in a plain elementwise kernel, "
+                    "not a denominator"}
 
 
 def read_ceiling(setup, reps=10):
