@@ -278,6 +278,52 @@ def cpu_baseline_multi(setup, seconds):
                       f"numpy, dequantization included, {dt:.1f} s"}
 
 
+def dense_attention_context(w, ctx, reps=10):
+    """Context for the multi-query kernel: the library's dense fp16 attention
+    (torch scaled_dot_product_attention, flash backend, else the
+    memory-efficient one) on the workload's shape -- every sequence's
+    q_len queries over its whole context, all query heads (K and V expanded
+    to them beforehand), no quantization, no block tables and no mask, so
+    every query sees every key -- over two sets of K and V used in turn.
+    TFLOP/s counts 4 D per (query, key, head) as the kernel's figure does."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    S, Hq, D, n = w.num_seqs, w.num_q_heads, w.head_dim, w.q_len
+    L_ = int(max(ctx))
+    g = torch.Generator(device="cuda").manual_seed(17)
+    q = torch.randn(S, Hq, n, D, dtype=torch.float16, device="cuda", generator=g)
+    kv = [[torch.randn(S, Hq, L_, D, dtype=torch.float16, device="cuda", generator=g) for _ in range(2)]
+          for _ in range(2)]
+    stream = torch.cuda.current_stream()
+    for name, be in (("flash", SDPBackend.FLASH_ATTENTION), ("memory-efficient", SDPBackend.EFFICIENT_ATTENTION)):
+        try:
+            with sdpa_kernel(be):
+                ms = []
+                for i in range(reps + 4):
+                    k, v = kv[i % 2]
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    F.scaled_dot_product_attention(q, k, v)
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    if i >= 4:
+                        ms.append(a.elapsed_time(b))
+        except RuntimeError:
+            continue
+        t = float(np.median(ms))
+        flops = 4 * D * Hq * n * L_ * S
+        del q, kv
+        return {"kernel": f"torch scaled_dot_product_attention ({name} backend), fp16, dense", "ms": round(t, 4),
+                "flops": flops, "tflops": round(flops / (t * 1e-3) / 1e12, 1),
+                "frac": round(flops / (t * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                "note": "context for roofline.frac: the same shape as dense fp16 tensors with every key "
+                        "visible (no codes to convert, no tables, no mask), not a denominator"}
+    return None
+
+
 def bench_multi(w, args):
     """Multi-query (chunked prefill) attention: K timed calls of
     paged_attn_multi_query over the workload's pool."""
@@ -325,6 +371,9 @@ def bench_multi(w, args):
                      "traffic": measured_traffic(w.name),
                      "flops_per_launch": flops, "bytes_per_launch": nbytes},
     }
+    if not args.only_timed:
+        print("dense attention context", file=sys.stderr, flush=True)
+        line["roofline"]["library_dense_attention"] = dense_attention_context(w, setup.ctx)
     if not args.no_cpu_baseline:
         print("cpu baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline_multi(setup, args.cpu_seconds)
